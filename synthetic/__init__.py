@@ -1,0 +1,151 @@
+"""Seeded synthetic inputs shaped like the workloads of the W4A16 group-wise INT4 pages.
+
+This module only draws random tensors; it holds none of the quantization arithmetic.
+Both the CPU oracle tests and the GPU path take their inputs from here, so the two sides
+see identical bytes.
+
+Distribution recipe (stated once, used everywhere):
+
+* Weights: ``randn`` in fp32 times ``sigma``.  A set of "outlier" input channels
+  (columns of W) is multiplied by a factor in fp32, then the tensor is cast once to the
+  target dtype (round-to-nearest-even for bf16/fp16).  The outlier fraction is about 0.1%
+  of the input channels, the share the page "Quantization Algorithms 단권화" gives for
+  emergent outlier channels (LLM.int8() chapter, "problem: emergent outlier").
+* Activations: ``randn`` in fp32 (standard normal), optionally with the same outlier
+  channels scaled, then cast once to the activation dtype.
+* Outlier channel set: ``randperm(K)[:round(0.001*K)]`` from the weight's own generator,
+  so weight and activation outliers sit on the same channels.
+
+Every generator is a ``torch.Generator`` seeded with the stated seed.  Host (CPU)
+generation is the default.  ``device="cuda"`` uses a seeded device generator (a
+different stream of numbers than the CPU one, still deterministic); it serves the
+multi-gigabyte checkpoint sweep, whose parity is checked on rows copied back to the host.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional, Sequence
+
+import torch
+
+__all__ = [
+    "outlier_channels",
+    "weight",
+    "activations",
+    "Matrix",
+    "TINY",
+    "DECODE_7B",
+    "MLP_SWEEP",
+    "PREFILL_70B",
+    "checkpoint_7b",
+]
+
+
+def outlier_channels(k: int, seed: int, fraction: float = 0.001) -> torch.Tensor:
+    """Indices of the outlier input channels for a K-wide matrix (int64, sorted)."""
+    n_out = int(round(fraction * k))
+    g = torch.Generator().manual_seed(int(seed) * 7919 + 17)
+    idx = torch.randperm(k, generator=g)[:n_out]
+    return torch.sort(idx).values
+
+
+def weight(n: int, k: int, sigma: float, seed: int, dtype=torch.bfloat16,
+           outlier_factor: float = 0.0, device: str = "cpu") -> torch.Tensor:
+    """W [n, k] ~ N(0, sigma^2), optional outlier input channels times ``outlier_factor``."""
+    if device == "cpu":
+        g = torch.Generator().manual_seed(int(seed))
+    else:
+        g = torch.Generator(device=device).manual_seed(int(seed))
+    w = torch.randn(n, k, generator=g, dtype=torch.float32, device=device)
+    w.mul_(sigma)
+    if outlier_factor:
+        cols = outlier_channels(k, seed).to(device)
+        w[:, cols] *= outlier_factor
+    return w.to(dtype)
+
+
+def activations(m: int, k: int, seed: int, dtype=torch.bfloat16,
+                outlier_seed: Optional[int] = None, outlier_factor: float = 0.0,
+                device: str = "cpu") -> torch.Tensor:
+    """x [m, k] ~ N(0, 1); channels of ``outlier_channels(k, outlier_seed)`` times a factor."""
+    if device == "cpu":
+        g = torch.Generator().manual_seed(int(seed))
+    else:
+        g = torch.Generator(device=device).manual_seed(int(seed))
+    x = torch.randn(m, k, generator=g, dtype=torch.float32, device=device)
+    if outlier_factor and outlier_seed is not None:
+        cols = outlier_channels(k, outlier_seed).to(device)
+        x[:, cols] *= outlier_factor
+    return x.to(dtype)
+
+
+@dataclasses.dataclass(frozen=True)
+class Matrix:
+    """One projection-shaped weight matrix of a workload."""
+    name: str
+    n: int            # output features (rows of W)
+    k: int            # input features (columns of W, the group axis)
+    sigma: float
+    seed: int
+    outlier_factor: float = 0.0
+    dtype: torch.dtype = torch.bfloat16
+
+    def make(self, device: str = "cpu") -> torch.Tensor:
+        return weight(self.n, self.k, self.sigma, self.seed, self.dtype,
+                      self.outlier_factor, device)
+
+
+# Tiny reference: W fp32 [256 x 512] ~ N(0, 0.02), x bf16 [1 x 512] ~ N(0, 1), group 128.
+TINY = dict(
+    w=Matrix("tiny", 256, 512, 0.02, seed=0, dtype=torch.float32),
+    x_seed=1, m=1, group_size=128,
+)
+
+# 7B-like decode projections, M = 1, group 128, asymmetric; 0.1% outlier columns x20.
+DECODE_7B = dict(
+    mats=[Matrix("attn_4096x4096", 4096, 4096, 0.02, seed=2, outlier_factor=20.0),
+          Matrix("mlp_11008x4096", 11008, 4096, 0.02, seed=3, outlier_factor=20.0)],
+    x_seed=4, m=1, group_size=128, symmetric=False,
+)
+
+# 7B-like MLP batch sweep: both MLP orientations, g in {32, 64, 128}, sym and asym,
+# M in {1, 2, 4, 8, 16} (first M rows of one x per K).
+MLP_SWEEP = dict(
+    mats=[Matrix("up_11008x4096", 11008, 4096, 0.02, seed=5),
+          Matrix("down_4096x11008", 4096, 11008, 0.02, seed=6)],
+    x_seed=7, ms=(1, 2, 4, 8, 16), group_sizes=(32, 64, 128), symmetric=(False, True),
+)
+
+# 70B-like prefill: W [28672 x 8192] ~ N(0, 0.015) with 0.1% outlier channels x20,
+# x [2048 x 8192] ~ N(0, 1) with the same channels x10; group 128 asymmetric.
+PREFILL_70B = dict(
+    w=Matrix("mlp_28672x8192", 28672, 8192, 0.015, seed=8, outlier_factor=20.0),
+    x_seed=9, m=2048, x_outlier_factor=10.0, group_size=128, symmetric=False,
+)
+
+
+def checkpoint_7b(layers: int = 32) -> List[Matrix]:
+    """The 32-layer 7B-like checkpoint: per layer q, k, v, o [4096x4096], gate, up
+    [11008x4096], down [4096x11008], bf16 ~ N(0, 0.02); seed 100 + 7*layer + index."""
+    shapes = [("q", 4096, 4096), ("k", 4096, 4096), ("v", 4096, 4096), ("o", 4096, 4096),
+              ("gate", 11008, 4096), ("up", 11008, 4096), ("down", 4096, 11008)]
+    out = []
+    for layer in range(layers):
+        for idx, (nm, n, k) in enumerate(shapes):
+            out.append(Matrix(f"L{layer}.{nm}", n, k, 0.02, seed=100 + 7 * layer + idx))
+    return out
+
+
+def sample_rows(n: int, count: int, seed: int) -> torch.Tensor:
+    """A seeded, sorted sample of ``count`` distinct row indices in [0, n), always
+    including the first and the last row (edges of the tiling)."""
+    count = min(count, n)
+    g = torch.Generator().manual_seed(int(seed))
+    idx = torch.randperm(n, generator=g)[:count]
+    idx = torch.unique(torch.cat([idx, torch.tensor([0, n - 1])]))
+    return idx[:max(count, 2)] if idx.numel() > count + 2 else idx
+
+
+def as_u16(t: torch.Tensor):
+    """Raw 16-bit patterns of a bf16/fp16 tensor as a numpy uint16 array (host copy)."""
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view("uint16")

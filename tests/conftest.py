@@ -1,0 +1,29 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+TESTS = os.path.dirname(os.path.abspath(__file__))
+if TESTS not in sys.path:
+    sys.path.insert(0, TESTS)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU; runs the HIP path")
+    config.addinivalue_line("markers", "slow: long CPU test")
+
+
+def pytest_runtest_setup(item):
+    if "gpu" in item.keywords:
+        import torch
+        if not torch.cuda.is_available():
+            pytest.fail("GPU test selected but no GPU is visible to torch")
+
+
+@pytest.fixture(scope="session")
+def orc():
+    import oracle
+    return oracle.default()

@@ -1,0 +1,334 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Each ``check_*`` takes an ``oracle.Oracle`` and raises ``AssertionError`` on a mismatch.
+The same checks run against the real oracle (test_oracle_pins.py) and against copies of
+its C source with a planted mistake (test_oracle_mutants.py), which must each fail at
+least one check.
+
+What pins what:
+  * hand-worked groups (tests/golden/hand_worked_groups.txt): codes, scales, zero points
+    and word layout, derived by hand from the affine quantizer of "LLM Quantization:
+    GPTQ·AWQ·SmoothQuant·FP8·KV Cache (7/10)" §Affine Quantization;
+  * numpy's float16 conversion (an independent implementation) pins fp32 <-> fp16;
+  * closed-form properties: code ranges, zero exactly representable, |x - x_hat| <= s/2
+    for unclipped weights, 15*S and 7*S against the data range, 2^4 levels;
+  * brute force: each code is the nearest grid level (search over all 16 levels);
+  * byte accounting from the pages' arithmetic (payload P*b/8, fp16 scale per 128 weights
+    = 0.015625 B/weight, 32 four-bit codes + one fp16 scale = 4.5 bits/weight);
+  * the fp64 matmul against numpy's float64 matmul of the dequantized weights, one-hot
+    and zero activations, integer data with unit scales.
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                      "hand_worked_groups.txt")
+
+
+# --------------------------------------------------------------------------- helpers
+
+def load_golden():
+    rows = []
+    with open(GOLDEN, encoding="utf-8") as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            f = [c.strip() for c in line.split("|")]
+            rows.append(dict(
+                name=f[0], sym=(f[1] == "sym"), g=int(f[2]),
+                values=np.array([np.float32(v) for v in f[3].split()], dtype=np.float32),
+                s16=int(f[4], 16), z=int(f[5]),
+                codes=[int(c) for c in f[6].split()],
+                words=[int(w, 16) for w in f[7].split()]))
+    return rows
+
+
+def unpack_codes(qweight: np.ndarray, k: int) -> np.ndarray:
+    """Stored 4-bit codes [n, k] from packed words (little-endian nibbles)."""
+    q = qweight.astype(np.uint64)
+    shifts = (4 * np.arange(8, dtype=np.uint64))
+    codes = (q[:, :, None] >> shifts[None, None, :]) & np.uint64(0xF)
+    return codes.reshape(qweight.shape[0], k).astype(np.int64)
+
+
+def unpack_zeros(zeros: np.ndarray, G: int) -> np.ndarray:
+    z = zeros.astype(np.uint64)
+    shifts = (4 * np.arange(8, dtype=np.uint64))
+    nib = (z[:, :, None] >> shifts[None, None, :]) & np.uint64(0xF)
+    return nib.reshape(zeros.shape[0], -1)[:, :G].astype(np.int64)
+
+
+def f16_values(scales: np.ndarray) -> np.ndarray:
+    return scales.view(np.float16).astype(np.float64)
+
+
+def random_weights(seed: int, n: int, k: int) -> np.ndarray:
+    """A mix of distributions that stresses every branch: normal, heavy outliers,
+    one-sided groups, all-zero rows, constant rows, tiny values (subnormal fp16
+    scales) and huge values (fp16 scale saturation)."""
+    rng = np.random.default_rng(seed)
+    w = rng.standard_normal((n, k)).astype(np.float32) * np.float32(0.02)
+    w[1] *= 50                                   # wide row
+    w[2, ::37] *= 400                            # sparse outliers
+    w[3] = np.abs(w[3]) + np.float32(0.5)        # all positive (one-sided)
+    w[4] = -np.abs(w[4]) - np.float32(0.25)      # all negative (one-sided)
+    w[5] = 0                                     # degenerate groups
+    w[6] = np.float32(0.375)                     # constant row
+    w[7] *= np.float32(1e-4)                     # scales in the fp16 subnormal range
+    w[10] *= np.float32(1e-7)                    # scales that underflow fp16 to zero
+    w[8] = rng.standard_normal(k).astype(np.float32) * np.float32(3e5)  # scale > 65504
+    w[9] = np.round(rng.standard_normal(k) * 3).astype(np.float32)      # small integers
+    return w
+
+
+# --------------------------------------------------------------------------- checks
+
+def check_golden_groups(o):
+    for r in load_golden():
+        v = r["values"].reshape(1, -1)
+        q, s, z = o.quantize_pack(v, r["g"], r["sym"])
+        k = v.shape[1]
+        codes = unpack_codes(q, k)[0].tolist()
+        assert codes == r["codes"], (r["name"], codes, r["codes"])
+        assert [int(x) for x in q[0]] == r["words"], (r["name"], [hex(int(x)) for x in q[0]])
+        assert int(s[0, 0]) == r["s16"], (r["name"], hex(int(s[0, 0])))
+        if not r["sym"]:
+            assert int(unpack_zeros(z, 1)[0, 0]) == r["z"], (r["name"], int(z[0, 0]))
+        # dequantized value of each code: S * (u - z), z = 8 for symmetric
+        xh = o.dequant(q, s, z, 1, k, r["g"], r["sym"])[0]
+        S = float(np.uint16(r["s16"]).view(np.float16))
+        zz = 8 if r["sym"] else r["z"]
+        assert np.array_equal(xh, S * (np.array(r["codes"], dtype=np.float64) - zz)), r["name"]
+
+
+def check_fp16_conversion(o):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float32)
+    finite = np.isfinite(ref)
+    # widening: every binary16 pattern
+    for b, r in zip(bits.tolist(), ref.tolist()):
+        got = o.f16_bits_to_f32(b)
+        if np.isnan(r):
+            assert np.isnan(got), hex(b)
+        else:
+            assert got == r and np.signbit(got) == np.signbit(r), (hex(b), got, r)
+    # narrowing: exact values, midpoints (ties), and one fp32 ulp either side
+    vals = ref[finite & (np.abs(ref) < np.float32(65504))]
+    vals = np.sort(np.unique(vals[vals >= 0]))
+    mids = ((vals[:-1].astype(np.float64) + vals[1:]) / 2).astype(np.float32)
+    up = np.nextafter(mids, np.float32(np.inf))
+    dn = np.nextafter(mids, np.float32(-np.inf))
+    rng = np.random.default_rng(0)
+    rnd = rng.integers(0, 2 ** 32, 20000, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    special = np.array([0.0, -0.0, 65504, 65519.996, 65520, 65536, 1e9, np.inf, -np.inf,
+                        2.0 ** -24, 2.0 ** -25, 2.0 ** -25 * 1.0000001, 2.0 ** -26,
+                        2.0 ** -14, 2.0 ** -14 * (1 - 2 ** -11), 6.1e-5, 1e-45, -1e-45],
+                       dtype=np.float32)
+    pool = np.concatenate([vals, -vals, mids, -mids, up, dn, rnd, special]).astype(np.float32)
+    for f in pool.tolist():
+        f32 = np.float32(f)
+        with np.errstate(over="ignore"):
+            want = np.array([f32]).astype(np.float16).view(np.uint16)[0]
+        got = o.f32_to_f16_bits(float(f32))
+        if np.isnan(f32):
+            assert (got & 0x7C00) == 0x7C00 and (got & 0x3FF), hex(got)
+        else:
+            assert got == int(want), (float(f32), hex(got), hex(int(want)))
+
+
+def _quantize_many(o, w, g, sym):
+    n, k = w.shape
+    q, s, z = o.quantize_pack(w, g, sym)
+    G = k // g
+    codes = unpack_codes(q, k)
+    S = f16_values(s)
+    zz = np.full((n, G), 8, dtype=np.int64) if sym else unpack_zeros(z, G)
+    return q, s, z, codes, S, zz
+
+
+def check_invariants(o):
+    for seed, (n, k, g) in enumerate([(12, 256, 32), (12, 512, 64), (12, 1024, 128),
+                                      (12, 96, 32)]):
+        w = random_weights(seed, n, k)
+        for sym in (False, True):
+            q, s, z, codes, S, zz = _quantize_many(o, w, g, sym)
+            G = k // g
+            assert codes.min() >= 0 and codes.max() <= 15
+            normal_g = ((s & 0x7C00) != 0) & (s != 0x7BFF)   # normal, unsaturated scale
+            if sym:
+                # |x / S| <= 7 (1 + 2^-11) rounds to <= 7 when S is a normal fp16 value,
+                # so symmetric codes never need q = -8
+                assert (codes[np.repeat(normal_g, g, axis=1)] != 0).all()
+            assert zz.min() >= 0 and zz.max() <= 15
+            assert np.all(np.isfinite(S)) and np.all(S > 0)
+            xh = o.dequant(q, s, z, n, k, g, sym)
+            Sk = np.repeat(S, g, axis=1)
+            zk = np.repeat(zz, g, axis=1)
+            # x_hat is S * (u - z) with the stored z
+            assert np.array_equal(xh, Sk * (codes - zk))
+            wd = w.astype(np.float64)
+            err = np.abs(wd - xh)
+            bound = Sk / 2 * (1 + 2.0 ** -19)
+            big = err > bound
+            # zero is exactly representable: a zero weight lands on the zero point
+            zero = wd == 0
+            assert np.all(codes[zero] == zk[zero]) and np.all(xh[zero] == 0)
+            if sym:
+                # no clipping in symmetric mode while S is a normal fp16 value
+                nz = np.repeat(normal_g, g, axis=1)
+                assert not np.any(big & nz), np.argwhere(big & nz)[:4]
+            else:
+                sat = np.repeat(s == 0x7BFF, g, axis=1)
+                clip = big & ~sat
+                # clipping happens only from above, at the top code
+                assert np.all((codes[clip] == 15) & (wd[clip] > xh[clip])), \
+                    np.argwhere(clip & ((codes != 15) | (wd <= xh)))[:4]
+                # with a normal fp16 scale it costs less than one level; a subnormal scale
+                # can round far below s and clip more, but only when 15*S < the range
+                normal = np.repeat((s & 0x7C00) != 0, g, axis=1)
+                assert np.all(err[clip & normal] < Sk[clip & normal])
+                wg_ = wd.reshape(n, G, g)
+                span_ = np.maximum(wg_.max(axis=2), 0) - np.minimum(wg_.min(axis=2), 0)
+                short = np.repeat(15 * S < span_, g, axis=1)
+                assert np.all(short[clip])
+            # the grid spans the data: 15 S (asym) or 7 S (sym) equals the range up to
+            # the fp16 rounding of the scale
+            wg = wd.reshape(n, G, g)
+            if sym:
+                span = np.abs(wg).max(axis=2)
+                lev = 7.0
+            else:
+                span = np.maximum(wg.max(axis=2), 0) - np.minimum(wg.min(axis=2), 0)
+                lev = 15.0
+            ok = (span == 0) | (s == 0x7BFF) | (span < 2.0 ** -14 * lev)
+            rel = np.abs(lev * S - span) / np.where(span > 0, span, 1)
+            assert np.all(ok | (rel <= 2.0 ** -11 * 1.0001)), rel[~ok].max()
+
+
+def check_brute_force_nearest(o):
+    rng = np.random.default_rng(7)
+    for trial in range(40):
+        g = int(rng.choice([8, 16, 32]))
+        n = 8
+        w = (rng.standard_normal((n, 4 * g)) * rng.choice([0.02, 1.0, 30.0])).astype(np.float32)
+        if trial % 5 == 0:
+            w += np.float32(rng.standard_normal())
+        for sym in (False, True):
+            q, s, z, codes, S, zz = _quantize_many(o, w, g, sym)
+            Sk = np.repeat(S, g, axis=1)
+            zk = np.repeat(zz, g, axis=1)
+            levels = np.arange(16, dtype=np.float64)
+            grid = Sk[:, :, None] * (levels[None, None, :] - zk[:, :, None])
+            d = np.abs(w.astype(np.float64)[:, :, None] - grid)
+            if sym:
+                d[:, :, 0] = np.inf  # q = -8 is outside what max|x|/7 can reach
+            best = d.argmin(axis=2)
+            srt = np.sort(d, axis=2)
+            clear = (srt[:, :, 1] - srt[:, :, 0]) > 1e-6 * Sk  # not a near-tie
+            assert np.all(codes[clear] == best[clear]), np.argwhere(codes != best)[:4]
+
+
+def check_levels_and_bytes(o):
+    # 4 bits -> 2^4 = 16 levels: the L16 golden group reaches all of them
+    rows = {r["name"]: r for r in load_golden()}
+    assert sorted(set(rows["L16"]["codes"])) == list(range(16))
+    # payload = P * b / 8 bytes; 7e9 parameters at 4 bits = 3.5e9 bytes
+    qw, sc, zw = o.sizes(4096, 4096, 128)
+    assert qw * 4 == 4096 * 4096 * 4 // 8
+    P = 7_000_000_000
+    assert o.sizes(1, 8 * (P // 8), 8)[0] * 4 == P * 4 // 8 == 3_500_000_000
+    # one fp16 scale per 128 weights = 2/128 = 0.015625 bytes per weight
+    assert sc * 2 / (4096 * 4096) == 0.015625
+    # zero points: 8 four-bit values per word, rows padded to whole words
+    assert zw == 4096 * ((4096 // 128 + 7) // 8)
+    assert o.sizes(11008, 11008, 128)[2] == 11008 * 11  # 86 groups -> 11 words per row
+    # symmetric, group 32: 32 four-bit codes + one fp16 scale = 4.5 bits per weight
+    qw, sc, _ = o.sizes(64, 4096, 32)
+    assert (qw * 4 + sc * 2) * 8 / (64 * 4096) == 4.5
+
+
+def check_dequant_closed_forms(o):
+    # integer data with range [0, 15] (asym) or max |x| = 7 (sym) has S = 1 exactly and
+    # dequantizes to itself
+    rng = np.random.default_rng(3)
+    a = rng.integers(0, 16, (6, 64)).astype(np.float32)
+    a[:, 0], a[:, 1], a[:, 32], a[:, 63] = 0, 15, 0, 15
+    q, s, z = o.quantize_pack(a, 32, False)
+    assert np.all(s == 0x3C00)
+    assert np.array_equal(o.dequant(q, s, z, 6, 64, 32, False), a.astype(np.float64))
+    b = rng.integers(-7, 8, (6, 64)).astype(np.float32)
+    b[:, 0], b[:, 33] = 7, -7
+    q, s, z = o.quantize_pack(b, 32, True)
+    assert np.all(s == 0x3C00)
+    assert np.array_equal(o.dequant(q, s, z, 6, 64, 32, True), b.astype(np.float64))
+    # symmetric storage is asymmetric storage with every zero point equal to 8
+    w = random_weights(11, 12, 256)
+    q, s, _ = o.quantize_pack(w, 64, True)
+    eights = np.full((12, 1), 0x88888888, dtype=np.uint32)
+    assert np.array_equal(o.dequant(q, s, eights, 12, 256, 64, False),
+                          o.dequant(q, s, eights, 12, 256, 64, True))
+
+
+def check_linear(o):
+    rng = np.random.default_rng(5)
+    n, k, g, m = 24, 384, 64, 3
+    w = random_weights(21, n, k)
+    for sym in (False, True):
+        q, s, z = o.quantize_pack(w, g, sym)
+        xh = o.dequant(q, s, z, n, k, g, sym)
+        x = rng.standard_normal((m, k)).astype(np.float32)
+        y, yabs = o.linear(x, q, s, z, n, k, g, sym)
+        ref = x.astype(np.float64) @ xh.T
+        refabs = np.abs(x.astype(np.float64)) @ np.abs(xh).T
+        assert np.allclose(y, ref, rtol=1e-12, atol=1e-12 * refabs.max())
+        assert np.allclose(yabs, refabs, rtol=1e-12)
+        # sampled (m, n) pairs equal the full result
+        rows, cols = np.array([2, 0]), np.array([23, 5, 0, 7])
+        ys, _ = o.linear(x, q, s, z, n, k, g, sym, rows=rows, cols=cols)
+        assert np.array_equal(ys, y[np.ix_(rows, cols)])
+        # one-hot activation picks one dequantized column exactly; zero gives zero
+        for kk in (0, 1, 63, 64, k - 1):
+            e = np.zeros((1, k), dtype=np.float32)
+            e[0, kk] = 1
+            ye, _ = o.linear(e, q, s, z, n, k, g, sym)
+            assert np.array_equal(ye[0], xh[:, kk])
+        y0, _ = o.linear(np.zeros((2, k), dtype=np.float32), q, s, z, n, k, g, sym)
+        assert np.all(y0 == 0)
+        # bf16 and fp16 activations are read exactly
+        xb = x.astype(np.float16)
+        yb, _ = o.linear(xb, q, s, z, n, k, g, sym)
+        assert np.allclose(yb, xb.astype(np.float64) @ xh.T, rtol=1e-12,
+                           atol=1e-12 * refabs.max())
+        bits = (x.view(np.uint32) >> 16).astype(np.uint16)   # truncated to bf16
+        xbf = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        yb2, _ = o.linear((bits, 2), q, s, z, n, k, g, sym)
+        assert np.allclose(yb2, xbf @ xh.T, rtol=1e-12, atol=1e-12 * refabs.max())
+    # integer weights with unit scales and integer activations give exact integers
+    a = rng.integers(0, 16, (8, 128)).astype(np.float32)
+    a[:, 0], a[:, 1] = 0, 15
+    q, s, z = o.quantize_pack(a, 128, False)
+    xi = rng.integers(-4, 5, (2, 128)).astype(np.float32)
+    y, _ = o.linear(xi, q, s, z, 8, 128, 128, False)
+    assert np.array_equal(y, xi.astype(np.float64) @ a.astype(np.float64).T)
+
+
+def check_argument_rejection(o):
+    w = np.zeros((2, 96), dtype=np.float32)
+    for g in (64, 7, 12):          # 96 is not a multiple of 64 or 7; 12 leaves k % 8 == 0
+        try:
+            o.quantize_pack(w, g, False)
+        except ValueError:
+            assert g != 12, "k=96, g=12 is a valid layout"
+            continue
+        assert g == 12, f"group {g} should be rejected for k=96"
+    assert o.lib.orc_quantize_pack(None, 0, 2, 96, 0, 0, None, None, None, None) == -1
+    assert o.lib.orc_quantize_pack(None, 0, 2, 20, 4, 0, None, None, None, None) == -1
+
+
+ALL_CHECKS = [check_golden_groups, check_fp16_conversion, check_invariants,
+              check_brute_force_nearest, check_levels_and_bytes, check_dequant_closed_forms,
+              check_linear, check_argument_rejection]

@@ -1,0 +1,60 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each case copies the oracle's C source, plants one plausible mistake (a wrong rounding
+order, a dropped term, a wrong sign or index, a swapped operand ...), compiles the copy
+on the CPU and runs every pin against it.  At least one pin has to fail; a mutant that
+passes every pin would mean the pins cannot tell that mistake from the real definition.
+"""
+import os
+
+import pytest
+
+import oracle
+import pins
+
+MUTANTS = [
+    ("add_then_round", "rintf(v[t] / S) + (float)z", "rintf(v[t] / S + (float)z)"),
+    ("quantize_with_fp32_scale", "rintf(v[t] / S) + (float)z", "rintf(v[t] / s) + (float)z"),
+    ("no_zero_extension", "float x_min = 0.0f, x_max = 0.0f;",
+     "float x_min = v[0], x_max = v[0];"),
+    ("sym_divides_by_8", "s = amax / 7.0f;", "s = amax / 8.0f;"),
+    ("sym_uses_signed_max", "amax = fmaxf(amax, fabsf(v[t]));", "amax = fmaxf(amax, v[t]);"),
+    ("asym_divides_by_16", "s = (x_max - x_min) / 15.0f;", "s = (x_max - x_min) / 16.0f;"),
+    ("nibbles_reversed", "|= u << (4 * (col % 8));", "|= u << (4 * (7 - col % 8));"),
+    ("zero_point_sign", "rintf(-x_min / S)", "rintf(x_min / S)"),
+    ("zero_word_index", "zeros[row * zw + j / 8] |= (uint32_t)z << (4 * (j % 8));",
+     "zeros[row * zw + j / 8] |= (uint32_t)z << (4 * (j / 8));"),
+    ("fp16_truncates", "if (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) h += 1u;", ""),
+    ("fp16_ties_away", "(rem == 0x1000u && (h & 1u))", "(rem == 0x1000u)"),
+    ("fp16_subnormal_exponent", "mag = ldexpf((float)m, -24);", "mag = ldexpf((float)m, -25);"),
+    ("degenerate_scale_zero", "s16 = 0x3C00u;  /* 1.0 */", "s16 = 0x0000u;"),
+    ("sym_stores_twos_complement", "symmetric ? q + 8 : q", "symmetric ? (q & 15) : q"),
+    ("asym_range_0_14", "const float q_max = symmetric ? 7.0f : 15.0f;",
+     "const float q_max = symmetric ? 7.0f : 14.0f;"),
+    ("dequant_drops_zero", "return S * ((double)u - (double)z);", "return S * (double)u;"),
+    ("dequant_group_index", "const int64_t j = col / g;", "const int64_t j = col / 8;"),
+    ("linear_drops_first_term", "acc += xv * wrow[kk];", "if (kk) acc += xv * wrow[kk];"),
+    ("linear_transposed_x", "load_elem(x, x_dtype, row_m * k + kk)",
+     "load_elem(x, x_dtype, kk * m + row_m)"),
+    ("bf16_widening_shift", "uint32_t bits = (uint32_t)b << 16;",
+     "uint32_t bits = (uint32_t)b << 15;"),
+    ("zero_rows_padding", "return n * ((k / g + 7) / 8);", "return n * ((k / g) / 8);"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, name, old, new):
+    src = open(oracle.SOURCE, encoding="utf-8").read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique/present"
+    path = tmp_path / "mutant.c"
+    path.write_text(src.replace(old, new), encoding="utf-8")
+    lib = oracle.compile_source(str(path), str(tmp_path / "libmutant.so"),
+                                include_dir=os.path.dirname(oracle.SOURCE))
+    o = oracle.Oracle(lib)
+    caught = []
+    for check in pins.ALL_CHECKS:
+        try:
+            check(o)
+        except Exception as exc:  # AssertionError, or a crash-free error from bad output
+            caught.append(f"{check.__name__}: {type(exc).__name__}")
+    assert caught, f"mutant {name} passed every pin"
