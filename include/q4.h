@@ -1,0 +1,108 @@
+/* q4.h — C ABI of the MI355X (gfx950) group-wise INT4 weight-only (W4A16) library.
+ *
+ * What the operations are (pages cited by title and section):
+ *   [FL7] "LLM Quantization: GPTQ·AWQ·SmoothQuant·FP8·KV Cache (7/10)", blog.ruahverce.com
+ *   [QA1] "Quantization Algorithms 단권화", brianyu43.github.io (V10)
+ *   [YJ]  "최신 LLM 양자화 기술 총정리 — GPTQ·AWQ부터 FP8·MXFP4·KV 캐시 양자화까지",
+ *         youngju.dev (Korean and English versions)
+ *
+ * Packed format (canonical, layout version 1).  W is [n][k] row-major: n output features,
+ * k input features.  A group is g consecutive input columns of one row ([FL7] §Per-group),
+ * G = k / g groups per row.
+ *   qweight : uint32 [n][k/8]; the 4-bit code of column 8j+i is bits 4i..4i+3 of word j.
+ *   scales  : fp16 bit patterns [n][G], the scale S of each group.
+ *   zeros   : uint32 [n][ceil(G/8)]; zero point of group 8j+i in bits 4i..4i+3 of word j,
+ *             unused pad nibbles are 0.  Asymmetric mode only.
+ * Asymmetric codes are q in [0,15] stored as is; symmetric codes q in [-8,7] are stored
+ * as u = q + 8 (an implicit zero point of 8) ([QA1] §Signed ↔ Unsigned gives the ranges).
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are device memory owned by the caller.  The library allocates
+ *     nothing, frees nothing and does not synchronize: work is enqueued on `stream`
+ *     (NULL = the default stream) and the call returns.
+ *   - Arguments are validated on the host before anything is enqueued; an invalid call
+ *     returns a non-zero q4_status and touches no memory.  A launch failure reported by
+ *     the runtime returns Q4_ERR_LAUNCH.  Faults during execution surface at the
+ *     caller's next synchronization, as for any asynchronous HIP work.
+ *   - Sizes: 1 <= n, 1 <= k, k % group_size == 0, group_size in {32, 64, 128}, and
+ *     n*k < 2^40 (so every element index fits comfortably in 64 bits).
+ *   - Alignment: w, x, qweight and w_out 16 bytes; zeros and y 4 bytes; scales 2 bytes.
+ *   - There is no fallback path: each call runs the hand-written kernel named by
+ *     q4_last_kernel(), or fails.
+ */
+#ifndef Q4_H
+#define Q4_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    Q4_OK = 0,
+    Q4_ERR_NULL = 1,    /* a required pointer is NULL */
+    Q4_ERR_SHAPE = 2,   /* n, k or m out of range, or k not a multiple of group_size */
+    Q4_ERR_GROUP = 3,   /* group_size not in {32, 64, 128} */
+    Q4_ERR_DTYPE = 4,   /* dtype not accepted by this entry point */
+    Q4_ERR_ALIGN = 5,   /* a pointer misses its required alignment */
+    Q4_ERR_LAUNCH = 6   /* the HIP runtime rejected the kernel launch */
+} q4_status;
+
+typedef enum { Q4_F32 = 0, Q4_F16 = 1, Q4_BF16 = 2 } q4_dtype;
+
+/* RTN quantize-and-pack of W [n][k] (F32, F16 or BF16) into the packed format.
+ *   q = clamp(round(w/s) + z, q_min, q_max)      [FL7] §Affine Quantization
+ * with, per group, computed in fp32:
+ *   asymmetric: s = (max(x_max,0) - min(x_min,0)) / 15, z = clamp(round(-min(x_min,0)/S), 0, 15)
+ *               ([FL7] §Symmetric과 Asymmetric, zero kept exactly representable);
+ *   symmetric:  s = max|x| / 7, z = 0, q in [-8, 7] stored as q + 8.
+ * S is s rounded to fp16 (round-to-nearest-even); S = 0 is replaced by 1.0 and S = inf by
+ * 65504; the codes are computed with S, round() is round-half-to-even, the division is
+ * IEEE fp32.  Codes, scales and zeros are bit-identical to the CPU definition.
+ * zeros may be NULL when symmetric != 0 (it is not written then). */
+q4_status q4_quantize_pack(const void* w, q4_dtype w_dtype, int64_t n, int64_t k,
+                           int32_t group_size, int32_t symmetric,
+                           uint32_t* qweight, uint16_t* scales, uint32_t* zeros,
+                           hipStream_t stream);
+
+/* Path B of [FL7] §Kernel이 없으면 압축 이점이 사라진다 (full dequantization):
+ *   w_out[n][k] = S * (u - z),   x_hat = s(q - z)   [FL7] §Affine Quantization
+ * with z = 8 in symmetric mode.  F32 output is exact; F16 and BF16 outputs are one
+ * round-to-nearest-even of the exact value. */
+q4_status q4_dequant(const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros,
+                     int64_t n, int64_t k, int32_t group_size, int32_t symmetric,
+                     void* w_out, q4_dtype out_dtype, hipStream_t stream);
+
+/* Path A of the same section (fused load / dequant / matmul, higher-precision
+ * accumulation); W4A16 as in [YJ] §Notation (4-bit weights, 16-bit activations):
+ *   y[m][n] = sum_k x[m][k] * S[n][k/g] * (u[n][k] - z[n][k/g])
+ * x is [m][k] F16 or BF16; y is [m][n] fp32, accumulated in fp32.  m >= 1.
+ * m <= 16 runs the decode GEMV kernel, larger m the prefill GEMM kernel. */
+q4_status q4_w4a16_gemm(const void* x, q4_dtype x_dtype, int64_t m,
+                        const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros,
+                        int64_t n, int64_t k, int32_t group_size, int32_t symmetric,
+                        float* y, hipStream_t stream);
+
+/* Element counts of the three packed arrays (payload + metadata, [FL7] §Memory 계산은
+ * Payload와 Metadata로 나눈다): n*k/8 words, n*(k/g) scales, n*ceil((k/g)/8) words.
+ * Return -1 for arguments the entry points would reject. */
+int64_t q4_qweight_words(int64_t n, int64_t k);
+int64_t q4_scale_count(int64_t n, int64_t k, int32_t group_size);
+int64_t q4_zero_words(int64_t n, int64_t k, int32_t group_size);
+
+/* Static description of a status code. */
+const char* q4_status_str(q4_status s);
+
+/* Name of the kernel the calling thread's last successful entry-point call enqueued
+ * ("" before any), so callers can verify which kernel ran ([FL7] §Silent Fallback). */
+const char* q4_last_kernel(void);
+
+/* Version of the packed layout described above (1). */
+int32_t q4_layout_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

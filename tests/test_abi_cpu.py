@@ -1,0 +1,105 @@
+"""The C ABI on the CPU: the library loads, exports every function include/q4.h
+declares, and rejects bad arguments on the host before any device work (so these
+calls are safe without a GPU).  No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import w4a16_group_wise_q4_amd as q4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4.h")
+
+OK, NULL, SHAPE, GROUP, DTYPE, ALIGN = 0, 1, 2, 3, 4, 5
+A16 = 0x10000          # a 16-byte aligned fake device address (never dereferenced)
+F32, F16, BF16 = 0, 1, 2
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q4_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    lib = q4.lib()
+    names = declared_functions()
+    assert set(names) == set(q4.EXPORTED), names
+    for nm in names:
+        assert hasattr(lib, nm), nm
+
+
+def test_layout_version_and_initial_state():
+    assert q4.q4_layout_version() == 1
+    assert q4.q4_last_kernel() == ""
+
+
+def test_status_strings():
+    lib = q4.lib()
+    for code in range(7):
+        s = lib.q4_status_str(code).decode()
+        assert s and s != "unknown status"
+    assert lib.q4_status_str(99).decode() == "unknown status"
+
+
+def test_size_helpers_match_oracle_and_pages(orc):
+    for (n, k, g) in [(256, 512, 128), (4096, 4096, 128), (11008, 4096, 32), (4096, 11008, 128),
+                      (28672, 8192, 128), (3, 96, 32), (1, 64, 64)]:
+        assert (q4.q4_qweight_words(n, k), q4.q4_scale_count(n, k, g),
+                q4.q4_zero_words(n, k, g)) == orc.sizes(n, k, g)
+    # fp16 scale per 128 weights: 0.015625 bytes per weight
+    assert q4.q4_scale_count(4096, 4096, 128) * 2 / 4096 ** 2 == 0.015625
+    # symmetric group 32: 4.5 bits per weight (32 codes + one fp16 scale)
+    n, k = 64, 4096
+    assert (q4.q4_qweight_words(n, k) * 32 + q4.q4_scale_count(n, k, 32) * 16) / (n * k) == 4.5
+    # rejected layouts report -1
+    assert q4.q4_scale_count(4, 100, 32) == -1
+    assert q4.q4_zero_words(4, 128, 16) == -1
+    assert q4.q4_qweight_words(0, 8) == -1
+
+
+def _qp(w=A16, dt=BF16, n=16, k=256, g=128, sym=0, qw=A16, sc=A16, zr=A16):
+    return q4.lib().q4_quantize_pack(w, dt, n, k, g, sym, qw, sc, zr, None)
+
+
+def _dq(qw=A16, sc=A16, zr=A16, n=16, k=256, g=128, sym=0, out=A16, od=F32):
+    return q4.lib().q4_dequant(qw, sc, zr, n, k, g, sym, out, od, None)
+
+
+def _mm(x=A16, xd=BF16, m=1, qw=A16, sc=A16, zr=A16, n=16, k=256, g=128, sym=0, y=A16):
+    return q4.lib().q4_w4a16_gemm(x, xd, m, qw, sc, zr, n, k, g, sym, y, None)
+
+
+@pytest.mark.parametrize("call,code", [
+    (lambda: _qp(g=16), GROUP), (lambda: _qp(g=256), GROUP), (lambda: _qp(k=96, g=64), SHAPE),
+    (lambda: _qp(n=0), SHAPE), (lambda: _qp(k=0), SHAPE), (lambda: _qp(n=-1), SHAPE),
+    (lambda: _qp(n=1 << 31), SHAPE), (lambda: _qp(n=1 << 30, k=1 << 20), SHAPE),
+    (lambda: _qp(dt=7), DTYPE), (lambda: _qp(w=None), NULL), (lambda: _qp(qw=None), NULL),
+    (lambda: _qp(sc=None), NULL), (lambda: _qp(zr=None), NULL),
+    (lambda: _qp(w=A16 + 8), ALIGN), (lambda: _qp(qw=A16 + 4), ALIGN),
+    (lambda: _qp(sc=A16 + 1), ALIGN), (lambda: _qp(zr=A16 + 2), ALIGN),
+    (lambda: _dq(g=48), GROUP), (lambda: _dq(k=200), SHAPE), (lambda: _dq(od=5), DTYPE),
+    (lambda: _dq(out=None), NULL), (lambda: _dq(zr=None), NULL), (lambda: _dq(out=A16 + 4), ALIGN),
+    (lambda: _mm(m=0), SHAPE), (lambda: _mm(m=-3), SHAPE), (lambda: _mm(xd=F32), DTYPE),
+    (lambda: _mm(x=None), NULL), (lambda: _mm(y=None), NULL), (lambda: _mm(zr=None), NULL),
+    (lambda: _mm(x=A16 + 2), ALIGN), (lambda: _mm(y=A16 + 2), ALIGN), (lambda: _mm(g=100), GROUP),
+    (lambda: _mm(k=320, g=128), SHAPE),
+])
+def test_host_validation_rejects_before_launch(call, code):
+    assert call() == code
+    assert q4.q4_last_kernel() == ""  # nothing was launched
+
+
+def test_symmetric_accepts_null_zeros_in_validation():
+    # symmetric mode needs no zero points; with a bad group the call still fails on the
+    # group (validated first), proving the NULL zeros pointer itself is accepted
+    assert _qp(sym=1, zr=None, g=16) == GROUP
+    assert _mm(sym=1, zr=None, m=0) == SHAPE
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        q4.q4_quantize_pack(torch.zeros(4, 128), 128, False)

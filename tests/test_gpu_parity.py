@@ -1,0 +1,278 @@
+"""HIP path vs the CPU oracle, through the C ABI (needs an MI355X).
+
+Packing (codes, fp16 scales, zero points) must match bit for bit; the W4A16 matmul must
+satisfy |y - y_oracle| <= 1e-3 * (|x| . |x_hat|^T) + 1e-5 elementwise, with y_oracle the
+fp64 product of x and the oracle's dequantized weights.  Every output buffer sits inside
+a sentinel-filled guard region that must come back untouched.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import pins
+import synthetic
+import w4a16_group_wise_q4_amd as q4
+from gpu_util import (DEV, SENTINEL_F32, SENTINEL_I32, assert_linear_close, assert_pack_exact,
+                      guard_intact, guarded, host_input, note, pack_guarded)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_linear(x_cpu, p, guard=True):
+    m = x_cpu.shape[0]
+    yb, yv = guarded((m, p.n), torch.float32, SENTINEL_F32)
+    q4.q4_w4a16_gemm(x_cpu.to(DEV), p, out=yv)
+    kname = q4.q4_last_kernel()
+    torch.cuda.synchronize()
+    assert guard_intact(yb), "store outside y"
+    return yv.cpu().numpy(), kname
+
+
+def check_guards(bufs, sym):
+    qb, sb, zb = bufs
+    assert guard_intact(qb, sentinel=SENTINEL_I32), "store outside qweight"
+    assert guard_intact(sb, sentinel=-1), "store outside scales"
+    if not sym:
+        assert guard_intact(zb, sentinel=SENTINEL_I32), "store outside zeros"
+
+
+# ----------------------------------------------------------------------------- packing
+
+@pytest.mark.parametrize("sym", [False, True])
+def test_quant_tiny_reference(sym):
+    cfg = synthetic.TINY
+    w = cfg["w"].make()
+    note(f"quant tiny fp32 {tuple(w.shape)} g=128 sym={sym}")
+    p, bufs = pack_guarded(w.to(DEV), 128, sym)
+    torch.cuda.synchronize()
+    assert q4.q4_last_kernel() == "q4_quant_pack_f32"
+    check_guards(bufs, sym)
+    assert_pack_exact(p, host_input(w), 128, sym)
+
+
+@pytest.mark.parametrize("idx", [0, 1])
+def test_quant_decode_7b(idx):
+    mat = synthetic.DECODE_7B["mats"][idx]
+    w = mat.make()
+    note(f"quant {mat.name} bf16 g=128 asym")
+    p, bufs = pack_guarded(w.to(DEV), 128, False)
+    torch.cuda.synchronize()
+    check_guards(bufs, False)
+    assert_pack_exact(p, host_input(w), 128, False)
+
+
+@pytest.mark.parametrize("g", [32, 64, 128])
+@pytest.mark.parametrize("sym", [False, True])
+@pytest.mark.parametrize("idx", [0, 1])
+def test_quant_mlp_sweep(idx, g, sym):
+    mat = synthetic.MLP_SWEEP["mats"][idx]
+    w = mat.make()
+    note(f"quant {mat.name} g={g} sym={sym}")
+    p, bufs = pack_guarded(w.to(DEV), g, sym)
+    torch.cuda.synchronize()
+    check_guards(bufs, sym)
+    assert_pack_exact(p, host_input(w), g, sym)
+
+
+def test_quant_prefill_70b_full():
+    mat = synthetic.PREFILL_70B["w"]
+    w = mat.make()
+    note(f"quant {mat.name} bf16 g=128 asym (full tensor)")
+    p, bufs = pack_guarded(w.to(DEV), 128, False)
+    torch.cuda.synchronize()
+    check_guards(bufs, False)
+    assert_pack_exact(p, host_input(w), 128, False)
+
+
+@pytest.mark.parametrize("sym", [False, True])
+def test_quant_checkpoint_sampled_rows(sym):
+    """Two layers of the 32-layer checkpoint, generated on the device; seeded sample of
+    rows (always including the first and last) compared against the oracle."""
+    for mat in synthetic.checkpoint_7b(2):
+        w_dev = mat.make(device="cuda")
+        note(f"quant checkpoint {mat.name} sym={sym}")
+        p, _ = pack_guarded(w_dev, 128, sym)
+        torch.cuda.synchronize()
+        rows = synthetic.sample_rows(mat.n, 48, mat.seed).numpy()
+        w_rows = w_dev[torch.as_tensor(rows, device=DEV)].cpu()
+        assert_pack_exact(p, host_input(w_rows), 128, sym, rows=rows)
+
+
+EDGE_SHAPES = [(1, 32, 32), (3, 96, 32), (5, 64, 64), (7, 192, 64), (17, 384, 128),
+               (33, 11008, 128), (2, 8 * 128 * 3 + 128, 128), (9, 4096 + 32, 32)]
+
+
+@pytest.mark.parametrize("n,k,g", EDGE_SHAPES)
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("sym", [False, True])
+def test_quant_edge_cases(n, k, g, dtype, sym):
+    """Odd shapes (one group, partial zero-point words, single rows) and the stress
+    distribution: all-zero and constant rows, one-sided groups, outliers, scales in the
+    fp16 subnormal range, scales that underflow to 0 or overflow to inf."""
+    base = pins.random_weights(n * 1000 + k, max(n, 12), k)[:n] if n >= 1 else None
+    w = torch.from_numpy(base).to(dtype)
+    if dtype == torch.float16:
+        w = torch.nan_to_num(w, posinf=60000.0, neginf=-60000.0)
+    note(f"quant edge n={n} k={k} g={g} {dtype} sym={sym}")
+    p, bufs = pack_guarded(w.to(DEV), g, sym)
+    torch.cuda.synchronize()
+    check_guards(bufs, sym)
+    assert_pack_exact(p, host_input(w), g, sym)
+
+
+# ----------------------------------------------------------------------------- dequant
+
+@pytest.mark.parametrize("g,sym", [(32, False), (64, True), (128, False), (128, True)])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.float16, torch.bfloat16])
+def test_dequant(g, sym, out_dtype):
+    w = torch.from_numpy(pins.random_weights(77, 40, 1024))
+    note(f"dequant g={g} sym={sym} -> {out_dtype}")
+    p, _ = pack_guarded(w.to(DEV), g, sym)
+    ob, ov = guarded((40, 1024), out_dtype, 0)
+    q4.q4_dequant(p, out=ov)
+    torch.cuda.synchronize()
+    assert q4.q4_last_kernel().startswith("q4_dequant_")
+    assert (ob[:256] == 0).all() and (ob[-256:] == 0).all(), "store outside w_out"
+    qo, so, zo = assert_pack_exact(p, host_input(w), g, sym)
+    ref = oracle.dequant(qo, so, zo, 40, 1024, g, sym)
+    ref32 = torch.from_numpy(ref.astype(np.float32))
+    assert np.array_equal(ref32.numpy().astype(np.float64), ref), "S*(u-z) exact in fp32"
+    got = ov.cpu()
+    want = ref32.to(out_dtype)  # one round-to-nearest-even of the exact value
+    assert torch.equal(got.view(torch.int16) if out_dtype != torch.float32 else got,
+                       want.view(torch.int16) if out_dtype != torch.float32 else want)
+
+
+# ----------------------------------------------------------------------------- matmul
+
+@pytest.mark.parametrize("sym", [False, True])
+@pytest.mark.parametrize("m", [1, 40])
+def test_linear_tiny_reference(sym, m):
+    cfg = synthetic.TINY
+    w = cfg["w"].make()
+    x = synthetic.activations(m, w.shape[1], cfg["x_seed"])
+    note(f"linear tiny m={m} sym={sym}")
+    p, _ = pack_guarded(w.to(DEV), 128, sym)
+    y, kname = run_linear(x, p)
+    assert kname == ("q4_gemv_mfma_bf16" if m <= 16 else "q4_gemm_mfma_bf16")
+    packed = assert_pack_exact(p, host_input(w), 128, sym)
+    assert_linear_close(y, host_input(x), packed, 256, 512, 128, sym, what=kname)
+
+
+@pytest.mark.parametrize("idx", [0, 1])
+def test_gemv_decode_7b_full(idx):
+    cfg = synthetic.DECODE_7B
+    mat = cfg["mats"][idx]
+    w = mat.make()
+    x = synthetic.activations(1, mat.k, cfg["x_seed"])
+    note(f"gemv {mat.name} m=1 g=128 asym")
+    p, _ = pack_guarded(w.to(DEV), 128, False)
+    y, kname = run_linear(x, p)
+    packed = assert_pack_exact(p, host_input(w), 128, False)
+    assert_linear_close(y, host_input(x), packed, mat.n, mat.k, 128, False, what=kname)
+
+
+@pytest.mark.parametrize("g", [32, 64, 128])
+@pytest.mark.parametrize("sym", [False, True])
+@pytest.mark.parametrize("idx", [0, 1])
+def test_gemv_mlp_sweep(idx, g, sym):
+    """All five batch sizes on one packed matrix; columns sampled (every 7th plus the
+    first and last), all rows."""
+    cfg = synthetic.MLP_SWEEP
+    mat = cfg["mats"][idx]
+    w = mat.make()
+    p, _ = pack_guarded(w.to(DEV), g, sym)
+    packed = assert_pack_exact(p, host_input(w), g, sym)
+    x16 = synthetic.activations(16, mat.k, cfg["x_seed"])
+    cols = np.unique(np.concatenate([np.arange(0, mat.n, 7), [mat.n - 1]]))
+    for m in cfg["ms"]:
+        note(f"gemv {mat.name} m={m} g={g} sym={sym}")
+        x = x16[:m].contiguous()
+        y, kname = run_linear(x, p)
+        assert kname == "q4_gemv_mfma_bf16"
+        assert_linear_close(y, host_input(x), packed, mat.n, mat.k, g, sym, cols=cols,
+                            what=f"{kname} m={m}")
+
+
+GEMV_EDGE = [(1, 16, 32, 32), (16, 1, 32, 32), (5, 37, 96, 32), (16, 33, 192, 64),
+             (3, 300, 4096 + 64, 64), (2, 17, 4096 + 32, 32), (11, 129, 1280, 128),
+             (16, 4096, 11008, 128), (8, 1000, 256, 128)]
+
+
+@pytest.mark.parametrize("m,n,k,g", GEMV_EDGE)
+@pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("sym", [False, True])
+def test_gemv_edge_cases(m, n, k, g, xdtype, sym):
+    w = torch.from_numpy(pins.random_weights(n + 3 * k, max(n, 12), k)[:n])
+    x = synthetic.activations(m, k, seed=m * 31 + k).to(xdtype)
+    note(f"gemv edge m={m} n={n} k={k} g={g} {xdtype} sym={sym}")
+    p, _ = pack_guarded(w.to(DEV), g, sym)
+    y, kname = run_linear(x, p)
+    assert kname == ("q4_gemv_mfma_f16" if xdtype == torch.float16 else "q4_gemv_mfma_bf16")
+    packed = assert_pack_exact(p, host_input(w), g, sym)
+    assert_linear_close(y, host_input(x), packed, n, k, g, sym, what=kname)
+
+
+@pytest.mark.parametrize("m", [1, 5, 16, 17, 64])
+@pytest.mark.parametrize("sym", [False, True])
+def test_linear_special_inputs(m, sym):
+    """x = 0 gives exactly 0; one-hot x picks one dequantized column exactly."""
+    n, k, g = 48, 512, 64
+    w = torch.from_numpy(pins.random_weights(5, n, k))
+    p, _ = pack_guarded(w.to(DEV), g, sym)
+    qo, so, zo = assert_pack_exact(p, host_input(w), g, sym)
+    xhat = oracle.dequant(qo, so, zo, n, k, g, sym)
+    note(f"linear zero x m={m} sym={sym}")
+    y, _ = run_linear(torch.zeros(m, k, dtype=torch.bfloat16), p)
+    assert np.all(y == 0)
+    x = torch.zeros(m, k, dtype=torch.bfloat16)
+    cols = [(7 * i + 3) % k for i in range(m)]
+    for i, kk in enumerate(cols):
+        x[i, kk] = 1.0
+    note(f"linear one-hot x m={m} sym={sym}")
+    y, _ = run_linear(x, p)
+    for i, kk in enumerate(cols):
+        assert np.array_equal(y[i].astype(np.float64), xhat[:, kk]), (i, kk)
+
+
+GEMM_CASES = [(17, 64, 256, 128), (130, 200, 384, 64), (300, 129, 96, 32), (256, 256, 1024, 128),
+              (129, 1000, 4096 + 64, 64), (64, 48, 11008, 128)]
+
+
+@pytest.mark.parametrize("m,n,k,g", GEMM_CASES)
+@pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("sym", [False, True])
+def test_gemm_cases(m, n, k, g, xdtype, sym):
+    w = torch.from_numpy(pins.random_weights(m + n + k, max(n, 12), k)[:n])
+    x = synthetic.activations(m, k, seed=m + 7 * k).to(xdtype)
+    note(f"gemm m={m} n={n} k={k} g={g} {xdtype} sym={sym}")
+    p, _ = pack_guarded(w.to(DEV), g, sym)
+    y, kname = run_linear(x, p)
+    assert kname == ("q4_gemm_mfma_f16" if xdtype == torch.float16 else "q4_gemm_mfma_bf16")
+    packed = assert_pack_exact(p, host_input(w), g, sym)
+    assert_linear_close(y, host_input(x), packed, n, k, g, sym, what=kname)
+
+
+def test_gemm_prefill_70b_sampled():
+    """The 70B-like prefill at full size, in the configuration the benchmark times;
+    checked on a seeded sample of 40 activation rows x 320 weight rows (with edges)."""
+    cfg = synthetic.PREFILL_70B
+    mat = cfg["w"]
+    w = mat.make()
+    x = synthetic.activations(cfg["m"], mat.k, cfg["x_seed"], outlier_seed=mat.seed,
+                              outlier_factor=cfg["x_outlier_factor"])
+    note(f"gemm prefill {mat.name} m={cfg['m']}")
+    p, _ = pack_guarded(w.to(DEV), 128, False)
+    y, kname = run_linear(x, p)
+    assert kname == "q4_gemm_mfma_bf16"
+    assert np.isfinite(y).all()
+    rows_w = synthetic.sample_rows(mat.n, 320, 11).numpy()
+    rows_x = synthetic.sample_rows(cfg["m"], 40, 12).numpy()
+    w_rows = w[torch.as_tensor(rows_w)]
+    qo, so, zo = assert_pack_exact(p, host_input(w_rows), 128, False, rows=rows_w)
+    yr, ya = oracle.linear(host_input(x), qo, so, zo, len(rows_w), mat.k, 128, False,
+                           rows=rows_x)
+    yg = y[np.ix_(rows_x, rows_w)]
+    ok = oracle.within_tolerance(yg, yr, ya)
+    assert ok.all(), f"{int((~ok).sum())} sampled outputs outside the bound"

@@ -1,0 +1,186 @@
+"""Python binding of libq4, the MI355X (gfx950) group-wise INT4 weight-only library.
+
+Argument marshalling only: every step runs in the HIP kernels behind the C ABI
+(include/q4.h).  torch supplies device memory and the current stream.  There is no
+CPU path: if the shared library is missing and cannot be built, importing the binding
+raises.
+
+Entry points (same names as the C ABI):
+    q4_quantize_pack(w, group_size, symmetric)          -> PackedWeight
+    q4_dequant(packed, out_dtype)                       -> W_hat [n, k]
+    q4_w4a16_gemm(x, packed)                            -> y [m, n] fp32
+    q4_last_kernel()                                    -> name of the last kernel run
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _build
+
+__all__ = ["PackedWeight", "q4_quantize_pack", "q4_dequant", "q4_w4a16_gemm", "q4_last_kernel",
+           "q4_qweight_words", "q4_scale_count", "q4_zero_words", "q4_layout_version",
+           "library_path", "Q4Error"]
+
+Q4_F32, Q4_F16, Q4_BF16 = 0, 1, 2
+_DTYPE_CODE = {torch.float32: Q4_F32, torch.float16: Q4_F16, torch.bfloat16: Q4_BF16}
+
+EXPORTED = ("q4_quantize_pack", "q4_dequant", "q4_w4a16_gemm", "q4_qweight_words",
+            "q4_scale_count", "q4_zero_words", "q4_status_str", "q4_last_kernel",
+            "q4_layout_version")
+
+
+class Q4Error(RuntimeError):
+    """A non-OK q4_status returned by the library."""
+
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"q4 status {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _build.LIBRARY
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_build.LIBRARY):
+        _build.build()  # raises if hipcc fails: there is no fallback
+    lib = ctypes.CDLL(_build.LIBRARY)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.q4_quantize_pack.argtypes = [vp, ctypes.c_int, i64, i64, i32, i32, vp, vp, vp, vp]
+    lib.q4_quantize_pack.restype = ctypes.c_int
+    lib.q4_dequant.argtypes = [vp, vp, vp, i64, i64, i32, i32, vp, ctypes.c_int, vp]
+    lib.q4_dequant.restype = ctypes.c_int
+    lib.q4_w4a16_gemm.argtypes = [vp, ctypes.c_int, i64, vp, vp, vp, i64, i64, i32, i32, vp, vp]
+    lib.q4_w4a16_gemm.restype = ctypes.c_int
+    lib.q4_qweight_words.argtypes = [i64, i64]
+    lib.q4_qweight_words.restype = i64
+    lib.q4_scale_count.argtypes = [i64, i64, i32]
+    lib.q4_scale_count.restype = i64
+    lib.q4_zero_words.argtypes = [i64, i64, i32]
+    lib.q4_zero_words.restype = i64
+    lib.q4_status_str.argtypes = [ctypes.c_int]
+    lib.q4_status_str.restype = ctypes.c_char_p
+    lib.q4_last_kernel.argtypes = []
+    lib.q4_last_kernel.restype = ctypes.c_char_p
+    lib.q4_layout_version.argtypes = []
+    lib.q4_layout_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def lib():
+    """The loaded ctypes library (raw C ABI)."""
+    return _load()
+
+
+def _check(code: int):
+    if code != 0:
+        raise Q4Error(code, _load().q4_status_str(code).decode())
+
+
+def _stream(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev_ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need_cuda(name: str, t: torch.Tensor):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor (the library has no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+@dataclass
+class PackedWeight:
+    """Canonical packed INT4 weight: qweight int32 [n, k/8] (uint32 bit patterns),
+    scales float16 [n, k/g], zeros int32 [n, ceil(k/g/8)] or None when symmetric."""
+    qweight: torch.Tensor
+    scales: torch.Tensor
+    zeros: Optional[torch.Tensor]
+    n: int
+    k: int
+    group_size: int
+    symmetric: bool
+
+
+def q4_qweight_words(n: int, k: int) -> int:
+    return int(_load().q4_qweight_words(n, k))
+
+
+def q4_scale_count(n: int, k: int, group_size: int) -> int:
+    return int(_load().q4_scale_count(n, k, group_size))
+
+
+def q4_zero_words(n: int, k: int, group_size: int) -> int:
+    return int(_load().q4_zero_words(n, k, group_size))
+
+
+def q4_layout_version() -> int:
+    return int(_load().q4_layout_version())
+
+
+def q4_last_kernel() -> str:
+    return _load().q4_last_kernel().decode()
+
+
+def empty_packed(n: int, k: int, group_size: int, symmetric: bool, device) -> PackedWeight:
+    G = k // group_size
+    return PackedWeight(
+        qweight=torch.empty((n, k // 8), dtype=torch.int32, device=device),
+        scales=torch.empty((n, G), dtype=torch.float16, device=device),
+        zeros=None if symmetric else torch.empty((n, (G + 7) // 8), dtype=torch.int32, device=device),
+        n=n, k=k, group_size=group_size, symmetric=bool(symmetric))
+
+
+def q4_quantize_pack(w: torch.Tensor, group_size: int = 128, symmetric: bool = False,
+                     out: Optional[PackedWeight] = None) -> PackedWeight:
+    """RTN quantize-and-pack W [n, k] (fp32 / fp16 / bf16, on the GPU)."""
+    _need_cuda("w", w)
+    if w.dim() != 2 or w.dtype not in _DTYPE_CODE:
+        raise ValueError("w must be a 2-D fp32, fp16 or bf16 tensor")
+    n, k = w.shape
+    p = out if out is not None else empty_packed(n, k, group_size, symmetric, w.device)
+    _check(_load().q4_quantize_pack(_dev_ptr(w), _DTYPE_CODE[w.dtype], n, k, group_size,
+                                    int(bool(symmetric)), _dev_ptr(p.qweight),
+                                    _dev_ptr(p.scales), _dev_ptr(p.zeros), _stream(w)))
+    return p
+
+
+def q4_dequant(p: PackedWeight, out_dtype: torch.dtype = torch.float32,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Full dequantization S * (u - z) -> [n, k] in out_dtype (fp32 exact)."""
+    _need_cuda("qweight", p.qweight)
+    o = out if out is not None else torch.empty((p.n, p.k), dtype=out_dtype,
+                                                device=p.qweight.device)
+    _check(_load().q4_dequant(_dev_ptr(p.qweight), _dev_ptr(p.scales), _dev_ptr(p.zeros),
+                              p.n, p.k, p.group_size, int(p.symmetric), _dev_ptr(o),
+                              _DTYPE_CODE[o.dtype], _stream(o)))
+    return o
+
+
+def q4_w4a16_gemm(x: torch.Tensor, p: PackedWeight,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = x · (S (u - z))^T, x [m, k] fp16/bf16, y [m, n] fp32."""
+    _need_cuda("x", x)
+    if x.dim() != 2 or x.dtype not in (torch.float16, torch.bfloat16) or x.shape[1] != p.k:
+        raise ValueError("x must be [m, k] fp16 or bf16 with k matching the packed weight")
+    m = x.shape[0]
+    y = out if out is not None else torch.empty((m, p.n), dtype=torch.float32, device=x.device)
+    _check(_load().q4_w4a16_gemm(_dev_ptr(x), _DTYPE_CODE[x.dtype], m, _dev_ptr(p.qweight),
+                                 _dev_ptr(p.scales), _dev_ptr(p.zeros), p.n, p.k,
+                                 p.group_size, int(p.symmetric), _dev_ptr(y), _stream(x)))
+    return y

@@ -1,0 +1,134 @@
+// q4_abi.cpp — the C ABI of libq4 (declared in include/q4.h).
+//
+// Validates every argument on the host before anything is enqueued, picks the kernel
+// (decode GEMV for m <= 16, prefill GEMM otherwise), launches it on the caller's stream
+// and records the launched kernel's name per thread, so a caller can check which kernel
+// ran ("LLM Quantization: GPTQ·AWQ·SmoothQuant·FP8·KV Cache (7/10)", §Silent Fallback:
+// verify the selected kernel and that nothing fell back).  There is no fallback path.
+#include "q4.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "q4_device.h"
+
+namespace {
+
+thread_local const char* g_last_kernel = "";
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+
+bool group_ok(int32_t g) { return g == 32 || g == 64 || g == 128; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+q4_status check_layout(int64_t n, int64_t k, int32_t g) {
+    if (!group_ok(g)) return Q4_ERR_GROUP;
+    if (n < 1 || k < 1 || n > kMaxDim || k > kMaxDim) return Q4_ERR_SHAPE;
+    if (k % g != 0) return Q4_ERR_SHAPE;
+    if (n > kMaxElems / k) return Q4_ERR_SHAPE;
+    return Q4_OK;
+}
+
+q4_status check_packed(const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros,
+                       int32_t symmetric) {
+    if (!qweight || !scales || (!symmetric && !zeros)) return Q4_ERR_NULL;
+    if (!aligned(qweight, 16) || !aligned(scales, 2) || (!symmetric && !aligned(zeros, 4)))
+        return Q4_ERR_ALIGN;
+    return Q4_OK;
+}
+
+q4_status finish(hipError_t e, const char* name) {
+    if (e != hipSuccess) return Q4_ERR_LAUNCH;
+    g_last_kernel = name;
+    return Q4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+q4_status q4_quantize_pack(const void* w, q4_dtype w_dtype, int64_t n, int64_t k,
+                           int32_t group_size, int32_t symmetric, uint32_t* qweight,
+                           uint16_t* scales, uint32_t* zeros, hipStream_t stream) {
+    q4_status st = check_layout(n, k, group_size);
+    if (st != Q4_OK) return st;
+    if (w_dtype != Q4_F32 && w_dtype != Q4_F16 && w_dtype != Q4_BF16) return Q4_ERR_DTYPE;
+    if (!w) return Q4_ERR_NULL;
+    if ((st = check_packed(qweight, scales, zeros, symmetric)) != Q4_OK) return st;
+    if (!aligned(w, 16)) return Q4_ERR_ALIGN;
+    const char* name = "";
+    hipError_t e = q4k_quant_pack(w, (int)w_dtype, n, k, group_size, symmetric ? 1 : 0, qweight,
+                                  scales, zeros, stream, &name);
+    return finish(e, name);
+}
+
+q4_status q4_dequant(const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros,
+                     int64_t n, int64_t k, int32_t group_size, int32_t symmetric, void* w_out,
+                     q4_dtype out_dtype, hipStream_t stream) {
+    q4_status st = check_layout(n, k, group_size);
+    if (st != Q4_OK) return st;
+    if (out_dtype != Q4_F32 && out_dtype != Q4_F16 && out_dtype != Q4_BF16) return Q4_ERR_DTYPE;
+    if ((st = check_packed(qweight, scales, zeros, symmetric)) != Q4_OK) return st;
+    if (!w_out) return Q4_ERR_NULL;
+    if (!aligned(w_out, 16)) return Q4_ERR_ALIGN;
+    const char* name = "";
+    hipError_t e = q4k_dequant(qweight, scales, zeros, n, k, group_size, symmetric ? 1 : 0, w_out,
+                               (int)out_dtype, stream, &name);
+    return finish(e, name);
+}
+
+q4_status q4_w4a16_gemm(const void* x, q4_dtype x_dtype, int64_t m, const uint32_t* qweight,
+                        const uint16_t* scales, const uint32_t* zeros, int64_t n, int64_t k,
+                        int32_t group_size, int32_t symmetric, float* y, hipStream_t stream) {
+    q4_status st = check_layout(n, k, group_size);
+    if (st != Q4_OK) return st;
+    if (m < 1 || m > kMaxDim || m > kMaxElems / k || m > kMaxElems / n) return Q4_ERR_SHAPE;
+    if (x_dtype != Q4_F16 && x_dtype != Q4_BF16) return Q4_ERR_DTYPE;
+    if (!x || !y) return Q4_ERR_NULL;
+    if ((st = check_packed(qweight, scales, zeros, symmetric)) != Q4_OK) return st;
+    if (!aligned(x, 16) || !aligned(y, 4)) return Q4_ERR_ALIGN;
+    const char* name = "";
+    hipError_t e;
+    if (m <= 16)
+        e = q4k_gemv(x, (int)x_dtype, (int)m, qweight, scales, zeros, n, k, group_size,
+                     symmetric ? 1 : 0, y, stream, &name);
+    else
+        e = q4k_gemm(x, (int)x_dtype, m, qweight, scales, zeros, n, k, group_size,
+                     symmetric ? 1 : 0, y, stream, &name);
+    return finish(e, name);
+}
+
+int64_t q4_qweight_words(int64_t n, int64_t k) {
+    if (n < 1 || k < 1 || k % 8 != 0) return -1;
+    return n * (k / 8);
+}
+
+int64_t q4_scale_count(int64_t n, int64_t k, int32_t group_size) {
+    if (check_layout(n, k, group_size) != Q4_OK) return -1;
+    return n * (k / group_size);
+}
+
+int64_t q4_zero_words(int64_t n, int64_t k, int32_t group_size) {
+    if (check_layout(n, k, group_size) != Q4_OK) return -1;
+    return n * ((k / group_size + 7) / 8);
+}
+
+const char* q4_status_str(q4_status s) {
+    switch (s) {
+    case Q4_OK: return "ok";
+    case Q4_ERR_NULL: return "a required pointer is NULL";
+    case Q4_ERR_SHAPE: return "shape out of range (n, k, m >= 1; k a multiple of group_size)";
+    case Q4_ERR_GROUP: return "group_size must be 32, 64 or 128";
+    case Q4_ERR_DTYPE: return "dtype not accepted by this entry point";
+    case Q4_ERR_ALIGN: return "pointer misaligned (w/x/qweight/w_out 16 B, zeros/y 4 B, scales 2 B)";
+    case Q4_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+const char* q4_last_kernel(void) { return g_last_kernel; }
+
+int32_t q4_layout_version(void) { return 1; }
+
+}  // extern "C"

@@ -1,0 +1,97 @@
+// q4_device.h — device-side helpers shared by the gfx950 kernels of libq4.
+//
+// Operand types for the CDNA4 16x16x32 MFMA, the exponent-bias nibble decoders and the
+// host-side launcher declarations.  Everything here is specific to gfx950 (wave64,
+// v_mfma_f32_16x16x32_{bf16,f16}).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- MFMA wrappers
+// D(16x16, fp32) += A(16x32) * B(32x16).  Lane l supplies row l%16 of A and column l%16
+// of B for k-slot block l/16 (8 values each, same slot order in A and B), and receives
+// D[4*(l/16) + i][l%16] in element i of the result.
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- nibble decoders
+// A packed word holds the codes of 8 consecutive columns, column i in bits 4i..4i+3.
+// Decoded pairs come out as (column i, column i+4) in one 32-bit register, i = 0..3, so
+// operand element 2i is column i and element 2i+1 is column i+4.  The activation operand
+// is permuted the same way (pair_perm below).
+
+// bf16 exponent bias: 0x4300 is 128.0 with a zero 7-bit mantissa, so OR-ing a nibble into
+// the low mantissa bits gives exactly 128 + u.
+__device__ __forceinline__ u32x4 decode_bf16_biased(uint32_t w) {
+    u32x4 r;
+    r[0] = (w & 0x000F000Fu) | 0x43004300u;
+    r[1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
+    r[2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
+    r[3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+    return r;
+}
+
+// fp16 exponent bias: 0x6400 is 1024.0 with a zero 10-bit mantissa -> 1024 + u; then a
+// packed fp16 subtraction of (1024 + z) leaves the exact small integer u - z.
+__device__ __forceinline__ u32x4 decode_f16_exact(uint32_t w, f16x2 bias) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t t = ((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
+        f16x2 v = __builtin_bit_cast(f16x2, t) - bias;
+        r[i] = __builtin_bit_cast(uint32_t, v);
+    }
+    return r;
+}
+
+// Activation operand in the decoder's slot order: from 8 consecutive 16-bit values
+// x0..x7 (four words, natural order) build pairs (x_i, x_{i+4}).
+__device__ __forceinline__ u32x4 pair_perm(u32x4 x) {
+    u32x4 r;
+    // v_perm_b32 selector: bytes of {src0 (4..7), src1 (0..3)}; pick low/high halves.
+    r[0] = __builtin_amdgcn_perm(x[2], x[0], 0x05040100u);  // (x0, x4)
+    r[1] = __builtin_amdgcn_perm(x[2], x[0], 0x07060302u);  // (x1, x5)
+    r[2] = __builtin_amdgcn_perm(x[3], x[1], 0x05040100u);  // (x2, x6)
+    r[3] = __builtin_amdgcn_perm(x[3], x[1], 0x07060302u);  // (x3, x7)
+    return r;
+}
+
+__device__ __forceinline__ float f16_bits_to_float(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
+}  // namespace q4
+
+// ---------------------------------------------------------------- launchers
+// Implemented in the .hip files, called by the C ABI after validation.  Each returns the
+// hipError_t of its launch and writes the launched kernel's name.
+hipError_t q4k_quant_pack(const void* w, int w_dtype, int64_t n, int64_t k, int g, int sym,
+                          uint32_t* qweight, uint16_t* scales, uint32_t* zeros,
+                          hipStream_t stream, const char** kname);
+hipError_t q4k_dequant(const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros,
+                       int64_t n, int64_t k, int g, int sym, void* out, int out_dtype,
+                       hipStream_t stream, const char** kname);
+hipError_t q4k_gemv(const void* x, int x_dtype, int m, const uint32_t* qweight,
+                    const uint16_t* scales, const uint32_t* zeros, int64_t n, int64_t k, int g,
+                    int sym, float* y, hipStream_t stream, const char** kname);
+hipError_t q4k_gemm(const void* x, int x_dtype, int64_t m, const uint32_t* qweight,
+                    const uint16_t* scales, const uint32_t* zeros, int64_t n, int64_t k, int g,
+                    int sym, float* y, hipStream_t stream, const char** kname);

@@ -1,0 +1,195 @@
+// quant_pack.hip — RTN quantize-and-pack of W [n][k] into the canonical packed format
+// for gfx950.
+//
+// Method: the affine quantizer q = clamp(round(w/s) + z, q_min, q_max) of
+// "LLM Quantization: GPTQ·AWQ·SmoothQuant·FP8·KV Cache (7/10)" (blog.ruahverce.com),
+// §Affine Quantization, with per-group statistics (§Per-group: g consecutive weights
+// share one scale) and the symmetric / asymmetric scale and zero point of
+// §Symmetric과 Asymmetric; INT4 code ranges [-8,7] / [0,15] from
+// "Quantization Algorithms 단권화" §Signed ↔ Unsigned; round-to-nearest as the
+// calibration-free RTN baseline of the same page (§Calibration-free).
+//
+// Work mapping (HBM-bound: 2 or 4 bytes read and 0.5 byte written per weight):
+//   one wave = one row x 8 consecutive groups = exactly one 32-bit zero-point word;
+//   lane l handles E = g/8 consecutive weights of group l/8; the 8 lanes of a group
+//   reduce min/max (or max|w|) with three xor shuffles; each lane then packs its E
+//   codes (E/8 words, or half a word when g = 32) and the wave writes a contiguous
+//   run of 4*g bytes of qweight.  The 8 zero points are OR-combined across the wave.
+//
+// Arithmetic is IEEE fp32 in the order written (no contraction, correctly rounded
+// division, round-half-to-even via rintf), so codes, scales and zero points are
+// bit-identical to the plain CPU definition.
+#include "q4_device.h"
+
+#pragma clang fp contract(off)
+
+namespace {
+
+template <int E, int DT>
+__device__ __forceinline__ void load_group_slice(const void* base, int64_t elem_off, float (&v)[E]) {
+    if constexpr (DT == 0) {
+        const float* p = reinterpret_cast<const float*>(base) + elem_off;
+        if constexpr (E % 4 == 0) {
+#pragma unroll
+            for (int i = 0; i < E / 4; ++i) {
+                float4 t = reinterpret_cast<const float4*>(p)[i];
+                v[4 * i + 0] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+            }
+        }
+    } else {
+        const uint16_t* p = reinterpret_cast<const uint16_t*>(base) + elem_off;
+        uint32_t words[E / 2];
+        if constexpr (E >= 8) {
+#pragma unroll
+            for (int i = 0; i < E / 8; ++i) {
+                q4::u32x4 t = reinterpret_cast<const q4::u32x4*>(p)[i];
+                words[4 * i + 0] = t[0]; words[4 * i + 1] = t[1];
+                words[4 * i + 2] = t[2]; words[4 * i + 3] = t[3];
+            }
+        } else {
+            q4::u32x2 t = *reinterpret_cast<const q4::u32x2*>(p);
+            words[0] = t[0]; words[1] = t[1];
+        }
+#pragma unroll
+        for (int i = 0; i < E / 2; ++i) {
+            uint16_t lo = (uint16_t)(words[i] & 0xFFFFu), hi = (uint16_t)(words[i] >> 16);
+            if constexpr (DT == 2) {  // bf16: the upper half of an fp32
+                v[2 * i] = __builtin_bit_cast(float, (uint32_t)lo << 16);
+                v[2 * i + 1] = __builtin_bit_cast(float, (uint32_t)hi << 16);
+            } else {                  // fp16
+                v[2 * i] = (float)__builtin_bit_cast(_Float16, lo);
+                v[2 * i + 1] = (float)__builtin_bit_cast(_Float16, hi);
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ float xor_max(float v, int m) { return fmaxf(v, __shfl_xor(v, m, 64)); }
+__device__ __forceinline__ float xor_min(float v, int m) { return fminf(v, __shfl_xor(v, m, 64)); }
+
+template <int G, bool SYM, int DT>
+__global__ __launch_bounds__(256) void quant_pack_kernel(const void* __restrict__ w, int64_t k,
+                                                         uint32_t* __restrict__ qweight,
+                                                         uint16_t* __restrict__ scales,
+                                                         uint32_t* __restrict__ zeros,
+                                                         int64_t tasks) {
+    constexpr int E = G / 8;  // weights per lane
+    const int lane = threadIdx.x & 63;
+    const int64_t task = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (task >= tasks) return;  // wave-uniform
+    const int64_t n_groups = k / G;
+    const int64_t zwords = (n_groups + 7) >> 3;
+    const int64_t row = task / zwords;
+    const int64_t zw = task - row * zwords;
+    const int grp = lane >> 3;
+    const int t = lane & 7;
+    const int64_t gidx = zw * 8 + grp;
+    const bool valid = gidx < n_groups;
+    const int64_t elem_off = row * k + gidx * G + (int64_t)t * E;
+
+    float v[E];
+    if (valid) {
+        load_group_slice<E, DT>(w, elem_off, v);
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[e] = 0.0f;
+    }
+
+    // group statistics: zero-extended [min, max] (asymmetric) or max |w| (symmetric)
+    float s;
+    float x_min = 0.0f, x_max = 0.0f;
+    if constexpr (SYM) {
+        float amax = 0.0f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(v[e]));
+        amax = xor_max(amax, 1);
+        amax = xor_max(amax, 2);
+        amax = xor_max(amax, 4);
+        s = amax / 7.0f;
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            x_min = fminf(x_min, v[e]);
+            x_max = fmaxf(x_max, v[e]);
+        }
+        x_min = xor_min(x_min, 1); x_max = xor_max(x_max, 1);
+        x_min = xor_min(x_min, 2); x_max = xor_max(x_max, 2);
+        x_min = xor_min(x_min, 4); x_max = xor_max(x_max, 4);
+        s = (x_max - x_min) / 15.0f;
+    }
+    // stored fp16 scale (round-to-nearest-even), degenerate values replaced
+    uint16_t s16 = __builtin_bit_cast(uint16_t, (_Float16)s);
+    if ((s16 & 0x7FFFu) == 0) s16 = 0x3C00u;
+    if (s16 == 0x7C00u) s16 = 0x7BFFu;
+    const float S = (float)__builtin_bit_cast(_Float16, s16);
+
+    float zf = 0.0f;
+    if constexpr (!SYM) zf = fminf(fmaxf(rintf(-x_min / S), 0.0f), 15.0f);
+    constexpr float q_min = SYM ? -8.0f : 0.0f;
+    constexpr float q_max = SYM ? 7.0f : 15.0f;
+
+    uint32_t packed[(E + 7) / 8];
+#pragma unroll
+    for (int j = 0; j < (E + 7) / 8; ++j) packed[j] = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const float qf = fminf(fmaxf(rintf(v[e] / S) + zf, q_min), q_max);
+        const uint32_t u = (uint32_t)((int)qf + (SYM ? 8 : 0));
+        packed[e / 8] |= u << (4 * (e % 8));
+    }
+
+    if (valid) {
+        const int64_t nib = elem_off;  // code index == element index
+        if constexpr (E == 16) {
+            q4::u32x2 o;
+            o[0] = packed[0];
+            o[1] = packed[1];
+            *reinterpret_cast<q4::u32x2*>(qweight + nib / 8) = o;
+        } else if constexpr (E == 8) {
+            qweight[nib / 8] = packed[0];
+        } else {  // E == 4: half a word
+            reinterpret_cast<uint16_t*>(qweight)[nib / 4] = (uint16_t)packed[0];
+        }
+        if (t == 0) scales[row * n_groups + gidx] = s16;
+    }
+    if constexpr (!SYM) {
+        uint32_t zn = valid ? ((uint32_t)(int)zf << (4 * grp)) : 0u;
+        zn |= __shfl_xor(zn, 8, 64);
+        zn |= __shfl_xor(zn, 16, 64);
+        zn |= __shfl_xor(zn, 32, 64);
+        if (lane == 0) zeros[row * zwords + zw] = zn;
+    }
+}
+
+template <int G, bool SYM>
+hipError_t launch_dt(const void* w, int dt, int64_t n, int64_t k, uint32_t* qw, uint16_t* sc,
+                     uint32_t* zr, hipStream_t st, const char** kname) {
+    const int64_t zwords = (k / G + 7) / 8;
+    const int64_t tasks = n * zwords;
+    const int waves = 4;
+    const dim3 grid((unsigned)((tasks + waves - 1) / waves)), block(64 * waves);
+    static const char* names[3] = {"q4_quant_pack_f32", "q4_quant_pack_f16", "q4_quant_pack_bf16"};
+    *kname = names[dt];
+    if (dt == 0)
+        hipLaunchKernelGGL((quant_pack_kernel<G, SYM, 0>), grid, block, 0, st, w, k, qw, sc, zr, tasks);
+    else if (dt == 1)
+        hipLaunchKernelGGL((quant_pack_kernel<G, SYM, 1>), grid, block, 0, st, w, k, qw, sc, zr, tasks);
+    else
+        hipLaunchKernelGGL((quant_pack_kernel<G, SYM, 2>), grid, block, 0, st, w, k, qw, sc, zr, tasks);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t q4k_quant_pack(const void* w, int w_dtype, int64_t n, int64_t k, int g, int sym,
+                          uint32_t* qweight, uint16_t* scales, uint32_t* zeros,
+                          hipStream_t stream, const char** kname) {
+    switch (g * 2 + (sym ? 1 : 0)) {
+    case 64: return launch_dt<32, false>(w, w_dtype, n, k, qweight, scales, zeros, stream, kname);
+    case 65: return launch_dt<32, true>(w, w_dtype, n, k, qweight, scales, zeros, stream, kname);
+    case 128: return launch_dt<64, false>(w, w_dtype, n, k, qweight, scales, zeros, stream, kname);
+    case 129: return launch_dt<64, true>(w, w_dtype, n, k, qweight, scales, zeros, stream, kname);
+    case 256: return launch_dt<128, false>(w, w_dtype, n, k, qweight, scales, zeros, stream, kname);
+    default: return launch_dt<128, true>(w, w_dtype, n, k, qweight, scales, zeros, stream, kname);
+    }
+}
