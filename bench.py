@@ -1,0 +1,293 @@
+"""Benchmark of the W4A16 group-wise INT4 hot path on one MI355X.
+
+Metric: W4A16 GEMV achieved HBM GB/s at M=1 (7B-like decode projections 4096x4096 and
+11008x4096, group 128, asymmetric), with the GEMM TFLOP/s of the 70B-like prefill and the
+quantize/pack GB/s of the 32-layer 7B-like checkpoint reported alongside.
+
+A timed step is one decode pass: the W4A16 GEMV over both projections at M=1.  Each step
+reads a different copy of the packed weights (the copies together exceed twice the
+256 MB Infinity Cache), so every step streams its weights from HBM.  Inputs are
+resident in HBM before the timed region starts.
+
+Algorithmic bytes (what the method must move, nothing else):
+  GEMV   per launch: n*k/2 (codes) + 2*n*k/g (fp16 scales) + 4*n*ceil(k/g/8) (zeros)
+                     + 2*m*k (x, bf16) + 4*m*n (y, fp32)
+  GEMM   2*m*n*k flop against the bf16 dense MFMA peak
+  quantize per weight: 2 (bf16 read) + 0.5 (codes); per group 2 (scale) + 0.5 (zero)
+
+Prints one JSON line.  ``--gpus`` above 1 is refused: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+MALL_BYTES = 256 * 2 ** 20
+METRIC = "W4A16 GEMV achieved HBM GB/s (% peak) at M=1; GEMM TFLOP/s (% MFMA peak)"
+
+
+def gemv_bytes(m, n, k, g, sym):
+    zeros = 0 if sym else 4 * n * ((k // g + 7) // 8)
+    return n * k // 2 + 2 * n * (k // g) + zeros + 2 * m * k + 4 * m * n
+
+
+def quant_bytes(n, k, g, sym, in_bytes=2):
+    zeros = 0 if sym else 4 * n * ((k // g + 7) // 8)
+    return n * k * in_bytes + n * k // 2 + 2 * n * (k // g) + zeros
+
+
+def source_digest(*names):
+    h = hashlib.sha256()
+    for nm in names:
+        with open(os.path.join(ROOT, "w4a16_group_wise_q4_amd", "csrc", nm), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(summary_name, digest):
+    """Measured HBM bytes per launch from a committed rocprofv3 PMC summary, if it was
+    taken on the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", summary_name)
+    if not os.path.exists(path):
+        return None
+    text = open(path, encoding="utf-8").read()
+    src = re.search(r"source_digest:\s*([0-9a-f]+)", text)
+    val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not src or not val or src.group(1) != digest:
+        return None
+    return float(val.group(1))
+
+
+def event_ms(fn, reps):
+    """Mean duration in ms of one launch of ``fn``: HIP events on the launch stream around
+    ``reps`` back-to-back launches (fn(r) picks the r-th input copy)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for r in range(reps):
+        fn(r)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / reps
+
+
+def timed_sweep(fn_list, reps):
+    """Wall seconds of ``reps`` passes over fn_list, events around the whole region."""
+    import torch
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for r in range(reps):
+        for fn in fn_list:
+            fn(r)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / 1e3
+
+
+def cpu_baseline(seconds=12.0):
+    """The CPU oracle (plain scalar C, one thread) on a bounded sample of the decode
+    workload: full fp64 passes over both projections at M=1."""
+    import numpy as np
+
+    import oracle
+    import synthetic
+    cfg = synthetic.DECODE_7B
+    packs, total = [], 0
+    x = synthetic.activations(1, 4096, cfg["x_seed"])
+    xb = (synthetic.as_u16(x), oracle.BF16)
+    for mat in cfg["mats"]:
+        w = mat.make()
+        q, s, z = oracle.quantize_pack((synthetic.as_u16(w), oracle.BF16), 128, False)
+        packs.append((q, s, z, mat.n, mat.k))
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        for q, s, z, n, k in packs:
+            oracle.linear(xb, q, s, z, n, k, 128, False)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    per_pass = sum(gemv_bytes(1, n, k, 128, False) for _, _, _, n, k in packs)
+    return {"value": round(per_pass * passes / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{passes} single-thread fp64 oracle passes of y = x.W_hat^T over the "
+                      f"4096x4096 and 11008x4096 g128 asym projections at M=1 ({el:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--legs", default="gemv,gemm,quant,sweep",
+                    help="comma list of legs besides the headline decode GEMV")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 512 MiB device-to-device copy 5 times (the "
+                         "reference kernel for scaling HBM byte counters) and exit")
+    args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        nbytes = 512 * 2 ** 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "launches": 5}))
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synthetic
+    import w4a16_group_wise_q4_amd as q4
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    legs = set(args.legs.split(","))
+    out = {}
+
+    # ------------------------------------------------------------ decode GEMV (the metric)
+    cfg = synthetic.DECODE_7B
+    base = []
+    for mat in cfg["mats"]:
+        base.append(q4.q4_quantize_pack(mat.make().to(dev), 128, False))
+    step_bytes = sum(gemv_bytes(1, p.n, p.k, 128, False) for p in base)
+    copies = max(2, -(-4 * MALL_BYTES // step_bytes))  # >= 2x MALL of distinct weights
+    packs = [[q4.PackedWeight(p.qweight.clone(), p.scales.clone(), p.zeros.clone(), p.n, p.k,
+                              128, False) for p in base] for _ in range(copies)]
+    x = synthetic.activations(1, 4096, cfg["x_seed"]).to(dev)
+    ys = [torch.empty((1, p.n), dtype=torch.float32, device=dev) for p in base]
+
+    def gemv_fn(i):
+        return lambda r: q4.q4_w4a16_gemm(x, packs[r % copies][i], out=ys[i])
+
+    fns = [gemv_fn(i) for i in range(len(base))]
+    for r in range(args.warmup):
+        for f in fns:
+            f(r)
+    torch.cuda.synchronize()
+    gemv_kernel = q4.q4_last_kernel()
+    # the timed region: exactly K steps, synchronized on both sides, nothing else inside
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for r in range(args.steps):
+        for f in fns:
+            f(r)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_step = wall * 1e3 / args.steps
+    # kernel durations: HIP events on the launch stream around back-to-back launches of
+    # each shape (a separate pass from the timed steps)
+    launch_ms = [event_ms(f, args.steps) for f in fns]
+    value = step_bytes * args.steps / wall / 1e9
+    mean_launch_ms = sum(launch_ms) / len(launch_ms)
+    mean_launch_bytes = step_bytes / len(base)
+    achieved = mean_launch_bytes / (mean_launch_ms * 1e-3) / 1e9
+    digest = source_digest("gemv.hip", "q4_device.h")
+    traffic = profiled_traffic("q4_gemv_decode_7b_m1_pmc.md", digest)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "kernel": gemv_kernel,
+                "per_launch_us": {f"{p.n}x{p.k}": round(t * 1e3, 3) for p, t in zip(base, launch_ms)},
+                "bytes_per_launch": {f"{p.n}x{p.k}": gemv_bytes(1, p.n, p.k, 128, False) for p in base},
+                "source_digest": digest}
+
+    # ------------------------------------------------------------ prefill GEMM
+    if "gemm" in legs:
+        c4 = synthetic.PREFILL_70B
+        mat = c4["w"]
+        pw = q4.q4_quantize_pack(mat.make().to(dev), 128, False)
+        xg = synthetic.activations(c4["m"], mat.k, c4["x_seed"], outlier_seed=mat.seed,
+                                   outlier_factor=c4["x_outlier_factor"]).to(dev)
+        yg = torch.empty((c4["m"], mat.n), dtype=torch.float32, device=dev)
+        f = lambda r: q4.q4_w4a16_gemm(xg, pw, out=yg)
+        for r in range(3):
+            f(r)
+        torch.cuda.synchronize()
+        kname = q4.q4_last_kernel()
+        t = event_ms(f, 10) * 1e-3
+        flops = 2.0 * c4["m"] * mat.n * mat.k
+        out["gemm"] = {"workload": f"70B-like prefill x[{c4['m']}x{mat.k}] . W[{mat.n}x{mat.k}]^T "
+                                   "g128 asym", "kernel": kname, "ms": round(t * 1e3, 4),
+                       "tflops": round(flops / t / 1e12, 2),
+                       "frac_mfma_bf16": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4)}
+        del pw, xg, yg
+
+    # ------------------------------------------------------------ checkpoint quantize + GEMV sweep
+    if "quant" in legs or "sweep" in legs:
+        mats = synthetic.checkpoint_7b(32)
+        ws = [m_.make(device="cuda") for m_ in mats]
+        torch.cuda.synchronize()
+        res = {}
+        for sym in (False, True):
+            pk = [q4.empty_packed(m_.n, m_.k, 128, sym, dev) for m_ in mats]
+            fq = [(lambda r, i=i: q4.q4_quantize_pack(ws[i], 128, sym, out=pk[i])) for i in range(len(mats))]
+            for f in fq:
+                f(0)
+            torch.cuda.synchronize()
+            kname = q4.q4_last_kernel()
+            wall_q = timed_sweep(fq, 3) / 3
+            qb = sum(quant_bytes(m_.n, m_.k, 128, sym) for m_ in mats)
+            res["asym" if not sym else "sym"] = {
+                "kernel": kname, "bytes": qb, "sweep_ms": round(wall_q * 1e3, 3),
+                "gbs": round(qb / wall_q / 1e9, 1),
+                "frac_hbm": round(qb / wall_q / 1e9 / HBM_PEAK_GBS, 4)}
+            if not sym and "sweep" in legs:
+                xs = {4096: synthetic.activations(1, 4096, 10).to(dev),
+                      11008: synthetic.activations(1, 11008, 10).to(dev)}
+                yy = {n_: torch.empty((1, n_), dtype=torch.float32, device=dev) for n_ in (4096, 11008)}
+                fg = [(lambda r, i=i: q4.q4_w4a16_gemm(xs[mats[i].k], pk[i], out=yy[mats[i].n]))
+                      for i in range(len(mats))]
+                for f in fg:
+                    f(0)
+                torch.cuda.synchronize()
+                wall_g = timed_sweep(fg, 3) / 3
+                gb = sum(gemv_bytes(1, m_.n, m_.k, 128, False) for m_ in mats)
+                res["gemv_sweep_m1"] = {"bytes": gb, "sweep_ms": round(wall_g * 1e3, 3),
+                                        "gbs": round(gb / wall_g / 1e9, 1),
+                                        "frac_hbm": round(gb / wall_g / 1e9 / HBM_PEAK_GBS, 4)}
+            del pk
+        res["workload"] = "32-layer 7B-like checkpoint, 224 bf16 matrices, 6.48e9 weights, g128"
+        out["checkpoint"] = res
+        del ws
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) weights with 0.1% outlier input channels x20, "
+                "N(0,1) activations)",
+        "config": {"workload": "7B-like decode GEMV, W [4096x4096] and [11008x4096], g=128 asym "
+                               "uint4, x bf16 [1x4096], M=1", "group_size": 128, "m": 1,
+                   "weight_copies": copies, "bytes_per_step": step_bytes},
+        "roofline": roofline,
+    }
+    line.update(out)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

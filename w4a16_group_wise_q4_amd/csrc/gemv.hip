@@ -8,21 +8,30 @@
 // bandwidth-bound (§Batch와 Context에 따라 속도가 달라진다), so the kernel is built
 // around streaming the packed weights once at HBM speed.
 //
-// Mapping.  A wave owns a tile of 16 output rows.  Lane l handles row n0 + l%16 and
+// Mapping.  Work is split into tiles of 16 output rows.  Lane l handles row n0 + l%16 and
 // k-slot block c = l/16 of a 16x16x32 MFMA: the 16 rows are the MFMA's N columns, the
-// (zero-padded) activation rows are its M rows, so m = 1..16 costs the same.  A
-// workgroup of S waves covers the whole K range of one row tile (wave w takes a
-// contiguous slice of 128-column units); partial tiles are summed through LDS, so the
-// result is written once, without atomics, in a fixed order.
+// (zero-padded) activation rows are its M rows, so m = 1..16 costs the same.  The waves
+// of a workgroup split the K range of a tile into contiguous slices of 128-column units;
+// partial tiles are summed through LDS, so y is written once, without atomics, in a
+// fixed order.  Workgroups are persistent: each takes tiles blockIdx.x, +gridDim.x, ...
+// and stages the activations in LDS once for all of them (when they fit; otherwise one
+// tile per workgroup and the activations are staged in column chunks).
 //
-// Loads.  Per group and lane, G/32 consecutive packed words (one dwordx4 for g = 128):
-// lane block c holds words [GW*h + LW*c, +LW) of a group of GW = g/8 words, so the 32
-// k-slots of each MFMA lie in one group and the per-group scale can be applied to the
-// MFMA result.
+// Memory.  All global reads are raw buffer loads (SGPR resource, per-lane row offset,
+// scalar unit offset; reads past a resource's end return zero, which pads rows past N
+// without branches).  The packed weights are the only stream on the hot path: per
+// wave-wide load they touch 16 rows x 64 bytes.  A tile's scales and zero points are
+// copied to LDS once per tile with coalesced loads, and the activations live in LDS,
+// already permuted into the decoder's slot order, with an all-zero row feeding the
+// MFMA's padding rows.  The packed weights stream through registers in double-buffered
+// batches of kDepth units.  Per group and lane the loads are g/32 consecutive packed
+// words (one dwordx4 at g = 128): lane block c holds words [GW*h + LW*c, +LW) of a group
+// of GW = g/8 words, so the 32 k-slots of each MFMA lie in one group and the group's
+// scale applies to the MFMA result.
 //
 // Dequantization.  bf16 activations: a nibble OR-ed into the mantissa of 128.0 gives
-// the exact bf16 value 128 + u (one AND-OR per two weights).  The offset is removed per
-// group with a second MFMA whose weight operand is the constant 128 + z (also exact in
+// the exact bf16 value 128 + u (one v_and_or_b32 per two weights).  The offset is removed
+// per group with a second MFMA whose weight operand is the constant 128 + z (also exact in
 // bf16):
 //   sum x(u - z) = D - C,   D = sum x(128 + u),  C = sum x(128 + z).
 // Where every code of a group equals its zero point (an all-zero group), D and C are the
@@ -33,119 +42,499 @@
 
 namespace {
 
-constexpr int kMaxWaves = 8;
+constexpr int kMaxWaves = 8;           // waves per workgroup (all on one 16-row tile)
+constexpr int kDepth = 4;              // 128-column units per batch (two batches in flight)
+constexpr int kLdsBudget = 96 * 1024;  // LDS per workgroup (activations + metadata + sums)
+constexpr int kStage = 4;              // activation vectors per thread per staging pass
+constexpr int kMS = 4;                 // scale entries per thread per tile (chunked kernel)
+constexpr int kMZ = 2;                 // zero-point words per thread per tile (chunked kernel)
+constexpr int kPS = 8;                 // scale entries per thread per tile (streaming kernel)
+constexpr int kPZ = 2;                 // zero-point dwords per thread per tile (streaming kernel)
+constexpr int kOOB = 0x40000000;       // a buffer offset past every resource: reads 0
 
+// One lane's share of one 128-column unit: 4 packed words (one per MFMA).
+struct Unit {
+    uint32_t w[4];
+};
+
+// Dequantize-and-multiply of one 128-column unit for one lane, accumulated into acc.
+// xs: this lane's activation row in LDS (16-byte vectors, chunk-relative), s_row / z_row:
+// this lane's row of the tile metadata in LDS, gbase: index of the unit's first group
+// relative to that metadata, valid_groups: how many of the unit's NH groups exist.
 template <int G, bool SYM, bool XF16>
-__global__ __launch_bounds__(512) void gemv_kernel(const uint16_t* __restrict__ x, int M,
-                                                   const uint32_t* __restrict__ qweight,
-                                                   const uint16_t* __restrict__ scales,
-                                                   const uint32_t* __restrict__ zeros, int N,
-                                                   int K, float* __restrict__ y) {
+__device__ __forceinline__ void unit_mac(q4::f32x4& acc, const Unit& d, const q4::u32x4* xs,
+                                         int wrel, const uint16_t* s_row,
+                                         const uint32_t* z_row, int gbase, bool ok0, int c,
+                                         uint32_t kMask, uint32_t kBias, int KWrem) {
+    constexpr int GW = G / 8, LW = G / 32, NH = 4 / LW;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        const bool ok = ok0 && (GW * h < KWrem);  // a short last unit has fewer groups
+        const int hh = GW * h < KWrem ? h : 0;    // keep every index inside the row
+        const int gl = gbase + hh;
+        q4::u32x4 xa[LW];
+#pragma unroll
+        for (int a = 0; a < LW; ++a) xa[a] = xs[wrel + GW * hh + LW * c + a];
+        const float s = q4::f16_bits_to_float(s_row[gl]);
+        int z = 8;
+        if constexpr (!SYM) z = (int)((z_row[gl >> 3] >> (4 * (gl & 7))) & 0xFu);
+        q4::f32x4 dv = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (XF16) {
+            const _Float16 b = (_Float16)(1024 + z);
+            const q4::f16x2 bias = {b, b};
+#pragma unroll
+            for (int a = 0; a < LW; ++a)
+                dv = q4::mfma_f16(xa[a], q4::decode_f16_exact(d.w[hh * LW + a], bias), dv);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = ok ? acc[i] + s * dv[i] : acc[i];
+        } else {
+            const uint32_t zb = (uint32_t)z * 0x00010001u + kBias;  // bf16 (128+z) x2
+            const q4::u32x4 zop = {zb, zb, zb, zb};
+            q4::f32x4 dc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int a = 0; a < LW; ++a) {
+                dv = q4::mfma_bf16(xa[a], q4::decode_bf16_biased(d.w[hh * LW + a], kMask, kBias), dv);
+                dc = q4::mfma_bf16(xa[a], zop, dc);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = ok ? acc[i] + s * (dv[i] - dc[i]) : acc[i];
+        }
+    }
+}
+
+// Loads one lane's packed words of unit u (clamped inside the row).
+template <int G>
+__device__ __forceinline__ void unit_load(Unit& d, q4::rsrc rq, int qoff, int u, int KW) {
+    constexpr int GW = G / 8, LW = G / 32, NH = 4 / LW;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        int wbase = u * 16 + GW * h;
+        wbase = wbase < KW ? wbase : KW - GW;
+        if constexpr (LW == 4) {
+            const q4::u32x4 t = q4::buf_load_x4(rq, qoff, wbase * 4);
+            d.w[0] = t[0]; d.w[1] = t[1]; d.w[2] = t[2]; d.w[3] = t[3];
+        } else if constexpr (LW == 2) {
+            const q4::u32x2 t = q4::buf_load_x2(rq, qoff, wbase * 4);
+            d.w[2 * h] = t[0]; d.w[2 * h + 1] = t[1];
+        } else {
+            d.w[h] = q4::buf_load_x1(rq, qoff, wbase * 4);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Streaming kernel (the activations fit in LDS): persistent workgroups, each wave runs one
+// continuous stream of 4-unit batches over (tile, its K slice), double-buffered, so the
+// next tile's weights are in flight while the current tile is computed and reduced.
+// LDS: activations [(M+1)][RS] | metadata x2 | partial sums x2.
+template <int G, bool SYM, bool XF16>
+__global__ __launch_bounds__(512) void gemv_stream_kernel(const uint16_t* __restrict__ x, int M,
+                                                          const uint32_t* __restrict__ qweight,
+                                                          const uint16_t* __restrict__ scales,
+                                                          const uint32_t* __restrict__ zeros,
+                                                          int N, int K, float* __restrict__ y) {
+    extern __shared__ q4::u32x4 lds[];
+    const int tid = threadIdx.x, nthreads = blockDim.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int S = nthreads >> 6;
+    const int col = lane & 15, c = lane >> 4;
+    const int KW = K / 8, n_groups = K / G, zwords = (n_groups + 7) >> 3;
+    const int tiles = (N + 15) / 16;
+    const int RS = KW + 1;
+    const int xs_end = (M + 1) * RS;
+    const int s_ent = 16 * n_groups;     // scale entries of a tile (16 rows, contiguous)
+    const int s_dw = 8 * n_groups;       // ... in dwords (the zero block starts after them)
+    const int z_dw = SYM ? 0 : 16 * zwords;
+    const int meta_vec = (s_dw + z_dw + 3) / 4;
+    uint32_t* meta0 = reinterpret_cast<uint32_t*>(lds + xs_end);
+    q4::f32x4* red0 = reinterpret_cast<q4::f32x4*>(lds + xs_end + 2 * meta_vec);
+    const q4::u32x4* xs = lds + (col < M ? col : M) * RS;  // padding lanes: zero row
+
+    const uint32_t kMask = q4::vreg_const(0x000F000Fu);
+    const uint32_t kBias = q4::vreg_const(0x43004300u);
+
+    const int units = (K + 127) / 128;
+    const int per = (units + S - 1) / S;
+    const int u0 = wave * per;
+    const int u1 = u0 + per < units ? u0 + per : units;
+    const int ulast = u1 > u0 ? u1 - 1 : 0;
+    const int nb = (per + kDepth - 1) / kDepth;  // batches per tile
+    const int ntiles = tiles > (int)blockIdx.x ? (tiles - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+    const int total = ntiles * nb;               // batches in this wave's stream
+
+    auto tile_of = [&](int i) { return (int)blockIdx.x + (i / nb) * (int)gridDim.x; };
+
+    // metadata of tile t: scales block (16*n_groups fp16, copied entry by entry so no
+    // load straddles the end of the array) then zero block (16*zwords dwords)
+    auto meta_load = [&](int t, uint32_t (&mv)[kPS + kPZ]) {
+        const int n0 = t * 16;
+        const int rows = N - n0 < 16 ? N - n0 : 16;
+        const q4::rsrc rs = q4::make_rsrc(scales + (int64_t)n0 * n_groups, (uint32_t)rows * n_groups * 2u);
+#pragma unroll
+        for (int j = 0; j < kPS; ++j) {
+            const int e = j * nthreads + tid;
+            mv[j] = q4::buf_load_u16(rs, e < s_ent ? e * 2 : kOOB, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < kPZ; ++j) {
+            if constexpr (SYM) {
+                mv[kPS + j] = 0u;
+            } else {
+                const q4::rsrc rz = q4::make_rsrc(zeros + (int64_t)n0 * zwords, (uint32_t)rows * zwords * 4u);
+                const int e = j * nthreads + tid;
+                mv[kPS + j] = q4::buf_load_x1(rz, e < z_dw ? e * 4 : kOOB, 0);
+            }
+        }
+    };
+    auto meta_store = [&](uint32_t* dst, const uint32_t (&mv)[kPS + kPZ]) {
+#pragma unroll
+        for (int j = 0; j < kPS; ++j) {
+            const int e = j * nthreads + tid;
+            if (e < s_ent) reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)mv[j];
+        }
+#pragma unroll
+        for (int j = 0; j < kPZ; ++j) {
+            const int e = j * nthreads + tid;
+            if (e < z_dw) dst[s_dw + e] = mv[kPS + j];
+        }
+    };
+    // issue the 4 units of stream batch i
+    auto batch_load = [&](Unit (&bf)[kDepth], int i) {
+        const int t = tile_of(i);
+        const int b = i - (i / nb) * nb;
+        const int n0 = t * 16;
+        const int rows = N - n0 < 16 ? N - n0 : 16;
+        const q4::rsrc rq = q4::make_rsrc(qweight + (int64_t)n0 * KW, (uint32_t)rows * KW * 4u);
+        const int qoff = col < rows ? col * KW * 4 + c * (G / 32) * 4 : kOOB;
+#pragma unroll
+        for (int j = 0; j < kDepth; ++j) {
+            const int u = u0 + b * kDepth + j;
+            unit_load<G>(bf[j], rq, qoff, u < u1 ? u : ulast, KW);
+        }
+    };
+
+    q4::f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    auto batch_compute = [&](const Unit (&bf)[kDepth], int i, const uint32_t* meta) {
+        const int b = i - (i / nb) * nb;
+        const uint16_t* s_row = reinterpret_cast<const uint16_t*>(meta) + col * n_groups;
+        const uint32_t* z_row = meta + s_dw + col * zwords;
+#pragma unroll
+        for (int j = 0; j < kDepth; ++j) {
+            const int u = u0 + b * kDepth + j;
+            const bool ok = u < u1;
+            const int ue = ok ? u : ulast;
+            unit_mac<G, SYM, XF16>(acc, bf[j], xs, ue * 16, s_row, z_row, ue * (4 / (G / 32)), ok,
+                                   c, kMask, kBias, KW - ue * 16);
+        }
+    };
+
+    // ---- prologue: activations, first tile's metadata, first two batches
+    Unit bufA[kDepth], bufB[kDepth];
+    {
+        q4::u32x4 xv[kStage];
+        const int nvec = xs_end;
+#pragma unroll
+        for (int j = 0; j < kStage; ++j) {
+            const int v = j * nthreads + tid;
+            const int m = v / RS, jj = v - m * RS;
+            const bool real = v < nvec && m < M && jj < KW;
+            xv[j] = q4::buf_load_x4(q4::make_rsrc(x, (uint32_t)M * K * 2u), real ? (m * K + 8 * jj) * 2 : kOOB, 0);
+        }
+        uint32_t mv[kPS + kPZ];
+        if (ntiles > 0) meta_load(tile_of(0), mv);
+        if (total > 0) batch_load(bufA, 0);
+        if (total > 1) batch_load(bufB, 1);
+#pragma unroll
+        for (int j = 0; j < kStage; ++j) {
+            const int v = j * nthreads + tid;
+            if (v < nvec) lds[v] = q4::pair_perm(xv[j]);
+        }
+        for (int v0 = kStage * nthreads; v0 < nvec; v0 += nthreads) {  // larger m*k only
+            const int v = v0 + tid;
+            const int m = v / RS, jj = v - m * RS;
+            const bool real = v < nvec && m < M && jj < KW;
+            const q4::u32x4 t = q4::buf_load_x4(q4::make_rsrc(x, (uint32_t)M * K * 2u),
+                                                real ? (m * K + 8 * jj) * 2 : kOOB, 0);
+            if (v < nvec) lds[v] = q4::pair_perm(t);
+        }
+        if (ntiles > 0) meta_store(meta0, mv);
+    }
+    __syncthreads();
+
+    uint32_t mnext[kPS + kPZ];
+    // ---- the stream
+    auto step = [&](Unit (&bf)[kDepth], int i) {
+        const int tl = i / nb;                 // tile ordinal within this workgroup
+        const int b = i - tl * nb;
+        const uint32_t* meta = meta0 + (tl & 1) * 4 * meta_vec;
+        if (b == 0 && tl + 1 < ntiles) meta_load(tile_of(i + nb), mnext);
+        batch_compute(bf, i, meta);
+        if (i + 2 < total) batch_load(bf, i + 2);
+        if (b == nb - 1) {  // tile done: publish partial sums, next metadata; one barrier
+            q4::f32x4* red = red0 + (tl & 1) * 64 * S;
+            red[wave * 64 + lane] = acc;
+            acc = q4::f32x4{0.f, 0.f, 0.f, 0.f};
+            if (tl + 1 < ntiles) meta_store(meta0 + ((tl + 1) & 1) * 4 * meta_vec, mnext);
+            __syncthreads();
+            const int t = tile_of(i);
+            const int n0 = t * 16;
+            if (wave == tl % S && n0 + col < N) {  // rotating finisher wave
+                q4::f32x4 sum = red[lane];
+                for (int w = 1; w < S; ++w) {
+                    const q4::f32x4 r = red[w * 64 + lane];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) sum[q] += r[q];
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int m = 4 * c + q;
+                    if (m < M) y[(int64_t)m * N + n0 + col] = sum[q];
+                }
+            }
+        }
+    };
+    for (int i = 0; i < total; i += 2) {
+        step(bufA, i);
+        if (i + 1 < total) step(bufB, i + 1);
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Chunked kernel (the activations do not fit in LDS): one tile per workgroup, activations
+// staged in column chunks.
+// LDS layout (16-byte vectors):
+//   [0, (M+1)*RS)        activation chunk: row m at m*RS, row M all zeros
+//   [xs_end, +META)      tile metadata: scales [16][cg] fp16, then zero words [16][czw]
+//   [.., + waves*64)     cross-wave partial sums
+template <int G, bool SYM, bool XF16>
+__global__ __launch_bounds__(512) void gemv_chunk_kernel(const uint16_t* __restrict__ x, int M,
+                                                         const uint32_t* __restrict__ qweight,
+                                                         const uint16_t* __restrict__ scales,
+                                                         const uint32_t* __restrict__ zeros, int N,
+                                                         int K, int KC, float* __restrict__ y) {
     constexpr int GW = G / 8;   // packed words per group
     constexpr int LW = G / 32;  // words per lane per group (one MFMA per word)
     constexpr int NH = 4 / LW;  // groups per 128-column unit
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int S = blockDim.x >> 6;
+    extern __shared__ q4::u32x4 lds[];
+
+    const int tid = threadIdx.x;
+    const int nthreads = blockDim.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
+    const int S = nthreads >> 6;
     const int col = lane & 15;
     const int c = lane >> 4;
-    const int n_real = blockIdx.x * 16 + col;
-    const int n = n_real < N ? n_real : N - 1;  // rows past N load row N-1, store nothing
     const int KW = K / 8;
     const int n_groups = K / G;
     const int zwords = (n_groups + 7) >> 3;
-    const int units = (K + 127) / 128;
-    const int u0 = (int)((int64_t)wave * units / S);
-    const int u1 = (int)((int64_t)(wave + 1) * units / S);
-    const uint32_t* qrow = qweight + (int64_t)n * KW;
-    const uint16_t* xrow = x + (int64_t)col * K;
-    const bool xvalid = col < M;
+    const int RS = KC / 8 + 1;                   // LDS activation row stride (vectors)
+    const int cg = (KC + G - 1) / G;             // groups per chunk (KC is a multiple of 8*G)
+    const int czw = (cg + 7) >> 3;               // zero words per chunk row
+    const int xs_end = (M + 1) * RS;
+    uint16_t* meta_s = reinterpret_cast<uint16_t*>(lds + xs_end);
+    uint32_t* meta_z = reinterpret_cast<uint32_t*>(lds + xs_end) + (16 * cg + 1) / 2;
+    const int meta_vec = ((16 * cg + 1) / 2 + 16 * czw + 3) / 4;
+    q4::f32x4* red = reinterpret_cast<q4::f32x4*>(lds + xs_end + meta_vec);
+    const q4::u32x4* xs = lds + (col < M ? col : M) * RS;  // padding lanes: zero row
+
+    const q4::rsrc rx = q4::make_rsrc(x, (uint32_t)M * K * 2u);
+    const uint32_t kMask = q4::vreg_const(0x000F000Fu);
+    const uint32_t kBias = q4::vreg_const(0x43004300u);
+
+    const int tile = blockIdx.x;
+    const int n0 = tile * 16;
+    const int rows = N - n0 < 16 ? N - n0 : 16;
+    const q4::rsrc rq = q4::make_rsrc(qweight + (int64_t)n0 * KW, (uint32_t)rows * KW * 4u);
+    const q4::rsrc rs = q4::make_rsrc(scales + (int64_t)n0 * n_groups, (uint32_t)rows * n_groups * 2u);
+    const q4::rsrc rz = q4::make_rsrc(zeros + (int64_t)n0 * zwords, (uint32_t)rows * zwords * 4u);
+    const int qoff = col < rows ? col * KW * 4 + c * LW * 4 : kOOB;
 
     q4::f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    Unit bufA[kDepth], bufB[kDepth];
+    auto load_batch = [&](Unit(&bf)[kDepth], int ub, int u1, int ulast) {
+#pragma unroll
+        for (int i = 0; i < kDepth; ++i) unit_load<G>(bf[i], rq, qoff, ub + i < u1 ? ub + i : ulast, KW);
+    };
+    // padding units (past the wave's range) were loaded from ulast and are computed as
+    // ulast, so every index stays inside the chunk; their result is not added
+    auto compute_batch = [&](const Unit(&bf)[kDepth], int ub, int u1, int ulast, int cb) {
+#pragma unroll
+        for (int i = 0; i < kDepth; ++i) {
+            const bool ok = ub + i < u1;
+            const int ue = ok ? ub + i : ulast;
+            unit_mac<G, SYM, XF16>(acc, bf[i], xs, ue * 16 - cb / 8, meta_s + col * cg,
+                                   meta_z + col * czw, ue * NH - cb / G, ok, c, kMask, kBias,
+                                   KW - ue * 16);
+        }
+    };
 
-    for (int u = u0; u < u1; ++u) {
+    for (int cb = 0; cb < K; cb += KC) {
+        const int ce = cb + KC < K ? cb + KC : K;
+        const int cu0 = cb / 128, cu1 = (ce + 127) / 128;
+        const int per = (cu1 - cu0 + S - 1) / S;  // units per wave (the last may have fewer)
+        const int u0 = cu0 + wave * per;
+        const int u1 = u0 + per < cu1 ? u0 + per : cu1;
+        const int ulast = u1 > u0 ? u1 - 1 : cu0;  // in-range unit to point idle loads at
+        const int nb = (per + kDepth - 1) / kDepth;  // batches of kDepth units
+
+        // 1. issue the activation chunk, the chunk's metadata, the first two weight batches
+        const int vpr = (ce - cb) / 8;
+        const int nvec = xs_end;
+        q4::u32x4 xv[kStage];
 #pragma unroll
-        for (int h = 0; h < NH; ++h) {
-            const int wbase = u * 16 + GW * h;  // first packed word of this group
-            if (wbase >= KW) break;
-            const int gidx = wbase / GW;
-            uint32_t wd[LW];
-            if constexpr (LW == 4) {
-                q4::u32x4 t = *reinterpret_cast<const q4::u32x4*>(qrow + wbase + 4 * c);
-                wd[0] = t[0]; wd[1] = t[1]; wd[2] = t[2]; wd[3] = t[3];
-            } else if constexpr (LW == 2) {
-                q4::u32x2 t = *reinterpret_cast<const q4::u32x2*>(qrow + wbase + 2 * c);
-                wd[0] = t[0]; wd[1] = t[1];
-            } else {
-                wd[0] = qrow[wbase + c];
-            }
-            q4::u32x4 xa[LW];
+        for (int j = 0; j < kStage; ++j) {
+            const int v = j * nthreads + tid;
+            const int m = v / RS, jj = v - m * RS;
+            const bool real = v < nvec && m < M && jj < vpr;
+            xv[j] = q4::buf_load_x4(rx, real ? (m * K + cb + 8 * jj) * 2 : kOOB, 0);
+        }
+        const int gc0 = cb / G, ngc = (ce - cb + G - 1) / G, zc0 = gc0 >> 3;
+        const int nzc = (ngc + 7) >> 3;
+        uint32_t sv[kMS], zv[kMZ];
 #pragma unroll
-            for (int a = 0; a < LW; ++a) {
-                if (xvalid)
-                    xa[a] = q4::pair_perm(
-                        *reinterpret_cast<const q4::u32x4*>(xrow + 8 * (wbase + LW * c + a)));
-                else
-                    xa[a] = q4::u32x4{0u, 0u, 0u, 0u};
-            }
-            const float s = q4::f16_bits_to_float(scales[(int64_t)n * n_groups + gidx]);
-            int z = 8;
-            if constexpr (!SYM)
-                z = (int)((zeros[(int64_t)n * zwords + (gidx >> 3)] >> (4 * (gidx & 7))) & 0xFu);
-            q4::f32x4 d = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (XF16) {
-                const _Float16 b = (_Float16)(1024 + z);
-                const q4::f16x2 bias = {b, b};
+        for (int j = 0; j < kMS; ++j) {
+            const int e = j * nthreads + tid;  // scale entry (row r, chunk group g)
+            const int r = e / cg, g = e - r * cg;
+            const bool real = r < 16 && g < ngc;
+            sv[j] = q4::buf_load_u16(rs, real ? (r * n_groups + gc0 + g) * 2 : kOOB, 0);
+        }
 #pragma unroll
-                for (int a = 0; a < LW; ++a) d = q4::mfma_f16(xa[a], q4::decode_f16_exact(wd[a], bias), d);
+        for (int j = 0; j < kMZ; ++j) {
+            const int e = j * nthreads + tid;  // zero word entry (row r, chunk word q)
+            const int r = e / czw, q = e - r * czw;
+            const bool real = !SYM && r < 16 && q < nzc;
+            zv[j] = SYM ? 0u : q4::buf_load_x1(rz, real ? (r * zwords + zc0 + q) * 4 : kOOB, 0);
+        }
+        load_batch(bufA, u0, u1, ulast);
+        if (nb > 1) load_batch(bufB, u0 + kDepth, u1, ulast);
+
+        if (cb > 0) __syncthreads();  // LDS free for reuse
+        // 2. park activations and metadata in LDS
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] += s * d[i];
-            } else {
-                const uint32_t zb = (0x4300u | (uint32_t)z) * 0x00010001u;  // bf16 (128+z) x2
-                const q4::u32x4 zop = {zb, zb, zb, zb};
-                q4::f32x4 dc = {0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < kStage; ++j) {
+            const int v = j * nthreads + tid;
+            if (v < nvec) lds[v] = q4::pair_perm(xv[j]);
+        }
+        for (int v0 = kStage * nthreads; v0 < nvec; v0 += nthreads) {
+            const int v = v0 + tid;
+            const int m = v / RS, jj = v - m * RS;
+            const bool real = v < nvec && m < M && jj < vpr;
+            const q4::u32x4 t = q4::buf_load_x4(rx, real ? (m * K + cb + 8 * jj) * 2 : kOOB, 0);
+            if (v < nvec) lds[v] = q4::pair_perm(t);
+        }
 #pragma unroll
-                for (int a = 0; a < LW; ++a) {
-                    d = q4::mfma_bf16(xa[a], q4::decode_bf16_biased(wd[a]), d);
-                    dc = q4::mfma_bf16(xa[a], zop, dc);
-                }
+        for (int j = 0; j < kMS; ++j) {
+            const int e = j * nthreads + tid;
+            if (e < 16 * cg) meta_s[e] = (uint16_t)sv[j];
+        }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] += s * (d[i] - dc[i]);
+        for (int j = 0; j < kMZ; ++j) {
+            const int e = j * nthreads + tid;
+            if (e < 16 * czw) meta_z[e] = zv[j];
+        }
+        __syncthreads();
+        // 3. double-buffered batches: batch b+2 is requested once batch b is consumed
+        for (int b = 0; b < nb; b += 2) {
+            compute_batch(bufA, u0 + b * kDepth, u1, ulast, cb);
+            if (b + 2 < nb) load_batch(bufA, u0 + (b + 2) * kDepth, u1, ulast);
+            if (b + 1 < nb) {
+                compute_batch(bufB, u0 + (b + 1) * kDepth, u1, ulast, cb);
+                if (b + 3 < nb) load_batch(bufB, u0 + (b + 3) * kDepth, u1, ulast);
             }
         }
     }
 
-    __shared__ q4::f32x4 red[kMaxWaves][64];
-    red[wave][lane] = acc;
+    // 4. cross-wave sum of the tile, written once
+    red[wave * 64 + lane] = acc;
     __syncthreads();
-    if (wave == 0 && n_real < N) {
-        q4::f32x4 t = red[0][lane];
+    if (wave == 0 && col < rows) {
+        q4::f32x4 t = red[lane];
         for (int w = 1; w < S; ++w) {
-            const q4::f32x4 r = red[w][lane];
+            const q4::f32x4 r = red[w * 64 + lane];
 #pragma unroll
             for (int i = 0; i < 4; ++i) t[i] += r[i];
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int m = 4 * c + i;
-            if (m < M) y[(int64_t)m * N + n_real] = t[i];
+            if (m < M) y[(int64_t)m * N + n0 + col] = t[i];
         }
     }
 }
 
+int g_num_cus = 0;
+
 template <int G, bool SYM>
 hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16_t* sc,
                   const uint32_t* zr, int n, int k, float* y, hipStream_t st, const char** kname) {
-    const int units = (k + 127) / 128;
-    const int waves = units < kMaxWaves ? units : kMaxWaves;
-    const dim3 grid((unsigned)((n + 15) / 16)), block(64 * waves);
+    if (g_num_cus == 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&g_num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            g_num_cus <= 0)
+            g_num_cus = 256;
+    }
+    // waves: about kDepth units each, at most kMaxWaves
+    const int units_k = (k + 127) / 128;
+    int waves = (units_k + kDepth - 1) / kDepth;
+    waves = waves < 1 ? 1 : (waves > kMaxWaves ? kMaxWaves : waves);
+    const int threads = 64 * waves;
+    const int tiles = (n + 15) / 16;
     const uint16_t* xp = reinterpret_cast<const uint16_t*>(x);
+    const int ng = k / G, zw = (ng + 7) / 8;
+    // streaming kernel when the activations (plus zero row), two metadata copies and two
+    // sets of partial sums fit, and a tile's metadata fits the per-thread copy
+    const int meta_vec = (8 * ng + (SYM ? 0 : 16 * zw) + 3) / 4;
+    const size_t lds_stream = (size_t)((m + 1) * (k / 8 + 1) + 2 * meta_vec + 2 * waves * 64) * 16;
+    const bool stream = lds_stream <= (size_t)kLdsBudget && 16 * ng <= kPS * threads &&
+                        16 * zw <= kPZ * threads;
+    if (stream) {
+        auto run = [&](auto kern, const char* name) {
+            static int cached_threads = -1, cached_per_cu = 1;
+            static size_t cached_lds = 0;
+            if (cached_threads != threads || cached_lds != lds_stream) {
+                int per_cu = 0;
+                if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, lds_stream) != hipSuccess ||
+                    per_cu < 1)
+                    per_cu = 1;
+                cached_threads = threads;
+                cached_lds = lds_stream;
+                cached_per_cu = per_cu;
+            }
+            const int cap = g_num_cus * cached_per_cu;
+            const int grid = tiles < cap ? tiles : cap;
+            *kname = name;
+            hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds_stream, st, xp, m, qw, sc, zr, n, k, y);
+            return hipGetLastError();
+        };
+        if (xd == 1) return run(gemv_stream_kernel<G, SYM, true>, "q4_gemv_mfma_f16");
+        return run(gemv_stream_kernel<G, SYM, false>, "q4_gemv_mfma_bf16");
+    }
+    auto lds_bytes = [&](int kc) {
+        const int cg = (kc + G - 1) / G, czw = (cg + 7) / 8;
+        const int mv = ((16 * cg + 1) / 2 + 16 * czw + 3) / 4;
+        return (size_t)((m + 1) * (kc / 8 + 1) + mv + waves * 64) * 16;
+    };
+    auto fits = [&](int kc) {
+        const int cg = (kc + G - 1) / G, czw = (cg + 7) / 8;
+        return lds_bytes(kc) <= (size_t)kLdsBudget && 16 * cg <= kMS * threads &&
+               16 * czw <= kMZ * threads;
+    };
+    // activation chunk: the largest multiple of 8 groups (and of 128 columns) that fits
+    const int step = 8 * G > 128 ? 8 * G : 128;
+    int kc = step;
+    while (kc + step < k && fits(kc + step)) kc += step;
+    if (kc > k) kc = k;
+    const size_t lds = lds_bytes(kc);
     if (xd == 1) {
         *kname = "q4_gemv_mfma_f16";
-        hipLaunchKernelGGL((gemv_kernel<G, SYM, true>), grid, block, 0, st, xp, m, qw, sc, zr, n, k, y);
+        hipLaunchKernelGGL((gemv_chunk_kernel<G, SYM, true>), dim3(tiles), dim3(threads), lds, st, xp, m,
+                           qw, sc, zr, n, k, kc, y);
     } else {
         *kname = "q4_gemv_mfma_bf16";
-        hipLaunchKernelGGL((gemv_kernel<G, SYM, false>), grid, block, 0, st, xp, m, qw, sc, zr, n, k, y);
+        hipLaunchKernelGGL((gemv_chunk_kernel<G, SYM, false>), dim3(tiles), dim3(threads), lds, st, xp, m,
+                           qw, sc, zr, n, k, kc, y);
     }
     return hipGetLastError();
 }

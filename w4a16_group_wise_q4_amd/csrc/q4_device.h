@@ -38,14 +38,24 @@ __device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
 // operand element 2i is column i and element 2i+1 is column i+4.  The activation operand
 // is permuted the same way (pair_perm below).
 
+// A constant held in a VGPR the optimizer cannot see through.  gfx9 VOP3 encodings take no
+// literal operand, so (a & K1) | K2 with literal K1, K2 becomes two VOP2 ops; with both
+// constants in registers it is a single v_and_or_b32.
+__device__ __forceinline__ uint32_t vreg_const(uint32_t k) {
+    uint32_t r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(k));
+    return r;
+}
+
 // bf16 exponent bias: 0x4300 is 128.0 with a zero 7-bit mantissa, so OR-ing a nibble into
-// the low mantissa bits gives exactly 128 + u.
-__device__ __forceinline__ u32x4 decode_bf16_biased(uint32_t w) {
+// the low mantissa bits gives exactly 128 + u.  mask = 0x000F000F, bias = 0x43004300 (in
+// registers, see vreg_const): 3 shifts + 4 v_and_or_b32 per word.
+__device__ __forceinline__ u32x4 decode_bf16_biased(uint32_t w, uint32_t mask, uint32_t bias) {
     u32x4 r;
-    r[0] = (w & 0x000F000Fu) | 0x43004300u;
-    r[1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-    r[2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
-    r[3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+    r[0] = (w & mask) | bias;
+    r[1] = ((w >> 4) & mask) | bias;
+    r[2] = ((w >> 8) & mask) | bias;
+    r[3] = ((w >> 12) & mask) | bias;
     return r;
 }
 
@@ -76,6 +86,30 @@ __device__ __forceinline__ u32x4 pair_perm(u32x4 x) {
 
 __device__ __forceinline__ float f16_bits_to_float(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// ---------------------------------------------------------------- raw buffer loads
+// A buffer resource (V#) in SGPRs: 64-bit base, byte size; the gfx9-family fourth word.
+// Raw loads take a per-lane byte offset and a wave-uniform byte offset; any access whose
+// offset reaches past num_bytes returns zero instead of touching memory.
+typedef __amdgpu_buffer_rsrc_t rsrc;
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ rsrc make_rsrc(const void* base, uint32_t num_bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes,
+                                             kRsrcWord3);
+}
+__device__ __forceinline__ u32x4 buf_load_x4(rsrc r, int voff, int soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ u32x2 buf_load_x2(rsrc r, int voff, int soff) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t buf_load_x1(rsrc r, int voff, int soff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t buf_load_u16(rsrc r, int voff, int soff) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
 }
 
 }  // namespace q4
