@@ -1,13 +1,17 @@
 """Benchmark of the W4A16 group-wise INT4 hot path on one MI355X.
 
-Metric: W4A16 GEMV achieved HBM GB/s at M=1 (7B-like decode projections 4096x4096 and
-11008x4096, group 128, asymmetric), with the GEMM TFLOP/s of the 70B-like prefill and the
-quantize/pack GB/s of the 32-layer 7B-like checkpoint reported alongside.
+Metric: W4A16 GEMV achieved HBM GB/s at M=1 on the 7B-like decode projections
+(4096x4096 and 11008x4096, group 128, asymmetric), with the prefill GEMM TFLOP/s (70B-like
+28672x8192, M=2048) and the quantize/pack GB/s of the 32-layer 7B-like checkpoint in the
+same JSON line.
 
-A timed step is one decode pass: the W4A16 GEMV over both projections at M=1.  Each step
-reads a different copy of the packed weights (the copies together exceed twice the
-256 MB Infinity Cache), so every step streams its weights from HBM.  Inputs are
-resident in HBM before the timed region starts.
+A timed step is one decode pass: the W4A16 GEMV over both projections at M=1, one launch
+each.  Each step reads a different copy of the packed weights (the copies together are
+four times the 256 MB Infinity Cache), so every step streams its weights from HBM.  The
+steps are replayed from captured HIP graphs (the launches themselves are identical to
+direct calls; the graph removes the Python/ctypes launch cost of ~7 us per call, which
+would otherwise dominate the ~10 us kernels).  Inputs are resident in HBM before the
+timed region starts.
 
 Algorithmic bytes (what the method must move, nothing else):
   GEMV   per launch: n*k/2 (codes) + 2*n*k/g (fp16 scales) + 4*n*ceil(k/g/8) (zeros)
@@ -68,47 +72,47 @@ def profiled_traffic(summary_name, digest):
     return float(val.group(1))
 
 
-def event_ms(fn, reps):
-    """Mean duration in ms of one launch of ``fn``: HIP events on the launch stream around
-    ``reps`` back-to-back launches (fn(r) picks the r-th input copy)."""
+def capture(fns):
+    """A HIP graph of the given launches, in order (captured on a side stream)."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):          # warm the launch path on the capture stream
+        for f in fns[:2]:
+            f()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    return g
+
+
+def graph_ms(graph, reps):
+    """Mean duration in ms of one replay: HIP events on the launch stream."""
     import torch
     stream = torch.cuda.current_stream()
+    graph.replay()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
-    for r in range(reps):
-        fn(r)
+    for _ in range(reps):
+        graph.replay()
     t1.record(stream)
     torch.cuda.synchronize()
     return t0.elapsed_time(t1) / reps
 
 
-def timed_sweep(fn_list, reps):
-    """Wall seconds of ``reps`` passes over fn_list, events around the whole region."""
-    import torch
-    stream = torch.cuda.current_stream()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for r in range(reps):
-        for fn in fn_list:
-            fn(r)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / 1e3
-
-
 def cpu_baseline(seconds=12.0):
     """The CPU oracle (plain scalar C, one thread) on a bounded sample of the decode
     workload: full fp64 passes over both projections at M=1."""
-    import numpy as np
-
     import oracle
     import synthetic
     cfg = synthetic.DECODE_7B
-    packs, total = [], 0
+    packs = []
     x = synthetic.activations(1, 4096, cfg["x_seed"])
     xb = (synthetic.as_u16(x), oracle.BF16)
     for mat in cfg["mats"]:
@@ -133,10 +137,10 @@ def cpu_baseline(seconds=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=340)
+    ap.add_argument("--warmup", type=int, default=34)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--legs", default="gemv,gemm,quant,sweep",
+    ap.add_argument("--legs", default="gemm,quant,sweep",
                     help="comma list of legs besides the headline decode GEMV")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy 5 times (the "
@@ -164,43 +168,49 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    legs = set(args.legs.split(","))
+    legs = set(args.legs.split(",")) if args.legs else set()
     out = {}
 
     # ------------------------------------------------------------ decode GEMV (the metric)
     cfg = synthetic.DECODE_7B
-    base = []
-    for mat in cfg["mats"]:
-        base.append(q4.q4_quantize_pack(mat.make().to(dev), 128, False))
+    base = [q4.q4_quantize_pack(mat.make().to(dev), 128, False) for mat in cfg["mats"]]
     step_bytes = sum(gemv_bytes(1, p.n, p.k, 128, False) for p in base)
-    copies = max(2, -(-4 * MALL_BYTES // step_bytes))  # >= 2x MALL of distinct weights
+    copies = max(2, -(-4 * MALL_BYTES // step_bytes))  # 4x the Infinity Cache
     packs = [[q4.PackedWeight(p.qweight.clone(), p.scales.clone(), p.zeros.clone(), p.n, p.k,
                               128, False) for p in base] for _ in range(copies)]
     x = synthetic.activations(1, 4096, cfg["x_seed"]).to(dev)
     ys = [torch.empty((1, p.n), dtype=torch.float32, device=dev) for p in base]
 
-    def gemv_fn(i):
-        return lambda r: q4.q4_w4a16_gemm(x, packs[r % copies][i], out=ys[i])
+    def step_fns(c):
+        return [lambda c=c, i=i: q4.q4_w4a16_gemm(x, packs[c][i], out=ys[i]) for i in range(len(base))]
 
-    fns = [gemv_fn(i) for i in range(len(base))]
-    for r in range(args.warmup):
-        for f in fns:
-            f(r)
+    for f in step_fns(0):
+        f()
     torch.cuda.synchronize()
     gemv_kernel = q4.q4_last_kernel()
-    # the timed region: exactly K steps, synchronized on both sides, nothing else inside
+    full = capture([f for c in range(copies) for f in step_fns(c)])
+    tail_n = args.steps % copies
+    tail = capture([f for c in range(tail_n) for f in step_fns(c)]) if tail_n else None
+    for _ in range(max(1, args.warmup // copies)):
+        full.replay()
     torch.cuda.synchronize()
+    # the timed region: exactly K steps, synchronized on both sides, nothing else inside
     t_start = time.perf_counter()
-    for r in range(args.steps):
-        for f in fns:
-            f(r)
+    for _ in range(args.steps // copies):
+        full.replay()
+    if tail is not None:
+        tail.replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_step = wall * 1e3 / args.steps
-    # kernel durations: HIP events on the launch stream around back-to-back launches of
-    # each shape (a separate pass from the timed steps)
-    launch_ms = [event_ms(f, args.steps) for f in fns]
     value = step_bytes * args.steps / wall / 1e9
+
+    # kernel durations: HIP events on the launch stream around graph replays of one shape
+    # (every copy once), a pass separate from the timed steps
+    launch_ms = []
+    for i in range(len(base)):
+        g = capture([lambda c=c: q4.q4_w4a16_gemm(x, packs[c][i], out=ys[i]) for c in range(copies)])
+        launch_ms.append(graph_ms(g, 10) / copies)
     mean_launch_ms = sum(launch_ms) / len(launch_ms)
     mean_launch_bytes = step_bytes / len(base)
     achieved = mean_launch_bytes / (mean_launch_ms * 1e-3) / 1e9
@@ -212,6 +222,7 @@ def main():
                 "per_launch_us": {f"{p.n}x{p.k}": round(t * 1e3, 3) for p, t in zip(base, launch_ms)},
                 "bytes_per_launch": {f"{p.n}x{p.k}": gemv_bytes(1, p.n, p.k, 128, False) for p in base},
                 "source_digest": digest}
+    del packs
 
     # ------------------------------------------------------------ prefill GEMM
     if "gemm" in legs:
@@ -221,12 +232,11 @@ def main():
         xg = synthetic.activations(c4["m"], mat.k, c4["x_seed"], outlier_seed=mat.seed,
                                    outlier_factor=c4["x_outlier_factor"]).to(dev)
         yg = torch.empty((c4["m"], mat.n), dtype=torch.float32, device=dev)
-        f = lambda r: q4.q4_w4a16_gemm(xg, pw, out=yg)
-        for r in range(3):
-            f(r)
+        q4.q4_w4a16_gemm(xg, pw, out=yg)
         torch.cuda.synchronize()
         kname = q4.q4_last_kernel()
-        t = event_ms(f, 10) * 1e-3
+        g = capture([lambda: q4.q4_w4a16_gemm(xg, pw, out=yg)] * 5)
+        t = graph_ms(g, 4) / 5 * 1e-3
         flops = 2.0 * c4["m"] * mat.n * mat.k
         out["gemm"] = {"workload": f"70B-like prefill x[{c4['m']}x{mat.k}] . W[{mat.n}x{mat.k}]^T "
                                    "g128 asym", "kernel": kname, "ms": round(t * 1e3, 4),
@@ -242,31 +252,29 @@ def main():
         res = {}
         for sym in (False, True):
             pk = [q4.empty_packed(m_.n, m_.k, 128, sym, dev) for m_ in mats]
-            fq = [(lambda r, i=i: q4.q4_quantize_pack(ws[i], 128, sym, out=pk[i])) for i in range(len(mats))]
+            fq = [(lambda i=i: q4.q4_quantize_pack(ws[i], 128, sym, out=pk[i])) for i in range(len(mats))]
             for f in fq:
-                f(0)
+                f()
             torch.cuda.synchronize()
             kname = q4.q4_last_kernel()
-            wall_q = timed_sweep(fq, 3) / 3
+            t_q = graph_ms(capture(fq), 3) * 1e-3
             qb = sum(quant_bytes(m_.n, m_.k, 128, sym) for m_ in mats)
             res["asym" if not sym else "sym"] = {
-                "kernel": kname, "bytes": qb, "sweep_ms": round(wall_q * 1e3, 3),
-                "gbs": round(qb / wall_q / 1e9, 1),
-                "frac_hbm": round(qb / wall_q / 1e9 / HBM_PEAK_GBS, 4)}
+                "kernel": kname, "bytes": qb, "sweep_ms": round(t_q * 1e3, 3),
+                "gbs": round(qb / t_q / 1e9, 1), "frac_hbm": round(qb / t_q / 1e9 / HBM_PEAK_GBS, 4)}
             if not sym and "sweep" in legs:
                 xs = {4096: synthetic.activations(1, 4096, 10).to(dev),
                       11008: synthetic.activations(1, 11008, 10).to(dev)}
                 yy = {n_: torch.empty((1, n_), dtype=torch.float32, device=dev) for n_ in (4096, 11008)}
-                fg = [(lambda r, i=i: q4.q4_w4a16_gemm(xs[mats[i].k], pk[i], out=yy[mats[i].n]))
+                fg = [(lambda i=i: q4.q4_w4a16_gemm(xs[mats[i].k], pk[i], out=yy[mats[i].n]))
                       for i in range(len(mats))]
                 for f in fg:
-                    f(0)
-                torch.cuda.synchronize()
-                wall_g = timed_sweep(fg, 3) / 3
+                    f()
+                t_g = graph_ms(capture(fg), 3) * 1e-3
                 gb = sum(gemv_bytes(1, m_.n, m_.k, 128, False) for m_ in mats)
-                res["gemv_sweep_m1"] = {"bytes": gb, "sweep_ms": round(wall_g * 1e3, 3),
-                                        "gbs": round(gb / wall_g / 1e9, 1),
-                                        "frac_hbm": round(gb / wall_g / 1e9 / HBM_PEAK_GBS, 4)}
+                res["gemv_sweep_m1"] = {"bytes": gb, "sweep_ms": round(t_g * 1e3, 3),
+                                        "gbs": round(gb / t_g / 1e9, 1),
+                                        "frac_hbm": round(gb / t_g / 1e9 / HBM_PEAK_GBS, 4)}
             del pk
         res["workload"] = "32-layer 7B-like checkpoint, 224 bf16 matrices, 6.48e9 weights, g128"
         out["checkpoint"] = res
@@ -280,7 +288,8 @@ def main():
                 "N(0,1) activations)",
         "config": {"workload": "7B-like decode GEMV, W [4096x4096] and [11008x4096], g=128 asym "
                                "uint4, x bf16 [1x4096], M=1", "group_size": 128, "m": 1,
-                   "weight_copies": copies, "bytes_per_step": step_bytes},
+                   "weight_copies": copies, "bytes_per_step": step_bytes,
+                   "launch": "one GEMV launch per projection, replayed from HIP graphs"},
         "roofline": roofline,
     }
     line.update(out)

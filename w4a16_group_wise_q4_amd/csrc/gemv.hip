@@ -124,11 +124,11 @@ __device__ __forceinline__ void unit_load(Unit& d, q4::rsrc rq, int qoff, int u,
 
 // ---------------------------------------------------------------------------------------
 // Streaming kernel (the activations fit in LDS): persistent workgroups, each wave runs one
-// continuous stream of 4-unit batches over (tile, its K slice), double-buffered, so the
-// next tile's weights are in flight while the current tile is computed and reduced.
+// continuous stream of D-unit batches over (tile, its K slice) with R batches in flight,
+// so the next tile's weights are in flight while the current tile is computed and reduced.
 // LDS: activations [(M+1)][RS] | metadata x2 | partial sums x2.
-template <int G, bool SYM, bool XF16>
-__global__ __launch_bounds__(512) void gemv_stream_kernel(const uint16_t* __restrict__ x, int M,
+template <int G, bool SYM, bool XF16, int R, int D, int MAXT, int MINW>
+__global__ __launch_bounds__(MAXT, MINW) void gemv_stream_kernel(const uint16_t* __restrict__ x, int M,
                                                           const uint32_t* __restrict__ qweight,
                                                           const uint16_t* __restrict__ scales,
                                                           const uint32_t* __restrict__ zeros,
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(512) void gemv_stream_kernel(const uint16_t* __rest
     const int u0 = wave * per;
     const int u1 = u0 + per < units ? u0 + per : units;
     const int ulast = u1 > u0 ? u1 - 1 : 0;
-    const int nb = (per + kDepth - 1) / kDepth;  // batches per tile
+    const int nb = (per + D - 1) / D;  // batches per tile
     const int ntiles = tiles > (int)blockIdx.x ? (tiles - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
     const int total = ntiles * nb;               // batches in this wave's stream
 
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(512) void gemv_stream_kernel(const uint16_t* __rest
         }
     };
     // issue the 4 units of stream batch i
-    auto batch_load = [&](Unit (&bf)[kDepth], int i) {
+    auto batch_load = [&](Unit (&bf)[D], int i) {
         const int t = tile_of(i);
         const int b = i - (i / nb) * nb;
         const int n0 = t * 16;
@@ -208,20 +208,20 @@ __global__ __launch_bounds__(512) void gemv_stream_kernel(const uint16_t* __rest
         const q4::rsrc rq = q4::make_rsrc(qweight + (int64_t)n0 * KW, (uint32_t)rows * KW * 4u);
         const int qoff = col < rows ? col * KW * 4 + c * (G / 32) * 4 : kOOB;
 #pragma unroll
-        for (int j = 0; j < kDepth; ++j) {
-            const int u = u0 + b * kDepth + j;
+        for (int j = 0; j < D; ++j) {
+            const int u = u0 + b * D + j;
             unit_load<G>(bf[j], rq, qoff, u < u1 ? u : ulast, KW);
         }
     };
 
     q4::f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    auto batch_compute = [&](const Unit (&bf)[kDepth], int i, const uint32_t* meta) {
+    auto batch_compute = [&](const Unit (&bf)[D], int i, const uint32_t* meta) {
         const int b = i - (i / nb) * nb;
         const uint16_t* s_row = reinterpret_cast<const uint16_t*>(meta) + col * n_groups;
         const uint32_t* z_row = meta + s_dw + col * zwords;
 #pragma unroll
-        for (int j = 0; j < kDepth; ++j) {
-            const int u = u0 + b * kDepth + j;
+        for (int j = 0; j < D; ++j) {
+            const int u = u0 + b * D + j;
             const bool ok = u < u1;
             const int ue = ok ? u : ulast;
             unit_mac<G, SYM, XF16>(acc, bf[j], xs, ue * 16, s_row, z_row, ue * (4 / (G / 32)), ok,
@@ -229,8 +229,8 @@ __global__ __launch_bounds__(512) void gemv_stream_kernel(const uint16_t* __rest
         }
     };
 
-    // ---- prologue: activations, first tile's metadata, first two batches
-    Unit bufA[kDepth], bufB[kDepth];
+    // ---- prologue: activations, first tile's metadata, first R batches
+    Unit buf[R][D];
     {
         q4::u32x4 xv[kStage];
         const int nvec = xs_end;
@@ -243,8 +243,9 @@ __global__ __launch_bounds__(512) void gemv_stream_kernel(const uint16_t* __rest
         }
         uint32_t mv[kPS + kPZ];
         if (ntiles > 0) meta_load(tile_of(0), mv);
-        if (total > 0) batch_load(bufA, 0);
-        if (total > 1) batch_load(bufB, 1);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (r < total) batch_load(buf[r], r);
 #pragma unroll
         for (int j = 0; j < kStage; ++j) {
             const int v = j * nthreads + tid;
@@ -264,13 +265,13 @@ __global__ __launch_bounds__(512) void gemv_stream_kernel(const uint16_t* __rest
 
     uint32_t mnext[kPS + kPZ];
     // ---- the stream
-    auto step = [&](Unit (&bf)[kDepth], int i) {
+    auto step = [&](Unit (&bf)[D], int i) {
         const int tl = i / nb;                 // tile ordinal within this workgroup
         const int b = i - tl * nb;
         const uint32_t* meta = meta0 + (tl & 1) * 4 * meta_vec;
         if (b == 0 && tl + 1 < ntiles) meta_load(tile_of(i + nb), mnext);
         batch_compute(bf, i, meta);
-        if (i + 2 < total) batch_load(bf, i + 2);
+        if (i + R < total) batch_load(bf, i + R);
         if (b == nb - 1) {  // tile done: publish partial sums, next metadata; one barrier
             q4::f32x4* red = red0 + (tl & 1) * 64 * S;
             red[wave * 64 + lane] = acc;
@@ -294,9 +295,10 @@ __global__ __launch_bounds__(512) void gemv_stream_kernel(const uint16_t* __rest
             }
         }
     };
-    for (int i = 0; i < total; i += 2) {
-        step(bufA, i);
-        if (i + 1 < total) step(bufB, i + 1);
+    for (int i = 0; i < total; i += R) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (i + r < total) step(buf[r], i + r);
     }
 }
 
@@ -475,20 +477,49 @@ hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16
             g_num_cus <= 0)
             g_num_cus = 256;
     }
-    // waves: about kDepth units each, at most kMaxWaves
+    // Workgroup shape.  With tiles to spare (at least two per CU): 4-wave workgroups with
+    // 4-unit batches, three batches in flight, several workgroups resident per CU.  With
+    // at most one tile per CU the whole matrix is requested at once and the time after the
+    // data arrives dominates, so the tile is spread over up to 16 waves of 2-unit batches.
+    // Otherwise 8 waves of 4-unit batches.
     const int units_k = (k + 127) / 128;
-    int waves = (units_k + kDepth - 1) / kDepth;
-    waves = waves < 1 ? 1 : (waves > kMaxWaves ? kMaxWaves : waves);
-    const int threads = 64 * waves;
     const int tiles = (n + 15) / 16;
+    int shape;  // 0: 8 waves, D=4, R=2   1: 4 waves, D=4, R=3   2: up to 16 waves, D=2, R=2
+    int waves;
+    if (tiles >= 2 * g_num_cus) {
+        shape = 1;
+        waves = (units_k + 3) / 4;
+        waves = waves < 1 ? 1 : (waves > 4 ? 4 : waves);
+    } else if (tiles <= g_num_cus && units_k >= 16 && G >= 64) {
+        shape = 2;
+        waves = (units_k + 1) / 2;
+        waves = waves > 16 ? 16 : waves;
+    } else {
+        shape = 0;
+        waves = (units_k + 3) / 4;
+        waves = waves < 1 ? 1 : (waves > kMaxWaves ? kMaxWaves : waves);
+    }
     const uint16_t* xp = reinterpret_cast<const uint16_t*>(x);
     const int ng = k / G, zw = (ng + 7) / 8;
     // streaming kernel when the activations (plus zero row), two metadata copies and two
     // sets of partial sums fit, and a tile's metadata fits the per-thread copy
     const int meta_vec = (8 * ng + (SYM ? 0 : 16 * zw) + 3) / 4;
-    const size_t lds_stream = (size_t)((m + 1) * (k / 8 + 1) + 2 * meta_vec + 2 * waves * 64) * 16;
-    const bool stream = lds_stream <= (size_t)kLdsBudget && 16 * ng <= kPS * threads &&
-                        16 * zw <= kPZ * threads;
+    auto stream_lds = [&](int w) {
+        return (size_t)((m + 1) * (k / 8 + 1) + 2 * meta_vec + 2 * w * 64) * 16;
+    };
+    auto stream_fits = [&](int w) {
+        return stream_lds(w) <= (size_t)kLdsBudget && 16 * ng <= kPS * 64 * w &&
+               16 * zw <= kPZ * 64 * w;
+    };
+    if (shape == 2 && !stream_fits(waves)) {  // too much LDS for 16 waves: 8-wave shape
+        shape = 0;
+        waves = (units_k + 3) / 4;
+        waves = waves < 1 ? 1 : (waves > kMaxWaves ? kMaxWaves : waves);
+    }
+    const bool stream = stream_fits(waves);
+    if (!stream && waves > kMaxWaves) waves = kMaxWaves;  // the chunked kernel's bound
+    const int threads = 64 * waves;
+    const size_t lds_stream = stream_lds(waves);
     if (stream) {
         auto run = [&](auto kern, const char* name) {
             static int cached_threads = -1, cached_per_cu = 1;
@@ -508,8 +539,19 @@ hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16
             hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds_stream, st, xp, m, qw, sc, zr, n, k, y);
             return hipGetLastError();
         };
-        if (xd == 1) return run(gemv_stream_kernel<G, SYM, true>, "q4_gemv_mfma_f16");
-        return run(gemv_stream_kernel<G, SYM, false>, "q4_gemv_mfma_bf16");
+        constexpr int R1 = G == 128 ? 3 : 2;
+        if (shape == 1) {
+            if (xd == 1) return run(gemv_stream_kernel<G, SYM, true, R1, 4, 256, 2>, "q4_gemv_mfma_f16");
+            return run(gemv_stream_kernel<G, SYM, false, R1, 4, 256, 2>, "q4_gemv_mfma_bf16");
+        }
+        if constexpr (G >= 64) {
+            if (shape == 2) {
+                if (xd == 1) return run(gemv_stream_kernel<G, SYM, true, 2, 2, 1024, 1>, "q4_gemv_mfma_f16");
+                return run(gemv_stream_kernel<G, SYM, false, 2, 2, 1024, 1>, "q4_gemv_mfma_bf16");
+            }
+        }
+        if (xd == 1) return run(gemv_stream_kernel<G, SYM, true, 2, 4, 512, 1>, "q4_gemv_mfma_f16");
+        return run(gemv_stream_kernel<G, SYM, false, 2, 4, 512, 1>, "q4_gemv_mfma_bf16");
     }
     auto lds_bytes = [&](int kc) {
         const int cg = (kc + G - 1) / G, czw = (cg + 7) / 8;
