@@ -10,7 +10,8 @@
  * k input features.  A group is g consecutive input columns of one row ([FL7] §Per-group),
  * G = k / g groups per row.
  *   qweight : uint32 [n][k/8]; the 4-bit code of column 8j+i is bits 4i..4i+3 of word j.
- *   scales  : fp16 bit patterns [n][G], the scale S of each group.
+ *   scales  : fp16 bit patterns [n][G], the scale S of each group.  The matmul and
+ *             dequant entry points take any finite S; a group with S = 0 contributes 0.
  *   zeros   : uint32 [n][ceil(G/8)]; zero point of group 8j+i in bits 4i..4i+3 of word j,
  *             unused pad nibbles are 0.  Asymmetric mode only.
  * Asymmetric codes are q in [0,15] stored as is; symmetric codes q in [-8,7] are stored
@@ -78,7 +79,8 @@ q4_status q4_dequant(const uint32_t* qweight, const uint16_t* scales, const uint
 /* Path A of the same section (fused load / dequant / matmul, higher-precision
  * accumulation); W4A16 as in [YJ] §Notation (4-bit weights, 16-bit activations):
  *   y[m][n] = sum_k x[m][k] * S[n][k/g] * (u[n][k] - z[n][k/g])
- * x is [m][k] F16 or BF16; y is [m][n] fp32, accumulated in fp32.  m >= 1.
+ * x is [m][k] F16 or BF16; y is [m][n] fp32, accumulated in fp32.  m >= 1, and beyond
+ * the shared size rules k <= 2^22 and m*n <= 2^38 (Q4_ERR_SHAPE otherwise).
  * m <= 16 runs the decode GEMV kernel, larger m the prefill GEMM kernel. */
 q4_status q4_w4a16_gemm(const void* x, q4_dtype x_dtype, int64_t m,
                         const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros,

@@ -217,7 +217,12 @@ def test_gemv_edge_cases(m, n, k, g, xdtype, sym):
 @pytest.mark.parametrize("m", [1, 5, 16, 17, 64])
 @pytest.mark.parametrize("sym", [False, True])
 def test_linear_special_inputs(m, sym):
-    """x = 0 gives exactly 0; one-hot x picks one dequantized column exactly."""
+    """x = 0 gives exactly 0; one-hot x picks one dequantized column.  The decode GEMV
+    reproduces it exactly (exact products, one scale multiply per group).  The prefill
+    GEMM keeps its sums in units of the current group's scale and moves them to the next
+    group's units with an fp32 ratio: a column in group j passes through two roundings
+    (ratio, product) per later group and one final product, so its relative error is at
+    most (2 * (G - 1 - j) + 1) * 2^-24 to first order."""
     n, k, g = 48, 512, 64
     w = torch.from_numpy(pins.random_weights(5, n, k))
     p, _ = pack_guarded(w.to(DEV), g, sym)
@@ -233,7 +238,39 @@ def test_linear_special_inputs(m, sym):
     note(f"linear one-hot x m={m} sym={sym}")
     y, _ = run_linear(x, p)
     for i, kk in enumerate(cols):
-        assert np.array_equal(y[i].astype(np.float64), xhat[:, kk]), (i, kk)
+        if m <= 16:
+            assert np.array_equal(y[i].astype(np.float64), xhat[:, kk]), (i, kk)
+        else:
+            later = k // g - 1 - kk // g
+            bound = (2 * later + 1) * 2.0 ** -24 * (1 + 2.0 ** -20) * np.abs(xhat[:, kk])
+            assert np.all(np.abs(y[i].astype(np.float64) - xhat[:, kk]) <= bound), (i, kk)
+
+
+@pytest.mark.parametrize("m", [1, 16, 17, 300])
+@pytest.mark.parametrize("sym", [False, True])
+def test_linear_zero_scale_groups(m, sym):
+    """Packed weights from elsewhere may hold S = 0 for a group (a group of zeros stored
+    without the 1.0 substitute): such a group contributes exactly 0.  Zero scales sit at
+    the first, last and consecutive groups of some rows and cover whole rows of others."""
+    n, k, g = 200, 1024, 64
+    G = k // g
+    w = torch.from_numpy(pins.random_weights(11, n, k))
+    p, _ = pack_guarded(w.to(DEV), g, sym)
+    qo, so, zo = assert_pack_exact(p, host_input(w), g, sym)
+    so = so.copy()
+    rng = np.random.default_rng(12)
+    for r in range(0, n, 3):
+        so[r, rng.choice(G, size=3, replace=False)] = 0
+    so[1, 0] = so[2, G - 1] = 0
+    so[4, 3:9] = 0
+    so[5, :] = 0
+    so[n - 1, :] = 0
+    p.scales.copy_(torch.from_numpy(so.view(np.float16)).to(DEV))
+    x = synthetic.activations(m, k, seed=13)
+    note(f"linear zero-scale groups m={m} sym={sym}")
+    y, kname = run_linear(x, p)
+    assert np.all(y[:, 5] == 0) and np.all(y[:, n - 1] == 0)
+    assert_linear_close(y, host_input(x), (qo, so, zo), n, k, g, sym, what=kname)
 
 
 GEMM_CASES = [(17, 64, 256, 128), (130, 200, 384, 64), (300, 129, 96, 32), (256, 256, 1024, 128),
