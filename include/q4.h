@@ -80,7 +80,7 @@ q4_status q4_dequant(const uint32_t* qweight, const uint16_t* scales, const uint
  * accumulation); W4A16 as in [YJ] §Notation (4-bit weights, 16-bit activations):
  *   y[m][n] = sum_k x[m][k] * S[n][k/g] * (u[n][k] - z[n][k/g])
  * x is [m][k] F16 or BF16; y is [m][n] fp32, accumulated in fp32.  m >= 1, and beyond
- * the shared size rules k <= 2^22 and m*n <= 2^38 (Q4_ERR_SHAPE otherwise).
+ * the shared size rules k <= 2^22, n <= 2^25 and m*n <= 2^38 (Q4_ERR_SHAPE otherwise).
  * m <= 16 runs the decode GEMV kernel, larger m the prefill GEMM kernel. */
 q4_status q4_w4a16_gemm(const void* x, q4_dtype x_dtype, int64_t m,
                         const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros,

@@ -86,7 +86,7 @@ def _mm(x=A16, xd=BF16, m=1, qw=A16, sc=A16, zr=A16, n=16, k=256, g=128, sym=0, 
     (lambda: _mm(x=None), NULL), (lambda: _mm(y=None), NULL), (lambda: _mm(zr=None), NULL),
     (lambda: _mm(x=A16 + 2), ALIGN), (lambda: _mm(y=A16 + 2), ALIGN), (lambda: _mm(g=100), GROUP),
     (lambda: _mm(k=320, g=128), SHAPE), (lambda: _mm(k=(1 << 22) + 128), SHAPE),
-    (lambda: _mm(m=1 << 20, n=(1 << 18) + 1), SHAPE),
+    (lambda: _mm(m=1 << 20, n=(1 << 18) + 1), SHAPE), (lambda: _mm(n=(1 << 25) + 1, k=128), SHAPE),
 ])
 def test_host_validation_rejects_before_launch(call, code):
     assert call() == code

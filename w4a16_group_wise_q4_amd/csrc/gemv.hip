@@ -50,7 +50,8 @@ constexpr int kMS = 4;                 // scale entries per thread per tile (chu
 constexpr int kMZ = 2;                 // zero-point words per thread per tile (chunked kernel)
 constexpr int kPS = 8;                 // scale entries per thread per tile (streaming kernel)
 constexpr int kPZ = 2;                 // zero-point dwords per thread per tile (streaming kernel)
-constexpr int kOOB = 0x40000000;       // a buffer offset past every resource: reads 0
+constexpr int kOOB = 0x40000000;       // a buffer offset past every load resource: reads 0
+constexpr uint32_t kStoreOOB = 0xFFFFFFF0u;  // a store offset past the y resource: dropped
 
 // One lane's share of one 128-column unit: 4 packed words (one per MFMA).
 struct Unit {
@@ -125,14 +126,25 @@ __device__ __forceinline__ void unit_load(Unit& d, q4::rsrc rq, int qoff, int u,
 // ---------------------------------------------------------------------------------------
 // Streaming kernel (the activations fit in LDS): persistent workgroups, each wave runs one
 // continuous stream of D-unit batches over (tile, its K slice) with R batches in flight,
-// so the next tile's weights are in flight while the current tile is computed and reduced.
-// LDS: activations [(M+1)][RS] | metadata x2 | partial sums x2.
-template <int G, bool SYM, bool XF16, int R, int D, int MAXT, int MINW>
+// so the next tile's weights are in flight while the current one is computed and reduced.
+//
+// The hardware counts outstanding loads in issue order and a wait names how many may
+// remain in flight, so the stream stays overlapped only if every wait the compiler emits
+// is a static count.  Hence: no load and no LDS store of loaded data sits behind a
+// branch (lanes or batches with nothing to load use an offset past the buffer's end and
+// read zeros; lanes with nothing to store write a private spare slot), the batches of a
+// tile are a whole number of ring turns (nb % R == 0) so ring slots are static, and y
+// is written with buffer stores that every wave issues (off the end when not its turn).
+//
+// LDS (16-byte vectors): activations [(M+1)][RS] | metadata x2 (each with a spare area
+// of one dword per thread) | partial sums x2 ([S][64] each).
+template <int G, bool SYM, bool XF16, int R, int D, int MAXT, int MINW, bool MULTI>
 __global__ __launch_bounds__(MAXT, MINW) void gemv_stream_kernel(const uint16_t* __restrict__ x, int M,
                                                           const uint32_t* __restrict__ qweight,
                                                           const uint16_t* __restrict__ scales,
                                                           const uint32_t* __restrict__ zeros,
                                                           int N, int K, float* __restrict__ y) {
+    constexpr int LW = G / 32;
     extern __shared__ q4::u32x4 lds[];
     const int tid = threadIdx.x, nthreads = blockDim.x;
     const int lane = tid & 63;
@@ -143,12 +155,13 @@ __global__ __launch_bounds__(MAXT, MINW) void gemv_stream_kernel(const uint16_t*
     const int tiles = (N + 15) / 16;
     const int RS = KW + 1;
     const int xs_end = (M + 1) * RS;
-    const int s_ent = 16 * n_groups;     // scale entries of a tile (16 rows, contiguous)
-    const int s_dw = 8 * n_groups;       // ... in dwords (the zero block starts after them)
+    const int s_ent = 16 * n_groups;       // scale entries of a tile (16 rows, contiguous)
+    const int s_dw = 8 * n_groups;         // ... in dwords (the zero block starts after them)
     const int z_dw = SYM ? 0 : 16 * zwords;
     const int meta_vec = (s_dw + z_dw + 3) / 4;
+    const int mbuf = meta_vec + nthreads / 4;  // one metadata copy plus its spare dwords
     uint32_t* meta0 = reinterpret_cast<uint32_t*>(lds + xs_end);
-    q4::f32x4* red0 = reinterpret_cast<q4::f32x4*>(lds + xs_end + 2 * meta_vec);
+    q4::f32x4* red0 = reinterpret_cast<q4::f32x4*>(lds + xs_end + 2 * mbuf);
     const q4::u32x4* xs = lds + (col < M ? col : M) * RS;  // padding lanes: zero row
 
     const uint32_t kMask = q4::vreg_const(0x000F000Fu);
@@ -159,18 +172,21 @@ __global__ __launch_bounds__(MAXT, MINW) void gemv_stream_kernel(const uint16_t*
     const int u0 = wave * per;
     const int u1 = u0 + per < units ? u0 + per : units;
     const int ulast = u1 > u0 ? u1 - 1 : 0;
-    const int nb = (per + D - 1) / D;  // batches per tile
-    const int ntiles = tiles > (int)blockIdx.x ? (tiles - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
-    const int total = ntiles * nb;               // batches in this wave's stream
+    const int nb = R * ((per + D * R - 1) / (D * R));  // batches per tile, whole ring turns
+    // grid <= tiles; MULTI == false means grid == tiles (one tile per workgroup)
+    const int ntiles = MULTI ? (tiles - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 1;
 
-    auto tile_of = [&](int i) { return (int)blockIdx.x + (i / nb) * (int)gridDim.x; };
+    auto tile_n0 = [&](int tl) { return ((int)blockIdx.x + tl * (int)gridDim.x) * 16; };
 
-    // metadata of tile t: scales block (16*n_groups fp16, copied entry by entry so no
-    // load straddles the end of the array) then zero block (16*zwords dwords)
-    auto meta_load = [&](int t, uint32_t (&mv)[kPS + kPZ]) {
-        const int n0 = t * 16;
-        const int rows = N - n0 < 16 ? N - n0 : 16;
-        const q4::rsrc rs = q4::make_rsrc(scales + (int64_t)n0 * n_groups, (uint32_t)rows * n_groups * 2u);
+    // metadata of tile ordinal tl (none for tl >= ntiles: every offset off the end): scales
+    // block (16*n_groups fp16, copied entry by entry so no load straddles the end of the
+    // array) then zero block (16*zwords dwords)
+    auto meta_load = [&](int tl, uint32_t (&mv)[kPS + kPZ]) {
+        const int n0 = tile_n0(tl);
+        int rows = N - n0 < 16 ? N - n0 : 16;
+        rows = tl < ntiles ? rows : 0;
+        const q4::rsrc rs = q4::make_rsrc(scales + (int64_t)(tl < ntiles ? n0 : 0) * n_groups,
+                                          (uint32_t)rows * n_groups * 2u);
 #pragma unroll
         for (int j = 0; j < kPS; ++j) {
             const int e = j * nthreads + tid;
@@ -181,42 +197,42 @@ __global__ __launch_bounds__(MAXT, MINW) void gemv_stream_kernel(const uint16_t*
             if constexpr (SYM) {
                 mv[kPS + j] = 0u;
             } else {
-                const q4::rsrc rz = q4::make_rsrc(zeros + (int64_t)n0 * zwords, (uint32_t)rows * zwords * 4u);
+                const q4::rsrc rz = q4::make_rsrc(zeros + (int64_t)(tl < ntiles ? n0 : 0) * zwords,
+                                                  (uint32_t)rows * zwords * 4u);
                 const int e = j * nthreads + tid;
                 mv[kPS + j] = q4::buf_load_x1(rz, e < z_dw ? e * 4 : kOOB, 0);
             }
         }
     };
     auto meta_store = [&](uint32_t* dst, const uint32_t (&mv)[kPS + kPZ]) {
+        uint16_t* d16 = reinterpret_cast<uint16_t*>(dst);
+        const int spare = 4 * meta_vec + tid;  // this thread's spare dword
 #pragma unroll
         for (int j = 0; j < kPS; ++j) {
             const int e = j * nthreads + tid;
-            if (e < s_ent) reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)mv[j];
+            d16[e < s_ent ? e : 2 * spare] = (uint16_t)mv[j];
         }
 #pragma unroll
         for (int j = 0; j < kPZ; ++j) {
             const int e = j * nthreads + tid;
-            if (e < z_dw) dst[s_dw + e] = mv[kPS + j];
+            dst[e < z_dw ? s_dw + e : spare] = mv[kPS + j];
         }
     };
-    // issue the 4 units of stream batch i
-    auto batch_load = [&](Unit (&bf)[D], int i) {
-        const int t = tile_of(i);
-        const int b = i - (i / nb) * nb;
-        const int n0 = t * 16;
+    // issue batch b of tile ordinal tl (a batch past the end of the stream reads nothing)
+    auto batch_load = [&](Unit (&bf)[D], int tl, int b) {
+        const int n0 = tile_n0(tl < ntiles ? tl : 0);
         const int rows = N - n0 < 16 ? N - n0 : 16;
         const q4::rsrc rq = q4::make_rsrc(qweight + (int64_t)n0 * KW, (uint32_t)rows * KW * 4u);
-        const int qoff = col < rows ? col * KW * 4 + c * (G / 32) * 4 : kOOB;
+        const int qoff = col < rows && tl < ntiles ? col * KW * 4 + c * LW * 4 : kOOB;
 #pragma unroll
         for (int j = 0; j < D; ++j) {
             const int u = u0 + b * D + j;
-            unit_load<G>(bf[j], rq, qoff, u < u1 ? u : ulast, KW);
+            unit_load<G>(bf[j], rq, u < u1 ? qoff : kOOB, u < u1 ? u : ulast, KW);
         }
     };
 
     q4::f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    auto batch_compute = [&](const Unit (&bf)[D], int i, const uint32_t* meta) {
-        const int b = i - (i / nb) * nb;
+    auto batch_compute = [&](const Unit (&bf)[D], int b, const uint32_t* meta) {
         const uint16_t* s_row = reinterpret_cast<const uint16_t*>(meta) + col * n_groups;
         const uint32_t* z_row = meta + s_dw + col * zwords;
 #pragma unroll
@@ -224,7 +240,7 @@ __global__ __launch_bounds__(MAXT, MINW) void gemv_stream_kernel(const uint16_t*
             const int u = u0 + b * D + j;
             const bool ok = u < u1;
             const int ue = ok ? u : ulast;
-            unit_mac<G, SYM, XF16>(acc, bf[j], xs, ue * 16, s_row, z_row, ue * (4 / (G / 32)), ok,
+            unit_mac<G, SYM, XF16>(acc, bf[j], xs, ue * 16, s_row, z_row, ue * (4 / LW), ok,
                                    c, kMask, kBias, KW - ue * 16);
         }
     };
@@ -233,72 +249,86 @@ __global__ __launch_bounds__(MAXT, MINW) void gemv_stream_kernel(const uint16_t*
     Unit buf[R][D];
     {
         q4::u32x4 xv[kStage];
-        const int nvec = xs_end;
+        const q4::rsrc rx = q4::make_rsrc(x, (uint32_t)M * K * 2u);
 #pragma unroll
         for (int j = 0; j < kStage; ++j) {
             const int v = j * nthreads + tid;
             const int m = v / RS, jj = v - m * RS;
-            const bool real = v < nvec && m < M && jj < KW;
-            xv[j] = q4::buf_load_x4(q4::make_rsrc(x, (uint32_t)M * K * 2u), real ? (m * K + 8 * jj) * 2 : kOOB, 0);
+            const bool real = v < xs_end && m < M && jj < KW;
+            xv[j] = q4::buf_load_x4(rx, real ? (m * K + 8 * jj) * 2 : kOOB, 0);
         }
+        // issue order is wait order: activations (cache-hot), metadata, then the weight
+        // ring, so staging the first two never waits for the weights
+        __builtin_amdgcn_sched_barrier(0);
         uint32_t mv[kPS + kPZ];
-        if (ntiles > 0) meta_load(tile_of(0), mv);
+        meta_load(0, mv);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int r = 0; r < R; ++r)
-            if (r < total) batch_load(buf[r], r);
+        for (int r = 0; r < R; ++r) batch_load(buf[r], 0, r);  // R <= nb
+        __builtin_amdgcn_sched_barrier(0);
+        q4::u32x4* spare = reinterpret_cast<q4::u32x4*>(red0) + tid;  // unused until tile 0 ends
 #pragma unroll
         for (int j = 0; j < kStage; ++j) {
             const int v = j * nthreads + tid;
-            if (v < nvec) lds[v] = q4::pair_perm(xv[j]);
+            *(v < xs_end ? lds + v : spare) = q4::pair_perm(xv[j]);
         }
-        for (int v0 = kStage * nthreads; v0 < nvec; v0 += nthreads) {  // larger m*k only
+        for (int v0 = kStage * nthreads; v0 < xs_end; v0 += nthreads) {  // larger m*k only
             const int v = v0 + tid;
             const int m = v / RS, jj = v - m * RS;
-            const bool real = v < nvec && m < M && jj < KW;
-            const q4::u32x4 t = q4::buf_load_x4(q4::make_rsrc(x, (uint32_t)M * K * 2u),
-                                                real ? (m * K + 8 * jj) * 2 : kOOB, 0);
-            if (v < nvec) lds[v] = q4::pair_perm(t);
+            const bool real = v < xs_end && m < M && jj < KW;
+            const q4::u32x4 t = q4::buf_load_x4(rx, real ? (m * K + 8 * jj) * 2 : kOOB, 0);
+            *(v < xs_end ? lds + v : spare) = q4::pair_perm(t);
         }
-        if (ntiles > 0) meta_store(meta0, mv);
+        meta_store(meta0, mv);
     }
     __syncthreads();
 
-    uint32_t mnext[kPS + kPZ];
-    // ---- the stream
-    auto step = [&](Unit (&bf)[D], int i) {
-        const int tl = i / nb;                 // tile ordinal within this workgroup
-        const int b = i - tl * nb;
-        const uint32_t* meta = meta0 + (tl & 1) * 4 * meta_vec;
-        if (b == 0 && tl + 1 < ntiles) meta_load(tile_of(i + nb), mnext);
-        batch_compute(bf, i, meta);
-        if (i + R < total) batch_load(bf, i + R);
-        if (b == nb - 1) {  // tile done: publish partial sums, next metadata; one barrier
-            q4::f32x4* red = red0 + (tl & 1) * 64 * S;
-            red[wave * 64 + lane] = acc;
-            acc = q4::f32x4{0.f, 0.f, 0.f, 0.f};
-            if (tl + 1 < ntiles) meta_store(meta0 + ((tl + 1) & 1) * 4 * meta_vec, mnext);
-            __syncthreads();
-            const int t = tile_of(i);
-            const int n0 = t * 16;
-            if (wave == tl % S && n0 + col < N) {  // rotating finisher wave
-                q4::f32x4 sum = red[lane];
-                for (int w = 1; w < S; ++w) {
-                    const q4::f32x4 r = red[w * 64 + lane];
+    const q4::rsrc ry = q4::make_rsrc(y, (uint32_t)M * (uint32_t)N * 4u);
+    for (int tl = 0; tl < ntiles; ++tl) {
+        uint32_t mnext[kPS + kPZ];
+        // next tile's metadata.  Its loads sit behind the ring's, so the first wait of the
+        // tile also covers them; a one-tile grid has nothing to fetch and skips them.
+        if constexpr (MULTI) meta_load(tl + 1, mnext);
+        const uint32_t* meta = meta0 + (tl & 1) * 4 * mbuf;
+        int b = 0;
+        do {
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) sum[q] += r[q];
-                }
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int m = 4 * c + q;
-                    if (m < M) y[(int64_t)m * N + n0 + col] = sum[q];
-                }
+            for (int r = 0; r < R; ++r) {
+                batch_compute(buf[r], b + r, meta);
+                const int nx = b + r + R;          // the batch that refills this slot
+                const bool wrap = nx >= nb;
+                batch_load(buf[r], wrap ? tl + 1 : tl, wrap ? nx - nb : nx);
+                // keep the refill right behind the compute that frees its registers, so
+                // loads are issued as early as the ring allows
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            b += R;
+        } while (b < nb);
+        // tile done: publish partial sums and the next tile's metadata; one barrier
+        q4::f32x4* red = red0 + (tl & 1) * 64 * S;
+        red[wave * 64 + lane] = acc;
+        acc = q4::f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (MULTI) meta_store(meta0 + ((tl + 1) & 1) * 4 * mbuf, mnext);
+        __syncthreads();
+        const int n0 = tile_n0(tl);
+        const bool fin = wave == tl % S;  // rotating finisher wave
+        float sum[4] = {0.f, 0.f, 0.f, 0.f};  // a plain array: see f32_bits
+        if (fin) {
+            for (int w = 0; w < S; ++w) {
+                const q4::f32x4 t = red[w * 64 + lane];
+                sum[0] += t.x;
+                sum[1] += t.y;
+                sum[2] += t.z;
+                sum[3] += t.w;
             }
         }
-    };
-    for (int i = 0; i < total; i += R) {
 #pragma unroll
-        for (int r = 0; r < R; ++r)
-            if (i + r < total) step(buf[r], i + r);
+        for (int q = 0; q < 4; ++q) {
+            const int m = 4 * c + q;
+            const bool st = fin && m < M && n0 + col < N;
+            const uint32_t off = st ? ((uint32_t)m * (uint32_t)N + (uint32_t)(n0 + col)) * 4u : kStoreOOB;
+            __builtin_amdgcn_raw_buffer_store_b32(q4::f32_bits(sum[q]), ry, (int)off, 0, 0);
+        }
     }
 }
 
@@ -477,14 +507,14 @@ hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16
             g_num_cus <= 0)
             g_num_cus = 256;
     }
-    // Workgroup shape.  With tiles to spare (at least two per CU): 4-wave workgroups with
-    // 4-unit batches, three batches in flight, several workgroups resident per CU.  With
-    // at most one tile per CU the whole matrix is requested at once and the time after the
-    // data arrives dominates, so the tile is spread over up to 16 waves of 2-unit batches.
-    // Otherwise 8 waves of 4-unit batches.
+    // Workgroup shape.  With tiles to spare (at least two per CU): 4-wave workgroups,
+    // several resident per CU, two batches in flight per wave.  With at most one tile per
+    // CU the whole matrix is requested at once and the time after the data arrives
+    // dominates, so the tile is spread over up to 16 waves of 2-unit batches.  Otherwise
+    // 8 waves of 2-unit batches.
     const int units_k = (k + 127) / 128;
     const int tiles = (n + 15) / 16;
-    int shape;  // 0: 8 waves, D=4, R=2   1: 4 waves, D=4, R=3   2: up to 16 waves, D=2, R=2
+    int shape;  // 0: up to 8 waves   1: up to 4 waves   2: up to 16 waves
     int waves;
     if (tiles >= 2 * g_num_cus) {
         shape = 1;
@@ -504,8 +534,8 @@ hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16
     // streaming kernel when the activations (plus zero row), two metadata copies and two
     // sets of partial sums fit, and a tile's metadata fits the per-thread copy
     const int meta_vec = (8 * ng + (SYM ? 0 : 16 * zw) + 3) / 4;
-    auto stream_lds = [&](int w) {
-        return (size_t)((m + 1) * (k / 8 + 1) + 2 * meta_vec + 2 * w * 64) * 16;
+    auto stream_lds = [&](int w) {  // activations, 2 x (metadata + spare dwords), 2 x partial sums
+        return (size_t)((m + 1) * (k / 8 + 1) + 2 * (meta_vec + 16 * w) + 2 * w * 64) * 16;
     };
     auto stream_fits = [&](int w) {
         return stream_lds(w) <= (size_t)kLdsBudget && 16 * ng <= kPS * 64 * w &&
@@ -521,37 +551,59 @@ hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16
     const int threads = 64 * waves;
     const size_t lds_stream = stream_lds(waves);
     if (stream) {
-        auto run = [&](auto kern, const char* name) {
-            static int cached_threads = -1, cached_per_cu = 1;
-            static size_t cached_lds = 0;
+        // Workgroups resident per CU for a kernel at this shape (cached per kernel and
+        // thread).  When every tile gets its own workgroup the one-tile form runs (no
+        // metadata prefetch for a next tile); otherwise persistent workgroups take turns.
+        auto per_cu = [&](auto kern) {
+            thread_local int cached_threads = -1, cached = 1;
+            thread_local size_t cached_lds = 0;
             if (cached_threads != threads || cached_lds != lds_stream) {
-                int per_cu = 0;
-                if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, lds_stream) != hipSuccess ||
-                    per_cu < 1)
-                    per_cu = 1;
+                int v = 0;
+                if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kern, threads, lds_stream) != hipSuccess || v < 1)
+                    v = 1;
                 cached_threads = threads;
                 cached_lds = lds_stream;
-                cached_per_cu = per_cu;
+                cached = v;
             }
-            const int cap = g_num_cus * cached_per_cu;
-            const int grid = tiles < cap ? tiles : cap;
+            return cached;
+        };
+        auto run = [&](auto k_multi, auto k_one, const char* name) {
+            const int cap = g_num_cus * per_cu(k_multi);
             *kname = name;
-            hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds_stream, st, xp, m, qw, sc, zr, n, k, y);
+            if (tiles <= cap)
+                hipLaunchKernelGGL(k_one, dim3(tiles), dim3(threads), lds_stream, st, xp, m, qw, sc, zr, n, k, y);
+            else
+                hipLaunchKernelGGL(k_multi, dim3(cap), dim3(threads), lds_stream, st, xp, m, qw, sc, zr, n, k, y);
             return hipGetLastError();
         };
-        constexpr int R1 = G == 128 ? 3 : 2;
+        // A tile's batches are whole ring turns (D units per batch, R batches in flight);
+        // pick the batch size that leaves the fewest idle unit slots in a wave's slice.
+        const int per = (units_k + waves - 1) / waves;
+        const bool wide = 8 * ((per + 7) / 8) - per <= 4 * ((per + 3) / 4) - per;
         if (shape == 1) {
-            if (xd == 1) return run(gemv_stream_kernel<G, SYM, true, R1, 4, 256, 2>, "q4_gemv_mfma_f16");
-            return run(gemv_stream_kernel<G, SYM, false, R1, 4, 256, 2>, "q4_gemv_mfma_bf16");
+            if (wide) {
+                if (xd == 1) return run(gemv_stream_kernel<G, SYM, true, 2, 4, 256, 2, true>,
+                                        gemv_stream_kernel<G, SYM, true, 2, 4, 256, 2, false>, "q4_gemv_mfma_f16");
+                return run(gemv_stream_kernel<G, SYM, false, 2, 4, 256, 2, true>,
+                           gemv_stream_kernel<G, SYM, false, 2, 4, 256, 2, false>, "q4_gemv_mfma_bf16");
+            }
+            if (xd == 1) return run(gemv_stream_kernel<G, SYM, true, 2, 2, 256, 2, true>,
+                                    gemv_stream_kernel<G, SYM, true, 2, 2, 256, 2, false>, "q4_gemv_mfma_f16");
+            return run(gemv_stream_kernel<G, SYM, false, 2, 2, 256, 2, true>,
+                       gemv_stream_kernel<G, SYM, false, 2, 2, 256, 2, false>, "q4_gemv_mfma_bf16");
         }
         if constexpr (G >= 64) {
-            if (shape == 2) {
-                if (xd == 1) return run(gemv_stream_kernel<G, SYM, true, 2, 2, 1024, 1>, "q4_gemv_mfma_f16");
-                return run(gemv_stream_kernel<G, SYM, false, 2, 2, 1024, 1>, "q4_gemv_mfma_bf16");
+            if (shape == 2) {  // tiles <= CUs: always one tile per workgroup
+                if (xd == 1) return run(gemv_stream_kernel<G, SYM, true, 1, 2, 1024, 1, true>,
+                                        gemv_stream_kernel<G, SYM, true, 1, 2, 1024, 1, false>, "q4_gemv_mfma_f16");
+                return run(gemv_stream_kernel<G, SYM, false, 1, 2, 1024, 1, true>,
+                           gemv_stream_kernel<G, SYM, false, 1, 2, 1024, 1, false>, "q4_gemv_mfma_bf16");
             }
         }
-        if (xd == 1) return run(gemv_stream_kernel<G, SYM, true, 2, 4, 512, 1>, "q4_gemv_mfma_f16");
-        return run(gemv_stream_kernel<G, SYM, false, 2, 4, 512, 1>, "q4_gemv_mfma_bf16");
+        if (xd == 1) return run(gemv_stream_kernel<G, SYM, true, 2, 2, 512, 1, true>,
+                                gemv_stream_kernel<G, SYM, true, 2, 2, 512, 1, false>, "q4_gemv_mfma_f16");
+        return run(gemv_stream_kernel<G, SYM, false, 2, 2, 512, 1, true>,
+                   gemv_stream_kernel<G, SYM, false, 2, 2, 512, 1, false>, "q4_gemv_mfma_bf16");
     }
     auto lds_bytes = [&](int kc) {
         const int cg = (kc + G - 1) / G, czw = (cg + 7) / 8;

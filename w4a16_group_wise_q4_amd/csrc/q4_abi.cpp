@@ -19,9 +19,12 @@ thread_local const char* g_last_kernel = "";
 constexpr int64_t kMaxElems = int64_t(1) << 40;
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
 // The matmul kernels address one tile's activations (up to 256 rows of k bf16 values)
-// and its output grid with 32-bit offsets: k <= 2^22 and m*n <= 2^38 keep both in range.
+// and their outputs with 32-bit offsets: k <= 2^22, n <= 2^25 and m*n <= 2^38 keep every
+// offset in range.
 constexpr int64_t kMaxMatmulK = int64_t(1) << 22;
 constexpr int64_t kMaxMatmulOut = int64_t(1) << 38;
+// The GEMV addresses y (at most 16 rows of n fp32) with 32-bit buffer offsets.
+constexpr int64_t kMaxMatmulN = int64_t(1) << 25;
 
 bool group_ok(int32_t g) { return g == 32 || g == 64 || g == 128; }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -87,7 +90,7 @@ q4_status q4_w4a16_gemm(const void* x, q4_dtype x_dtype, int64_t m, const uint32
                         int32_t group_size, int32_t symmetric, float* y, hipStream_t stream) {
     q4_status st = check_layout(n, k, group_size);
     if (st != Q4_OK) return st;
-    if (k > kMaxMatmulK) return Q4_ERR_SHAPE;
+    if (k > kMaxMatmulK || n > kMaxMatmulN) return Q4_ERR_SHAPE;
     if (m < 1 || m > kMaxDim || m > kMaxElems / k || m > kMaxMatmulOut / n) return Q4_ERR_SHAPE;
     if (x_dtype != Q4_F16 && x_dtype != Q4_BF16) return Q4_ERR_DTYPE;
     if (!x || !y) return Q4_ERR_NULL;

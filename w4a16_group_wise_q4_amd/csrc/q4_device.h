@@ -84,6 +84,11 @@ __device__ __forceinline__ u32x4 pair_perm(u32x4 x) {
     return r;
 }
 
+// Bits of an fp32 value.  Callers pass plain floats: with this compiler, bit-casting an
+// element v[i] of an ext_vector_type (directly or after inlining, when v is updated element
+// by element) has produced element 0 for every i.
+__device__ __forceinline__ uint32_t f32_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
+
 __device__ __forceinline__ float f16_bits_to_float(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
 }
