@@ -17,8 +17,11 @@
 //   run of 4*g bytes of qweight.  The 8 zero points are OR-combined across the wave.
 //
 // Arithmetic is IEEE fp32 in the order written (no contraction, correctly rounded
-// division, round-half-to-even via rintf), so codes, scales and zero points are
-// bit-identical to the plain CPU definition.
+// divisions for the scale and zero point, round-half-to-even), so codes, scales and zero
+// points are bit-identical to the plain CPU definition.  The per-weight quotient w/S of
+// 16-bit weights comes from a reciprocal and one FMA correction whose rounded value equals
+// that of the IEEE quotient for every reachable (w, S) pair, a property checked
+// exhaustively by the test suite; fp32 weights use the IEEE division itself.
 #include "q4_device.h"
 
 #pragma clang fp contract(off)
@@ -131,11 +134,35 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(const void* __restrict_
     uint32_t packed[(E + 7) / 8];
 #pragma unroll
     for (int j = 0; j < (E + 7) / 8; ++j) packed[j] = 0;
+    if constexpr (DT == 0) {
+        // fp32 weights: the IEEE quotient, element by element
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const float qf = fminf(fmaxf(rintf(v[e] / S) + zf, q_min), q_max);
-        const uint32_t u = (uint32_t)((int)qf + (SYM ? 8 : 0));
-        packed[e / 8] |= u << (4 * (e % 8));
+        for (int e = 0; e < E; ++e) {
+            const float qf = fminf(fmaxf(rintf(v[e] / S) + zf, q_min), q_max);
+            const uint32_t u = (uint32_t)((int)qf + (SYM ? 8 : 0));
+            packed[e / 8] |= u << (4 * (e % 8));
+        }
+    } else {
+        // 16-bit weights: one correctly rounded reciprocal per group and one FMA
+        // correction per weight.  For every finite fp16 scale S and every finite bf16 or
+        // fp16 weight v with |v/S| <= 64, rint of the corrected quotient equals rint of
+        // the IEEE quotient v/S (checked exhaustively; a group's own weights always have
+        // |v/S| < 23 unless S saturated at 65504, where the quotient stays finite and
+        // the code clamps the same way).  Rounding to an integer is the 1.5 * 2^23
+        // addition (exact round-half-to-even for |q| <= 64), then z is added and the
+        // code clamped to [0, 15] in integers.
+        const float y = 1.0f / S;
+        const int zi = SYM ? 8 : (int)zf;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float q0 = v[e] * y;
+            const float r = __builtin_fmaf(-q0, S, v[e]);
+            float q = __builtin_fmaf(r, y, q0);
+            q = __builtin_amdgcn_fmed3f(q, -64.0f, 64.0f);
+            const int qi = (int)(__builtin_bit_cast(uint32_t, q + 12582912.0f) - 0x4B400000u);
+            const int u = min(max(qi + zi, 0), 15);
+            packed[e / 8] |= (uint32_t)u << (4 * (e % 8));
+        }
     }
 
     if (valid) {
