@@ -121,6 +121,50 @@ def test_quant_edge_cases(n, k, g, dtype, sym):
     assert_pack_exact(p, host_input(w), g, sym)
 
 
+def scale_tie_rows(dtype, count=64, g=32):
+    """Rows of asymmetric groups whose fp32 scale (x_max - x_min) / 15 lies exactly halfway
+    between two fp16 values, so the stored scale depends on rounding to fp32 first and then
+    to fp16 with ties to even.  Each group holds x_max = a > 0 and x_min = -b <= 0 with
+    a + b = 15 * m, m an fp16 midpoint; a and b are representable in the weight dtype."""
+    rng = np.random.default_rng(21)
+    rows = []
+    while len(rows) < count:
+        h = int(rng.integers(0x1400, 0x5800))            # fp16 bits: normal range
+        lo = np.array([h], dtype=np.uint16).view(np.float16).astype(np.float64)[0]
+        hi = np.array([h + 1], dtype=np.uint16).view(np.float16).astype(np.float64)[0]
+        m = (lo + hi) / 2                                 # exact in fp64 and in fp32
+        T = np.float32(15 * m)
+        if float(T) != 15 * m:
+            continue
+        a = torch.tensor([float(T)], dtype=torch.float32).to(dtype).float().item()
+        if a > float(T):
+            a = float(np.nextafter(np.float32(a), np.float32(0)))
+            a = torch.tensor([a], dtype=torch.float32).to(dtype).float().item()
+        b = float(T) - a
+        if b < 0 or torch.tensor([b]).to(dtype).float().item() != b or a <= 0:
+            continue
+        if float(np.float32(a) + np.float32(b)) != float(T):
+            continue
+        grp = np.zeros(g, dtype=np.float32)
+        grp[0], grp[1] = a, -b
+        grp[2:] = np.float32(a) * rng.uniform(0.0, 1.0, g - 2).astype(np.float32)  # inside [-b, a]
+        rows.append(grp)
+    return torch.from_numpy(np.stack(rows)).to(dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16, torch.bfloat16])
+def test_quant_scale_ties(dtype):
+    """Scales exactly on an fp16 rounding tie: the stored scale is the double rounding
+    (fp32, then fp16 ties-to-even) of the definition, never a single rounding of the
+    exact quotient."""
+    w = scale_tie_rows(dtype)
+    note(f"quant scale ties {dtype}")
+    p, bufs = pack_guarded(w.to(DEV), 32, False)
+    torch.cuda.synchronize()
+    check_guards(bufs, False)
+    assert_pack_exact(p, host_input(w), 32, False)
+
+
 # ----------------------------------------------------------------------------- dequant
 
 @pytest.mark.parametrize("g,sym", [(32, False), (64, True), (128, False), (128, True)])

@@ -28,40 +28,64 @@
 
 namespace {
 
+// x / d for d = 15 or 7 from the correctly rounded reciprocal and one FMA correction: equal to
+// the IEEE quotient for every finite non-negative fp32 x (checked exhaustively).
+template <int D>
+__device__ __forceinline__ float div_const(float x) {
+    constexpr float c = 1.0f / (float)D;
+    const float q0 = x * c;
+    const float r = __builtin_fmaf(-q0, (float)D, x);
+    return __builtin_fmaf(r, c, q0);
+}
+
+// The quotient v / S for a 16-bit weight v and a stored fp16 scale S, given y = 1/S
+// (correctly rounded): rounds to the same integer as the IEEE quotient wherever a group's
+// weights can land (checked exhaustively over all fp16 scales and 16-bit weights), clamped
+// to [-64, 64], which leaves every code unchanged.
+__device__ __forceinline__ float quot16(float v, float S, float y) {
+    const float q0 = v * y;
+    const float r = __builtin_fmaf(-q0, S, v);
+    return __builtin_amdgcn_fmed3f(__builtin_fmaf(r, y, q0), -64.0f, 64.0f);
+}
+
+// round-half-to-even of q (|q| <= 64) as an integer: the 1.5 * 2^23 addition
+__device__ __forceinline__ int rne_small(float q) {
+    return (int)(__builtin_bit_cast(uint32_t, q + 12582912.0f) - 0x4B400000u);
+}
+
+// One lane's E consecutive weights at byte offset off of the row resource (zeros past it).
 template <int E, int DT>
-__device__ __forceinline__ void load_group_slice(const void* base, int64_t elem_off, float (&v)[E]) {
+__device__ __forceinline__ void load_slice(q4::rsrc r, uint32_t off, float (&v)[E]) {
     if constexpr (DT == 0) {
-        const float* p = reinterpret_cast<const float*>(base) + elem_off;
-        if constexpr (E % 4 == 0) {
 #pragma unroll
-            for (int i = 0; i < E / 4; ++i) {
-                float4 t = reinterpret_cast<const float4*>(p)[i];
-                v[4 * i + 0] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
-            }
+        for (int i = 0; i < E / 4; ++i) {
+            // bit-cast the whole vector, then read elements (see f32_bits)
+            const q4::f32x4 t = __builtin_bit_cast(q4::f32x4, q4::buf_load_x4(r, (int)(off + 16u * i), 0));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[4 * i + j] = t[j];
         }
     } else {
-        const uint16_t* p = reinterpret_cast<const uint16_t*>(base) + elem_off;
         uint32_t words[E / 2];
         if constexpr (E >= 8) {
 #pragma unroll
             for (int i = 0; i < E / 8; ++i) {
-                q4::u32x4 t = reinterpret_cast<const q4::u32x4*>(p)[i];
-                words[4 * i + 0] = t[0]; words[4 * i + 1] = t[1];
-                words[4 * i + 2] = t[2]; words[4 * i + 3] = t[3];
+                const q4::u32x4 t = q4::buf_load_x4(r, (int)(off + 16u * i), 0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) words[4 * i + j] = t[j];
             }
         } else {
-            q4::u32x2 t = *reinterpret_cast<const q4::u32x2*>(p);
-            words[0] = t[0]; words[1] = t[1];
+            const q4::u32x2 t = q4::buf_load_x2(r, (int)off, 0);
+            words[0] = t[0];
+            words[1] = t[1];
         }
 #pragma unroll
         for (int i = 0; i < E / 2; ++i) {
-            uint16_t lo = (uint16_t)(words[i] & 0xFFFFu), hi = (uint16_t)(words[i] >> 16);
             if constexpr (DT == 2) {  // bf16: the upper half of an fp32
-                v[2 * i] = __builtin_bit_cast(float, (uint32_t)lo << 16);
-                v[2 * i + 1] = __builtin_bit_cast(float, (uint32_t)hi << 16);
+                v[2 * i] = __builtin_bit_cast(float, words[i] << 16);
+                v[2 * i + 1] = __builtin_bit_cast(float, words[i] & 0xFFFF0000u);
             } else {                  // fp16
-                v[2 * i] = (float)__builtin_bit_cast(_Float16, lo);
-                v[2 * i + 1] = (float)__builtin_bit_cast(_Float16, hi);
+                v[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(words[i] & 0xFFFFu));
+                v[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(words[i] >> 16));
             }
         }
     }
@@ -70,139 +94,150 @@ __device__ __forceinline__ void load_group_slice(const void* base, int64_t elem_
 __device__ __forceinline__ float xor_max(float v, int m) { return fmaxf(v, __shfl_xor(v, m, 64)); }
 __device__ __forceinline__ float xor_min(float v, int m) { return fminf(v, __shfl_xor(v, m, 64)); }
 
+// Persistent waves: wave gw starts at (row r0, zero word z0) = (gw / Z, gw % Z) and steps
+// by R rows and Z zero words, so every (row, zero word) task is done exactly once.
 template <int G, bool SYM, int DT>
-__global__ __launch_bounds__(256) void quant_pack_kernel(const void* __restrict__ w, int64_t k,
+__global__ __launch_bounds__(256) void quant_pack_kernel(const void* __restrict__ w, int n, int k,
                                                          uint32_t* __restrict__ qweight,
                                                          uint16_t* __restrict__ scales,
-                                                         uint32_t* __restrict__ zeros,
-                                                         int64_t tasks) {
-    constexpr int E = G / 8;  // weights per lane
+                                                         uint32_t* __restrict__ zeros, int R, int Z) {
+    constexpr int E = G / 8;                // weights per lane
+    constexpr uint32_t EB = DT == 0 ? 4 : 2;  // bytes per weight
+    constexpr uint32_t kOff = 0xFFFFFFF0u;   // an offset past every resource
     const int lane = threadIdx.x & 63;
-    const int64_t task = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    if (task >= tasks) return;  // wave-uniform
-    const int64_t n_groups = k / G;
-    const int64_t zwords = (n_groups + 7) >> 3;
-    const int64_t row = task / zwords;
-    const int64_t zw = task - row * zwords;
+    const int gw = (int)blockIdx.x * (int)(blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r0 = gw / Z, z0 = gw - r0 * Z;
+    if (r0 >= R) return;  // wave-uniform: the few waves past R * Z
+    const int n_groups = k / G;
+    const int zwords = (n_groups + 7) >> 3;
     const int grp = lane >> 3;
     const int t = lane & 7;
-    const int64_t gidx = zw * 8 + grp;
-    const bool valid = gidx < n_groups;
-    const int64_t elem_off = row * k + gidx * G + (int64_t)t * E;
 
-    float v[E];
-    if (valid) {
-        load_group_slice<E, DT>(w, elem_off, v);
-    } else {
-#pragma unroll
-        for (int e = 0; e < E; ++e) v[e] = 0.0f;
-    }
+    for (int row = r0; row < n; row += R) {
+        const q4::rsrc rw = q4::make_rsrc(reinterpret_cast<const char*>(w) + (int64_t)row * k * EB,
+                                          (uint32_t)k * EB);
+        const q4::rsrc rq = q4::make_rsrc(qweight + (int64_t)row * (k / 8), (uint32_t)k / 2u);
+        const q4::rsrc rs = q4::make_rsrc(scales + (int64_t)row * n_groups, (uint32_t)n_groups * 2u);
+        const q4::rsrc rz = q4::make_rsrc(zeros + (int64_t)row * zwords, (uint32_t)zwords * 4u);
+        for (int zw = z0; zw < zwords; zw += Z) {
+            const int gidx = zw * 8 + grp;
+            const bool valid = gidx < n_groups;
+            const uint32_t elem = (uint32_t)gidx * G + (uint32_t)t * E;  // within the row
+            float v[E];
+            load_slice<E, DT>(rw, valid ? elem * EB : kOff, v);
 
-    // group statistics: zero-extended [min, max] (asymmetric) or max |w| (symmetric)
-    float s;
-    float x_min = 0.0f, x_max = 0.0f;
-    if constexpr (SYM) {
-        float amax = 0.0f;
+            // group statistics: zero-extended [min, max] (asymmetric) or max |w| (symmetric)
+            float s, x_min = 0.0f, x_max = 0.0f;
+            if constexpr (SYM) {
+                float amax = 0.0f;
 #pragma unroll
-        for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(v[e]));
-        amax = xor_max(amax, 1);
-        amax = xor_max(amax, 2);
-        amax = xor_max(amax, 4);
-        s = amax / 7.0f;
-    } else {
+                for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(v[e]));
+                amax = xor_max(amax, 1);
+                amax = xor_max(amax, 2);
+                amax = xor_max(amax, 4);
+                s = div_const<7>(amax);
+            } else {
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            x_min = fminf(x_min, v[e]);
-            x_max = fmaxf(x_max, v[e]);
+                for (int e = 0; e < E; ++e) {
+                    x_min = fminf(x_min, v[e]);
+                    x_max = fmaxf(x_max, v[e]);
+                }
+                x_min = xor_min(x_min, 1); x_max = xor_max(x_max, 1);
+                x_min = xor_min(x_min, 2); x_max = xor_max(x_max, 2);
+                x_min = xor_min(x_min, 4); x_max = xor_max(x_max, 4);
+                s = div_const<15>(x_max - x_min);
+            }
+            // stored fp16 scale: s is rounded to fp32 first, then to fp16 (round-to-nearest-
+            // even both times).  The empty asm pins s as an fp32 value: otherwise the compiler
+            // folds the last FMA of the division and the conversion into one fp16-rounding
+            // instruction, which differs from the double rounding on fp16 ties.
+            asm volatile("" : "+v"(s));
+            uint16_t s16 = __builtin_bit_cast(uint16_t, (_Float16)s);
+            if ((s16 & 0x7FFFu) == 0) s16 = 0x3C00u;
+            if (s16 == 0x7C00u) s16 = 0x7BFFu;
+            const float S = (float)__builtin_bit_cast(_Float16, s16);
+
+            uint32_t packed[(E + 7) / 8];
+#pragma unroll
+            for (int j = 0; j < (E + 7) / 8; ++j) packed[j] = 0;
+            int zi = 8;
+            if constexpr (DT == 0) {
+                // fp32 weights: IEEE quotients
+                float zf = 0.0f;
+                if constexpr (!SYM) zf = fminf(fmaxf(rintf(-x_min / S), 0.0f), 15.0f);
+                constexpr float q_min = SYM ? -8.0f : 0.0f;
+                constexpr float q_max = SYM ? 7.0f : 15.0f;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float qf = fminf(fmaxf(rintf(v[e] / S) + zf, q_min), q_max);
+                    packed[e / 8] |= (uint32_t)((int)qf + (SYM ? 8 : 0)) << (4 * (e % 8));
+                }
+                if constexpr (!SYM) zi = (int)zf;
+            } else {
+                // 16-bit weights: correctly rounded reciprocal once, corrected quotients;
+                // -x_min is itself one of the group's weights (or 0)
+                const float y = 1.0f / S;
+                if constexpr (!SYM) zi = min(max(rne_small(quot16(-x_min, S, y)), 0), 15);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const int u = min(max(rne_small(quot16(v[e], S, y)) + zi, 0), 15);
+                    packed[e / 8] |= (uint32_t)u << (4 * (e % 8));
+                }
+            }
+
+            // codes: E/2 bytes per lane, contiguous across the wave
+            const uint32_t qoff = valid ? elem / 2u : kOff;
+            if constexpr (E == 16) {
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(q4::u32x2, q4::u32x2{packed[0], packed[1]}),
+                                                      rq, (int)qoff, 0, 0);
+            } else if constexpr (E == 8) {
+                __builtin_amdgcn_raw_buffer_store_b32(packed[0], rq, (int)qoff, 0, 0);
+            } else {  // E == 4: half a word
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)packed[0], rq, (int)qoff, 0, 0);
+            }
+            __builtin_amdgcn_raw_buffer_store_b16(s16, rs, (int)(valid && t == 0 ? (uint32_t)gidx * 2u : kOff), 0, 0);
+            if constexpr (!SYM) {
+                uint32_t zn = valid ? ((uint32_t)zi << (4 * grp)) : 0u;
+                zn |= __shfl_xor(zn, 8, 64);
+                zn |= __shfl_xor(zn, 16, 64);
+                zn |= __shfl_xor(zn, 32, 64);
+                __builtin_amdgcn_raw_buffer_store_b32(zn, rz, (int)(lane == 0 ? (uint32_t)zw * 4u : kOff), 0, 0);
+            }
         }
-        x_min = xor_min(x_min, 1); x_max = xor_max(x_max, 1);
-        x_min = xor_min(x_min, 2); x_max = xor_max(x_max, 2);
-        x_min = xor_min(x_min, 4); x_max = xor_max(x_max, 4);
-        s = (x_max - x_min) / 15.0f;
-    }
-    // stored fp16 scale (round-to-nearest-even), degenerate values replaced
-    uint16_t s16 = __builtin_bit_cast(uint16_t, (_Float16)s);
-    if ((s16 & 0x7FFFu) == 0) s16 = 0x3C00u;
-    if (s16 == 0x7C00u) s16 = 0x7BFFu;
-    const float S = (float)__builtin_bit_cast(_Float16, s16);
-
-    float zf = 0.0f;
-    if constexpr (!SYM) zf = fminf(fmaxf(rintf(-x_min / S), 0.0f), 15.0f);
-    constexpr float q_min = SYM ? -8.0f : 0.0f;
-    constexpr float q_max = SYM ? 7.0f : 15.0f;
-
-    uint32_t packed[(E + 7) / 8];
-#pragma unroll
-    for (int j = 0; j < (E + 7) / 8; ++j) packed[j] = 0;
-    if constexpr (DT == 0) {
-        // fp32 weights: the IEEE quotient, element by element
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const float qf = fminf(fmaxf(rintf(v[e] / S) + zf, q_min), q_max);
-            const uint32_t u = (uint32_t)((int)qf + (SYM ? 8 : 0));
-            packed[e / 8] |= u << (4 * (e % 8));
-        }
-    } else {
-        // 16-bit weights: one correctly rounded reciprocal per group and one FMA
-        // correction per weight.  For every finite fp16 scale S and every finite bf16 or
-        // fp16 weight v with |v/S| <= 64, rint of the corrected quotient equals rint of
-        // the IEEE quotient v/S (checked exhaustively; a group's own weights always have
-        // |v/S| < 23 unless S saturated at 65504, where the quotient stays finite and
-        // the code clamps the same way).  Rounding to an integer is the 1.5 * 2^23
-        // addition (exact round-half-to-even for |q| <= 64), then z is added and the
-        // code clamped to [0, 15] in integers.
-        const float y = 1.0f / S;
-        const int zi = SYM ? 8 : (int)zf;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const float q0 = v[e] * y;
-            const float r = __builtin_fmaf(-q0, S, v[e]);
-            float q = __builtin_fmaf(r, y, q0);
-            q = __builtin_amdgcn_fmed3f(q, -64.0f, 64.0f);
-            const int qi = (int)(__builtin_bit_cast(uint32_t, q + 12582912.0f) - 0x4B400000u);
-            const int u = min(max(qi + zi, 0), 15);
-            packed[e / 8] |= (uint32_t)u << (4 * (e % 8));
-        }
-    }
-
-    if (valid) {
-        const int64_t nib = elem_off;  // code index == element index
-        if constexpr (E == 16) {
-            q4::u32x2 o;
-            o[0] = packed[0];
-            o[1] = packed[1];
-            *reinterpret_cast<q4::u32x2*>(qweight + nib / 8) = o;
-        } else if constexpr (E == 8) {
-            qweight[nib / 8] = packed[0];
-        } else {  // E == 4: half a word
-            reinterpret_cast<uint16_t*>(qweight)[nib / 4] = (uint16_t)packed[0];
-        }
-        if (t == 0) scales[row * n_groups + gidx] = s16;
-    }
-    if constexpr (!SYM) {
-        uint32_t zn = valid ? ((uint32_t)(int)zf << (4 * grp)) : 0u;
-        zn |= __shfl_xor(zn, 8, 64);
-        zn |= __shfl_xor(zn, 16, 64);
-        zn |= __shfl_xor(zn, 32, 64);
-        if (lane == 0) zeros[row * zwords + zw] = zn;
     }
 }
+
+int g_num_cus = 0;
 
 template <int G, bool SYM>
 hipError_t launch_dt(const void* w, int dt, int64_t n, int64_t k, uint32_t* qw, uint16_t* sc,
                      uint32_t* zr, hipStream_t st, const char** kname) {
+    if (g_num_cus == 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&g_num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            g_num_cus <= 0)
+            g_num_cus = 256;
+    }
     const int64_t zwords = (k / G + 7) / 8;
+    // enough waves to keep every SIMD busy (8 per SIMD), no more than there are tasks
+    const int64_t cap = (int64_t)g_num_cus * 32;
     const int64_t tasks = n * zwords;
-    const int waves = 4;
-    const dim3 grid((unsigned)((tasks + waves - 1) / waves)), block(64 * waves);
+    const int64_t waves = tasks < cap ? tasks : cap;
+    const int64_t Z = zwords < waves ? zwords : waves;
+    int64_t R = waves / Z;
+    if (R > n) R = n;
+    const int64_t blocks = (R * Z + 3) / 4;
     static const char* names[3] = {"q4_quant_pack_f32", "q4_quant_pack_f16", "q4_quant_pack_bf16"};
     *kname = names[dt];
+    const dim3 grid((unsigned)blocks), block(256);
+    const int ni = (int)n, ki = (int)k, Ri = (int)R, Zi = (int)Z;
     if (dt == 0)
-        hipLaunchKernelGGL((quant_pack_kernel<G, SYM, 0>), grid, block, 0, st, w, k, qw, sc, zr, tasks);
+        hipLaunchKernelGGL((quant_pack_kernel<G, SYM, 0>), grid, block, 0, st, w, ni, ki, qw, sc, zr, Ri, Zi);
     else if (dt == 1)
-        hipLaunchKernelGGL((quant_pack_kernel<G, SYM, 1>), grid, block, 0, st, w, k, qw, sc, zr, tasks);
+        hipLaunchKernelGGL((quant_pack_kernel<G, SYM, 1>), grid, block, 0, st, w, ni, ki, qw, sc, zr, Ri, Zi);
     else
-        hipLaunchKernelGGL((quant_pack_kernel<G, SYM, 2>), grid, block, 0, st, w, k, qw, sc, zr, tasks);
+        hipLaunchKernelGGL((quant_pack_kernel<G, SYM, 2>), grid, block, 0, st, w, ni, ki, qw, sc, zr, Ri, Zi);
     return hipGetLastError();
 }
 
