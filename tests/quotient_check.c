@@ -22,8 +22,32 @@ static float f16(uint32_t h) {
     else mag = ldexpf((float)(m | 1024), (int)e - 25);
     return s ? -mag : mag;
 }
+/* Mode 2: the scale's constant divisions x / 15 and x / 7 from the correctly rounded
+   reciprocal and one FMA correction must equal the IEEE quotient for every finite
+   non-negative fp32 x (the range x_max - x_min and max |w| are never negative). */
+static int check_constant_divisions(void) {
+    const float ds[2] = {15.0f, 7.0f};
+    long long bad = 0;
+    for (int di = 0; di < 2; ++di) {
+        const float d = ds[di];
+        const float c = 1.0f / d;
+#pragma omp parallel for reduction(+:bad) schedule(static, 1 << 16)
+        for (long long u = 0; u < 0x7F800000LL; ++u) {
+            const float x = from_bits((uint32_t)u);
+            const float ref = x / d;
+            const float q0 = x * c;
+            const float r = fmaf(-q0, d, x);
+            const float q1 = fmaf(r, c, q0);
+            if (memcmp(&q1, &ref, 4) != 0) ++bad;
+        }
+    }
+    printf("constant divisions bad %lld\n", bad);
+    return bad != 0;
+}
+
 int main(int argc, char** argv) {
     int mode = atoi(argv[1]);
+    if (mode == 2) return check_constant_divisions();
     long long bad = 0, checked = 0, far = 0;
 #pragma omp parallel for reduction(+:bad,checked,far) schedule(dynamic, 64)
     for (int sb = 1; sb < 0x7C00; ++sb) {
