@@ -4,35 +4,51 @@
 //
 // Large-batch prefill is compute-bound ("LLM Quantization: GPTQ·AWQ·SmoothQuant·FP8·KV
 // Cache (7/10)", §Batch와 Context에 따라 속도가 달라진다), so this is a dense MFMA
-// contraction with the dequantization fused into the tile loads (path A of
+// contraction with the dequantization fused into the operand path (path A of
 // §Kernel이 없으면 압축 이점이 사라진다).
 //
-// Tiles.  A workgroup of 4 waves computes a 256 x 128 block of y (256 activation rows x
-// 128 weight rows); wave w owns rows [64w, 64w+64) x all 128 columns as 2 x 4 tiles of
-// v_mfma_f32_32x32x16 (bf16 or fp16 inputs, fp32 accumulation).  The K loop walks 32
-// columns per stage through double-buffered LDS: while the MFMAs of stage s run, the
-// packed words and activations of stage s+1 are already in registers, and are
-// dequantized and parked in the other LDS buffer afterwards (one barrier per stage).
+// Tiles.  A workgroup of 4 waves computes a 128 x 256 block of y (128 activation rows x
+// 256 weight rows); wave w owns all 128 rows x weight rows [64w, 64w+64) as 4 x 2 tiles
+// of v_mfma_f32_32x32x16 (bf16 or fp16 inputs, fp32 accumulation).  The K loop walks 64
+// columns per stage.
+//
+// Operands.  Activations are shared by the 4 waves: they go from HBM/L2 straight into a
+// three-stage LDS ring with buffer-to-LDS loads (no registers), two stages ahead of the
+// MFMAs, in an XOR-swizzled layout (16-byte chunk c of row r at position c ^ (r & 7)) that
+// makes both the 1 KB loads and the operand reads bank-conflict free.  Weights are not
+// shared: each lane of the 32x32x16 MFMA's weight operand needs 8 consecutive k of one
+// weight row, which is exactly one packed word, so every lane loads its own words (and
+// the scale and zero point of its row) into registers two stages ahead and dequantizes
+// them right before the MFMA.  Every stage issues the same loads in the same order, so
+// each wait is a fixed count and the two stages in flight stay in flight.
+//
+// k slots.  An MFMA consumes 16 k: lanes 0-31 supply 8 and lanes 32-63 another 8.  With
+// g >= 64 lane half h takes words 4h..4h+3 of the stage (one 16-byte load) and MFMA kk
+// uses word 4h+kk; with g = 32 the halves interleave (words 2h, 2h+1, 4+2h, 5+2h) so each
+// MFMA stays inside one group.  The activation operand reads the matching chunks.
 //
 // Exactness.  The weight operand is the exact small integer u - z (|u - z| <= 15, exact
 // in bf16 and fp16), so every product is exact and every sum is fp32.  The per-group
 // scale is applied without a second set of accumulators: within group g the accumulator
 // is kept in units of S[n][g]; entering group g it is multiplied by S[n][g-1] / S[n][g],
-// and the epilogue multiplies by the last group's scale.  Zero stays exactly zero.
+// and the epilogue multiplies by the last group's scale.  A group with S = 0 contributes
+// nothing (its operand is zeroed and the units stay those of the previous group).
 //
 // Placement.  Consecutive workgroups land on consecutive XCDs (8 per MI355X), so block b
-// takes activation block b % mtiles first: with 8 row blocks (m = 2048) each XCD's L2
-// keeps one 4 MB activation block while the packed weights stream through.
+// takes activation block b % mtiles: with 16 row blocks (m = 2048) each XCD's L2 holds
+// two 2 MB activation blocks while the packed weights stream through.
 #include "q4_device.h"
 
 namespace {
 
-constexpr int BM = 256, BN = 128, BK = 32;
+constexpr int BM = 128, BN = 256, BK = 64;
 constexpr int NTHREADS = 256;
-constexpr int XS = BK + 8;  // LDS row stride in 16-bit elements (80 bytes: conflict-free)
-constexpr int kOOB = 0x40000000;
+constexpr int RING = 3;                   // LDS stages of activations
+constexpr int A_STAGE = BM * BK * 2;      // bytes of one activation stage (16 KB)
+constexpr uint32_t kOOB = 0x80000000u;    // an offset past every resource: reads 0
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
 
 __device__ __forceinline__ f32x16 mfma32_bf16(q4::u32x4 a, q4::u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(q4::bf16x8, a),
@@ -43,19 +59,19 @@ __device__ __forceinline__ f32x16 mfma32_f16(q4::u32x4 a, q4::u32x4 b, f32x16 c)
                                                   __builtin_bit_cast(q4::f16x8, b), c, 0, 0, 0);
 }
 
-// 8 codes of one packed word minus z, as exact 16-bit floats in natural column order
-// (elements 0..7 = columns 8j..8j+7).  Bytes 128 + u - z (no borrow between bytes), then
-// XOR 0x80 gives u - z as signed bytes, converted exactly to fp32 and narrowed by keeping
-// the upper half (bf16) or converting (fp16; small integers are exact either way).
+// 8 codes of one packed word minus z, as exact 16-bit floats in natural k order
+// (elements 0..7 = k 8j..8j+7).  Bytes 128 + u - z (no borrow between bytes), then XOR 0x80
+// gives u - z as signed bytes, converted exactly to fp32 and narrowed by keeping the upper
+// half (bf16) or converting (fp16; small integers are exact either way).
 template <bool XF16>
 __device__ __forceinline__ q4::u32x4 dequant_word(uint32_t w, uint32_t zrep) {
-    const uint32_t lo = (((w & 0x0F0F0F0Fu) | 0x80808080u) - zrep) ^ 0x80808080u;         // cols 0,2,4,6
-    const uint32_t hi = ((((w >> 4) & 0x0F0F0F0Fu) | 0x80808080u) - zrep) ^ 0x80808080u;  // cols 1,3,5,7
+    const uint32_t lo = (((w & 0x0F0F0F0Fu) | 0x80808080u) - zrep) ^ 0x80808080u;         // k 0,2,4,6
+    const uint32_t hi = ((((w >> 4) & 0x0F0F0F0Fu) | 0x80808080u) - zrep) ^ 0x80808080u;  // k 1,3,5,7
     q4::u32x4 r;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-        const float e = (float)(int8_t)((lo >> (8 * b)) & 0xFF);  // column 2b
-        const float o = (float)(int8_t)((hi >> (8 * b)) & 0xFF);  // column 2b+1
+        const float e = (float)(int8_t)((lo >> (8 * b)) & 0xFF);
+        const float o = (float)(int8_t)((hi >> (8 * b)) & 0xFF);
         if constexpr (XF16) {
             const q4::f16x2 v = {(_Float16)e, (_Float16)o};
             r[b] = __builtin_bit_cast(uint32_t, v);
@@ -66,144 +82,216 @@ __device__ __forceinline__ q4::u32x4 dequant_word(uint32_t w, uint32_t zrep) {
     return r;
 }
 
+// word of the stage (0..7) that lane half h feeds to MFMA kk
+template <int G>
+__device__ __forceinline__ constexpr int word_of(int kk, int h) {
+    return G >= 64 ? 4 * h + kk : (kk & 1) + 2 * h + 4 * (kk >> 1);
+}
+
+// Per-lane weight-side registers of one stage: the lane's 4 words for each of its two
+// 32-row blocks, the scales of the stage's groups (1, or 2 when g = 32) and the zero word.
+template <int G>
+struct BStage {
+    static constexpr int NGS = G == 32 ? 2 : 1;
+    uint32_t w[2][4];
+    uint32_t s[2][NGS];
+    uint32_t z[2];
+};
+
 template <int G, bool SYM, bool XF16>
 __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const uint16_t* __restrict__ x, int M,
                                                           const uint32_t* __restrict__ qweight,
                                                           const uint16_t* __restrict__ scales,
                                                           const uint32_t* __restrict__ zeros,
                                                           int N, int K, float* __restrict__ y) {
-    __shared__ __attribute__((aligned(16))) uint16_t a_lds[2][BM * XS];
-    __shared__ __attribute__((aligned(16))) uint16_t b_lds[2][BN * XS];
-    __shared__ float s_lds[2][BN];
-
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // RING x A_STAGE
+    constexpr int NGS = BStage<G>::NGS;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int mtiles = (M + BM - 1) / BM;
-    const int mt = blockIdx.x % mtiles, nt = blockIdx.x / mtiles;  // XCD-friendly order
+    const int mt = (int)blockIdx.x % mtiles, nt = (int)blockIdx.x / mtiles;  // XCD-friendly order
     const int m0 = mt * BM, n0 = nt * BN;
     const int KW = K / 8;
     const int n_groups = K / G;
     const int zwords = (n_groups + 7) >> 3;
-    constexpr int SPG = G / BK;  // stages per group
-    const int stages = K / BK;
+    const int stages = (K + BK - 1) / BK;
 
-    const int arows = M - m0 < BM ? M - m0 : BM;
-    const int brows = N - n0 < BN ? N - n0 : BN;
-    const q4::rsrc rx = q4::make_rsrc(x + (int64_t)m0 * K, (uint32_t)arows * K * 2u);
-    const q4::rsrc rq = q4::make_rsrc(qweight + (int64_t)n0 * KW, (uint32_t)brows * KW * 4u);
-    const q4::rsrc rs = q4::make_rsrc(scales + (int64_t)n0 * n_groups, (uint32_t)brows * n_groups * 2u);
-    const q4::rsrc rz = q4::make_rsrc(zeros + (int64_t)n0 * zwords, (uint32_t)brows * zwords * 4u);
+    // activations of this row block
+    const int arows = __builtin_amdgcn_readfirstlane(M - m0 < BM ? M - m0 : BM);
+    const q4::rsrc rx = q4::make_rsrc(x + (int64_t)m0 * K, (uint32_t)arows * (uint32_t)K * 2u);
+    // this wave's 64 weight rows
+    const int wn0 = n0 + 64 * wave;
+    int wrows = N - wn0;
+    wrows = wrows < 0 ? 0 : (wrows > 64 ? 64 : wrows);
+    // uniform values computed with vector instructions: pin them to scalars, or every load
+    // through the resources below becomes a waterfall loop
+    wrows = __builtin_amdgcn_readfirstlane(wrows);
+    const int wbase = __builtin_amdgcn_readfirstlane(wrows > 0 ? wn0 : 0);
+    const q4::rsrc rq = q4::make_rsrc(qweight + (int64_t)wbase * KW, (uint32_t)wrows * (uint32_t)KW * 4u);
+    const q4::rsrc rs = q4::make_rsrc(scales + (int64_t)wbase * n_groups, (uint32_t)wrows * (uint32_t)n_groups * 2u);
+    const q4::rsrc rz = q4::make_rsrc(zeros + (int64_t)wbase * zwords, (uint32_t)wrows * (uint32_t)zwords * 4u);
 
-    // loader roles per stage: activations, 256 rows x 64 bytes, thread t loads row t
-    // (4 x 16 B); weights, 128 rows x 16 words, thread t loads 2 words of row t/2 (half
-    // t%2) plus, at a group start, that row's scale and zero-point word.
-    const int xoff = tid < arows ? tid * K * 2 : kOOB;
-    const int wr = tid >> 1, wh = tid & 1;
-    const int woff = wr < brows ? (wr * KW + 2 * wh) * 4 : kOOB;
-    const int soff = wr < brows ? wr * n_groups * 2 : kOOB;
-    const int zoff = wr < brows ? wr * zwords * 4 : kOOB;
+    const int col = lane & 31, h = lane >> 5;
 
-    q4::u32x4 xa[4];
-    q4::u32x2 wq;
-    uint32_t zword = 0, sraw = 0;
-    auto gload = [&](int s) {
-        const int k0 = s * BK;
+    // Per-lane parts of every stage's load offsets.  Offsets that must read nothing are
+    // OR-ed with kOOB (bitwise, so the compiler keeps the loads unconditional: a load
+    // behind a branch would make the waits conservative).
+    auto oob = [](bool ok) { return ok ? 0u : kOOB; };
+    const int ca = (lane & 7) ^ ((lane >> 3) & 7);  // activation chunk this lane moves (rows are 8-aligned per DMA)
+    uint32_t aoff[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xa[i] = q4::buf_load_x4(rx, xoff, (k0 + 8 * i) * 2);
-        wq = q4::buf_load_x2(rq, woff, k0 / 2);
-        if (s % SPG == 0) {
-            const int g = k0 / G;
-            sraw = q4::buf_load_u16(rs, soff, g * 2);
-            if constexpr (!SYM) zword = q4::buf_load_x1(rz, zoff, (g >> 3) * 4);
+    for (int q = 0; q < 4; ++q)
+        aoff[q] = ((uint32_t)(32 * wave + 8 * q + (lane >> 3)) * (uint32_t)K + 8u * ca) * 2u;
+    uint32_t qoff[2], soff[2], zoff[2];
+    bool rlive[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const uint32_t row = (uint32_t)(32 * j + col);
+        rlive[j] = (int)row < wrows;
+        qoff[j] = row * (uint32_t)KW * 4u;
+        soff[j] = row * (uint32_t)n_groups * 2u;
+        zoff[j] = row * (uint32_t)zwords * 4u;
+    }
+
+    // ---- loads of one stage (fixed count and order: 4 activation DMAs, then per block j
+    //      the words, the scales and the zero word)
+    auto load_a = [&](int s) {  // rows [32 wave, +32) of stage s into ring slot s % RING
+        const int k0 = s * BK;
+        const uint32_t mask = oob(k0 + 8 * ca < K);
+        uint8_t* slot = smem + (s % RING) * A_STAGE;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr)(slot + (32 * wave + 8 * q) * (BK * 2)), 16,
+                                                     (int)((aoff[q] + 2u * (uint32_t)k0) | mask), 0, 0, 0);
+    };
+    auto load_b = [&](BStage<G>& b, int s) {
+        const int w0 = s * (BK / 8);  // first word of the stage within a row
+        int g0 = G == 128 ? (s >> 1) : (G == 64 ? s : 2 * s);  // first group of the stage
+        g0 = g0 < n_groups ? g0 : n_groups - 1;  // past the end (prefetch of no stage): any valid
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const bool live = rlive[j] && s < stages;
+            if constexpr (G >= 64) {
+                const int wd = w0 + 4 * h;
+                const q4::u32x4 t = q4::buf_load_x4(rq, (int)((qoff[j] + 4u * wd) | oob(live && wd < KW)), 0);
+                b.w[j][0] = t[0]; b.w[j][1] = t[1]; b.w[j][2] = t[2]; b.w[j][3] = t[3];
+            } else {
+                const int wa = w0 + 2 * h, wb = w0 + 4 + 2 * h;
+                const q4::u32x2 ta = q4::buf_load_x2(rq, (int)((qoff[j] + 4u * wa) | oob(live && wa < KW)), 0);
+                const q4::u32x2 tb = q4::buf_load_x2(rq, (int)((qoff[j] + 4u * wb) | oob(live && wb < KW)), 0);
+                b.w[j][0] = ta[0]; b.w[j][1] = ta[1]; b.w[j][2] = tb[0]; b.w[j][3] = tb[1];
+            }
+#pragma unroll
+            for (int q = 0; q < NGS; ++q) {
+                const int gq = g0 + q < n_groups ? g0 + q : n_groups - 1;
+                b.s[j][q] = q4::buf_load_u16(rs, (int)((soff[j] + 2u * gq) | oob(live)), 0);
+            }
+            if constexpr (!SYM)
+                b.z[j] = q4::buf_load_x1(rz, (int)((zoff[j] + 4u * (g0 >> 3)) | oob(live)), 0);
+            else
+                b.z[j] = 0u;
         }
     };
-    auto park = [&](int s, int buf) {
-        const int g = (s * BK) / G;
-        q4::u32x4* ap = reinterpret_cast<q4::u32x4*>(&a_lds[buf][tid * XS]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ap[i] = xa[i];
-        int z = 8;
-        if constexpr (!SYM) z = (int)((zword >> (4 * (g & 7))) & 0xFu);
-        const uint32_t zrep = (uint32_t)z * 0x01010101u;
-        // A group whose scale is zero contributes exactly nothing: its weights are parked
-        // as zeros and the accumulator keeps the previous group's units (rows past N read
-        // scale 0 from outside the buffer and take the same path).
-        const uint32_t keep = (sraw & 0x7FFFu) != 0 ? 0xFFFFFFFFu : 0u;
-        q4::u32x4* bp = reinterpret_cast<q4::u32x4*>(&b_lds[buf][wr * XS + 16 * wh]);
-        bp[0] = dequant_word<XF16>(wq[0], zrep) & keep;
-        bp[1] = dequant_word<XF16>(wq[1], zrep) & keep;
-        if (s % SPG == 0 && wh == 0) s_lds[(s / SPG) & 1][wr] = q4::f16_bits_to_float((uint16_t)sraw);
-    };
 
-    f32x16 acc[2][4];
+    f32x16 acc[4][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    float s_cur[2] = {1.f, 1.f};
+    int g_cur = -1;
 
-    const int col = lane & 31, half = lane >> 5;
-    float s_cur[4] = {1.f, 1.f, 1.f, 1.f};
-
-    gload(0);
-    park(0, 0);
-    __syncthreads();
-    for (int s = 0; s < stages; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < stages) gload(s + 1);
-        if (s % SPG == 0) {  // entering a group: rescale to its units
-            const float* sl = s_lds[(s / SPG) & 1];
+    // ---- compute of one stage
+    auto compute = [&](const BStage<G>& b, int s) {
+        const uint8_t* slot = smem + (s % RING) * A_STAGE;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float sn = sl[32 * j + col];
-                const float ratio = sn != 0.0f ? s_cur[j] / sn : 1.0f;
-                if (sn != 0.0f) s_cur[j] = sn;
-                if (s != 0) {
+        for (int kk = 0; kk < 4; ++kk) {
+            const int q = G == 32 ? (kk >> 1) : 0;                           // group slot of this MFMA
+            const int gk = G == 128 ? (s >> 1) : (G == 64 ? s : 2 * s + q);  // its group
+            float sn[2];
+            uint32_t keep[2], zrep[2];
 #pragma unroll
-                    for (int i = 0; i < 2; ++i)
+            for (int j = 0; j < 2; ++j) {
+                sn[j] = q4::f16_bits_to_float((uint16_t)b.s[j][q]);
+                keep[j] = sn[j] != 0.0f ? 0xFFFFFFFFu : 0u;
+                const int z = SYM ? 8 : (int)((b.z[j] >> (4 * (gk & 7))) & 0xFu);
+                zrep[j] = (uint32_t)z * 0x01010101u;
+            }
+            if (gk != g_cur) {  // wave-uniform: entering a new group, rescale to its units
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const float ratio = sn[j] != 0.0f && g_cur >= 0 ? s_cur[j] / sn[j] : 1.0f;
+                    if (sn[j] != 0.0f) s_cur[j] = sn[j];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
 #pragma unroll
                         for (int r = 0; r < 16; ++r) acc[i][j][r] *= ratio;
                 }
+                g_cur = gk;
+            }
+            q4::u32x4 bop[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) bop[j] = dequant_word<XF16>(b.w[j][kk], zrep[j]) & keep[j];
+            const int c = word_of<G>(kk, h);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 32 * i + col;
+                const q4::u32x4 a = *reinterpret_cast<const q4::u32x4*>(slot + r * (BK * 2) + ((c ^ (r & 7)) << 4));
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    if constexpr (XF16)
+                        acc[i][j] = mfma32_f16(a, bop[j], acc[i][j]);
+                    else
+                        acc[i][j] = mfma32_bf16(a, bop[j], acc[i][j]);
+                }
             }
         }
-        const uint16_t* al = a_lds[buf];
-        const uint16_t* bl = b_lds[buf];
-#pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            q4::u32x4 af[2], bf[4];
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-                af[i] = *reinterpret_cast<const q4::u32x4*>(&al[(wave * 64 + 32 * i + col) * XS + 16 * kk + 8 * half]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                bf[j] = *reinterpret_cast<const q4::u32x4*>(&bl[(32 * j + col) * XS + 16 * kk + 8 * half]);
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if constexpr (XF16)
-                        acc[i][j] = mfma32_f16(af[i], bf[j], acc[i][j]);
-                    else
-                        acc[i][j] = mfma32_bf16(af[i], bf[j], acc[i][j]);
-                }
-        }
-        if (s + 1 < stages) park(s + 1, buf ^ 1);
-        __syncthreads();
-    }
+    };
 
-    // epilogue: back to true units, store.  Lane (col, half), register r of a 32x32 tile
-    // holds row (r & 3) + 4*half + 8*(r >> 2), column col.
+    // ---- pipeline: stages s and s+1 are in flight when stage s starts
+    constexpr int LOADS = 4 + 2 * ((G >= 64 ? 1 : 2) + NGS + (SYM ? 0 : 1));  // vector loads per stage
+    constexpr int WAIT = (LOADS & 15) | ((LOADS >> 4) << 14) | (0x7 << 4) | (0xF << 8);  // vmcnt(LOADS)
+    BStage<G> bs[3];
+    load_a(0);
+    load_b(bs[0], 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(1);
+    load_b(bs[1], 1);
+    __builtin_amdgcn_sched_barrier(0);
+    auto step = [&](int s, BStage<G>& cur, BStage<G>& nxt2) {
+        // This wave's loads of stage s have landed (those of stage s+1 stay in flight); the
+        // barrier then makes every wave's activation DMA visible and frees slot s-1.  A plain
+        // s_barrier: __syncthreads() would also wait for the DMA of stage s+1.
+        __builtin_amdgcn_s_waitcnt(WAIT);
+        asm volatile("s_barrier" ::: "memory");
+        load_a(s + 2);                     // (past the last stage: offsets off the end)
+        load_b(nxt2, s + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(cur, s);
+    };
+    int s = 0;
+    for (; s + 3 <= stages; s += 3) {
+        step(s, bs[0], bs[2]);
+        step(s + 1, bs[1], bs[0]);
+        step(s + 2, bs[2], bs[1]);
+    }
+    if (s < stages) step(s, bs[0], bs[2]);
+    if (s + 1 < stages) step(s + 1, bs[1], bs[0]);
+
+    // epilogue: back to true units, store.  Lane (col, h), register r of a 32x32 tile holds
+    // row (r & 3) + 4h + 8(r >> 2), column col.
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int nn = n0 + 32 * j + col;
+    for (int j = 0; j < 2; ++j) {
+        const int nn = wn0 + 32 * j + col;
         if (nn >= N) continue;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int mm = m0 + wave * 64 + 32 * i + (r & 3) + 4 * half + 8 * (r >> 2);
+                const int mm = m0 + 32 * i + (r & 3) + 4 * h + 8 * (r >> 2);
                 if (mm < M) y[(int64_t)mm * N + nn] = acc[i][j][r] * s_cur[j];
             }
     }
@@ -214,13 +302,14 @@ hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16
                   const uint32_t* zr, int n, int k, float* y, hipStream_t st, const char** kname) {
     const int mtiles = (m + BM - 1) / BM, ntiles = (n + BN - 1) / BN;
     const dim3 grid((unsigned)(mtiles * ntiles)), block(NTHREADS);
+    const size_t lds = (size_t)RING * A_STAGE;
     const uint16_t* xp = reinterpret_cast<const uint16_t*>(x);
     if (xd == 1) {
         *kname = "q4_gemm_mfma_f16";
-        hipLaunchKernelGGL((gemm_kernel<G, SYM, true>), grid, block, 0, st, xp, m, qw, sc, zr, n, k, y);
+        hipLaunchKernelGGL((gemm_kernel<G, SYM, true>), grid, block, lds, st, xp, m, qw, sc, zr, n, k, y);
     } else {
         *kname = "q4_gemm_mfma_bf16";
-        hipLaunchKernelGGL((gemm_kernel<G, SYM, false>), grid, block, 0, st, xp, m, qw, sc, zr, n, k, y);
+        hipLaunchKernelGGL((gemm_kernel<G, SYM, false>), grid, block, lds, st, xp, m, qw, sc, zr, n, k, y);
     }
     return hipGetLastError();
 }
