@@ -76,7 +76,8 @@ __device__ __forceinline__ q4::u32x4 dequant_word(uint32_t w, uint32_t zrep) {
             const q4::f16x2 v = {(_Float16)e, (_Float16)o};
             r[b] = __builtin_bit_cast(uint32_t, v);
         } else {
-            r[b] = (__builtin_bit_cast(uint32_t, e) >> 16) | (__builtin_bit_cast(uint32_t, o) & 0xFFFF0000u);
+            // upper halves of the two fp32 values: bytes 2,3 of e then bytes 2,3 of o
+            r[b] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, o), __builtin_bit_cast(uint32_t, e), 0x07060302u);
         }
     }
     return r;
@@ -134,61 +135,59 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const uint16_t* __res
 
     const int col = lane & 31, h = lane >> 5;
 
-    // Per-lane parts of every stage's load offsets.  Offsets that must read nothing are
-    // OR-ed with kOOB (bitwise, so the compiler keeps the loads unconditional: a load
-    // behind a branch would make the waits conservative).
-    auto oob = [](bool ok) { return ok ? 0u : kOOB; };
-    const int ca = (lane & 7) ^ ((lane >> 3) & 7);  // activation chunk this lane moves (rows are 8-aligned per DMA)
+    // Per-lane parts of the load offsets; the per-stage part is a uniform scalar offset.
+    // Rows past the end of a block read nothing (their per-lane offset carries kOOB).
+    // Loads for the two stages after the last one read whatever lies in range and are
+    // never used, so they need no masking.  The k tail (k % 64 == 32) needs it: the
+    // activation chunks past k are read as zeros, so whatever the weight words past the
+    // end of a row hold meets a zero.
+    const int ca = (lane & 7) ^ ((lane >> 3) & 7);  // activation chunk this lane moves (DMA rows are 8-aligned)
     uint32_t aoff[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
         aoff[q] = ((uint32_t)(32 * wave + 8 * q + (lane >> 3)) * (uint32_t)K + 8u * ca) * 2u;
+    const int tail_chunks = (K % BK) / 8;  // valid chunks of a short last stage (0: none short)
+    const uint32_t tail_mask = tail_chunks != 0 && ca >= tail_chunks ? kOOB : 0u;
     uint32_t qoff[2], soff[2], zoff[2];
-    bool rlive[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const uint32_t row = (uint32_t)(32 * j + col);
-        rlive[j] = (int)row < wrows;
-        qoff[j] = row * (uint32_t)KW * 4u;
-        soff[j] = row * (uint32_t)n_groups * 2u;
-        zoff[j] = row * (uint32_t)zwords * 4u;
+        const uint32_t rowmask = (int)row < wrows ? 0u : kOOB;
+        qoff[j] = (row * (uint32_t)KW * 4u + (G >= 64 ? 16u : 8u) * h) | rowmask;
+        soff[j] = (row * (uint32_t)n_groups * 2u) | rowmask;
+        zoff[j] = (row * (uint32_t)zwords * 4u) | rowmask;
     }
 
     // ---- loads of one stage (fixed count and order: 4 activation DMAs, then per block j
     //      the words, the scales and the zero word)
     auto load_a = [&](int s) {  // rows [32 wave, +32) of stage s into ring slot s % RING
-        const int k0 = s * BK;
-        const uint32_t mask = oob(k0 + 8 * ca < K);
+        const uint32_t tm = s == stages - 1 ? tail_mask : 0u;
+        const int so = __builtin_amdgcn_readfirstlane(2 * s * BK);
         uint8_t* slot = smem + (s % RING) * A_STAGE;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr)(slot + (32 * wave + 8 * q) * (BK * 2)), 16,
-                                                     (int)((aoff[q] + 2u * (uint32_t)k0) | mask), 0, 0, 0);
+                                                     (int)(aoff[q] | tm), so, 0, 0);
     };
     auto load_b = [&](BStage<G>& b, int s) {
-        const int w0 = s * (BK / 8);  // first word of the stage within a row
-        int g0 = G == 128 ? (s >> 1) : (G == 64 ? s : 2 * s);  // first group of the stage
-        g0 = g0 < n_groups ? g0 : n_groups - 1;  // past the end (prefetch of no stage): any valid
+        const int wso = __builtin_amdgcn_readfirstlane(4 * s * (BK / 8));  // the stage's first word
+        const int g0 = G == 128 ? (s >> 1) : (G == 64 ? s : 2 * s);        // its first group
+        const int sso = __builtin_amdgcn_readfirstlane(2 * g0);
+        const int zso = __builtin_amdgcn_readfirstlane(4 * (g0 >> 3));
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const bool live = rlive[j] && s < stages;
             if constexpr (G >= 64) {
-                const int wd = w0 + 4 * h;
-                const q4::u32x4 t = q4::buf_load_x4(rq, (int)((qoff[j] + 4u * wd) | oob(live && wd < KW)), 0);
+                const q4::u32x4 t = q4::buf_load_x4(rq, (int)qoff[j], wso);
                 b.w[j][0] = t[0]; b.w[j][1] = t[1]; b.w[j][2] = t[2]; b.w[j][3] = t[3];
             } else {
-                const int wa = w0 + 2 * h, wb = w0 + 4 + 2 * h;
-                const q4::u32x2 ta = q4::buf_load_x2(rq, (int)((qoff[j] + 4u * wa) | oob(live && wa < KW)), 0);
-                const q4::u32x2 tb = q4::buf_load_x2(rq, (int)((qoff[j] + 4u * wb) | oob(live && wb < KW)), 0);
+                const q4::u32x2 ta = q4::buf_load_x2(rq, (int)qoff[j], wso);
+                const q4::u32x2 tb = q4::buf_load_x2(rq, (int)qoff[j], wso + 16);
                 b.w[j][0] = ta[0]; b.w[j][1] = ta[1]; b.w[j][2] = tb[0]; b.w[j][3] = tb[1];
             }
 #pragma unroll
-            for (int q = 0; q < NGS; ++q) {
-                const int gq = g0 + q < n_groups ? g0 + q : n_groups - 1;
-                b.s[j][q] = q4::buf_load_u16(rs, (int)((soff[j] + 2u * gq) | oob(live)), 0);
-            }
+            for (int q = 0; q < NGS; ++q) b.s[j][q] = q4::buf_load_u16(rs, (int)soff[j], sso + 2 * q);
             if constexpr (!SYM)
-                b.z[j] = q4::buf_load_x1(rz, (int)((zoff[j] + 4u * (g0 >> 3)) | oob(live)), 0);
+                b.z[j] = q4::buf_load_x1(rz, (int)zoff[j], zso);
             else
                 b.z[j] = 0u;
         }
@@ -204,44 +203,67 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const uint16_t* __res
     float s_cur[2] = {1.f, 1.f};
     int g_cur = -1;
 
+    // LDS operand addresses: row 32i + col of the slot, chunk word_of(kk, h) at its swizzled
+    // position ((32i + col) & 7 == col & 7, so one address per kk; i goes in the offset)
+    uint32_t apos[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+        apos[kk] = (uint32_t)col * (BK * 2) + ((uint32_t)(word_of<G>(kk, h) ^ (col & 7)) << 4);
+
     // ---- compute of one stage
     auto compute = [&](const BStage<G>& b, int s) {
         const uint8_t* slot = smem + (s % RING) * A_STAGE;
+        float sn[NGS][2], ratio[NGS][2];
+        uint32_t zrep[NGS][2];
+        bool fresh[NGS], zmask[NGS];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int q = G == 32 ? (kk >> 1) : 0;                           // group slot of this MFMA
-            const int gk = G == 128 ? (s >> 1) : (G == 64 ? s : 2 * s + q);  // its group
-            float sn[2];
-            uint32_t keep[2], zrep[2];
+        for (int q = 0; q < NGS; ++q) {  // the stage's groups (one, or two when g = 32)
+            const int gk = G == 128 ? (s >> 1) : (G == 64 ? s : 2 * s + q);
+            bool zs = false;
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                sn[j] = q4::f16_bits_to_float((uint16_t)b.s[j][q]);
-                keep[j] = sn[j] != 0.0f ? 0xFFFFFFFFu : 0u;
+                sn[q][j] = q4::f16_bits_to_float((uint16_t)b.s[j][q]);
+                zs = zs || sn[q][j] == 0.0f;
                 const int z = SYM ? 8 : (int)((b.z[j] >> (4 * (gk & 7))) & 0xFu);
-                zrep[j] = (uint32_t)z * 0x01010101u;
+                zrep[q][j] = (uint32_t)z * 0x01010101u;
             }
-            if (gk != g_cur) {  // wave-uniform: entering a new group, rescale to its units
+            zmask[q] = __builtin_amdgcn_ballot_w64(zs) != 0;  // a zero scale anywhere in the wave
+            // entering a new group (wave-uniform): the accumulator moves to its units
+            fresh[q] = gk != g_cur;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) ratio[q][j] = 1.0f;
+            if (fresh[q]) {
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    const float ratio = sn[j] != 0.0f && g_cur >= 0 ? s_cur[j] / sn[j] : 1.0f;
-                    if (sn[j] != 0.0f) s_cur[j] = sn[j];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) acc[i][j][r] *= ratio;
+                    ratio[q][j] = sn[q][j] != 0.0f && g_cur >= 0 ? s_cur[j] / sn[q][j] : 1.0f;
+                    if (sn[q][j] != 0.0f) s_cur[j] = sn[q][j];
                 }
                 g_cur = gk;
             }
+        }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int q = G == 32 ? (kk >> 1) : 0;  // group slot of this MFMA
+            const bool rescale = fresh[q] && (G == 32 ? (kk & 1) == 0 : kk == 0);
             q4::u32x4 bop[2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) bop[j] = dequant_word<XF16>(b.w[j][kk], zrep[j]) & keep[j];
-            const int c = word_of<G>(kk, h);
+            for (int j = 0; j < 2; ++j) bop[j] = dequant_word<XF16>(b.w[j][kk], zrep[q][j]);
+            if (zmask[q]) {  // rare: zero the operand of zero-scale groups
+#pragma unroll
+                for (int j = 0; j < 2; ++j) bop[j] &= sn[q][j] != 0.0f ? 0xFFFFFFFFu : 0u;
+            }
+            const uint8_t* ab = slot + apos[kk];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = 32 * i + col;
-                const q4::u32x4 a = *reinterpret_cast<const q4::u32x4*>(slot + r * (BK * 2) + ((c ^ (r & 7)) << 4));
+                const q4::u32x4 a = *reinterpret_cast<const q4::u32x4*>(ab + i * 32 * (BK * 2));
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
+                    // each 32x32 tile moves to the new group's units right before its own MFMA,
+                    // so the multiplies issue while the MFMAs of the other tiles run
+                    if (rescale) {
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) acc[i][j][e] *= ratio[q][j];
+                    }
                     if constexpr (XF16)
                         acc[i][j] = mfma32_f16(a, bop[j], acc[i][j]);
                     else
