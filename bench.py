@@ -5,13 +5,15 @@ Metric: W4A16 GEMV achieved HBM GB/s at M=1 on the 7B-like decode projections
 28672x8192, M=2048) and the quantize/pack GB/s of the 32-layer 7B-like checkpoint in the
 same JSON line.
 
-A timed step is one decode pass: the W4A16 GEMV over both projections at M=1, one launch
-each.  Each step reads a different copy of the packed weights (the copies together are
-four times the 256 MB Infinity Cache), so every step streams its weights from HBM.  The
-steps are replayed from captured HIP graphs (the launches themselves are identical to
-direct calls; the graph removes the Python/ctypes launch cost of ~7 us per call, which
-would otherwise dominate the ~10 us kernels).  Inputs are resident in HBM before the
-timed region starts.
+A timed step is one decode pass: the W4A16 GEMV over both projections at M=1, issued as
+one grouped call (q4_w4a16_gemm_grouped: both problems in one launch of the decode
+kernel).  The same projections issued as two single-problem calls are measured too and
+reported under "single_launches".  Each step reads a different copy of the packed
+weights (the copies together are four times the 256 MB Infinity Cache), so every step
+streams its weights from HBM.  The steps are replayed from captured HIP graphs (the
+launches themselves are identical to direct calls; the graph removes the Python/ctypes
+launch cost of ~7 us per call, which would otherwise dominate the ~10 us kernels).
+Inputs are resident in HBM before the timed region starts.
 
 Algorithmic bytes (what the method must move, nothing else):
   GEMV   per launch: n*k/2 (codes) + 2*n*k/g (fp16 scales) + 4*n*ceil(k/g/8) (zeros)
@@ -181,7 +183,10 @@ def main():
     x = synthetic.activations(1, 4096, cfg["x_seed"]).to(dev)
     ys = [torch.empty((1, p.n), dtype=torch.float32, device=dev) for p in base]
 
-    def step_fns(c):
+    def step_fns(c):  # one grouped launch: both projections
+        return [lambda c=c: q4.q4_w4a16_gemm_grouped(x, packs[c], outs=ys)]
+
+    def single_fns(c):  # the same step as one launch per projection
         return [lambda c=c, i=i: q4.q4_w4a16_gemm(x, packs[c][i], out=ys[i]) for i in range(len(base))]
 
     for f in step_fns(0):
@@ -205,23 +210,30 @@ def main():
     ms_step = wall * 1e3 / args.steps
     value = step_bytes * args.steps / wall / 1e9
 
-    # kernel durations: HIP events on the launch stream around graph replays of one shape
-    # (every copy once), a pass separate from the timed steps
-    launch_ms = []
+    # kernel durations: HIP events on the launch stream around graph replays (every copy
+    # once), a pass separate from the timed steps.  The grouped launch is the step's
+    # kernel; the single-problem launches are timed per shape.
+    launch_ms = graph_ms(capture([f for c in range(copies) for f in step_fns(c)]), 10) / copies
+    achieved = step_bytes / (launch_ms * 1e-3) / 1e9
+    single_ms = []
     for i in range(len(base)):
         g = capture([lambda c=c: q4.q4_w4a16_gemm(x, packs[c][i], out=ys[i]) for c in range(copies)])
-        launch_ms.append(graph_ms(g, 10) / copies)
-    mean_launch_ms = sum(launch_ms) / len(launch_ms)
-    mean_launch_bytes = step_bytes / len(base)
-    achieved = mean_launch_bytes / (mean_launch_ms * 1e-3) / 1e9
+        single_ms.append(graph_ms(g, 10) / copies)
+    single_step_ms = graph_ms(capture([f for c in range(copies) for f in single_fns(c)]), 10) / copies
     digest = source_digest("gemv.hip", "q4_device.h")
     traffic = profiled_traffic("q4_gemv_decode_7b_m1_pmc.md", digest)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "kernel": gemv_kernel,
-                "per_launch_us": {f"{p.n}x{p.k}": round(t * 1e3, 3) for p, t in zip(base, launch_ms)},
-                "bytes_per_launch": {f"{p.n}x{p.k}": gemv_bytes(1, p.n, p.k, 128, False) for p in base},
+                "per_launch_us": round(launch_ms * 1e3, 3), "bytes_per_launch": step_bytes,
                 "source_digest": digest}
+    single = {"kernel": gemv_kernel,
+              "per_launch_us": {f"{p.n}x{p.k}": round(t * 1e3, 3) for p, t in zip(base, single_ms)},
+              "bytes_per_launch": {f"{p.n}x{p.k}": gemv_bytes(1, p.n, p.k, 128, False) for p in base},
+              "achieved_gbs": {f"{p.n}x{p.k}": round(gemv_bytes(1, p.n, p.k, 128, False) / (t * 1e-3) / 1e9, 1)
+                               for p, t in zip(base, single_ms)},
+              "step_us": round(single_step_ms * 1e3, 3),
+              "step_gbs": round(step_bytes / (single_step_ms * 1e-3) / 1e9, 1)}
     del packs
 
     # ------------------------------------------------------------ prefill GEMM
@@ -289,8 +301,10 @@ def main():
         "config": {"workload": "7B-like decode GEMV, W [4096x4096] and [11008x4096], g=128 asym "
                                "uint4, x bf16 [1x4096], M=1", "group_size": 128, "m": 1,
                    "weight_copies": copies, "bytes_per_step": step_bytes,
-                   "launch": "one GEMV launch per projection, replayed from HIP graphs"},
+                   "launch": "one grouped GEMV launch per step (both projections), replayed "
+                             "from HIP graphs"},
         "roofline": roofline,
+        "single_launches": single,
     }
     line.update(out)
     if not args.no_cpu_baseline:

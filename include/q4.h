@@ -87,6 +87,29 @@ q4_status q4_w4a16_gemm(const void* x, q4_dtype x_dtype, int64_t m,
                         int64_t n, int64_t k, int32_t group_size, int32_t symmetric,
                         float* y, hipStream_t stream);
 
+/* One problem of a grouped call: y = x . x_hat^T for one packed weight. */
+typedef struct {
+    const void* x;            /* [m][k] activations, in the dtype of the call */
+    const uint32_t* qweight;  /* [n][k/8] packed codes */
+    const uint16_t* scales;   /* [n][k/g] fp16 bit patterns */
+    const uint32_t* zeros;    /* [n][ceil(k/g/8)] zero points; may be NULL when symmetric */
+    int64_t n;                /* output features of this problem */
+    float* y;                 /* [m][n] fp32 output */
+} q4_gemm_problem;
+
+/* Several independent W4A16 products that share m, k, group_size, symmetry and the
+ * activation dtype, e.g. the q, k, v or the gate and up projections of one decoder layer.
+ * Decode is bandwidth-bound ([FL7] §Batch와 Context에 따라 속도가 달라진다), and a small
+ * projection pays a launch's ramp-up and tail for little data; with m <= 16 all problems
+ * run in one launch of the decode GEMV kernel when their activations fit its on-chip
+ * staging, otherwise (and for m > 16) one after another.  Each y meets the same accuracy
+ * bound as a q4_w4a16_gemm call on that problem (the order of the fp32 sums may differ).
+ * problems is a host array of 1 <= count <= 8 entries; every entry is validated as for
+ * q4_w4a16_gemm before anything is enqueued. */
+q4_status q4_w4a16_gemm_grouped(const q4_gemm_problem* problems, int32_t count,
+                                q4_dtype x_dtype, int64_t m, int64_t k, int32_t group_size,
+                                int32_t symmetric, hipStream_t stream);
+
 /* Element counts of the three packed arrays (payload + metadata, [FL7] §Memory 계산은
  * Payload와 Metadata로 나눈다): n*k/8 words, n*(k/g) scales, n*ceil((k/g)/8) words.
  * Return -1 for arguments the entry points would reject. */

@@ -104,3 +104,39 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
         q4.q4_quantize_pack(torch.zeros(4, 128), 128, False)
+
+
+def _grouped(probs, count=None, xd=BF16, m=1, k=256, g=128, sym=0):
+    arr = (q4.GemmProblem * max(1, len(probs)))()
+    for i, pr in enumerate(probs):
+        arr[i] = pr
+    return q4.lib().q4_w4a16_gemm_grouped(arr if probs else None, len(probs) if count is None else count,
+                                          xd, m, k, g, sym, None)
+
+
+def _prob(x=A16, qw=A16, sc=A16, zr=A16, n=16, y=A16):
+    return q4.GemmProblem(x, qw, sc, zr, n, y)
+
+
+@pytest.mark.parametrize("call,code", [
+    (lambda: _grouped([]), NULL),
+    (lambda: _grouped([_prob()], count=0), SHAPE),
+    (lambda: _grouped([_prob()] * 9), SHAPE),
+    (lambda: _grouped([_prob(), _prob(n=0)]), SHAPE),
+    (lambda: _grouped([_prob(), _prob(y=None)]), NULL),
+    (lambda: _grouped([_prob(), _prob(zr=None)]), NULL),
+    (lambda: _grouped([_prob(x=A16 + 2), _prob()]), ALIGN),
+    (lambda: _grouped([_prob(), _prob()], g=100), GROUP),
+    (lambda: _grouped([_prob(), _prob()], xd=F32), DTYPE),
+    (lambda: _grouped([_prob(), _prob()], m=0), SHAPE),
+    (lambda: _grouped([_prob(), _prob()], k=(1 << 22) + 128), SHAPE),
+])
+def test_grouped_validation_rejects_before_launch(call, code):
+    """Every entry is checked before anything is enqueued; the first failure is returned."""
+    assert call() == code
+    assert q4.q4_last_kernel() == ""
+
+
+def test_grouped_symmetric_accepts_null_zeros_in_validation():
+    # a bad group size is reported although every zeros pointer is NULL: NULL is accepted
+    assert _grouped([_prob(zr=None), _prob(zr=None)], g=16, sym=1) == GROUP

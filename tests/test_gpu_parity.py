@@ -317,6 +317,65 @@ def test_linear_zero_scale_groups(m, sym):
     assert_linear_close(y, host_input(x), (qo, so, zo), n, k, g, sym, what=kname)
 
 
+def test_gemm_grouped_decode_pair():
+    """The two 7B-like decode projections in one grouped launch (shared x, m = 1): each
+    output matches the oracle over all rows and columns."""
+    cfg = synthetic.DECODE_7B
+    mats = cfg["mats"]
+    ws = [m_.make() for m_ in mats]
+    x = synthetic.activations(1, mats[0].k, cfg["x_seed"])
+    note("grouped decode pair m=1 g=128 asym")
+    packs = [pack_guarded(w.to(DEV), 128, False)[0] for w in ws]
+    guards = [guarded((1, p.n), torch.float32, SENTINEL_F32) for p in packs]
+    q4.q4_w4a16_gemm_grouped(x.to(DEV), packs, outs=[v for _, v in guards])
+    torch.cuda.synchronize()
+    assert q4.q4_last_kernel() == "q4_gemv_mfma_bf16"
+    for w, p, (gb, gv) in zip(ws, packs, guards):
+        assert guard_intact(gb), "store outside y"
+        packed = assert_pack_exact(p, host_input(w), 128, False)
+        assert_linear_close(gv.cpu().numpy(), host_input(x), packed, p.n, p.k, 128, False,
+                            what="grouped")
+
+
+@pytest.mark.parametrize("m", [1, 5, 16])
+@pytest.mark.parametrize("g,sym", [(32, False), (128, True), (64, False)])
+@pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
+def test_gemm_grouped_mixed(m, g, sym, xdtype):
+    """Three problems of different n (ragged tiles), each with its own activations."""
+    k = 1024
+    ns = [48, 200, 1000]
+    ws = [torch.from_numpy(pins.random_weights(31 + i, max(n, 12), k)[:n]) for i, n in enumerate(ns)]
+    xs = [synthetic.activations(m, k, seed=40 + i).to(xdtype) for i in range(len(ns))]
+    note(f"grouped mixed m={m} g={g} sym={sym} {xdtype}")
+    packs = [pack_guarded(w.to(DEV), g, sym)[0] for w in ws]
+    guards = [guarded((m, n), torch.float32, SENTINEL_F32) for n in ns]
+    q4.q4_w4a16_gemm_grouped([x.to(DEV) for x in xs], packs, outs=[v for _, v in guards])
+    torch.cuda.synchronize()
+    assert q4.q4_last_kernel().startswith("q4_gemv_mfma_")
+    for w, x, p, (gb, gv) in zip(ws, xs, packs, guards):
+        assert guard_intact(gb), "store outside y"
+        packed = assert_pack_exact(p, host_input(w), g, sym)
+        assert_linear_close(gv.cpu().numpy(), host_input(x), packed, p.n, k, g, sym,
+                            what="grouped")
+
+
+@pytest.mark.parametrize("m,k", [(40, 512), (16, 11008)])
+def test_gemm_grouped_one_by_one(m, k):
+    """m > 16 (prefill GEMM per problem) and activations too large to stage on chip
+    (decode kernel per problem): same results, one launch per problem."""
+    ns = [64, 130]
+    ws = [torch.from_numpy(pins.random_weights(50 + i, max(n, 12), k)[:n]) for i, n in enumerate(ns)]
+    x = synthetic.activations(m, k, seed=60)
+    note(f"grouped one-by-one m={m} k={k}")
+    packs = [pack_guarded(w.to(DEV), 128, False)[0] for w in ws]
+    ys = q4.q4_w4a16_gemm_grouped(x.to(DEV), packs)
+    torch.cuda.synchronize()
+    for w, p, y in zip(ws, packs, ys):
+        packed = assert_pack_exact(p, host_input(w), 128, False)
+        assert_linear_close(y.cpu().numpy(), host_input(x), packed, p.n, k, 128, False,
+                            what="grouped")
+
+
 GEMM_CASES = [(17, 64, 256, 128), (130, 200, 384, 64), (300, 129, 96, 32), (256, 256, 1024, 128),
               (129, 1000, 4096 + 64, 64), (64, 48, 11008, 128)]
 

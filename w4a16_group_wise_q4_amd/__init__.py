@@ -9,6 +9,7 @@ Entry points (same names as the C ABI):
     q4_quantize_pack(w, group_size, symmetric)          -> PackedWeight
     q4_dequant(packed, out_dtype)                       -> W_hat [n, k]
     q4_w4a16_gemm(x, packed)                            -> y [m, n] fp32
+    q4_w4a16_gemm_grouped(xs, packs)                    -> [y_i], one launch when m <= 16
     q4_last_kernel()                                    -> name of the last kernel run
 """
 from __future__ import annotations
@@ -22,16 +23,27 @@ import torch
 
 from . import _build
 
-__all__ = ["PackedWeight", "q4_quantize_pack", "q4_dequant", "q4_w4a16_gemm", "q4_last_kernel",
+__all__ = ["PackedWeight", "q4_quantize_pack", "q4_dequant", "q4_w4a16_gemm",
+           "q4_w4a16_gemm_grouped", "q4_last_kernel",
            "q4_qweight_words", "q4_scale_count", "q4_zero_words", "q4_layout_version",
            "library_path", "Q4Error"]
 
 Q4_F32, Q4_F16, Q4_BF16 = 0, 1, 2
 _DTYPE_CODE = {torch.float32: Q4_F32, torch.float16: Q4_F16, torch.bfloat16: Q4_BF16}
 
-EXPORTED = ("q4_quantize_pack", "q4_dequant", "q4_w4a16_gemm", "q4_qweight_words",
+EXPORTED = ("q4_quantize_pack", "q4_dequant", "q4_w4a16_gemm", "q4_w4a16_gemm_grouped",
+            "q4_qweight_words",
             "q4_scale_count", "q4_zero_words", "q4_status_str", "q4_last_kernel",
             "q4_layout_version")
+
+
+class GemmProblem(ctypes.Structure):
+    """q4_gemm_problem of the C ABI."""
+    _fields_ = [("x", ctypes.c_void_p), ("qweight", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("zeros", ctypes.c_void_p), ("n", ctypes.c_int64), ("y", ctypes.c_void_p)]
+
+
+MAX_GROUP = 8
 
 
 class Q4Error(RuntimeError):
@@ -63,6 +75,9 @@ def _load():
     lib.q4_dequant.restype = ctypes.c_int
     lib.q4_w4a16_gemm.argtypes = [vp, ctypes.c_int, i64, vp, vp, vp, i64, i64, i32, i32, vp, vp]
     lib.q4_w4a16_gemm.restype = ctypes.c_int
+    lib.q4_w4a16_gemm_grouped.argtypes = [ctypes.POINTER(GemmProblem), i32, ctypes.c_int, i64, i64,
+                                          i32, i32, vp]
+    lib.q4_w4a16_gemm_grouped.restype = ctypes.c_int
     lib.q4_qweight_words.argtypes = [i64, i64]
     lib.q4_qweight_words.restype = i64
     lib.q4_scale_count.argtypes = [i64, i64, i32]
@@ -184,3 +199,34 @@ def q4_w4a16_gemm(x: torch.Tensor, p: PackedWeight,
                                  _dev_ptr(p.scales), _dev_ptr(p.zeros), p.n, p.k,
                                  p.group_size, int(p.symmetric), _dev_ptr(y), _stream(x)))
     return y
+
+
+def q4_w4a16_gemm_grouped(xs, packs, outs=None):
+    """y_i = x_i · (S_i (u_i - z_i))^T for up to 8 problems sharing m, k, group size,
+    symmetry and activation dtype; with m <= 16 they run in one launch.  xs may be a
+    single tensor (shared by all problems) or one tensor per problem."""
+    packs = list(packs)
+    count = len(packs)
+    if not 1 <= count <= MAX_GROUP:
+        raise ValueError(f"1 to {MAX_GROUP} problems per call")
+    xs = [xs] * count if isinstance(xs, torch.Tensor) else list(xs)
+    if len(xs) != count:
+        raise ValueError("one activation tensor per problem (or one shared)")
+    p0, x0 = packs[0], xs[0]
+    for x, p in zip(xs, packs):
+        _need_cuda("x", x)
+        if (x.shape != x0.shape or x.dtype != x0.dtype or x.dim() != 2 or p.k != p0.k
+                or p.group_size != p0.group_size or p.symmetric != p0.symmetric or x.shape[1] != p.k):
+            raise ValueError("problems must share m, k, group size, symmetry and dtype")
+    if x0.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("activations must be fp16 or bf16")
+    m = x0.shape[0]
+    ys = list(outs) if outs is not None else [
+        torch.empty((m, p.n), dtype=torch.float32, device=x0.device) for p in packs]
+    arr = (GemmProblem * count)()
+    for i, (x, p, y) in enumerate(zip(xs, packs, ys)):
+        arr[i] = GemmProblem(x.data_ptr(), p.qweight.data_ptr(), p.scales.data_ptr(),
+                             None if p.zeros is None else p.zeros.data_ptr(), p.n, y.data_ptr())
+    _check(_load().q4_w4a16_gemm_grouped(arr, count, _DTYPE_CODE[x0.dtype], m, p0.k,
+                                         p0.group_size, int(p0.symmetric), _stream(x0)))
+    return ys

@@ -53,6 +53,13 @@ constexpr int kPZ = 2;                 // zero-point dwords per thread per tile 
 constexpr int kOOB = 0x40000000;       // a buffer offset past every load resource: reads 0
 constexpr uint32_t kStoreOOB = 0xFFFFFFF0u;  // a store offset past the y resource: dropped
 
+// The problems of one launch (a single one, or several sharing m, k, g and dtype):
+// workgroups [tile0[p], tile0[p+1]) serve problem p.
+struct GemvBatch {
+    q4::GemvProblem p[q4::kMaxGroup];
+    int count;
+};
+
 // One lane's share of one 128-column unit: 4 packed words (one per MFMA).
 struct Unit {
     uint32_t w[4];
@@ -139,13 +146,21 @@ __device__ __forceinline__ void unit_load(Unit& d, q4::rsrc rq, int qoff, int u,
 // LDS (16-byte vectors): activations [(M+1)][RS] | metadata x2 (each with a spare area
 // of one dword per thread) | partial sums x2 ([S][64] each).
 template <int G, bool SYM, bool XF16, int R, int D, int MAXT, int MINW, bool MULTI>
-__global__ __launch_bounds__(MAXT, MINW) void gemv_stream_kernel(const uint16_t* __restrict__ x, int M,
-                                                          const uint32_t* __restrict__ qweight,
-                                                          const uint16_t* __restrict__ scales,
-                                                          const uint32_t* __restrict__ zeros,
-                                                          int N, int K, float* __restrict__ y) {
+__global__ __launch_bounds__(MAXT, MINW) void gemv_stream_kernel(const GemvBatch bt, int M, int K) {
     constexpr int LW = G / 32;
     extern __shared__ q4::u32x4 lds[];
+    // this workgroup's problem (wave-uniform; MULTI launches carry a single problem)
+    int pi = 0;
+#pragma unroll
+    for (int i = 1; i < q4::kMaxGroup; ++i)
+        if (i < bt.count && (int)blockIdx.x >= bt.p[i].tile0) pi = i;
+    const uint16_t* __restrict__ x = reinterpret_cast<const uint16_t*>(bt.p[pi].x);
+    const uint32_t* __restrict__ qweight = bt.p[pi].qweight;
+    const uint16_t* __restrict__ scales = bt.p[pi].scales;
+    const uint32_t* __restrict__ zeros = bt.p[pi].zeros;
+    float* __restrict__ y = bt.p[pi].y;
+    const int N = bt.p[pi].n;
+    const int bx = (int)blockIdx.x - bt.p[pi].tile0;  // tile index within the problem
     const int tid = threadIdx.x, nthreads = blockDim.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -174,9 +189,9 @@ __global__ __launch_bounds__(MAXT, MINW) void gemv_stream_kernel(const uint16_t*
     const int ulast = u1 > u0 ? u1 - 1 : 0;
     const int nb = R * ((per + D * R - 1) / (D * R));  // batches per tile, whole ring turns
     // grid <= tiles; MULTI == false means grid == tiles (one tile per workgroup)
-    const int ntiles = MULTI ? (tiles - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 1;
+    const int ntiles = MULTI ? (tiles - 1 - bx) / (int)gridDim.x + 1 : 1;
 
-    auto tile_n0 = [&](int tl) { return ((int)blockIdx.x + tl * (int)gridDim.x) * 16; };
+    auto tile_n0 = [&](int tl) { return (bx + tl * (int)gridDim.x) * 16; };
 
     // metadata of tile ordinal tl (none for tl >= ntiles: every offset off the end): scales
     // block (16*n_groups fp16, copied entry by entry so no load straddles the end of the
@@ -497,9 +512,11 @@ __global__ __launch_bounds__(512) void gemv_chunk_kernel(const uint16_t* __restr
 
 int g_num_cus = 0;
 
+// One problem (batch == nullptr) or a batch of problems whose tiles add up to n rows.
 template <int G, bool SYM>
 hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16_t* sc,
-                  const uint32_t* zr, int n, int k, float* y, hipStream_t st, const char** kname) {
+                  const uint32_t* zr, int n, int k, float* y, hipStream_t st, const char** kname,
+                  const GemvBatch* batch = nullptr, int batch_tiles = 0) {
     if (g_num_cus == 0) {
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
@@ -513,7 +530,7 @@ hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16
     // dominates, so the tile is spread over up to 16 waves of 2-unit batches.  Otherwise
     // 8 waves of 2-unit batches.
     const int units_k = (k + 127) / 128;
-    const int tiles = (n + 15) / 16;
+    const int tiles = batch != nullptr ? batch_tiles : (n + 15) / 16;
     int shape;  // 0: up to 8 waves   1: up to 4 waves   2: up to 16 waves
     int waves;
     if (tiles >= 2 * g_num_cus) {
@@ -547,6 +564,7 @@ hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16
         waves = waves < 1 ? 1 : (waves > kMaxWaves ? kMaxWaves : waves);
     }
     const bool stream = stream_fits(waves);
+    if (!stream && batch != nullptr) return hipErrorNotSupported;  // one by one instead
     if (!stream && waves > kMaxWaves) waves = kMaxWaves;  // the chunked kernel's bound
     const int threads = 64 * waves;
     const size_t lds_stream = stream_lds(waves);
@@ -568,12 +586,19 @@ hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16
             return cached;
         };
         auto run = [&](auto k_multi, auto k_one, const char* name) {
-            const int cap = g_num_cus * per_cu(k_multi);
             *kname = name;
+            if (batch != nullptr) {  // several problems: one workgroup per tile
+                hipLaunchKernelGGL(k_one, dim3(tiles), dim3(threads), lds_stream, st, *batch, m, k);
+                return hipGetLastError();
+            }
+            GemvBatch one{};
+            one.p[0] = q4::GemvProblem{x, qw, sc, zr, y, n, 0};
+            one.count = 1;
+            const int cap = g_num_cus * per_cu(k_multi);
             if (tiles <= cap)
-                hipLaunchKernelGGL(k_one, dim3(tiles), dim3(threads), lds_stream, st, xp, m, qw, sc, zr, n, k, y);
+                hipLaunchKernelGGL(k_one, dim3(tiles), dim3(threads), lds_stream, st, one, m, k);
             else
-                hipLaunchKernelGGL(k_multi, dim3(cap), dim3(threads), lds_stream, st, xp, m, qw, sc, zr, n, k, y);
+                hipLaunchKernelGGL(k_multi, dim3(cap), dim3(threads), lds_stream, st, one, m, k);
             return hipGetLastError();
         };
         // A tile's batches are whole ring turns (D units per batch, R batches in flight);
@@ -648,3 +673,27 @@ hipError_t q4k_gemv(const void* x, int x_dtype, int m, const uint32_t* qweight,
     default: return launch<128, true>(x, x_dtype, m, qweight, scales, zeros, ni, ki, y, stream, kname);
     }
 }
+
+hipError_t q4k_gemv_grouped(const q4::GemvProblem* problems, int count, int x_dtype, int m,
+                            int64_t k, int g, int sym, hipStream_t stream, const char** kname) {
+    if (count < 1 || count > q4::kMaxGroup) return hipErrorInvalidValue;
+    GemvBatch batch{};
+    int tiles = 0;
+    for (int i = 0; i < count; ++i) {
+        batch.p[i] = problems[i];
+        batch.p[i].tile0 = tiles;
+        tiles += (problems[i].n + 15) / 16;
+    }
+    batch.count = count;
+    const int ki = (int)k, rows = 16 * tiles;
+    const void* x = problems[0].x;
+    switch (g * 2 + (sym ? 1 : 0)) {
+    case 64: return launch<32, false>(x, x_dtype, m, nullptr, nullptr, nullptr, rows, ki, nullptr, stream, kname, &batch, tiles);
+    case 65: return launch<32, true>(x, x_dtype, m, nullptr, nullptr, nullptr, rows, ki, nullptr, stream, kname, &batch, tiles);
+    case 128: return launch<64, false>(x, x_dtype, m, nullptr, nullptr, nullptr, rows, ki, nullptr, stream, kname, &batch, tiles);
+    case 129: return launch<64, true>(x, x_dtype, m, nullptr, nullptr, nullptr, rows, ki, nullptr, stream, kname, &batch, tiles);
+    case 256: return launch<128, false>(x, x_dtype, m, nullptr, nullptr, nullptr, rows, ki, nullptr, stream, kname, &batch, tiles);
+    default: return launch<128, true>(x, x_dtype, m, nullptr, nullptr, nullptr, rows, ki, nullptr, stream, kname, &batch, tiles);
+    }
+}
+

@@ -85,9 +85,11 @@ q4_status q4_dequant(const uint32_t* qweight, const uint16_t* scales, const uint
     return finish(e, name);
 }
 
-q4_status q4_w4a16_gemm(const void* x, q4_dtype x_dtype, int64_t m, const uint32_t* qweight,
-                        const uint16_t* scales, const uint32_t* zeros, int64_t n, int64_t k,
-                        int32_t group_size, int32_t symmetric, float* y, hipStream_t stream) {
+namespace {
+// The size, dtype, pointer and alignment rules of q4_w4a16_gemm for one problem.
+q4_status check_matmul(const void* x, q4_dtype x_dtype, int64_t m, const uint32_t* qweight,
+                       const uint16_t* scales, const uint32_t* zeros, int64_t n, int64_t k,
+                       int32_t group_size, int32_t symmetric, const float* y) {
     q4_status st = check_layout(n, k, group_size);
     if (st != Q4_OK) return st;
     if (k > kMaxMatmulK || n > kMaxMatmulN) return Q4_ERR_SHAPE;
@@ -96,6 +98,54 @@ q4_status q4_w4a16_gemm(const void* x, q4_dtype x_dtype, int64_t m, const uint32
     if (!x || !y) return Q4_ERR_NULL;
     if ((st = check_packed(qweight, scales, zeros, symmetric)) != Q4_OK) return st;
     if (!aligned(x, 16) || !aligned(y, 4)) return Q4_ERR_ALIGN;
+    return Q4_OK;
+}
+}  // namespace
+
+q4_status q4_w4a16_gemm_grouped(const q4_gemm_problem* problems, int32_t count,
+                                q4_dtype x_dtype, int64_t m, int64_t k, int32_t group_size,
+                                int32_t symmetric, hipStream_t stream) {
+    if (!problems) return Q4_ERR_NULL;
+    if (count < 1 || count > q4::kMaxGroup) return Q4_ERR_SHAPE;
+    int64_t rows = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        const q4_gemm_problem& p = problems[i];
+        const q4_status st = check_matmul(p.x, x_dtype, m, p.qweight, p.scales, p.zeros, p.n, k,
+                                          group_size, symmetric, p.y);
+        if (st != Q4_OK) return st;
+        rows += (p.n + 15) / 16 * 16;
+    }
+    const char* name = "";
+    if (m <= 16 && count > 1 && rows <= kMaxMatmulN) {
+        q4::GemvProblem gp[q4::kMaxGroup];
+        for (int32_t i = 0; i < count; ++i)
+            gp[i] = q4::GemvProblem{problems[i].x, problems[i].qweight, problems[i].scales,
+                                    symmetric ? nullptr : problems[i].zeros, problems[i].y,
+                                    (int)problems[i].n, 0};
+        const hipError_t e = q4k_gemv_grouped(gp, count, (int)x_dtype, (int)m, k, group_size,
+                                              symmetric ? 1 : 0, stream, &name);
+        if (e != hipErrorNotSupported) return finish(e, name);
+    }
+    for (int32_t i = 0; i < count; ++i) {  // one launch per problem
+        const q4_gemm_problem& p = problems[i];
+        hipError_t e;
+        if (m <= 16)
+            e = q4k_gemv(p.x, (int)x_dtype, (int)m, p.qweight, p.scales, p.zeros, p.n, k, group_size,
+                         symmetric ? 1 : 0, p.y, stream, &name);
+        else
+            e = q4k_gemm(p.x, (int)x_dtype, m, p.qweight, p.scales, p.zeros, p.n, k, group_size,
+                         symmetric ? 1 : 0, p.y, stream, &name);
+        if (e != hipSuccess) return Q4_ERR_LAUNCH;
+    }
+    return finish(hipSuccess, name);
+}
+
+q4_status q4_w4a16_gemm(const void* x, q4_dtype x_dtype, int64_t m, const uint32_t* qweight,
+                        const uint16_t* scales, const uint32_t* zeros, int64_t n, int64_t k,
+                        int32_t group_size, int32_t symmetric, float* y, hipStream_t stream) {
+    const q4_status st = check_matmul(x, x_dtype, m, qweight, scales, zeros, n, k, group_size,
+                                      symmetric, y);
+    if (st != Q4_OK) return st;
     const char* name = "";
     hipError_t e;
     if (m <= 16)

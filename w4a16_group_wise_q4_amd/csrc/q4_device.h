@@ -131,6 +131,24 @@ hipError_t q4k_dequant(const uint32_t* qweight, const uint16_t* scales, const ui
 hipError_t q4k_gemv(const void* x, int x_dtype, int m, const uint32_t* qweight,
                     const uint16_t* scales, const uint32_t* zeros, int64_t n, int64_t k, int g,
                     int sym, float* y, hipStream_t stream, const char** kname);
+// One problem of a grouped decode launch (y = x . x_hat^T); tile0 is filled by the launcher.
+namespace q4 {
+constexpr int kMaxGroup = 8;
+struct GemvProblem {
+    const void* x;
+    const uint32_t* qweight;
+    const uint16_t* scales;
+    const uint32_t* zeros;
+    float* y;
+    int n;
+    int tile0;
+};
+}  // namespace q4
+// Runs count problems (shared m <= 16, k, g, sym, dtype) in one launch when their
+// activations fit the streaming kernel; returns hipErrorNotSupported (enqueuing nothing)
+// otherwise, so the caller runs them one by one.
+hipError_t q4k_gemv_grouped(const q4::GemvProblem* problems, int count, int x_dtype, int m,
+                            int64_t k, int g, int sym, hipStream_t stream, const char** kname);
 hipError_t q4k_gemm(const void* x, int x_dtype, int64_t m, const uint32_t* qweight,
                     const uint16_t* scales, const uint32_t* zeros, int64_t n, int64_t k, int g,
                     int sym, float* y, hipStream_t stream, const char** kname);
