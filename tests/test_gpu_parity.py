@@ -199,7 +199,7 @@ def test_linear_tiny_reference(sym, m):
     note(f"linear tiny m={m} sym={sym}")
     p, _ = pack_guarded(w.to(DEV), 128, sym)
     y, kname = run_linear(x, p)
-    assert kname == ("q4_gemv_mfma_bf16" if m <= 16 else "q4_gemm_mfma_bf16")
+    assert kname in (gemv_kernels() if m <= 16 else {"q4_gemm_mfma_bf16"})
     packed = assert_pack_exact(p, host_input(w), 128, sym)
     assert_linear_close(y, host_input(x), packed, 256, 512, 128, sym, what=kname)
 
@@ -213,6 +213,7 @@ def test_gemv_decode_7b_full(idx):
     note(f"gemv {mat.name} m=1 g=128 asym")
     p, _ = pack_guarded(w.to(DEV), 128, False)
     y, kname = run_linear(x, p)
+    assert kname == "q4_gemv_tile_bf16"
     packed = assert_pack_exact(p, host_input(w), 128, False)
     assert_linear_close(y, host_input(x), packed, mat.n, mat.k, 128, False, what=kname)
 
@@ -234,9 +235,36 @@ def test_gemv_mlp_sweep(idx, g, sym):
         note(f"gemv {mat.name} m={m} g={g} sym={sym}")
         x = x16[:m].contiguous()
         y, kname = run_linear(x, p)
-        assert kname == "q4_gemv_mfma_bf16"
+        assert kname in gemv_kernels()
         assert_linear_close(y, host_input(x), packed, mat.n, mat.k, g, sym, cols=cols,
                             what=f"{kname} m={m}")
+
+
+def gemv_kernels(xdtype=torch.bfloat16):
+    """Names of the decode kernels for an activation dtype: the tile kernel (group size
+    128, m <= 4, K split evenly over the waves) and the streaming kernel."""
+    t = "f16" if xdtype == torch.float16 else "bf16"
+    return {f"q4_gemv_tile_{t}", f"q4_gemv_mfma_{t}"}
+
+
+# (m, n, k): every slice shape of the tile kernel (4, 8 or 16 units per wave, one to eight
+# waves), ragged tiles, m = 1..4
+TILE_CASES = [(1, 1, 512), (2, 17, 512), (4, 33, 1024), (3, 100, 2048), (2, 300, 5120),
+              (4, 48, 8192), (1, 130, 8192), (1, 16, 2560), (3, 15, 1536), (1, 40, 7168)]
+
+
+@pytest.mark.parametrize("m,n,k", TILE_CASES)
+@pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("sym", [False, True])
+def test_gemv_tile_cases(m, n, k, xdtype, sym):
+    w = torch.from_numpy(pins.random_weights(n + 5 * k + m, max(n, 12), k)[:n])
+    x = synthetic.activations(m, k, seed=m * 17 + k).to(xdtype)
+    note(f"gemv tile m={m} n={n} k={k} {xdtype} sym={sym}")
+    p, _ = pack_guarded(w.to(DEV), 128, sym)
+    y, kname = run_linear(x, p)
+    assert kname == ("q4_gemv_tile_f16" if xdtype == torch.float16 else "q4_gemv_tile_bf16")
+    packed = assert_pack_exact(p, host_input(w), 128, sym)
+    assert_linear_close(y, host_input(x), packed, n, k, 128, sym, what=kname)
 
 
 GEMV_EDGE = [(1, 16, 32, 32), (16, 1, 32, 32), (5, 37, 96, 32), (16, 33, 192, 64),
@@ -253,33 +281,34 @@ def test_gemv_edge_cases(m, n, k, g, xdtype, sym):
     note(f"gemv edge m={m} n={n} k={k} g={g} {xdtype} sym={sym}")
     p, _ = pack_guarded(w.to(DEV), g, sym)
     y, kname = run_linear(x, p)
-    assert kname == ("q4_gemv_mfma_f16" if xdtype == torch.float16 else "q4_gemv_mfma_bf16")
+    assert kname in gemv_kernels(xdtype)
     packed = assert_pack_exact(p, host_input(w), g, sym)
     assert_linear_close(y, host_input(x), packed, n, k, g, sym, what=kname)
 
 
-@pytest.mark.parametrize("m", [1, 5, 16, 17, 64])
+@pytest.mark.parametrize("m,g", [(1, 64), (5, 64), (16, 64), (17, 64), (64, 64), (1, 128),
+                                 (3, 128)])
 @pytest.mark.parametrize("sym", [False, True])
-def test_linear_special_inputs(m, sym):
+def test_linear_special_inputs(m, g, sym):
     """x = 0 gives exactly 0; one-hot x picks one dequantized column.  The decode GEMV
     reproduces it exactly (exact products, one scale multiply per group).  The prefill
     GEMM keeps its sums in units of the current group's scale and moves them to the next
     group's units with an fp32 ratio: a column in group j passes through two roundings
     (ratio, product) per later group and one final product, so its relative error is at
     most (2 * (G - 1 - j) + 1) * 2^-24 to first order."""
-    n, k, g = 48, 512, 64
+    n, k = 48, 512
     w = torch.from_numpy(pins.random_weights(5, n, k))
     p, _ = pack_guarded(w.to(DEV), g, sym)
     qo, so, zo = assert_pack_exact(p, host_input(w), g, sym)
     xhat = oracle.dequant(qo, so, zo, n, k, g, sym)
-    note(f"linear zero x m={m} sym={sym}")
+    note(f"linear zero x m={m} g={g} sym={sym}")
     y, _ = run_linear(torch.zeros(m, k, dtype=torch.bfloat16), p)
     assert np.all(y == 0)
     x = torch.zeros(m, k, dtype=torch.bfloat16)
     cols = [(7 * i + 3) % k for i in range(m)]
     for i, kk in enumerate(cols):
         x[i, kk] = 1.0
-    note(f"linear one-hot x m={m} sym={sym}")
+    note(f"linear one-hot x m={m} g={g} sym={sym}")
     y, _ = run_linear(x, p)
     for i, kk in enumerate(cols):
         if m <= 16:
@@ -290,13 +319,13 @@ def test_linear_special_inputs(m, sym):
             assert np.all(np.abs(y[i].astype(np.float64) - xhat[:, kk]) <= bound), (i, kk)
 
 
-@pytest.mark.parametrize("m", [1, 16, 17, 300])
+@pytest.mark.parametrize("m,g", [(1, 64), (16, 64), (17, 64), (300, 64), (1, 128), (4, 128)])
 @pytest.mark.parametrize("sym", [False, True])
-def test_linear_zero_scale_groups(m, sym):
+def test_linear_zero_scale_groups(m, g, sym):
     """Packed weights from elsewhere may hold S = 0 for a group (a group of zeros stored
     without the 1.0 substitute): such a group contributes exactly 0.  Zero scales sit at
     the first, last and consecutive groups of some rows and cover whole rows of others."""
-    n, k, g = 200, 1024, 64
+    n, k = 200, 1024
     G = k // g
     w = torch.from_numpy(pins.random_weights(11, n, k))
     p, _ = pack_guarded(w.to(DEV), g, sym)
@@ -311,7 +340,7 @@ def test_linear_zero_scale_groups(m, sym):
     so[n - 1, :] = 0
     p.scales.copy_(torch.from_numpy(so.view(np.float16)).to(DEV))
     x = synthetic.activations(m, k, seed=13)
-    note(f"linear zero-scale groups m={m} sym={sym}")
+    note(f"linear zero-scale groups m={m} g={g} sym={sym}")
     y, kname = run_linear(x, p)
     assert np.all(y[:, 5] == 0) and np.all(y[:, n - 1] == 0)
     assert_linear_close(y, host_input(x), (qo, so, zo), n, k, g, sym, what=kname)
@@ -329,7 +358,7 @@ def test_gemm_grouped_decode_pair():
     guards = [guarded((1, p.n), torch.float32, SENTINEL_F32) for p in packs]
     q4.q4_w4a16_gemm_grouped(x.to(DEV), packs, outs=[v for _, v in guards])
     torch.cuda.synchronize()
-    assert q4.q4_last_kernel() == "q4_gemv_mfma_bf16"
+    assert q4.q4_last_kernel() == "q4_gemv_tile_bf16"
     for w, p, (gb, gv) in zip(ws, packs, guards):
         assert guard_intact(gb), "store outside y"
         packed = assert_pack_exact(p, host_input(w), 128, False)
@@ -351,7 +380,7 @@ def test_gemm_grouped_mixed(m, g, sym, xdtype):
     guards = [guarded((m, n), torch.float32, SENTINEL_F32) for n in ns]
     q4.q4_w4a16_gemm_grouped([x.to(DEV) for x in xs], packs, outs=[v for _, v in guards])
     torch.cuda.synchronize()
-    assert q4.q4_last_kernel().startswith("q4_gemv_mfma_")
+    assert q4.q4_last_kernel() in gemv_kernels(xdtype)
     for w, x, p, (gb, gv) in zip(ws, xs, packs, guards):
         assert guard_intact(gb), "store outside y"
         packed = assert_pack_exact(p, host_input(w), g, sym)

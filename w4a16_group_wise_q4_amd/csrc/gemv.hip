@@ -348,6 +348,167 @@ __global__ __launch_bounds__(MAXT, MINW) void gemv_stream_kernel(const GemvBatch
 }
 
 // ---------------------------------------------------------------------------------------
+// Tile kernel: group size 128, m <= 4, and K an exact multiple of the waves' slices.  One
+// 16-row tile per workgroup; its S waves split K into equal slices of UPW 128-column units
+// (one group each).  A wave issues every load it needs at once, in wait order: its slice
+// of the activations, the scales and zero points of its groups (straight into registers:
+// lane l needs those of row l%16 only), then its UPW units of packed weights.  The
+// activation slice goes to a wave-private LDS region in the decoder's slot order, so no
+// barrier precedes the arithmetic; only the cross-wave sum of the tile's partial results
+// meets at one.  Activation rows past m feed MFMA rows whose outputs are never stored, so
+// lane l reads row min(l%16, m-1) and no zero padding is staged.  Unit offsets are
+// compile-time constants, so loads and LDS reads carry them as immediates.
+//
+// LDS (16-byte vectors): S x [MQ][UPW*16] activation slices | S x 64 x MQ partial sums.
+template <bool SYM, bool XF16, int UPW, int MQ, bool GROUPED>
+__global__ __launch_bounds__(512) void gemv_tile_kernel(const GemvBatch bt, int M, int K) {
+    constexpr int XV = UPW / 4;      // activation vectors per lane per row of the slice
+    constexpr int SV = UPW / 2;      // scale dwords per lane (two fp16 each)
+    constexpr int SLICE = UPW * 16;  // activation vectors per row of the slice
+    constexpr int ZV = UPW > 8 ? 2 : 1;
+    extern __shared__ q4::u32x4 lds[];
+    int pi = 0;
+    if constexpr (GROUPED) {
+#pragma unroll
+        for (int i = 1; i < q4::kMaxGroup; ++i)
+            if (i < bt.count && (int)blockIdx.x >= bt.p[i].tile0) pi = i;
+    }
+    const uint16_t* __restrict__ x = reinterpret_cast<const uint16_t*>(bt.p[pi].x);
+    const uint32_t* __restrict__ qweight = bt.p[pi].qweight;
+    const uint16_t* __restrict__ scales = bt.p[pi].scales;
+    const uint32_t* __restrict__ zeros = bt.p[pi].zeros;
+    float* __restrict__ y = bt.p[pi].y;
+    const int N = bt.p[pi].n;
+    const int n0 = ((int)blockIdx.x - bt.p[pi].tile0) * 16;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int S = blockDim.x >> 6;
+    const int r = lane & 15, c = lane >> 4;
+    const int KW = K >> 3, ng = K >> 7, zw = (ng + 7) >> 3;
+    const int rows = N - n0 < 16 ? N - n0 : 16;
+    const int U0 = w * UPW;  // this wave's first unit (= group)
+
+    // ---- prologue: every load of the wave, in the order it is waited for
+    q4::u32x4 xv[MQ][XV];
+    {
+        const q4::rsrc rx = q4::make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+#pragma unroll
+        for (int m = 0; m < MQ; ++m)
+#pragma unroll
+            for (int j = 0; j < XV; ++j) {
+                const int off = (m * K + U0 * 128 + (j * 64 + lane) * 8) * 2;
+                xv[m][j] = q4::buf_load_x4(rx, m < M ? off : kOOB, 0);
+            }
+    }
+    uint32_t sv[SV];
+    {
+        const q4::rsrc rs = q4::make_rsrc(scales + (int64_t)n0 * ng, (uint32_t)rows * ng * 2u);
+        const int so = r < rows ? (r * ng + U0) * 2 : kOOB;
+        if constexpr (SV == 2) {
+            const q4::u32x2 t = q4::buf_load_x2(rs, so, 0);
+            sv[0] = t[0];
+            sv[1] = t[1];
+        } else {
+#pragma unroll
+            for (int j = 0; j < SV / 4; ++j) {
+                const q4::u32x4 t = q4::buf_load_x4(rs, so, 16 * j);
+                sv[4 * j] = t[0];
+                sv[4 * j + 1] = t[1];
+                sv[4 * j + 2] = t[2];
+                sv[4 * j + 3] = t[3];
+            }
+        }
+    }
+    uint32_t zv[ZV] = {};
+    if constexpr (!SYM) {
+        const q4::rsrc rz = q4::make_rsrc(zeros + (int64_t)n0 * zw, (uint32_t)rows * zw * 4u);
+        const int zo = r < rows ? (r * zw + (U0 >> 3)) * 4 : kOOB;
+        if constexpr (ZV == 2) {
+            const q4::u32x2 t = q4::buf_load_x2(rz, zo, 0);
+            zv[0] = t[0];
+            zv[1] = t[1];
+        } else {
+            zv[0] = q4::buf_load_x1(rz, zo, 0);
+        }
+    }
+    q4::u32x4 wv[UPW];
+    {
+        const q4::rsrc rq = q4::make_rsrc(qweight + (int64_t)n0 * KW, (uint32_t)rows * KW * 4u);
+        const int qo = r < rows ? r * KW * 4 + c * 16 : kOOB;
+#pragma unroll
+        for (int u = 0; u < UPW; ++u) wv[u] = q4::buf_load_x4(rq, qo, (U0 + u) * 64);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- this wave's activation slice into its LDS region, in the decoder's slot order
+    q4::u32x4* xw = lds + w * (MQ * SLICE);
+#pragma unroll
+    for (int m = 0; m < MQ; ++m)
+#pragma unroll
+        for (int j = 0; j < XV; ++j) xw[m * SLICE + j * 64 + lane] = q4::pair_perm(xv[m][j]);
+
+    // ---- dequantize and multiply, one unit (one group) at a time, as the loads land
+    const int mrow = r < M ? r : M - 1;
+    const q4::u32x4* xr = xw + mrow * SLICE + 4 * c;
+    const uint32_t kMask = q4::vreg_const(0x000F000Fu);
+    const uint32_t kBias = q4::vreg_const(0x43004300u);
+    float acc[MQ];
+#pragma unroll
+    for (int q = 0; q < MQ; ++q) acc[q] = 0.f;
+#pragma unroll
+    for (int u = 0; u < UPW; ++u) {
+        q4::u32x4 xa[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) xa[a] = xr[u * 16 + a];
+        const uint32_t sw = sv[u >> 1];
+        const float s = q4::f16_bits_to_float((uint16_t)((u & 1) ? (sw >> 16) : sw));
+        int z = 8;
+        if constexpr (!SYM) z = (int)((zv[u >> 3] >> (4 * ((U0 + u) & 7))) & 0xFu);
+        q4::f32x4 dv = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (XF16) {
+            const _Float16 b = (_Float16)(1024 + z);
+            const q4::f16x2 bias = {b, b};
+#pragma unroll
+            for (int a = 0; a < 4; ++a) dv = q4::mfma_f16(xa[a], q4::decode_f16_exact(wv[u][a], bias), dv);
+#pragma unroll
+            for (int q = 0; q < MQ; ++q) acc[q] += s * dv[q];
+        } else {
+            const uint32_t zb = (uint32_t)z * 0x00010001u + kBias;  // bf16 (128+z) x2
+            const q4::u32x4 zop = {zb, zb, zb, zb};
+            q4::f32x4 dc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                dv = q4::mfma_bf16(xa[a], q4::decode_bf16_biased(wv[u][a], kMask, kBias), dv);
+                dc = q4::mfma_bf16(xa[a], zop, dc);
+            }
+#pragma unroll
+            for (int q = 0; q < MQ; ++q) acc[q] += s * (dv[q] - dc[q]);
+        }
+    }
+
+    // ---- cross-wave sum (lanes 0..15 hold rows m = 0..MQ-1 of the tile's 16 columns)
+    float* red = reinterpret_cast<float*>(lds + S * MQ * SLICE);
+#pragma unroll
+    for (int q = 0; q < MQ; ++q) red[(w * 64 + lane) * MQ + q] = acc[q];
+    __syncthreads();
+    if (w == 0) {
+        float sum[MQ];
+#pragma unroll
+        for (int q = 0; q < MQ; ++q) sum[q] = 0.f;
+        for (int v = 0; v < S; ++v)
+#pragma unroll
+            for (int q = 0; q < MQ; ++q) sum[q] += red[(v * 64 + lane) * MQ + q];
+        const q4::rsrc ry = q4::make_rsrc(y, (uint32_t)M * (uint32_t)N * 4u);
+#pragma unroll
+        for (int q = 0; q < MQ; ++q) {
+            const bool st = lane < 16 && q < M && r < rows;
+            const uint32_t off = st ? ((uint32_t)q * (uint32_t)N + (uint32_t)(n0 + r)) * 4u : kStoreOOB;
+            __builtin_amdgcn_raw_buffer_store_b32(q4::f32_bits(sum[q]), ry, (int)off, 0, 0);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
 // Chunked kernel (the activations do not fit in LDS): one tile per workgroup, activations
 // staged in column chunks.
 // LDS layout (16-byte vectors):
@@ -512,6 +673,54 @@ __global__ __launch_bounds__(512) void gemv_chunk_kernel(const uint16_t* __restr
 
 int g_num_cus = 0;
 
+// The tile kernel's shape for group size 128 and m <= 4: K in S equal slices of UPW units
+// (UPW in {4, 8, 16}, S <= 8, four waves preferred), activations within the LDS budget.
+// Returns false when K does not split that way.
+bool tile_shape(int m, int k, int* upw, int* waves) {
+    if (m > 4 || k % 128 != 0) return false;
+    const int units = k / 128;
+    *upw = 0;
+    if (units % 4 == 0 && (units == 16 || units == 32 || units == 64)) {
+        *upw = units / 4;
+        *waves = 4;
+    }
+    for (int u : {8, 16, 4})
+        if (*upw == 0 && units % u == 0 && units / u <= 8) {
+            *upw = u;
+            *waves = units / u;
+        }
+    const int mq = m <= 1 ? 1 : 4;
+    return *upw != 0 && (size_t)mq * k * 2 + (size_t)*waves * 64 * mq * 4 <= (size_t)kLdsBudget;
+}
+
+template <bool SYM, bool XF16, bool GR>
+hipError_t launch_tile_x(int upw, int mq, dim3 grid, dim3 block, size_t lds, hipStream_t st,
+                         const GemvBatch& bt, int m, int k) {
+#define Q4_TILE(U, Q)                                                                                    \
+    if (upw == U && mq == Q) {                                                                           \
+        hipLaunchKernelGGL((gemv_tile_kernel<SYM, XF16, U, Q, GR>), grid, block, lds, st, bt, m, k);    \
+        return hipGetLastError();                                                                        \
+    }
+    Q4_TILE(4, 1) Q4_TILE(8, 1) Q4_TILE(16, 1) Q4_TILE(4, 4) Q4_TILE(8, 4) Q4_TILE(16, 4)
+#undef Q4_TILE
+    return hipErrorInvalidValue;
+}
+
+template <bool SYM>
+hipError_t launch_tile(int xd, int m, int k, int upw, int waves, int tiles, const GemvBatch& bt,
+                       hipStream_t st, const char** kname) {
+    const int mq = m <= 1 ? 1 : 4;
+    const size_t lds = (size_t)mq * k * 2 + (size_t)waves * 64 * mq * 4;
+    const dim3 grid(tiles), block(64 * waves);
+    const bool grouped = bt.count > 1;
+    *kname = xd == 1 ? "q4_gemv_tile_f16" : "q4_gemv_tile_bf16";
+    if (xd == 1)
+        return grouped ? launch_tile_x<SYM, true, true>(upw, mq, grid, block, lds, st, bt, m, k)
+                       : launch_tile_x<SYM, true, false>(upw, mq, grid, block, lds, st, bt, m, k);
+    return grouped ? launch_tile_x<SYM, false, true>(upw, mq, grid, block, lds, st, bt, m, k)
+                   : launch_tile_x<SYM, false, false>(upw, mq, grid, block, lds, st, bt, m, k);
+}
+
 // One problem (batch == nullptr) or a batch of problems whose tiles add up to n rows.
 template <int G, bool SYM>
 hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16_t* sc,
@@ -531,6 +740,23 @@ hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16
     // 8 waves of 2-unit batches.
     const int units_k = (k + 127) / 128;
     const int tiles = batch != nullptr ? batch_tiles : (n + 15) / 16;
+    if constexpr (G == 128) {
+        // the tile kernel reads scales as dwords: every scale array 4-byte aligned
+        bool sc4 = true;
+        if (batch != nullptr) {
+            for (int i = 0; i < batch->count; ++i) sc4 = sc4 && ((uintptr_t)batch->p[i].scales & 3) == 0;
+        } else {
+            sc4 = ((uintptr_t)sc & 3) == 0;
+        }
+        int upw = 0, tw = 0;
+        if (sc4 && tile_shape(m, k, &upw, &tw)) {
+            if (batch != nullptr) return launch_tile<SYM>(xd, m, k, upw, tw, tiles, *batch, st, kname);
+            GemvBatch one{};
+            one.p[0] = q4::GemvProblem{x, qw, sc, zr, y, n, 0};
+            one.count = 1;
+            return launch_tile<SYM>(xd, m, k, upw, tw, tiles, one, st, kname);
+        }
+    }
     int shape;  // 0: up to 8 waves   1: up to 4 waves   2: up to 16 waves
     int waves;
     if (tiles >= 2 * g_num_cus) {
