@@ -247,10 +247,11 @@ def gemv_kernels(xdtype=torch.bfloat16):
     return {f"q4_gemv_tile_{t}", f"q4_gemv_mfma_{t}"}
 
 
-# (m, n, k): every slice shape of the tile kernel (4, 8 or 16 units per wave, one to eight
-# waves), ragged tiles, m = 1..4
+# (m, n, k): every slice width of the tile kernel (2, 4, 8, 12 and 16 units per wave, two
+# to fourteen waves, a short last slice), ragged tiles, m = 1..4
 TILE_CASES = [(1, 1, 512), (2, 17, 512), (4, 33, 1024), (3, 100, 2048), (2, 300, 5120),
-              (4, 48, 8192), (1, 130, 8192), (1, 16, 2560), (3, 15, 1536), (1, 40, 7168)]
+              (4, 48, 8192), (1, 130, 8192), (1, 16, 2560), (3, 15, 1536), (1, 40, 7168),
+              (1, 70, 11008), (2, 50, 11008), (1, 20, 28672), (3, 9, 14336)]
 
 
 @pytest.mark.parametrize("m,n,k", TILE_CASES)
