@@ -254,18 +254,36 @@ TILE_CASES = [(1, 1, 512), (2, 17, 512), (4, 33, 1024), (3, 100, 2048), (2, 300,
               (1, 70, 11008), (2, 50, 11008), (1, 20, 28672), (3, 9, 14336)]
 
 
+def tile_fits(g, m, k, n, num_cus=256):
+    """Whether the launcher picks the tile kernel: the same rule as its shape search
+    (slices of 2..16 units, at most 16 waves at m = 1 and 8 otherwise, an even group count,
+    activations and partial sums within 96 KiB of LDS)."""
+    if m > 4 or k % 128 or (k // g) % 2:
+        return False
+    units, mq = k // 128, (1 if m <= 1 else 4)
+    max_upw = {128: 16, 64: 12, 32: 8}[g]
+    for u in (2, 4, 8, 12, 16):
+        sw = -(-units // u)
+        if u <= max_upw and sw <= (16 if mq == 1 else 8) and \
+                m * sw * u * 256 + sw * 64 * mq * 4 <= 96 * 1024:
+            return True
+    return False
+
+
 @pytest.mark.parametrize("m,n,k", TILE_CASES)
+@pytest.mark.parametrize("g", [32, 64, 128])
 @pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
 @pytest.mark.parametrize("sym", [False, True])
-def test_gemv_tile_cases(m, n, k, xdtype, sym):
-    w = torch.from_numpy(pins.random_weights(n + 5 * k + m, max(n, 12), k)[:n])
+def test_gemv_tile_cases(m, n, k, g, xdtype, sym):
+    w = torch.from_numpy(pins.random_weights(n + 5 * k + m + g, max(n, 12), k)[:n])
     x = synthetic.activations(m, k, seed=m * 17 + k).to(xdtype)
-    note(f"gemv tile m={m} n={n} k={k} {xdtype} sym={sym}")
-    p, _ = pack_guarded(w.to(DEV), 128, sym)
+    note(f"gemv tile m={m} n={n} k={k} g={g} {xdtype} sym={sym}")
+    p, _ = pack_guarded(w.to(DEV), g, sym)
     y, kname = run_linear(x, p)
-    assert kname == ("q4_gemv_tile_f16" if xdtype == torch.float16 else "q4_gemv_tile_bf16")
-    packed = assert_pack_exact(p, host_input(w), 128, sym)
-    assert_linear_close(y, host_input(x), packed, n, k, 128, sym, what=kname)
+    t = "f16" if xdtype == torch.float16 else "bf16"
+    assert kname == (f"q4_gemv_tile_{t}" if tile_fits(g, m, k, n) else f"q4_gemv_mfma_{t}")
+    packed = assert_pack_exact(p, host_input(w), g, sym)
+    assert_linear_close(y, host_input(x), packed, n, k, g, sym, what=kname)
 
 
 GEMV_EDGE = [(1, 16, 32, 32), (16, 1, 32, 32), (5, 37, 96, 32), (16, 33, 192, 64),

@@ -39,6 +39,7 @@
 // fp16 activations: 1024 + u in fp16 minus (1024 + z) with one packed fp16 subtraction
 // gives the exact u - z.  Either way products are exact and sums are fp32.
 #include "q4_device.h"
+#include "gemv_tile.h"
 
 namespace {
 
@@ -53,12 +54,7 @@ constexpr int kPZ = 2;                 // zero-point dwords per thread per tile 
 constexpr int kOOB = 0x40000000;       // a buffer offset past every load resource: reads 0
 constexpr uint32_t kStoreOOB = 0xFFFFFFF0u;  // a store offset past the y resource: dropped
 
-// The problems of one launch (a single one, or several sharing m, k, g and dtype):
-// workgroups [tile0[p], tile0[p+1]) serve problem p.
-struct GemvBatch {
-    q4::GemvProblem p[q4::kMaxGroup];
-    int count;
-};
+using GemvBatch = q4::GemvBatch;
 
 // One lane's share of one 128-column unit: 4 packed words (one per MFMA).
 struct Unit {
@@ -348,187 +344,6 @@ __global__ __launch_bounds__(MAXT, MINW) void gemv_stream_kernel(const GemvBatch
 }
 
 // ---------------------------------------------------------------------------------------
-// Tile kernel: group size 128, m <= 4.  One 16-row tile per workgroup; its S waves split K
-// into slices of UPW 128-column units (one group each), wave w taking units [w*UPW,
-// w*UPW + nu) with nu = min(UPW, units - w*UPW), so only the last wave may be short.  A
-// wave issues every load it needs at once, in wait order: its slice of the activations,
-// the scales and zero points of its groups (straight into registers: lane l needs those of
-// row l%16 only), then its packed weights; slots past nu read nothing (an offset past the
-// buffer) and are masked out of the sums.  The activation slice goes to a wave-private LDS
-// region in the decoder's slot order, so no barrier precedes the arithmetic; only the
-// cross-wave sum of the tile's partial results meets at one.  Activation rows past m feed
-// MFMA rows whose outputs are never stored, so lane l reads row min(l%16, m-1) and no zero
-// padding is staged.  Unit offsets are compile-time constants, so loads and LDS reads
-// carry them as immediates.
-//
-// LDS (16-byte vectors): S x [m][UPW*16] activation slices | S x 64 x MQ partial sums.
-template <bool SYM, bool XF16, int UPW, int MQ, bool GROUPED>
-__global__ __launch_bounds__(MQ == 1 ? 1024 : 512) void gemv_tile_kernel(const GemvBatch bt, int M, int K) {
-    constexpr int XV = UPW >= 4 ? UPW / 4 : 1;  // activation vectors per lane per row of the slice
-    constexpr int SV = UPW / 2;                 // scale dwords per lane (two fp16 each)
-    constexpr int SLICE = UPW * 16;             // activation vectors per row of the slice
-    constexpr int ZV = UPW > 8 ? 2 : 1;         // zero-point words spanned by a slice
-    extern __shared__ q4::u32x4 lds[];
-    int pi = 0;
-    if constexpr (GROUPED) {
-#pragma unroll
-        for (int i = 1; i < q4::kMaxGroup; ++i)
-            if (i < bt.count && (int)blockIdx.x >= bt.p[i].tile0) pi = i;
-    }
-    const uint16_t* __restrict__ x = reinterpret_cast<const uint16_t*>(bt.p[pi].x);
-    const uint32_t* __restrict__ qweight = bt.p[pi].qweight;
-    const uint16_t* __restrict__ scales = bt.p[pi].scales;
-    const uint32_t* __restrict__ zeros = bt.p[pi].zeros;
-    float* __restrict__ y = bt.p[pi].y;
-    const int N = bt.p[pi].n;
-    const int n0 = ((int)blockIdx.x - bt.p[pi].tile0) * 16;
-    const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    const int S = blockDim.x >> 6;
-    const int r = lane & 15, c = lane >> 4;
-    const int KW = K >> 3, ng = K >> 7, zw = (ng + 7) >> 3;
-    const int rows = N - n0 < 16 ? N - n0 : 16;
-    const int U0 = w * UPW;  // this wave's first unit (= group); even, as UPW is
-    const int nu = ng - U0 < UPW ? ng - U0 : UPW;
-
-    // ---- prologue: every load of the wave, in the order it is waited for
-    q4::u32x4 xv[MQ][XV];
-    {
-        const q4::rsrc rx = q4::make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
-#pragma unroll
-        for (int m = 0; m < MQ; ++m)
-#pragma unroll
-            for (int j = 0; j < XV; ++j) {
-                // a two-unit slice has 32 vectors per row: lanes 32..63 repeat 0..31
-                const int v = UPW >= 4 ? j * 64 + lane : (lane & 31);
-                const int off = (m * K + U0 * 128 + v * 8) * 2;
-                xv[m][j] = q4::buf_load_x4(rx, m < M ? off : kOOB, 0);
-            }
-    }
-    uint32_t sv[SV];
-    {
-        const q4::rsrc rs = q4::make_rsrc(scales + (int64_t)n0 * ng, (uint32_t)rows * ng * 2u);
-        const int so = r < rows ? (r * ng + U0) * 2 : kOOB;
-#pragma unroll
-        for (int j = 0; j < SV / 4; ++j) {
-            const q4::u32x4 t = q4::buf_load_x4(rs, so, 16 * j);
-            sv[4 * j] = t[0];
-            sv[4 * j + 1] = t[1];
-            sv[4 * j + 2] = t[2];
-            sv[4 * j + 3] = t[3];
-        }
-        if constexpr (SV % 4 >= 2) {
-            const q4::u32x2 t = q4::buf_load_x2(rs, so, 16 * (SV / 4));
-            sv[SV / 4 * 4] = t[0];
-            sv[SV / 4 * 4 + 1] = t[1];
-        }
-        if constexpr (SV % 2 == 1) sv[SV - 1] = q4::buf_load_x1(rs, so, 4 * (SV - 1));
-    }
-    uint32_t zv[ZV] = {};
-    if constexpr (!SYM) {
-        const q4::rsrc rz = q4::make_rsrc(zeros + (int64_t)n0 * zw, (uint32_t)rows * zw * 4u);
-        const int zo = r < rows ? (r * zw + (U0 >> 3)) * 4 : kOOB;
-        if constexpr (ZV == 2) {
-            const q4::u32x2 t = q4::buf_load_x2(rz, zo, 0);
-            zv[0] = t[0];
-            zv[1] = t[1];
-        } else {
-            zv[0] = q4::buf_load_x1(rz, zo, 0);
-        }
-    }
-    q4::u32x4 wv[UPW];
-    {
-        const q4::rsrc rq = q4::make_rsrc(qweight + (int64_t)n0 * KW, (uint32_t)rows * KW * 4u);
-        const int qo = r < rows ? r * KW * 4 + c * 16 : kOOB;
-#pragma unroll
-        for (int u = 0; u < UPW; ++u) wv[u] = q4::buf_load_x4(rq, qo, u < nu ? (U0 + u) * 64 : kOOB);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // ---- this wave's activation slice into its LDS region, in the decoder's slot order.
-    // Rows m..MQ-1 (zeros) go to this wave's partial-sum slots, which it overwrites later:
-    // no store (and so no load) sits behind a branch.
-    q4::u32x4* xw = lds + w * (M * SLICE);
-    q4::u32x4* spare = lds + S * M * SLICE + w * 64 + lane;
-#pragma unroll
-    for (int m = 0; m < MQ; ++m)
-#pragma unroll
-        for (int j = 0; j < XV; ++j) {
-            q4::u32x4* dst = xw + m * SLICE + (UPW >= 4 ? j * 64 + lane : (lane & 31));
-            *(m == 0 || m < M ? dst : spare) = q4::pair_perm(xv[m][j]);
-        }
-
-    // zero points of the slice's groups from nibble 0 on (a slice may start mid-word)
-    uint32_t zlo = zv[0], zhi = ZV == 2 ? zv[ZV - 1] : 0u;
-    if constexpr (!SYM && UPW % 8 != 0) {
-        const uint32_t sh = 4u * (uint32_t)(U0 & 7);
-        zlo = __builtin_amdgcn_alignbit(zhi, zv[0], sh);
-        zhi = ZV == 2 ? zhi >> sh : 0u;
-    }
-
-    // ---- dequantize and multiply, one unit (one group) at a time, as the loads land
-    const int mrow = r < M ? r : M - 1;
-    const q4::u32x4* xr = xw + mrow * SLICE + 4 * c;
-    const uint32_t kMask = q4::vreg_const(0x000F000Fu);
-    const uint32_t kBias = q4::vreg_const(0x43004300u);
-    float acc[MQ];
-#pragma unroll
-    for (int q = 0; q < MQ; ++q) acc[q] = 0.f;
-#pragma unroll
-    for (int u = 0; u < UPW; ++u) {
-        const bool valid = u < nu;
-        q4::u32x4 xa[4];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) xa[a] = xr[u * 16 + a];
-        const uint32_t sw = sv[u >> 1];
-        const float s = q4::f16_bits_to_float((uint16_t)((u & 1) ? (sw >> 16) : sw));
-        int z = 8;
-        if constexpr (!SYM) z = (int)(((u < 8 ? zlo : zhi) >> (4 * (u & 7))) & 0xFu);
-        q4::f32x4 dv = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (XF16) {
-            const _Float16 b = (_Float16)(1024 + z);
-            const q4::f16x2 bias = {b, b};
-#pragma unroll
-            for (int a = 0; a < 4; ++a) dv = q4::mfma_f16(xa[a], q4::decode_f16_exact(wv[u][a], bias), dv);
-#pragma unroll
-            for (int q = 0; q < MQ; ++q) acc[q] = valid ? acc[q] + s * dv[q] : acc[q];
-        } else {
-            const uint32_t zb = (uint32_t)z * 0x00010001u + kBias;  // bf16 (128+z) x2
-            const q4::u32x4 zop = {zb, zb, zb, zb};
-            q4::f32x4 dc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                dv = q4::mfma_bf16(xa[a], q4::decode_bf16_biased(wv[u][a], kMask, kBias), dv);
-                dc = q4::mfma_bf16(xa[a], zop, dc);
-            }
-#pragma unroll
-            for (int q = 0; q < MQ; ++q) acc[q] = valid ? acc[q] + s * (dv[q] - dc[q]) : acc[q];
-        }
-    }
-
-    // ---- cross-wave sum (lanes 0..15 hold rows m = 0..MQ-1 of the tile's 16 columns)
-    float* red = reinterpret_cast<float*>(lds + S * M * SLICE);
-#pragma unroll
-    for (int q = 0; q < MQ; ++q) red[(w * 64 + lane) * MQ + q] = acc[q];
-    __syncthreads();
-    if (w == 0) {
-        float sum[MQ];
-#pragma unroll
-        for (int q = 0; q < MQ; ++q) sum[q] = 0.f;
-        for (int v = 0; v < S; ++v)
-#pragma unroll
-            for (int q = 0; q < MQ; ++q) sum[q] += red[(v * 64 + lane) * MQ + q];
-        const q4::rsrc ry = q4::make_rsrc(y, (uint32_t)M * (uint32_t)N * 4u);
-#pragma unroll
-        for (int q = 0; q < MQ; ++q) {
-            const bool st = lane < 16 && q < M && r < rows;
-            const uint32_t off = st ? ((uint32_t)q * (uint32_t)N + (uint32_t)(n0 + r)) * 4u : kStoreOOB;
-            __builtin_amdgcn_raw_buffer_store_b32(q4::f32_bits(sum[q]), ry, (int)off, 0, 0);
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------------------
 // Chunked kernel (the activations do not fit in LDS): one tile per workgroup, activations
 // staged in column chunks.
 // LDS layout (16-byte vectors):
@@ -693,65 +508,6 @@ __global__ __launch_bounds__(512) void gemv_chunk_kernel(const uint16_t* __restr
 
 int g_num_cus = 0;
 
-// The tile kernel's shape for group size 128 and m <= 4: S slices of UPW units (UPW in
-// {2, 4, 8, 12, 16}; S = ceil(units / UPW) waves, at most 16 for m = 1 and 8 otherwise, the
-// kernel's launch bound), an even number of groups per row (the scales are read as
-// dwords) and activations within the LDS budget.  Among the shapes that fit, the one
-// nearest the target wave count wins, then the one with fewer idle slots.  The target is
-// eight waves while one round of eight-wave workgroups holds every tile (the arithmetic
-// of a tile spreads over more SIMDs and the tail after the last load is short), four
-// when the tiles need several rounds (more loads in flight per wave, less per-workgroup
-// overhead per byte).  Returns false when no shape fits.
-bool tile_shape(int m, int k, int tiles, int* upw, int* waves) {
-    if (m > 4 || k % 128 != 0 || (k / 128) % 2 != 0) return false;
-    const int units = k / 128, mq = m <= 1 ? 1 : 4, max_waves = mq == 1 ? 16 : 8;
-    // with more tiles than one round of eight-wave workgroups holds, fewer waves per tile
-    const int target = tiles > 4 * (g_num_cus > 0 ? g_num_cus : 256) ? 4 : 8;
-    *upw = 0;
-    for (int u : {2, 4, 8, 12, 16}) {
-        const int sw = (units + u - 1) / u;
-        if (sw > max_waves || (size_t)m * sw * u * 256 + (size_t)sw * 64 * mq * 4 > (size_t)kLdsBudget)
-            continue;
-        auto key = [&](int uu, int ww) {  // smaller is better
-            return (ww > target ? ww - target : target - ww) * 4096 + (ww * uu - units);
-        };
-        if (*upw == 0 || key(u, sw) < key(*upw, *waves)) {
-            *upw = u;
-            *waves = sw;
-        }
-    }
-    return *upw != 0;
-}
-
-template <bool SYM, bool XF16, bool GR>
-hipError_t launch_tile_x(int upw, int mq, dim3 grid, dim3 block, size_t lds, hipStream_t st,
-                         const GemvBatch& bt, int m, int k) {
-#define Q4_TILE(U, Q)                                                                                    \
-    if (upw == U && mq == Q) {                                                                           \
-        hipLaunchKernelGGL((gemv_tile_kernel<SYM, XF16, U, Q, GR>), grid, block, lds, st, bt, m, k);    \
-        return hipGetLastError();                                                                        \
-    }
-    Q4_TILE(2, 1) Q4_TILE(4, 1) Q4_TILE(8, 1) Q4_TILE(12, 1) Q4_TILE(16, 1)
-    Q4_TILE(2, 4) Q4_TILE(4, 4) Q4_TILE(8, 4) Q4_TILE(12, 4) Q4_TILE(16, 4)
-#undef Q4_TILE
-    return hipErrorInvalidValue;
-}
-
-template <bool SYM>
-hipError_t launch_tile(int xd, int m, int k, int upw, int waves, int tiles, const GemvBatch& bt,
-                       hipStream_t st, const char** kname) {
-    const int mq = m <= 1 ? 1 : 4;
-    const size_t lds = (size_t)m * waves * upw * 256 + (size_t)waves * 64 * mq * 4;
-    const dim3 grid(tiles), block(64 * waves);
-    const bool grouped = bt.count > 1;
-    *kname = xd == 1 ? "q4_gemv_tile_f16" : "q4_gemv_tile_bf16";
-    if (xd == 1)
-        return grouped ? launch_tile_x<SYM, true, true>(upw, mq, grid, block, lds, st, bt, m, k)
-                       : launch_tile_x<SYM, true, false>(upw, mq, grid, block, lds, st, bt, m, k);
-    return grouped ? launch_tile_x<SYM, false, true>(upw, mq, grid, block, lds, st, bt, m, k)
-                   : launch_tile_x<SYM, false, false>(upw, mq, grid, block, lds, st, bt, m, k);
-}
-
 // One problem (batch == nullptr) or a batch of problems whose tiles add up to n rows.
 template <int G, bool SYM>
 hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16_t* sc,
@@ -771,7 +527,7 @@ hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16
     // 8 waves of 2-unit batches.
     const int units_k = (k + 127) / 128;
     const int tiles = batch != nullptr ? batch_tiles : (n + 15) / 16;
-    if constexpr (G == 128) {
+    {
         // the tile kernel reads scales as dwords: every scale array 4-byte aligned
         bool sc4 = true;
         if (batch != nullptr) {
@@ -780,12 +536,16 @@ hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16
             sc4 = ((uintptr_t)sc & 3) == 0;
         }
         int upw = 0, tw = 0;
-        if (sc4 && tile_shape(m, k, tiles, &upw, &tw)) {
-            if (batch != nullptr) return launch_tile<SYM>(xd, m, k, upw, tw, tiles, *batch, st, kname);
+        if (sc4 && q4t::tile_shape(G, m, k, tiles, g_num_cus, &upw, &tw)) {
             GemvBatch one{};
-            one.p[0] = q4::GemvProblem{x, qw, sc, zr, y, n, 0};
-            one.count = 1;
-            return launch_tile<SYM>(xd, m, k, upw, tw, tiles, one, st, kname);
+            if (batch == nullptr) {
+                one.p[0] = q4::GemvProblem{x, qw, sc, zr, y, n, 0};
+                one.count = 1;
+            }
+            const GemvBatch& bt = batch != nullptr ? *batch : one;
+            if constexpr (G == 32) return q4k_gemv_tile_g32(SYM, xd, m, k, upw, tw, bt, tiles, st, kname);
+            if constexpr (G == 64) return q4k_gemv_tile_g64(SYM, xd, m, k, upw, tw, bt, tiles, st, kname);
+            return q4k_gemv_tile_g128(SYM, xd, m, k, upw, tw, bt, tiles, st, kname);
         }
     }
     int shape;  // 0: up to 8 waves   1: up to 4 waves   2: up to 16 waves

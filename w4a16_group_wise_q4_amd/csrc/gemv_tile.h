@@ -1,0 +1,341 @@
+// gemv_tile.h — decode W4A16 tile kernel (m <= 4) for gfx950, any group size in {32, 64, 128}.
+//
+//   y[m][n] = sum_g S[n][g] * sum_{k in g} x[m][k] * (u[n][k] - z[n][g])
+//
+// Path A of "LLM Quantization: GPTQ·AWQ·SmoothQuant·FP8·KV Cache (7/10)"
+// (§Kernel이 없으면 압축 이점이 사라진다), for the bandwidth-bound decode case
+// (§Batch와 Context에 따라 속도가 달라진다): the packed weights are streamed once,
+// dequantized in registers and multiplied with fp32 accumulation.
+//
+// One 16-row tile per workgroup; its S waves split K into slices of UPW 128-column units,
+// wave w taking units [w*UPW, w*UPW + nu) with nu = min(UPW, units - w*UPW), so only the
+// last wave may be short.  A wave issues every load it needs at once, in wait order: its
+// slice of the activations, the scales and zero points of its groups (straight into
+// registers: lane l needs those of row l%16 only), then its packed weights; slots past nu
+// read nothing (an offset past the buffer) and are masked out of the sums.  The activation
+// slice goes to a wave-private LDS region in the decoder's slot order, so no barrier
+// precedes the arithmetic; only the cross-wave sum of the tile's partial results meets at
+// one.  Activation rows past m feed MFMA rows whose outputs are never stored, so lane l
+// reads row min(l%16, m-1) and no zero padding is staged.  Unit offsets are compile-time
+// constants, so loads and LDS reads carry them as immediates.
+//
+// Weights.  Lane l (row r = l%16, lane row c = l/16) loads the 16 bytes of words 4c..4c+3
+// of each unit: 16 rows x 64 bytes per wave-wide load for every group size.  A 16x16x32
+// MFMA takes one word from each lane row, and its product can only be scaled afterwards if
+// those four words share a group.  At g = 128 they do; at g = 64 one v_permlane32_swap per
+// register pair moves the second group's words into the upper registers; at g = 32 a
+// further v_permlane16_swap per pair completes the 4x4 transpose so that register a holds
+// word c of group a.  The activation vectors are read in the matching order:
+//   g = 128: register a, lane row c -> unit word 4c + a
+//   g = 64:  register a, lane row c -> unit word 8(a/2) + a%2 + 4(c%2) + 2(c/2)
+//   g = 32:  register a, lane row c -> unit word 4a + c
+//
+// Dequantization as in the streaming kernel: bf16 activations multiply 128 + u (exact,
+// the nibble OR-ed into the mantissa of 128.0) and a second MFMA with the constant 128 + z
+// is subtracted per group, so an all-zero-point group gives exactly zero; fp16 activations
+// multiply the exact u - z from one packed fp16 subtraction of 1024 + z.
+//
+// LDS (16-byte vectors): S x [m][UPW*16] activation slices | S x 64 x MQ partial sums.
+#pragma once
+
+#include "q4_device.h"
+
+namespace q4t {
+
+constexpr int kOOB = 0x40000000;             // a buffer offset past every load resource: reads 0
+constexpr uint32_t kStoreOOB = 0xFFFFFFF0u;  // a store offset past the y resource: dropped
+constexpr int kLdsBudget = 96 * 1024;        // LDS per workgroup
+
+constexpr int gcd8(int v) { return (v & 7) == 0 ? 8 : ((v & 3) == 0 ? 4 : ((v & 1) == 0 ? 2 : 1)); }
+
+// NV consecutive dwords at byte offset off of resource rs (chunks of 4, 2, 1).
+template <int NV>
+__device__ __forceinline__ void load_dwords(q4::rsrc rs, int off, uint32_t (&v)[NV]) {
+#pragma unroll
+    for (int j = 0; j < NV / 4; ++j) {
+        const q4::u32x4 t = q4::buf_load_x4(rs, off, 16 * j);
+        v[4 * j] = t[0];
+        v[4 * j + 1] = t[1];
+        v[4 * j + 2] = t[2];
+        v[4 * j + 3] = t[3];
+    }
+    if constexpr (NV % 4 >= 2) {
+        const q4::u32x2 t = q4::buf_load_x2(rs, off, 16 * (NV / 4));
+        v[NV / 4 * 4] = t[0];
+        v[NV / 4 * 4 + 1] = t[1];
+    }
+    if constexpr (NV % 2 == 1) v[NV - 1] = q4::buf_load_x1(rs, off, 4 * (NV - 1));
+}
+
+__device__ __forceinline__ void swap32(uint32_t& a, uint32_t& b) {
+    const auto t = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    a = t[0];
+    b = t[1];
+}
+__device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
+    const auto t = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    a = t[0];
+    b = t[1];
+}
+
+template <int G, bool SYM, bool XF16, int UPW, int MQ, bool GROUPED>
+__global__ __launch_bounds__(MQ == 1 ? 1024 : 512) void gemv_tile_kernel(const q4::GemvBatch bt, int M, int K) {
+    constexpr int NG = 128 / G;                // groups per unit
+    constexpr int RPG = 4 / NG;                // MFMAs (registers) per group
+    constexpr int GPS = UPW * NG;              // groups per slice
+    constexpr int XV = UPW >= 4 ? UPW / 4 : 1;  // activation vectors per lane per row of the slice
+    constexpr int SV = GPS / 2;                // scale dwords per lane (two fp16 each)
+    constexpr int ZOFF = GPS % 8 == 0 ? 0 : 8 - gcd8(GPS);  // largest nibble offset of a slice
+    constexpr int ZV = (ZOFF + GPS + 7) / 8;   // zero-point words a slice can span
+    constexpr int SLICE = UPW * 16;            // activation vectors per row of the slice
+    extern __shared__ q4::u32x4 lds[];
+    int pi = 0;
+    if constexpr (GROUPED) {
+#pragma unroll
+        for (int i = 1; i < q4::kMaxGroup; ++i)
+            if (i < bt.count && (int)blockIdx.x >= bt.p[i].tile0) pi = i;
+    }
+    const uint16_t* __restrict__ x = reinterpret_cast<const uint16_t*>(bt.p[pi].x);
+    const uint32_t* __restrict__ qweight = bt.p[pi].qweight;
+    const uint16_t* __restrict__ scales = bt.p[pi].scales;
+    const uint32_t* __restrict__ zeros = bt.p[pi].zeros;
+    float* __restrict__ y = bt.p[pi].y;
+    const int N = bt.p[pi].n;
+    const int n0 = ((int)blockIdx.x - bt.p[pi].tile0) * 16;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int S = blockDim.x >> 6;
+    const int r = lane & 15, c = lane >> 4;
+    const int KW = K >> 3, units = K >> 7, ng = K / G, zw = (ng + 7) >> 3;
+    const int rows = N - n0 < 16 ? N - n0 : 16;
+    const int U0 = w * UPW;  // this wave's first unit
+    const int G0 = U0 * NG;  // ... and first group
+    const int nu = units - U0 < UPW ? units - U0 : UPW;
+
+    // ---- prologue: every load of the wave, in the order it is waited for
+    q4::u32x4 xv[MQ][XV];
+    {
+        const q4::rsrc rx = q4::make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+#pragma unroll
+        for (int m = 0; m < MQ; ++m)
+#pragma unroll
+            for (int j = 0; j < XV; ++j) {
+                // a two-unit slice has 32 vectors per row: lanes 32..63 repeat 0..31
+                const int v = UPW >= 4 ? j * 64 + lane : (lane & 31);
+                const int off = (m * K + U0 * 128 + v * 8) * 2;
+                xv[m][j] = q4::buf_load_x4(rx, m < M ? off : kOOB, 0);
+            }
+    }
+    uint32_t sv[SV];
+    {
+        const q4::rsrc rs = q4::make_rsrc(scales + (int64_t)n0 * ng, (uint32_t)rows * ng * 2u);
+        load_dwords<SV>(rs, r < rows ? (r * ng + G0) * 2 : kOOB, sv);
+    }
+    uint32_t zv[ZV] = {};
+    if constexpr (!SYM) {
+        const q4::rsrc rz = q4::make_rsrc(zeros + (int64_t)n0 * zw, (uint32_t)rows * zw * 4u);
+        load_dwords<ZV>(rz, r < rows ? (r * zw + (G0 >> 3)) * 4 : kOOB, zv);
+    }
+    q4::u32x4 wv[UPW];
+    {
+        const q4::rsrc rq = q4::make_rsrc(qweight + (int64_t)n0 * KW, (uint32_t)rows * KW * 4u);
+        const int qo = r < rows ? r * KW * 4 + c * 16 : kOOB;
+#pragma unroll
+        for (int u = 0; u < UPW; ++u) wv[u] = q4::buf_load_x4(rq, qo, u < nu ? (U0 + u) * 64 : kOOB);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- this wave's activation slice into its LDS region, in the decoder's slot order.
+    // Rows m..MQ-1 (zeros) go to this wave's partial-sum slots, which it overwrites later:
+    // no store (and so no load) sits behind a branch.
+    q4::u32x4* xw = lds + w * (M * SLICE);
+    q4::u32x4* spare = lds + S * M * SLICE + w * 64 + lane;
+#pragma unroll
+    for (int m = 0; m < MQ; ++m)
+#pragma unroll
+        for (int j = 0; j < XV; ++j) {
+            q4::u32x4* dst = xw + m * SLICE + (UPW >= 4 ? j * 64 + lane : (lane & 31));
+            *(m == 0 || m < M ? dst : spare) = q4::pair_perm(xv[m][j]);
+        }
+
+    // zero points of the slice's groups from nibble 0 on (a slice may start mid-word)
+    uint32_t zs[ZV];
+#pragma unroll
+    for (int j = 0; j < ZV; ++j) zs[j] = zv[j];
+    if constexpr (!SYM && ZOFF != 0) {
+        const uint32_t sh = 4u * (uint32_t)(G0 & 7);
+#pragma unroll
+        for (int j = 0; j + 1 < ZV; ++j) zs[j] = __builtin_amdgcn_alignbit(zv[j + 1], zv[j], sh);
+        zs[ZV - 1] = zv[ZV - 1] >> sh;
+    }
+
+    // ---- dequantize and multiply, one unit at a time, as the loads land
+    const int mrow = r < M ? r : M - 1;
+    const int lb = G == 128 ? 4 * c : (G == 64 ? 4 * (c & 1) + 2 * (c >> 1) : c);
+    const q4::u32x4* xr = xw + mrow * SLICE + lb;
+    const uint32_t kMask = q4::vreg_const(0x000F000Fu);
+    const uint32_t kBias = q4::vreg_const(0x43004300u);
+    float acc[MQ];
+#pragma unroll
+    for (int q = 0; q < MQ; ++q) acc[q] = 0.f;
+#pragma unroll
+    for (int u = 0; u < UPW; ++u) {
+        const bool valid = u < nu;
+        uint32_t wq[4] = {wv[u][0], wv[u][1], wv[u][2], wv[u][3]};
+        if constexpr (G <= 64) {
+            swap32(wq[0], wq[2]);
+            swap32(wq[1], wq[3]);
+        }
+        if constexpr (G == 32) {
+            swap16(wq[0], wq[1]);
+            swap16(wq[2], wq[3]);
+        }
+        q4::u32x4 xa[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const int imm = G == 128 ? a : (G == 64 ? 8 * (a >> 1) + (a & 1) : 4 * a);
+            xa[a] = xr[u * 16 + imm];
+        }
+#pragma unroll
+        for (int h = 0; h < NG; ++h) {
+            const int gi = u * NG + h;  // group within the slice
+            const uint32_t sw = sv[gi >> 1];
+            const float s = q4::f16_bits_to_float((uint16_t)((gi & 1) ? (sw >> 16) : sw));
+            int z = 8;
+            if constexpr (!SYM) z = (int)((zs[gi >> 3] >> (4 * (gi & 7))) & 0xFu);
+            q4::f32x4 dv = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (XF16) {
+                const _Float16 b = (_Float16)(1024 + z);
+                const q4::f16x2 bias = {b, b};
+#pragma unroll
+                for (int t = 0; t < RPG; ++t) {
+                    const int a = h * RPG + t;
+                    dv = q4::mfma_f16(xa[a], q4::decode_f16_exact(wq[a], bias), dv);
+                }
+#pragma unroll
+                for (int q = 0; q < MQ; ++q) acc[q] = valid ? acc[q] + s * dv[q] : acc[q];
+            } else {
+                const uint32_t zb = (uint32_t)z * 0x00010001u + kBias;  // bf16 (128+z) x2
+                const q4::u32x4 zop = {zb, zb, zb, zb};
+                q4::f32x4 dc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int t = 0; t < RPG; ++t) {
+                    const int a = h * RPG + t;
+                    dv = q4::mfma_bf16(xa[a], q4::decode_bf16_biased(wq[a], kMask, kBias), dv);
+                    dc = q4::mfma_bf16(xa[a], zop, dc);
+                }
+#pragma unroll
+                for (int q = 0; q < MQ; ++q) acc[q] = valid ? acc[q] + s * (dv[q] - dc[q]) : acc[q];
+            }
+        }
+    }
+
+    // ---- cross-wave sum (lanes 0..15 hold rows m = 0..MQ-1 of the tile's 16 columns)
+    float* red = reinterpret_cast<float*>(lds + S * M * SLICE);
+#pragma unroll
+    for (int q = 0; q < MQ; ++q) red[(w * 64 + lane) * MQ + q] = acc[q];
+    __syncthreads();
+    if (w == 0) {
+        float sum[MQ];
+#pragma unroll
+        for (int q = 0; q < MQ; ++q) sum[q] = 0.f;
+        for (int v = 0; v < S; ++v)
+#pragma unroll
+            for (int q = 0; q < MQ; ++q) sum[q] += red[(v * 64 + lane) * MQ + q];
+        const q4::rsrc ry = q4::make_rsrc(y, (uint32_t)M * (uint32_t)N * 4u);
+#pragma unroll
+        for (int q = 0; q < MQ; ++q) {
+            const bool st = lane < 16 && q < M && r < rows;
+            const uint32_t off = st ? ((uint32_t)q * (uint32_t)N + (uint32_t)(n0 + r)) * 4u : kStoreOOB;
+            __builtin_amdgcn_raw_buffer_store_b32(q4::f32_bits(sum[q]), ry, (int)off, 0, 0);
+        }
+    }
+}
+
+// Slice widths per group size (the g = 32 and g = 64 metadata registers grow with the
+// slice; these stay within the launch bounds' register budgets).
+constexpr int kMaxUpw128 = 16, kMaxUpw64 = 12, kMaxUpw32 = 8;
+
+// The tile kernel's shape: S slices of UPW units (UPW in {2, 4, 8, 12, 16} up to the group
+// size's maximum; S = ceil(units / UPW) waves, at most 16 for m = 1 and 8 otherwise, the
+// kernel's launch bound), K a multiple of 128, an even number of groups per row (scales are
+// read as dwords) and activations within the LDS budget.  Among the shapes that fit, the
+// one nearest the target wave count wins, then the one with fewer idle slots.  The target
+// is eight waves while one round of eight-wave workgroups holds every tile (the arithmetic
+// of a tile spreads over more SIMDs and the tail after the last load is short), four when
+// the tiles need several rounds (more loads in flight per wave, less per-workgroup
+// overhead per byte).  Returns false when no shape fits.
+inline bool tile_shape(int g, int m, int k, int tiles, int num_cus, int* upw, int* waves) {
+    if (m > 4 || k % 128 != 0 || (k / g) % 2 != 0) return false;
+    const int units = k / 128, mq = m <= 1 ? 1 : 4, max_waves = mq == 1 ? 16 : 8;
+    const int max_upw = g == 128 ? kMaxUpw128 : (g == 64 ? kMaxUpw64 : kMaxUpw32);
+    const int target = tiles > 4 * (num_cus > 0 ? num_cus : 256) ? 4 : 8;
+    *upw = 0;
+    auto key = [&](int uu, int ww) {  // smaller is better
+        return (ww > target ? ww - target : target - ww) * 4096 + (ww * uu - units);
+    };
+    for (int u : {2, 4, 8, 12, 16}) {
+        const int sw = (units + u - 1) / u;
+        if (u > max_upw || sw > max_waves ||
+            (size_t)m * sw * u * 256 + (size_t)sw * 64 * mq * 4 > (size_t)kLdsBudget)
+            continue;
+        if (*upw == 0 || key(u, sw) < key(*upw, *waves)) {
+            *upw = u;
+            *waves = sw;
+        }
+    }
+    return *upw != 0;
+}
+
+template <int G, bool SYM, bool XF16, bool GR, int U>
+hipError_t launch_upw(int mq, dim3 grid, dim3 block, size_t lds, hipStream_t st,
+                      const q4::GemvBatch& bt, int m, int k) {
+    if (mq == 1)
+        hipLaunchKernelGGL((gemv_tile_kernel<G, SYM, XF16, U, 1, GR>), grid, block, lds, st, bt, m, k);
+    else
+        hipLaunchKernelGGL((gemv_tile_kernel<G, SYM, XF16, U, 4, GR>), grid, block, lds, st, bt, m, k);
+    return hipGetLastError();
+}
+
+template <int G, bool SYM, bool XF16, bool GR>
+hipError_t launch_x(int upw, int mq, dim3 grid, dim3 block, size_t lds, hipStream_t st,
+                    const q4::GemvBatch& bt, int m, int k) {
+    switch (upw) {
+    case 2: return launch_upw<G, SYM, XF16, GR, 2>(mq, grid, block, lds, st, bt, m, k);
+    case 4: return launch_upw<G, SYM, XF16, GR, 4>(mq, grid, block, lds, st, bt, m, k);
+    case 8: return launch_upw<G, SYM, XF16, GR, 8>(mq, grid, block, lds, st, bt, m, k);
+    case 12:
+        if constexpr (G >= 64) return launch_upw<G, SYM, XF16, GR, 12>(mq, grid, block, lds, st, bt, m, k);
+        break;
+    case 16:
+        if constexpr (G == 128) return launch_upw<G, SYM, XF16, GR, 16>(mq, grid, block, lds, st, bt, m, k);
+        break;
+    default: break;
+    }
+    return hipErrorInvalidValue;
+}
+
+// Launch for a shape from tile_shape: one workgroup of 64 * waves threads per tile.
+template <int G>
+hipError_t launch_tile(int sym, int xd, int m, int k, int upw, int waves, const q4::GemvBatch& bt,
+                       int tiles, hipStream_t st, const char** kname) {
+    const int mq = m <= 1 ? 1 : 4;
+    const size_t lds = (size_t)m * waves * upw * 256 + (size_t)waves * 64 * mq * 4;
+    const dim3 grid(tiles), block(64 * waves);
+    const bool gr = bt.count > 1;
+    *kname = xd == 1 ? "q4_gemv_tile_f16" : "q4_gemv_tile_bf16";
+    if (sym) {
+        if (xd == 1)
+            return gr ? launch_x<G, true, true, true>(upw, mq, grid, block, lds, st, bt, m, k)
+                      : launch_x<G, true, true, false>(upw, mq, grid, block, lds, st, bt, m, k);
+        return gr ? launch_x<G, true, false, true>(upw, mq, grid, block, lds, st, bt, m, k)
+                  : launch_x<G, true, false, false>(upw, mq, grid, block, lds, st, bt, m, k);
+    }
+    if (xd == 1)
+        return gr ? launch_x<G, false, true, true>(upw, mq, grid, block, lds, st, bt, m, k)
+                  : launch_x<G, false, true, false>(upw, mq, grid, block, lds, st, bt, m, k);
+    return gr ? launch_x<G, false, false, true>(upw, mq, grid, block, lds, st, bt, m, k)
+              : launch_x<G, false, false, false>(upw, mq, grid, block, lds, st, bt, m, k);
+}
+
+}  // namespace q4t

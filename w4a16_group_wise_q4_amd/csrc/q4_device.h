@@ -143,7 +143,24 @@ struct GemvProblem {
     int n;
     int tile0;
 };
+// The problems of one decode launch (a single one, or several sharing m, k, g and dtype):
+// workgroups [p[i].tile0, p[i+1].tile0) serve problem i.
+struct GemvBatch {
+    GemvProblem p[kMaxGroup];
+    int count;
+};
 }  // namespace q4
+// Decode tile kernel for one group size (32, 64 or 128): UPW units per wave, `waves` waves
+// per 16-row tile, one workgroup per tile of the batch.
+hipError_t q4k_gemv_tile_g32(int sym, int x_dtype, int m, int k, int upw, int waves,
+                             const q4::GemvBatch& batch, int tiles, hipStream_t stream,
+                             const char** kname);
+hipError_t q4k_gemv_tile_g64(int sym, int x_dtype, int m, int k, int upw, int waves,
+                             const q4::GemvBatch& batch, int tiles, hipStream_t stream,
+                             const char** kname);
+hipError_t q4k_gemv_tile_g128(int sym, int x_dtype, int m, int k, int upw, int waves,
+                              const q4::GemvBatch& batch, int tiles, hipStream_t stream,
+                              const char** kname);
 // Runs count problems (shared m <= 16, k, g, sym, dtype) in one launch when their
 // activations fit the streaming kernel; returns hipErrorNotSupported (enqueuing nothing)
 // otherwise, so the caller runs them one by one.
