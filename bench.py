@@ -142,7 +142,7 @@ def main():
     ap.add_argument("--steps", type=int, default=340)
     ap.add_argument("--warmup", type=int, default=34)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--legs", default="gemm,quant,sweep",
+    ap.add_argument("--legs", default="gemm,quant,sweep,mlp",
                     help="comma list of legs besides the headline decode GEMV")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy 5 times (the "
@@ -220,7 +220,7 @@ def main():
         g = capture([lambda c=c: q4.q4_w4a16_gemm(x, packs[c][i], out=ys[i]) for c in range(copies)])
         single_ms.append(graph_ms(g, 10) / copies)
     single_step_ms = graph_ms(capture([f for c in range(copies) for f in single_fns(c)]), 10) / copies
-    digest = source_digest("gemv.hip", "q4_device.h")
+    digest = source_digest("gemv.hip", "gemv_tile.h", "gemv_tile_g128.hip", "q4_device.h")
     traffic = profiled_traffic("q4_gemv_decode_7b_m1_pmc.md", digest)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -255,6 +255,40 @@ def main():
                        "tflops": round(flops / t / 1e12, 2),
                        "frac_mfma_bf16": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4)}
         del pw, xg, yg
+
+    # ------------------------------------------------------------ MLP batch sweep (GEMV, m <= 16)
+    if "mlp" in legs:
+        c3 = synthetic.MLP_SWEEP
+        res = {}
+        for mat in c3["mats"]:
+            w = mat.make().to(dev)
+            x16 = synthetic.activations(16, mat.k, c3["x_seed"]).to(dev)
+            for g in c3["group_sizes"]:
+                for sym in c3["symmetric"]:
+                    p0 = q4.q4_quantize_pack(w, g, sym)
+                    nb = gemv_bytes(1, mat.n, mat.k, g, sym)
+                    cps = max(2, -(-4 * MALL_BYTES // nb))
+                    pks = [q4.PackedWeight(p0.qweight.clone(), p0.scales.clone(),
+                                           None if sym else p0.zeros.clone(), mat.n, mat.k, g, sym)
+                           for _ in range(cps)]
+                    row = {}
+                    for m in c3["ms"]:
+                        xm = x16[:m].contiguous()
+                        ym = torch.empty((m, mat.n), dtype=torch.float32, device=dev)
+                        q4.q4_w4a16_gemm(xm, pks[0], out=ym)
+                        torch.cuda.synchronize()
+                        kname = q4.q4_last_kernel()
+                        t = graph_ms(capture([lambda pp=pp: q4.q4_w4a16_gemm(xm, pp, out=ym)
+                                              for pp in pks]), 5) / cps * 1e-3
+                        byt = gemv_bytes(m, mat.n, mat.k, g, sym)
+                        row[f"m{m}"] = {"us": round(t * 1e6, 3), "gbs": round(byt / t / 1e9, 1),
+                                        "frac_hbm": round(byt / t / 1e9 / HBM_PEAK_GBS, 4),
+                                        "kernel": kname}
+                    res[f"{mat.n}x{mat.k} g{g} {'sym' if sym else 'asym'}"] = row
+                    del pks, p0
+            del w
+        out["mlp_sweep"] = {"workload": "7B-like MLP GEMV, W [11008x4096] and [4096x11008], "
+                                        "m in 1..16, one launch per product", "results": res}
 
     # ------------------------------------------------------------ checkpoint quantize + GEMV sweep
     if "quant" in legs or "sweep" in legs:

@@ -241,10 +241,10 @@ def test_gemv_mlp_sweep(idx, g, sym):
 
 
 def gemv_kernels(xdtype=torch.bfloat16):
-    """Names of the decode kernels for an activation dtype: the tile kernel (group size
-    128, m <= 4, K split evenly over the waves) and the streaming kernel."""
+    """Names of the decode kernels for an activation dtype: the tile kernel (m <= 4), the
+    wide tile kernel (4 < m <= 16) and the streaming kernel (shapes neither takes)."""
     t = "f16" if xdtype == torch.float16 else "bf16"
-    return {f"q4_gemv_tile_{t}", f"q4_gemv_mfma_{t}"}
+    return {f"q4_gemv_tile_{t}", f"q4_gemv_wide_{t}", f"q4_gemv_mfma_{t}"}
 
 
 # (m, n, k): every slice width of the tile kernel (2, 4, 8, 12 and 16 units per wave, two
@@ -270,6 +270,37 @@ def tile_fits(g, m, k, n, num_cus=256):
     return False
 
 
+def wide_fits(g, m, k):
+    """Whether the wide tile kernel can take a product (m <= 16; the launcher uses it for
+    m > 4 and for the m <= 4 shapes the tile kernel cannot take): slices of 4..16 units over
+    at most eight waves, K a multiple of 128, an even group count."""
+    if not 1 <= m <= 16 or k % 128 or (k // g) % 2:
+        return False
+    return any(-(-(k // 128) // u) <= 8 for u in (4, 8, 12, 16))
+
+
+# (m, n, k): slice widths 4, 8, 12 and 16, one to eight waves, short last slices, ragged
+# tiles, m = 5..16
+WIDE_CASES = [(5, 17, 512), (8, 100, 1024), (16, 33, 4096), (12, 64, 5120), (9, 48, 11008),
+              (16, 20, 16384), (6, 130, 2560), (16, 1, 1536)]
+
+
+@pytest.mark.parametrize("m,n,k", WIDE_CASES)
+@pytest.mark.parametrize("g", [32, 64, 128])
+@pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("sym", [False, True])
+def test_gemv_wide_cases(m, n, k, g, xdtype, sym):
+    w = torch.from_numpy(pins.random_weights(n + 7 * k + m + g, max(n, 12), k)[:n])
+    x = synthetic.activations(m, k, seed=m * 19 + k).to(xdtype)
+    note(f"gemv wide m={m} n={n} k={k} g={g} {xdtype} sym={sym}")
+    p, _ = pack_guarded(w.to(DEV), g, sym)
+    y, kname = run_linear(x, p)
+    t = "f16" if xdtype == torch.float16 else "bf16"
+    assert kname == (f"q4_gemv_wide_{t}" if wide_fits(g, m, k) else f"q4_gemv_mfma_{t}")
+    packed = assert_pack_exact(p, host_input(w), g, sym)
+    assert_linear_close(y, host_input(x), packed, n, k, g, sym, what=kname)
+
+
 @pytest.mark.parametrize("m,n,k", TILE_CASES)
 @pytest.mark.parametrize("g", [32, 64, 128])
 @pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
@@ -281,7 +312,8 @@ def test_gemv_tile_cases(m, n, k, g, xdtype, sym):
     p, _ = pack_guarded(w.to(DEV), g, sym)
     y, kname = run_linear(x, p)
     t = "f16" if xdtype == torch.float16 else "bf16"
-    assert kname == (f"q4_gemv_tile_{t}" if tile_fits(g, m, k, n) else f"q4_gemv_mfma_{t}")
+    want = "tile" if tile_fits(g, m, k, n) else ("wide" if wide_fits(g, m, k) else "mfma")
+    assert kname == f"q4_gemv_{want}_{t}"
     packed = assert_pack_exact(p, host_input(w), g, sym)
     assert_linear_close(y, host_input(x), packed, n, k, g, sym, what=kname)
 
@@ -407,20 +439,21 @@ def test_gemm_grouped_mixed(m, g, sym, xdtype):
                             what="grouped")
 
 
-@pytest.mark.parametrize("m,k", [(40, 512), (16, 11008)])
-def test_gemm_grouped_one_by_one(m, k):
-    """m > 16 (prefill GEMM per problem) and activations too large to stage on chip
-    (decode kernel per problem): same results, one launch per problem."""
+@pytest.mark.parametrize("m,k,g", [(40, 512, 128), (16, 4160, 64), (16, 11008, 128)])
+def test_gemm_grouped_one_by_one(m, k, g):
+    """m > 16 (prefill GEMM per problem), a K no tile kernel takes with activations too
+    large for the streaming kernel's LDS (decode kernel per problem), and the wide tile
+    kernel over both problems in one launch: same results either way."""
     ns = [64, 130]
     ws = [torch.from_numpy(pins.random_weights(50 + i, max(n, 12), k)[:n]) for i, n in enumerate(ns)]
     x = synthetic.activations(m, k, seed=60)
-    note(f"grouped one-by-one m={m} k={k}")
-    packs = [pack_guarded(w.to(DEV), 128, False)[0] for w in ws]
+    note(f"grouped one-by-one m={m} k={k} g={g}")
+    packs = [pack_guarded(w.to(DEV), g, False)[0] for w in ws]
     ys = q4.q4_w4a16_gemm_grouped(x.to(DEV), packs)
     torch.cuda.synchronize()
     for w, p, y in zip(ws, packs, ys):
-        packed = assert_pack_exact(p, host_input(w), 128, False)
-        assert_linear_close(y.cpu().numpy(), host_input(x), packed, p.n, k, 128, False,
+        packed = assert_pack_exact(p, host_input(w), g, False)
+        assert_linear_close(y.cpu().numpy(), host_input(x), packed, p.n, k, g, False,
                             what="grouped")
 
 

@@ -535,17 +535,19 @@ hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16
         } else {
             sc4 = ((uintptr_t)sc & 3) == 0;
         }
-        int upw = 0, tw = 0;
-        if (sc4 && q4t::tile_shape(G, m, k, tiles, g_num_cus, &upw, &tw)) {
+        int upw = 0, tw = 0, wide = 0;
+        const bool fits = sc4 && (q4t::tile_shape(G, m, k, tiles, g_num_cus, &upw, &tw) ||
+                                  (wide = q4t::wide_shape(G, m, k, &upw, &tw)));
+        if (fits) {
             GemvBatch one{};
             if (batch == nullptr) {
                 one.p[0] = q4::GemvProblem{x, qw, sc, zr, y, n, 0};
                 one.count = 1;
             }
             const GemvBatch& bt = batch != nullptr ? *batch : one;
-            if constexpr (G == 32) return q4k_gemv_tile_g32(SYM, xd, m, k, upw, tw, bt, tiles, st, kname);
-            if constexpr (G == 64) return q4k_gemv_tile_g64(SYM, xd, m, k, upw, tw, bt, tiles, st, kname);
-            return q4k_gemv_tile_g128(SYM, xd, m, k, upw, tw, bt, tiles, st, kname);
+            if constexpr (G == 32) return q4k_gemv_tile_g32(SYM, xd, m, k, upw, tw, wide, bt, tiles, st, kname);
+            if constexpr (G == 64) return q4k_gemv_tile_g64(SYM, xd, m, k, upw, tw, wide, bt, tiles, st, kname);
+            return q4k_gemv_tile_g128(SYM, xd, m, k, upw, tw, wide, bt, tiles, st, kname);
         }
     }
     int shape;  // 0: up to 8 waves   1: up to 4 waves   2: up to 16 waves

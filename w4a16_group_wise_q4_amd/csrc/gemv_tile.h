@@ -252,6 +252,174 @@ __global__ __launch_bounds__(MQ == 1 ? 1024 : 512) void gemv_tile_kernel(const q
     }
 }
 
+// Wide tile kernel: 4 < m <= 16.  Same tiles, slices and metadata as the tile kernel, but
+// the activations are not staged in LDS (m x K of them does not fit there for the larger
+// projections).  Per unit, each lane loads the 64 bytes of activation row l%16 that its
+// four MFMA k-blocks use (the words its weight registers hold after the transpose) from
+// the L2-resident activations, and puts them in the decoder's slot order in registers.
+// The wave keeps two batches of D units (activations and weights) in flight: once a batch
+// is computed its registers take the batch two ahead, all offsets and waits static.  All
+// 16 MFMA rows are activation rows (zero rows past m), so every lane holds four outputs.
+template <int G, bool SYM, bool XF16, int UPW, bool GROUPED>
+__global__ __launch_bounds__(512) void gemv_wide_kernel(const q4::GemvBatch bt, int M, int K) {
+    constexpr int D = 2;            // units per batch
+    constexpr int NB = UPW / D;     // batches per slice (at least two)
+    constexpr int NG = 128 / G, RPG = 4 / NG, GPS = UPW * NG, SV = GPS / 2;
+    constexpr int ZOFF = GPS % 8 == 0 ? 0 : 8 - gcd8(GPS);
+    constexpr int ZV = (ZOFF + GPS + 7) / 8;
+    extern __shared__ q4::u32x4 lds[];
+    int pi = 0;
+    if constexpr (GROUPED) {
+#pragma unroll
+        for (int i = 1; i < q4::kMaxGroup; ++i)
+            if (i < bt.count && (int)blockIdx.x >= bt.p[i].tile0) pi = i;
+    }
+    const uint16_t* __restrict__ x = reinterpret_cast<const uint16_t*>(bt.p[pi].x);
+    const uint32_t* __restrict__ qweight = bt.p[pi].qweight;
+    const uint16_t* __restrict__ scales = bt.p[pi].scales;
+    const uint32_t* __restrict__ zeros = bt.p[pi].zeros;
+    float* __restrict__ y = bt.p[pi].y;
+    const int N = bt.p[pi].n;
+    const int n0 = ((int)blockIdx.x - bt.p[pi].tile0) * 16;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int S = blockDim.x >> 6;
+    const int r = lane & 15, c = lane >> 4;
+    const int KW = K >> 3, units = K >> 7, ng = K / G, zw = (ng + 7) >> 3;
+    const int rows = N - n0 < 16 ? N - n0 : 16;
+    const int U0 = w * UPW, G0 = U0 * NG;
+    const int nu = units - U0 < UPW ? units - U0 : UPW;
+
+    // ---- metadata of the slice (waited for before the first unit)
+    uint32_t sv[SV];
+    {
+        const q4::rsrc rs = q4::make_rsrc(scales + (int64_t)n0 * ng, (uint32_t)rows * ng * 2u);
+        load_dwords<SV>(rs, r < rows ? (r * ng + G0) * 2 : kOOB, sv);
+    }
+    uint32_t zv[ZV] = {};
+    if constexpr (!SYM) {
+        const q4::rsrc rz = q4::make_rsrc(zeros + (int64_t)n0 * zw, (uint32_t)rows * zw * 4u);
+        load_dwords<ZV>(rz, r < rows ? (r * zw + (G0 >> 3)) * 4 : kOOB, zv);
+    }
+
+    // ---- activations and weights of a batch: per unit four activation vectors of row l%16
+    // (lane part of the word index in the per-lane offset, register part in the uniform
+    // one), then the unit's packed words
+    const int lb = G == 128 ? 4 * c : (G == 64 ? 4 * (c & 1) + 2 * (c >> 1) : c);
+    const q4::rsrc rx = q4::make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+    const int xo = r < M ? r * K * 2 + lb * 16 : kOOB;
+    const q4::rsrc rq = q4::make_rsrc(qweight + (int64_t)n0 * KW, (uint32_t)rows * KW * 4u);
+    const int qo = r < rows ? r * KW * 4 + c * 16 : kOOB;
+    q4::u32x4 xb[2][D][4];
+    q4::u32x4 wb[2][D];
+    auto load_batch = [&](int b, q4::u32x4 (&xs)[D][4], q4::u32x4 (&ws)[D]) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            const int u = b * D + j;
+            const bool ok = u < nu;
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const int imm = G == 128 ? a : (G == 64 ? 8 * (a >> 1) + (a & 1) : 4 * a);
+                xs[j][a] = q4::buf_load_x4(rx, xo, ok ? (U0 + u) * 256 + imm * 16 : kOOB);
+            }
+            ws[j] = q4::buf_load_x4(rq, qo, ok ? (U0 + u) * 64 : kOOB);
+        }
+    };
+    load_batch(0, xb[0], wb[0]);
+    load_batch(1, xb[1], wb[1]);
+    __builtin_amdgcn_sched_barrier(0);
+
+    uint32_t zs[ZV];
+#pragma unroll
+    for (int j = 0; j < ZV; ++j) zs[j] = zv[j];
+    if constexpr (!SYM && ZOFF != 0) {
+        const uint32_t sh = 4u * (uint32_t)(G0 & 7);
+#pragma unroll
+        for (int j = 0; j + 1 < ZV; ++j) zs[j] = __builtin_amdgcn_alignbit(zv[j + 1], zv[j], sh);
+        zs[ZV - 1] = zv[ZV - 1] >> sh;
+    }
+
+    const uint32_t kMask = q4::vreg_const(0x000F000Fu);
+    const uint32_t kBias = q4::vreg_const(0x43004300u);
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const int slot = b & 1;
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            const int u = b * D + j;
+            const bool valid = u < nu;
+            uint32_t wq[4] = {wb[slot][j][0], wb[slot][j][1], wb[slot][j][2], wb[slot][j][3]};
+            if constexpr (G <= 64) {
+                swap32(wq[0], wq[2]);
+                swap32(wq[1], wq[3]);
+            }
+            if constexpr (G == 32) {
+                swap16(wq[0], wq[1]);
+                swap16(wq[2], wq[3]);
+            }
+            q4::u32x4 xa[4];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) xa[a] = q4::pair_perm(xb[slot][j][a]);
+#pragma unroll
+            for (int h = 0; h < NG; ++h) {
+                const int gi = u * NG + h;
+                const uint32_t sw = sv[gi >> 1];
+                const float s = q4::f16_bits_to_float((uint16_t)((gi & 1) ? (sw >> 16) : sw));
+                int z = 8;
+                if constexpr (!SYM) z = (int)((zs[gi >> 3] >> (4 * (gi & 7))) & 0xFu);
+                q4::f32x4 dv = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (XF16) {
+                    const _Float16 bb = (_Float16)(1024 + z);
+                    const q4::f16x2 bias = {bb, bb};
+#pragma unroll
+                    for (int t = 0; t < RPG; ++t) {
+                        const int a = h * RPG + t;
+                        dv = q4::mfma_f16(xa[a], q4::decode_f16_exact(wq[a], bias), dv);
+                    }
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc[q] = valid ? acc[q] + s * dv[q] : acc[q];
+                } else {
+                    const uint32_t zb = (uint32_t)z * 0x00010001u + kBias;
+                    const q4::u32x4 zop = {zb, zb, zb, zb};
+                    q4::f32x4 dc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int t = 0; t < RPG; ++t) {
+                        const int a = h * RPG + t;
+                        dv = q4::mfma_bf16(xa[a], q4::decode_bf16_biased(wq[a], kMask, kBias), dv);
+                        dc = q4::mfma_bf16(xa[a], zop, dc);
+                    }
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc[q] = valid ? acc[q] + s * (dv[q] - dc[q]) : acc[q];
+                }
+            }
+        }
+        // refill this slot with the batch two ahead, right behind the compute that freed it
+        if (b + 2 < NB) load_batch(b + 2, xb[slot], wb[slot]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- cross-wave sum: lane l holds rows m = 4(l/16)..+3 of column l%16
+    float* red = reinterpret_cast<float*>(lds);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) red[(w * 64 + lane) * 4 + q] = acc[q];
+    __syncthreads();
+    if (w == 0) {
+        float sum[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int v = 0; v < S; ++v)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) sum[q] += red[(v * 64 + lane) * 4 + q];
+        const q4::rsrc ry = q4::make_rsrc(y, (uint32_t)M * (uint32_t)N * 4u);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int m = 4 * c + q;
+            const bool st = m < M && r < rows;
+            const uint32_t off = st ? ((uint32_t)m * (uint32_t)N + (uint32_t)(n0 + r)) * 4u : kStoreOOB;
+            __builtin_amdgcn_raw_buffer_store_b32(q4::f32_bits(sum[q]), ry, (int)off, 0, 0);
+        }
+    }
+}
+
 // Slice widths per group size (the g = 32 and g = 64 metadata registers grow with the
 // slice; these stay within the launch bounds' register budgets).
 constexpr int kMaxUpw128 = 16, kMaxUpw64 = 12, kMaxUpw32 = 8;
@@ -279,6 +447,26 @@ inline bool tile_shape(int g, int m, int k, int tiles, int num_cus, int* upw, in
         if (u > max_upw || sw > max_waves ||
             (size_t)m * sw * u * 256 + (size_t)sw * 64 * mq * 4 > (size_t)kLdsBudget)
             continue;
+        if (*upw == 0 || key(u, sw) < key(*upw, *waves)) {
+            *upw = u;
+            *waves = sw;
+        }
+    }
+    return *upw != 0;
+}
+
+// The wide kernel's shape (m <= 16; it serves 4 < m and the m <= 4 shapes the tile kernel
+// cannot take): slices of 4, 8, 12 or 16 units, S = ceil(units / UPW) <= 8 waves, K a
+// multiple of 128 and an even number of groups per row; the shape nearest eight waves with
+// the fewest idle slots.
+inline bool wide_shape(int g, int m, int k, int* upw, int* waves) {
+    if (m < 1 || m > 16 || k % 128 != 0 || (k / g) % 2 != 0) return false;
+    const int units = k / 128;
+    *upw = 0;
+    for (int u : {4, 8, 12, 16}) {
+        const int sw = (units + u - 1) / u;
+        if (sw > 8) continue;
+        auto key = [&](int uu, int ww) { return (8 - ww) * 4096 + (ww * uu - units); };
         if (*upw == 0 || key(u, sw) < key(*upw, *waves)) {
             *upw = u;
             *waves = sw;
@@ -315,10 +503,42 @@ hipError_t launch_x(int upw, int mq, dim3 grid, dim3 block, size_t lds, hipStrea
     return hipErrorInvalidValue;
 }
 
-// Launch for a shape from tile_shape: one workgroup of 64 * waves threads per tile.
+template <int G, bool SYM, bool XF16, bool GR>
+hipError_t launch_wide(int upw, dim3 grid, dim3 block, size_t lds, hipStream_t st,
+                       const q4::GemvBatch& bt, int m, int k) {
+#define Q4_WIDE(U)                                                                                 \
+    if (upw == U) {                                                                                \
+        hipLaunchKernelGGL((gemv_wide_kernel<G, SYM, XF16, U, GR>), grid, block, lds, st, bt, m, k); \
+        return hipGetLastError();                                                                  \
+    }
+    Q4_WIDE(4) Q4_WIDE(8) Q4_WIDE(12) Q4_WIDE(16)
+#undef Q4_WIDE
+    return hipErrorInvalidValue;
+}
+
+// Launch for a shape from tile_shape (wide == 0) or wide_shape (wide != 0): one workgroup
+// of 64 * waves threads per tile.
 template <int G>
-hipError_t launch_tile(int sym, int xd, int m, int k, int upw, int waves, const q4::GemvBatch& bt,
-                       int tiles, hipStream_t st, const char** kname) {
+hipError_t launch_tile(int sym, int xd, int m, int k, int upw, int waves, int wide,
+                       const q4::GemvBatch& bt, int tiles, hipStream_t st, const char** kname) {
+    if (wide) {  // wide kernel: partial sums only in LDS
+        const size_t lds = (size_t)waves * 64 * 4 * 4;
+        const dim3 grid(tiles), block(64 * waves);
+        const bool gr = bt.count > 1;
+        *kname = xd == 1 ? "q4_gemv_wide_f16" : "q4_gemv_wide_bf16";
+        if (sym) {
+            if (xd == 1)
+                return gr ? launch_wide<G, true, true, true>(upw, grid, block, lds, st, bt, m, k)
+                          : launch_wide<G, true, true, false>(upw, grid, block, lds, st, bt, m, k);
+            return gr ? launch_wide<G, true, false, true>(upw, grid, block, lds, st, bt, m, k)
+                      : launch_wide<G, true, false, false>(upw, grid, block, lds, st, bt, m, k);
+        }
+        if (xd == 1)
+            return gr ? launch_wide<G, false, true, true>(upw, grid, block, lds, st, bt, m, k)
+                      : launch_wide<G, false, true, false>(upw, grid, block, lds, st, bt, m, k);
+        return gr ? launch_wide<G, false, false, true>(upw, grid, block, lds, st, bt, m, k)
+                  : launch_wide<G, false, false, false>(upw, grid, block, lds, st, bt, m, k);
+    }
     const int mq = m <= 1 ? 1 : 4;
     const size_t lds = (size_t)m * waves * upw * 256 + (size_t)waves * 64 * mq * 4;
     const dim3 grid(tiles), block(64 * waves);

@@ -2,8 +2,8 @@
 // unit per group size, so they compile in parallel).
 #include "gemv_tile.h"
 
-hipError_t q4k_gemv_tile_g32(int sym, int x_dtype, int m, int k, int upw, int waves,
+hipError_t q4k_gemv_tile_g32(int sym, int x_dtype, int m, int k, int upw, int waves, int wide,
                              const q4::GemvBatch& batch, int tiles, hipStream_t stream,
                              const char** kname) {
-    return q4t::launch_tile<32>(sym, x_dtype, m, k, upw, waves, batch, tiles, stream, kname);
+    return q4t::launch_tile<32>(sym, x_dtype, m, k, upw, waves, wide, batch, tiles, stream, kname);
 }

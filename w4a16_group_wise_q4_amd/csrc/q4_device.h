@@ -150,15 +150,16 @@ struct GemvBatch {
     int count;
 };
 }  // namespace q4
-// Decode tile kernel for one group size (32, 64 or 128): UPW units per wave, `waves` waves
-// per 16-row tile, one workgroup per tile of the batch.
-hipError_t q4k_gemv_tile_g32(int sym, int x_dtype, int m, int k, int upw, int waves,
+// Decode tile kernels for one group size (32, 64 or 128): UPW units per wave, `waves` waves
+// per 16-row tile, one workgroup per tile of the batch; wide != 0 selects the kernel for
+// m up to 16 that streams the activations instead of staging them.
+hipError_t q4k_gemv_tile_g32(int sym, int x_dtype, int m, int k, int upw, int waves, int wide,
                              const q4::GemvBatch& batch, int tiles, hipStream_t stream,
                              const char** kname);
-hipError_t q4k_gemv_tile_g64(int sym, int x_dtype, int m, int k, int upw, int waves,
+hipError_t q4k_gemv_tile_g64(int sym, int x_dtype, int m, int k, int upw, int waves, int wide,
                              const q4::GemvBatch& batch, int tiles, hipStream_t stream,
                              const char** kname);
-hipError_t q4k_gemv_tile_g128(int sym, int x_dtype, int m, int k, int upw, int waves,
+hipError_t q4k_gemv_tile_g128(int sym, int x_dtype, int m, int k, int upw, int waves, int wide,
                               const q4::GemvBatch& batch, int tiles, hipStream_t stream,
                               const char** kname);
 // Runs count problems (shared m <= 16, k, g, sym, dtype) in one launch when their
