@@ -199,22 +199,28 @@ def main():
     for _ in range(max(1, args.warmup // copies)):
         full.replay()
     torch.cuda.synchronize()
-    # the timed region: exactly K steps, synchronized on both sides, nothing else inside
+    # the timed region: exactly K steps, synchronized on both sides, nothing else inside;
+    # HIP events on the stream the graphs replay on bracket the same K launches (one
+    # grouped GEMV launch per step), which gives the kernel's average launch duration
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t_start = time.perf_counter()
+    ev0.record()
     for _ in range(args.steps // copies):
         full.replay()
     if tail is not None:
         tail.replay()
+    ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_step = wall * 1e3 / args.steps
     value = step_bytes * args.steps / wall / 1e9
-
-    # kernel durations: HIP events on the launch stream around graph replays (every copy
-    # once), a pass separate from the timed steps.  The grouped launch is the step's
-    # kernel; the single-problem launches are timed per shape.
-    launch_ms = graph_ms(capture([f for c in range(copies) for f in step_fns(c)]), 10) / copies
+    launch_ms = ev0.elapsed_time(ev1) / args.steps
     achieved = step_bytes / (launch_ms * 1e-3) / 1e9
+
+    # for comparison: the same projections as one launch each (HIP events around graph
+    # replays of every copy, a pass of its own)
     single_ms = []
     for i in range(len(base)):
         g = capture([lambda c=c: q4.q4_w4a16_gemm(x, packs[c][i], out=ys[i]) for c in range(copies)])
