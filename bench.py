@@ -313,7 +313,19 @@ def main():
             qb = sum(quant_bytes(m_.n, m_.k, 128, sym) for m_ in mats)
             res["asym" if not sym else "sym"] = {
                 "kernel": kname, "bytes": qb, "sweep_ms": round(t_q * 1e3, 3),
-                "gbs": round(qb / t_q / 1e9, 1), "frac_hbm": round(qb / t_q / 1e9 / HBM_PEAK_GBS, 4)}
+                "gbs": round(qb / t_q / 1e9, 1), "frac_hbm": round(qb / t_q / 1e9 / HBM_PEAK_GBS, 4),
+                "launch": "one launch per matrix (224)"}
+            # the same conversion one layer (seven matrices) per grouped launch
+            fqg = [(lambda b=b: q4.q4_quantize_pack_grouped(ws[b:b + 7], 128, sym, outs=pk[b:b + 7]))
+                   for b in range(0, len(mats), 7)]
+            for f in fqg:
+                f()
+            torch.cuda.synchronize()
+            t_qg = graph_ms(capture(fqg), 3) * 1e-3
+            res[("asym" if not sym else "sym") + "_grouped"] = {
+                "kernel": q4.q4_last_kernel(), "bytes": qb, "sweep_ms": round(t_qg * 1e3, 3),
+                "gbs": round(qb / t_qg / 1e9, 1), "frac_hbm": round(qb / t_qg / 1e9 / HBM_PEAK_GBS, 4),
+                "launch": "one grouped launch per layer (32)"}
             if not sym and "sweep" in legs:
                 xs = {4096: synthetic.activations(1, 4096, 10).to(dev),
                       11008: synthetic.activations(1, 11008, 10).to(dev)}
@@ -326,7 +338,29 @@ def main():
                 gb = sum(gemv_bytes(1, m_.n, m_.k, 128, False) for m_ in mats)
                 res["gemv_sweep_m1"] = {"bytes": gb, "sweep_ms": round(t_g * 1e3, 3),
                                         "gbs": round(gb / t_g / 1e9, 1),
-                                        "frac_hbm": round(gb / t_g / 1e9 / HBM_PEAK_GBS, 4)}
+                                        "frac_hbm": round(gb / t_g / 1e9 / HBM_PEAK_GBS, 4),
+                                        "launch": "one launch per matrix (224)"}
+                # as a decode step issues them: q/k/v share their input and so do gate/up,
+                # so each layer is four launches (q+k+v grouped, o, gate+up grouped, down)
+                ys_ = {i: torch.empty((1, mats[i].n), dtype=torch.float32, device=dev)
+                       for i in range(len(mats))}
+                fgg = []
+                for base_i in range(0, len(mats), 7):
+                    for idx in ([0, 1, 2], [3], [4, 5], [6]):
+                        ii = [base_i + j for j in idx]
+                        kk = mats[ii[0]].k
+                        if len(ii) == 1:
+                            fgg.append(lambda i=ii[0], kk=kk: q4.q4_w4a16_gemm(xs[kk], pk[i], out=ys_[i]))
+                        else:
+                            fgg.append(lambda ii=ii, kk=kk: q4.q4_w4a16_gemm_grouped(
+                                xs[kk], [pk[i] for i in ii], outs=[ys_[i] for i in ii]))
+                for f in fgg:
+                    f()
+                t_gg = graph_ms(capture(fgg), 3) * 1e-3
+                res["gemv_sweep_m1_grouped"] = {
+                    "bytes": gb, "sweep_ms": round(t_gg * 1e3, 3), "gbs": round(gb / t_gg / 1e9, 1),
+                    "frac_hbm": round(gb / t_gg / 1e9 / HBM_PEAK_GBS, 4),
+                    "launch": "four launches per layer (q+k+v grouped, o, gate+up grouped, down)"}
             del pk
         res["workload"] = "32-layer 7B-like checkpoint, 224 bf16 matrices, 6.48e9 weights, g128"
         out["checkpoint"] = res

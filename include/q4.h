@@ -62,11 +62,33 @@ typedef enum { Q4_F32 = 0, Q4_F16 = 1, Q4_BF16 = 2 } q4_dtype;
  * S is s rounded to fp16 (round-to-nearest-even); S = 0 is replaced by 1.0 and S = inf by
  * 65504; the codes are computed with S, round() is round-half-to-even, the division is
  * IEEE fp32.  Codes, scales and zeros are bit-identical to the CPU definition.
- * zeros may be NULL when symmetric != 0 (it is not written then). */
+ * zeros may be NULL when symmetric != 0 (it is not written then).  Beyond the shared size
+ * rules, k <= 2^28 (a row is addressed with 32-bit byte offsets). */
 q4_status q4_quantize_pack(const void* w, q4_dtype w_dtype, int64_t n, int64_t k,
                            int32_t group_size, int32_t symmetric,
                            uint32_t* qweight, uint16_t* scales, uint32_t* zeros,
                            hipStream_t stream);
+
+/* One matrix of a grouped quantize/pack call. */
+typedef struct {
+    const void* w;        /* [n][k] weights, in the dtype of the call */
+    int64_t n;            /* rows (output features) */
+    int64_t k;            /* columns (input features), a multiple of group_size */
+    uint32_t* qweight;    /* [n][k/8] packed codes (written) */
+    uint16_t* scales;     /* [n][k/g] fp16 bit patterns (written) */
+    uint32_t* zeros;      /* [n][ceil(k/g/8)] zero points (written); may be NULL when symmetric */
+} q4_quant_problem;
+
+/* Quantize/pack of several matrices that share dtype, group size and mode (e.g. the seven
+ * linear layers of one decoder layer) in one launch, each exactly as q4_quantize_pack
+ * would: same codes, scales and zero points, bit for bit ([FL7] §Per-group, applied per
+ * matrix).  Each matrix may have its own n and k.  One launch streams all of them, so
+ * small matrices do not each pay a launch's ramp-up and tail.  problems is a host array
+ * of 1 <= count <= 8 entries; every entry is validated as for q4_quantize_pack before
+ * anything is enqueued. */
+q4_status q4_quantize_pack_grouped(const q4_quant_problem* problems, int32_t count,
+                                   q4_dtype w_dtype, int32_t group_size, int32_t symmetric,
+                                   hipStream_t stream);
 
 /* Path B of [FL7] §Kernel이 없으면 압축 이점이 사라진다 (full dequantization):
  *   w_out[n][k] = S * (u - z),   x_hat = s(q - z)   [FL7] §Affine Quantization

@@ -140,3 +140,41 @@ def test_grouped_validation_rejects_before_launch(call, code):
 def test_grouped_symmetric_accepts_null_zeros_in_validation():
     # a bad group size is reported although every zeros pointer is NULL: NULL is accepted
     assert _grouped([_prob(zr=None), _prob(zr=None)], g=16, sym=1) == GROUP
+
+
+def _qgrouped(probs, count=None, wd=BF16, g=128, sym=0):
+    arr = (q4.QuantProblem * max(1, len(probs)))()
+    for i, pr in enumerate(probs):
+        arr[i] = pr
+    return q4.lib().q4_quantize_pack_grouped(arr if probs else None,
+                                             len(probs) if count is None else count, wd, g, sym, None)
+
+
+def _qprob(w=A16, n=16, k=256, qw=A16, sc=A16, zr=A16):
+    return q4.QuantProblem(w, n, k, qw, sc, zr)
+
+
+@pytest.mark.parametrize("call,code", [
+    (lambda: _qgrouped([]), NULL),
+    (lambda: _qgrouped([_qprob()], count=0), SHAPE),
+    (lambda: _qgrouped([_qprob()] * 9), SHAPE),
+    (lambda: _qgrouped([_qprob(), _qprob(n=0)]), SHAPE),
+    (lambda: _qgrouped([_qprob(), _qprob(k=200)]), SHAPE),
+    (lambda: _qgrouped([_qprob(), _qprob(k=(1 << 28) + 128)]), SHAPE),
+    (lambda: _qgrouped([_qprob(), _qprob(w=None)]), NULL),
+    (lambda: _qgrouped([_qprob(), _qprob(zr=None)]), NULL),
+    (lambda: _qgrouped([_qprob(), _qprob(qw=A16 + 4)]), ALIGN),
+    (lambda: _qgrouped([_qprob(), _qprob(w=A16 + 8)]), ALIGN),
+    (lambda: _qgrouped([_qprob(), _qprob()], g=48), GROUP),
+    (lambda: _qgrouped([_qprob(), _qprob()], wd=7), DTYPE),
+])
+def test_grouped_quantize_validation_rejects_before_launch(call, code):
+    """Every matrix is checked before anything is enqueued; the first failure is returned."""
+    assert call() == code
+    assert q4.q4_last_kernel() == ""
+
+
+def test_quantize_row_length_limit():
+    lib = q4.lib()
+    assert lib.q4_quantize_pack(A16, F32, 1, (1 << 28) + 128, 128, 0, A16, A16, A16, None) == SHAPE
+    assert _qgrouped([_qprob(zr=None), _qprob(zr=None)], g=16, sym=1) == GROUP

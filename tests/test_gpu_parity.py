@@ -165,6 +165,40 @@ def test_quant_scale_ties(dtype):
     assert_pack_exact(p, host_input(w), 32, False)
 
 
+@pytest.mark.parametrize("g", [32, 64, 128])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("sym", [False, True])
+def test_quant_grouped(g, dtype, sym):
+    """Several matrices of different shapes (one row, one group, partial zero-point words,
+    the stress distribution) in one grouped launch: each bit-identical to the oracle, no
+    store outside its buffers."""
+    shapes = [(33, 8 * g * 3 + g), (1, g), (200, 1024), (7, 4096 + g), (64, 256 if g < 256 else g)]
+    ws = []
+    for i, (n, k) in enumerate(shapes):
+        w = torch.from_numpy(pins.random_weights(300 + 7 * i + g, max(n, 12), k)[:n]).to(dtype)
+        if dtype == torch.float16:
+            w = torch.nan_to_num(w, posinf=60000.0, neginf=-60000.0)
+        ws.append(w)
+    note(f"quant grouped g={g} {dtype} sym={sym}")
+    outs, bufs = [], []
+    for w in ws:
+        n, k = w.shape
+        G = k // g
+        qb, qv = guarded((n, k // 8), torch.int32, SENTINEL_I32)
+        sb, sv = guarded((n, G), torch.int16, -1)
+        zb, zv = (None, None) if sym else guarded((n, (G + 7) // 8), torch.int32, SENTINEL_I32)
+        outs.append(q4.PackedWeight(qweight=qv, scales=sv.view(torch.float16), zeros=zv, n=n, k=k,
+                                    group_size=g, symmetric=sym))
+        bufs.append((qb, sb, zb))
+    q4.q4_quantize_pack_grouped([w.to(DEV) for w in ws], g, sym, outs=outs)
+    torch.cuda.synchronize()
+    assert q4.q4_last_kernel() == {torch.float32: "q4_quant_pack_f32", torch.float16: "q4_quant_pack_f16",
+                                   torch.bfloat16: "q4_quant_pack_bf16"}[dtype]
+    for w, p, b in zip(ws, outs, bufs):
+        check_guards(b, sym)
+        assert_pack_exact(p, host_input(w), g, sym)
+
+
 # ----------------------------------------------------------------------------- dequant
 
 @pytest.mark.parametrize("g,sym", [(32, False), (64, True), (128, False), (128, True)])

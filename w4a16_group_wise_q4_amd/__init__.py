@@ -23,7 +23,8 @@ import torch
 
 from . import _build
 
-__all__ = ["PackedWeight", "q4_quantize_pack", "q4_dequant", "q4_w4a16_gemm",
+__all__ = ["PackedWeight", "q4_quantize_pack", "q4_quantize_pack_grouped", "q4_dequant",
+           "q4_w4a16_gemm",
            "q4_w4a16_gemm_grouped", "q4_last_kernel",
            "q4_qweight_words", "q4_scale_count", "q4_zero_words", "q4_layout_version",
            "library_path", "Q4Error"]
@@ -31,7 +32,8 @@ __all__ = ["PackedWeight", "q4_quantize_pack", "q4_dequant", "q4_w4a16_gemm",
 Q4_F32, Q4_F16, Q4_BF16 = 0, 1, 2
 _DTYPE_CODE = {torch.float32: Q4_F32, torch.float16: Q4_F16, torch.bfloat16: Q4_BF16}
 
-EXPORTED = ("q4_quantize_pack", "q4_dequant", "q4_w4a16_gemm", "q4_w4a16_gemm_grouped",
+EXPORTED = ("q4_quantize_pack", "q4_quantize_pack_grouped", "q4_dequant", "q4_w4a16_gemm",
+            "q4_w4a16_gemm_grouped",
             "q4_qweight_words",
             "q4_scale_count", "q4_zero_words", "q4_status_str", "q4_last_kernel",
             "q4_layout_version")
@@ -41,6 +43,12 @@ class GemmProblem(ctypes.Structure):
     """q4_gemm_problem of the C ABI."""
     _fields_ = [("x", ctypes.c_void_p), ("qweight", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("zeros", ctypes.c_void_p), ("n", ctypes.c_int64), ("y", ctypes.c_void_p)]
+
+
+class QuantProblem(ctypes.Structure):
+    """q4_quant_problem of the C ABI."""
+    _fields_ = [("w", ctypes.c_void_p), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("qweight", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("zeros", ctypes.c_void_p)]
 
 
 MAX_GROUP = 8
@@ -71,6 +79,9 @@ def _load():
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     lib.q4_quantize_pack.argtypes = [vp, ctypes.c_int, i64, i64, i32, i32, vp, vp, vp, vp]
     lib.q4_quantize_pack.restype = ctypes.c_int
+    lib.q4_quantize_pack_grouped.argtypes = [ctypes.POINTER(QuantProblem), i32, ctypes.c_int, i32,
+                                             i32, vp]
+    lib.q4_quantize_pack_grouped.restype = ctypes.c_int
     lib.q4_dequant.argtypes = [vp, vp, vp, i64, i64, i32, i32, vp, ctypes.c_int, vp]
     lib.q4_dequant.restype = ctypes.c_int
     lib.q4_w4a16_gemm.argtypes = [vp, ctypes.c_int, i64, vp, vp, vp, i64, i64, i32, i32, vp, vp]
@@ -173,6 +184,30 @@ def q4_quantize_pack(w: torch.Tensor, group_size: int = 128, symmetric: bool = F
                                     int(bool(symmetric)), _dev_ptr(p.qweight),
                                     _dev_ptr(p.scales), _dev_ptr(p.zeros), _stream(w)))
     return p
+
+
+def q4_quantize_pack_grouped(ws, group_size: int = 128, symmetric: bool = False, outs=None):
+    """Quantize/pack up to 8 matrices (same dtype, group size and mode; each its own shape)
+    in one launch; the same bits as one q4_quantize_pack call per matrix."""
+    ws = list(ws)
+    count = len(ws)
+    if not 1 <= count <= MAX_GROUP:
+        raise ValueError(f"1 to {MAX_GROUP} matrices per call")
+    for w in ws:
+        _need_cuda("w", w)
+        if w.dim() != 2 or w.dtype not in _DTYPE_CODE or w.dtype != ws[0].dtype:
+            raise ValueError("matrices must be 2-D fp32, fp16 or bf16 tensors of one dtype")
+    ps = list(outs) if outs is not None else [
+        empty_packed(w.shape[0], w.shape[1], group_size, symmetric, w.device) for w in ws]
+    if len(ps) != count:
+        raise ValueError("one output per matrix")
+    arr = (QuantProblem * count)()
+    for i, (w, p) in enumerate(zip(ws, ps)):
+        arr[i] = QuantProblem(w.data_ptr(), w.shape[0], w.shape[1], p.qweight.data_ptr(),
+                              p.scales.data_ptr(), None if p.zeros is None else p.zeros.data_ptr())
+    _check(_load().q4_quantize_pack_grouped(arr, count, _DTYPE_CODE[ws[0].dtype], group_size,
+                                            int(bool(symmetric)), _stream(ws[0])))
+    return ps
 
 
 def q4_dequant(p: PackedWeight, out_dtype: torch.dtype = torch.float32,

@@ -45,6 +45,23 @@ q4_status check_packed(const uint32_t* qweight, const uint16_t* scales, const ui
     return Q4_OK;
 }
 
+// A row of w is addressed with 32-bit byte offsets (up to 4 bytes per weight).
+constexpr int64_t kMaxQuantK = int64_t(1) << 28;
+
+// The size, dtype, pointer and alignment rules of q4_quantize_pack for one matrix.
+q4_status check_quant(const void* w, q4_dtype w_dtype, int64_t n, int64_t k, int32_t group_size,
+                      int32_t symmetric, const uint32_t* qweight, const uint16_t* scales,
+                      const uint32_t* zeros) {
+    q4_status st = check_layout(n, k, group_size);
+    if (st != Q4_OK) return st;
+    if (k > kMaxQuantK) return Q4_ERR_SHAPE;
+    if (w_dtype != Q4_F32 && w_dtype != Q4_F16 && w_dtype != Q4_BF16) return Q4_ERR_DTYPE;
+    if (!w) return Q4_ERR_NULL;
+    if ((st = check_packed(qweight, scales, zeros, symmetric)) != Q4_OK) return st;
+    if (!aligned(w, 16)) return Q4_ERR_ALIGN;
+    return Q4_OK;
+}
+
 q4_status finish(hipError_t e, const char* name) {
     if (e != hipSuccess) return Q4_ERR_LAUNCH;
     g_last_kernel = name;
@@ -58,15 +75,31 @@ extern "C" {
 q4_status q4_quantize_pack(const void* w, q4_dtype w_dtype, int64_t n, int64_t k,
                            int32_t group_size, int32_t symmetric, uint32_t* qweight,
                            uint16_t* scales, uint32_t* zeros, hipStream_t stream) {
-    q4_status st = check_layout(n, k, group_size);
+    q4_status st = check_quant(w, w_dtype, n, k, group_size, symmetric, qweight, scales, zeros);
     if (st != Q4_OK) return st;
-    if (w_dtype != Q4_F32 && w_dtype != Q4_F16 && w_dtype != Q4_BF16) return Q4_ERR_DTYPE;
-    if (!w) return Q4_ERR_NULL;
-    if ((st = check_packed(qweight, scales, zeros, symmetric)) != Q4_OK) return st;
-    if (!aligned(w, 16)) return Q4_ERR_ALIGN;
     const char* name = "";
     hipError_t e = q4k_quant_pack(w, (int)w_dtype, n, k, group_size, symmetric ? 1 : 0, qweight,
                                   scales, zeros, stream, &name);
+    return finish(e, name);
+}
+
+q4_status q4_quantize_pack_grouped(const q4_quant_problem* problems, int32_t count,
+                                   q4_dtype w_dtype, int32_t group_size, int32_t symmetric,
+                                   hipStream_t stream) {
+    if (!problems) return Q4_ERR_NULL;
+    if (count < 1 || count > q4::kMaxGroup) return Q4_ERR_SHAPE;
+    q4::QuantProblem qp[q4::kMaxGroup];
+    for (int i = 0; i < count; ++i) {
+        const q4_quant_problem& p = problems[i];
+        const q4_status st = check_quant(p.w, w_dtype, p.n, p.k, group_size, symmetric, p.qweight,
+                                         p.scales, p.zeros);
+        if (st != Q4_OK) return st;
+        qp[i] = q4::QuantProblem{p.w, p.qweight, p.scales, symmetric ? nullptr : p.zeros, (int)p.n,
+                                 (int)p.k};
+    }
+    const char* name = "";
+    const hipError_t e = q4k_quant_pack_grouped(qp, count, (int)w_dtype, group_size,
+                                                symmetric ? 1 : 0, stream, &name);
     return finish(e, name);
 }
 

@@ -149,7 +149,23 @@ struct GemvBatch {
     GemvProblem p[kMaxGroup];
     int count;
 };
+// One matrix of a grouped quantize/pack launch, and the launch's problems.
+struct QuantProblem {
+    const void* w;
+    uint32_t* qweight;
+    uint16_t* scales;
+    uint32_t* zeros;
+    int n;
+    int k;
+};
+struct QuantBatch {
+    QuantProblem p[kMaxGroup];
+    int count;
+};
 }  // namespace q4
+// Several matrices sharing dtype, group size and mode quantized in one launch.
+hipError_t q4k_quant_pack_grouped(const q4::QuantProblem* problems, int count, int w_dtype, int g,
+                                  int sym, hipStream_t stream, const char** kname);
 // Decode tile kernels for one group size (32, 64 or 128): UPW units per wave, `waves` waves
 // per 16-row tile, one workgroup per tile of the batch; wide != 0 selects the kernel for
 // m up to 16 that streams the activations instead of staging them.

@@ -94,114 +94,124 @@ __device__ __forceinline__ void load_slice(q4::rsrc r, uint32_t off, float (&v)[
 __device__ __forceinline__ float xor_max(float v, int m) { return fmaxf(v, __shfl_xor(v, m, 64)); }
 __device__ __forceinline__ float xor_min(float v, int m) { return fminf(v, __shfl_xor(v, m, 64)); }
 
-// Persistent waves: wave gw starts at (row r0, zero word z0) = (gw / Z, gw % Z) and steps
-// by R rows and Z zero words, so every (row, zero word) task is done exactly once.
+// Persistent waves over the (row, zero word) tasks of every problem of the launch, one
+// problem after another.  For a problem with Z = min(zero words per row, waves) and
+// R = min(waves / Z, n), wave gw starts at (row r0, zero word z0) = (gw / Z, gw % Z) and
+// steps by R rows and Z zero words, so every task is done exactly once and consecutive
+// matrices of a grouped launch form one stream.
 template <int G, bool SYM, int DT>
-__global__ __launch_bounds__(256) void quant_pack_kernel(const void* __restrict__ w, int n, int k,
-                                                         uint32_t* __restrict__ qweight,
-                                                         uint16_t* __restrict__ scales,
-                                                         uint32_t* __restrict__ zeros, int R, int Z) {
+__global__ __launch_bounds__(256) void quant_pack_kernel(const q4::QuantBatch bt) {
     constexpr int E = G / 8;                // weights per lane
     constexpr uint32_t EB = DT == 0 ? 4 : 2;  // bytes per weight
     constexpr uint32_t kOff = 0xFFFFFFF0u;   // an offset past every resource
     const int lane = threadIdx.x & 63;
+    const int waves = (int)gridDim.x * (int)(blockDim.x >> 6);
     const int gw = (int)blockIdx.x * (int)(blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int r0 = gw / Z, z0 = gw - r0 * Z;
-    if (r0 >= R) return;  // wave-uniform: the few waves past R * Z
-    const int n_groups = k / G;
-    const int zwords = (n_groups + 7) >> 3;
     const int grp = lane >> 3;
     const int t = lane & 7;
+    for (int pi = 0; pi < bt.count; ++pi) {
+        const void* __restrict__ w = bt.p[pi].w;
+        uint32_t* __restrict__ qweight = bt.p[pi].qweight;
+        uint16_t* __restrict__ scales = bt.p[pi].scales;
+        uint32_t* __restrict__ zeros = bt.p[pi].zeros;
+        const int n = bt.p[pi].n, k = bt.p[pi].k;
+        const int n_groups = k / G;
+        const int zwords = (n_groups + 7) >> 3;
+        const int Z = zwords < waves ? zwords : waves;
+        const int R = waves / Z < n ? waves / Z : n;
+        const int r0 = gw / Z, z0 = gw - r0 * Z;
+        if (r0 >= R) continue;  // wave-uniform: the waves past R * Z sit this problem out
 
-    for (int row = r0; row < n; row += R) {
-        const q4::rsrc rw = q4::make_rsrc(reinterpret_cast<const char*>(w) + (int64_t)row * k * EB,
-                                          (uint32_t)k * EB);
-        const q4::rsrc rq = q4::make_rsrc(qweight + (int64_t)row * (k / 8), (uint32_t)k / 2u);
-        const q4::rsrc rs = q4::make_rsrc(scales + (int64_t)row * n_groups, (uint32_t)n_groups * 2u);
-        const q4::rsrc rz = q4::make_rsrc(zeros + (int64_t)row * zwords, (uint32_t)zwords * 4u);
-        for (int zw = z0; zw < zwords; zw += Z) {
-            const int gidx = zw * 8 + grp;
-            const bool valid = gidx < n_groups;
-            const uint32_t elem = (uint32_t)gidx * G + (uint32_t)t * E;  // within the row
-            float v[E];
-            load_slice<E, DT>(rw, valid ? elem * EB : kOff, v);
+        for (int row = r0; row < n; row += R) {
+            const q4::rsrc rw = q4::make_rsrc(reinterpret_cast<const char*>(w) + (int64_t)row * k * EB,
+                                              (uint32_t)k * EB);
+            const q4::rsrc rq = q4::make_rsrc(qweight + (int64_t)row * (k / 8), (uint32_t)k / 2u);
+            const q4::rsrc rs = q4::make_rsrc(scales + (int64_t)row * n_groups, (uint32_t)n_groups * 2u);
+            const q4::rsrc rz = q4::make_rsrc(zeros + (int64_t)row * zwords, (uint32_t)zwords * 4u);
+            for (int zw = z0; zw < zwords; zw += Z) {
+                const int gidx = zw * 8 + grp;
+                const bool valid = gidx < n_groups;
+                const uint32_t elem = (uint32_t)gidx * G + (uint32_t)t * E;  // within the row
+                float v[E];
+                load_slice<E, DT>(rw, valid ? elem * EB : kOff, v);
 
-            // group statistics: zero-extended [min, max] (asymmetric) or max |w| (symmetric)
-            float s, x_min = 0.0f, x_max = 0.0f;
-            if constexpr (SYM) {
-                float amax = 0.0f;
+                // group statistics: zero-extended [min, max] (asymmetric) or max |w| (symmetric)
+                float s, x_min = 0.0f, x_max = 0.0f;
+                if constexpr (SYM) {
+                    float amax = 0.0f;
 #pragma unroll
-                for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(v[e]));
-                amax = xor_max(amax, 1);
-                amax = xor_max(amax, 2);
-                amax = xor_max(amax, 4);
-                s = div_const<7>(amax);
-            } else {
+                    for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(v[e]));
+                    amax = xor_max(amax, 1);
+                    amax = xor_max(amax, 2);
+                    amax = xor_max(amax, 4);
+                    s = div_const<7>(amax);
+                } else {
 #pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    x_min = fminf(x_min, v[e]);
-                    x_max = fmaxf(x_max, v[e]);
+                    for (int e = 0; e < E; ++e) {
+                        x_min = fminf(x_min, v[e]);
+                        x_max = fmaxf(x_max, v[e]);
+                    }
+                    x_min = xor_min(x_min, 1); x_max = xor_max(x_max, 1);
+                    x_min = xor_min(x_min, 2); x_max = xor_max(x_max, 2);
+                    x_min = xor_min(x_min, 4); x_max = xor_max(x_max, 4);
+                    s = div_const<15>(x_max - x_min);
                 }
-                x_min = xor_min(x_min, 1); x_max = xor_max(x_max, 1);
-                x_min = xor_min(x_min, 2); x_max = xor_max(x_max, 2);
-                x_min = xor_min(x_min, 4); x_max = xor_max(x_max, 4);
-                s = div_const<15>(x_max - x_min);
-            }
-            // stored fp16 scale: s is rounded to fp32 first, then to fp16 (round-to-nearest-
-            // even both times).  The empty asm pins s as an fp32 value: otherwise the compiler
-            // folds the last FMA of the division and the conversion into one fp16-rounding
-            // instruction, which differs from the double rounding on fp16 ties.
-            asm volatile("" : "+v"(s));
-            uint16_t s16 = __builtin_bit_cast(uint16_t, (_Float16)s);
-            if ((s16 & 0x7FFFu) == 0) s16 = 0x3C00u;
-            if (s16 == 0x7C00u) s16 = 0x7BFFu;
-            const float S = (float)__builtin_bit_cast(_Float16, s16);
+                // stored fp16 scale: s is rounded to fp32 first, then to fp16 (round-to-nearest-
+                // even both times).  The empty asm pins s as an fp32 value: otherwise the compiler
+                // folds the last FMA of the division and the conversion into one fp16-rounding
+                // instruction, which differs from the double rounding on fp16 ties.
+                asm volatile("" : "+v"(s));
+                uint16_t s16 = __builtin_bit_cast(uint16_t, (_Float16)s);
+                if ((s16 & 0x7FFFu) == 0) s16 = 0x3C00u;
+                if (s16 == 0x7C00u) s16 = 0x7BFFu;
+                const float S = (float)__builtin_bit_cast(_Float16, s16);
 
-            uint32_t packed[(E + 7) / 8];
+                uint32_t packed[(E + 7) / 8];
 #pragma unroll
-            for (int j = 0; j < (E + 7) / 8; ++j) packed[j] = 0;
-            int zi = 8;
-            if constexpr (DT == 0) {
-                // fp32 weights: IEEE quotients
-                float zf = 0.0f;
-                if constexpr (!SYM) zf = fminf(fmaxf(rintf(-x_min / S), 0.0f), 15.0f);
-                constexpr float q_min = SYM ? -8.0f : 0.0f;
-                constexpr float q_max = SYM ? 7.0f : 15.0f;
+                for (int j = 0; j < (E + 7) / 8; ++j) packed[j] = 0;
+                int zi = 8;
+                if constexpr (DT == 0) {
+                    // fp32 weights: IEEE quotients
+                    float zf = 0.0f;
+                    if constexpr (!SYM) zf = fminf(fmaxf(rintf(-x_min / S), 0.0f), 15.0f);
+                    constexpr float q_min = SYM ? -8.0f : 0.0f;
+                    constexpr float q_max = SYM ? 7.0f : 15.0f;
 #pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const float qf = fminf(fmaxf(rintf(v[e] / S) + zf, q_min), q_max);
-                    packed[e / 8] |= (uint32_t)((int)qf + (SYM ? 8 : 0)) << (4 * (e % 8));
+                    for (int e = 0; e < E; ++e) {
+                        const float qf = fminf(fmaxf(rintf(v[e] / S) + zf, q_min), q_max);
+                        packed[e / 8] |= (uint32_t)((int)qf + (SYM ? 8 : 0)) << (4 * (e % 8));
+                    }
+                    if constexpr (!SYM) zi = (int)zf;
+                } else {
+                    // 16-bit weights: correctly rounded reciprocal once, corrected quotients;
+                    // -x_min is itself one of the group's weights (or 0)
+                    const float y = 1.0f / S;
+                    if constexpr (!SYM) zi = min(max(rne_small(quot16(-x_min, S, y)), 0), 15);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const int u = min(max(rne_small(quot16(v[e], S, y)) + zi, 0), 15);
+                        packed[e / 8] |= (uint32_t)u << (4 * (e % 8));
+                    }
                 }
-                if constexpr (!SYM) zi = (int)zf;
-            } else {
-                // 16-bit weights: correctly rounded reciprocal once, corrected quotients;
-                // -x_min is itself one of the group's weights (or 0)
-                const float y = 1.0f / S;
-                if constexpr (!SYM) zi = min(max(rne_small(quot16(-x_min, S, y)), 0), 15);
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const int u = min(max(rne_small(quot16(v[e], S, y)) + zi, 0), 15);
-                    packed[e / 8] |= (uint32_t)u << (4 * (e % 8));
-                }
-            }
 
-            // codes: E/2 bytes per lane, contiguous across the wave
-            const uint32_t qoff = valid ? elem / 2u : kOff;
-            if constexpr (E == 16) {
-                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(q4::u32x2, q4::u32x2{packed[0], packed[1]}),
-                                                      rq, (int)qoff, 0, 0);
-            } else if constexpr (E == 8) {
-                __builtin_amdgcn_raw_buffer_store_b32(packed[0], rq, (int)qoff, 0, 0);
-            } else {  // E == 4: half a word
-                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)packed[0], rq, (int)qoff, 0, 0);
-            }
-            __builtin_amdgcn_raw_buffer_store_b16(s16, rs, (int)(valid && t == 0 ? (uint32_t)gidx * 2u : kOff), 0, 0);
-            if constexpr (!SYM) {
-                uint32_t zn = valid ? ((uint32_t)zi << (4 * grp)) : 0u;
-                zn |= __shfl_xor(zn, 8, 64);
-                zn |= __shfl_xor(zn, 16, 64);
-                zn |= __shfl_xor(zn, 32, 64);
-                __builtin_amdgcn_raw_buffer_store_b32(zn, rz, (int)(lane == 0 ? (uint32_t)zw * 4u : kOff), 0, 0);
+                // codes: E/2 bytes per lane, contiguous across the wave
+                const uint32_t qoff = valid ? elem / 2u : kOff;
+                if constexpr (E == 16) {
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(q4::u32x2, q4::u32x2{packed[0], packed[1]}),
+                                                          rq, (int)qoff, 0, 0);
+                } else if constexpr (E == 8) {
+                    __builtin_amdgcn_raw_buffer_store_b32(packed[0], rq, (int)qoff, 0, 0);
+                } else {  // E == 4: half a word
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)packed[0], rq, (int)qoff, 0, 0);
+                }
+                __builtin_amdgcn_raw_buffer_store_b16(s16, rs, (int)(valid && t == 0 ? (uint32_t)gidx * 2u : kOff), 0, 0);
+                if constexpr (!SYM) {
+                    uint32_t zn = valid ? ((uint32_t)zi << (4 * grp)) : 0u;
+                    zn |= __shfl_xor(zn, 8, 64);
+                    zn |= __shfl_xor(zn, 16, 64);
+                    zn |= __shfl_xor(zn, 32, 64);
+                    __builtin_amdgcn_raw_buffer_store_b32(zn, rz, (int)(lane == 0 ? (uint32_t)zw * 4u : kOff), 0, 0);
+                }
             }
         }
     }
@@ -210,8 +220,7 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(const void* __restrict_
 int g_num_cus = 0;
 
 template <int G, bool SYM>
-hipError_t launch_dt(const void* w, int dt, int64_t n, int64_t k, uint32_t* qw, uint16_t* sc,
-                     uint32_t* zr, hipStream_t st, const char** kname) {
+hipError_t launch_dt(const q4::QuantBatch& bt, int dt, hipStream_t st, const char** kname) {
     if (g_num_cus == 0) {
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
@@ -219,26 +228,38 @@ hipError_t launch_dt(const void* w, int dt, int64_t n, int64_t k, uint32_t* qw, 
             g_num_cus <= 0)
             g_num_cus = 256;
     }
-    const int64_t zwords = (k / G + 7) / 8;
-    // enough waves to keep every SIMD busy (8 per SIMD), no more than there are tasks
+    // enough waves to keep every SIMD busy (8 per SIMD), no more than the largest problem
+    // has tasks
     const int64_t cap = (int64_t)g_num_cus * 32;
-    const int64_t tasks = n * zwords;
+    int64_t tasks = 0;
+    for (int i = 0; i < bt.count; ++i) {
+        const int64_t t = (int64_t)bt.p[i].n * ((bt.p[i].k / G + 7) / 8);
+        tasks = t > tasks ? t : tasks;
+    }
     const int64_t waves = tasks < cap ? tasks : cap;
-    const int64_t Z = zwords < waves ? zwords : waves;
-    int64_t R = waves / Z;
-    if (R > n) R = n;
-    const int64_t blocks = (R * Z + 3) / 4;
+    const int64_t blocks = (waves + 3) / 4;
     static const char* names[3] = {"q4_quant_pack_f32", "q4_quant_pack_f16", "q4_quant_pack_bf16"};
     *kname = names[dt];
     const dim3 grid((unsigned)blocks), block(256);
-    const int ni = (int)n, ki = (int)k, Ri = (int)R, Zi = (int)Z;
     if (dt == 0)
-        hipLaunchKernelGGL((quant_pack_kernel<G, SYM, 0>), grid, block, 0, st, w, ni, ki, qw, sc, zr, Ri, Zi);
+        hipLaunchKernelGGL((quant_pack_kernel<G, SYM, 0>), grid, block, 0, st, bt);
     else if (dt == 1)
-        hipLaunchKernelGGL((quant_pack_kernel<G, SYM, 1>), grid, block, 0, st, w, ni, ki, qw, sc, zr, Ri, Zi);
+        hipLaunchKernelGGL((quant_pack_kernel<G, SYM, 1>), grid, block, 0, st, bt);
     else
-        hipLaunchKernelGGL((quant_pack_kernel<G, SYM, 2>), grid, block, 0, st, w, ni, ki, qw, sc, zr, Ri, Zi);
+        hipLaunchKernelGGL((quant_pack_kernel<G, SYM, 2>), grid, block, 0, st, bt);
     return hipGetLastError();
+}
+
+hipError_t launch_batch(const q4::QuantBatch& bt, int w_dtype, int g, int sym, hipStream_t st,
+                        const char** kname) {
+    switch (g * 2 + (sym ? 1 : 0)) {
+    case 64: return launch_dt<32, false>(bt, w_dtype, st, kname);
+    case 65: return launch_dt<32, true>(bt, w_dtype, st, kname);
+    case 128: return launch_dt<64, false>(bt, w_dtype, st, kname);
+    case 129: return launch_dt<64, true>(bt, w_dtype, st, kname);
+    case 256: return launch_dt<128, false>(bt, w_dtype, st, kname);
+    default: return launch_dt<128, true>(bt, w_dtype, st, kname);
+    }
 }
 
 }  // namespace
@@ -246,12 +267,17 @@ hipError_t launch_dt(const void* w, int dt, int64_t n, int64_t k, uint32_t* qw, 
 hipError_t q4k_quant_pack(const void* w, int w_dtype, int64_t n, int64_t k, int g, int sym,
                           uint32_t* qweight, uint16_t* scales, uint32_t* zeros,
                           hipStream_t stream, const char** kname) {
-    switch (g * 2 + (sym ? 1 : 0)) {
-    case 64: return launch_dt<32, false>(w, w_dtype, n, k, qweight, scales, zeros, stream, kname);
-    case 65: return launch_dt<32, true>(w, w_dtype, n, k, qweight, scales, zeros, stream, kname);
-    case 128: return launch_dt<64, false>(w, w_dtype, n, k, qweight, scales, zeros, stream, kname);
-    case 129: return launch_dt<64, true>(w, w_dtype, n, k, qweight, scales, zeros, stream, kname);
-    case 256: return launch_dt<128, false>(w, w_dtype, n, k, qweight, scales, zeros, stream, kname);
-    default: return launch_dt<128, true>(w, w_dtype, n, k, qweight, scales, zeros, stream, kname);
-    }
+    q4::QuantBatch bt{};
+    bt.p[0] = q4::QuantProblem{w, qweight, scales, zeros, (int)n, (int)k};
+    bt.count = 1;
+    return launch_batch(bt, w_dtype, g, sym, stream, kname);
+}
+
+hipError_t q4k_quant_pack_grouped(const q4::QuantProblem* problems, int count, int w_dtype, int g,
+                                  int sym, hipStream_t stream, const char** kname) {
+    if (count < 1 || count > q4::kMaxGroup) return hipErrorInvalidValue;
+    q4::QuantBatch bt{};
+    for (int i = 0; i < count; ++i) bt.p[i] = problems[i];
+    bt.count = count;
+    return launch_batch(bt, w_dtype, g, sym, stream, kname);
 }
