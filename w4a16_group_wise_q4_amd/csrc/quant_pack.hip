@@ -122,18 +122,37 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(const q4::QuantBatch bt
         const int r0 = gw / Z, z0 = gw - r0 * Z;
         if (r0 >= R) continue;  // wave-uniform: the waves past R * Z sit this problem out
 
-        for (int row = r0; row < n; row += R) {
-            const q4::rsrc rw = q4::make_rsrc(reinterpret_cast<const char*>(w) + (int64_t)row * k * EB,
+        // one task's weights (none past the last row: an offset past the resource)
+        auto issue = [&](int rr, int zz, float (&dst)[E]) {
+            const bool live = rr < n;
+            const q4::rsrc rw = q4::make_rsrc(reinterpret_cast<const char*>(w) + (int64_t)(live ? rr : 0) * k * EB,
                                               (uint32_t)k * EB);
-            const q4::rsrc rq = q4::make_rsrc(qweight + (int64_t)row * (k / 8), (uint32_t)k / 2u);
-            const q4::rsrc rs = q4::make_rsrc(scales + (int64_t)row * n_groups, (uint32_t)n_groups * 2u);
-            const q4::rsrc rz = q4::make_rsrc(zeros + (int64_t)row * zwords, (uint32_t)zwords * 4u);
-            for (int zw = z0; zw < zwords; zw += Z) {
+            const int gi = zz * 8 + grp;
+            const uint32_t el = (uint32_t)gi * G + (uint32_t)t * E;
+            load_slice<E, DT>(rw, live && gi < n_groups ? el * EB : kOff, dst);
+        };
+        // tasks in order (row, zero word), the next task's weights loaded before this
+        // task's arithmetic so that one load is always in flight behind the compute
+        int row = r0, zw = z0;
+        float vn[E];
+        issue(row, zw, vn);
+        while (row < n) {
+            float v[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) v[e] = vn[e];
+            int nrow = row, nzw = zw + Z;
+            if (nzw >= zwords) {
+                nzw = z0;
+                nrow = row + R;
+            }
+            issue(nrow, nzw, vn);
+            {
+                const q4::rsrc rq = q4::make_rsrc(qweight + (int64_t)row * (k / 8), (uint32_t)k / 2u);
+                const q4::rsrc rs = q4::make_rsrc(scales + (int64_t)row * n_groups, (uint32_t)n_groups * 2u);
+                const q4::rsrc rz = q4::make_rsrc(zeros + (int64_t)row * zwords, (uint32_t)zwords * 4u);
                 const int gidx = zw * 8 + grp;
                 const bool valid = gidx < n_groups;
                 const uint32_t elem = (uint32_t)gidx * G + (uint32_t)t * E;  // within the row
-                float v[E];
-                load_slice<E, DT>(rw, valid ? elem * EB : kOff, v);
 
                 // group statistics: zero-extended [min, max] (asymmetric) or max |w| (symmetric)
                 float s, x_min = 0.0f, x_max = 0.0f;
@@ -213,6 +232,8 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(const q4::QuantBatch bt
                     __builtin_amdgcn_raw_buffer_store_b32(zn, rz, (int)(lane == 0 ? (uint32_t)zw * 4u : kOff), 0, 0);
                 }
             }
+            row = nrow;
+            zw = nzw;
         }
     }
 }
