@@ -74,6 +74,8 @@ class Oracle:
         lib.orc_bf16_to_f32.restype = ctypes.c_float
         lib.orc_quantize_pack.argtypes = [vp, c_int, c_i64, c_i64, c_i64, c_int, vp, vp, vp, vp]
         lib.orc_quantize_pack.restype = c_int
+        lib.orc_quantize_pack_mse.argtypes = [vp, c_int, c_i64, c_i64, c_i64, c_int, vp, vp, vp, vp]
+        lib.orc_quantize_pack_mse.restype = c_int
         lib.orc_dequant_f64.argtypes = [vp, vp, vp, c_i64, c_i64, c_i64, c_int, vp]
         lib.orc_dequant_f64.restype = c_int
         lib.orc_linear_f64.argtypes = [vp, c_int, c_i64, vp, c_i64, vp, vp, vp,
@@ -116,6 +118,26 @@ class Oracle:
             raise ValueError("oracle quantize_pack rejected the arguments")
         if with_diag:
             return qweight, scales, zeros, onesided
+        return qweight, scales, zeros
+
+    def quantize_pack_mse(self, w, group_size: int, symmetric: bool, with_choice: bool = False):
+        """MSE-optimal clip search + pack of W [n, k]: (qweight, scales, zeros) as
+        quantize_pack, and with ``with_choice`` the chosen ratio index per group (alpha =
+        (20 - i) / 20)."""
+        arr, code = _as_input(w)
+        n, k = arr.shape
+        G = k // group_size
+        qweight = np.zeros((n, k // 8), dtype=np.uint32)
+        scales = np.zeros((n, G), dtype=np.uint16)
+        zeros = np.zeros((n, (G + 7) // 8), dtype=np.uint32)
+        choice = np.zeros((n, G), dtype=np.uint8)
+        rc = self.lib.orc_quantize_pack_mse(_ptr(arr), code, n, k, group_size,
+                                            int(bool(symmetric)), _ptr(qweight), _ptr(scales),
+                                            _ptr(zeros), _ptr(choice))
+        if rc != 0:
+            raise ValueError("oracle quantize_pack_mse rejected the arguments")
+        if with_choice:
+            return qweight, scales, zeros, choice
         return qweight, scales, zeros
 
     def dequant(self, qweight, scales, zeros, n: int, k: int, group_size: int,

@@ -176,6 +176,120 @@ int orc_quantize_pack(const void* w, int w_dtype, int64_t n, int64_t k, int64_t 
     return 0;
 }
 
+/* ---------------------------------------------------------------- MSE-optimal clipping */
+
+/* Clip search per group ([FL7] §Clipping Trade-off: pick the clipping threshold that
+ * minimizes the local reconstruction error; [QA1] §MSE-optimal: argmin ||x - x_dq||^2).
+ * Readings where the pages leave the search open:
+ *   M1 candidates: clip ratios alpha_i = (20 - i) / 20 in fp32, i = 0..10 (1.0 down to 0.5),
+ *      tried in that order;
+ *   M2 a candidate quantizes exactly as RTN does (R1-R8) with its range scaled by alpha:
+ *      asymmetric [alpha*min(x_min,0), alpha*max(x_max,0)], symmetric alpha*max|x|, each
+ *      product one fp32 rounding; the zero point divides -alpha*min(x_min,0) by S in fp32;
+ *      weights outside the clipped range saturate at the end codes;
+ *   M3 the error of a candidate is sum over the group of (x - S*(q - z))^2 in IEEE binary64:
+ *      the group is cut into 8 chunks of g/8 consecutive weights, each chunk summed in
+ *      order from 0, then the chunk sums are added pairwise,
+ *      ((c0 + c1) + (c2 + c3)) + ((c4 + c5) + (c6 + c7));
+ *   M4 the candidate with the smallest error wins; an equal error keeps the earlier
+ *      (larger) ratio, so alpha = 1 (plain RTN) wins unless clipping strictly helps. */
+#define ORC_MSE_CANDIDATES 11
+
+/* scale, zero point and codes of one group for clip ratio alpha; returns the error (M3) */
+static double mse_candidate(const float* v, int64_t g, int symmetric, float alpha,
+                            uint16_t* s16_out, int* z_out, int* q_out) {
+    float s, lo = 0.0f;
+    if (symmetric) {
+        float amax = 0.0f;
+        for (int64_t t = 0; t < g; ++t) amax = fmaxf(amax, fabsf(v[t]));
+        s = (alpha * amax) / 7.0f;
+    } else {
+        float x_min = 0.0f, x_max = 0.0f;
+        for (int64_t t = 0; t < g; ++t) {
+            x_min = fminf(x_min, v[t]);
+            x_max = fmaxf(x_max, v[t]);
+        }
+        lo = alpha * x_min;
+        const float hi = alpha * x_max;
+        s = (hi - lo) / 15.0f;
+    }
+    uint16_t s16 = orc_f32_to_f16_rne(s);
+    if ((s16 & 0x7FFFu) == 0) s16 = 0x3C00u;
+    if (s16 == 0x7C00u) s16 = 0x7BFFu;
+    const float S = orc_f16_to_f32(s16);
+    const float q_min = symmetric ? -8.0f : 0.0f;
+    const float q_max = symmetric ? 7.0f : 15.0f;
+    int z = 0;
+    if (!symmetric) z = (int)clampf(rintf(-lo / S), q_min, q_max);
+    const int64_t chunk = g / 8;
+    double part[8];
+    for (int c = 0; c < 8; ++c) {
+        double acc = 0.0;
+        for (int64_t t = c * chunk; t < (c + 1) * chunk; ++t) {
+            const int q = (int)clampf(rintf(v[t] / S) + (float)z, q_min, q_max);
+            if (q_out) q_out[t] = q;
+            const double xhat = (double)S * (double)(q - z);
+            const double d = (double)v[t] - xhat;
+            acc = acc + d * d;
+        }
+        part[c] = acc;
+    }
+    const double err = ((part[0] + part[1]) + (part[2] + part[3])) +
+                       ((part[4] + part[5]) + (part[6] + part[7]));
+    *s16_out = s16;
+    *z_out = z;
+    return err;
+}
+
+int orc_quantize_pack_mse(const void* w, int w_dtype, int64_t n, int64_t k, int64_t g,
+                          int symmetric, uint32_t* qweight, uint16_t* scales, uint32_t* zeros,
+                          uint8_t* choice) {
+    if (n < 0 || k < 0 || g < 8 || g % 8 != 0 || k % g != 0 || k % 8 != 0) return -1;
+    const int64_t G = k / g;
+    const int64_t zw = (G + 7) / 8;
+    memset(qweight, 0, (size_t)(n * (k / 8)) * sizeof(uint32_t));
+    if (!symmetric) memset(zeros, 0, (size_t)(n * zw) * sizeof(uint32_t));
+    float* v = (float*)malloc((size_t)g * sizeof(float));
+    int* q = (int*)malloc((size_t)g * sizeof(int));
+    if (!v || !q) {
+        free(v);
+        free(q);
+        return -1;
+    }
+    for (int64_t row = 0; row < n; ++row) {
+        for (int64_t j = 0; j < G; ++j) {
+            for (int64_t t = 0; t < g; ++t) v[t] = load_elem(w, w_dtype, row * k + j * g + t);
+            /* M1, M4: scan the ratios, keep the first smallest error */
+            int best = 0;
+            double best_err = 0.0;
+            for (int i = 0; i < ORC_MSE_CANDIDATES; ++i) {
+                const float alpha = (float)(20 - i) / 20.0f;
+                uint16_t s16;
+                int z;
+                const double e = mse_candidate(v, g, symmetric, alpha, &s16, &z, NULL);
+                if (i == 0 || e < best_err) {
+                    best = i;
+                    best_err = e;
+                }
+            }
+            uint16_t s16;
+            int z;
+            mse_candidate(v, g, symmetric, (float)(20 - best) / 20.0f, &s16, &z, q);
+            scales[row * G + j] = s16;
+            if (!symmetric) zeros[row * zw + j / 8] |= (uint32_t)z << (4 * (j % 8));
+            if (choice) choice[row * G + j] = (uint8_t)best;
+            for (int64_t t = 0; t < g; ++t) {
+                const uint32_t u = (uint32_t)(symmetric ? q[t] + 8 : q[t]);
+                const int64_t col = j * g + t;
+                qweight[row * (k / 8) + col / 8] |= u << (4 * (col % 8));
+            }
+        }
+    }
+    free(v);
+    free(q);
+    return 0;
+}
+
 /* ---------------------------------------------------------------- dequant */
 
 static double xhat_elem(const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros,

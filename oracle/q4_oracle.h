@@ -52,6 +52,16 @@ int orc_quantize_pack(const void* w, int w_dtype, int64_t n, int64_t k, int64_t 
                       int symmetric, uint32_t* qweight, uint16_t* scales,
                       uint32_t* zeros, uint8_t* onesided);
 
+/* MSE-optimal clip search ([FL7] §Clipping Trade-off; [QA1] §MSE-optimal): per group, the
+ * RTN quantization of the range scaled by each clip ratio alpha_i = (20 - i) / 20,
+ * i = 0..10, scored by the fp64 squared reconstruction error summed in 8 chunks of g/8
+ * weights and then pairwise; the first smallest error wins (alpha = 1 is plain RTN).
+ * Same packed layout as orc_quantize_pack.  choice[n*G] (may be NULL) receives i.
+ * Returns 0 on success, -1 on bad arguments (also g % 8 != 0). */
+int orc_quantize_pack_mse(const void* w, int w_dtype, int64_t n, int64_t k, int64_t g,
+                          int symmetric, uint32_t* qweight, uint16_t* scales,
+                          uint32_t* zeros, uint8_t* choice);
+
 /* x_hat[n][k] = S * (u - z) in fp64 (exact), z = stored zero (asym) or 8 (sym). */
 int orc_dequant_f64(const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros,
                     int64_t n, int64_t k, int64_t g, int symmetric, double* out);

@@ -329,6 +329,111 @@ def check_argument_rejection(o):
     assert o.lib.orc_quantize_pack(None, 0, 2, 20, 4, 0, None, None, None, None) == -1
 
 
+# --------------------------------------------------------------------------- MSE clip search
+
+MSE_CANDIDATES = 11
+
+
+def _fp16_scale(s32):
+    """Stored fp16 scale bits of an fp32 scale, degenerate values replaced (numpy's own
+    float16 conversion, round-to-nearest-even)."""
+    with np.errstate(over="ignore"):         # scales past fp16's range become inf, then 65504
+        b = int(np.array([s32], dtype=np.float32).astype(np.float16).view(np.uint16)[0])
+    if b & 0x7FFF == 0:
+        b = 0x3C00
+    if b == 0x7C00:
+        b = 0x7BFF
+    return b
+
+
+def mse_candidates_numpy(v, sym):
+    """Every clip ratio alpha = (20 - i) / 20 of one group v (float32), quantized the way
+    the affine RTN quantizer does with the range scaled by alpha, written again in numpy:
+    a list of (error in float64, s16 bits, z, codes) per candidate."""
+    f32 = np.float32
+    out = []
+    for i in range(MSE_CANDIDATES):
+        alpha = f32(20 - i) / f32(20)
+        if sym:
+            s = (alpha * np.max(np.abs(v))) / f32(7)
+            lo = f32(0)
+        else:
+            mn = min(f32(0), v.min())
+            mx = max(f32(0), v.max())
+            lo = alpha * mn
+            s = (alpha * mx - lo) / f32(15)
+        s16 = _fp16_scale(s)
+        S = np.array([s16], dtype=np.uint16).view(np.float16).astype(np.float32)[0]
+        qmin, qmax = (f32(-8), f32(7)) if sym else (f32(0), f32(15))
+        z = 0 if sym else int(np.clip(np.rint(-lo / S), qmin, qmax))
+        q = np.clip(np.rint(v / S) + f32(z), qmin, qmax).astype(np.int64)
+        xhat = np.float64(S) * (q - z).astype(np.float64)
+        err = float(np.sum((v.astype(np.float64) - xhat) ** 2))
+        out.append((err, s16, z, q))
+    return out
+
+
+def check_mse_brute_force(o):
+    """Each group's pick is a minimal-error candidate of an independent numpy search (up
+    to the order of the fp64 sum), no earlier candidate quantizes the group identically
+    (equal errors keep the earlier ratio), and the stored bits are that candidate's."""
+    for seed, n, k, g, sym in [(41, 12, 256, 32, False), (42, 12, 256, 128, True),
+                               (43, 12, 512, 64, False), (44, 12, 128, 32, True)]:
+        w = random_weights(seed, n, k)
+        w[11, :g] = np.linspace(-1, 1, g, dtype=np.float32)
+        w[11, g - 1] = np.float32(20)              # one far outlier
+        q, s, z, ch = o.quantize_pack_mse(w, g, sym, with_choice=True)
+        G = k // g
+        codes = unpack_codes(q, k)
+        zz = unpack_zeros(z, G) if not sym else None
+        picked_clip = 0
+        for row in range(n):
+            for j in range(G):
+                v = w[row, j * g:(j + 1) * g]
+                cands = mse_candidates_numpy(v, sym)
+                i = int(ch[row, j])
+                assert 0 <= i < MSE_CANDIDATES
+                err, s16, zc, qc = cands[i]
+                emin = min(c[0] for c in cands)
+                assert err <= emin * (1 + 1e-12), (seed, row, j, i, err, emin)
+                for i2 in range(i):
+                    c2 = cands[i2]
+                    assert not (c2[1] == s16 and c2[2] == zc and np.array_equal(c2[3], qc)), \
+                        (seed, row, j, i, i2)
+                    assert c2[0] >= err * (1 - 1e-12), (seed, row, j, i, i2)
+                assert int(s[row, j]) == s16, (seed, row, j)
+                u = codes[row, j * g:(j + 1) * g]
+                assert np.array_equal(u, qc + 8 if sym else qc), (seed, row, j)
+                if not sym:
+                    assert int(zz[row, j]) == zc, (seed, row, j)
+                picked_clip += i > 0
+        assert picked_clip > 0, "no group chose a clipped range"
+    # a Gaussian group: a clipped range strictly lowers the error below plain RTN's
+    w = np.random.default_rng(45).standard_normal((1, 128)).astype(np.float32)
+    _, _, _, ch = o.quantize_pack_mse(w, 128, False, with_choice=True)
+    c = mse_candidates_numpy(w[0], False)
+    assert int(ch[0, 0]) > 0 and c[int(ch[0, 0])][0] < c[0][0] * (1 - 1e-6)
+
+
+def check_mse_rtn_limit(o):
+    """alpha = 1 is plain RTN: wherever the search keeps it, the bits equal the RTN
+    quantizer's (itself pinned by the hand-worked groups)."""
+    for g, sym in [(32, False), (128, True), (64, False)]:
+        w = random_weights(50 + g, 12, 512)
+        qm, sm, zm, ch = o.quantize_pack_mse(w, g, sym, with_choice=True)
+        qr, sr, zr = o.quantize_pack(w, g, sym)
+        G = 512 // g
+        keep = ch == 0
+        assert keep.any()
+        assert np.array_equal(sm[keep], sr[keep])
+        cm, cr = unpack_codes(qm, 512), unpack_codes(qr, 512)
+        for row, j in zip(*np.nonzero(keep)):
+            assert np.array_equal(cm[row, j * g:(j + 1) * g], cr[row, j * g:(j + 1) * g])
+        if not sym:
+            assert np.array_equal(unpack_zeros(zm, G)[keep], unpack_zeros(zr, G)[keep])
+
+
 ALL_CHECKS = [check_golden_groups, check_fp16_conversion, check_invariants,
               check_brute_force_nearest, check_levels_and_bytes, check_dequant_closed_forms,
-              check_linear, check_argument_rejection]
+              check_linear, check_argument_rejection, check_mse_brute_force,
+              check_mse_rtn_limit]

@@ -39,6 +39,16 @@ MUTANTS = [
     ("bf16_widening_shift", "uint32_t bits = (uint32_t)b << 16;",
      "uint32_t bits = (uint32_t)b << 15;"),
     ("zero_rows_padding", "return n * ((k / g + 7) / 8);", "return n * ((k / g) / 8);"),
+    ("mse_ties_keep_later", "if (i == 0 || e < best_err) {", "if (i == 0 || e <= best_err) {"),
+    ("mse_grid_step", "const float alpha = (float)(20 - i) / 20.0f;",
+     "const float alpha = (float)(20 - i) / 21.0f;"),
+    ("mse_error_drops_zero_point", "const double xhat = (double)S * (double)(q - z);",
+     "const double xhat = (double)S * (double)q;"),
+    ("mse_clips_low_end_only", "const float hi = alpha * x_max;", "const float hi = x_max;"),
+    ("mse_picks_largest_error", "if (i == 0 || e < best_err) {", "if (i == 0 || e > best_err) {"),
+    ("mse_zero_point_unclipped", "if (!symmetric) z = (int)clampf(rintf(-lo / S), q_min, q_max);",
+     "if (!symmetric) z = (int)clampf(rintf(-lo / S) + 1.0f, q_min, q_max);"),
+    ("mse_sym_range_unscaled", "s = (alpha * amax) / 7.0f;", "s = amax / 7.0f;"),
 ]
 
 
