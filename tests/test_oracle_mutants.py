@@ -13,24 +13,28 @@ import oracle
 import pins
 
 MUTANTS = [
-    ("add_then_round", "rintf(v[t] / S) + (float)z", "rintf(v[t] / S + (float)z)"),
-    ("quantize_with_fp32_scale", "rintf(v[t] / S) + (float)z", "rintf(v[t] / s) + (float)z"),
-    ("no_zero_extension", "float x_min = 0.0f, x_max = 0.0f;",
+    ("add_then_round", "float qf = clampf(rintf(v[t] / S) + (float)z,",
+     "float qf = clampf(rintf(v[t] / S + (float)z),"),
+    ("quantize_with_fp32_scale", "float qf = clampf(rintf(v[t] / S) + (float)z,",
+     "float qf = clampf(rintf(v[t] / s) + (float)z,"),
+    ("no_zero_extension", "float x_min = 0.0f, x_max = 0.0f; /* zero-extended range (R5) */",
      "float x_min = v[0], x_max = v[0];"),
     ("sym_divides_by_8", "s = amax / 7.0f;", "s = amax / 8.0f;"),
-    ("sym_uses_signed_max", "amax = fmaxf(amax, fabsf(v[t]));", "amax = fmaxf(amax, v[t]);"),
+    ("sym_uses_signed_max", "amax = fmaxf(amax, fabsf(v[t]));\n                s = amax / 7.0f;",
+     "amax = fmaxf(amax, v[t]);\n                s = amax / 7.0f;"),
     ("asym_divides_by_16", "s = (x_max - x_min) / 15.0f;", "s = (x_max - x_min) / 16.0f;"),
-    ("nibbles_reversed", "|= u << (4 * (col % 8));", "|= u << (4 * (7 - col % 8));"),
+    ("nibbles_reversed", "                int64_t col = j * g + t;\n                qweight[row * (k / 8) + col / 8] |= u << (4 * (col % 8));",
+     "                int64_t col = j * g + t;\n                qweight[row * (k / 8) + col / 8] |= u << (4 * (7 - col % 8));"),
     ("zero_point_sign", "rintf(-x_min / S)", "rintf(x_min / S)"),
-    ("zero_word_index", "zeros[row * zw + j / 8] |= (uint32_t)z << (4 * (j % 8));",
-     "zeros[row * zw + j / 8] |= (uint32_t)z << (4 * (j / 8));"),
+    ("zero_word_index", "zeros[row * zw + j / 8] |= (uint32_t)z << (4 * (j % 8));\n                if (onesided)",
+     "zeros[row * zw + j / 8] |= (uint32_t)z << (4 * (j / 8));\n                if (onesided)"),
     ("fp16_truncates", "if (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) h += 1u;", ""),
     ("fp16_ties_away", "(rem == 0x1000u && (h & 1u))", "(rem == 0x1000u)"),
     ("fp16_subnormal_exponent", "mag = ldexpf((float)m, -24);", "mag = ldexpf((float)m, -25);"),
     ("degenerate_scale_zero", "s16 = 0x3C00u;  /* 1.0 */", "s16 = 0x0000u;"),
     ("sym_stores_twos_complement", "symmetric ? q + 8 : q", "symmetric ? (q & 15) : q"),
-    ("asym_range_0_14", "const float q_max = symmetric ? 7.0f : 15.0f;",
-     "const float q_max = symmetric ? 7.0f : 14.0f;"),
+    ("asym_range_0_14", "const float q_max = symmetric ? 7.0f : 15.0f;\n\n    memset",
+     "const float q_max = symmetric ? 7.0f : 14.0f;\n\n    memset"),
     ("dequant_drops_zero", "return S * ((double)u - (double)z);", "return S * (double)u;"),
     ("dequant_group_index", "const int64_t j = col / g;", "const int64_t j = col / 8;"),
     ("linear_drops_first_term", "acc += xv * wrow[kk];", "if (kk) acc += xv * wrow[kk];"),
