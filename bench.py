@@ -142,7 +142,7 @@ def main():
     ap.add_argument("--steps", type=int, default=340)
     ap.add_argument("--warmup", type=int, default=34)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--legs", default="gemm,quant,sweep,mlp",
+    ap.add_argument("--legs", default="gemm,quant,sweep,mlp,mse",
                     help="comma list of legs besides the headline decode GEMV")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy 5 times (the "
@@ -261,6 +261,30 @@ def main():
                        "tflops": round(flops / t / 1e12, 2),
                        "frac_mfma_bf16": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4)}
         del pw, xg, yg
+
+    # ------------------------------------------------------------ MSE clip search (quantize)
+    if "mse" in legs:
+        res = {}
+        for mat in cfg["mats"]:
+            w = mat.make().to(dev)
+            wf = w.float()
+            for sym in (False, True):
+                pm = q4.q4_quantize_pack_mse(w, 128, sym)
+                kname = q4.q4_last_kernel()
+                pr = q4.q4_quantize_pack(w, 128, sym)
+                torch.cuda.synchronize()
+                t = graph_ms(capture([lambda: q4.q4_quantize_pack_mse(w, 128, sym, out=pm)] * 3), 3) / 3 * 1e-3
+                e_m = (q4.q4_dequant(pm) - wf).double().pow(2).sum().item()
+                e_r = (q4.q4_dequant(pr) - wf).double().pow(2).sum().item()
+                qb = quant_bytes(mat.n, mat.k, 128, sym)
+                res[f"{mat.n}x{mat.k} {'sym' if sym else 'asym'}"] = {
+                    "kernel": kname, "us": round(t * 1e6, 1), "gbs": round(qb / t / 1e9, 1),
+                    "gweights_per_s": round(mat.n * mat.k / t / 1e9, 1),
+                    "sq_error_vs_rtn": round(e_m / e_r, 4)}
+                del pm, pr
+            del w, wf
+        out["mse_clip"] = {"workload": "7B-like decode matrices, bf16, g128, clip ratios (20-i)/20, "
+                                       "i = 0..10, per group", "bound": "alu", "results": res}
 
     # ------------------------------------------------------------ MLP batch sweep (GEMV, m <= 16)
     if "mlp" in legs:

@@ -69,6 +69,26 @@ q4_status q4_quantize_pack(const void* w, q4_dtype w_dtype, int64_t n, int64_t k
                            uint32_t* qweight, uint16_t* scales, uint32_t* zeros,
                            hipStream_t stream);
 
+/* Quantize-and-pack with the clipping threshold chosen per group to minimize the
+ * reconstruction error ([FL7] §Clipping Trade-off: a clipped range trades a larger error
+ * on the few outliers for a finer grid on the rest; the MSE-optimal criterion
+ * argmin ||x - x_dq||^2 of [QA1] §MSE-optimal).  Each group tries the clip ratios
+ * alpha_i = (20 - i) / 20, i = 0..10, in that order: the q4_quantize_pack computation with
+ * the range scaled by alpha (asymmetric [alpha*min(x_min,0), alpha*max(x_max,0)], the zero
+ * point from -alpha*min(x_min,0) / S; symmetric alpha*max|x|), weights outside the
+ * clipped range saturating at the end codes.  A candidate's error is the sum of
+ * (x - S(q - z))^2 in IEEE fp64, each group's 8 chunks of g/8 consecutive weights summed
+ * in order and then added pairwise ((c0+c1)+(c2+c3))+((c4+c5)+(c6+c7)); the first smallest
+ * error wins, so alpha = 1 (the q4_quantize_pack result) is kept unless clipping strictly
+ * lowers the error.  Output is the same packed format, bit-identical to the CPU
+ * definition.  Arguments, limits and errors as for q4_quantize_pack.  The search costs
+ * about a dozen fp32/fp64 operations per weight and candidate: it is bound by ALU
+ * throughput, not memory. */
+q4_status q4_quantize_pack_mse(const void* w, q4_dtype w_dtype, int64_t n, int64_t k,
+                               int32_t group_size, int32_t symmetric,
+                               uint32_t* qweight, uint16_t* scales, uint32_t* zeros,
+                               hipStream_t stream);
+
 /* One matrix of a grouped quantize/pack call. */
 typedef struct {
     const void* w;        /* [n][k] weights, in the dtype of the call */

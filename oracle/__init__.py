@@ -192,6 +192,10 @@ def quantize_pack(*a, **kw):
     return default().quantize_pack(*a, **kw)
 
 
+def quantize_pack_mse(*a, **kw):
+    return default().quantize_pack_mse(*a, **kw)
+
+
 def dequant(*a, **kw):
     return default().dequant(*a, **kw)
 

@@ -178,3 +178,17 @@ def test_quantize_row_length_limit():
     lib = q4.lib()
     assert lib.q4_quantize_pack(A16, F32, 1, (1 << 28) + 128, 128, 0, A16, A16, A16, None) == SHAPE
     assert _qgrouped([_qprob(zr=None), _qprob(zr=None)], g=16, sym=1) == GROUP
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, BF16, 4, 128, 128, 0, A16, A16, A16, None), NULL),
+    ((A16, BF16, 4, 100, 32, 0, A16, A16, A16, None), SHAPE),
+    ((A16, BF16, 4, 128, 16, 0, A16, A16, A16, None), GROUP),
+    ((A16, 9, 4, 128, 128, 0, A16, A16, A16, None), DTYPE),
+    ((A16, BF16, 4, 128, 128, 0, A16, A16, None, None), NULL),
+    ((A16 + 4, BF16, 4, 128, 128, 0, A16, A16, A16, None), ALIGN),
+    ((A16, F32, 1, (1 << 28) + 128, 128, 1, A16, A16, None, None), SHAPE),
+])
+def test_quantize_mse_validation_rejects_before_launch(args, code):
+    assert q4.lib().q4_quantize_pack_mse(*args) == code
+    assert q4.q4_last_kernel() == ""

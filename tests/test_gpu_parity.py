@@ -199,6 +199,60 @@ def test_quant_grouped(g, dtype, sym):
         assert_pack_exact(p, host_input(w), g, sym)
 
 
+MSE_SHAPES = [(12, 256, 32), (12, 512, 64), (12, 1024, 128), (1, 32, 32), (5, 4096 + 64, 64),
+              (33, 11008, 128)]
+
+
+@pytest.mark.parametrize("n,k,g", MSE_SHAPES)
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("sym", [False, True])
+def test_quant_mse(n, k, g, dtype, sym):
+    """The clip search on the GPU picks the same ratio per group as the oracle, so codes,
+    scales and zero points are bit-identical; the stress rows cover degenerate, one-sided,
+    saturated and subnormal-scale groups."""
+    w = torch.from_numpy(pins.random_weights(900 + n + k + g, max(n, 12), k)[:n]).to(dtype)
+    if dtype == torch.float16:
+        w = torch.nan_to_num(w, posinf=60000.0, neginf=-60000.0)
+    note(f"quant mse n={n} k={k} g={g} {dtype} sym={sym}")
+    G = k // g
+    qb, qv = guarded((n, k // 8), torch.int32, SENTINEL_I32)
+    sb, sv = guarded((n, G), torch.int16, -1)
+    zb, zv = (None, None) if sym else guarded((n, (G + 7) // 8), torch.int32, SENTINEL_I32)
+    p = q4.PackedWeight(qweight=qv, scales=sv.view(torch.float16), zeros=zv, n=n, k=k,
+                        group_size=g, symmetric=sym)
+    q4.q4_quantize_pack_mse(w.to(DEV), g, sym, out=p)
+    torch.cuda.synchronize()
+    assert q4.q4_last_kernel() == {torch.float32: "q4_quant_mse_f32", torch.float16: "q4_quant_mse_f16",
+                                   torch.bfloat16: "q4_quant_mse_bf16"}[dtype]
+    check_guards((qb, sb, zb), sym)
+    qo, so, zo = oracle.quantize_pack_mse(host_input(w), g, sym)
+    assert np.array_equal(p.qweight.cpu().numpy().view(np.uint32), qo)
+    assert np.array_equal(p.scales.cpu().numpy().view(np.uint16), so)
+    if not sym:
+        assert np.array_equal(p.zeros.cpu().numpy().view(np.uint32), zo)
+
+
+def test_quant_mse_decode_7b_sampled():
+    """The 4096x4096 decode matrix at full size (bf16, g128 asym): a seeded sample of 64
+    rows against the oracle, and the whole matrix's squared error below RTN's."""
+    mat = synthetic.DECODE_7B["mats"][0]
+    w = mat.make()
+    note("quant mse decode 4096x4096 g128 asym")
+    p = q4.q4_quantize_pack_mse(w.to(DEV), 128, False)
+    r = q4.q4_quantize_pack(w.to(DEV), 128, False)
+    torch.cuda.synchronize()
+    rows_t = synthetic.sample_rows(mat.n, 64, seed=17)
+    rows = rows_t.numpy()
+    qo, so, zo = oracle.quantize_pack_mse(host_input(w[rows_t].contiguous()), 128, False)
+    assert np.array_equal(p.qweight.cpu().numpy().view(np.uint32)[rows], qo)
+    assert np.array_equal(p.scales.cpu().numpy().view(np.uint16)[rows], so)
+    assert np.array_equal(p.zeros.cpu().numpy().view(np.uint32)[rows], zo)
+    wf = w.float().to(DEV)
+    e_mse = (q4.q4_dequant(p) - wf).double().pow(2).sum().item()
+    e_rtn = (q4.q4_dequant(r) - wf).double().pow(2).sum().item()
+    assert e_mse < e_rtn
+
+
 # ----------------------------------------------------------------------------- dequant
 
 @pytest.mark.parametrize("g,sym", [(32, False), (64, True), (128, False), (128, True)])

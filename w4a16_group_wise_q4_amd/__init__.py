@@ -23,7 +23,8 @@ import torch
 
 from . import _build
 
-__all__ = ["PackedWeight", "q4_quantize_pack", "q4_quantize_pack_grouped", "q4_dequant",
+__all__ = ["PackedWeight", "q4_quantize_pack", "q4_quantize_pack_grouped", "q4_quantize_pack_mse",
+           "q4_dequant",
            "q4_w4a16_gemm",
            "q4_w4a16_gemm_grouped", "q4_last_kernel",
            "q4_qweight_words", "q4_scale_count", "q4_zero_words", "q4_layout_version",
@@ -32,7 +33,8 @@ __all__ = ["PackedWeight", "q4_quantize_pack", "q4_quantize_pack_grouped", "q4_d
 Q4_F32, Q4_F16, Q4_BF16 = 0, 1, 2
 _DTYPE_CODE = {torch.float32: Q4_F32, torch.float16: Q4_F16, torch.bfloat16: Q4_BF16}
 
-EXPORTED = ("q4_quantize_pack", "q4_quantize_pack_grouped", "q4_dequant", "q4_w4a16_gemm",
+EXPORTED = ("q4_quantize_pack", "q4_quantize_pack_grouped", "q4_quantize_pack_mse", "q4_dequant",
+            "q4_w4a16_gemm",
             "q4_w4a16_gemm_grouped",
             "q4_qweight_words",
             "q4_scale_count", "q4_zero_words", "q4_status_str", "q4_last_kernel",
@@ -79,6 +81,8 @@ def _load():
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     lib.q4_quantize_pack.argtypes = [vp, ctypes.c_int, i64, i64, i32, i32, vp, vp, vp, vp]
     lib.q4_quantize_pack.restype = ctypes.c_int
+    lib.q4_quantize_pack_mse.argtypes = [vp, ctypes.c_int, i64, i64, i32, i32, vp, vp, vp, vp]
+    lib.q4_quantize_pack_mse.restype = ctypes.c_int
     lib.q4_quantize_pack_grouped.argtypes = [ctypes.POINTER(QuantProblem), i32, ctypes.c_int, i32,
                                              i32, vp]
     lib.q4_quantize_pack_grouped.restype = ctypes.c_int
@@ -183,6 +187,21 @@ def q4_quantize_pack(w: torch.Tensor, group_size: int = 128, symmetric: bool = F
     _check(_load().q4_quantize_pack(_dev_ptr(w), _DTYPE_CODE[w.dtype], n, k, group_size,
                                     int(bool(symmetric)), _dev_ptr(p.qweight),
                                     _dev_ptr(p.scales), _dev_ptr(p.zeros), _stream(w)))
+    return p
+
+
+def q4_quantize_pack_mse(w: torch.Tensor, group_size: int = 128, symmetric: bool = False,
+                         out: Optional[PackedWeight] = None) -> PackedWeight:
+    """Quantize-and-pack W [n, k] with the per-group clipping ratio that minimizes the
+    squared reconstruction error (ratios (20 - i)/20, i = 0..10); same packed format."""
+    _need_cuda("w", w)
+    if w.dim() != 2 or w.dtype not in _DTYPE_CODE:
+        raise ValueError("w must be a 2-D fp32, fp16 or bf16 tensor")
+    n, k = w.shape
+    p = out if out is not None else empty_packed(n, k, group_size, symmetric, w.device)
+    _check(_load().q4_quantize_pack_mse(_dev_ptr(w), _DTYPE_CODE[w.dtype], n, k, group_size,
+                                        int(bool(symmetric)), _dev_ptr(p.qweight),
+                                        _dev_ptr(p.scales), _dev_ptr(p.zeros), _stream(w)))
     return p
 
 

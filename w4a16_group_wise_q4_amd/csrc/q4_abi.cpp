@@ -83,6 +83,17 @@ q4_status q4_quantize_pack(const void* w, q4_dtype w_dtype, int64_t n, int64_t k
     return finish(e, name);
 }
 
+q4_status q4_quantize_pack_mse(const void* w, q4_dtype w_dtype, int64_t n, int64_t k,
+                               int32_t group_size, int32_t symmetric, uint32_t* qweight,
+                               uint16_t* scales, uint32_t* zeros, hipStream_t stream) {
+    q4_status st = check_quant(w, w_dtype, n, k, group_size, symmetric, qweight, scales, zeros);
+    if (st != Q4_OK) return st;
+    const char* name = "";
+    hipError_t e = q4k_quant_mse(w, (int)w_dtype, n, k, group_size, symmetric ? 1 : 0, qweight,
+                                 scales, zeros, stream, &name);
+    return finish(e, name);
+}
+
 q4_status q4_quantize_pack_grouped(const q4_quant_problem* problems, int32_t count,
                                    q4_dtype w_dtype, int32_t group_size, int32_t symmetric,
                                    hipStream_t stream) {

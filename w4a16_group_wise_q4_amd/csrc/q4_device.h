@@ -125,6 +125,9 @@ __device__ __forceinline__ uint32_t buf_load_u16(rsrc r, int voff, int soff) {
 hipError_t q4k_quant_pack(const void* w, int w_dtype, int64_t n, int64_t k, int g, int sym,
                           uint32_t* qweight, uint16_t* scales, uint32_t* zeros,
                           hipStream_t stream, const char** kname);
+hipError_t q4k_quant_mse(const void* w, int w_dtype, int64_t n, int64_t k, int g, int sym,
+                         uint32_t* qweight, uint16_t* scales, uint32_t* zeros,
+                         hipStream_t stream, const char** kname);
 hipError_t q4k_dequant(const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros,
                        int64_t n, int64_t k, int g, int sym, void* out, int out_dtype,
                        hipStream_t stream, const char** kname);
