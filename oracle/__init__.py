@@ -81,6 +81,12 @@ class Oracle:
         lib.orc_linear_f64.argtypes = [vp, c_int, c_i64, vp, c_i64, vp, vp, vp,
                                        c_i64, c_i64, c_i64, c_int, vp, c_i64, vp, vp]
         lib.orc_linear_f64.restype = c_int
+        lib.orc_kv_quantize.argtypes = [vp, c_int, c_i64, c_i64, c_i64, c_i64, c_int, c_i64, c_i64,
+                                        vp, vp, vp]
+        lib.orc_kv_quantize.restype = c_int
+        lib.orc_kv_attention_f64.argtypes = [vp, c_int, c_i64, c_i64, c_i64, c_i64, vp, vp, vp,
+                                             vp, vp, vp, c_i64, c_int, ctypes.c_double, vp, vp, vp]
+        lib.orc_kv_attention_f64.restype = c_int
         lib.orc_qweight_words.argtypes = [c_i64, c_i64]
         lib.orc_qweight_words.restype = c_i64
         lib.orc_scale_count.argtypes = [c_i64, c_i64, c_i64]
@@ -170,6 +176,47 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle linear rejected the arguments")
         return y, yabs
+
+    # ------------------------------------------------------------ KV cache
+    def kv_cache(self, heads: int, t_cap: int, d: int, group_size: int):
+        """An empty head-major cache (qcache, scache, zcache) of heads * t_cap rows."""
+        return (np.zeros((heads * t_cap, d // 8), dtype=np.uint32),
+                np.zeros((heads * t_cap, d // group_size), dtype=np.uint16),
+                np.zeros((heads * t_cap, (d // group_size + 7) // 8), dtype=np.uint32))
+
+    def kv_quantize(self, kv, group_size: int, symmetric: bool, cache, t0: int):
+        """Quantize kv [t_new, heads, d] (an input as ``quantize_pack`` takes) into rows h * t_cap + t0 + t of ``cache`` (the
+        arrays of ``kv_cache``), in place."""
+        arr, code = _as_input(kv)
+        t_new, heads, d = arr.shape
+        qc, sc, zc = cache
+        t_cap = qc.shape[0] // heads
+        rc = self.lib.orc_kv_quantize(_ptr(arr), code, t_new, heads, d, group_size,
+                                      int(bool(symmetric)), t_cap, t0, _ptr(qc), _ptr(sc),
+                                      _ptr(zc))
+        if rc != 0:
+            raise ValueError("oracle kv_quantize rejected the arguments")
+        return cache
+
+    def kv_attention(self, q, kcache, vcache, n_tok: int, group_size: int, symmetric: bool,
+                     scale: float):
+        """(out [heads, d], score_abs [heads], v_abs [heads, d]) in float64 for queries
+        q [heads, d] over the first n_tok tokens of the head-major caches."""
+        qa, code = _as_input(q)
+        heads, d = qa.shape
+        kq, ks, kz = (np.ascontiguousarray(a) for a in kcache)
+        vq, vs, vz = (np.ascontiguousarray(a) for a in vcache)
+        t_cap = kq.shape[0] // heads
+        out = np.zeros((heads, d), dtype=np.float64)
+        sabs = np.zeros(heads, dtype=np.float64)
+        vabs = np.zeros((heads, d), dtype=np.float64)
+        rc = self.lib.orc_kv_attention_f64(_ptr(qa), code, heads, d, n_tok, t_cap, _ptr(kq),
+                                           _ptr(ks), _ptr(kz), _ptr(vq), _ptr(vs), _ptr(vz),
+                                           group_size, int(bool(symmetric)), float(scale),
+                                           _ptr(out), _ptr(sabs), _ptr(vabs))
+        if rc != 0:
+            raise ValueError("oracle kv_attention rejected the arguments")
+        return out, sabs, vabs
 
     def sizes(self, n: int, k: int, group_size: int) -> Tuple[int, int, int]:
         """Element counts of (qweight words, scales, zero words)."""

@@ -346,3 +346,87 @@ int orc_linear_f64(const void* x, int x_dtype, int64_t m, const int64_t* rows, i
     free(wrow);
     return 0;
 }
+
+/* ---------------------------------------------------------------- KV cache */
+
+/* [QA1] KV-cache chapter, §INT4 group scheme and §asym 선택 이유: the K (or V) row of one
+ * token and one head, d values, is quantized in groups of g consecutive head dimensions,
+ * each group with its own scale and zero point, recomputed for every token as it arrives
+ * (per-token scales, §Per-token scale 수식).  The group quantizer is the RTN of
+ * orc_quantize_pack.  Reading K1: one layer's cache is head-major, token t of head h in row
+ * h * t_cap + t of the packed layout with k = d. */
+int orc_kv_quantize(const void* kv, int dtype, int64_t t_new, int64_t heads, int64_t d, int64_t g,
+                    int symmetric, int64_t t_cap, int64_t t0, uint32_t* qcache,
+                    uint16_t* scache, uint32_t* zcache) {
+    if (t_new < 0 || heads < 1 || d < 1 || g < 1 || d % g != 0 || d % 8 != 0) return -1;
+    if (t0 < 0 || t0 + t_new > t_cap) return -1;
+    const int64_t G = d / g;
+    const int64_t zw = (G + 7) / 8;
+    const size_t esize = dtype == ORC_F32 ? 4 : 2;
+    for (int64_t t = 0; t < t_new; ++t) {
+        for (int64_t h = 0; h < heads; ++h) {
+            const char* src = (const char*)kv + (size_t)((t * heads + h) * d) * esize;
+            const int64_t r = h * t_cap + t0 + t;
+            const int rc = orc_quantize_pack(src, dtype, 1, d, g, symmetric, qcache + r * (d / 8),
+                                             scache + r * G, symmetric ? NULL : zcache + r * zw,
+                                             NULL);
+            if (rc != 0) return rc;
+        }
+    }
+    return 0;
+}
+
+/* Decode attention over the quantized cache, in fp64 ([QA1] KV-cache chapter, §Attention에서의
+ * 결합: the dequantized K and V enter the attention matmuls).  For each head h, with the
+ * cached tokens t = 0 .. n_tok-1 dequantized as in orc_dequant_f64 (x_hat = S (u - z)):
+ *   s_t = scale * sum_i q[h][i] K_hat[h][t][i]
+ *   out[h][i] = sum_t exp(s_t - M) V_hat[h][t][i] / sum_t exp(s_t - M),  M = max_t s_t
+ * (softmax; subtracting M changes nothing mathematically and keeps exp in range).
+ * score_abs[h] (may be NULL) = max_t |scale| sum_i |q[h][i]| |K_hat[h][t][i]| and
+ * v_abs[h][i] (may be NULL) = max_t |V_hat[h][t][i]|: the tolerance references. */
+int orc_kv_attention_f64(const void* q, int q_dtype, int64_t heads, int64_t d, int64_t n_tok,
+                         int64_t t_cap, const uint32_t* kq, const uint16_t* ks, const uint32_t* kz,
+                         const uint32_t* vq, const uint16_t* vs, const uint32_t* vz, int64_t g,
+                         int symmetric, double scale, double* out, double* score_abs,
+                         double* v_abs) {
+    if (heads < 1 || d < 1 || n_tok < 1 || n_tok > t_cap || g < 1 || d % g != 0 || d % 8 != 0)
+        return -1;
+    double* s = (double*)malloc((size_t)n_tok * sizeof(double));
+    double* qh = (double*)malloc((size_t)d * sizeof(double));
+    if (!s || !qh) { free(s); free(qh); return -1; }
+    for (int64_t h = 0; h < heads; ++h) {
+        for (int64_t i = 0; i < d; ++i) qh[i] = (double)load_elem(q, q_dtype, h * d + i);
+        double M = -HUGE_VAL, sabs_max = 0.0;
+        for (int64_t t = 0; t < n_tok; ++t) {
+            const int64_t r = h * t_cap + t;
+            double acc = 0.0, aabs = 0.0;
+            for (int64_t i = 0; i < d; ++i) {
+                const double kh = xhat_elem(kq, ks, kz, r, i, d, g, symmetric);
+                acc += qh[i] * kh;
+                aabs += fabs(qh[i]) * fabs(kh);
+            }
+            s[t] = scale * acc;
+            if (s[t] > M) M = s[t];
+            if (fabs(scale) * aabs > sabs_max) sabs_max = fabs(scale) * aabs;
+        }
+        double l = 0.0;
+        for (int64_t t = 0; t < n_tok; ++t) {
+            s[t] = exp(s[t] - M);  /* now the unnormalized probability */
+            l += s[t];
+        }
+        for (int64_t i = 0; i < d; ++i) {
+            double acc = 0.0, vmax = 0.0;
+            for (int64_t t = 0; t < n_tok; ++t) {
+                const double vh = xhat_elem(vq, vs, vz, h * t_cap + t, i, d, g, symmetric);
+                acc += s[t] * vh;
+                if (fabs(vh) > vmax) vmax = fabs(vh);
+            }
+            out[h * d + i] = acc / l;
+            if (v_abs) v_abs[h * d + i] = vmax;
+        }
+        if (score_abs) score_abs[h] = sabs_max;
+    }
+    free(s);
+    free(qh);
+    return 0;
+}

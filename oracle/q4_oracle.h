@@ -12,7 +12,9 @@
  *          §Group Scale Overhead 예, §어떤 Tensor를 Quantize하는가 / Weight-only,
  *          §Kernel이 없으면 압축 이점이 사라진다 (path A fused / path B full dequant).
  *   [QA1]  "Quantization Algorithms 단권화", brianyu43.github.io (V10)
- *          §Uniform Symmetric, §Signed ↔ Unsigned (INT4 ranges), §Calibration-free (RTN).
+ *          §Uniform Symmetric, §Signed ↔ Unsigned (INT4 ranges), §Calibration-free (RTN),
+ *          §MSE-optimal; KV-cache chapter: §KV cache의 bandwidth 부담, §Per-token scale 수식,
+ *          §asym 선택 이유, §Attention에서의 결합, §INT4 group scheme.
  *
  * Parity status: every function here is pinned by tests (hand-worked groups, closed
  * forms, invariants, brute force, an independent fp16 converter); none is
@@ -74,6 +76,26 @@ int orc_linear_f64(const void* x, int x_dtype, int64_t m, const int64_t* rows, i
                    const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros,
                    int64_t n, int64_t k, int64_t g, int symmetric,
                    const int64_t* cols, int64_t n_cols, double* y, double* yabs);
+
+/* KV cache ([QA1] KV-cache chapter, §INT4 group scheme): kv [t_new][heads][d] (new tokens)
+ * quantized per (token, head) in groups of g along d, as orc_quantize_pack does for one row,
+ * into rows h * t_cap + t0 + t of a head-major cache in the packed layout with k = d
+ * (qcache [heads*t_cap][d/8], scache [heads*t_cap][d/g], zcache [heads*t_cap][ceil(d/g/8)],
+ * zcache untouched and may be NULL when symmetric).  Other rows are left as they are.
+ * Returns 0, or -1 on bad arguments (t0 + t_new > t_cap, d % g != 0, ...). */
+int orc_kv_quantize(const void* kv, int dtype, int64_t t_new, int64_t heads, int64_t d, int64_t g,
+                    int symmetric, int64_t t_cap, int64_t t0, uint32_t* qcache,
+                    uint16_t* scache, uint32_t* zcache);
+
+/* Decode attention over the first n_tok tokens of that cache, fp64:
+ * out[h][i] = sum_t softmax_t(scale * q[h] . K_hat[h][t]) V_hat[h][t][i], q [heads][d] in
+ * q_dtype.  score_abs[heads] = max_t |scale| sum_i |q_i K_hat_ti| and v_abs[heads][d] =
+ * max_t |V_hat_ti| (both may be NULL) are the tolerance references. */
+int orc_kv_attention_f64(const void* q, int q_dtype, int64_t heads, int64_t d, int64_t n_tok,
+                         int64_t t_cap, const uint32_t* kq, const uint16_t* ks, const uint32_t* kz,
+                         const uint32_t* vq, const uint16_t* vs, const uint32_t* vz, int64_t g,
+                         int symmetric, double scale, double* out, double* score_abs,
+                         double* v_abs);
 
 /* Sizes of the three arrays, in elements of their own type. */
 int64_t orc_qweight_words(int64_t n, int64_t k);

@@ -16,7 +16,13 @@ What pins what:
   * byte accounting from the pages' arithmetic (payload P*b/8, fp16 scale per 128 weights
     = 0.015625 B/weight, 32 four-bit codes + one fp16 scale = 4.5 bits/weight);
   * the fp64 matmul against numpy's float64 matmul of the dequantized weights, one-hot
-    and zero activations, integer data with unit scales.
+    and zero activations, integer data with unit scales;
+  * the KV cache ("Quantization Algorithms 단권화", KV-cache chapter, §INT4 group scheme):
+    cache rows against the weight quantizer applied to each (token, head) row, appends in
+    steps against one append, untouched rows; attention against the special cases
+    softmax reduces to (one token: that token's value; zero query: the mean; two tokens:
+    the logistic form; a huge scale: the top-scoring token's value), token-order
+    invariance and a brute-force loop with Python's math.exp.
 """
 from __future__ import annotations
 
@@ -433,7 +439,109 @@ def check_mse_rtn_limit(o):
             assert np.array_equal(unpack_zeros(zm, G)[keep], unpack_zeros(zr, G)[keep])
 
 
+# --------------------------------------------------------------------------- KV cache
+
+def _kv_fill(o, seed, heads, t_cap, d, g, sym, n_tok):
+    """Random K and V for n_tok tokens quantized into fresh head-major caches."""
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((n_tok, heads, d)).astype(np.float32)
+    v = (rng.standard_normal((n_tok, heads, d)) * 0.5 + 0.25).astype(np.float32)
+    kc, vc = o.kv_cache(heads, t_cap, d, g), o.kv_cache(heads, t_cap, d, g)
+    o.kv_quantize(k, g, sym, kc, 0)
+    o.kv_quantize(v, g, sym, vc, 0)
+    return k, v, kc, vc
+
+
+def _kv_hat(o, cache, heads, d, g, sym):
+    qc, sc, zc = cache
+    rows = qc.shape[0]
+    return o.dequant(qc, sc, zc, rows, d, g, sym).reshape(heads, rows // heads, d)
+
+
+def check_kv_cache_placement(o):
+    heads, t_cap, d, g = 3, 10, 128, 32
+    kv = random_weights(31, 7 * heads, d).reshape(7, heads, d)
+    for sym in (False, True):
+        cache = o.kv_cache(heads, t_cap, d, g)
+        cache[0][:], cache[1][:], cache[2][:] = 0xDEADBEEF, 0x1234, 0xCAFEF00D
+        o.kv_quantize(kv[:5], g, sym, cache, 2)      # a prefill of 5 tokens at positions 2..6
+        o.kv_quantize(kv[5:6], g, sym, cache, 7)     # then one decode token at position 7
+        rq, rs, rz = o.quantize_pack(kv[:6].reshape(6 * heads, d), g, sym)
+        qc, sc, zc = cache
+        for t in range(6):
+            for h in range(heads):
+                r, src = h * t_cap + 2 + t, t * heads + h
+                assert np.array_equal(qc[r], rq[src]) and np.array_equal(sc[r], rs[src])
+                if not sym:
+                    assert np.array_equal(zc[r], rz[src])
+        for h in range(heads):
+            for t in (0, 1, 8, 9):                   # rows never written
+                r = h * t_cap + t
+                assert np.all(qc[r] == 0xDEADBEEF) and np.all(sc[r] == 0x1234)
+        if sym:
+            assert np.all(zc == 0xCAFEF00D)          # symmetric caches have no zero points
+        # writing past the cache's capacity is refused
+        try:
+            o.kv_quantize(kv[:4], g, sym, cache, 7)
+        except ValueError:
+            pass
+        else:
+            raise AssertionError("t0 + t_new > t_cap accepted")
+
+
+def check_kv_attention(o):
+    import math
+    heads, t_cap, d, g = 4, 24, 64, 32
+    rng = np.random.default_rng(41)
+    for sym in (False, True):
+        _, _, kc, vc = _kv_fill(o, 43 + sym, heads, t_cap, d, g, sym, t_cap)
+        kh, vh = _kv_hat(o, kc, heads, d, g, sym), _kv_hat(o, vc, heads, d, g, sym)
+        q = rng.standard_normal((heads, d)).astype(np.float32)
+        q64 = q.astype(np.float64)
+        scores = (kh @ q64[:, :, None])[..., 0]      # [heads, t_cap], unscaled
+        # one token: its softmax weight is exactly 1
+        out, _, _ = o.kv_attention(q, kc, vc, 1, g, sym, 0.125)
+        assert np.array_equal(out, vh[:, 0])
+        # zero query: equal weights, the mean of the cached values
+        out, _, _ = o.kv_attention(np.zeros_like(q), kc, vc, 17, g, sym, 0.125)
+        assert np.allclose(out, vh[:, :17].mean(axis=1), rtol=1e-13, atol=1e-15)
+        # two tokens: o = v1 + (v0 - v1) / (1 + e^(s1 - s0))
+        out, _, _ = o.kv_attention(q, kc, vc, 2, g, sym, 0.125)
+        s = 0.125 * scores[:, :2]
+        ref = vh[:, 1] + (vh[:, 0] - vh[:, 1]) / (1.0 + np.exp(s[:, 1] - s[:, 0]))[:, None]
+        assert np.allclose(out, ref, rtol=1e-12, atol=1e-13)
+        # a huge scale leaves the top-scoring token alone (every other weight underflows)
+        n = 20
+        srt = np.sort(scores[:, :n], axis=1)
+        gap = float((srt[:, -1] - srt[:, -2]).min())
+        big = 1000.0 / gap
+        out, _, _ = o.kv_attention(q, kc, vc, n, g, sym, big)
+        top = scores[:, :n].argmax(axis=1)
+        assert np.array_equal(out, vh[np.arange(heads), top])
+        # tolerance references
+        out, sabs, vabs = o.kv_attention(q, kc, vc, n, g, sym, 0.125)
+        assert np.allclose(sabs, 0.125 * (np.abs(kh[:, :n]) @ np.abs(q64)[:, :, None])[..., 0]
+                           .max(axis=1), rtol=1e-13)
+        assert np.array_equal(vabs, np.abs(vh[:, :n]).max(axis=1))
+        # the order of the cached tokens does not matter
+        k, v, _, _ = _kv_fill(o, 43 + sym, heads, t_cap, d, g, sym, t_cap)
+        perm = rng.permutation(n)
+        kc2, vc2 = o.kv_cache(heads, t_cap, d, g), o.kv_cache(heads, t_cap, d, g)
+        o.kv_quantize(np.ascontiguousarray(k[:n][perm]), g, sym, kc2, 0)
+        o.kv_quantize(np.ascontiguousarray(v[:n][perm]), g, sym, vc2, 0)
+        out2, _, _ = o.kv_attention(q, kc2, vc2, n, g, sym, 0.125)
+        assert np.allclose(out2, out, rtol=1e-12, atol=1e-14)
+        # brute force with Python floats on a small slice: heads 0..1, 5 tokens
+        out5, _, _ = o.kv_attention(q, kc, vc, 5, g, sym, 0.125)
+        for h in range(2):
+            sc = [0.125 * sum(float(q[h, i]) * float(kh[h, t, i]) for i in range(d)) for t in range(5)]
+            w = [math.exp(x - max(sc)) for x in sc]
+            for i in (0, 7, 31, 32, 63):
+                val = sum(w[t] * float(vh[h, t, i]) for t in range(5)) / sum(w)
+                assert abs(out5[h, i] - val) <= 1e-12 * max(1.0, abs(val))
+
+
 ALL_CHECKS = [check_golden_groups, check_fp16_conversion, check_invariants,
               check_brute_force_nearest, check_levels_and_bytes, check_dequant_closed_forms,
               check_linear, check_argument_rejection, check_mse_brute_force,
-              check_mse_rtn_limit]
+              check_mse_rtn_limit, check_kv_cache_placement, check_kv_attention]

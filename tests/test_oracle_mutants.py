@@ -53,6 +53,23 @@ MUTANTS = [
     ("mse_zero_point_unclipped", "if (!symmetric) z = (int)clampf(rintf(-lo / S), q_min, q_max);",
      "if (!symmetric) z = (int)clampf(rintf(-lo / S) + 1.0f, q_min, q_max);"),
     ("mse_sym_range_unscaled", "s = (alpha * amax) / 7.0f;", "s = amax / 7.0f;"),
+    ("kv_cache_token_major", "const int64_t r = h * t_cap + t0 + t;",
+     "const int64_t r = (t0 + t) * heads + h;"),
+    ("kv_cache_ignores_t0", "const int64_t r = h * t_cap + t0 + t;", "const int64_t r = h * t_cap + t;"),
+    ("kv_input_head_major", "(size_t)((t * heads + h) * d) * esize",
+     "(size_t)((h * t_new + t) * d) * esize"),
+    ("kv_attn_token_major", "const int64_t r = h * t_cap + t;\n            double acc",
+     "const int64_t r = t * heads + h;\n            double acc"),
+    ("kv_attn_value_token_shift", "xhat_elem(vq, vs, vz, h * t_cap + t, i",
+     "xhat_elem(vq, vs, vz, h * t_cap + (t + 1) % n_tok, i"),
+    ("kv_attn_keys_as_values", "xhat_elem(vq, vs, vz,", "xhat_elem(kq, ks, kz,"),
+    ("kv_attn_value_scales_from_keys", "xhat_elem(vq, vs, vz,", "xhat_elem(vq, ks, vz,"),
+    ("kv_attn_no_scale", "s[t] = scale * acc;", "s[t] = acc;"),
+    ("kv_attn_unnormalized", "out[h * d + i] = acc / l;", "out[h * d + i] = acc;"),
+    ("kv_attn_exp_sign", "s[t] = exp(s[t] - M);", "s[t] = exp(M - s[t]);"),
+    ("kv_attn_query_of_head0", "load_elem(q, q_dtype, h * d + i)", "load_elem(q, q_dtype, i)"),
+    ("kv_attn_drops_last_token", "for (int64_t t = 0; t < n_tok; ++t) {\n            s[t] = exp",
+     "for (int64_t t = 0; t < n_tok; ++t) {\n            if (t == n_tok - 1 && t) { s[t] = 0; continue; }\n            s[t] = exp"),
 ]
 
 
