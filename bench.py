@@ -20,6 +20,9 @@ Algorithmic bytes (what the method must move, nothing else):
                      + 2*m*k (x, bf16) + 4*m*n (y, fp32)
   GEMM   2*m*n*k flop against the bf16 dense MFMA peak
   quantize per weight: 2 (bf16 read) + 0.5 (codes); per group 2 (scale) + 0.5 (zero)
+  KV attention per layer: both INT4 caches over the context (per token and head
+                     d/2 codes + 2*d/g scale bytes + 4*ceil(d/g/8) zero-word bytes, each),
+                     q (bf16), out (fp32)
 
 Prints one JSON line.  ``--gpus`` above 1 is refused: this build runs on one GPU.
 """
@@ -28,6 +31,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -108,6 +112,62 @@ def graph_ms(graph, reps):
     return t0.elapsed_time(t1) / reps
 
 
+def kv_cache_bytes(heads, t, d, g, sym=False):
+    """Bytes of one INT4 cache (K or V) holding t tokens: codes, scales, zero words."""
+    zeros = 0 if sym else 4 * ((d // g + 7) // 8)
+    return heads * t * (d // 2 + 2 * (d // g) + zeros)
+
+
+def kv_leg(q4, synthetic, torch, dev, layers=32):
+    """One decode step of 7B-shaped attention over every layer's INT4 K and V caches
+    (4096-token context), plus the quantize calls that fill and extend the caches."""
+    ck = synthetic.KV_7B
+    H, D, g, T = ck["heads"], ck["head_dim"], ck["group_size"], ck["t"]
+    k = synthetic.kv_tokens(T, H, D, ck["k_seed"], "k").to(dev)
+    v = synthetic.kv_tokens(T, H, D, ck["v_seed"], "v").to(dev)
+    q = synthetic.query(H, D, ck["q_seed"]).to(dev)
+    scale = 1.0 / math.sqrt(D)
+    kcs = [q4.empty_kv_cache(H, ck["t_cap"], D, g, False, dev) for _ in range(layers)]
+    vcs = [q4.empty_kv_cache(H, ck["t_cap"], D, g, False, dev) for _ in range(layers)]
+    fill = ([lambda c=c: q4.q4_kv_quantize(k, c, 0) for c in kcs] +
+            [lambda c=c: q4.q4_kv_quantize(v, c, 0) for c in vcs])
+    for f in fill:
+        f()
+    torch.cuda.synchronize()
+    qname = q4.q4_last_kernel()
+    t_fill = graph_ms(capture(fill), 3) / len(fill) * 1e-3
+    k1, v1 = k[T - 1:].contiguous(), v[T - 1:].contiguous()
+    app = ([lambda c=c: q4.q4_kv_quantize(k1, c, T - 1) for c in kcs] +
+           [lambda c=c: q4.q4_kv_quantize(v1, c, T - 1) for c in vcs])
+    t_app = graph_ms(capture(app), 5) / len(app) * 1e-3
+    ws_bytes = q4.q4_kv_attention_workspace(H, D, T)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    outs = torch.empty((layers, H, D), dtype=torch.float32, device=dev)
+    att = [lambda i=i: q4.q4_kv_attention(q, kcs[i], vcs[i], T, scale, out=outs[i], workspace=ws)
+           for i in range(layers)]
+    att[0]()
+    torch.cuda.synchronize()
+    aname = q4.q4_last_kernel()
+    t_att = graph_ms(capture(att), 5) / layers * 1e-3
+    cache = kv_cache_bytes(H, T, D, g)
+    att_bytes = 2 * cache + H * D * 2 + H * D * 4
+    fill_bytes = H * T * D * 2 + cache
+    bf16_cache = 2 * H * T * D * 2
+    return {
+        "workload": f"7B-shaped decode attention, {H} heads x head_dim {D}, {T}-token context, "
+                    f"INT4 K and V caches g{g} asym, one step over {layers} layers",
+        "attention": {"kernel": aname, "us_per_layer": round(t_att * 1e6, 3),
+                      "bytes_per_layer": att_bytes,
+                      "gbs": round(att_bytes / t_att / 1e9, 1),
+                      "frac_hbm": round(att_bytes / t_att / 1e9 / HBM_PEAK_GBS, 4),
+                      "cache_bytes_vs_bf16": round(2 * cache / bf16_cache, 4)},
+        "prefill_quantize": {"kernel": qname, "tokens": T, "us": round(t_fill * 1e6, 2),
+                             "gbs": round(fill_bytes / t_fill / 1e9, 1),
+                             "frac_hbm": round(fill_bytes / t_fill / 1e9 / HBM_PEAK_GBS, 4)},
+        "decode_append": {"tokens": 1, "us": round(t_app * 1e6, 3)},
+    }
+
+
 def cpu_baseline(seconds=12.0):
     """The CPU oracle (plain scalar C, one thread) on a bounded sample of the decode
     workload: full fp64 passes over both projections at M=1."""
@@ -142,7 +202,7 @@ def main():
     ap.add_argument("--steps", type=int, default=340)
     ap.add_argument("--warmup", type=int, default=34)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--legs", default="gemm,quant,sweep,mlp,mse",
+    ap.add_argument("--legs", default="gemm,quant,sweep,mlp,mse,kv",
                     help="comma list of legs besides the headline decode GEMV")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy 5 times (the "
@@ -285,6 +345,10 @@ def main():
             del w, wf
         out["mse_clip"] = {"workload": "7B-like decode matrices, bf16, g128, clip ratios (20-i)/20, "
                                        "i = 0..10, per group", "bound": "alu", "results": res}
+
+    # ------------------------------------------------------------ INT4 KV cache (decode attention)
+    if "kv" in legs:
+        out["kv_cache"] = kv_leg(q4, synthetic, torch, dev)
 
     # ------------------------------------------------------------ MLP batch sweep (GEMV, m <= 16)
     if "mlp" in legs:

@@ -152,6 +152,65 @@ q4_status q4_w4a16_gemm_grouped(const q4_gemm_problem* problems, int32_t count,
                                 q4_dtype x_dtype, int64_t m, int64_t k, int32_t group_size,
                                 int32_t symmetric, hipStream_t stream);
 
+/* ---- INT4 KV cache ([QA1] KV-cache chapter: §KV cache의 bandwidth 부담, §Per-token scale
+ * 수식, §asym 선택 이유, §Attention에서의 결합, §INT4 group scheme; [FL7] §KV Cache
+ * Quantization).  One layer's K cache, and separately its V cache, for `heads` heads of
+ * head_dim d with room for t_cap tokens, is head-major: token t of head h is row
+ * h * t_cap + t of the packed format above with n = heads * t_cap and k = d, i.e. groups
+ * of g consecutive head dimensions with one fp16 scale and one zero point per
+ * (token, head, group):
+ *   qcache uint32 [heads*t_cap][d/8], scache fp16 [heads*t_cap][d/g],
+ *   zcache uint32 [heads*t_cap][ceil(d/g/8)] (asymmetric only, may be NULL otherwise).
+ * The pages' scheme is asymmetric with g = 32 and d = 128; symmetric codes are accepted
+ * too. */
+
+/* Append t_new tokens to a cache: kv [t_new][heads][d] (F32, F16 or BF16, the new tokens'
+ * K or V as the projection produces them) is quantized per (token, head) exactly as
+ * q4_quantize_pack quantizes one row, scales and zero points recomputed for every token,
+ * into rows h * t_cap + t0 + t, t = 0 .. t_new-1.  A prefill writes its prompt in one call,
+ * a decode step its one token.  No other row is touched.  Requires t_new >= 1, t0 >= 0,
+ * t0 + t_new <= t_cap, d % group_size == 0, d <= 2^16 and heads * t_cap < 2^31 (else
+ * Q4_ERR_SHAPE); dtype, pointer and alignment rules as q4_quantize_pack (kv and qcache
+ * 16 bytes). */
+q4_status q4_kv_quantize(const void* kv, q4_dtype kv_dtype, int64_t t_new, int64_t heads,
+                         int64_t head_dim, int32_t group_size, int32_t symmetric, int64_t t_cap,
+                         int64_t t0, uint32_t* qcache, uint16_t* scache, uint32_t* zcache,
+                         hipStream_t stream);
+
+/* Bytes of workspace q4_kv_attention needs for (heads, head_dim, n_tok): head_dim + 2
+ * floats for each of at most ceil(n_tok * head_dim / 8192) chunks per head.  Never smaller
+ * for a larger n_tok, so one workspace sized for the cache capacity serves every decode
+ * step.  -1 for sizes q4_kv_attention rejects. */
+int64_t q4_kv_attention_workspace(int64_t heads, int64_t head_dim, int64_t n_tok);
+
+/* Decode attention, one query per head, over tokens 0 .. n_tok-1 of a quantized K and V
+ * cache (same heads, head_dim, group_size, symmetric and t_cap):
+ *   out[h][i] = sum_t softmax_t(scale * q[h] . K_hat[h][t]) * V_hat[h][t][i],
+ *   K_hat = S (u - z) per group (z = 8 when symmetric), V_hat alike,
+ * with the dequantization inside the kernel, so the cache is read once at 4 bits
+ * ([QA1] §Attention에서의 결합).  q [heads][head_dim] F16 or BF16; out fp32
+ * [heads][head_dim]; scale is the caller's (usually 1/sqrt(head_dim)).  The tokens of a
+ * head are split into chunks (a rule that depends on heads, head_dim and n_tok alone, so
+ * results repeat bit for bit), each reduced in `workspace` to a reference maximum, its sum
+ * of exponentials and its unnormalized output; a second kernel combines each head's
+ * chunks in chunk order.  workspace: device memory of at least q4_kv_attention_workspace
+ * bytes, 16-byte aligned, contents on entry ignored; calls that share a workspace must
+ * not run concurrently.  Arithmetic is fp32: with u = 2^-24, gamma(n) = n*u/(1-n*u) and
+ * L = ceil(n_tok * head_dim / 8192) + 32 (a bound on the longest chain of fp32 additions),
+ * the score error is at most delta = gamma(64) |scale| max_t sum_i |q_i| 30 S_K(t, i), and
+ * |out - exact| <= 2 (delta + gamma(L + 8)) max_t |V_hat[t][i]| + gamma(L) 60 max_t S_V(t, i)
+ * (exact = the same formula in exact arithmetic on the stored codes).
+ * Requires head_dim in {64, 128, 256}, group_size <= head_dim, 1 <= heads <= 65536,
+ * 1 <= n_tok <= t_cap, n_tok <= 2^24, heads * t_cap < 2^31 (else Q4_ERR_SHAPE; a short
+ * workspace is Q4_ERR_SHAPE too); alignment: q, kq, vq, workspace 16 bytes, kz, vz, out
+ * 4 bytes, ks, vs 2 bytes. */
+q4_status q4_kv_attention(const void* q, q4_dtype q_dtype, int64_t heads, int64_t head_dim,
+                          int64_t n_tok, int64_t t_cap, const uint32_t* kq, const uint16_t* ks,
+                          const uint32_t* kz, const uint32_t* vq, const uint16_t* vs,
+                          const uint32_t* vz, int32_t group_size, int32_t symmetric, float scale,
+                          float* out, void* workspace, int64_t workspace_bytes,
+                          hipStream_t stream);
+
 /* Element counts of the three packed arrays (payload + metadata, [FL7] §Memory 계산은
  * Payload와 Metadata로 나눈다): n*k/8 words, n*(k/g) scales, n*ceil((k/g)/8) words.
  * Return -1 for arguments the entry points would reject. */

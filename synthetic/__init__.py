@@ -15,6 +15,11 @@ Distribution recipe (stated once, used everywhere):
   channels scaled, then cast once to the activation dtype.
 * Outlier channel set: ``randperm(K)[:round(0.001*K)]`` from the weight's own generator,
   so weight and activation outliers sit on the same channels.
+* KV-cache tokens (the KV-cache chapter of "Quantization Algorithms 단권화" describes K as
+  centred near zero with a mild per-channel skew and V as asymmetric with magnitudes that
+  vary from token to token): K[t, h, i] = N(0, 1) + b[h, i] with a per-channel offset
+  b ~ N(0, 0.5); V[t, h, i] = N(0, 1) * m[t, h] + 0.25 with a per-token magnitude
+  m = exp(N(0, 0.5)); queries q[h, i] ~ N(0, 1).  Drawn in fp32, cast once.
 
 Every generator is a ``torch.Generator`` seeded with the stated seed.  Host (CPU)
 generation is the default.  ``device="cuda"`` uses a seeded device generator (a
@@ -38,6 +43,9 @@ __all__ = [
     "MLP_SWEEP",
     "PREFILL_70B",
     "checkpoint_7b",
+    "kv_tokens",
+    "query",
+    "KV_7B",
 ]
 
 
@@ -149,3 +157,31 @@ def sample_rows(n: int, count: int, seed: int) -> torch.Tensor:
 def as_u16(t: torch.Tensor):
     """Raw 16-bit patterns of a bf16/fp16 tensor as a numpy uint16 array (host copy)."""
     return t.detach().cpu().contiguous().view(torch.int16).numpy().view("uint16")
+
+
+def kv_tokens(t: int, heads: int, head_dim: int, seed: int, kind: str,
+              dtype=torch.bfloat16) -> torch.Tensor:
+    """New KV-cache entries [t, heads, head_dim] of the K ("k") or V ("v") recipe."""
+    g = torch.Generator().manual_seed(int(seed))
+    x = torch.randn((t, heads, head_dim), generator=g, dtype=torch.float32)
+    if kind == "k":
+        b = torch.randn((1, heads, head_dim), generator=g, dtype=torch.float32) * 0.5
+        x = x + b
+    elif kind == "v":
+        m = torch.exp(torch.randn((t, heads, 1), generator=g, dtype=torch.float32) * 0.5)
+        x = x * m + 0.25
+    else:
+        raise ValueError("kind must be 'k' or 'v'")
+    return x.to(dtype)
+
+
+def query(heads: int, head_dim: int, seed: int, dtype=torch.bfloat16) -> torch.Tensor:
+    """One decode step's queries q [heads, head_dim] ~ N(0, 1)."""
+    g = torch.Generator().manual_seed(int(seed))
+    return torch.randn((heads, head_dim), generator=g, dtype=torch.float32).to(dtype)
+
+
+# 7B-shaped decode attention over an INT4 cache: 32 heads of 128 dimensions, groups of 32
+# along the head dimension, asymmetric (the pages' KV scheme), a 4096-token context.
+KV_7B = dict(heads=32, head_dim=128, group_size=32, symmetric=False, t=4096, t_cap=4096,
+             k_seed=200, v_seed=201, q_seed=202)

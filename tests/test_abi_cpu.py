@@ -192,3 +192,72 @@ def test_quantize_row_length_limit():
 def test_quantize_mse_validation_rejects_before_launch(args, code):
     assert q4.lib().q4_quantize_pack_mse(*args) == code
     assert q4.q4_last_kernel() == ""
+
+
+def _kvq(kv=A16, dt=BF16, t_new=1, heads=4, d=128, g=32, sym=0, t_cap=16, t0=0, qc=A16, sc=A16,
+         zc=A16):
+    return q4.lib().q4_kv_quantize(kv, dt, t_new, heads, d, g, sym, t_cap, t0, qc, sc, zc, None)
+
+
+@pytest.mark.parametrize("call,code", [
+    (lambda: _kvq(g=16), GROUP), (lambda: _kvq(t_new=0), SHAPE), (lambda: _kvq(t0=-1), SHAPE),
+    (lambda: _kvq(t0=15, t_new=2), SHAPE), (lambda: _kvq(t0=16), SHAPE),
+    (lambda: _kvq(heads=0), SHAPE), (lambda: _kvq(d=96, g=64), SHAPE),
+    (lambda: _kvq(d=1 << 17, g=128), SHAPE), (lambda: _kvq(heads=1 << 16, t_cap=1 << 15), SHAPE),
+    (lambda: _kvq(t_cap=0), SHAPE), (lambda: _kvq(dt=7), DTYPE), (lambda: _kvq(kv=None), NULL),
+    (lambda: _kvq(qc=None), NULL), (lambda: _kvq(sc=None), NULL), (lambda: _kvq(zc=None), NULL),
+    (lambda: _kvq(kv=A16 + 8), ALIGN), (lambda: _kvq(qc=A16 + 4), ALIGN),
+    (lambda: _kvq(zc=A16 + 2), ALIGN),
+])
+def test_kv_quantize_validation_rejects_before_launch(call, code):
+    assert call() == code
+    assert q4.q4_last_kernel() == ""
+
+
+def test_kv_quantize_symmetric_accepts_null_zeros():
+    assert _kvq(sym=1, zc=None, g=16) == GROUP
+    assert _kvq(sym=1, zc=None, t_new=0) == SHAPE
+
+
+def _kva(q=A16, qd=BF16, heads=4, d=128, n_tok=100, t_cap=128, kq=A16, ks=A16, kz=A16, vq=A16,
+         vs=A16, vz=A16, g=32, sym=0, scale=0.088, out=A16, ws=A16, ws_bytes=1 << 30):
+    return q4.lib().q4_kv_attention(q, qd, heads, d, n_tok, t_cap, kq, ks, kz, vq, vs, vz, g, sym,
+                                    scale, out, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("call,code", [
+    (lambda: _kva(g=16), GROUP), (lambda: _kva(d=96), SHAPE), (lambda: _kva(d=512), SHAPE),
+    (lambda: _kva(d=64, g=128), SHAPE), (lambda: _kva(n_tok=0), SHAPE),
+    (lambda: _kva(n_tok=129), SHAPE), (lambda: _kva(heads=0), SHAPE),
+    (lambda: _kva(heads=65537, t_cap=128), SHAPE),
+    (lambda: _kva(n_tok=(1 << 24) + 1, t_cap=(1 << 24) + 1, heads=1), SHAPE),
+    (lambda: _kva(heads=1 << 10, t_cap=1 << 21), SHAPE),
+    (lambda: _kva(qd=F32), DTYPE), (lambda: _kva(q=None), NULL), (lambda: _kva(out=None), NULL),
+    (lambda: _kva(ws=None), NULL), (lambda: _kva(kz=None), NULL), (lambda: _kva(vs=None), NULL),
+    (lambda: _kva(vq=None), NULL), (lambda: _kva(q=A16 + 8), ALIGN),
+    (lambda: _kva(ws=A16 + 4), ALIGN), (lambda: _kva(out=A16 + 2), ALIGN),
+    (lambda: _kva(kq=A16 + 4), ALIGN), (lambda: _kva(vz=A16 + 2), ALIGN),
+    (lambda: _kva(ws_bytes=16), SHAPE),
+])
+def test_kv_attention_validation_rejects_before_launch(call, code):
+    assert call() == code
+    assert q4.q4_last_kernel() == ""
+
+
+def test_kv_attention_symmetric_accepts_null_zeros():
+    assert _kva(sym=1, kz=None, vz=None, g=16) == GROUP
+
+
+def test_kv_attention_workspace_size():
+    # (head_dim + 2) floats for each of at most ceil(n_tok * head_dim / 8192) chunks per
+    # head; never smaller for a larger n_tok
+    lib = q4.lib()
+    for heads, d, n in [(32, 128, 4096), (1, 128, 5000), (3, 64, 777), (64, 256, 1), (8, 128, 4113)]:
+        assert lib.q4_kv_attention_workspace(heads, d, n) == 4 * heads * (d + 2) * -(-n * d // 8192)
+    assert lib.q4_kv_attention_workspace(32, 128, 4096) == 32 * 64 * 130 * 4
+    for heads, d in [(1, 256), (2, 128), (32, 128), (5, 64)]:
+        sizes = [lib.q4_kv_attention_workspace(heads, d, n) for n in range(1, 20000, 7)]
+        assert all(a <= b for a, b in zip(sizes, sizes[1:]))
+    assert lib.q4_kv_attention_workspace(32, 96, 4096) == -1
+    assert lib.q4_kv_attention_workspace(0, 128, 4096) == -1
+    assert lib.q4_kv_attention_workspace(4, 128, 0) == -1

@@ -10,6 +10,8 @@ Entry points (same names as the C ABI):
     q4_dequant(packed, out_dtype)                       -> W_hat [n, k]
     q4_w4a16_gemm(x, packed)                            -> y [m, n] fp32
     q4_w4a16_gemm_grouped(xs, packs)                    -> [y_i], one launch when m <= 16
+    q4_kv_quantize(kv, cache, t0)                       -> appends tokens to a KvCache
+    q4_kv_attention(q, kcache, vcache, n_tok, scale)    -> out [heads, d] fp32
     q4_last_kernel()                                    -> name of the last kernel run
 """
 from __future__ import annotations
@@ -26,7 +28,8 @@ from . import _build
 __all__ = ["PackedWeight", "q4_quantize_pack", "q4_quantize_pack_grouped", "q4_quantize_pack_mse",
            "q4_dequant",
            "q4_w4a16_gemm",
-           "q4_w4a16_gemm_grouped", "q4_last_kernel",
+           "q4_w4a16_gemm_grouped", "q4_last_kernel", "KvCache", "empty_kv_cache",
+           "q4_kv_quantize", "q4_kv_attention", "q4_kv_attention_workspace",
            "q4_qweight_words", "q4_scale_count", "q4_zero_words", "q4_layout_version",
            "library_path", "Q4Error"]
 
@@ -35,8 +38,8 @@ _DTYPE_CODE = {torch.float32: Q4_F32, torch.float16: Q4_F16, torch.bfloat16: Q4_
 
 EXPORTED = ("q4_quantize_pack", "q4_quantize_pack_grouped", "q4_quantize_pack_mse", "q4_dequant",
             "q4_w4a16_gemm",
-            "q4_w4a16_gemm_grouped",
-            "q4_qweight_words",
+            "q4_w4a16_gemm_grouped", "q4_kv_quantize", "q4_kv_attention",
+            "q4_kv_attention_workspace", "q4_qweight_words",
             "q4_scale_count", "q4_zero_words", "q4_status_str", "q4_last_kernel",
             "q4_layout_version")
 
@@ -93,6 +96,14 @@ def _load():
     lib.q4_w4a16_gemm_grouped.argtypes = [ctypes.POINTER(GemmProblem), i32, ctypes.c_int, i64, i64,
                                           i32, i32, vp]
     lib.q4_w4a16_gemm_grouped.restype = ctypes.c_int
+    lib.q4_kv_quantize.argtypes = [vp, ctypes.c_int, i64, i64, i64, i32, i32, i64, i64, vp, vp, vp,
+                                   vp]
+    lib.q4_kv_quantize.restype = ctypes.c_int
+    lib.q4_kv_attention_workspace.argtypes = [i64, i64, i64]
+    lib.q4_kv_attention_workspace.restype = i64
+    lib.q4_kv_attention.argtypes = [vp, ctypes.c_int, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp,
+                                    i32, i32, ctypes.c_float, vp, vp, i64, vp]
+    lib.q4_kv_attention.restype = ctypes.c_int
     lib.q4_qweight_words.argtypes = [i64, i64]
     lib.q4_qweight_words.restype = i64
     lib.q4_scale_count.argtypes = [i64, i64, i32]
@@ -284,3 +295,78 @@ def q4_w4a16_gemm_grouped(xs, packs, outs=None):
     _check(_load().q4_w4a16_gemm_grouped(arr, count, _DTYPE_CODE[x0.dtype], m, p0.k,
                                          p0.group_size, int(p0.symmetric), _stream(x0)))
     return ys
+
+
+# ------------------------------------------------------------------ INT4 KV cache
+
+@dataclass
+class KvCache:
+    """One layer's head-major INT4 K (or V) cache: token t of head h is row h * t_cap + t
+    of the packed format with k = head_dim: qcache int32 [heads*t_cap, d/8], scache
+    float16 [heads*t_cap, d/g], zcache int32 [heads*t_cap, ceil(d/g/8)] or None when
+    symmetric."""
+    qcache: torch.Tensor
+    scache: torch.Tensor
+    zcache: Optional[torch.Tensor]
+    heads: int
+    t_cap: int
+    head_dim: int
+    group_size: int
+    symmetric: bool
+
+
+def empty_kv_cache(heads: int, t_cap: int, head_dim: int, group_size: int = 32,
+                   symmetric: bool = False, device="cuda") -> KvCache:
+    p = empty_packed(heads * t_cap, head_dim, group_size, symmetric, device)
+    return KvCache(p.qweight, p.scales, p.zeros, heads, t_cap, head_dim, group_size,
+                   bool(symmetric))
+
+
+def q4_kv_quantize(kv: torch.Tensor, cache: KvCache, t0: int) -> KvCache:
+    """Quantize kv [t_new, heads, head_dim] (fp32 / fp16 / bf16) into token positions
+    t0 .. t0 + t_new - 1 of ``cache``."""
+    _need_cuda("kv", kv)
+    if kv.dim() != 3 or kv.dtype not in _DTYPE_CODE:
+        raise ValueError("kv must be a 3-D fp32, fp16 or bf16 tensor [t_new, heads, head_dim]")
+    t_new, heads, d = kv.shape
+    if heads != cache.heads or d != cache.head_dim:
+        raise ValueError("kv does not match the cache's heads / head_dim")
+    _check(_load().q4_kv_quantize(_dev_ptr(kv), _DTYPE_CODE[kv.dtype], t_new, heads, d,
+                                  cache.group_size, int(cache.symmetric), cache.t_cap, t0,
+                                  _dev_ptr(cache.qcache), _dev_ptr(cache.scache),
+                                  _dev_ptr(cache.zcache), _stream(kv)))
+    return cache
+
+
+def q4_kv_attention_workspace(heads: int, head_dim: int, n_tok: int) -> int:
+    return int(_load().q4_kv_attention_workspace(heads, head_dim, n_tok))
+
+
+def q4_kv_attention(q: torch.Tensor, kcache: KvCache, vcache: KvCache, n_tok: int,
+                    scale: float, out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode attention of q [heads, head_dim] (fp16 / bf16) over tokens 0 .. n_tok-1 of
+    the INT4 caches; returns out [heads, head_dim] fp32.  A ``workspace`` passed in is
+    sized with q4_kv_attention_workspace for the largest n_tok it will serve."""
+    _need_cuda("q", q)
+    if q.dim() != 2 or q.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("q must be a 2-D fp16 or bf16 tensor [heads, head_dim]")
+    heads, d = q.shape
+    for c in (kcache, vcache):
+        if (c.heads, c.head_dim) != (heads, d):
+            raise ValueError("q does not match the caches' heads / head_dim")
+    if (kcache.group_size, kcache.symmetric, kcache.t_cap) != \
+            (vcache.group_size, vcache.symmetric, vcache.t_cap):
+        raise ValueError("K and V caches must share group_size, symmetry and t_cap")
+    if out is None:
+        out = torch.empty((heads, d), dtype=torch.float32, device=q.device)
+    need = q4_kv_attention_workspace(heads, d, n_tok)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check(_load().q4_kv_attention(
+        _dev_ptr(q), _DTYPE_CODE[q.dtype], heads, d, n_tok, kcache.t_cap,
+        _dev_ptr(kcache.qcache), _dev_ptr(kcache.scache), _dev_ptr(kcache.zcache),
+        _dev_ptr(vcache.qcache), _dev_ptr(vcache.scache), _dev_ptr(vcache.zcache),
+        kcache.group_size, int(kcache.symmetric), float(scale), _dev_ptr(out),
+        _dev_ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q)))
+    return out

@@ -201,6 +201,73 @@ q4_status q4_w4a16_gemm(const void* x, q4_dtype x_dtype, int64_t m, const uint32
     return finish(e, name);
 }
 
+namespace {
+constexpr int64_t kMaxKvHeads = 65536;
+constexpr int64_t kMaxKvTokens = int64_t(1) << 24;
+constexpr int64_t kMaxKvDim = 65536;
+
+// Sizes shared by both KV entry points: head-major cache rows heads * t_cap index as int.
+q4_status check_kv_sizes(int64_t heads, int64_t head_dim, int32_t g, int64_t t_cap) {
+    if (!group_ok(g)) return Q4_ERR_GROUP;
+    if (heads < 1 || head_dim < 1 || t_cap < 1 || head_dim > kMaxKvDim) return Q4_ERR_SHAPE;
+    if (head_dim % g != 0) return Q4_ERR_SHAPE;
+    if (t_cap > kMaxDim / heads) return Q4_ERR_SHAPE;
+    return Q4_OK;
+}
+
+bool kv_attention_dims_ok(int64_t heads, int64_t head_dim, int64_t n_tok) {
+    return (head_dim == 64 || head_dim == 128 || head_dim == 256) && heads >= 1 &&
+           heads <= kMaxKvHeads && n_tok >= 1 && n_tok <= kMaxKvTokens;
+}
+}  // namespace
+
+q4_status q4_kv_quantize(const void* kv, q4_dtype kv_dtype, int64_t t_new, int64_t heads,
+                         int64_t head_dim, int32_t group_size, int32_t symmetric, int64_t t_cap,
+                         int64_t t0, uint32_t* qcache, uint16_t* scache, uint32_t* zcache,
+                         hipStream_t stream) {
+    q4_status st = check_kv_sizes(heads, head_dim, group_size, t_cap);
+    if (st != Q4_OK) return st;
+    if (t_new < 1 || t0 < 0 || t0 > t_cap - t_new) return Q4_ERR_SHAPE;
+    st = check_quant(kv, kv_dtype, t_new * heads, head_dim, group_size, symmetric, qcache, scache,
+                     zcache);
+    if (st != Q4_OK) return st;
+    const char* name = "";
+    const hipError_t e = q4k_kv_quantize(kv, (int)kv_dtype, t_new, heads, head_dim, group_size,
+                                         symmetric ? 1 : 0, t_cap, t0, qcache, scache,
+                                         symmetric ? nullptr : zcache, stream, &name);
+    return finish(e, name);
+}
+
+int64_t q4_kv_attention_workspace(int64_t heads, int64_t head_dim, int64_t n_tok) {
+    if (!kv_attention_dims_ok(heads, head_dim, n_tok)) return -1;
+    return heads * q4k_kv_max_chunks(head_dim, n_tok) * (head_dim + 2) * (int64_t)sizeof(float);
+}
+
+q4_status q4_kv_attention(const void* q, q4_dtype q_dtype, int64_t heads, int64_t head_dim,
+                          int64_t n_tok, int64_t t_cap, const uint32_t* kq, const uint16_t* ks,
+                          const uint32_t* kz, const uint32_t* vq, const uint16_t* vs,
+                          const uint32_t* vz, int32_t group_size, int32_t symmetric, float scale,
+                          float* out, void* workspace, int64_t workspace_bytes,
+                          hipStream_t stream) {
+    q4_status st = check_kv_sizes(heads, head_dim, group_size, t_cap);
+    if (st != Q4_OK) return st;
+    if (!kv_attention_dims_ok(heads, head_dim, n_tok) || n_tok > t_cap) return Q4_ERR_SHAPE;
+    if (q_dtype != Q4_F16 && q_dtype != Q4_BF16) return Q4_ERR_DTYPE;
+    if (!q || !out || !workspace) return Q4_ERR_NULL;
+    if ((st = check_packed(kq, ks, kz, symmetric)) != Q4_OK) return st;
+    if ((st = check_packed(vq, vs, vz, symmetric)) != Q4_OK) return st;
+    if (!aligned(q, 16) || !aligned(out, 4) || !aligned(workspace, 16)) return Q4_ERR_ALIGN;
+    if (workspace_bytes < q4_kv_attention_workspace(heads, head_dim, n_tok)) return Q4_ERR_SHAPE;
+    int chunks = 0, loads = 0;
+    q4k_kv_attention_shape(heads, head_dim, n_tok, &chunks, &loads);
+    const char* name = "";
+    const hipError_t e = q4k_kv_attention(
+        q, (int)q_dtype, kq, ks, symmetric ? nullptr : kz, vq, vs, symmetric ? nullptr : vz, heads,
+        head_dim, n_tok, t_cap, group_size, symmetric ? 1 : 0, scale, out,
+        static_cast<float*>(workspace), chunks, loads, stream, &name);
+    return finish(e, name);
+}
+
 int64_t q4_qweight_words(int64_t n, int64_t k) {
     if (n < 1 || k < 1 || k % 8 != 0) return -1;
     return n * (k / 8);

@@ -125,6 +125,22 @@ __device__ __forceinline__ uint32_t buf_load_u16(rsrc r, int voff, int soff) {
 hipError_t q4k_quant_pack(const void* w, int w_dtype, int64_t n, int64_t k, int g, int sym,
                           uint32_t* qweight, uint16_t* scales, uint32_t* zeros,
                           hipStream_t stream, const char** kname);
+// New tokens of a KV cache: kv [t_new][heads][d] quantized per (token, head) group of g
+// along d into the head-major packed cache at token positions t0 .. t0 + t_new - 1.
+hipError_t q4k_kv_quantize(const void* kv, int dtype, int64_t t_new, int64_t heads, int64_t d, int g,
+                           int sym, int64_t t_cap, int64_t t0, uint32_t* qcache, uint16_t* scache,
+                           uint32_t* zcache, hipStream_t stream, const char** kname);
+// Decode attention over INT4 K/V caches: the chunk split (chunks per head; loads per wave,
+// a chunk being 4 waves x loads x 2048/d tokens; never more than max_chunks per head) and
+// the two launches (per-chunk partials into workspace, then the combine).
+void q4k_kv_attention_shape(int64_t heads, int64_t d, int64_t n_tok, int* chunks, int* loads);
+int64_t q4k_kv_max_chunks(int64_t d, int64_t n_tok);
+hipError_t q4k_kv_attention(const void* q, int q_dtype, const uint32_t* kq, const uint16_t* ks,
+                            const uint32_t* kz, const uint32_t* vq, const uint16_t* vs,
+                            const uint32_t* vz, int64_t heads, int64_t d, int64_t n_tok,
+                            int64_t t_cap, int g, int sym, float scale, float* out,
+                            float* workspace, int chunks, int loads, hipStream_t stream,
+                            const char** kname);
 hipError_t q4k_quant_mse(const void* w, int w_dtype, int64_t n, int64_t k, int g, int sym,
                          uint32_t* qweight, uint16_t* scales, uint32_t* zeros,
                          hipStream_t stream, const char** kname);
@@ -152,7 +168,9 @@ struct GemvBatch {
     GemvProblem p[kMaxGroup];
     int count;
 };
-// One matrix of a grouped quantize/pack launch, and the launch's problems.
+// One matrix of a grouped quantize/pack launch, and the launch's problems.  With
+// heads > 0 the input rows are (token, head) pairs r = t * heads + h of new KV-cache
+// entries and output row r goes to cache row h * t_cap + t0 + t (a head-major cache).
 struct QuantProblem {
     const void* w;
     uint32_t* qweight;
@@ -160,6 +178,9 @@ struct QuantProblem {
     uint32_t* zeros;
     int n;
     int k;
+    int heads;
+    int t_cap;
+    int t0;
 };
 struct QuantBatch {
     QuantProblem p[kMaxGroup];

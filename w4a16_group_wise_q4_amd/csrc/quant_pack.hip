@@ -51,6 +51,7 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(const q4::QuantBatch bt
         uint16_t* __restrict__ scales = bt.p[pi].scales;
         uint32_t* __restrict__ zeros = bt.p[pi].zeros;
         const int n = bt.p[pi].n, k = bt.p[pi].k;
+        const int heads = bt.p[pi].heads, t_cap = bt.p[pi].t_cap, t0 = bt.p[pi].t0;
         const int n_groups = k / G;
         const int zwords = (n_groups + 7) >> 3;
         const int Z = zwords < waves ? zwords : waves;
@@ -83,9 +84,11 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(const q4::QuantBatch bt
             }
             issue(nrow, nzw, vn);
             {
-                const q4::rsrc rq = q4::make_rsrc(qweight + (int64_t)row * (k / 8), (uint32_t)k / 2u);
-                const q4::rsrc rs = q4::make_rsrc(scales + (int64_t)row * n_groups, (uint32_t)n_groups * 2u);
-                const q4::rsrc rz = q4::make_rsrc(zeros + (int64_t)row * zwords, (uint32_t)zwords * 4u);
+                // output row: the same row, or the (head, token) slot of a KV cache
+                const int64_t orow = heads > 0 ? (int64_t)(row % heads) * t_cap + t0 + row / heads : row;
+                const q4::rsrc rq = q4::make_rsrc(qweight + orow * (k / 8), (uint32_t)k / 2u);
+                const q4::rsrc rs = q4::make_rsrc(scales + orow * n_groups, (uint32_t)n_groups * 2u);
+                const q4::rsrc rz = q4::make_rsrc(zeros + orow * zwords, (uint32_t)zwords * 4u);
                 const int gidx = zw * 8 + grp;
                 const bool valid = gidx < n_groups;
                 const uint32_t elem = (uint32_t)gidx * G + (uint32_t)t * E;  // within the row
@@ -228,6 +231,19 @@ hipError_t q4k_quant_pack(const void* w, int w_dtype, int64_t n, int64_t k, int 
     bt.p[0] = q4::QuantProblem{w, qweight, scales, zeros, (int)n, (int)k};
     bt.count = 1;
     return launch_batch(bt, w_dtype, g, sym, stream, kname);
+}
+
+hipError_t q4k_kv_quantize(const void* kv, int dtype, int64_t t_new, int64_t heads, int64_t d, int g,
+                           int sym, int64_t t_cap, int64_t t0, uint32_t* qcache, uint16_t* scache,
+                           uint32_t* zcache, hipStream_t stream, const char** kname) {
+    q4::QuantBatch bt{};
+    bt.p[0] = q4::QuantProblem{kv, qcache, scache, zcache, (int)(t_new * heads), (int)d,
+                               (int)heads, (int)t_cap, (int)t0};
+    bt.count = 1;
+    const hipError_t e = launch_batch(bt, dtype, g, sym, stream, kname);
+    static const char* names[3] = {"q4_kv_quant_f32", "q4_kv_quant_f16", "q4_kv_quant_bf16"};
+    *kname = names[dtype];
+    return e;
 }
 
 hipError_t q4k_quant_pack_grouped(const q4::QuantProblem* problems, int count, int w_dtype, int g,
