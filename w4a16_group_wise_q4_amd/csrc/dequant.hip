@@ -5,7 +5,7 @@
 //
 // One thread per packed word (8 weights).  S (11 significant bits) times u - z (at most
 // 5 bits) is exact in fp32; fp16 / bf16 outputs are one round-to-nearest-even of it.
-#include "q4_device.h"
+#include "q4_launch.h"
 
 namespace {
 

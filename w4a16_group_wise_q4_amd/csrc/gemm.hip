@@ -37,7 +37,7 @@
 // Placement.  Consecutive workgroups land on consecutive XCDs (8 per MI355X), so block b
 // takes activation block b % mtiles: with 16 row blocks (m = 2048) each XCD's L2 holds
 // two 2 MB activation blocks while the packed weights stream through.
-#include "q4_device.h"
+#include "q4_launch.h"
 
 namespace {
 

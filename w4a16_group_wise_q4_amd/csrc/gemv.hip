@@ -40,6 +40,7 @@
 // gives the exact u - z.  Either way products are exact and sums are fp32.
 #include "q4_device.h"
 #include "gemv_tile.h"
+#include "q4_launch.h"
 
 namespace {
 

@@ -29,7 +29,7 @@
 // p_t S_t z separately.  Everything is fp32; no fp32 addition chain is longer than
 // chunks + 32 terms (at most 8 tokens per lane, 3 levels within a row of lanes, 16 rows of
 // the workgroup, the chunks, the rest).
-#include "q4_device.h"
+#include "q4_launch.h"
 
 namespace {
 

@@ -10,7 +10,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "q4_device.h"
+#include "q4_launch.h"
 
 namespace {
 

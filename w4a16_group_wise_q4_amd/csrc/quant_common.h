@@ -4,7 +4,7 @@
 // contraction off).
 #pragma once
 
-#include "q4_device.h"
+#include "q4_launch.h"
 
 #pragma clang fp contract(off)
 
