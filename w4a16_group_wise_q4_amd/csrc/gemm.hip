@@ -241,8 +241,23 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const uint16_t* __res
                 g_cur = gk;
             }
         }
+        // g = 128: the activation operands of two MFMA k-slots are read from LDS ahead of
+        // their MFMAs (32 registers), so each MFMA waits for a read issued long before.  At
+        // g = 32 and 64 (a group boundary every stage or two per stage, with its rescale) the
+        // extra registers would spill: one read per MFMA, as it is needed.
+        constexpr int AP = G == 128 ? 2 : 1;
+        q4::u32x4 aop[AP][4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
+            if constexpr (AP == 2) {
+                if ((kk & 1) == 0) {
+#pragma unroll
+                    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            aop[k2][i] = *reinterpret_cast<const q4::u32x4*>(slot + apos[kk + k2] + i * 32 * (BK * 2));
+                }
+            }
             const int q = G == 32 ? (kk >> 1) : 0;  // group slot of this MFMA
             const bool rescale = fresh[q] && (G == 32 ? (kk & 1) == 0 : kk == 0);
             q4::u32x4 bop[2];
@@ -255,7 +270,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const uint16_t* __res
             const uint8_t* ab = slot + apos[kk];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const q4::u32x4 a = *reinterpret_cast<const q4::u32x4*>(ab + i * 32 * (BK * 2));
+                const q4::u32x4 a = AP == 2 ? aop[(kk & 1) % AP][i]
+                                            : *reinterpret_cast<const q4::u32x4*>(ab + i * 32 * (BK * 2));
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     // each 32x32 tile moves to the new group's units right before its own MFMA,
