@@ -202,7 +202,7 @@ def main():
     ap.add_argument("--steps", type=int, default=340)
     ap.add_argument("--warmup", type=int, default=34)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--legs", default="gemm,quant,sweep,mlp,mse,kv",
+    ap.add_argument("--legs", default="gemm,quant,sweep,mlp,mse,kv,midm",
                     help="comma list of legs besides the headline decode GEMV")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy 5 times (the "
@@ -349,6 +349,37 @@ def main():
     # ------------------------------------------------------------ INT4 KV cache (decode attention)
     if "kv" in legs:
         out["kv_cache"] = kv_leg(q4, synthetic, torch, dev)
+
+    # ------------------------------------------------------------ mid-M (17..256) products
+    if "midm" in legs:
+        res = {}
+        shapes = [("up_11008x4096", 11008, 4096, 5), ("down_4096x11008", 4096, 11008, 6),
+                  ("mlp70b_28672x8192", 28672, 8192, 8)]
+        for nm, n_, k_, seed in shapes:
+            w = synthetic.weight(n_, k_, 0.02, seed).to(dev)
+            p0 = q4.q4_quantize_pack(w, 128, False)
+            del w
+            nb = gemv_bytes(1, n_, k_, 128, False)
+            cps = max(2, -(-4 * MALL_BYTES // nb))
+            pks = [q4.PackedWeight(p0.qweight.clone(), p0.scales.clone(), p0.zeros.clone(), n_, k_, 128, False)
+                   for _ in range(cps)]
+            x256 = synthetic.activations(256, k_, 7).to(dev)
+            row = {}
+            for m in (17, 32, 64, 128, 256):
+                xm = x256[:m].contiguous()
+                ym = torch.empty((m, n_), dtype=torch.float32, device=dev)
+                q4.q4_w4a16_gemm(xm, pks[0], out=ym)
+                torch.cuda.synchronize()
+                kname = q4.q4_last_kernel()
+                t = graph_ms(capture([lambda pp=pp: q4.q4_w4a16_gemm(xm, pp, out=ym) for pp in pks]), 3) / cps * 1e-3
+                byt = gemv_bytes(m, n_, k_, 128, False)
+                row[f"m{m}"] = {"us": round(t * 1e6, 2), "gbs": round(byt / t / 1e9, 1),
+                                "frac_hbm": round(byt / t / 1e9 / HBM_PEAK_GBS, 4),
+                                "tflops": round(2.0 * m * n_ * k_ / t / 1e12, 1), "kernel": kname}
+            res[nm] = row
+            del pks, p0, x256
+        out["midm"] = {"workload": "W4A16 products at m = 17..256 (decode batches of the pages' "
+                                   "concurrency grid, short prompts), g128 asym, bf16 x", "results": res}
 
     # ------------------------------------------------------------ MLP batch sweep (GEMV, m <= 16)
     if "mlp" in legs:

@@ -123,7 +123,12 @@ q4_status q4_dequant(const uint32_t* qweight, const uint16_t* scales, const uint
  *   y[m][n] = sum_k x[m][k] * S[n][k/g] * (u[n][k] - z[n][k/g])
  * x is [m][k] F16 or BF16; y is [m][n] fp32, accumulated in fp32.  m >= 1, and beyond
  * the shared size rules k <= 2^22, n <= 2^25 and m*n <= 2^38 (Q4_ERR_SHAPE otherwise).
- * m <= 16 runs the decode GEMV kernel, larger m the prefill GEMM kernel. */
+ * m <= 16 runs the decode GEMV kernel.  16 < m <= 256 runs the decode GEMV on 16-row
+ * chunks of x (the full chunks in grouped launches of up to 8, the rest in one more) when
+ * the prefill GEMM's grid of 128 x 256 tiles fits in one round (at most 2 workgroups per
+ * compute unit) and ceil(m/16) * n < 73728: then each chunk streams the weight faster
+ * than the under-filled GEMM covers it.  Otherwise the prefill GEMM kernel runs.  Every
+ * path meets the same accuracy bound. */
 q4_status q4_w4a16_gemm(const void* x, q4_dtype x_dtype, int64_t m,
                         const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros,
                         int64_t n, int64_t k, int32_t group_size, int32_t symmetric,

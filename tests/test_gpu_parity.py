@@ -287,7 +287,7 @@ def test_linear_tiny_reference(sym, m):
     note(f"linear tiny m={m} sym={sym}")
     p, _ = pack_guarded(w.to(DEV), 128, sym)
     y, kname = run_linear(x, p)
-    assert kname in (gemv_kernels() if m <= 16 else {"q4_gemm_mfma_bf16"})
+    assert kname in matmul_kernels(m, 256)
     packed = assert_pack_exact(p, host_input(w), 128, sym)
     assert_linear_close(y, host_input(x), packed, 256, 512, 128, sym, what=kname)
 
@@ -545,14 +545,30 @@ def test_gemm_grouped_one_by_one(m, k, g):
                             what="grouped")
 
 
-GEMM_CASES = [(17, 64, 256, 128), (130, 200, 384, 64), (300, 129, 96, 32), (256, 256, 1024, 128),
-              (129, 1000, 4096 + 64, 64), (64, 48, 11008, 128)]
+def gemm_path(m, n, num_cus=256):
+    """Mirror of the C ABI's choice for 16 < m: the GEMV on 16-row chunks (m <= 256) when
+    the GEMM's grid (128 x 256 tiles) fits in one round and ceil(m/16) * n < 73728."""
+    chunks = -(-m // 16)
+    gemm_wgs = -(-m // 128) * -(-n // 256)
+    chunked = m <= 256 and gemm_wgs <= 2 * num_cus and chunks * n < 72 * 1024
+    return not chunked
+
+
+def matmul_kernels(m, n, xdtype=torch.bfloat16):
+    gemm = {"q4_gemm_mfma_f16" if xdtype == torch.float16 else "q4_gemm_mfma_bf16"}
+    return gemm if m > 16 and gemm_path(m, n) else gemv_kernels(xdtype)
+
+
+# the prefill GEMM itself, also at small m where the grid is wide (n large)
+GEMM_CASES = [(17, 40960, 256, 128), (130, 8200, 384, 64), (300, 129, 96, 32), (256, 8192, 1024, 128),
+              (129, 8448, 4096 + 64, 64), (64, 20480, 512, 32), (257, 300, 512, 128), (128, 11008, 1024, 64)]
 
 
 @pytest.mark.parametrize("m,n,k,g", GEMM_CASES)
 @pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
 @pytest.mark.parametrize("sym", [False, True])
 def test_gemm_cases(m, n, k, g, xdtype, sym):
+    assert gemm_path(m, n)
     w = torch.from_numpy(pins.random_weights(m + n + k, max(n, 12), k)[:n])
     x = synthetic.activations(m, k, seed=m + 7 * k).to(xdtype)
     note(f"gemm m={m} n={n} k={k} g={g} {xdtype} sym={sym}")
@@ -560,7 +576,34 @@ def test_gemm_cases(m, n, k, g, xdtype, sym):
     y, kname = run_linear(x, p)
     assert kname == ("q4_gemm_mfma_f16" if xdtype == torch.float16 else "q4_gemm_mfma_bf16")
     packed = assert_pack_exact(p, host_input(w), g, sym)
-    assert_linear_close(y, host_input(x), packed, n, k, g, sym, what=kname)
+    # wide shapes: every activation row against a seeded sample of 200 weight rows
+    cols = None if m * n * k <= 1 << 28 else synthetic.sample_rows(n, 200, 3).numpy()
+    assert_linear_close(y, host_input(x), packed, n, k, g, sym, cols=cols, what=kname)
+
+
+# 16 < m <= 256 on narrow grids: the GEMV on 16-row chunks (full chunks grouped by up to 8,
+# the rest alone), including m = 17 (one full chunk and one row), multiples of 16, and
+# m > 128 (two grouped launches)
+MIDM_CASES = [(17, 64, 256, 128), (64, 48, 11008, 128), (40, 1000, 4096, 64), (128, 300, 1024, 32),
+              (33, 4096, 11008, 128), (96, 11008, 4096, 128), (112, 5, 512, 64), (256, 300, 1024, 128),
+              (200, 4096, 11008, 128), (145, 64, 256, 32), (32, 28672, 1024, 128)]
+
+
+@pytest.mark.parametrize("m,n,k,g", MIDM_CASES)
+@pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("sym", [False, True])
+def test_midm_chunked_cases(m, n, k, g, xdtype, sym):
+    assert not gemm_path(m, n)
+    w = torch.from_numpy(pins.random_weights(m + n + k, max(n, 12), k)[:n])
+    x = synthetic.activations(m, k, seed=m + 7 * k).to(xdtype)
+    note(f"mid-m chunked m={m} n={n} k={k} g={g} {xdtype} sym={sym}")
+    p, _ = pack_guarded(w.to(DEV), g, sym)
+    y, kname = run_linear(x, p)
+    assert kname in gemv_kernels(xdtype)
+    packed = assert_pack_exact(p, host_input(w), g, sym)
+    # large shapes: every activation row against a seeded sample of 200 weight rows
+    cols = None if n * k <= 1 << 24 else synthetic.sample_rows(n, 200, 5).numpy()
+    assert_linear_close(y, host_input(x), packed, n, k, g, sym, cols=cols, what=kname)
 
 
 def test_gemm_prefill_70b_sampled():

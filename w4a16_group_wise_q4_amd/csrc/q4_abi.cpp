@@ -1,7 +1,8 @@
 // q4_abi.cpp — the C ABI of libq4 (declared in include/q4.h).
 //
 // Validates every argument on the host before anything is enqueued, picks the kernel
-// (decode GEMV for m <= 16, prefill GEMM otherwise), launches it on the caller's stream
+// (decode GEMV for m <= 16, the GEMV on 16-row chunks for narrow grids up to m = 256,
+// prefill GEMM otherwise), launches it on the caller's stream
 // and records the launched kernel's name per thread, so a caller can check which kernel
 // ran ("LLM Quantization: GPTQ·AWQ·SmoothQuant·FP8·KV Cache (7/10)", §Silent Fallback:
 // verify the selected kernel and that nothing fell back).  There is no fallback path.
@@ -130,6 +131,64 @@ q4_status q4_dequant(const uint32_t* qweight, const uint16_t* scales, const uint
 }
 
 namespace {
+// Compute units of the current device (cached per device; 256 if the query fails).
+int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int c = 0;
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+            c = 256;
+        cus[dev] = c;
+    }
+    return cus[dev];
+}
+
+// One W4A16 product, validated.  m <= 16: the decode GEMV.  16 < m <= 256: the GEMV on
+// 16-row chunks of x sharing the weight (full chunks in grouped launches of up to 8, the
+// rest alone) when that is faster than the prefill GEMM, else the GEMM.  A GEMM grid of
+// 128 x 256 tiles that fits in one round (at most 2 workgroups per CU) takes about
+// k x 20.7 ns on MI355X whatever m and n, while each chunk streams the n x k/2 bytes of
+// codes at about 1.7 TB/s; so the chunks win while chunks x n stays under about 72K rows.
+// ([FL7] §Batch와 Context에 따라 속도가 달라진다: decode batches sit between the
+// bandwidth-bound and the compute-bound regime.)
+bool chunked_gemv(int64_t m, int64_t n, int cus) {
+    if (m <= 16 || m > 256) return false;
+    const int64_t chunks = (m + 15) / 16;
+    const int64_t gemm_wgs = ((m + 127) / 128) * ((n + 255) / 256);
+    return gemm_wgs <= 2 * (int64_t)cus && chunks * n < 72 * 1024;
+}
+
+hipError_t run_product(const void* x, int xd, int64_t m, const uint32_t* qw, const uint16_t* sc,
+                       const uint32_t* zr, int64_t n, int64_t k, int g, int sym, float* y,
+                       hipStream_t st, const char** name) {
+    if (m <= 16) return q4k_gemv(x, xd, (int)m, qw, sc, zr, n, k, g, sym, y, st, name);
+    if (!chunked_gemv(m, n, device_cus())) return q4k_gemm(x, xd, m, qw, sc, zr, n, k, g, sym, y, st, name);
+    const int64_t full = m / 16, rem = m % 16;
+    const uint16_t* xs = static_cast<const uint16_t*>(x);
+    for (int64_t c0 = 0; c0 < full; c0 += q4::kMaxGroup) {
+        const int64_t cnt = full - c0 < q4::kMaxGroup ? full - c0 : q4::kMaxGroup;
+        q4::GemvProblem gp[q4::kMaxGroup];
+        for (int64_t c = 0; c < cnt; ++c)
+            gp[c] = q4::GemvProblem{xs + (c0 + c) * 16 * k, qw, sc, zr, y + (c0 + c) * 16 * n, (int)n, 0};
+        hipError_t e = hipErrorNotSupported;
+        if (cnt > 1) e = q4k_gemv_grouped(gp, (int)cnt, xd, 16, k, g, sym, st, name);
+        if (e == hipErrorNotSupported) {
+            for (int64_t c = 0; c < cnt; ++c) {
+                e = q4k_gemv(gp[c].x, xd, 16, qw, sc, zr, n, k, g, sym, gp[c].y, st, name);
+                if (e != hipSuccess) return e;
+            }
+        } else if (e != hipSuccess) {
+            return e;
+        }
+    }
+    if (rem > 0)
+        return q4k_gemv(xs + full * 16 * k, xd, (int)rem, qw, sc, zr, n, k, g, sym, y + full * 16 * n, st,
+                        name);
+    return hipSuccess;
+}
+
 // The size, dtype, pointer and alignment rules of q4_w4a16_gemm for one problem.
 q4_status check_matmul(const void* x, q4_dtype x_dtype, int64_t m, const uint32_t* qweight,
                        const uint16_t* scales, const uint32_t* zeros, int64_t n, int64_t k,
@@ -170,15 +229,11 @@ q4_status q4_w4a16_gemm_grouped(const q4_gemm_problem* problems, int32_t count,
                                               symmetric ? 1 : 0, stream, &name);
         if (e != hipErrorNotSupported) return finish(e, name);
     }
-    for (int32_t i = 0; i < count; ++i) {  // one launch per problem
+    for (int32_t i = 0; i < count; ++i) {  // one product at a time
         const q4_gemm_problem& p = problems[i];
-        hipError_t e;
-        if (m <= 16)
-            e = q4k_gemv(p.x, (int)x_dtype, (int)m, p.qweight, p.scales, p.zeros, p.n, k, group_size,
-                         symmetric ? 1 : 0, p.y, stream, &name);
-        else
-            e = q4k_gemm(p.x, (int)x_dtype, m, p.qweight, p.scales, p.zeros, p.n, k, group_size,
-                         symmetric ? 1 : 0, p.y, stream, &name);
+        const hipError_t e = run_product(p.x, (int)x_dtype, m, p.qweight, p.scales,
+                                         symmetric ? nullptr : p.zeros, p.n, k, group_size,
+                                         symmetric ? 1 : 0, p.y, stream, &name);
         if (e != hipSuccess) return Q4_ERR_LAUNCH;
     }
     return finish(hipSuccess, name);
@@ -191,13 +246,8 @@ q4_status q4_w4a16_gemm(const void* x, q4_dtype x_dtype, int64_t m, const uint32
                                       symmetric, y);
     if (st != Q4_OK) return st;
     const char* name = "";
-    hipError_t e;
-    if (m <= 16)
-        e = q4k_gemv(x, (int)x_dtype, (int)m, qweight, scales, zeros, n, k, group_size,
-                     symmetric ? 1 : 0, y, stream, &name);
-    else
-        e = q4k_gemm(x, (int)x_dtype, m, qweight, scales, zeros, n, k, group_size,
-                     symmetric ? 1 : 0, y, stream, &name);
+    const hipError_t e = run_product(x, (int)x_dtype, m, qweight, scales, symmetric ? nullptr : zeros, n,
+                                     k, group_size, symmetric ? 1 : 0, y, stream, &name);
     return finish(e, name);
 }
 
