@@ -545,3 +545,120 @@ ALL_CHECKS = [check_golden_groups, check_fp16_conversion, check_invariants,
               check_brute_force_nearest, check_levels_and_bytes, check_dequant_closed_forms,
               check_linear, check_argument_rejection, check_mse_brute_force,
               check_mse_rtn_limit, check_kv_cache_placement, check_kv_attention]
+
+
+# --------------------------------------------------------------------------- GPTQ
+
+def _gptq_x(seed, t, k, rank=8):
+    """Correlated calibration tokens: N(0,1) plus a few shared factors."""
+    rng = np.random.default_rng(seed)
+    f = rng.standard_normal((t, rank))
+    b = rng.standard_normal((k, rank)) / np.sqrt(rank)
+    return (rng.standard_normal((t, k)) + 1.5 * f @ b.T).astype(np.float32)
+
+
+def check_gptq_hessian(gq, o):
+    """H = 2 X^T X (numpy's fp64 matmul), the diagonal scaled by 1 + 0.01, a dead feature's
+    diagonal 1 + 0.01 and its row and column zero."""
+    x = _gptq_x(60, 50, 32)
+    x[:, 5] = 0
+    h = gq.hessian(x)
+    ref = 2.0 * x.astype(np.float64).T @ x.astype(np.float64)
+    off = ~np.eye(32, dtype=bool)
+    assert np.allclose(h[off], ref[off], rtol=1e-13, atol=1e-12)
+    d = np.diag(ref).copy()
+    d[5] = 1.0
+    assert np.allclose(np.diag(h), d * 1.01, rtol=1e-13)
+    assert np.all(h[5, off[5]] == 0) and np.all(h[off[:, 5], 5] == 0)
+
+
+def check_gptq_identity_is_rtn(gq, o):
+    """With H a multiple of the identity nothing propagates: GPTQ is RTN, bit for bit."""
+    for g, sym in [(32, False), (128, True), (64, False)]:
+        w = random_weights(61 + g, 12, 256)
+        qg, sg, zg = gq.gptq_quantize(w, 3.7 * np.eye(256), g, sym, oracle=o)
+        qr, sr, zr = o.quantize_pack(w, g, sym)
+        assert np.array_equal(qg, qr) and np.array_equal(sg, sr)
+        if not sym:
+            assert np.array_equal(zg, zr)
+
+
+def check_gptq_pair_closed_form(gq, o):
+    """Only features 0 and 1 coupled, H = [[a, b], [b, c]] (+ identity elsewhere): column
+    1 is quantized at w_1 + (w_0 - w_hat_0) b / c (the one-step optimal update), every
+    other column as RTN."""
+    n, k, g = 48, 64, 32
+    w = random_weights(62, n, k)
+    a, b, c = 2.0, 1.2, 1.3
+    h = np.eye(k)
+    h[0, 0], h[0, 1], h[1, 0], h[1, 1] = a, b, b, c
+    for sym in (False, True):
+        qg, sg, zg = gq.gptq_quantize(w, h, g, sym, oracle=o)
+        qr, _, zr = o.quantize_pack(w, g, sym)
+        cg, cr = unpack_codes(qg, k), unpack_codes(qr, k)
+        assert np.array_equal(cg[:, 2:], cr[:, 2:]) and np.array_equal(cg[:, 0], cr[:, 0])
+        s0 = f16_values(sg)[:, 0]
+        z0 = np.full(n, 8) if sym else unpack_zeros(zr, k // g)[:, 0]
+        w64 = w.astype(np.float64)
+        w_hat0 = s0 * (cr[:, 0] - z0)
+        w1 = w64[:, 1] + (w64[:, 0] - w_hat0) * b / c
+        u1 = np.clip(np.rint(w1 / s0) + z0, 0, 15)
+        assert np.array_equal(cg[:, 1], u1), (sym, cg[:, 1], u1)
+        assert not np.array_equal(cg[:, 1], cr[:, 1]), "the pair should change a code"
+
+
+def check_gptq_block_and_scale_invariance(gq, o):
+    """Blocks of 128 with the lazy update give the same codes as one block; scaling H by
+    a constant changes nothing."""
+    k = 384
+    x = _gptq_x(63, 600, k)
+    h = gq.hessian(x)
+    w = random_weights(64, 12, k)
+    q1, _, _ = gq.gptq_quantize(w, h, 64, False, oracle=o)
+    q2, _, _ = gq.gptq_quantize(w, h, 64, False, block=k, oracle=o)
+    q3, _, _ = gq.gptq_quantize(w, 7.25 * h, 64, False, oracle=o)
+    assert np.array_equal(q1, q2)
+    assert np.array_equal(q1, q3)
+
+
+def check_gptq_upper_factor_form(gq, o):
+    """An independent formulation: with H = U U^T (U upper, the Cholesky factor of H in
+    reversed order), column j is quantized at w_j + sum_{i<j} (w_i - w_hat_i) U_ij / U_jj.
+    No inverse is taken; the codes must equal the oracle's."""
+    n, k, g = 12, 128, 32
+    x = _gptq_x(65, 400, k)
+    h = gq.hessian(x)
+    w = random_weights(66, n, k)
+    qg, sg, zg = gq.gptq_quantize(w, h, g, False, oracle=o)
+    rev = np.linalg.cholesky(h[::-1, ::-1])          # J H J = R R^T, R lower
+    U = rev[::-1, ::-1]                               # H = U U^T, U upper
+    s = f16_values(sg)
+    z = unpack_zeros(zg, k // g)
+    w64 = w.astype(np.float64)
+    codes = np.zeros((n, k), dtype=np.int64)
+    d = np.zeros((n, k))
+    for j in range(k):
+        wj = w64[:, j] + (d[:, :j] @ U[:j, j]) / U[j, j]
+        u = np.clip(np.rint(wj / s[:, j // g]) + z[:, j // g], 0, 15)
+        codes[:, j] = u
+        d[:, j] = w64[:, j] - s[:, j // g] * (u - z[:, j // g])
+    assert np.array_equal(unpack_codes(qg, k), codes)
+
+
+def check_gptq_lowers_layer_error(gq, o):
+    """On correlated calibration data GPTQ's layer-output error is below RTN's."""
+    k, g = 256, 64
+    x = _gptq_x(67, 1000, k)
+    h = gq.hessian(x)
+    w = random_weights(68, 24, k)[12:]   # the Gaussian-like rows
+    for sym in (False, True):
+        qg, sg, zg = gq.gptq_quantize(w, h, g, sym, oracle=o)
+        qr, sr, zr = o.quantize_pack(w, g, sym)
+        eg = gq.layer_error(w, o.dequant(qg, sg, zg, 12, k, g, sym), x)
+        er = gq.layer_error(w, o.dequant(qr, sr, zr, 12, k, g, sym), x)
+        assert eg < 0.9 * er, (sym, eg, er)
+
+
+GPTQ_CHECKS = [check_gptq_hessian, check_gptq_identity_is_rtn, check_gptq_pair_closed_form,
+               check_gptq_block_and_scale_invariance, check_gptq_upper_factor_form,
+               check_gptq_lowers_layer_error]
