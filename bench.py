@@ -20,6 +20,8 @@ Algorithmic bytes (what the method must move, nothing else):
                      + 2*m*k (x, bf16) + 4*m*n (y, fp32)
   GEMM   2*m*n*k flop against the bf16 dense MFMA peak
   quantize per weight: 2 (bf16 read) + 0.5 (codes); per group 2 (scale) + 0.5 (zero)
+  GPTQ     fp32 work: k^2 * tokens (Hessian) + k^3/3 (Cholesky) + n * k^2 (updates), against the
+           fp32 vector peak (78.6 TFLOP/s without packed math)
   KV attention per layer: both INT4 caches over the context (per token and head
                      d/2 codes + 2*d/g scale bytes + 4*ceil(d/g/8) zero-word bytes, each),
                      q (bf16), out (fp32)
@@ -168,6 +170,40 @@ def kv_leg(q4, synthetic, torch, dev, layers=32):
     }
 
 
+def gptq_leg(q4, synthetic, torch, dev, tokens=2048):
+    """GPTQ of the 7B-like up projection [11008 x 4096] against 2048 synthetic calibration
+    tokens (N(0,1) plus 8 shared factors), g128 sym (the pages' GPTQ setting)."""
+    mat = synthetic.MLP_SWEEP["mats"][0]
+    n, k, g = mat.n, mat.k, 128
+    w = mat.make().to(dev)
+    gen = torch.Generator().manual_seed(300)
+    f = torch.randn((tokens, 8), generator=gen)
+    b = torch.randn((k, 8), generator=gen) / 8 ** 0.5
+    x = (torch.randn((tokens, k), generator=gen) + 1.5 * f @ b.T).to(torch.bfloat16).to(dev)
+    ws = torch.empty(q4.q4_gptq_workspace(n, k, g), dtype=torch.uint8, device=dev)
+    p = q4.q4_gptq_quantize(w, x, g, True, workspace=ws)
+    torch.cuda.synchronize()
+    kname = q4.q4_last_kernel()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 3
+    e0.record()
+    for _ in range(reps):
+        q4.q4_gptq_quantize(w, x, g, True, out=p, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    # fp32 work: Hessian lower triangle, Cholesky, error-feedback updates
+    flops = k * k * tokens + k ** 3 / 3 + n * k * k
+    r = q4.q4_quantize_pack(w, g, True)
+    xf = x.float()
+    wf = w.float()
+    err = lambda pk: float(((xf @ (wf - q4.q4_dequant(pk)).t()) ** 2).sum())
+    return {"workload": f"GPTQ of W [{n}x{k}] bf16, {tokens} calibration tokens, g{g} sym",
+            "kernel": kname, "ms": round(ms, 3), "tflops_fp32": round(flops / (ms * 1e-3) / 1e12, 2),
+            "frac_fp32_vector": round(flops / (ms * 1e-3) / 1e12 / 78.6, 4),
+            "layer_error_vs_rtn": round(err(p) / err(r), 4)}
+
+
 def cpu_baseline(seconds=12.0):
     """The CPU oracle (plain scalar C, one thread) on a bounded sample of the decode
     workload: full fp64 passes over both projections at M=1."""
@@ -202,7 +238,7 @@ def main():
     ap.add_argument("--steps", type=int, default=340)
     ap.add_argument("--warmup", type=int, default=34)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--legs", default="gemm,quant,sweep,mlp,mse,kv,midm",
+    ap.add_argument("--legs", default="gemm,quant,sweep,mlp,mse,kv,midm,gptq",
                     help="comma list of legs besides the headline decode GEMV")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy 5 times (the "
@@ -349,6 +385,10 @@ def main():
     # ------------------------------------------------------------ INT4 KV cache (decode attention)
     if "kv" in legs:
         out["kv_cache"] = kv_leg(q4, synthetic, torch, dev)
+
+    # ------------------------------------------------------------ GPTQ (one 7B-shaped layer)
+    if "gptq" in legs:
+        out["gptq"] = gptq_leg(q4, synthetic, torch, dev)
 
     # ------------------------------------------------------------ mid-M (17..256) products
     if "midm" in legs:

@@ -216,6 +216,30 @@ q4_status q4_kv_attention(const void* q, q4_dtype q_dtype, int64_t heads, int64_
                           float* out, void* workspace, int64_t workspace_bytes,
                           hipStream_t stream);
 
+/* ---- GPTQ ([QA1] GPTQ chapter: §Hessian 정의, §OBQ single-step 수식, §GPTQ block-wise,
+ * §알고리즘 개요, §설정 grid; [FL7] §GPTQ: Approximate Second-order Weight Quantization).
+ * Quantize W [n][k] (F32, F16 or BF16) into the packed format with the quantization
+ * error of each column carried into the columns not yet quantized, weighted by the
+ * calibration Hessian H = 2 X^T X of x [tokens][k] (F16 or BF16 activations):
+ *   - the group scales and zero points are q4_quantize_pack's on the original W (fixed
+ *     before the sweep, "static groups"; the format's groups are g consecutive columns);
+ *   - H's diagonal is scaled by 1 + damp (the pages use damp = 0.01); a zero diagonal entry
+ *     (a feature never active) becomes 1 first; 0 < damp <= 1;
+ *   - columns are taken in order; column j is quantized at w_j + sum_{i<j} d_i U_ij / U_jj,
+ *     d_i = w_i - w_hat_i, H = U U^T with U upper triangular: the pages' update
+ *     err_j = (w'_j - w_hat_j) / L_jj, w'_l -= err_j L_jl with H^-1 = L^T L, without the
+ *     inverse.
+ * All arithmetic is fp32 (Hessian, Cholesky factor, updates); a code can differ from an
+ * exact-arithmetic sweep where the updated weight falls within rounding of a code
+ * boundary.  workspace: device memory of at least q4_gptq_workspace(n, k, group_size)
+ * bytes (k*k + n*k + 64*n floats), 16-byte aligned, contents ignored; k <= 32768.  Other
+ * rules as q4_quantize_pack; x 16-byte aligned.  Runs about 5k/64 kernels on `stream`. */
+int64_t q4_gptq_workspace(int64_t n, int64_t k, int32_t group_size);
+q4_status q4_gptq_quantize(const void* w, q4_dtype w_dtype, int64_t n, int64_t k, const void* x,
+                           q4_dtype x_dtype, int64_t tokens, int32_t group_size, int32_t symmetric,
+                           float damp, uint32_t* qweight, uint16_t* scales, uint32_t* zeros,
+                           void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
 /* Element counts of the three packed arrays (payload + metadata, [FL7] §Memory 계산은
  * Payload와 Metadata로 나눈다): n*k/8 words, n*(k/g) scales, n*ceil((k/g)/8) words.
  * Return -1 for arguments the entry points would reject. */

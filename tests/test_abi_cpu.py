@@ -261,3 +261,28 @@ def test_kv_attention_workspace_size():
     assert lib.q4_kv_attention_workspace(32, 96, 4096) == -1
     assert lib.q4_kv_attention_workspace(0, 128, 4096) == -1
     assert lib.q4_kv_attention_workspace(4, 128, 0) == -1
+
+
+def _gq(w=A16, wd=BF16, n=16, k=256, x=A16, xd=BF16, tokens=64, g=128, sym=0, damp=0.01, qw=A16, sc=A16,
+        zr=A16, ws=A16, ws_bytes=1 << 40):
+    return q4.lib().q4_gptq_quantize(w, wd, n, k, x, xd, tokens, g, sym, damp, qw, sc, zr, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("call,code", [
+    (lambda: _gq(g=16), GROUP), (lambda: _gq(k=200), SHAPE), (lambda: _gq(tokens=0), SHAPE),
+    (lambda: _gq(k=32768 + 128), SHAPE), (lambda: _gq(damp=0.0), SHAPE), (lambda: _gq(damp=-1.0), SHAPE),
+    (lambda: _gq(damp=float("nan")), SHAPE), (lambda: _gq(damp=2.0), SHAPE), (lambda: _gq(xd=F32), DTYPE),
+    (lambda: _gq(wd=7), DTYPE), (lambda: _gq(x=None), NULL), (lambda: _gq(ws=None), NULL),
+    (lambda: _gq(w=None), NULL), (lambda: _gq(zr=None), NULL), (lambda: _gq(x=A16 + 2), ALIGN),
+    (lambda: _gq(ws=A16 + 4), ALIGN), (lambda: _gq(ws_bytes=1024), SHAPE),
+])
+def test_gptq_validation_rejects_before_launch(call, code):
+    assert call() == code
+    assert q4.q4_last_kernel() == ""
+
+
+def test_gptq_workspace_size():
+    lib = q4.lib()
+    assert lib.q4_gptq_workspace(11008, 4096, 128) == 4 * (4096 * 4096 + 11008 * 4096 + 64 * 11008)
+    assert lib.q4_gptq_workspace(16, 200, 32) == -1
+    assert lib.q4_gptq_workspace(16, 32768 + 128, 128) == -1

@@ -12,6 +12,7 @@ Entry points (same names as the C ABI):
     q4_w4a16_gemm_grouped(xs, packs)                    -> [y_i], one launch when m <= 16
     q4_kv_quantize(kv, cache, t0)                       -> appends tokens to a KvCache
     q4_kv_attention(q, kcache, vcache, n_tok, scale)    -> out [heads, d] fp32
+    q4_gptq_quantize(w, x, group_size, symmetric)       -> PackedWeight (GPTQ codes)
     q4_last_kernel()                                    -> name of the last kernel run
 """
 from __future__ import annotations
@@ -30,6 +31,7 @@ __all__ = ["PackedWeight", "q4_quantize_pack", "q4_quantize_pack_grouped", "q4_q
            "q4_w4a16_gemm",
            "q4_w4a16_gemm_grouped", "q4_last_kernel", "KvCache", "empty_kv_cache",
            "q4_kv_quantize", "q4_kv_attention", "q4_kv_attention_workspace",
+           "q4_gptq_quantize", "q4_gptq_workspace",
            "q4_qweight_words", "q4_scale_count", "q4_zero_words", "q4_layout_version",
            "library_path", "Q4Error"]
 
@@ -39,7 +41,8 @@ _DTYPE_CODE = {torch.float32: Q4_F32, torch.float16: Q4_F16, torch.bfloat16: Q4_
 EXPORTED = ("q4_quantize_pack", "q4_quantize_pack_grouped", "q4_quantize_pack_mse", "q4_dequant",
             "q4_w4a16_gemm",
             "q4_w4a16_gemm_grouped", "q4_kv_quantize", "q4_kv_attention",
-            "q4_kv_attention_workspace", "q4_qweight_words",
+            "q4_kv_attention_workspace", "q4_gptq_quantize", "q4_gptq_workspace",
+            "q4_qweight_words",
             "q4_scale_count", "q4_zero_words", "q4_status_str", "q4_last_kernel",
             "q4_layout_version")
 
@@ -104,6 +107,11 @@ def _load():
     lib.q4_kv_attention.argtypes = [vp, ctypes.c_int, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp,
                                     i32, i32, ctypes.c_float, vp, vp, i64, vp]
     lib.q4_kv_attention.restype = ctypes.c_int
+    lib.q4_gptq_workspace.argtypes = [i64, i64, i32]
+    lib.q4_gptq_workspace.restype = i64
+    lib.q4_gptq_quantize.argtypes = [vp, ctypes.c_int, i64, i64, vp, ctypes.c_int, i64, i32, i32,
+                                     ctypes.c_float, vp, vp, vp, vp, i64, vp]
+    lib.q4_gptq_quantize.restype = ctypes.c_int
     lib.q4_qweight_words.argtypes = [i64, i64]
     lib.q4_qweight_words.restype = i64
     lib.q4_scale_count.argtypes = [i64, i64, i32]
@@ -370,3 +378,34 @@ def q4_kv_attention(q: torch.Tensor, kcache: KvCache, vcache: KvCache, n_tok: in
         kcache.group_size, int(kcache.symmetric), float(scale), _dev_ptr(out),
         _dev_ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q)))
     return out
+
+
+# ------------------------------------------------------------------ GPTQ
+
+def q4_gptq_workspace(n: int, k: int, group_size: int) -> int:
+    return int(_load().q4_gptq_workspace(n, k, group_size))
+
+
+def q4_gptq_quantize(w: torch.Tensor, x: torch.Tensor, group_size: int = 128,
+                     symmetric: bool = False, damp: float = 0.01,
+                     out: Optional[PackedWeight] = None,
+                     workspace: Optional[torch.Tensor] = None) -> PackedWeight:
+    """GPTQ-quantize W [n, k] (fp32 / fp16 / bf16) against calibration activations
+    x [tokens, k] (fp16 / bf16); same packed format, RTN's group scales and zero points."""
+    _need_cuda("w", w)
+    _need_cuda("x", x)
+    if w.dim() != 2 or w.dtype not in _DTYPE_CODE:
+        raise ValueError("w must be a 2-D fp32, fp16 or bf16 tensor")
+    if x.dim() != 2 or x.dtype not in (torch.float16, torch.bfloat16) or x.shape[1] != w.shape[1]:
+        raise ValueError("x must be a 2-D fp16 or bf16 tensor [tokens, k]")
+    n, k = w.shape
+    p = out if out is not None else empty_packed(n, k, group_size, symmetric, w.device)
+    need = q4_gptq_workspace(n, k, group_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=w.device)
+    _check(_load().q4_gptq_quantize(_dev_ptr(w), _DTYPE_CODE[w.dtype], n, k, _dev_ptr(x),
+                                    _DTYPE_CODE[x.dtype], x.shape[0], group_size,
+                                    int(bool(symmetric)), float(damp), _dev_ptr(p.qweight),
+                                    _dev_ptr(p.scales), _dev_ptr(p.zeros), _dev_ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(w)))
+    return p

@@ -67,15 +67,6 @@ __device__ __forceinline__ float wave_max(float v) {
     v = fmaxf(v, across16(v));
     return fmaxf(v, across32(v));
 }
-__device__ __forceinline__ float wave_sum(float v) {
-    v += xor1(v);
-    v += xor2(v);
-    v += ror4(v);
-    v += ror8(v);
-    v += across16(v);
-    return v + across32(v);
-}
-
 // Sum over the LPT consecutive lanes of one token (lanes tl * LPT .. + LPT - 1).
 template <int LPT>
 __device__ __forceinline__ float token_sum(float v) {

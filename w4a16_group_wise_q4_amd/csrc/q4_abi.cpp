@@ -318,6 +318,34 @@ q4_status q4_kv_attention(const void* q, q4_dtype q_dtype, int64_t heads, int64_
     return finish(e, name);
 }
 
+namespace {
+constexpr int64_t kMaxGptqK = 32768;   // the k x k Hessian: at most 4 GiB of fp32
+}  // namespace
+
+int64_t q4_gptq_workspace(int64_t n, int64_t k, int32_t group_size) {
+    if (check_layout(n, k, group_size) != Q4_OK || k > kMaxGptqK) return -1;
+    return q4k_gptq_workspace_floats(n, k) * (int64_t)sizeof(float);
+}
+
+q4_status q4_gptq_quantize(const void* w, q4_dtype w_dtype, int64_t n, int64_t k, const void* x,
+                           q4_dtype x_dtype, int64_t tokens, int32_t group_size, int32_t symmetric,
+                           float damp, uint32_t* qweight, uint16_t* scales, uint32_t* zeros,
+                           void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+    q4_status st = check_quant(w, w_dtype, n, k, group_size, symmetric, qweight, scales, zeros);
+    if (st != Q4_OK) return st;
+    if (k > kMaxGptqK || tokens < 1 || tokens > kMaxDim || tokens > kMaxElems / k) return Q4_ERR_SHAPE;
+    if (!(damp > 0.0f) || !(damp <= 1.0f)) return Q4_ERR_SHAPE;
+    if (x_dtype != Q4_F16 && x_dtype != Q4_BF16) return Q4_ERR_DTYPE;
+    if (!x || !workspace) return Q4_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(workspace, 16)) return Q4_ERR_ALIGN;
+    if (workspace_bytes < q4_gptq_workspace(n, k, group_size)) return Q4_ERR_SHAPE;
+    const char* name = "";
+    const hipError_t e = q4k_gptq(w, (int)w_dtype, n, k, x, (int)x_dtype, tokens, group_size,
+                                  symmetric ? 1 : 0, damp, qweight, scales, symmetric ? nullptr : zeros,
+                                  static_cast<float*>(workspace), stream, &name);
+    return finish(e, name);
+}
+
 int64_t q4_qweight_words(int64_t n, int64_t k) {
     if (n < 1 || k < 1 || k % 8 != 0) return -1;
     return n * (k / 8);

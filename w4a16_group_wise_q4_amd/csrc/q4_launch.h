@@ -77,3 +77,9 @@ hipError_t q4k_gemv_grouped(const q4::GemvProblem* problems, int count, int x_dt
 hipError_t q4k_gemm(const void* x, int x_dtype, int64_t m, const uint32_t* qweight,
                     const uint16_t* scales, const uint32_t* zeros, int64_t n, int64_t k, int g,
                     int sym, float* y, hipStream_t stream, const char** kname);
+// GPTQ error-feedback quantization (static RTN group quantizers, codes chosen against the
+// calibration Hessian); workspace: k*k + n*k + 64*n floats.
+int64_t q4k_gptq_workspace_floats(int64_t n, int64_t k);
+hipError_t q4k_gptq(const void* w, int w_dtype, int64_t n, int64_t k, const void* x, int x_dtype,
+                    int64_t tokens, int g, int sym, float damp, uint32_t* qweight, uint16_t* scales,
+                    uint32_t* zeros, float* workspace, hipStream_t stream, const char** kname);
