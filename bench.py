@@ -153,6 +153,29 @@ def kv_leg(q4, synthetic, torch, dev, layers=32):
     t_att = graph_ms(capture(att), 5) / layers * 1e-3
     cache = kv_cache_bytes(H, T, D, g)
     att_bytes = 2 * cache + H * D * 2 + H * D * 4
+    del kcs, vcs, outs, ws
+    # batched decode: 16 sequences of the same length, their heads side by side (512 heads),
+    # 4 layers (1.3 GB of caches, past the Infinity Cache)
+    B, LB = 16, 4
+    kb = synthetic.kv_tokens(T, B * H, D, ck["k_seed"] + 10, "k").to(dev)
+    vb = synthetic.kv_tokens(T, B * H, D, ck["v_seed"] + 10, "v").to(dev)
+    qb = synthetic.query(B * H, D, ck["q_seed"] + 10).to(dev)
+    kbs = [q4.empty_kv_cache(B * H, T, D, g, False, dev) for _ in range(LB)]
+    vbs = [q4.empty_kv_cache(B * H, T, D, g, False, dev) for _ in range(LB)]
+    for c in kbs:
+        q4.q4_kv_quantize(kb, c, 0)
+    for c in vbs:
+        q4.q4_kv_quantize(vb, c, 0)
+    del kb, vb
+    wsb = torch.empty(q4.q4_kv_attention_workspace(B * H, D, T), dtype=torch.uint8, device=dev)
+    ob = torch.empty((LB, B * H, D), dtype=torch.float32, device=dev)
+    attb = [lambda i=i: q4.q4_kv_attention(qb, kbs[i], vbs[i], T, scale, out=ob[i], workspace=wsb)
+            for i in range(LB)]
+    attb[0]()
+    torch.cuda.synchronize()
+    t_attb = graph_ms(capture(attb), 3) / LB * 1e-3
+    att_bytes_b = 2 * kv_cache_bytes(B * H, T, D, g) + B * H * D * 6
+    del kbs, vbs, ob, wsb
     fill_bytes = H * T * D * 2 + cache
     bf16_cache = 2 * H * T * D * 2
     return {
@@ -163,6 +186,9 @@ def kv_leg(q4, synthetic, torch, dev, layers=32):
                       "gbs": round(att_bytes / t_att / 1e9, 1),
                       "frac_hbm": round(att_bytes / t_att / 1e9 / HBM_PEAK_GBS, 4),
                       "cache_bytes_vs_bf16": round(2 * cache / bf16_cache, 4)},
+        "attention_batch16": {"heads": B * H, "us_per_layer": round(t_attb * 1e6, 2),
+                              "bytes_per_layer": att_bytes_b, "gbs": round(att_bytes_b / t_attb / 1e9, 1),
+                              "frac_hbm": round(att_bytes_b / t_attb / 1e9 / HBM_PEAK_GBS, 4)},
         "prefill_quantize": {"kernel": qname, "tokens": T, "us": round(t_fill * 1e6, 2),
                              "gbs": round(fill_bytes / t_fill / 1e9, 1),
                              "frac_hbm": round(fill_bytes / t_fill / 1e9 / HBM_PEAK_GBS, 4)},
