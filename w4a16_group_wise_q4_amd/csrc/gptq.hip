@@ -25,7 +25,7 @@
 //      trailing lower triangle.
 //   4. C = 0 (n x k accumulators of sum_{i<j} d_i U_ij).  For each block of 64 columns:
 //      the sweep (one lane per weight row, the block's 64 columns in order) writes the
-//      codes and the errors d of the block; the update adds d_block * U[block, later] to
+//      codes and the errors d of the block (column-major); the update adds d_block * U[block, later] to
 //      the accumulators of every later column.
 // Everything is fp32; the codes are the sweep's decisions in fp32 (the oracle's in fp64
 // may differ where a value falls within rounding of a code boundary).
@@ -36,24 +36,48 @@ namespace {
 constexpr int NB = 64;  // panel and block width
 
 // ------------------------------------------------------------ 64 x 64 fp32 tile products
-// out[r][c] (r, c < 64) += sum_{s < 64} X[r][s] * Y[c][s], with X and Y in LDS as [64][65]
-// (padded rows: conflict-free column reads).  Thread t of 256 owns rows 4 (t / 16) .. +3
-// and columns 4 (t % 16) .. +3.
-__device__ __forceinline__ void tile_fma(const float (*X)[65], const float (*Y)[65], float (&acc)[4][4]) {
+// out[r][c] (r, c < 64) += sum_{s < 64} X[s][r] * Y[s][c], with X and Y in LDS k-major
+// ([64][64]: a row of 64 values per s).  Thread t of 256 owns rows 4 (t / 16) .. +3 and
+// columns 4 (t % 16) .. +3: per s one 16-byte read of X (shared by 16 threads) and one of Y
+// (16 consecutive threads read 64 consecutive floats) feed 16 FMAs.
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void tile_fma(const float (*X)[NB], const float (*Y)[NB], float (&acc)[4][4]) {
     const int t = threadIdx.x;
     const int r0 = 4 * (t >> 4), c0 = 4 * (t & 15);
-#pragma unroll 4
+#pragma unroll 8
     for (int s = 0; s < NB; ++s) {
-        float xv[4], yv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            xv[i] = X[r0 + i][s];
-            yv[i] = Y[c0 + i][s];
-        }
+        const f32x4v xv = *reinterpret_cast<const f32x4v*>(&X[s][r0]);
+        const f32x4v yv = *reinterpret_cast<const f32x4v*>(&Y[s][c0]);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(xv[i], yv[j], acc[i][j]);
+    }
+}
+
+// out[r][c] (r, c < 64) += sum_{s < 64} X[r][s] * Y[c][s], with X and Y in LDS row-major at a
+// row stride of RS floats.  Thread t owns rows t / 16 + 16 i and columns t % 16 + 16 j
+// (i, j < 4): per 4 values of s, four 16-byte reads of X (4 addresses per wave, broadcast)
+// and four of Y (16 addresses per wave, RS apart: every bank once) feed 64 FMAs.
+constexpr int RS = NB + 4;
+
+__device__ __forceinline__ void tile_fma_rows(const float (*X)[RS], const float (*Y)[RS], float (&acc)[4][4]) {
+    const int t = threadIdx.x;
+    const int r = t >> 4, c = t & 15;
+#pragma unroll 2
+    for (int s = 0; s < NB; s += 4) {
+        f32x4v xv[4], yv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xv[i] = *reinterpret_cast<const f32x4v*>(&X[r + 16 * i][s]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) yv[j] = *reinterpret_cast<const f32x4v*>(&Y[c + 16 * j][s]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(xv[i][q], yv[j][q], acc[i][j]);
     }
 }
 
@@ -71,17 +95,17 @@ __global__ __launch_bounds__(256) void hessian_kernel(const uint16_t* __restrict
     const int tiles = (k + NB - 1) / NB;
     const int I = blockIdx.x / tiles, J = blockIdx.x % tiles;
     if (J > I) return;  // upper tiles: not needed (uniform)
-    __shared__ float Xs[NB][65], Ys[NB][65];
+    __shared__ __attribute__((aligned(16))) float Xs[NB][NB], Ys[NB][NB];
     const int t = threadIdx.x;
     float acc[4][4] = {};
     for (int t0 = 0; t0 < tokens; t0 += NB) {
-        // token slice [t0, t0 + 64): Xs[a][s] = x[t0 + s][k-1-(64 I + a)], Ys likewise for J
+        // token slice [t0, t0 + 64): Xs[s][a] = x[t0 + s][k-1-(64 I + a)], Ys likewise for J
         for (int e = t; e < NB * NB; e += 256) {
             const int s = e / NB, a = e % NB;
             const int tok = t0 + s;
             const int fa = k - 1 - (NB * I + a), fb = k - 1 - (NB * J + a);
-            Xs[a][s] = tok < tokens && fa >= 0 ? half_to_float<XF16>(x[(int64_t)tok * k + fa]) : 0.f;
-            Ys[a][s] = tok < tokens && fb >= 0 ? half_to_float<XF16>(x[(int64_t)tok * k + fb]) : 0.f;
+            Xs[s][a] = tok < tokens && fa >= 0 ? half_to_float<XF16>(x[(int64_t)tok * k + fa]) : 0.f;
+            Ys[s][a] = tok < tokens && fb >= 0 ? half_to_float<XF16>(x[(int64_t)tok * k + fb]) : 0.f;
         }
         __syncthreads();
         tile_fma(Xs, Ys, acc);
@@ -113,17 +137,18 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(float* __restrict__ A, i
         T[r][c] = r < bw && c <= r ? A[(int64_t)(j0 + r) * k + j0 + c] : 0.f;
     }
     __syncthreads();
+    // thread t updates row r = t % 64, columns s = t / 64, +4, ... of the trailing block
+    const int ur = t & 63, us = t >> 6;
     for (int c = 0; c < bw; ++c) {
-        if (t == 0) T[c][c] = sqrtf(T[c][c]);
+        const float d = sqrtf(T[c][c]);  // every thread: no barrier between the root and its use
+        __syncthreads();                 // all have read T[c][c] before it is overwritten
+        if (t == c) T[c][c] = d;
+        if (t > c && t < bw) T[t][c] = T[t][c] / d;
         __syncthreads();
-        const float d = T[c][c];
-        for (int r = c + 1 + t; r < bw; r += 256) T[r][c] = T[r][c] / d;
-        __syncthreads();
-        // T[r][s] -= T[r][c] T[s][c] for c < s <= r < bw
-        const int m = bw - c - 1;
-        for (int e = t; e < m * m; e += 256) {
-            const int r = c + 1 + e / m, s = c + 1 + e % m;
-            if (s <= r) T[r][s] = __builtin_fmaf(-T[r][c], T[s][c], T[r][s]);
+        if (ur > c && ur < bw) {
+            const float lr = T[ur][c];
+            for (int s2 = c + 1 + ((us - (c + 1)) & 3); s2 <= ur; s2 += 4)
+                T[ur][s2] = __builtin_fmaf(-lr, T[s2][c], T[ur][s2]);
         }
         __syncthreads();
     }
@@ -169,7 +194,7 @@ __global__ __launch_bounds__(256) void chol_update_kernel(float* __restrict__ A,
     const int tiles = (k - base + NB - 1) / NB;
     const int I = blockIdx.x / tiles, J = blockIdx.x % tiles;
     if (J > I) return;  // uniform
-    __shared__ float Xs[NB][65], Ys[NB][65];
+    __shared__ __attribute__((aligned(16))) float Xs[NB][RS], Ys[NB][RS];
     const int t = threadIdx.x;
     for (int e = t; e < NB * NB; e += 256) {
         const int r = e / NB, s = e % NB;
@@ -179,13 +204,12 @@ __global__ __launch_bounds__(256) void chol_update_kernel(float* __restrict__ A,
     }
     __syncthreads();
     float acc[4][4] = {};
-    tile_fma(Xs, Ys, acc);
-    const int r0 = 4 * (t >> 4), c0 = 4 * (t & 15);
+    tile_fma_rows(Xs, Ys, acc);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int a = base + NB * I + r0 + i, b = base + NB * J + c0 + j;
+            const int a = base + NB * I + (t >> 4) + 16 * i, b = base + NB * J + (t & 15) + 16 * j;
             if (a < k && b <= a) A[(int64_t)a * k + b] -= acc[i][j];
         }
 }
@@ -222,6 +246,35 @@ __global__ __launch_bounds__(64) void sweep_kernel(const void* __restrict__ w, i
     const int row = (int)blockIdx.x * 64 + t;
     if (row >= n) return;
     const int n_groups = k / g, zwords = (n_groups + 7) / 8;
+    // the row's slice of C and of the weights for the block, in 16-byte loads (k is a multiple
+    // of 32 and the rows of w are 16-byte aligned)
+    float cv[NB], wv[NB];
+    const float* crow = C + (int64_t)row * k + j0;
+#pragma unroll
+    for (int q = 0; q < NB / 4; ++q) {
+        const f32x4v v = 4 * q < bw ? *reinterpret_cast<const f32x4v*>(crow + 4 * q) : f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cv[4 * q + e] = v[e];
+    }
+    if constexpr (DT == 0) {
+        const float* wrow = reinterpret_cast<const float*>(w) + (int64_t)row * k + j0;
+#pragma unroll
+        for (int q = 0; q < NB / 4; ++q) {
+            const f32x4v v = 4 * q < bw ? *reinterpret_cast<const f32x4v*>(wrow + 4 * q) : f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wv[4 * q + e] = v[e];
+        }
+    } else {
+        typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+        const uint16_t* wrow = reinterpret_cast<const uint16_t*>(w) + (int64_t)row * k + j0;
+#pragma unroll
+        for (int q = 0; q < NB / 8; ++q) {
+            const u32x4v v = 8 * q < bw ? *reinterpret_cast<const u32x4v*>(wrow + 8 * q) : u32x4v{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                wv[8 * q + e] = half_to_float<DT == 1>((uint16_t)(v[e / 2] >> (16 * (e % 2))));
+        }
+    }
     float d[NB];
     uint32_t words[NB / 8];
 #pragma unroll
@@ -233,13 +286,14 @@ __global__ __launch_bounds__(64) void sweep_kernel(const void* __restrict__ w, i
             const int col = j0 + j, gi = col / g;
             const float S = (float)__builtin_bit_cast(_Float16, scales[(int64_t)row * n_groups + gi]);
             const float z = SYM ? 8.f : (float)((zeros[(int64_t)row * zwords + gi / 8] >> (4 * (gi % 8))) & 0xFu);
-            const float wj = load_w<DT>(w, (int64_t)row * k + col);
-            float s = C[(int64_t)row * k + col];
+            // sum_{i<j} d_i U_ij in four interleaved partial sums (a shorter dependency chain)
+            float p[4] = {cv[j], 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < j; ++i) s = __builtin_fmaf(d[i], UT[j][i], s);
-            const float wp = wj + s / UT[j][j];
+            for (int i = 0; i < j; ++i) p[i & 3] = __builtin_fmaf(d[i], UT[j][i], p[i & 3]);
+            const float sum = (p[0] + p[1]) + (p[2] + p[3]);
+            const float wp = wv[j] + sum / UT[j][j];
             const float u = fminf(fmaxf(rintf(wp / S) + z, 0.f), 15.f);
-            d[j] = wj - S * (u - z);
+            d[j] = wv[j] - S * (u - z);
             words[j / 8] |= (uint32_t)u << (4 * (j % 8));
         }
     }
@@ -248,23 +302,26 @@ __global__ __launch_bounds__(64) void sweep_kernel(const void* __restrict__ w, i
         if (8 * q < bw) qweight[(int64_t)row * (k / 8) + j0 / 8 + q] = words[q];
 #pragma unroll
     for (int j = 0; j < NB; ++j)
-        if (j < bw) Dout[(int64_t)row * NB + j] = d[j];
+        if (j < bw) Dout[(int64_t)j * n + row] = d[j];
 }
 
-// C[r][l] += sum_{i<bw} D[r][i] U_{j0+i, l} for the later columns l >= j0 + bw, in 64 x 64
-// tiles (row tile R, column tile L); U_{j0+i, l} = A[k-1-(j0+i)][k-1-l].
+// C[r][l] += sum_{i<bw} D[i][r] U_{j0+i, l} for the later columns l >= j0 + bw, in 64 x 64
+// tiles (row tile R, column tile L); D holds the block's errors column-major ([64][n]) and
+// U_{j0+i, l} = A[k-1-(j0+i)][k-1-l].
 __global__ __launch_bounds__(256) void gptq_update_kernel(const float* __restrict__ A, const float* __restrict__ D,
                                                           float* __restrict__ C, int n, int k, int j0, int bw) {
     const int base = j0 + bw;
     const int ctiles = (k - base + NB - 1) / NB;
     const int R = blockIdx.x / ctiles, Lt = blockIdx.x % ctiles;
-    __shared__ float Xs[NB][65], Ys[NB][65];
+    __shared__ __attribute__((aligned(16))) float Xs[NB][NB], Ys[NB][NB];
     const int t = threadIdx.x;
     for (int e = t; e < NB * NB; e += 256) {
-        const int r = e / NB, s = e % NB;
-        const int row = NB * R + r, col = base + NB * Lt + r;
-        Xs[r][s] = row < n && s < bw ? D[(int64_t)row * NB + s] : 0.f;
-        Ys[r][s] = col < k && s < bw ? A[(int64_t)(k - 1 - (j0 + s)) * k + (k - 1 - col)] : 0.f;
+        // D is column-major ([64][n]) and U[j0 + s][col] has reversed, contiguous addresses
+        // along col: consecutive threads take consecutive rows, columns
+        const int s = e / NB, c = e % NB;
+        const int row = NB * R + c, col = base + NB * Lt + c;
+        Xs[s][c] = row < n && s < bw ? D[(int64_t)s * n + row] : 0.f;
+        Ys[s][c] = col < k && s < bw ? A[(int64_t)(k - 1 - (j0 + s)) * k + (k - 1 - col)] : 0.f;
     }
     __syncthreads();
     float acc[4][4] = {};
