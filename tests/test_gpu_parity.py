@@ -389,6 +389,54 @@ def test_gemv_wide_cases(m, n, k, g, xdtype, sym):
     assert_linear_close(y, host_input(x), packed, n, k, g, sym, what=kname)
 
 
+# (m, n, k, g): wide products with at least 4 x 256 tiles, which the launcher serves with two
+# 16-row tiles per workgroup (rows 16392: the last pair holds one tile of 8 rows); ring rows
+# 4, 8 and 16
+WIDE_PAIR_CASES = [(16, 16392, 512, 128), (5, 16392, 1024, 32), (8, 16400, 2048, 64),
+                   (4, 16392, 14336, 128)]
+
+
+@pytest.mark.parametrize("m,n,k,g", WIDE_PAIR_CASES)
+@pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("sym", [False, True])
+def test_gemv_wide_pair_cases(m, n, k, g, xdtype, sym):
+    w = torch.from_numpy(pins.random_weights(n + 11 * k + m + g, n, k))
+    x = synthetic.activations(m, k, seed=m * 23 + k).to(xdtype)
+    note(f"gemv wide pair m={m} n={n} k={k} g={g} {xdtype} sym={sym}")
+    p, _ = pack_guarded(w.to(DEV), g, sym)
+    assert not tile_fits(g, m, k, n) and wide_fits(g, m, k)
+    y, kname = run_linear(x, p)  # stores outside y are checked there
+    t = "f16" if xdtype == torch.float16 else "bf16"
+    assert kname == f"q4_gemv_wide_{t}"
+    packed = assert_pack_exact(p, host_input(w), g, sym)
+    # every 5th column and the last tile's rows (the ragged pair)
+    cols = np.unique(np.concatenate([np.arange(0, n, 5), np.arange(n - 24, n)]))
+    assert_linear_close(y, host_input(x), packed, n, k, g, sym, cols=cols, what=kname)
+
+
+@pytest.mark.parametrize("m", [6, 16])
+@pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
+def test_gemm_grouped_wide_pair(m, xdtype):
+    """Two problems with 1063 tiles in all (paired tiles, first workgroups recounted per
+    problem), ragged last pairs; every output of both."""
+    k, g, sym = 512, 64, False
+    ns = [9000, 8000 - 8]
+    ws = [torch.from_numpy(pins.random_weights(61 + i, n, k)) for i, n in enumerate(ns)]
+    x = synthetic.activations(m, k, seed=77).to(xdtype)
+    note(f"grouped wide pair m={m} {xdtype}")
+    packs = [pack_guarded(w.to(DEV), g, sym)[0] for w in ws]
+    guards = [guarded((m, n), torch.float32, SENTINEL_F32) for n in ns]
+    q4.q4_w4a16_gemm_grouped(x.to(DEV), packs, outs=[v for _, v in guards])
+    torch.cuda.synchronize()
+    t = "f16" if xdtype == torch.float16 else "bf16"
+    assert q4.q4_last_kernel() == f"q4_gemv_wide_{t}"
+    for w, p, (gb, gv) in zip(ws, packs, guards):
+        assert guard_intact(gb), "store outside y"
+        packed = assert_pack_exact(p, host_input(w), g, sym)
+        assert_linear_close(gv.cpu().numpy(), host_input(x), packed, p.n, k, g, sym,
+                            what="grouped pair")
+
+
 @pytest.mark.parametrize("m,n,k", TILE_CASES)
 @pytest.mark.parametrize("g", [32, 64, 128])
 @pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])

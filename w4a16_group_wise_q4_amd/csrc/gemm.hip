@@ -136,9 +136,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const uint16_t* __res
     const int col = lane & 31, h = lane >> 5;
 
     // Per-lane parts of the load offsets; the per-stage part is a uniform scalar offset.
-    // Rows past the end of a block read nothing (their per-lane offset carries kOOB).
-    // Loads for the two stages after the last one read whatever lies in range and are
-    // never used, so they need no masking.  The k tail (k % 64 == 32) needs it: the
+    // Rows past the end of a block read nothing (their per-lane offset carries kOOB), and
+    // so do the loads for the two stages after the last one (issued by the pipeline, never
+    // used): every mask goes into the per-lane offset.  The k tail (k % 64 == 32): the
     // activation chunks past k are read as zeros, so whatever the weight words past the
     // end of a row hold meets a zero.
     const int ca = (lane & 7) ^ ((lane >> 3) & 7);  // activation chunk this lane moves (DMA rows are 8-aligned)
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const uint16_t* __res
     // ---- loads of one stage (fixed count and order: 4 activation DMAs, then per block j
     //      the words, the scales and the zero word)
     auto load_a = [&](int s) {  // rows [32 wave, +32) of stage s into ring slot s % RING
-        const uint32_t tm = s == stages - 1 ? tail_mask : 0u;
+        const uint32_t tm = s >= stages ? kOOB : (s == stages - 1 ? tail_mask : 0u);
         const int so = __builtin_amdgcn_readfirstlane(2 * s * BK);
         uint8_t* slot = smem + (s % RING) * A_STAGE;
 #pragma unroll
@@ -174,20 +174,27 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const uint16_t* __res
         const int g0 = G == 128 ? (s >> 1) : (G == 64 ? s : 2 * s);        // its first group
         const int sso = __builtin_amdgcn_readfirstlane(2 * g0);
         const int zso = __builtin_amdgcn_readfirstlane(4 * (g0 >> 3));
+        const uint32_t pm = s >= stages ? kOOB : 0u;  // past the last stage: read nothing
+        // a short last stage (k % 64 == 32) holds words 0..3 and one group: the words and the
+        // scale past the row read nothing
+        const bool short_stage = s == stages - 1 && (K % BK) != 0;
+        const uint32_t hm = short_stage && (G == 32 || h == 1) ? kOOB : 0u;  // words 4..7
+        const uint32_t sm = short_stage ? kOOB : 0u;                         // second group
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             if constexpr (G >= 64) {
-                const q4::u32x4 t = q4::buf_load_x4(rq, (int)qoff[j], wso);
+                const q4::u32x4 t = q4::buf_load_x4(rq, (int)(qoff[j] | pm | hm), wso);
                 b.w[j][0] = t[0]; b.w[j][1] = t[1]; b.w[j][2] = t[2]; b.w[j][3] = t[3];
             } else {
-                const q4::u32x2 ta = q4::buf_load_x2(rq, (int)qoff[j], wso);
-                const q4::u32x2 tb = q4::buf_load_x2(rq, (int)qoff[j], wso + 16);
+                const q4::u32x2 ta = q4::buf_load_x2(rq, (int)(qoff[j] | pm), wso);
+                const q4::u32x2 tb = q4::buf_load_x2(rq, (int)(qoff[j] | pm | hm), wso + 16);
                 b.w[j][0] = ta[0]; b.w[j][1] = ta[1]; b.w[j][2] = tb[0]; b.w[j][3] = tb[1];
             }
 #pragma unroll
-            for (int q = 0; q < NGS; ++q) b.s[j][q] = q4::buf_load_u16(rs, (int)soff[j], sso + 2 * q);
+            for (int q = 0; q < NGS; ++q)
+                b.s[j][q] = q4::buf_load_u16(rs, (int)(soff[j] | pm | (q == 1 ? sm : 0u)), sso + 2 * q);
             if constexpr (!SYM)
-                b.z[j] = q4::buf_load_x1(rz, (int)zoff[j], zso);
+                b.z[j] = q4::buf_load_x1(rz, (int)(zoff[j] | pm), zso);
             else
                 b.z[j] = 0u;
         }

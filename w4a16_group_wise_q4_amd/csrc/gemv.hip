@@ -539,6 +539,7 @@ hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16
         int upw = 0, tw = 0, wide = 0;
         const bool fits = sc4 && (q4t::tile_shape(G, m, k, tiles, g_num_cus, &upw, &tw) ||
                                   (wide = q4t::wide_shape(G, m, k, &upw, &tw)));
+        if (wide && q4t::wide_pair(tiles, g_num_cus)) wide = 2;
         if (fits) {
             GemvBatch one{};
             if (batch == nullptr) {

@@ -48,23 +48,25 @@ constexpr int kLdsBudget = 96 * 1024;        // LDS per workgroup
 
 constexpr int gcd8(int v) { return (v & 7) == 0 ? 8 : ((v & 3) == 0 ? 4 : ((v & 1) == 0 ? 2 : 1)); }
 
-// NV consecutive dwords at byte offset off of resource rs (chunks of 4, 2, 1).
+// NV consecutive dwords at byte offset off of resource rs (chunks of 4, 2, 1).  The whole
+// offset is per-lane, so the range check covers every chunk (the last slice of the last
+// row may reach past the buffer: those dwords read zero).
 template <int NV>
 __device__ __forceinline__ void load_dwords(q4::rsrc rs, int off, uint32_t (&v)[NV]) {
 #pragma unroll
     for (int j = 0; j < NV / 4; ++j) {
-        const q4::u32x4 t = q4::buf_load_x4(rs, off, 16 * j);
+        const q4::u32x4 t = q4::buf_load_x4(rs, off + 16 * j, 0);
         v[4 * j] = t[0];
         v[4 * j + 1] = t[1];
         v[4 * j + 2] = t[2];
         v[4 * j + 3] = t[3];
     }
     if constexpr (NV % 4 >= 2) {
-        const q4::u32x2 t = q4::buf_load_x2(rs, off, 16 * (NV / 4));
+        const q4::u32x2 t = q4::buf_load_x2(rs, off + 16 * (NV / 4), 0);
         v[NV / 4 * 4] = t[0];
         v[NV / 4 * 4 + 1] = t[1];
     }
-    if constexpr (NV % 2 == 1) v[NV - 1] = q4::buf_load_x1(rs, off, 4 * (NV - 1));
+    if constexpr (NV % 2 == 1) v[NV - 1] = q4::buf_load_x1(rs, off + 4 * (NV - 1), 0);
 }
 
 __device__ __forceinline__ void swap32(uint32_t& a, uint32_t& b) {
@@ -141,7 +143,7 @@ __global__ __launch_bounds__(MQ == 1 ? 1024 : 512) void gemv_tile_kernel(const q
         const q4::rsrc rq = q4::make_rsrc(qweight + (int64_t)n0 * KW, (uint32_t)rows * KW * 4u);
         const int qo = r < rows ? r * KW * 4 + c * 16 : kOOB;
 #pragma unroll
-        for (int u = 0; u < UPW; ++u) wv[u] = q4::buf_load_x4(rq, qo, u < nu ? (U0 + u) * 64 : kOOB);
+        for (int u = 0; u < UPW; ++u) wv[u] = q4::buf_load_x4(rq, u < nu ? qo : kOOB, (U0 + u) * 64);
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -252,21 +254,32 @@ __global__ __launch_bounds__(MQ == 1 ? 1024 : 512) void gemv_tile_kernel(const q
     }
 }
 
-// Wide tile kernel: 4 < m <= 16.  Same tiles, slices and metadata as the tile kernel, but
-// the activations are not staged in LDS (m x K of them does not fit there for the larger
-// projections).  Per unit, each lane loads the 64 bytes of activation row l%16 that its
-// four MFMA k-blocks use (the words its weight registers hold after the transpose) from
-// the L2-resident activations, and puts them in the decoder's slot order in registers.
-// The wave keeps two batches of D units (activations and weights) in flight: once a batch
-// is computed its registers take the batch two ahead, all offsets and waits static.  All
-// 16 MFMA rows are activation rows (zero rows past m), so every lane holds four outputs.
-template <int G, bool SYM, bool XF16, int UPW, bool GROUPED>
+// Wide tile kernel: m <= 16 (4 < m, and the m <= 4 shapes the tile kernel cannot take).
+// Same tiles, slices and metadata as the tile kernel; the activations, m x K of which do
+// not fit in LDS for the larger projections, stream through a small wave-private LDS ring
+// instead.  The wave keeps two batches of D units in flight: per unit, MR/4 direct-to-LDS
+// loads of its activations (MR = 4, 8 or 16 rows; rows past m read nothing) and one load
+// of its packed words into registers.  Each direct load moves 4 whole rows x 256 bytes
+// (coalesced): lane l writes row 4a + l/16, position l%16 of that row, and fetches chunk
+// (l%16) ^ row into it, so that the MFMA-layout reads afterwards (16 rows at one chunk
+// index) hit 16 different bank groups.  Before a batch is read the wave waits for its
+// loads with a fixed count (the next batch's loads stay in flight); once it is computed,
+// its slots take the batch two ahead.  All 16 MFMA rows are activation rows (rows past m
+// read row m-1 and are never stored), so every lane holds four outputs.
+template <int G, bool SYM, bool XF16, int UPW, int MR, int D, int T, bool GROUPED>
 __global__ __launch_bounds__(512) void gemv_wide_kernel(const q4::GemvBatch bt, int M, int K) {
-    constexpr int D = 2;            // units per batch
     constexpr int NB = UPW / D;     // batches per slice (at least two)
     constexpr int NG = 128 / G, RPG = 4 / NG, GPS = UPW * NG, SV = GPS / 2;
     constexpr int ZOFF = GPS % 8 == 0 ? 0 : 8 - gcd8(GPS);
     constexpr int ZV = (ZOFF + GPS + 7) / 8;
+    constexpr int XR = MR / 4;                   // direct loads per unit
+    constexpr int UNIT_LDS = MR * 256;           // bytes of one unit's activations
+    constexpr int WAVE_LDS = 2 * D * UNIT_LDS;   // this wave's ring
+    constexpr int PER_BATCH = D * (XR + T);      // vector loads per batch
+    constexpr int WAIT_NEXT = (PER_BATCH & 15) | ((PER_BATCH >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+    constexpr int WAIT_ALL = (0x7 << 4) | (0xF << 8);   // vmcnt(0)
+    constexpr int WAIT_LDS = 0xF | (0x3 << 14) | (0x7 << 4);  // lgkmcnt(0)
+    static_assert(T * 1024 <= WAVE_LDS, "partial sums fit the ring");
     extern __shared__ q4::u32x4 lds[];
     int pi = 0;
     if constexpr (GROUPED) {
@@ -280,145 +293,211 @@ __global__ __launch_bounds__(512) void gemv_wide_kernel(const q4::GemvBatch bt, 
     const uint32_t* __restrict__ zeros = bt.p[pi].zeros;
     float* __restrict__ y = bt.p[pi].y;
     const int N = bt.p[pi].n;
-    const int n0 = ((int)blockIdx.x - bt.p[pi].tile0) * 16;
+    const int n0 = ((int)blockIdx.x - bt.p[pi].tile0) * 16 * T;  // T tiles of 16 rows
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int S = blockDim.x >> 6;
     const int r = lane & 15, c = lane >> 4;
     const int KW = K >> 3, units = K >> 7, ng = K / G, zw = (ng + 7) >> 3;
-    const int rows = N - n0 < 16 ? N - n0 : 16;
+    const int rows = N - n0 < 16 * T ? N - n0 : 16 * T;  // rows of the workgroup
     const int U0 = w * UPW, G0 = U0 * NG;
     const int nu = units - U0 < UPW ? units - U0 : UPW;
+    uint8_t* ring = reinterpret_cast<uint8_t*>(lds) + w * WAVE_LDS;
 
-    // ---- metadata of the slice (waited for before the first unit)
-    uint32_t sv[SV];
+    // ---- metadata of the slice, per tile (waited for before the first unit)
+    uint32_t sv[T][SV];
+    uint32_t zv[T][ZV] = {};
     {
         const q4::rsrc rs = q4::make_rsrc(scales + (int64_t)n0 * ng, (uint32_t)rows * ng * 2u);
-        load_dwords<SV>(rs, r < rows ? (r * ng + G0) * 2 : kOOB, sv);
-    }
-    uint32_t zv[ZV] = {};
-    if constexpr (!SYM) {
-        const q4::rsrc rz = q4::make_rsrc(zeros + (int64_t)n0 * zw, (uint32_t)rows * zw * 4u);
-        load_dwords<ZV>(rz, r < rows ? (r * zw + (G0 >> 3)) * 4 : kOOB, zv);
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const int rr = 16 * t + r;
+            load_dwords<SV>(rs, rr < rows ? (rr * ng + G0) * 2 : kOOB, sv[t]);
+        }
+        if constexpr (!SYM) {
+            const q4::rsrc rz = q4::make_rsrc(zeros + (int64_t)n0 * zw, (uint32_t)rows * zw * 4u);
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const int rr = 16 * t + r;
+                load_dwords<ZV>(rz, rr < rows ? (rr * zw + (G0 >> 3)) * 4 : kOOB, zv[t]);
+            }
+        }
     }
 
-    // ---- activations and weights of a batch: per unit four activation vectors of row l%16
-    // (lane part of the word index in the per-lane offset, register part in the uniform
-    // one), then the unit's packed words
-    const int lb = G == 128 ? 4 * c : (G == 64 ? 4 * (c & 1) + 2 * (c >> 1) : c);
+    // ---- loads of a batch: per unit the activation rows into the ring slot, then the
+    // unit's packed words of each tile
     const q4::rsrc rx = q4::make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
-    const int xo = r < M ? r * K * 2 + lb * 16 : kOOB;
+    uint32_t doff[XR];
+#pragma unroll
+    for (int a = 0; a < XR; ++a) {
+        const int R = 4 * a + (lane >> 4);
+        doff[a] = R < M ? (uint32_t)(R * K + 8 * ((lane & 15) ^ R)) * 2u : (uint32_t)kOOB;
+    }
     const q4::rsrc rq = q4::make_rsrc(qweight + (int64_t)n0 * KW, (uint32_t)rows * KW * 4u);
-    const int qo = r < rows ? r * KW * 4 + c * 16 : kOOB;
-    q4::u32x4 xb[2][D][4];
-    q4::u32x4 wb[2][D];
-    auto load_batch = [&](int b, q4::u32x4 (&xs)[D][4], q4::u32x4 (&ws)[D]) {
+    uint32_t qo[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) qo[t] = 16 * t + r < rows ? (uint32_t)((16 * t + r) * KW * 4 + c * 16) : (uint32_t)kOOB;
+    q4::u32x4 wb[2][D][T];
+    auto load_batch = [&](int b, q4::u32x4 (&ws)[D][T]) {
 #pragma unroll
         for (int j = 0; j < D; ++j) {
             const int u = b * D + j;
-            const bool ok = u < nu;
+            // slots past the slice read nothing: the mask goes into the per-lane offset
+            const uint32_t pm = u < nu ? 0u : (uint32_t)kOOB;
+            uint8_t* slot = ring + ((b & 1) * D + j) * UNIT_LDS;
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const int imm = G == 128 ? a : (G == 64 ? 8 * (a >> 1) + (a & 1) : 4 * a);
-                xs[j][a] = q4::buf_load_x4(rx, xo, ok ? (U0 + u) * 256 + imm * 16 : kOOB);
-            }
-            ws[j] = q4::buf_load_x4(rq, qo, ok ? (U0 + u) * 64 : kOOB);
+            for (int a = 0; a < XR; ++a)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)(slot + a * 1024),
+                                                         16, (int)(doff[a] | pm), (U0 + u) * 256, 0, 0);
+#pragma unroll
+            for (int t = 0; t < T; ++t) ws[j][t] = q4::buf_load_x4(rq, (int)(qo[t] | pm), (U0 + u) * 64);
         }
     };
-    load_batch(0, xb[0], wb[0]);
-    load_batch(1, xb[1], wb[1]);
+    // the metadata, batch 0 and batch 1 are issued in this order: the fixed wait counts
+    // below depend on it
+    __builtin_amdgcn_sched_barrier(0);
+    load_batch(0, wb[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    load_batch(1, wb[1]);
     __builtin_amdgcn_sched_barrier(0);
 
-    uint32_t zs[ZV];
+    uint32_t zs[T][ZV];
 #pragma unroll
-    for (int j = 0; j < ZV; ++j) zs[j] = zv[j];
-    if constexpr (!SYM && ZOFF != 0) {
-        const uint32_t sh = 4u * (uint32_t)(G0 & 7);
+    for (int t = 0; t < T; ++t) {
 #pragma unroll
-        for (int j = 0; j + 1 < ZV; ++j) zs[j] = __builtin_amdgcn_alignbit(zv[j + 1], zv[j], sh);
-        zs[ZV - 1] = zv[ZV - 1] >> sh;
+        for (int j = 0; j < ZV; ++j) zs[t][j] = zv[t][j];
+        if constexpr (!SYM && ZOFF != 0) {
+            const uint32_t sh = 4u * (uint32_t)(G0 & 7);
+#pragma unroll
+            for (int j = 0; j + 1 < ZV; ++j) zs[t][j] = __builtin_amdgcn_alignbit(zv[t][j + 1], zv[t][j], sh);
+            zs[t][ZV - 1] = zv[t][ZV - 1] >> sh;
+        }
+    }
+
+    // read addresses: row min(l%16, m-1), chunk lb + imm(a) at its swizzled position
+    const int mrow = r < M ? r : M - 1;
+    const int lb = G == 128 ? 4 * c : (G == 64 ? 4 * (c & 1) + 2 * (c >> 1) : c);
+    uint32_t xaddr[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const int imm = G == 128 ? a : (G == 64 ? 8 * (a >> 1) + (a & 1) : 4 * a);
+        xaddr[a] = (uint32_t)(mrow * 256 + (((lb + imm) ^ mrow) << 4));
     }
 
     const uint32_t kMask = q4::vreg_const(0x000F000Fu);
     const uint32_t kBias = q4::vreg_const(0x43004300u);
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    float acc[T][4];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[t][q] = 0.f;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
         const int slot = b & 1;
+        // this batch's loads have landed (the next batch's stay in flight)
+        if (b + 1 < NB)
+            __builtin_amdgcn_s_waitcnt(WAIT_NEXT);
+        else
+            __builtin_amdgcn_s_waitcnt(WAIT_ALL);
 #pragma unroll
         for (int j = 0; j < D; ++j) {
             const int u = b * D + j;
             const bool valid = u < nu;
-            uint32_t wq[4] = {wb[slot][j][0], wb[slot][j][1], wb[slot][j][2], wb[slot][j][3]};
-            if constexpr (G <= 64) {
-                swap32(wq[0], wq[2]);
-                swap32(wq[1], wq[3]);
-            }
-            if constexpr (G == 32) {
-                swap16(wq[0], wq[1]);
-                swap16(wq[2], wq[3]);
-            }
+            const uint8_t* sb = ring + (slot * D + j) * UNIT_LDS;
             q4::u32x4 xa[4];
 #pragma unroll
-            for (int a = 0; a < 4; ++a) xa[a] = q4::pair_perm(xb[slot][j][a]);
+            for (int a = 0; a < 4; ++a) xa[a] = q4::pair_perm(*reinterpret_cast<const q4::u32x4*>(sb + xaddr[a]));
 #pragma unroll
-            for (int h = 0; h < NG; ++h) {
-                const int gi = u * NG + h;
-                const uint32_t sw = sv[gi >> 1];
-                const float s = q4::f16_bits_to_float((uint16_t)((gi & 1) ? (sw >> 16) : sw));
-                int z = 8;
-                if constexpr (!SYM) z = (int)((zs[gi >> 3] >> (4 * (gi & 7))) & 0xFu);
-                q4::f32x4 dv = {0.f, 0.f, 0.f, 0.f};
-                if constexpr (XF16) {
-                    const _Float16 bb = (_Float16)(1024 + z);
-                    const q4::f16x2 bias = {bb, bb};
+            for (int t = 0; t < T; ++t) {
+                uint32_t wq[4] = {wb[slot][j][t][0], wb[slot][j][t][1], wb[slot][j][t][2], wb[slot][j][t][3]};
+                if constexpr (G <= 64) {
+                    swap32(wq[0], wq[2]);
+                    swap32(wq[1], wq[3]);
+                }
+                if constexpr (G == 32) {
+                    swap16(wq[0], wq[1]);
+                    swap16(wq[2], wq[3]);
+                }
 #pragma unroll
-                    for (int t = 0; t < RPG; ++t) {
-                        const int a = h * RPG + t;
-                        dv = q4::mfma_f16(xa[a], q4::decode_f16_exact(wq[a], bias), dv);
+                for (int h = 0; h < NG; ++h) {
+                    const int gi = u * NG + h;
+                    const uint32_t sw = sv[t][gi >> 1];
+                    const float s = q4::f16_bits_to_float((uint16_t)((gi & 1) ? (sw >> 16) : sw));
+                    int z = 8;
+                    if constexpr (!SYM) z = (int)((zs[t][gi >> 3] >> (4 * (gi & 7))) & 0xFu);
+                    q4::f32x4 dv = {0.f, 0.f, 0.f, 0.f};
+                    if constexpr (XF16) {
+                        const _Float16 bb = (_Float16)(1024 + z);
+                        const q4::f16x2 bias = {bb, bb};
+#pragma unroll
+                        for (int e = 0; e < RPG; ++e) {
+                            const int a = h * RPG + e;
+                            dv = q4::mfma_f16(xa[a], q4::decode_f16_exact(wq[a], bias), dv);
+                        }
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) acc[t][q] = valid ? acc[t][q] + s * dv[q] : acc[t][q];
+                    } else {
+                        const uint32_t zb = (uint32_t)z * 0x00010001u + kBias;
+                        const q4::u32x4 zop = {zb, zb, zb, zb};
+                        q4::f32x4 dc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int e = 0; e < RPG; ++e) {
+                            const int a = h * RPG + e;
+                            dv = q4::mfma_bf16(xa[a], q4::decode_bf16_biased(wq[a], kMask, kBias), dv);
+                            dc = q4::mfma_bf16(xa[a], zop, dc);
+                        }
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            acc[t][q] = valid ? acc[t][q] + s * (dv[q] - dc[q]) : acc[t][q];
                     }
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) acc[q] = valid ? acc[q] + s * dv[q] : acc[q];
-                } else {
-                    const uint32_t zb = (uint32_t)z * 0x00010001u + kBias;
-                    const q4::u32x4 zop = {zb, zb, zb, zb};
-                    q4::f32x4 dc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int t = 0; t < RPG; ++t) {
-                        const int a = h * RPG + t;
-                        dv = q4::mfma_bf16(xa[a], q4::decode_bf16_biased(wq[a], kMask, kBias), dv);
-                        dc = q4::mfma_bf16(xa[a], zop, dc);
-                    }
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) acc[q] = valid ? acc[q] + s * (dv[q] - dc[q]) : acc[q];
                 }
             }
         }
-        // refill this slot with the batch two ahead, right behind the compute that freed it
-        if (b + 2 < NB) load_batch(b + 2, xb[slot], wb[slot]);
+        __builtin_amdgcn_sched_barrier(0);
+        // refill these slots with the batch two ahead once every read of them has returned
+        if (b + 2 < NB) {
+            __builtin_amdgcn_s_waitcnt(WAIT_LDS);
+            load_batch(b + 2, wb[slot]);
+        }
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    // ---- cross-wave sum: lane l holds rows m = 4(l/16)..+3 of column l%16
-    float* red = reinterpret_cast<float*>(lds);
+    // ---- cross-wave sum: lane l holds rows m = 4(l/16)..+3 of column l%16 of each tile.
+    // Each wave writes into its own ring (its loads have all landed and been read).
+    __builtin_amdgcn_s_waitcnt(WAIT_LDS);
+    float* red = reinterpret_cast<float*>(ring);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) red[(w * 64 + lane) * 4 + q] = acc[q];
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) red[(t * 64 + lane) * 4 + q] = acc[t][q];
     __syncthreads();
     if (w == 0) {
-        float sum[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int v = 0; v < S; ++v)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) sum[q] += red[(v * 64 + lane) * 4 + q];
         const q4::rsrc ry = q4::make_rsrc(y, (uint32_t)M * (uint32_t)N * 4u);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int m = 4 * c + q;
-            const bool st = m < M && r < rows;
-            const uint32_t off = st ? ((uint32_t)m * (uint32_t)N + (uint32_t)(n0 + r)) * 4u : kStoreOOB;
-            __builtin_amdgcn_raw_buffer_store_b32(q4::f32_bits(sum[q]), ry, (int)off, 0, 0);
+        for (int t = 0; t < T; ++t) {
+            float sum[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int v = 0; v < S; ++v) {
+                const float* rv = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(lds) + v * WAVE_LDS);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) sum[q] += rv[(t * 64 + lane) * 4 + q];
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int m = 4 * c + q;
+                const bool st = m < M && 16 * t + r < rows;
+                const uint32_t off = st ? ((uint32_t)m * (uint32_t)N + (uint32_t)(n0 + 16 * t + r)) * 4u : kStoreOOB;
+                __builtin_amdgcn_raw_buffer_store_b32(q4::f32_bits(sum[q]), ry, (int)off, 0, 0);
+            }
         }
     }
 }
+
+// LDS of the wide kernel per workgroup: each wave's ring of two batches of D units.
+constexpr int wide_rows(int m) { return m <= 4 ? 4 : (m <= 8 ? 8 : 16); }
+constexpr int wide_batch(int m) { return m <= 8 ? 2 : 1; }
+inline size_t wide_lds(int m, int waves) { return (size_t)waves * 2 * wide_batch(m) * wide_rows(m) * 256; }
+// Two tiles per workgroup when the halved grid still holds two tiles per CU.
+inline bool wide_pair(int tiles, int num_cus) { return tiles >= 4 * (num_cus > 0 ? num_cus : 256); }
 
 // Slice widths per group size (the g = 32 and g = 64 metadata registers grow with the
 // slice; these stay within the launch bounds' register budgets).
@@ -503,41 +582,68 @@ hipError_t launch_x(int upw, int mq, dim3 grid, dim3 block, size_t lds, hipStrea
     return hipErrorInvalidValue;
 }
 
-template <int G, bool SYM, bool XF16, bool GR>
-hipError_t launch_wide(int upw, dim3 grid, dim3 block, size_t lds, hipStream_t st,
-                       const q4::GemvBatch& bt, int m, int k) {
-#define Q4_WIDE(U)                                                                                 \
-    if (upw == U) {                                                                                \
-        hipLaunchKernelGGL((gemv_wide_kernel<G, SYM, XF16, U, GR>), grid, block, lds, st, bt, m, k); \
-        return hipGetLastError();                                                                  \
+template <int G, bool SYM, bool XF16, bool GR, int MR, int T>
+hipError_t launch_wide_rows(int upw, dim3 grid, dim3 block, size_t lds, hipStream_t st,
+                            const q4::GemvBatch& bt, int m, int k) {
+    constexpr int D = MR <= 8 ? 2 : 1;
+    static_assert(D == wide_batch(MR), "ring shape");
+#define Q4_WIDE(U)                                                                                          \
+    if (upw == U) {                                                                                         \
+        hipLaunchKernelGGL((gemv_wide_kernel<G, SYM, XF16, U, MR, D, T, GR>), grid, block, lds, st, bt, m, k); \
+        return hipGetLastError();                                                                           \
     }
     Q4_WIDE(4) Q4_WIDE(8) Q4_WIDE(12) Q4_WIDE(16)
 #undef Q4_WIDE
     return hipErrorInvalidValue;
 }
 
-// Launch for a shape from tile_shape (wide == 0) or wide_shape (wide != 0): one workgroup
-// of 64 * waves threads per tile.
+template <int G, bool SYM, bool XF16, bool GR>
+hipError_t launch_wide(int upw, int pair, dim3 grid, dim3 block, size_t lds, hipStream_t st,
+                       const q4::GemvBatch& bt, int m, int k) {
+    switch (wide_rows(m) * 2 + pair) {
+    case 8: return launch_wide_rows<G, SYM, XF16, GR, 4, 1>(upw, grid, block, lds, st, bt, m, k);
+    case 9: return launch_wide_rows<G, SYM, XF16, GR, 4, 2>(upw, grid, block, lds, st, bt, m, k);
+    case 16: return launch_wide_rows<G, SYM, XF16, GR, 8, 1>(upw, grid, block, lds, st, bt, m, k);
+    case 17: return launch_wide_rows<G, SYM, XF16, GR, 8, 2>(upw, grid, block, lds, st, bt, m, k);
+    case 32: return launch_wide_rows<G, SYM, XF16, GR, 16, 1>(upw, grid, block, lds, st, bt, m, k);
+    default: return launch_wide_rows<G, SYM, XF16, GR, 16, 2>(upw, grid, block, lds, st, bt, m, k);
+    }
+}
+
+// Launch for a shape from tile_shape (wide == 0) or wide_shape (wide == 1: one workgroup of
+// 64 * waves threads per tile; wide == 2: per two tiles).
 template <int G>
 hipError_t launch_tile(int sym, int xd, int m, int k, int upw, int waves, int wide,
                        const q4::GemvBatch& bt, int tiles, hipStream_t st, const char** kname) {
-    if (wide) {  // wide kernel: partial sums only in LDS
-        const size_t lds = (size_t)waves * 64 * 4 * 4;
-        const dim3 grid(tiles), block(64 * waves);
+    if (wide) {  // wide kernel: each wave's activation ring (its partial sums reuse it)
+        // Two 16-row tiles per workgroup (sharing every activation unit) while that still
+        // leaves two tiles per CU; the problems' first workgroups are recounted for it.
+        const int pair = wide == 2 ? 1 : 0;
+        q4::GemvBatch bp = bt;
+        int groups = tiles;
+        if (pair) {
+            groups = 0;
+            for (int i = 0; i < bp.count; ++i) {
+                bp.p[i].tile0 = groups;
+                groups += (int)((bp.p[i].n + 31) / 32);
+            }
+        }
+        const size_t lds = wide_lds(m, waves);
+        const dim3 grid(groups), block(64 * waves);
         const bool gr = bt.count > 1;
         *kname = xd == 1 ? "q4_gemv_wide_f16" : "q4_gemv_wide_bf16";
         if (sym) {
             if (xd == 1)
-                return gr ? launch_wide<G, true, true, true>(upw, grid, block, lds, st, bt, m, k)
-                          : launch_wide<G, true, true, false>(upw, grid, block, lds, st, bt, m, k);
-            return gr ? launch_wide<G, true, false, true>(upw, grid, block, lds, st, bt, m, k)
-                      : launch_wide<G, true, false, false>(upw, grid, block, lds, st, bt, m, k);
+                return gr ? launch_wide<G, true, true, true>(upw, pair, grid, block, lds, st, bp, m, k)
+                          : launch_wide<G, true, true, false>(upw, pair, grid, block, lds, st, bp, m, k);
+            return gr ? launch_wide<G, true, false, true>(upw, pair, grid, block, lds, st, bp, m, k)
+                      : launch_wide<G, true, false, false>(upw, pair, grid, block, lds, st, bp, m, k);
         }
         if (xd == 1)
-            return gr ? launch_wide<G, false, true, true>(upw, grid, block, lds, st, bt, m, k)
-                      : launch_wide<G, false, true, false>(upw, grid, block, lds, st, bt, m, k);
-        return gr ? launch_wide<G, false, false, true>(upw, grid, block, lds, st, bt, m, k)
-                  : launch_wide<G, false, false, false>(upw, grid, block, lds, st, bt, m, k);
+            return gr ? launch_wide<G, false, true, true>(upw, pair, grid, block, lds, st, bp, m, k)
+                      : launch_wide<G, false, true, false>(upw, pair, grid, block, lds, st, bp, m, k);
+        return gr ? launch_wide<G, false, false, true>(upw, pair, grid, block, lds, st, bp, m, k)
+                  : launch_wide<G, false, false, false>(upw, pair, grid, block, lds, st, bp, m, k);
     }
     const int mq = m <= 1 ? 1 : 4;
     const size_t lds = (size_t)m * waves * upw * 256 + (size_t)waves * 64 * mq * 4;
