@@ -126,7 +126,7 @@ q4_status q4_dequant(const uint32_t* qweight, const uint16_t* scales, const uint
  * m <= 16 runs the decode GEMV kernel.  16 < m <= 256 runs the decode GEMV on 16-row
  * chunks of x (the full chunks in grouped launches of up to 8, the rest in one more) when
  * the prefill GEMM's grid of 128 x 256 tiles fits in one round (at most 2 workgroups per
- * compute unit) and ceil(m/16) * n < 73728: then each chunk streams the weight faster
+ * compute unit) and ceil(m/16) * n < 147456: then the chunks stream the weight faster
  * than the under-filled GEMM covers it.  Otherwise the prefill GEMM kernel runs.  Every
  * path meets the same accuracy bound. */
 q4_status q4_w4a16_gemm(const void* x, q4_dtype x_dtype, int64_t m,

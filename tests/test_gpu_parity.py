@@ -595,10 +595,10 @@ def test_gemm_grouped_one_by_one(m, k, g):
 
 def gemm_path(m, n, num_cus=256):
     """Mirror of the C ABI's choice for 16 < m: the GEMV on 16-row chunks (m <= 256) when
-    the GEMM's grid (128 x 256 tiles) fits in one round and ceil(m/16) * n < 73728."""
+    the GEMM's grid (128 x 256 tiles) fits in one round and ceil(m/16) * n < 147456."""
     chunks = -(-m // 16)
     gemm_wgs = -(-m // 128) * -(-n // 256)
-    chunked = m <= 256 and gemm_wgs <= 2 * num_cus and chunks * n < 72 * 1024
+    chunked = m <= 256 and gemm_wgs <= 2 * num_cus and chunks * n < 144 * 1024
     return not chunked
 
 
@@ -607,9 +607,11 @@ def matmul_kernels(m, n, xdtype=torch.bfloat16):
     return gemm if m > 16 and gemm_path(m, n) else gemv_kernels(xdtype)
 
 
-# the prefill GEMM itself, also at small m where the grid is wide (n large)
-GEMM_CASES = [(17, 40960, 256, 128), (130, 8200, 384, 64), (300, 129, 96, 32), (256, 8192, 1024, 128),
-              (129, 8448, 4096 + 64, 64), (64, 20480, 512, 32), (257, 300, 512, 128), (128, 11008, 1024, 64)]
+# the prefill GEMM itself, also at small m where the grid is wide (n large); k = 96 and 160
+# end on a half stage (k % 64 == 32, g = 32)
+GEMM_CASES = [(17, 73800, 256, 128), (130, 16400, 384, 64), (300, 129, 96, 32), (256, 9300, 1024, 128),
+              (129, 16448, 4096 + 64, 64), (64, 36900, 512, 32), (257, 300, 512, 128), (128, 18500, 1024, 64),
+              (40, 73800, 160, 32)]
 
 
 @pytest.mark.parametrize("m,n,k,g", GEMM_CASES)
@@ -634,7 +636,8 @@ def test_gemm_cases(m, n, k, g, xdtype, sym):
 # m > 128 (two grouped launches)
 MIDM_CASES = [(17, 64, 256, 128), (64, 48, 11008, 128), (40, 1000, 4096, 64), (128, 300, 1024, 32),
               (33, 4096, 11008, 128), (96, 11008, 4096, 128), (112, 5, 512, 64), (256, 300, 1024, 128),
-              (200, 4096, 11008, 128), (145, 64, 256, 32), (32, 28672, 1024, 128)]
+              (200, 4096, 11008, 128), (145, 64, 256, 32), (32, 28672, 1024, 128),
+              (64, 28672, 512, 64), (128, 11008, 512, 32)]
 
 
 @pytest.mark.parametrize("m,n,k,g", MIDM_CASES)

@@ -149,15 +149,16 @@ int device_cus() {
 // 16-row chunks of x sharing the weight (full chunks in grouped launches of up to 8, the
 // rest alone) when that is faster than the prefill GEMM, else the GEMM.  A GEMM grid of
 // 128 x 256 tiles that fits in one round (at most 2 workgroups per CU) takes about
-// k x 20.7 ns on MI355X whatever m and n, while each chunk streams the n x k/2 bytes of
-// codes at about 1.7 TB/s; so the chunks win while chunks x n stays under about 72K rows.
+// k x 20.7 ns on MI355X whatever m and n, while the chunks stream chunks x n x k/2 bytes of
+// codes at about 3.5 TB/s (the grouped chunks share the weight through the caches); so the
+// chunks win while chunks x n stays under about 144K rows.
 // ([FL7] §Batch와 Context에 따라 속도가 달라진다: decode batches sit between the
 // bandwidth-bound and the compute-bound regime.)
 bool chunked_gemv(int64_t m, int64_t n, int cus) {
     if (m <= 16 || m > 256) return false;
     const int64_t chunks = (m + 15) / 16;
     const int64_t gemm_wgs = ((m + 127) / 128) * ((n + 255) / 256);
-    return gemm_wgs <= 2 * (int64_t)cus && chunks * n < 72 * 1024;
+    return gemm_wgs <= 2 * (int64_t)cus && chunks * n < 144 * 1024;
 }
 
 hipError_t run_product(const void* x, int xd, int64_t m, const uint32_t* qw, const uint16_t* sc,
