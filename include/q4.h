@@ -232,7 +232,7 @@ q4_status q4_kv_attention(const void* q, q4_dtype q_dtype, int64_t heads, int64_
  * All arithmetic is fp32 (Hessian, Cholesky factor, updates); a code can differ from an
  * exact-arithmetic sweep where the updated weight falls within rounding of a code
  * boundary.  workspace: device memory of at least q4_gptq_workspace(n, k, group_size)
- * bytes (k*k + n*k + 64*n floats), 16-byte aligned, contents ignored; k <= 32768.  Other
+ * bytes (k*k + n*k + 256*n floats), 16-byte aligned, contents ignored; k <= 32768.  Other
  * rules as q4_quantize_pack; x 16-byte aligned.  Runs about 5k/64 kernels on `stream`. */
 int64_t q4_gptq_workspace(int64_t n, int64_t k, int32_t group_size);
 q4_status q4_gptq_quantize(const void* w, q4_dtype w_dtype, int64_t n, int64_t k, const void* x,

@@ -283,6 +283,6 @@ def test_gptq_validation_rejects_before_launch(call, code):
 
 def test_gptq_workspace_size():
     lib = q4.lib()
-    assert lib.q4_gptq_workspace(11008, 4096, 128) == 4 * (4096 * 4096 + 11008 * 4096 + 64 * 11008)
+    assert lib.q4_gptq_workspace(11008, 4096, 128) == 4 * (4096 * 4096 + 11008 * 4096 + 256 * 11008)
     assert lib.q4_gptq_workspace(16, 200, 32) == -1
     assert lib.q4_gptq_workspace(16, 32768 + 128, 128) == -1

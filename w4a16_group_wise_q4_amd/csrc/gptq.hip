@@ -20,65 +20,57 @@
 //   1. RTN quantize/pack: the static group scales and zero points (codes overwritten).
 //   2. A = reversed H, lower triangle, fp32: 2 sum_t x_t x_t^T; a zero diagonal becomes 1;
 //      the diagonal is scaled by 1 + damp.
-//   3. In-place blocked Cholesky of A (64-wide panels): factor the diagonal block in LDS,
-//      solve the rows below against it, subtract the panel's outer product from the
-//      trailing lower triangle.
+//   3. In-place blocked Cholesky of A (64-wide panels): factor the diagonal block in
+//      registers (and invert the factor), multiply the rows below by the inverse's
+//      transpose, subtract the panel's outer product from the trailing lower triangle.
 //   4. C = 0 (n x k accumulators of sum_{i<j} d_i U_ij).  For each block of 64 columns:
 //      the sweep (one lane per weight row, the block's 64 columns in order) writes the
-//      codes and the errors d of the block (column-major); the update adds d_block * U[block, later] to
-//      the accumulators of every later column.
+//      codes and the errors d of the block (column-major); updates add d * U[block, later]
+//      to the accumulators of later columns, lazily in super-blocks of 256 columns (see
+//      sweep_all).
 // Everything is fp32; the codes are the sweep's decisions in fp32 (the oracle's in fp64
 // may differ where a value falls within rounding of a code boundary).
 #include "q4_launch.h"
 
 namespace {
 
-constexpr int NB = 64;  // panel and block width
+constexpr int NB = 64;   // panel and block width
+constexpr int SB = 256;  // super-block width of the lazy updates (a multiple of NB)
 
 // ------------------------------------------------------------ 64 x 64 fp32 tile products
-// out[r][c] (r, c < 64) += sum_{s < 64} X[s][r] * Y[s][c], with X and Y in LDS k-major
-// ([64][64]: a row of 64 values per s).  Thread t of 256 owns rows 4 (t / 16) .. +3 and
-// columns 4 (t % 16) .. +3: per s one 16-byte read of X (shared by 16 threads) and one of Y
-// (16 consecutive threads read 64 consecutive floats) feed 16 FMAs.
+// On the fp32 matrix cores (v_mfma_f32_32x32x2_f32).  Four waves split the 64 x 64 output:
+// wave w computes rows 32 (w / 2) .. +31 and columns 32 (w % 2) .. +31.  Per MFMA, lane l
+// gives the A value of row l % 32 and the B value of column l % 32, both at inner index
+// s + l / 32; its 16 results are rows (e & 3) + 4 (l / 32) + 8 (e / 4) (e < 16) of
+// column l % 32 of the quadrant (tile_row / tile_col below).
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
+constexpr int RS = NB + 1;   // row stride of row-major LDS tiles (lanes of a read: all banks)
+constexpr int KS = NB;  // row stride of k-major LDS tiles (unpadded: occupancy over a 2-way read conflict)
 
-__device__ __forceinline__ void tile_fma(const float (*X)[NB], const float (*Y)[NB], float (&acc)[4][4]) {
-    const int t = threadIdx.x;
-    const int r0 = 4 * (t >> 4), c0 = 4 * (t & 15);
-#pragma unroll 8
-    for (int s = 0; s < NB; ++s) {
-        const f32x4v xv = *reinterpret_cast<const f32x4v*>(&X[s][r0]);
-        const f32x4v yv = *reinterpret_cast<const f32x4v*>(&Y[s][c0]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(xv[i], yv[j], acc[i][j]);
-    }
+__device__ __forceinline__ int tile_row(int e) {
+    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    return 32 * (w >> 1) + (e & 3) + 4 * (l >> 5) + 8 * (e >> 2);
+}
+__device__ __forceinline__ int tile_col() {
+    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    return 32 * (w & 1) + (l & 31);
 }
 
-// out[r][c] (r, c < 64) += sum_{s < 64} X[r][s] * Y[c][s], with X and Y in LDS row-major at a
-// row stride of RS floats.  Thread t owns rows t / 16 + 16 i and columns t % 16 + 16 j
-// (i, j < 4): per 4 values of s, four 16-byte reads of X (4 addresses per wave, broadcast)
-// and four of Y (16 addresses per wave, RS apart: every bank once) feed 64 FMAs.
-constexpr int RS = NB + 4;
+// acc += X^T Y over s < 64, with X and Y in LDS k-major (X[s][r], Y[s][c]) at stride KS.
+__device__ __forceinline__ void tile_mfma(const float (*X)[KS], const float (*Y)[KS], f32x16& acc) {
+    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int rb = 32 * (w >> 1) + (l & 31), cb = 32 * (w & 1) + (l & 31), h = l >> 5;
+#pragma unroll 8
+    for (int s = 0; s < NB; s += 2) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(X[s + h][rb], Y[s + h][cb], acc, 0, 0, 0);
+}
 
-__device__ __forceinline__ void tile_fma_rows(const float (*X)[RS], const float (*Y)[RS], float (&acc)[4][4]) {
-    const int t = threadIdx.x;
-    const int r = t >> 4, c = t & 15;
-#pragma unroll 2
-    for (int s = 0; s < NB; s += 4) {
-        f32x4v xv[4], yv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) xv[i] = *reinterpret_cast<const f32x4v*>(&X[r + 16 * i][s]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) yv[j] = *reinterpret_cast<const f32x4v*>(&Y[c + 16 * j][s]);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(xv[i][q], yv[j][q], acc[i][j]);
-    }
+// acc += X Y^T over s < 64, with X and Y in LDS row-major (X[r][s], Y[c][s]) at stride RS.
+__device__ __forceinline__ void tile_mfma_rows(const float (*X)[RS], const float (*Y)[RS], f32x16& acc) {
+    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int rb = 32 * (w >> 1) + (l & 31), cb = 32 * (w & 1) + (l & 31), h = l >> 5;
+#pragma unroll 8
+    for (int s = 0; s < NB; s += 2) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(X[rb][s + h], Y[cb][s + h], acc, 0, 0, 0);
 }
 
 template <bool XF16>
@@ -95,9 +87,9 @@ __global__ __launch_bounds__(256) void hessian_kernel(const uint16_t* __restrict
     const int tiles = (k + NB - 1) / NB;
     const int I = blockIdx.x / tiles, J = blockIdx.x % tiles;
     if (J > I) return;  // upper tiles: not needed (uniform)
-    __shared__ __attribute__((aligned(16))) float Xs[NB][NB], Ys[NB][NB];
+    __shared__ __attribute__((aligned(16))) float Xs[NB][KS], Ys[NB][KS];
     const int t = threadIdx.x;
-    float acc[4][4] = {};
+    f32x16 acc = {};
     for (int t0 = 0; t0 < tokens; t0 += NB) {
         // token slice [t0, t0 + 64): Xs[s][a] = x[t0 + s][k-1-(64 I + a)], Ys likewise for J
         for (int e = t; e < NB * NB; e += 256) {
@@ -108,83 +100,127 @@ __global__ __launch_bounds__(256) void hessian_kernel(const uint16_t* __restrict
             Ys[s][a] = tok < tokens && fb >= 0 ? half_to_float<XF16>(x[(int64_t)tok * k + fb]) : 0.f;
         }
         __syncthreads();
-        tile_fma(Xs, Ys, acc);
+        tile_mfma(Xs, Ys, acc);
         __syncthreads();
     }
-    const int r0 = 4 * (t >> 4), c0 = 4 * (t & 15);
+    const int cc = tile_col();
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int a = NB * I + r0 + i, b = NB * J + c0 + j;
-            if (a >= k || b > a) continue;
-            float h = 2.0f * acc[i][j];
-            if (a == b) {
-                if (h == 0.0f) h = 1.0f;  // a feature never active
-                h = h + damp * h;
-            }
-            A[(int64_t)a * k + b] = h;
+    for (int e = 0; e < 16; ++e) {
+        const int a = NB * I + tile_row(e), b = NB * J + cc;
+        if (a >= k || b > a) continue;
+        float h = 2.0f * acc[e];
+        if (a == b) {
+            if (h == 0.0f) h = 1.0f;  // a feature never active
+            h = h + damp * h;
         }
+        A[(int64_t)a * k + b] = h;
+    }
 }
 
 // ------------------------------------------------------------ step 3: blocked Cholesky
-// Factor the diagonal block A[j0 .. j0+bw)^2 (lower) in place, in LDS.
-__global__ __launch_bounds__(256) void chol_diag_kernel(float* __restrict__ A, int k, int j0, int bw) {
-    __shared__ float T[NB][NB + 1];
+// Factor the diagonal block A[j0 .. j0+bw)^2 (lower) in place, and store the inverse of the
+// factor, Linv = L^-1 (lower), by its strict lower part transposed into the block's upper
+// triangle, which nothing else uses: A[j0+s][j0+c] = Linv[c][s] for s < c.  (Linv's
+// diagonal is 1/L[c][c].)  Rows and columns past bw are an identity.
+//
+// Thread t holds row r = t % 64 of both matrices at the columns s = DW i + t/64 (i < 64/DW)
+// in registers; each of the DW waves owns one residue class of columns.  Step c, for
+// c = 0 .. 63:
+//   - the wave owning column c takes the root of its diagonal entry (lane c), scales the
+//     column and writes it to col[c] (each column once: no second barrier);
+//   - after the barrier every thread subtracts col[c][r] * col[c][s] from its entries s > c
+//     (right-looking factorization);
+//   - the inverse by forward substitution, one step behind: the rows of Linv below row c-1
+//     subtract L[r][c-1] * Linv[c-1][s], then row c divides by L[c][c] and goes to inv[c].
+// Sixteen waves keep each step's per-wave work short: the steps are a serial chain.
+constexpr int DW = 16, DPER = NB / DW;
+
+__global__ __launch_bounds__(64 * DW) void chol_diag_kernel(float* __restrict__ A, int k, int j0, int bw) {
+    __shared__ float col[NB][NB];  // col[c][r] = L[r][c] (0 above the diagonal)
+    __shared__ float inv[NB][NB];  // inv[c][s] = Linv[c][s] (0 right of the diagonal)
     const int t = threadIdx.x;
-    for (int e = t; e < NB * NB; e += 256) {
-        const int r = e / NB, c = e % NB;
-        T[r][c] = r < bw && c <= r ? A[(int64_t)(j0 + r) * k + j0 + c] : 0.f;
+    // w stays a vector value: as a scalar, the column predicates of a step would live in
+    // scalar register pairs and spill
+    const int r = t & 63, w = t >> 6;
+    float T[DPER], X[DPER];
+#pragma unroll
+    for (int i = 0; i < DPER; ++i) {
+        const int s = DW * i + w;
+        T[i] = r < bw && s <= r ? A[(int64_t)(j0 + r) * k + j0 + s] : (r == s ? 1.f : 0.f);
+        X[i] = r == s ? 1.f : 0.f;
     }
-    __syncthreads();
-    // thread t updates row r = t % 64, columns s = t / 64, +4, ... of the trailing block
-    const int ur = t & 63, us = t >> 6;
-    for (int c = 0; c < bw; ++c) {
-        const float d = sqrtf(T[c][c]);  // every thread: no barrier between the root and its use
-        __syncthreads();                 // all have read T[c][c] before it is overwritten
-        if (t == c) T[c][c] = d;
-        if (t > c && t < bw) T[t][c] = T[t][c] / d;
-        __syncthreads();
-        if (ur > c && ur < bw) {
-            const float lr = T[ur][c];
-            for (int s2 = c + 1 + ((us - (c + 1)) & 3); s2 <= ur; s2 += 4)
-                T[ur][s2] = __builtin_fmaf(-lr, T[s2][c], T[ur][s2]);
+    // fully unrolled: T[c / DW] must be a fixed register
+#pragma clang loop unroll(full)
+    for (int c = 0; c < NB; ++c) {
+        if (w == c % DW) {
+            const float v = T[c / DW];  // this lane's row, column c
+            const float dg = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), c));
+            const float d = sqrtf(dg);
+            const float l = r == c ? d : (r > c ? v / d : 0.f);
+            T[c / DW] = l;
+            col[c][r] = l;
         }
         __syncthreads();
+        // every read up front (broadcasts, always in range), then the updates as selects
+        float cs[DPER], is[DPER];
+#pragma unroll
+        for (int i = 0; i < DPER; ++i) {
+            cs[i] = col[c][DW * i + w];
+            is[i] = c > 0 ? inv[c - 1][DW * i + w] : 0.f;
+        }
+        const float lr = col[c][r];
+        const float lx = c > 0 ? col[c - 1][r] : 0.f;
+#pragma unroll
+        for (int i = 0; i < DPER; ++i) {
+            const int s = DW * i + w;
+            const float tv = __builtin_fmaf(-lr, cs[i], T[i]);
+            T[i] = s > c && s <= r ? tv : T[i];
+            const float xv = __builtin_fmaf(-lx, is[i], X[i]);
+            X[i] = c > 0 && r >= c && s <= c - 1 ? xv : X[i];
+        }
+        if (r == c) {
+            const float dinv = 1.0f / col[c][c];
+#pragma unroll
+            for (int i = 0; i < DPER; ++i) {
+                X[i] = DW * i + w <= c ? X[i] * dinv : 0.f;
+                inv[c][DW * i + w] = X[i];
+            }
+        }
     }
-    for (int e = t; e < NB * NB; e += 256) {
-        const int r = e / NB, c = e % NB;
-        if (r < bw && c <= r) A[(int64_t)(j0 + r) * k + j0 + c] = T[r][c];
+#pragma unroll
+    for (int i = 0; i < DPER; ++i) {
+        const int s = DW * i + w;
+        if (r < bw && s <= r) A[(int64_t)(j0 + r) * k + j0 + s] = T[i];
+        if (r < bw && s < r) A[(int64_t)(j0 + s) * k + j0 + r] = X[i];
     }
 }
 
-// Rows r >= j0 + bw: L[r][j0 + c] = (A[r][j0 + c] - sum_{s<c} L[r][j0+s] L[j0+c][j0+s]) / L[j0+c][j0+c].
+// Rows below the diagonal block, 64 per workgroup: L21 = A21 Linv^T, a 64 x 64 tile product
+// with the inverse stored by chol_diag_kernel (Y[c][s] = Linv[c][s]).
 __global__ __launch_bounds__(256) void chol_trsm_kernel(float* __restrict__ A, int k, int j0, int bw) {
-    __shared__ float D[NB][NB + 1];
+    __shared__ __attribute__((aligned(16))) float Xs[NB][RS], Ys[NB][RS];
     const int t = threadIdx.x;
+    const int base = j0 + bw + (int)blockIdx.x * NB;
     for (int e = t; e < NB * NB; e += 256) {
-        const int r = e / NB, c = e % NB;
-        D[r][c] = r < bw && c <= r ? A[(int64_t)(j0 + r) * k + j0 + c] : 0.f;
+        const int a = e / NB, b = e % NB;
+        Xs[a][b] = base + a < k && b < bw ? A[(int64_t)(base + a) * k + j0 + b] : 0.f;
+        // Ys[a][b] = Linv[a][b]
+        float v = 0.f;
+        if (a < bw && b < bw) {
+            if (b < a) v = A[(int64_t)(j0 + b) * k + j0 + a];
+            else if (b == a) v = 1.0f / A[(int64_t)(j0 + a) * k + j0 + a];
+        }
+        Ys[a][b] = v;
     }
     __syncthreads();
-    const int r = j0 + bw + (int)blockIdx.x * 256 + t;
-    if (r >= k) return;
-    float* row = A + (int64_t)r * k + j0;
-    float v[NB];
+    f32x16 acc = {};
+    tile_mfma_rows(Xs, Ys, acc);
+    const int cc = tile_col();
 #pragma unroll
-    for (int c = 0; c < NB; ++c) v[c] = c < bw ? row[c] : 0.f;
-#pragma unroll
-    for (int c = 0; c < NB; ++c) {
-        if (c < bw) {
-            float s = v[c];
-#pragma unroll
-            for (int q = 0; q < c; ++q) s = __builtin_fmaf(-v[q], D[c][q], s);
-            v[c] = s / D[c][c];
-        }
+    for (int e = 0; e < 16; ++e) {
+        const int a = base + tile_row(e);
+        if (a < k && cc < bw) A[(int64_t)a * k + j0 + cc] = acc[e];
     }
-#pragma unroll
-    for (int c = 0; c < NB; ++c)
-        if (c < bw) row[c] = v[c];
 }
 
 // Trailing update: A[a][b] -= sum_{s<bw} L[a][j0+s] L[b][j0+s] for j0+bw <= b <= a < k, in 64 x 64
@@ -203,15 +239,14 @@ __global__ __launch_bounds__(256) void chol_update_kernel(float* __restrict__ A,
         Ys[r][s] = b < k && s < bw ? A[(int64_t)b * k + j0 + s] : 0.f;
     }
     __syncthreads();
-    float acc[4][4] = {};
-    tile_fma_rows(Xs, Ys, acc);
+    f32x16 acc = {};
+    tile_mfma_rows(Xs, Ys, acc);
+    const int b = base + NB * J + tile_col();
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int a = base + NB * I + (t >> 4) + 16 * i, b = base + NB * J + (t & 15) + 16 * j;
-            if (a < k && b <= a) A[(int64_t)a * k + b] -= acc[i][j];
-        }
+    for (int e = 0; e < 16; ++e) {
+        const int a = base + NB * I + tile_row(e);
+        if (a < k && b <= a) A[(int64_t)a * k + b] -= acc[e];
+    }
 }
 
 // ------------------------------------------------------------ step 4: sweep and update
@@ -305,49 +340,66 @@ __global__ __launch_bounds__(64) void sweep_kernel(const void* __restrict__ w, i
         if (j < bw) Dout[(int64_t)j * n + row] = d[j];
 }
 
-// C[r][l] += sum_{i<bw} D[i][r] U_{j0+i, l} for the later columns l >= j0 + bw, in 64 x 64
-// tiles (row tile R, column tile L); D holds the block's errors column-major ([64][n]) and
+// C[r][l] += sum_{i < inner} D[i][r] U_{j0+i, l} for the columns col0 <= l < col1, in 64 x 64
+// tiles (row tile R, column tile L), the inner sum in chunks of 64 staged in LDS.  D holds
+// errors column-major ([inner][n], row i = weight column j0 + i) and
 // U_{j0+i, l} = A[k-1-(j0+i)][k-1-l].
 __global__ __launch_bounds__(256) void gptq_update_kernel(const float* __restrict__ A, const float* __restrict__ D,
-                                                          float* __restrict__ C, int n, int k, int j0, int bw) {
-    const int base = j0 + bw;
-    const int ctiles = (k - base + NB - 1) / NB;
+                                                          float* __restrict__ C, int n, int k, int j0, int inner,
+                                                          int col0, int col1) {
+    const int ctiles = (col1 - col0 + NB - 1) / NB;
     const int R = blockIdx.x / ctiles, Lt = blockIdx.x % ctiles;
-    __shared__ __attribute__((aligned(16))) float Xs[NB][NB], Ys[NB][NB];
+    __shared__ __attribute__((aligned(16))) float Xs[NB][KS], Ys[NB][KS];
     const int t = threadIdx.x;
-    for (int e = t; e < NB * NB; e += 256) {
-        // D is column-major ([64][n]) and U[j0 + s][col] has reversed, contiguous addresses
-        // along col: consecutive threads take consecutive rows, columns
-        const int s = e / NB, c = e % NB;
-        const int row = NB * R + c, col = base + NB * Lt + c;
-        Xs[s][c] = row < n && s < bw ? D[(int64_t)s * n + row] : 0.f;
-        Ys[s][c] = col < k && s < bw ? A[(int64_t)(k - 1 - (j0 + s)) * k + (k - 1 - col)] : 0.f;
-    }
-    __syncthreads();
-    float acc[4][4] = {};
-    tile_fma(Xs, Ys, acc);
-    const int r0 = 4 * (t >> 4), c0 = 4 * (t & 15);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = NB * R + r0 + i, col = base + NB * Lt + c0 + j;
-            if (row < n && col < k) C[(int64_t)row * k + col] += acc[i][j];
+    f32x16 acc = {};
+    for (int ch = 0; ch < inner; ch += NB) {
+        const int cw = inner - ch < NB ? inner - ch : NB;
+        for (int e = t; e < NB * NB; e += 256) {
+            // D is column-major and U[j0 + ch + s][col] has reversed, contiguous addresses
+            // along col: consecutive threads take consecutive rows, columns
+            const int s = e / NB, c = e % NB;
+            const int row = NB * R + c, col = col0 + NB * Lt + c;
+            Xs[s][c] = row < n && s < cw ? D[(int64_t)(ch + s) * n + row] : 0.f;
+            Ys[s][c] = col < col1 && s < cw ? A[(int64_t)(k - 1 - (j0 + ch + s)) * k + (k - 1 - col)] : 0.f;
         }
+        __syncthreads();
+        tile_mfma(Xs, Ys, acc);
+        __syncthreads();
+    }
+    const int col = col0 + NB * Lt + tile_col();
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int row = NB * R + tile_row(e);
+        if (row < n && col < col1) C[(int64_t)row * k + col] += acc[e];
+    }
 }
 
+void update(const float* A, const float* D, float* C, int n, int k, int j0, int inner, int col0, int col1,
+            hipStream_t st) {
+    if (col0 >= col1) return;
+    const int ctiles = (col1 - col0 + NB - 1) / NB;
+    hipLaunchKernelGGL(gptq_update_kernel, dim3(((n + NB - 1) / NB) * ctiles), dim3(256), 0, st, A, D, C, n, k, j0,
+                       inner, col0, col1);
+}
+
+// Lazy updates at two levels.  Blocks of 64 columns are swept in order inside super-blocks
+// of SB columns.  After a block, only the later columns of its super-block take its
+// errors; after a super-block, every column beyond it takes the errors of all its blocks
+// in one update with an inner size of SB.  The accumulator traffic falls by about SB / 64
+// against updating every later column after every block; the sums are the same.
 template <int DT, bool SYM>
 hipError_t sweep_all(const void* w, int n, int k, int g, const float* A, float* C, const uint16_t* sc,
                      const uint32_t* zr, uint32_t* qw, float* D, hipStream_t st) {
-    for (int j0 = 0; j0 < k; j0 += NB) {
-        const int bw = k - j0 < NB ? k - j0 : NB;
-        hipLaunchKernelGGL((sweep_kernel<DT, SYM>), dim3((n + 63) / 64), dim3(64), 0, st, w, n, k, g, A, C, sc,
-                           zr, qw, D, j0, bw);
-        if (j0 + bw < k) {
-            const int ctiles = (k - j0 - bw + NB - 1) / NB;
-            hipLaunchKernelGGL(gptq_update_kernel, dim3(((n + NB - 1) / NB) * ctiles), dim3(256), 0, st, A, D, C,
-                               n, k, j0, bw);
+    for (int s0 = 0; s0 < k; s0 += SB) {
+        const int s1 = k - s0 < SB ? k : s0 + SB;
+        for (int j0 = s0; j0 < s1; j0 += NB) {
+            const int bw = s1 - j0 < NB ? s1 - j0 : NB;
+            float* Db = D + (int64_t)(j0 - s0) * n;  // this block's rows of the super-block's errors
+            hipLaunchKernelGGL((sweep_kernel<DT, SYM>), dim3((n + 63) / 64), dim3(64), 0, st, w, n, k, g, A, C, sc,
+                               zr, qw, Db, j0, bw);
+            update(A, Db, C, n, k, j0, bw, j0 + bw, s1, st);   // the rest of the super-block
         }
+        update(A, D, C, n, k, s0, s1 - s0, s1, k, st);        // every column beyond it
     }
     return hipGetLastError();
 }
@@ -355,7 +407,7 @@ hipError_t sweep_all(const void* w, int n, int k, int g, const float* A, float* 
 }  // namespace
 
 int64_t q4k_gptq_workspace_floats(int64_t n, int64_t k) {
-    return k * k + n * k + n * NB;  // A, C, D
+    return k * k + n * k + n * SB;  // A, C, D
 }
 
 hipError_t q4k_gptq(const void* w, int w_dtype, int64_t n, int64_t k, const void* x, int x_dtype,
@@ -378,10 +430,10 @@ hipError_t q4k_gptq(const void* w, int w_dtype, int64_t n, int64_t k, const void
     // 3. Cholesky in place
     for (int j0 = 0; j0 < ki; j0 += NB) {
         const int bw = ki - j0 < NB ? ki - j0 : NB;
-        hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, st, A, ki, j0, bw);
+        hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(64 * DW), 0, st, A, ki, j0, bw);
         const int below = ki - j0 - bw;
         if (below > 0) {
-            hipLaunchKernelGGL(chol_trsm_kernel, dim3((below + 255) / 256), dim3(256), 0, st, A, ki, j0, bw);
+            hipLaunchKernelGGL(chol_trsm_kernel, dim3((below + NB - 1) / NB), dim3(256), 0, st, A, ki, j0, bw);
             const int tt = (below + NB - 1) / NB;
             hipLaunchKernelGGL(chol_update_kernel, dim3(tt * tt), dim3(256), 0, st, A, ki, j0, bw);
         }
