@@ -95,6 +95,10 @@ QUANT_CASES = [
     (2, 256, 128, 9, [(0, 9)]),
     (5, 128, 128, 33, [(32, 1)]),
     (7, 96, 32, 5, [(1, 3)]),                     # head_dim that attention does not take
+    (5, 64, 32, 11, [(2, 3), (9, 2)]),            # two groups per row, a part-filled last task
+    (3, 32, 32, 6, [(0, 5)]),                     # one group per row
+    (2, 512, 32, 4, [(1, 3)]),                    # 16 groups per row: the row kernel
+    (3, 512, 128, 5, [(0, 4)]),                   # a whole task per row
 ]
 
 

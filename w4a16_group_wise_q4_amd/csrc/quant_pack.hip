@@ -93,64 +93,10 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(const q4::QuantBatch bt
                 const bool valid = gidx < n_groups;
                 const uint32_t elem = (uint32_t)gidx * G + (uint32_t)t * E;  // within the row
 
-                // group statistics: zero-extended [min, max] (asymmetric) or max |w| (symmetric)
-                float s, x_min = 0.0f, x_max = 0.0f;
-                if constexpr (SYM) {
-                    float amax = 0.0f;
-#pragma unroll
-                    for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(v[e]));
-                    amax = xor_max(amax, 1);
-                    amax = xor_max(amax, 2);
-                    amax = xor_max(amax, 4);
-                    s = div_const<7>(amax);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < E; ++e) {
-                        x_min = fminf(x_min, v[e]);
-                        x_max = fmaxf(x_max, v[e]);
-                    }
-                    x_min = xor_min(x_min, 1); x_max = xor_max(x_max, 1);
-                    x_min = xor_min(x_min, 2); x_max = xor_max(x_max, 2);
-                    x_min = xor_min(x_min, 4); x_max = xor_max(x_max, 4);
-                    s = div_const<15>(x_max - x_min);
-                }
-                // stored fp16 scale: s is rounded to fp32 first, then to fp16 (round-to-nearest-
-                // even both times).  The empty asm pins s as an fp32 value: otherwise the compiler
-                // folds the last FMA of the division and the conversion into one fp16-rounding
-                // instruction, which differs from the double rounding on fp16 ties.
-                asm volatile("" : "+v"(s));
-                uint16_t s16 = __builtin_bit_cast(uint16_t, (_Float16)s);
-                if ((s16 & 0x7FFFu) == 0) s16 = 0x3C00u;
-                if (s16 == 0x7C00u) s16 = 0x7BFFu;
-                const float S = (float)__builtin_bit_cast(_Float16, s16);
-
+                uint16_t s16;
+                int zi;
                 uint32_t packed[(E + 7) / 8];
-#pragma unroll
-                for (int j = 0; j < (E + 7) / 8; ++j) packed[j] = 0;
-                int zi = 8;
-                if constexpr (DT == 0) {
-                    // fp32 weights: IEEE quotients
-                    float zf = 0.0f;
-                    if constexpr (!SYM) zf = fminf(fmaxf(rintf(-x_min / S), 0.0f), 15.0f);
-                    constexpr float q_min = SYM ? -8.0f : 0.0f;
-                    constexpr float q_max = SYM ? 7.0f : 15.0f;
-#pragma unroll
-                    for (int e = 0; e < E; ++e) {
-                        const float qf = fminf(fmaxf(rintf(v[e] / S) + zf, q_min), q_max);
-                        packed[e / 8] |= (uint32_t)((int)qf + (SYM ? 8 : 0)) << (4 * (e % 8));
-                    }
-                    if constexpr (!SYM) zi = (int)zf;
-                } else {
-                    // 16-bit weights: correctly rounded reciprocal once, corrected quotients;
-                    // -x_min is itself one of the group's weights (or 0)
-                    const float y = 1.0f / S;
-                    if constexpr (!SYM) zi = min(max(rne_small(quot16(-x_min, S, y)), 0), 15);
-#pragma unroll
-                    for (int e = 0; e < E; ++e) {
-                        const int u = min(max(rne_small(quot16(v[e], S, y)) + zi, 0), 15);
-                        packed[e / 8] |= (uint32_t)u << (4 * (e % 8));
-                    }
-                }
+                quant_group<G, SYM, DT>(v, s16, zi, packed);
 
                 // codes: E/2 bytes per lane, contiguous across the wave
                 const uint32_t qoff = valid ? elem / 2u : kOff;
@@ -173,6 +119,62 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(const q4::QuantBatch bt
             }
             row = nrow;
             zw = nzw;
+        }
+    }
+}
+
+// KV-cache rows (head_dim d dividing 512, at most 8 groups): one wave task is 512 consecutive weights, 512/d
+// input rows (contiguous in memory), and lane l quantizes weights 8l .. 8l+7 of it: row
+// 8l / d of the task, g/8 lanes per group.  A wave loads its task as one contiguous 1 KB
+// (bf16/fp16) and writes one code word per lane.  Each wave keeps P tasks' loads in
+// flight when there are tasks to spare.  The arithmetic is quant_group's, so the codes,
+// scales and zero points are those of the row kernel; the stores go to each row's
+// (head, token) slot of the cache with plain global stores (a wave's rows differ).
+template <int G, bool SYM, int DT>
+__global__ __launch_bounds__(256) void kv_quant_kernel(const void* __restrict__ kv, int rows, int d, int heads,
+                                                       int t_cap, int t0, uint32_t* __restrict__ qc,
+                                                       uint16_t* __restrict__ sc, uint32_t* __restrict__ zc) {
+    constexpr int E = 8, P = 4, LPG = G / E;
+    constexpr uint32_t EB = DT == 0 ? 4 : 2;
+    constexpr uint32_t kOff = 0xFFFFFFF0u;
+    const int lane = threadIdx.x & 63;
+    const int waves = (int)gridDim.x * (int)(blockDim.x >> 6);
+    const int gw = (int)blockIdx.x * (int)(blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int rpt = 512 / d;                  // rows per task
+    const int ro = (8 * lane) / d;            // this lane's row within the task
+    const int el = 8 * lane - ro * d;         // its first element within the row
+    const int gr = el / G;                    // its group within the row
+    const int lpr = d / 8;                    // lanes per row
+    const int tasks = (rows + rpt - 1) / rpt;
+    const q4::rsrc rw = q4::make_rsrc(kv, (uint32_t)rows * (uint32_t)d * EB);
+    for (int b = gw; b < tasks; b += P * waves) {
+        float v[P][E];
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const int tk = b + p * waves;
+            const bool live = tk < tasks && tk * rpt + ro < rows;
+            load_slice<E, DT>(rw, live ? ((uint32_t)tk * 512u + 8u * (uint32_t)lane) * EB : kOff, v[p]);
+        }
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const int tk = b + p * waves;
+            if (tk >= tasks) break;  // wave-uniform
+            const int row = tk * rpt + ro;  // input row: token * heads + head
+            uint16_t s16;
+            int zi;
+            uint32_t packed[1];
+            quant_group<G, SYM, DT, E>(v[p], s16, zi, packed);
+            // the row's zero word: the nibbles of its groups, OR-ed over the row's lanes
+            uint32_t zn = (uint32_t)zi << (4 * gr);
+#pragma unroll
+            for (int m = LPG; m < 64; m <<= 1)
+                if (m < lpr) zn |= __shfl_xor(zn, m, 64);
+            if (row < rows) {
+                const int64_t orow = (int64_t)(row % heads) * t_cap + t0 + row / heads;
+                qc[orow * (d / 8) + el / 8] = packed[0];
+                if (el % G == 0) sc[orow * (d / G) + gr] = s16;
+                if (!SYM && el == 0) zc[orow * ((d / G + 7) / 8)] = zn;
+            }
         }
     }
 }
@@ -233,15 +235,49 @@ hipError_t q4k_quant_pack(const void* w, int w_dtype, int64_t n, int64_t k, int 
     return launch_batch(bt, w_dtype, g, sym, stream, kname);
 }
 
+namespace {
+template <int G, bool SYM>
+hipError_t launch_kv(const void* kv, int dt, int rows, int d, int heads, int t_cap, int t0, uint32_t* qc,
+                     uint16_t* sc, uint32_t* zc, hipStream_t st) {
+    const int64_t tasks = ((int64_t)rows * d + 511) / 512;
+    const int64_t cap = (int64_t)(g_num_cus > 0 ? g_num_cus : 256) * 32;
+    const int64_t waves = tasks < cap ? tasks : cap;  // one task per wave while they last
+    const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+    if (dt == 0)
+        hipLaunchKernelGGL((kv_quant_kernel<G, SYM, 0>), grid, block, 0, st, kv, rows, d, heads, t_cap, t0, qc, sc, zc);
+    else if (dt == 1)
+        hipLaunchKernelGGL((kv_quant_kernel<G, SYM, 1>), grid, block, 0, st, kv, rows, d, heads, t_cap, t0, qc, sc, zc);
+    else
+        hipLaunchKernelGGL((kv_quant_kernel<G, SYM, 2>), grid, block, 0, st, kv, rows, d, heads, t_cap, t0, qc, sc, zc);
+    return hipGetLastError();
+}
+}  // namespace
+
 hipError_t q4k_kv_quantize(const void* kv, int dtype, int64_t t_new, int64_t heads, int64_t d, int g,
                            int sym, int64_t t_cap, int64_t t0, uint32_t* qcache, uint16_t* scache,
                            uint32_t* zcache, hipStream_t stream, const char** kname) {
+    static const char* names[3] = {"q4_kv_quant_f32", "q4_kv_quant_f16", "q4_kv_quant_bf16"};
+    const int64_t in_bytes = t_new * heads * d * (dtype == 0 ? 4 : 2);
+    // rows that divide a 512-weight task and hold at most one zero-point word
+    if (512 % d == 0 && d / g <= 8 && in_bytes < ((int64_t)1 << 31)) {
+        const int rows = (int)(t_new * heads), di = (int)d, hi = (int)heads, tc = (int)t_cap, t0i = (int)t0;
+        hipError_t e;
+        switch (g * 2 + (sym ? 1 : 0)) {
+        case 64: e = launch_kv<32, false>(kv, dtype, rows, di, hi, tc, t0i, qcache, scache, zcache, stream); break;
+        case 65: e = launch_kv<32, true>(kv, dtype, rows, di, hi, tc, t0i, qcache, scache, zcache, stream); break;
+        case 128: e = launch_kv<64, false>(kv, dtype, rows, di, hi, tc, t0i, qcache, scache, zcache, stream); break;
+        case 129: e = launch_kv<64, true>(kv, dtype, rows, di, hi, tc, t0i, qcache, scache, zcache, stream); break;
+        case 256: e = launch_kv<128, false>(kv, dtype, rows, di, hi, tc, t0i, qcache, scache, zcache, stream); break;
+        default: e = launch_kv<128, true>(kv, dtype, rows, di, hi, tc, t0i, qcache, scache, zcache, stream); break;
+        }
+        *kname = names[dtype];
+        return e;
+    }
     q4::QuantBatch bt{};
     bt.p[0] = q4::QuantProblem{kv, qcache, scache, zcache, (int)(t_new * heads), (int)d,
                                (int)heads, (int)t_cap, (int)t0};
     bt.count = 1;
     const hipError_t e = launch_batch(bt, dtype, g, sym, stream, kname);
-    static const char* names[3] = {"q4_kv_quant_f32", "q4_kv_quant_f16", "q4_kv_quant_bf16"};
     *kname = names[dtype];
     return e;
 }
