@@ -204,13 +204,15 @@ __global__ __launch_bounds__(256) void chol_trsm_kernel(float* __restrict__ A, i
     for (int e = t; e < NB * NB; e += 256) {
         const int a = e / NB, b = e % NB;
         Xs[a][b] = base + a < k && b < bw ? A[(int64_t)(base + a) * k + j0 + b] : 0.f;
-        // Ys[a][b] = Linv[a][b]
+        // Ys[c][s] = Linv[c][s], stored transposed in the block's upper triangle
+        // (A[j0+s][j0+c], s < c): consecutive threads take consecutive c, contiguous in A
+        const int s = e / NB, c = e % NB;
         float v = 0.f;
-        if (a < bw && b < bw) {
-            if (b < a) v = A[(int64_t)(j0 + b) * k + j0 + a];
-            else if (b == a) v = 1.0f / A[(int64_t)(j0 + a) * k + j0 + a];
+        if (c < bw && s < bw) {
+            if (s < c) v = A[(int64_t)(j0 + s) * k + j0 + c];
+            else if (s == c) v = 1.0f / A[(int64_t)(j0 + c) * k + j0 + c];
         }
-        Ys[a][b] = v;
+        Ys[c][s] = v;
     }
     __syncthreads();
     f32x16 acc = {};
@@ -262,82 +264,125 @@ __device__ __forceinline__ float load_w(const void* w, int64_t idx) {
     else return half_to_float<DT == 1>(reinterpret_cast<const uint16_t*>(w)[idx]);
 }
 
-// One lane per weight row; the block's columns j0 .. j0+bw-1 (bw = 64 or 32) in order.
-// U[i][j] for i, j in the block is A[k-1-(j0+i)][k-1-(j0+j)], staged transposed in LDS.
+// Four lanes per weight row (a quad of consecutive lanes); the block's columns j0 .. j0+bw-1
+// (bw = 64 or 32) in order.  Lane q of the quad holds the errors d_i of the columns
+// i = 4m + q and sums their share of sum_{i<j} d_i U_ij; the quad adds its four shares, so
+// every lane holds the same total and takes the same quantization decision for column j
+// (the errors of columns not yet reached are still zero, so the shares need no bounds).
+// U's block is staged transposed in LDS: UT[j][i] = U_ij (i <= j), zero elsewhere.
+// Lane q loads the block's C and weights for columns 16q .. 16q+15; column j's pair comes
+// from lane j / 16 of the quad by a lane broadcast.
+template <int SRC>
+__device__ __forceinline__ float quad_bcast_from(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), SRC * 0x55, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_bcast(float v, int src) {  // src folds to a constant in the unrolled sweep
+    switch (src) {
+    case 0: return quad_bcast_from<0>(v);
+    case 1: return quad_bcast_from<1>(v);
+    case 2: return quad_bcast_from<2>(v);
+    default: return quad_bcast_from<3>(v);
+    }
+}
+__device__ __forceinline__ float quad_sum(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));  // lane ^ 1
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));  // lane ^ 2
+}
+
 template <int DT, bool SYM>
-__global__ __launch_bounds__(64) void sweep_kernel(const void* __restrict__ w, int n, int k, int g,
-                                                   const float* __restrict__ A, const float* __restrict__ C,
-                                                   const uint16_t* __restrict__ scales,
-                                                   const uint32_t* __restrict__ zeros,
-                                                   uint32_t* __restrict__ qweight, float* __restrict__ Dout,
-                                                   int j0, int bw) {
+__global__ __launch_bounds__(256) void sweep_kernel(const void* __restrict__ w, int n, int k, int g,
+                                                    const float* __restrict__ A, const float* __restrict__ C,
+                                                    const uint16_t* __restrict__ scales,
+                                                    const uint32_t* __restrict__ zeros,
+                                                    uint32_t* __restrict__ qweight, float* __restrict__ Dout,
+                                                    int j0, int bw) {
     __shared__ float UT[NB][NB + 1];  // UT[j][i] = U_ij (i <= j), zero elsewhere
+    __shared__ float rU[NB];          // 1 / U_jj
     const int t = threadIdx.x;
-    for (int e = t; e < NB * NB; e += 64) {
-        const int j = e / NB, i = e % NB;
+    for (int e = t; e < NB * NB; e += 256) {
+        // consecutive threads take consecutive j: one row of A, contiguous (reversed) addresses
+        const int i = e / NB, j = e % NB;
         UT[j][i] = i <= j && j < bw ? A[(int64_t)(k - 1 - (j0 + i)) * k + (k - 1 - (j0 + j))] : 0.f;
     }
+    if (t < NB) rU[t] = t < bw ? 1.0f / A[(int64_t)(k - 1 - (j0 + t)) * k + (k - 1 - (j0 + t))] : 0.f;
     __syncthreads();
-    const int row = (int)blockIdx.x * 64 + t;
-    if (row >= n) return;
+    const int q = t & 3;
+    const int row = (int)blockIdx.x * 64 + (t >> 2);
+    if (row >= n) return;  // whole quads together; nothing below waits for other lanes
     const int n_groups = k / g, zwords = (n_groups + 7) / 8;
-    // the row's slice of C and of the weights for the block, in 16-byte loads (k is a multiple
-    // of 32 and the rows of w are 16-byte aligned)
-    float cv[NB], wv[NB];
-    const float* crow = C + (int64_t)row * k + j0;
+    // columns 16q .. 16q+15 of the row's C and weights, in 16-byte loads (k is a multiple of
+    // 32 and the rows of w are 16-byte aligned)
+    float cv[16], wv[16];
+    const int c0 = 16 * q;
+    const float* crow = C + (int64_t)row * k + j0 + c0;
 #pragma unroll
-    for (int q = 0; q < NB / 4; ++q) {
-        const f32x4v v = 4 * q < bw ? *reinterpret_cast<const f32x4v*>(crow + 4 * q) : f32x4v{0.f, 0.f, 0.f, 0.f};
+    for (int v = 0; v < 4; ++v) {
+        const f32x4v x = c0 + 4 * v < bw ? *reinterpret_cast<const f32x4v*>(crow + 4 * v) : f32x4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) cv[4 * q + e] = v[e];
+        for (int e = 0; e < 4; ++e) cv[4 * v + e] = x[e];
     }
     if constexpr (DT == 0) {
-        const float* wrow = reinterpret_cast<const float*>(w) + (int64_t)row * k + j0;
+        const float* wrow = reinterpret_cast<const float*>(w) + (int64_t)row * k + j0 + c0;
 #pragma unroll
-        for (int q = 0; q < NB / 4; ++q) {
-            const f32x4v v = 4 * q < bw ? *reinterpret_cast<const f32x4v*>(wrow + 4 * q) : f32x4v{0.f, 0.f, 0.f, 0.f};
+        for (int v = 0; v < 4; ++v) {
+            const f32x4v x = c0 + 4 * v < bw ? *reinterpret_cast<const f32x4v*>(wrow + 4 * v) : f32x4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) wv[4 * q + e] = v[e];
+            for (int e = 0; e < 4; ++e) wv[4 * v + e] = x[e];
         }
     } else {
         typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-        const uint16_t* wrow = reinterpret_cast<const uint16_t*>(w) + (int64_t)row * k + j0;
+        const uint16_t* wrow = reinterpret_cast<const uint16_t*>(w) + (int64_t)row * k + j0 + c0;
 #pragma unroll
-        for (int q = 0; q < NB / 8; ++q) {
-            const u32x4v v = 8 * q < bw ? *reinterpret_cast<const u32x4v*>(wrow + 8 * q) : u32x4v{0u, 0u, 0u, 0u};
+        for (int v = 0; v < 2; ++v) {
+            const u32x4v x = c0 + 8 * v < bw ? *reinterpret_cast<const u32x4v*>(wrow + 8 * v) : u32x4v{0u, 0u, 0u, 0u};
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                wv[8 * q + e] = half_to_float<DT == 1>((uint16_t)(v[e / 2] >> (16 * (e % 2))));
+                wv[8 * v + e] = half_to_float<DT == 1>((uint16_t)(x[e / 2] >> (16 * (e % 2))));
         }
     }
-    float d[NB];
+    float dl[NB / 4];  // d_i for i = 4m + q (zero until column i is quantized)
+#pragma unroll
+    for (int m = 0; m < NB / 4; ++m) dl[m] = 0.f;
     uint32_t words[NB / 8];
 #pragma unroll
-    for (int q = 0; q < NB / 8; ++q) words[q] = 0u;
+    for (int m = 0; m < NB / 8; ++m) words[m] = 0u;
+    // The column loop is a serial chain: the divisions by U_jj and by the scale are
+    // multiplications by reciprocals taken once per block and once per group, and the
+    // lane's share of each dot product runs in two interleaved sums.
+    float S = 1.f, rS = 1.f, z = 8.f;
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-        d[j] = 0.f;
         if (j < bw) {
             const int col = j0 + j, gi = col / g;
-            const float S = (float)__builtin_bit_cast(_Float16, scales[(int64_t)row * n_groups + gi]);
-            const float z = SYM ? 8.f : (float)((zeros[(int64_t)row * zwords + gi / 8] >> (4 * (gi % 8))) & 0xFu);
-            // sum_{i<j} d_i U_ij in four interleaved partial sums (a shorter dependency chain)
-            float p[4] = {cv[j], 0.f, 0.f, 0.f};
+            if (j == 0 || col % g == 0) {  // a new group (uniform)
+                S = (float)__builtin_bit_cast(_Float16, scales[(int64_t)row * n_groups + gi]);
+                rS = 1.0f / S;
+                if constexpr (!SYM) z = (float)((zeros[(int64_t)row * zwords + gi / 8] >> (4 * (gi % 8))) & 0xFu);
+            }
+            const float cj = quad_bcast(cv[j % 16], j / 16);
+            const float wj = quad_bcast(wv[j % 16], j / 16);
+            // this lane's share of sum_{i<j} d_i U_ij (entries with i >= j are zero)
+            float p0 = 0.f, p1 = 0.f;
 #pragma unroll
-            for (int i = 0; i < j; ++i) p[i & 3] = __builtin_fmaf(d[i], UT[j][i], p[i & 3]);
-            const float sum = (p[0] + p[1]) + (p[2] + p[3]);
-            const float wp = wv[j] + sum / UT[j][j];
-            const float u = fminf(fmaxf(rintf(wp / S) + z, 0.f), 15.f);
-            d[j] = wv[j] - S * (u - z);
+            for (int m = 0; m < (j + 3) / 4; ++m) {
+                if (m % 2 == 0) p0 = __builtin_fmaf(dl[m], UT[j][4 * m + q], p0);
+                else p1 = __builtin_fmaf(dl[m], UT[j][4 * m + q], p1);
+            }
+            const float sum = quad_sum(p0 + p1) + cj;
+            const float wp = __builtin_fmaf(sum, rU[j], wj);
+            const float u = fminf(fmaxf(rintf(wp * rS) + z, 0.f), 15.f);
+            const float dj = wj - S * (u - z);
+            dl[j / 4] = q == (j & 3) ? dj : dl[j / 4];
             words[j / 8] |= (uint32_t)u << (4 * (j % 8));
         }
     }
+    // lane q stores code words 2q, 2q+1 (columns 16q .. 16q+15) and its own errors
 #pragma unroll
-    for (int q = 0; q < NB / 8; ++q)
-        if (8 * q < bw) qweight[(int64_t)row * (k / 8) + j0 / 8 + q] = words[q];
+    for (int m = 0; m < NB / 8; ++m)
+        if (m / 2 == q && 8 * m < bw) qweight[(int64_t)row * (k / 8) + j0 / 8 + m] = words[m];
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
-        if (j < bw) Dout[(int64_t)j * n + row] = d[j];
+    for (int m = 0; m < NB / 4; ++m)
+        if (4 * m + q < bw) Dout[(int64_t)(4 * m + q) * n + row] = dl[m];
 }
 
 // C[r][l] += sum_{i < inner} D[i][r] U_{j0+i, l} for the columns col0 <= l < col1, in 64 x 64
@@ -395,7 +440,7 @@ hipError_t sweep_all(const void* w, int n, int k, int g, const float* A, float* 
         for (int j0 = s0; j0 < s1; j0 += NB) {
             const int bw = s1 - j0 < NB ? s1 - j0 : NB;
             float* Db = D + (int64_t)(j0 - s0) * n;  // this block's rows of the super-block's errors
-            hipLaunchKernelGGL((sweep_kernel<DT, SYM>), dim3((n + 63) / 64), dim3(64), 0, st, w, n, k, g, A, C, sc,
+            hipLaunchKernelGGL((sweep_kernel<DT, SYM>), dim3((n + 63) / 64), dim3(256), 0, st, w, n, k, g, A, C, sc,
                                zr, qw, Db, j0, bw);
             update(A, Db, C, n, k, j0, bw, j0 + bw, s1, st);   // the rest of the super-block
         }
