@@ -90,18 +90,33 @@ __global__ __launch_bounds__(256) void hessian_kernel(const uint16_t* __restrict
     __shared__ __attribute__((aligned(16))) float Xs[NB][KS], Ys[NB][KS];
     const int t = threadIdx.x;
     f32x16 acc = {};
-    for (int t0 = 0; t0 < tokens; t0 += NB) {
-        // token slice [t0, t0 + 64): Xs[s][a] = x[t0 + s][k-1-(64 I + a)], Ys likewise for J
-        for (int e = t; e < NB * NB; e += 256) {
-            const int s = e / NB, a = e % NB;
+    // token slice [t0, t0 + 64): Xs[s][a] = x[t0 + s][k-1-(64 I + a)], Ys likewise for J.
+    // This thread's 16 elements of a slice are loaded into registers a slice ahead, so the
+    // next slice's loads are in flight while the current one's products run.
+    constexpr int PER = NB * NB / 256;
+    uint16_t xr[PER], yr[PER];
+    auto fetch = [&](int t0) {
+#pragma unroll
+        for (int r = 0; r < PER; ++r) {
+            const int e = t + 256 * r, s = e / NB, a = e % NB;
             const int tok = t0 + s;
             const int fa = k - 1 - (NB * I + a), fb = k - 1 - (NB * J + a);
-            Xs[s][a] = tok < tokens && fa >= 0 ? half_to_float<XF16>(x[(int64_t)tok * k + fa]) : 0.f;
-            Ys[s][a] = tok < tokens && fb >= 0 ? half_to_float<XF16>(x[(int64_t)tok * k + fb]) : 0.f;
+            xr[r] = tok < tokens && fa >= 0 ? x[(int64_t)tok * k + fa] : (uint16_t)0;
+            yr[r] = tok < tokens && fb >= 0 ? x[(int64_t)tok * k + fb] : (uint16_t)0;
+        }
+    };
+    fetch(0);
+    for (int t0 = 0; t0 < tokens; t0 += NB) {
+        __syncthreads();  // the previous slice's products have read the tiles
+#pragma unroll
+        for (int r = 0; r < PER; ++r) {
+            const int e = t + 256 * r;
+            Xs[e / NB][e % NB] = half_to_float<XF16>(xr[r]);  // 0 bits convert to 0.0
+            Ys[e / NB][e % NB] = half_to_float<XF16>(yr[r]);
         }
         __syncthreads();
+        if (t0 + NB < tokens) fetch(t0 + NB);
         tile_mfma(Xs, Ys, acc);
-        __syncthreads();
     }
     const int cc = tile_col();
 #pragma unroll
@@ -397,19 +412,34 @@ __global__ __launch_bounds__(256) void gptq_update_kernel(const float* __restric
     __shared__ __attribute__((aligned(16))) float Xs[NB][KS], Ys[NB][KS];
     const int t = threadIdx.x;
     f32x16 acc = {};
-    for (int ch = 0; ch < inner; ch += NB) {
+    // this thread's 16 elements of a chunk in registers: the next chunk's loads are in
+    // flight while the current chunk's products run
+    constexpr int PER = NB * NB / 256;
+    float xr[PER], yr[PER];
+    auto fetch = [&](int ch) {
         const int cw = inner - ch < NB ? inner - ch : NB;
-        for (int e = t; e < NB * NB; e += 256) {
+#pragma unroll
+        for (int r = 0; r < PER; ++r) {
             // D is column-major and U[j0 + ch + s][col] has reversed, contiguous addresses
             // along col: consecutive threads take consecutive rows, columns
-            const int s = e / NB, c = e % NB;
+            const int e = t + 256 * r, s = e / NB, c = e % NB;
             const int row = NB * R + c, col = col0 + NB * Lt + c;
-            Xs[s][c] = row < n && s < cw ? D[(int64_t)(ch + s) * n + row] : 0.f;
-            Ys[s][c] = col < col1 && s < cw ? A[(int64_t)(k - 1 - (j0 + ch + s)) * k + (k - 1 - col)] : 0.f;
+            xr[r] = row < n && s < cw ? D[(int64_t)(ch + s) * n + row] : 0.f;
+            yr[r] = col < col1 && s < cw ? A[(int64_t)(k - 1 - (j0 + ch + s)) * k + (k - 1 - col)] : 0.f;
+        }
+    };
+    fetch(0);
+    for (int ch = 0; ch < inner; ch += NB) {
+        __syncthreads();  // the previous chunk's products have read the tiles
+#pragma unroll
+        for (int r = 0; r < PER; ++r) {
+            const int e = t + 256 * r;
+            Xs[e / NB][e % NB] = xr[r];
+            Ys[e / NB][e % NB] = yr[r];
         }
         __syncthreads();
+        if (ch + NB < inner) fetch(ch + NB);
         tile_mfma(Xs, Ys, acc);
-        __syncthreads();
     }
     const int col = col0 + NB * Lt + tile_col();
 #pragma unroll
