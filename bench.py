@@ -44,6 +44,13 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+# The clip search is bound by vector instruction issue: 256 CUs x 4 SIMDs x 16 lanes x
+# 2.4 GHz = 39.3e12 lane-instructions/s, over the vector instructions the g = 128 bf16
+# kernel issues per weight (its task loop: 3041 instructions per 16 weights per lane
+# asymmetric, 2640 symmetric, counted in the gfx950 assembly of this source).
+VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
+MSE_ALU_PEAK_GWEIGHTS = {"asym": round(VALU_LANE_OPS / (3041 / 16) / 1e9, 1),
+                         "sym": round(VALU_LANE_OPS / (2640 / 16) / 1e9, 1)}
 MALL_BYTES = 256 * 2 ** 20
 METRIC = "W4A16 GEMV achieved HBM GB/s (% peak) at M=1; GEMM TFLOP/s (% MFMA peak)"
 
@@ -399,14 +406,20 @@ def main():
                 e_m = (q4.q4_dequant(pm) - wf).double().pow(2).sum().item()
                 e_r = (q4.q4_dequant(pr) - wf).double().pow(2).sum().item()
                 qb = quant_bytes(mat.n, mat.k, 128, sym)
+                gw = mat.n * mat.k / t / 1e9
+                peak = MSE_ALU_PEAK_GWEIGHTS["sym" if sym else "asym"]
                 res[f"{mat.n}x{mat.k} {'sym' if sym else 'asym'}"] = {
                     "kernel": kname, "us": round(t * 1e6, 1), "gbs": round(qb / t / 1e9, 1),
-                    "gweights_per_s": round(mat.n * mat.k / t / 1e9, 1),
-                    "sq_error_vs_rtn": round(e_m / e_r, 4)}
+                    "gweights_per_s": round(gw, 1), "alu_peak_gweights_per_s": peak,
+                    "frac_alu": round(gw / peak, 4), "sq_error_vs_rtn": round(e_m / e_r, 4)}
                 del pm, pr
             del w, wf
         out["mse_clip"] = {"workload": "7B-like decode matrices, bf16, g128, clip ratios (20-i)/20, "
-                                       "i = 0..10, per group", "bound": "alu", "results": res}
+                                       "i = 0..10, per group", "bound": "alu",
+                           "alu_peak": "vector issue: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3e12 "
+                                       "lane-instructions/s over the kernel's vector instructions per "
+                                       "weight (190.1 asym, 165.0 sym at g128 bf16)",
+                           "results": res}
 
     # ------------------------------------------------------------ INT4 KV cache (decode attention)
     if "kv" in legs:
