@@ -18,8 +18,8 @@
 //
 // Steps, all on the caller's stream:
 //   1. RTN quantize/pack: the static group scales and zero points (codes overwritten).
-//   2. A = reversed H, lower triangle, fp32: 2 sum_t x_t x_t^T; a zero diagonal becomes 1;
-//      the diagonal is scaled by 1 + damp.
+//   2. A = reversed H, lower triangle, fp32: 2 sum_t x_t x_t^T (128 x 128 tiles); a zero
+//      diagonal becomes 1; the diagonal is scaled by 1 + damp.
 //   3. In-place blocked Cholesky of A (64-wide panels): factor the diagonal block in
 //      registers (and invert the factor), multiply the rows below by the inverse's
 //      transpose, subtract the panel's outer product from the trailing lower triangle.
@@ -80,56 +80,81 @@ __device__ __forceinline__ float half_to_float(uint16_t h) {
 }
 
 // ------------------------------------------------------------ step 2: reversed Hessian
-// Workgroup (I, J), I >= J, computes the 64 x 64 tile A[64 I ..][64 J ..] over all tokens.
+// Workgroup (I, J), I >= J, computes the 128 x 128 tile A[128 I ..][128 J ..] over all
+// tokens; wave w computes the 64 x 64 quadrant (w / 2, w % 2) as 2 x 2 MFMA tiles.  The
+// tiles are twice the panel width so that the activations are read half as often (each
+// token slice of a tile pair is staged once per 128 x 128 outputs).
+constexpr int HB = 128;
+
 template <bool XF16>
 __global__ __launch_bounds__(256) void hessian_kernel(const uint16_t* __restrict__ x, int tokens, int k,
                                                       float damp, float* __restrict__ A) {
-    const int tiles = (k + NB - 1) / NB;
+    const int tiles = (k + HB - 1) / HB;
     const int I = blockIdx.x / tiles, J = blockIdx.x % tiles;
     if (J > I) return;  // upper tiles: not needed (uniform)
-    __shared__ __attribute__((aligned(16))) float Xs[NB][KS], Ys[NB][KS];
+    // token slice [t0, t0 + 64): Xs[s][a] = x[t0 + s][k-1-(128 I + a)], Ys likewise for J
+    __shared__ __attribute__((aligned(16))) float Xs[NB][HB], Ys[NB][HB];
     const int t = threadIdx.x;
-    f32x16 acc = {};
-    // token slice [t0, t0 + 64): Xs[s][a] = x[t0 + s][k-1-(64 I + a)], Ys likewise for J.
-    // This thread's 16 elements of a slice are loaded into registers a slice ahead, so the
-    // next slice's loads are in flight while the current one's products run.
-    constexpr int PER = NB * NB / 256;
-    uint16_t xr[PER], yr[PER];
+    const int l = t & 63, w = t >> 6, h = l >> 5, li = l & 31;
+    const int rb = 64 * (w >> 1), cb = 64 * (w & 1);
+    f32x16 acc[2][2] = {};
+    // This thread's 16 feature pairs of a slice (one 32-bit word each: features a and a+1
+    // are adjacent, reversed, in the row) are loaded a slice ahead, so the next slice's
+    // loads are in flight while the current one's products run.  k is even and a row
+    // starts 4-byte aligned, so the pair (k-1-(128 I + a) - 1, k-1-(128 I + a)) is one word.
+    constexpr int PP = NB * HB / 2 / 256;
+    const uint32_t* x32 = reinterpret_cast<const uint32_t*>(x);
+    uint32_t xr[PP], yr[PP];
     auto fetch = [&](int t0) {
 #pragma unroll
-        for (int r = 0; r < PER; ++r) {
-            const int e = t + 256 * r, s = e / NB, a = e % NB;
+        for (int r = 0; r < PP; ++r) {
+            const int e = t + 256 * r, s = e / (HB / 2), a = 2 * (e % (HB / 2));
             const int tok = t0 + s;
-            const int fa = k - 1 - (NB * I + a), fb = k - 1 - (NB * J + a);
-            xr[r] = tok < tokens && fa >= 0 ? x[(int64_t)tok * k + fa] : (uint16_t)0;
-            yr[r] = tok < tokens && fb >= 0 ? x[(int64_t)tok * k + fb] : (uint16_t)0;
+            const int fa = k - 1 - (HB * I + a), fb = k - 1 - (HB * J + a);
+            xr[r] = tok < tokens && fa >= 0 ? x32[((int64_t)tok * k + fa - 1) / 2] : 0u;
+            yr[r] = tok < tokens && fb >= 0 ? x32[((int64_t)tok * k + fb - 1) / 2] : 0u;
         }
     };
     fetch(0);
     for (int t0 = 0; t0 < tokens; t0 += NB) {
         __syncthreads();  // the previous slice's products have read the tiles
 #pragma unroll
-        for (int r = 0; r < PER; ++r) {
-            const int e = t + 256 * r;
-            Xs[e / NB][e % NB] = half_to_float<XF16>(xr[r]);  // 0 bits convert to 0.0
-            Ys[e / NB][e % NB] = half_to_float<XF16>(yr[r]);
+        for (int r = 0; r < PP; ++r) {
+            const int e = t + 256 * r, s = e / (HB / 2), a = 2 * (e % (HB / 2));
+            // the high half is feature a (x[fa]), the low half feature a + 1 (x[fa - 1])
+            Xs[s][a] = half_to_float<XF16>((uint16_t)(xr[r] >> 16));
+            Xs[s][a + 1] = half_to_float<XF16>((uint16_t)(xr[r] & 0xFFFFu));
+            Ys[s][a] = half_to_float<XF16>((uint16_t)(yr[r] >> 16));
+            Ys[s][a + 1] = half_to_float<XF16>((uint16_t)(yr[r] & 0xFFFFu));
         }
         __syncthreads();
         if (t0 + NB < tokens) fetch(t0 + NB);
-        tile_mfma(Xs, Ys, acc);
-    }
-    const int cc = tile_col();
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const int a = NB * I + tile_row(e), b = NB * J + cc;
-        if (a >= k || b > a) continue;
-        float h = 2.0f * acc[e];
-        if (a == b) {
-            if (h == 0.0f) h = 1.0f;  // a feature never active
-            h = h + damp * h;
+#pragma unroll 4
+        for (int s = 0; s < NB; s += 2) {
+            const float a0 = Xs[s + h][rb + li], a1 = Xs[s + h][rb + 32 + li];
+            const float b0 = Ys[s + h][cb + li], b1 = Ys[s + h][cb + 32 + li];
+            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
+            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
+            acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
+            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
         }
-        A[(int64_t)a * k + b] = h;
     }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int a = HB * I + rb + 32 * i + (e & 3) + 4 * h + 8 * (e >> 2);
+                const int b = HB * J + cb + 32 * j + li;
+                if (a >= k || b > a) continue;
+                float hv = 2.0f * acc[i][j][e];
+                if (a == b) {
+                    if (hv == 0.0f) hv = 1.0f;  // a feature never active
+                    hv = hv + damp * hv;
+                }
+                A[(int64_t)a * k + b] = hv;
+            }
 }
 
 // ------------------------------------------------------------ step 3: blocked Cholesky
@@ -496,7 +521,7 @@ hipError_t q4k_gptq(const void* w, int w_dtype, int64_t n, int64_t k, const void
     float* D = C + n * k;
     const int ki = (int)k, ni = (int)n;
     // 2. reversed Hessian, lower triangle
-    const int tiles = (ki + NB - 1) / NB;
+    const int tiles = (ki + HB - 1) / HB;
     const uint16_t* xs = reinterpret_cast<const uint16_t*>(x);
     if (x_dtype == 1)
         hipLaunchKernelGGL(hessian_kernel<true>, dim3(tiles * tiles), dim3(256), 0, st, xs, (int)tokens, ki, damp, A);
