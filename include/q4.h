@@ -134,6 +134,19 @@ q4_status q4_w4a16_gemm(const void* x, q4_dtype x_dtype, int64_t m,
                         int64_t n, int64_t k, int32_t group_size, int32_t symmetric,
                         float* y, hipStream_t stream);
 
+/* q4_w4a16_gemm with the output written as y_dtype: Q4_F32 (identical to q4_w4a16_gemm),
+ * or Q4_F16 / Q4_BF16, the 16-bit activations that the next W4A16 layer takes ([YJ]
+ * §Notation: W4A16 is 4-bit weights with 16-bit activations).  The same kernels accumulate
+ * in fp32 and round each element once, to nearest even, as they store it (the output
+ * epilogue): a 16-bit y is exactly the rounding of the fp32 y this call would give with
+ * Q4_F32.  Accuracy: the bound above plus half an ulp of the 16-bit type (relative 2^-8
+ * for bf16, 2^-11 for fp16); fp16 outputs beyond 65504 become infinities.  y alignment: 4
+ * bytes for Q4_F32, 2 bytes otherwise; another y_dtype is Q4_ERR_DTYPE. */
+q4_status q4_w4a16_gemm_out(const void* x, q4_dtype x_dtype, int64_t m,
+                            const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros,
+                            int64_t n, int64_t k, int32_t group_size, int32_t symmetric,
+                            void* y, q4_dtype y_dtype, hipStream_t stream);
+
 /* One problem of a grouped call: y = x . x_hat^T for one packed weight. */
 typedef struct {
     const void* x;            /* [m][k] activations, in the dtype of the call */
@@ -141,7 +154,8 @@ typedef struct {
     const uint16_t* scales;   /* [n][k/g] fp16 bit patterns */
     const uint32_t* zeros;    /* [n][ceil(k/g/8)] zero points; may be NULL when symmetric */
     int64_t n;                /* output features of this problem */
-    float* y;                 /* [m][n] fp32 output */
+    void* y;                  /* [m][n] output: fp32 for q4_w4a16_gemm_grouped, y_dtype for
+                                 q4_w4a16_gemm_grouped_out */
 } q4_gemm_problem;
 
 /* Several independent W4A16 products that share m, k, group_size, symmetry and the
@@ -156,6 +170,12 @@ typedef struct {
 q4_status q4_w4a16_gemm_grouped(const q4_gemm_problem* problems, int32_t count,
                                 q4_dtype x_dtype, int64_t m, int64_t k, int32_t group_size,
                                 int32_t symmetric, hipStream_t stream);
+
+/* q4_w4a16_gemm_grouped with every y written as y_dtype (the output epilogue of
+ * q4_w4a16_gemm_out; the same rules per problem). */
+q4_status q4_w4a16_gemm_grouped_out(const q4_gemm_problem* problems, int32_t count,
+                                    q4_dtype x_dtype, int64_t m, int64_t k, int32_t group_size,
+                                    int32_t symmetric, q4_dtype y_dtype, hipStream_t stream);
 
 /* ---- INT4 KV cache ([QA1] KV-cache chapter: §KV cache의 bandwidth 부담, §Per-token scale
  * 수식, §asym 선택 이유, §Attention에서의 결합, §INT4 group scheme; [FL7] §KV Cache

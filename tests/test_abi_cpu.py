@@ -93,6 +93,37 @@ def test_host_validation_rejects_before_launch(call, code):
     assert q4.q4_last_kernel() == ""  # nothing was launched
 
 
+def _mmo(yd=BF16, y=A16, m=1, **kw):
+    a = dict(x=A16, xd=BF16, qw=A16, sc=A16, zr=A16, n=16, k=256, g=128, sym=0)
+    a.update(kw)
+    return q4.lib().q4_w4a16_gemm_out(a["x"], a["xd"], m, a["qw"], a["sc"], a["zr"], a["n"], a["k"],
+                                      a["g"], a["sym"], y, yd, None)
+
+
+@pytest.mark.parametrize("call,code", [
+    (lambda: _mmo(yd=3), DTYPE), (lambda: _mmo(yd=-1), DTYPE), (lambda: _mmo(y=None), NULL),
+    (lambda: _mmo(yd=F32, y=A16 + 2), ALIGN), (lambda: _mmo(yd=BF16, y=A16 + 1), ALIGN),
+    (lambda: _mmo(yd=F16, y=A16 + 1), ALIGN), (lambda: _mmo(m=0), SHAPE),
+    (lambda: _mmo(xd=F32), DTYPE),
+])
+def test_output_dtype_validation_rejects_before_launch(call, code):
+    """The output-dtype entry point: y_dtype is fp32, fp16 or bf16; a 16-bit y needs only
+    2-byte alignment (checked here by a y 2 bytes past a 16-byte boundary passing the
+    alignment rule and failing later on m)."""
+    assert call() == code
+    assert q4.q4_last_kernel() == ""
+
+
+def test_output_dtype_16bit_alignment_is_two_bytes():
+    assert _mmo(yd=BF16, y=A16 + 2, m=0) == SHAPE  # alignment passed, shape rejected
+    assert _mmo(yd=F32, y=A16 + 2, m=0) == SHAPE   # shape is checked first
+    arr = (q4.GemmProblem * 2)()
+    arr[0] = q4.GemmProblem(A16, A16, A16, A16, 16, A16 + 2)
+    arr[1] = q4.GemmProblem(A16, A16, A16, A16, 16, A16)
+    assert q4.lib().q4_w4a16_gemm_grouped_out(arr, 2, BF16, 1, 256, 128, 0, 4, None) == DTYPE
+    assert q4.lib().q4_w4a16_gemm_grouped_out(arr, 2, BF16, 1, 256, 128, 0, F32, None) == ALIGN
+
+
 def test_symmetric_accepts_null_zeros_in_validation():
     # symmetric mode needs no zero points; with a bad group the call still fails on the
     # group (validated first), proving the NULL zeros pointer itself is accepted

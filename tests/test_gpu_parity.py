@@ -679,3 +679,80 @@ def test_gemm_prefill_70b_sampled():
     yg = y[np.ix_(rows_x, rows_w)]
     ok = oracle.within_tolerance(yg, yr, ya)
     assert ok.all(), f"{int((~ok).sum())} sampled outputs outside the bound"
+
+
+# --------------------------------------------------------------------------- output epilogue
+# (m, n, k, g, path): every product path with a 16-bit output: the tile kernel, the wide
+# kernel (one tile and two tiles per workgroup), the streaming kernel (k not a multiple of
+# 128), the chunked mid-M GEMV and the prefill GEMM (a ragged m, and k ending on a half stage)
+EPILOGUE_CASES = [(1, 300, 1024, 128, "tile"), (3, 130, 2048, 64, "tile"), (8, 100, 1024, 32, "wide"),
+                  (16, 16392, 512, 128, "wide"), (2, 300, 4096 + 64, 64, "mfma"), (40, 1000, 1024, 64, "midm"),
+                  (300, 129, 96, 32, "gemm"), (257, 300, 512, 128, "gemm")]
+HALF_ULP = {torch.bfloat16: 2.0 ** -8, torch.float16: 2.0 ** -11}
+
+
+def assert_epilogue(y16: torch.Tensor, y32: np.ndarray, ydt, x, packed, n, k, g, sym, what):
+    """y16 is the round-to-nearest-even of the fp32 result of the same product (bit for
+    bit), and within the matmul bound plus half an ulp of the 16-bit type of the oracle."""
+    exp = torch.from_numpy(np.ascontiguousarray(y32)).to(ydt)
+    got = y16.cpu()
+    assert torch.equal(got.view(torch.int16), exp.view(torch.int16)), f"{what}: not the rounding of the fp32 sums"
+    qo, so, zo = packed
+    yr, ya = oracle.linear(host_input(x), qo, so, zo, n, k, g, sym)
+    base = 1e-3 * ya + 1e-5
+    bound = base + HALF_ULP[ydt] * (np.abs(yr) + base) + (2.0 ** -25 if ydt == torch.float16 else 0.0)
+    gv = got.float().numpy().astype(np.float64)
+    # sums beyond the 16-bit range (fp16 above 65504: the seeded stress rows) are signed
+    # infinities, as the rounding defines; the bound applies to the rest
+    over = ~np.isfinite(gv)
+    assert (np.sign(gv[over]) == np.sign(yr[over])).all() and (np.abs(yr[over]) > 65504 * 0.999).all(), \
+        f"{what}: an infinity where the sum is in range"
+    gv[over] = yr[over]
+    err = np.abs(gv - yr)
+    if not (err <= bound).all():
+        bad = np.argwhere(err > bound)[:4]
+        det = [(int(i), int(j), float(gv[i, j]), float(y32[i, j]), float(yr[i, j]), float(ya[i, j]),
+                float(bound[i, j])) for i, j in bad]
+        raise AssertionError(f"{what}: {int((err > bound).sum())} outside the bound; "
+                             f"(row, col, y16, y32, oracle, |x||w|, bound): {det}")
+
+
+@pytest.mark.parametrize("m,n,k,g,path", EPILOGUE_CASES)
+@pytest.mark.parametrize("ydt", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
+def test_output_epilogue(m, n, k, g, path, ydt, xdtype):
+    sym = (m + g) % 2 == 1
+    w = torch.from_numpy(pins.random_weights(n + 13 * k + m, max(n, 12), k)[:n])
+    x = synthetic.activations(m, k, seed=m * 29 + k).to(xdtype)
+    note(f"epilogue {path} m={m} n={n} k={k} g={g} {xdtype} -> {ydt} sym={sym}")
+    p, _ = pack_guarded(w.to(DEV), g, sym)
+    y32, k32 = run_linear(x, p)
+    yb, yv = guarded((m, n), ydt, SENTINEL_F32)
+    q4.q4_w4a16_gemm(x.to(DEV), p, out=yv)
+    k16 = q4.q4_last_kernel()
+    torch.cuda.synchronize()
+    assert guard_intact(yb), "store outside y"
+    assert k16 == k32, (k16, k32)  # the same path, only the store differs
+    packed = assert_pack_exact(p, host_input(w), g, sym)
+    assert_epilogue(yv, y32, ydt, x, packed, n, k, g, sym, f"{k16} -> {ydt}")
+
+
+@pytest.mark.parametrize("m", [1, 5])
+@pytest.mark.parametrize("ydt", [torch.bfloat16, torch.float16])
+def test_output_epilogue_grouped(m, ydt):
+    """Grouped products (one decode launch, shared and separate activations) with 16-bit
+    outputs: each the rounding of the same call's fp32 outputs."""
+    k, g, sym = 1024, 64, False
+    ns = [48, 200, 1000]
+    ws = [torch.from_numpy(pins.random_weights(71 + i, max(n, 12), k)[:n]) for i, n in enumerate(ns)]
+    x = synthetic.activations(m, k, seed=81)
+    note(f"epilogue grouped m={m} -> {ydt}")
+    packs = [pack_guarded(w.to(DEV), g, sym)[0] for w in ws]
+    y32 = q4.q4_w4a16_gemm_grouped(x.to(DEV), packs)
+    guards = [guarded((m, n), ydt, SENTINEL_F32) for n in ns]
+    q4.q4_w4a16_gemm_grouped(x.to(DEV), packs, outs=[v for _, v in guards])
+    torch.cuda.synchronize()
+    for w, p, y, (gb, gv) in zip(ws, packs, y32, guards):
+        assert guard_intact(gb), "store outside y"
+        packed = assert_pack_exact(p, host_input(w), g, sym)
+        assert_epilogue(gv, y.cpu().numpy(), ydt, x, packed, p.n, k, g, sym, f"grouped -> {ydt}")

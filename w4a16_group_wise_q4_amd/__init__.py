@@ -39,8 +39,8 @@ Q4_F32, Q4_F16, Q4_BF16 = 0, 1, 2
 _DTYPE_CODE = {torch.float32: Q4_F32, torch.float16: Q4_F16, torch.bfloat16: Q4_BF16}
 
 EXPORTED = ("q4_quantize_pack", "q4_quantize_pack_grouped", "q4_quantize_pack_mse", "q4_dequant",
-            "q4_w4a16_gemm",
-            "q4_w4a16_gemm_grouped", "q4_kv_quantize", "q4_kv_attention",
+            "q4_w4a16_gemm", "q4_w4a16_gemm_out",
+            "q4_w4a16_gemm_grouped", "q4_w4a16_gemm_grouped_out", "q4_kv_quantize", "q4_kv_attention",
             "q4_kv_attention_workspace", "q4_gptq_quantize", "q4_gptq_workspace",
             "q4_qweight_words",
             "q4_scale_count", "q4_zero_words", "q4_status_str", "q4_last_kernel",
@@ -96,9 +96,15 @@ def _load():
     lib.q4_dequant.restype = ctypes.c_int
     lib.q4_w4a16_gemm.argtypes = [vp, ctypes.c_int, i64, vp, vp, vp, i64, i64, i32, i32, vp, vp]
     lib.q4_w4a16_gemm.restype = ctypes.c_int
+    lib.q4_w4a16_gemm_out.argtypes = [vp, ctypes.c_int, i64, vp, vp, vp, i64, i64, i32, i32, vp,
+                                      ctypes.c_int, vp]
+    lib.q4_w4a16_gemm_out.restype = ctypes.c_int
     lib.q4_w4a16_gemm_grouped.argtypes = [ctypes.POINTER(GemmProblem), i32, ctypes.c_int, i64, i64,
                                           i32, i32, vp]
     lib.q4_w4a16_gemm_grouped.restype = ctypes.c_int
+    lib.q4_w4a16_gemm_grouped_out.argtypes = [ctypes.POINTER(GemmProblem), i32, ctypes.c_int, i64, i64,
+                                              i32, i32, ctypes.c_int, vp]
+    lib.q4_w4a16_gemm_grouped_out.restype = ctypes.c_int
     lib.q4_kv_quantize.argtypes = [vp, ctypes.c_int, i64, i64, i64, i32, i32, i64, i64, vp, vp, vp,
                                    vp]
     lib.q4_kv_quantize.restype = ctypes.c_int
@@ -261,23 +267,36 @@ def q4_dequant(p: PackedWeight, out_dtype: torch.dtype = torch.float32,
 
 
 def q4_w4a16_gemm(x: torch.Tensor, p: PackedWeight,
-                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """y = x · (S (u - z))^T, x [m, k] fp16/bf16, y [m, n] fp32."""
+                  out: Optional[torch.Tensor] = None,
+                  out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """y = x · (S (u - z))^T, x [m, k] fp16/bf16, y [m, n] fp32 (q4_w4a16_gemm), or fp16 /
+    bf16 rounded from the fp32 sums in the kernel's epilogue (q4_w4a16_gemm_out)."""
     _need_cuda("x", x)
     if x.dim() != 2 or x.dtype not in (torch.float16, torch.bfloat16) or x.shape[1] != p.k:
         raise ValueError("x must be [m, k] fp16 or bf16 with k matching the packed weight")
+    if out is not None:
+        out_dtype = out.dtype
+    if out_dtype not in _DTYPE_CODE:
+        raise ValueError("the output is fp32, fp16 or bf16")
     m = x.shape[0]
-    y = out if out is not None else torch.empty((m, p.n), dtype=torch.float32, device=x.device)
-    _check(_load().q4_w4a16_gemm(_dev_ptr(x), _DTYPE_CODE[x.dtype], m, _dev_ptr(p.qweight),
-                                 _dev_ptr(p.scales), _dev_ptr(p.zeros), p.n, p.k,
-                                 p.group_size, int(p.symmetric), _dev_ptr(y), _stream(x)))
+    y = out if out is not None else torch.empty((m, p.n), dtype=out_dtype, device=x.device)
+    if out_dtype == torch.float32:
+        _check(_load().q4_w4a16_gemm(_dev_ptr(x), _DTYPE_CODE[x.dtype], m, _dev_ptr(p.qweight),
+                                     _dev_ptr(p.scales), _dev_ptr(p.zeros), p.n, p.k,
+                                     p.group_size, int(p.symmetric), _dev_ptr(y), _stream(x)))
+    else:
+        _check(_load().q4_w4a16_gemm_out(_dev_ptr(x), _DTYPE_CODE[x.dtype], m, _dev_ptr(p.qweight),
+                                         _dev_ptr(p.scales), _dev_ptr(p.zeros), p.n, p.k,
+                                         p.group_size, int(p.symmetric), _dev_ptr(y),
+                                         _DTYPE_CODE[out_dtype], _stream(x)))
     return y
 
 
-def q4_w4a16_gemm_grouped(xs, packs, outs=None):
+def q4_w4a16_gemm_grouped(xs, packs, outs=None, out_dtype=torch.float32):
     """y_i = x_i · (S_i (u_i - z_i))^T for up to 8 problems sharing m, k, group size,
     symmetry and activation dtype; with m <= 16 they run in one launch.  xs may be a
-    single tensor (shared by all problems) or one tensor per problem."""
+    single tensor (shared by all problems) or one tensor per problem.  The outputs are
+    out_dtype (fp32, or fp16 / bf16 rounded in the epilogue), or that of outs."""
     packs = list(packs)
     count = len(packs)
     if not 1 <= count <= MAX_GROUP:
@@ -294,14 +313,26 @@ def q4_w4a16_gemm_grouped(xs, packs, outs=None):
     if x0.dtype not in (torch.float16, torch.bfloat16):
         raise ValueError("activations must be fp16 or bf16")
     m = x0.shape[0]
-    ys = list(outs) if outs is not None else [
-        torch.empty((m, p.n), dtype=torch.float32, device=x0.device) for p in packs]
+    if outs is not None:
+        outs = list(outs)
+        out_dtype = outs[0].dtype
+        if any(o.dtype != out_dtype for o in outs):
+            raise ValueError("every output of a grouped call has one dtype")
+    if out_dtype not in _DTYPE_CODE:
+        raise ValueError("the output is fp32, fp16 or bf16")
+    ys = outs if outs is not None else [
+        torch.empty((m, p.n), dtype=out_dtype, device=x0.device) for p in packs]
     arr = (GemmProblem * count)()
     for i, (x, p, y) in enumerate(zip(xs, packs, ys)):
         arr[i] = GemmProblem(x.data_ptr(), p.qweight.data_ptr(), p.scales.data_ptr(),
                              None if p.zeros is None else p.zeros.data_ptr(), p.n, y.data_ptr())
-    _check(_load().q4_w4a16_gemm_grouped(arr, count, _DTYPE_CODE[x0.dtype], m, p0.k,
-                                         p0.group_size, int(p0.symmetric), _stream(x0)))
+    if out_dtype == torch.float32:
+        _check(_load().q4_w4a16_gemm_grouped(arr, count, _DTYPE_CODE[x0.dtype], m, p0.k,
+                                             p0.group_size, int(p0.symmetric), _stream(x0)))
+    else:
+        _check(_load().q4_w4a16_gemm_grouped_out(arr, count, _DTYPE_CODE[x0.dtype], m, p0.k,
+                                                 p0.group_size, int(p0.symmetric),
+                                                 _DTYPE_CODE[out_dtype], _stream(x0)))
     return ys
 
 

@@ -104,7 +104,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const uint16_t* __res
                                                           const uint32_t* __restrict__ qweight,
                                                           const uint16_t* __restrict__ scales,
                                                           const uint32_t* __restrict__ zeros,
-                                                          int N, int K, float* __restrict__ y) {
+                                                          int N, int K, void* __restrict__ y, int ydt) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // RING x A_STAGE
     constexpr int NGS = BStage<G>::NGS;
     const int tid = threadIdx.x;
@@ -373,24 +373,24 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const uint16_t* __res
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int mm = m0 + 32 * i + (r & 3) + 4 * h + 8 * (r >> 2);
-                if (mm < M) y[(int64_t)mm * N + nn] = acc[i][j][r] * s_cur[j];
+                if (mm < M) q4::store_y(y, (int64_t)mm * N + nn, acc[i][j][r] * s_cur[j], ydt);
             }
     }
 }
 
 template <int G, bool SYM>
 hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16_t* sc,
-                  const uint32_t* zr, int n, int k, float* y, hipStream_t st, const char** kname) {
+                  const uint32_t* zr, int n, int k, void* y, int ydt, hipStream_t st, const char** kname) {
     const int mtiles = (m + BM - 1) / BM, ntiles = (n + BN - 1) / BN;
     const dim3 grid((unsigned)(mtiles * ntiles)), block(NTHREADS);
     const size_t lds = (size_t)RING * A_STAGE;
     const uint16_t* xp = reinterpret_cast<const uint16_t*>(x);
     if (xd == 1) {
         *kname = "q4_gemm_mfma_f16";
-        hipLaunchKernelGGL((gemm_kernel<G, SYM, true>), grid, block, lds, st, xp, m, qw, sc, zr, n, k, y);
+        hipLaunchKernelGGL((gemm_kernel<G, SYM, true>), grid, block, lds, st, xp, m, qw, sc, zr, n, k, y, ydt);
     } else {
         *kname = "q4_gemm_mfma_bf16";
-        hipLaunchKernelGGL((gemm_kernel<G, SYM, false>), grid, block, lds, st, xp, m, qw, sc, zr, n, k, y);
+        hipLaunchKernelGGL((gemm_kernel<G, SYM, false>), grid, block, lds, st, xp, m, qw, sc, zr, n, k, y, ydt);
     }
     return hipGetLastError();
 }
@@ -399,14 +399,14 @@ hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16
 
 hipError_t q4k_gemm(const void* x, int x_dtype, int64_t m, const uint32_t* qweight,
                     const uint16_t* scales, const uint32_t* zeros, int64_t n, int64_t k, int g,
-                    int sym, float* y, hipStream_t stream, const char** kname) {
+                    int sym, void* y, int ydt, hipStream_t stream, const char** kname) {
     const int mi = (int)m, ni = (int)n, ki = (int)k;
     switch (g * 2 + (sym ? 1 : 0)) {
-    case 64: return launch<32, false>(x, x_dtype, mi, qweight, scales, zeros, ni, ki, y, stream, kname);
-    case 65: return launch<32, true>(x, x_dtype, mi, qweight, scales, zeros, ni, ki, y, stream, kname);
-    case 128: return launch<64, false>(x, x_dtype, mi, qweight, scales, zeros, ni, ki, y, stream, kname);
-    case 129: return launch<64, true>(x, x_dtype, mi, qweight, scales, zeros, ni, ki, y, stream, kname);
-    case 256: return launch<128, false>(x, x_dtype, mi, qweight, scales, zeros, ni, ki, y, stream, kname);
-    default: return launch<128, true>(x, x_dtype, mi, qweight, scales, zeros, ni, ki, y, stream, kname);
+    case 64: return launch<32, false>(x, x_dtype, mi, qweight, scales, zeros, ni, ki, y, ydt, stream, kname);
+    case 65: return launch<32, true>(x, x_dtype, mi, qweight, scales, zeros, ni, ki, y, ydt, stream, kname);
+    case 128: return launch<64, false>(x, x_dtype, mi, qweight, scales, zeros, ni, ki, y, ydt, stream, kname);
+    case 129: return launch<64, true>(x, x_dtype, mi, qweight, scales, zeros, ni, ki, y, ydt, stream, kname);
+    case 256: return launch<128, false>(x, x_dtype, mi, qweight, scales, zeros, ni, ki, y, ydt, stream, kname);
+    default: return launch<128, true>(x, x_dtype, mi, qweight, scales, zeros, ni, ki, y, ydt, stream, kname);
     }
 }

@@ -155,7 +155,8 @@ __global__ __launch_bounds__(MAXT, MINW) void gemv_stream_kernel(const GemvBatch
     const uint32_t* __restrict__ qweight = bt.p[pi].qweight;
     const uint16_t* __restrict__ scales = bt.p[pi].scales;
     const uint32_t* __restrict__ zeros = bt.p[pi].zeros;
-    float* __restrict__ y = bt.p[pi].y;
+    void* __restrict__ y = bt.p[pi].y;
+    const int ydt = bt.ydt;
     const int N = bt.p[pi].n;
     const int bx = (int)blockIdx.x - bt.p[pi].tile0;  // tile index within the problem
     const int tid = threadIdx.x, nthreads = blockDim.x;
@@ -295,7 +296,7 @@ __global__ __launch_bounds__(MAXT, MINW) void gemv_stream_kernel(const GemvBatch
     }
     __syncthreads();
 
-    const q4::rsrc ry = q4::make_rsrc(y, (uint32_t)M * (uint32_t)N * 4u);
+    const q4::rsrc ry = q4::make_rsrc(y, (uint32_t)M * (uint32_t)N * q4::y_bytes(ydt));
     for (int tl = 0; tl < ntiles; ++tl) {
         uint32_t mnext[kPS + kPZ];
         // next tile's metadata.  Its loads sit behind the ring's, so the first wait of the
@@ -338,8 +339,8 @@ __global__ __launch_bounds__(MAXT, MINW) void gemv_stream_kernel(const GemvBatch
         for (int q = 0; q < 4; ++q) {
             const int m = 4 * c + q;
             const bool st = fin && m < M && n0 + col < N;
-            const uint32_t off = st ? ((uint32_t)m * (uint32_t)N + (uint32_t)(n0 + col)) * 4u : kStoreOOB;
-            __builtin_amdgcn_raw_buffer_store_b32(q4::f32_bits(sum[q]), ry, (int)off, 0, 0);
+            const uint32_t off = st ? ((uint32_t)m * (uint32_t)N + (uint32_t)(n0 + col)) * q4::y_bytes(ydt) : kStoreOOB;
+            q4::store_y(ry, off, sum[q], ydt);
         }
     }
 }
@@ -356,7 +357,7 @@ __global__ __launch_bounds__(512) void gemv_chunk_kernel(const uint16_t* __restr
                                                          const uint32_t* __restrict__ qweight,
                                                          const uint16_t* __restrict__ scales,
                                                          const uint32_t* __restrict__ zeros, int N,
-                                                         int K, int KC, float* __restrict__ y) {
+                                                         int K, int KC, void* __restrict__ y, int ydt) {
     constexpr int GW = G / 8;   // packed words per group
     constexpr int LW = G / 32;  // words per lane per group (one MFMA per word)
     constexpr int NH = 4 / LW;  // groups per 128-column unit
@@ -502,7 +503,7 @@ __global__ __launch_bounds__(512) void gemv_chunk_kernel(const uint16_t* __restr
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int m = 4 * c + i;
-            if (m < M) y[(int64_t)m * N + n0 + col] = t[i];
+            if (m < M) q4::store_y(y, (int64_t)m * N + n0 + col, t[i], ydt);
         }
     }
 }
@@ -512,7 +513,7 @@ int g_num_cus = 0;
 // One problem (batch == nullptr) or a batch of problems whose tiles add up to n rows.
 template <int G, bool SYM>
 hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16_t* sc,
-                  const uint32_t* zr, int n, int k, float* y, hipStream_t st, const char** kname,
+                  const uint32_t* zr, int n, int k, void* y, int ydt, hipStream_t st, const char** kname,
                   const GemvBatch* batch = nullptr, int batch_tiles = 0) {
     if (g_num_cus == 0) {
         int dev = 0;
@@ -545,6 +546,7 @@ hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16
             if (batch == nullptr) {
                 one.p[0] = q4::GemvProblem{x, qw, sc, zr, y, n, 0};
                 one.count = 1;
+                one.ydt = ydt;
             }
             const GemvBatch& bt = batch != nullptr ? *batch : one;
             if constexpr (G == 32) return q4k_gemv_tile_g32(SYM, xd, m, k, upw, tw, wide, bt, tiles, st, kname);
@@ -615,6 +617,7 @@ hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16
             GemvBatch one{};
             one.p[0] = q4::GemvProblem{x, qw, sc, zr, y, n, 0};
             one.count = 1;
+            one.ydt = ydt;
             const int cap = g_num_cus * per_cu(k_multi);
             if (tiles <= cap)
                 hipLaunchKernelGGL(k_one, dim3(tiles), dim3(threads), lds_stream, st, one, m, k);
@@ -670,11 +673,11 @@ hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16
     if (xd == 1) {
         *kname = "q4_gemv_mfma_f16";
         hipLaunchKernelGGL((gemv_chunk_kernel<G, SYM, true>), dim3(tiles), dim3(threads), lds, st, xp, m,
-                           qw, sc, zr, n, k, kc, y);
+                           qw, sc, zr, n, k, kc, y, ydt);
     } else {
         *kname = "q4_gemv_mfma_bf16";
         hipLaunchKernelGGL((gemv_chunk_kernel<G, SYM, false>), dim3(tiles), dim3(threads), lds, st, xp, m,
-                           qw, sc, zr, n, k, kc, y);
+                           qw, sc, zr, n, k, kc, y, ydt);
     }
     return hipGetLastError();
 }
@@ -683,20 +686,20 @@ hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16
 
 hipError_t q4k_gemv(const void* x, int x_dtype, int m, const uint32_t* qweight,
                     const uint16_t* scales, const uint32_t* zeros, int64_t n, int64_t k, int g,
-                    int sym, float* y, hipStream_t stream, const char** kname) {
+                    int sym, void* y, int ydt, hipStream_t stream, const char** kname) {
     const int ni = (int)n, ki = (int)k;
     switch (g * 2 + (sym ? 1 : 0)) {
-    case 64: return launch<32, false>(x, x_dtype, m, qweight, scales, zeros, ni, ki, y, stream, kname);
-    case 65: return launch<32, true>(x, x_dtype, m, qweight, scales, zeros, ni, ki, y, stream, kname);
-    case 128: return launch<64, false>(x, x_dtype, m, qweight, scales, zeros, ni, ki, y, stream, kname);
-    case 129: return launch<64, true>(x, x_dtype, m, qweight, scales, zeros, ni, ki, y, stream, kname);
-    case 256: return launch<128, false>(x, x_dtype, m, qweight, scales, zeros, ni, ki, y, stream, kname);
-    default: return launch<128, true>(x, x_dtype, m, qweight, scales, zeros, ni, ki, y, stream, kname);
+    case 64: return launch<32, false>(x, x_dtype, m, qweight, scales, zeros, ni, ki, y, ydt, stream, kname);
+    case 65: return launch<32, true>(x, x_dtype, m, qweight, scales, zeros, ni, ki, y, ydt, stream, kname);
+    case 128: return launch<64, false>(x, x_dtype, m, qweight, scales, zeros, ni, ki, y, ydt, stream, kname);
+    case 129: return launch<64, true>(x, x_dtype, m, qweight, scales, zeros, ni, ki, y, ydt, stream, kname);
+    case 256: return launch<128, false>(x, x_dtype, m, qweight, scales, zeros, ni, ki, y, ydt, stream, kname);
+    default: return launch<128, true>(x, x_dtype, m, qweight, scales, zeros, ni, ki, y, ydt, stream, kname);
     }
 }
 
 hipError_t q4k_gemv_grouped(const q4::GemvProblem* problems, int count, int x_dtype, int m,
-                            int64_t k, int g, int sym, hipStream_t stream, const char** kname) {
+                            int64_t k, int g, int sym, int ydt, hipStream_t stream, const char** kname) {
     if (count < 1 || count > q4::kMaxGroup) return hipErrorInvalidValue;
     GemvBatch batch{};
     int tiles = 0;
@@ -706,15 +709,16 @@ hipError_t q4k_gemv_grouped(const q4::GemvProblem* problems, int count, int x_dt
         tiles += (problems[i].n + 15) / 16;
     }
     batch.count = count;
+    batch.ydt = ydt;
     const int ki = (int)k, rows = 16 * tiles;
     const void* x = problems[0].x;
     switch (g * 2 + (sym ? 1 : 0)) {
-    case 64: return launch<32, false>(x, x_dtype, m, nullptr, nullptr, nullptr, rows, ki, nullptr, stream, kname, &batch, tiles);
-    case 65: return launch<32, true>(x, x_dtype, m, nullptr, nullptr, nullptr, rows, ki, nullptr, stream, kname, &batch, tiles);
-    case 128: return launch<64, false>(x, x_dtype, m, nullptr, nullptr, nullptr, rows, ki, nullptr, stream, kname, &batch, tiles);
-    case 129: return launch<64, true>(x, x_dtype, m, nullptr, nullptr, nullptr, rows, ki, nullptr, stream, kname, &batch, tiles);
-    case 256: return launch<128, false>(x, x_dtype, m, nullptr, nullptr, nullptr, rows, ki, nullptr, stream, kname, &batch, tiles);
-    default: return launch<128, true>(x, x_dtype, m, nullptr, nullptr, nullptr, rows, ki, nullptr, stream, kname, &batch, tiles);
+    case 64: return launch<32, false>(x, x_dtype, m, nullptr, nullptr, nullptr, rows, ki, nullptr, ydt, stream, kname, &batch, tiles);
+    case 65: return launch<32, true>(x, x_dtype, m, nullptr, nullptr, nullptr, rows, ki, nullptr, ydt, stream, kname, &batch, tiles);
+    case 128: return launch<64, false>(x, x_dtype, m, nullptr, nullptr, nullptr, rows, ki, nullptr, ydt, stream, kname, &batch, tiles);
+    case 129: return launch<64, true>(x, x_dtype, m, nullptr, nullptr, nullptr, rows, ki, nullptr, ydt, stream, kname, &batch, tiles);
+    case 256: return launch<128, false>(x, x_dtype, m, nullptr, nullptr, nullptr, rows, ki, nullptr, ydt, stream, kname, &batch, tiles);
+    default: return launch<128, true>(x, x_dtype, m, nullptr, nullptr, nullptr, rows, ki, nullptr, ydt, stream, kname, &batch, tiles);
     }
 }
 

@@ -101,7 +101,8 @@ __global__ __launch_bounds__(MQ == 1 ? 1024 : 512) void gemv_tile_kernel(const q
     const uint32_t* __restrict__ qweight = bt.p[pi].qweight;
     const uint16_t* __restrict__ scales = bt.p[pi].scales;
     const uint32_t* __restrict__ zeros = bt.p[pi].zeros;
-    float* __restrict__ y = bt.p[pi].y;
+    void* __restrict__ y = bt.p[pi].y;
+    const int ydt = bt.ydt;
     const int N = bt.p[pi].n;
     const int n0 = ((int)blockIdx.x - bt.p[pi].tile0) * 16;
     const int lane = threadIdx.x & 63;
@@ -244,12 +245,12 @@ __global__ __launch_bounds__(MQ == 1 ? 1024 : 512) void gemv_tile_kernel(const q
         for (int v = 0; v < S; ++v)
 #pragma unroll
             for (int q = 0; q < MQ; ++q) sum[q] += red[(v * 64 + lane) * MQ + q];
-        const q4::rsrc ry = q4::make_rsrc(y, (uint32_t)M * (uint32_t)N * 4u);
+        const q4::rsrc ry = q4::make_rsrc(y, (uint32_t)M * (uint32_t)N * q4::y_bytes(ydt));
 #pragma unroll
         for (int q = 0; q < MQ; ++q) {
             const bool st = lane < 16 && q < M && r < rows;
-            const uint32_t off = st ? ((uint32_t)q * (uint32_t)N + (uint32_t)(n0 + r)) * 4u : kStoreOOB;
-            __builtin_amdgcn_raw_buffer_store_b32(q4::f32_bits(sum[q]), ry, (int)off, 0, 0);
+            const uint32_t off = st ? ((uint32_t)q * (uint32_t)N + (uint32_t)(n0 + r)) * q4::y_bytes(ydt) : kStoreOOB;
+            q4::store_y(ry, off, sum[q], ydt);
         }
     }
 }
@@ -291,7 +292,8 @@ __global__ __launch_bounds__(512) void gemv_wide_kernel(const q4::GemvBatch bt, 
     const uint32_t* __restrict__ qweight = bt.p[pi].qweight;
     const uint16_t* __restrict__ scales = bt.p[pi].scales;
     const uint32_t* __restrict__ zeros = bt.p[pi].zeros;
-    float* __restrict__ y = bt.p[pi].y;
+    void* __restrict__ y = bt.p[pi].y;
+    const int ydt = bt.ydt;
     const int N = bt.p[pi].n;
     const int n0 = ((int)blockIdx.x - bt.p[pi].tile0) * 16 * T;  // T tiles of 16 rows
     const int lane = threadIdx.x & 63;
@@ -472,7 +474,7 @@ __global__ __launch_bounds__(512) void gemv_wide_kernel(const q4::GemvBatch bt, 
         for (int q = 0; q < 4; ++q) red[(t * 64 + lane) * 4 + q] = acc[t][q];
     __syncthreads();
     if (w == 0) {
-        const q4::rsrc ry = q4::make_rsrc(y, (uint32_t)M * (uint32_t)N * 4u);
+        const q4::rsrc ry = q4::make_rsrc(y, (uint32_t)M * (uint32_t)N * q4::y_bytes(ydt));
 #pragma unroll
         for (int t = 0; t < T; ++t) {
             float sum[4] = {0.f, 0.f, 0.f, 0.f};
@@ -485,8 +487,8 @@ __global__ __launch_bounds__(512) void gemv_wide_kernel(const q4::GemvBatch bt, 
             for (int q = 0; q < 4; ++q) {
                 const int m = 4 * c + q;
                 const bool st = m < M && 16 * t + r < rows;
-                const uint32_t off = st ? ((uint32_t)m * (uint32_t)N + (uint32_t)(n0 + 16 * t + r)) * 4u : kStoreOOB;
-                __builtin_amdgcn_raw_buffer_store_b32(q4::f32_bits(sum[q]), ry, (int)off, 0, 0);
+                const uint32_t off = st ? ((uint32_t)m * (uint32_t)N + (uint32_t)(n0 + 16 * t + r)) * q4::y_bytes(ydt) : kStoreOOB;
+                q4::store_y(ry, off, sum[q], ydt);
             }
         }
     }

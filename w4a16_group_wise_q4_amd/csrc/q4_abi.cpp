@@ -162,22 +162,24 @@ bool chunked_gemv(int64_t m, int64_t n, int cus) {
 }
 
 hipError_t run_product(const void* x, int xd, int64_t m, const uint32_t* qw, const uint16_t* sc,
-                       const uint32_t* zr, int64_t n, int64_t k, int g, int sym, float* y,
+                       const uint32_t* zr, int64_t n, int64_t k, int g, int sym, void* y, int ydt,
                        hipStream_t st, const char** name) {
-    if (m <= 16) return q4k_gemv(x, xd, (int)m, qw, sc, zr, n, k, g, sym, y, st, name);
-    if (!chunked_gemv(m, n, device_cus())) return q4k_gemm(x, xd, m, qw, sc, zr, n, k, g, sym, y, st, name);
+    if (m <= 16) return q4k_gemv(x, xd, (int)m, qw, sc, zr, n, k, g, sym, y, ydt, st, name);
+    if (!chunked_gemv(m, n, device_cus())) return q4k_gemm(x, xd, m, qw, sc, zr, n, k, g, sym, y, ydt, st, name);
     const int64_t full = m / 16, rem = m % 16;
     const uint16_t* xs = static_cast<const uint16_t*>(x);
+    char* yb = static_cast<char*>(y);
+    const int64_t ye = ydt == Q4_F32 ? 4 : 2;  // bytes per y element
     for (int64_t c0 = 0; c0 < full; c0 += q4::kMaxGroup) {
         const int64_t cnt = full - c0 < q4::kMaxGroup ? full - c0 : q4::kMaxGroup;
         q4::GemvProblem gp[q4::kMaxGroup];
         for (int64_t c = 0; c < cnt; ++c)
-            gp[c] = q4::GemvProblem{xs + (c0 + c) * 16 * k, qw, sc, zr, y + (c0 + c) * 16 * n, (int)n, 0};
+            gp[c] = q4::GemvProblem{xs + (c0 + c) * 16 * k, qw, sc, zr, yb + (c0 + c) * 16 * n * ye, (int)n, 0};
         hipError_t e = hipErrorNotSupported;
-        if (cnt > 1) e = q4k_gemv_grouped(gp, (int)cnt, xd, 16, k, g, sym, st, name);
+        if (cnt > 1) e = q4k_gemv_grouped(gp, (int)cnt, xd, 16, k, g, sym, ydt, st, name);
         if (e == hipErrorNotSupported) {
             for (int64_t c = 0; c < cnt; ++c) {
-                e = q4k_gemv(gp[c].x, xd, 16, qw, sc, zr, n, k, g, sym, gp[c].y, st, name);
+                e = q4k_gemv(gp[c].x, xd, 16, qw, sc, zr, n, k, g, sym, gp[c].y, ydt, st, name);
                 if (e != hipSuccess) return e;
             }
         } else if (e != hipSuccess) {
@@ -185,37 +187,38 @@ hipError_t run_product(const void* x, int xd, int64_t m, const uint32_t* qw, con
         }
     }
     if (rem > 0)
-        return q4k_gemv(xs + full * 16 * k, xd, (int)rem, qw, sc, zr, n, k, g, sym, y + full * 16 * n, st,
-                        name);
+        return q4k_gemv(xs + full * 16 * k, xd, (int)rem, qw, sc, zr, n, k, g, sym, yb + full * 16 * n * ye,
+                        ydt, st, name);
     return hipSuccess;
 }
 
-// The size, dtype, pointer and alignment rules of q4_w4a16_gemm for one problem.
+// The size, dtype, pointer and alignment rules of q4_w4a16_gemm_out for one problem.
 q4_status check_matmul(const void* x, q4_dtype x_dtype, int64_t m, const uint32_t* qweight,
                        const uint16_t* scales, const uint32_t* zeros, int64_t n, int64_t k,
-                       int32_t group_size, int32_t symmetric, const float* y) {
+                       int32_t group_size, int32_t symmetric, const void* y, q4_dtype y_dtype) {
     q4_status st = check_layout(n, k, group_size);
     if (st != Q4_OK) return st;
     if (k > kMaxMatmulK || n > kMaxMatmulN) return Q4_ERR_SHAPE;
     if (m < 1 || m > kMaxDim || m > kMaxElems / k || m > kMaxMatmulOut / n) return Q4_ERR_SHAPE;
     if (x_dtype != Q4_F16 && x_dtype != Q4_BF16) return Q4_ERR_DTYPE;
+    if (y_dtype != Q4_F32 && y_dtype != Q4_F16 && y_dtype != Q4_BF16) return Q4_ERR_DTYPE;
     if (!x || !y) return Q4_ERR_NULL;
     if ((st = check_packed(qweight, scales, zeros, symmetric)) != Q4_OK) return st;
-    if (!aligned(x, 16) || !aligned(y, 4)) return Q4_ERR_ALIGN;
+    if (!aligned(x, 16) || !aligned(y, y_dtype == Q4_F32 ? 4 : 2)) return Q4_ERR_ALIGN;
     return Q4_OK;
 }
 }  // namespace
 
-q4_status q4_w4a16_gemm_grouped(const q4_gemm_problem* problems, int32_t count,
-                                q4_dtype x_dtype, int64_t m, int64_t k, int32_t group_size,
-                                int32_t symmetric, hipStream_t stream) {
+q4_status q4_w4a16_gemm_grouped_out(const q4_gemm_problem* problems, int32_t count,
+                                    q4_dtype x_dtype, int64_t m, int64_t k, int32_t group_size,
+                                    int32_t symmetric, q4_dtype y_dtype, hipStream_t stream) {
     if (!problems) return Q4_ERR_NULL;
     if (count < 1 || count > q4::kMaxGroup) return Q4_ERR_SHAPE;
     int64_t rows = 0;
     for (int32_t i = 0; i < count; ++i) {
         const q4_gemm_problem& p = problems[i];
         const q4_status st = check_matmul(p.x, x_dtype, m, p.qweight, p.scales, p.zeros, p.n, k,
-                                          group_size, symmetric, p.y);
+                                          group_size, symmetric, p.y, y_dtype);
         if (st != Q4_OK) return st;
         rows += (p.n + 15) / 16 * 16;
     }
@@ -227,29 +230,44 @@ q4_status q4_w4a16_gemm_grouped(const q4_gemm_problem* problems, int32_t count,
                                     symmetric ? nullptr : problems[i].zeros, problems[i].y,
                                     (int)problems[i].n, 0};
         const hipError_t e = q4k_gemv_grouped(gp, count, (int)x_dtype, (int)m, k, group_size,
-                                              symmetric ? 1 : 0, stream, &name);
+                                              symmetric ? 1 : 0, (int)y_dtype, stream, &name);
         if (e != hipErrorNotSupported) return finish(e, name);
     }
     for (int32_t i = 0; i < count; ++i) {  // one product at a time
         const q4_gemm_problem& p = problems[i];
         const hipError_t e = run_product(p.x, (int)x_dtype, m, p.qweight, p.scales,
                                          symmetric ? nullptr : p.zeros, p.n, k, group_size,
-                                         symmetric ? 1 : 0, p.y, stream, &name);
+                                         symmetric ? 1 : 0, p.y, (int)y_dtype, stream, &name);
         if (e != hipSuccess) return Q4_ERR_LAUNCH;
     }
     return finish(hipSuccess, name);
 }
 
-q4_status q4_w4a16_gemm(const void* x, q4_dtype x_dtype, int64_t m, const uint32_t* qweight,
-                        const uint16_t* scales, const uint32_t* zeros, int64_t n, int64_t k,
-                        int32_t group_size, int32_t symmetric, float* y, hipStream_t stream) {
+q4_status q4_w4a16_gemm_grouped(const q4_gemm_problem* problems, int32_t count,
+                                q4_dtype x_dtype, int64_t m, int64_t k, int32_t group_size,
+                                int32_t symmetric, hipStream_t stream) {
+    return q4_w4a16_gemm_grouped_out(problems, count, x_dtype, m, k, group_size, symmetric, Q4_F32,
+                                     stream);
+}
+
+q4_status q4_w4a16_gemm_out(const void* x, q4_dtype x_dtype, int64_t m, const uint32_t* qweight,
+                            const uint16_t* scales, const uint32_t* zeros, int64_t n, int64_t k,
+                            int32_t group_size, int32_t symmetric, void* y, q4_dtype y_dtype,
+                            hipStream_t stream) {
     const q4_status st = check_matmul(x, x_dtype, m, qweight, scales, zeros, n, k, group_size,
-                                      symmetric, y);
+                                      symmetric, y, y_dtype);
     if (st != Q4_OK) return st;
     const char* name = "";
     const hipError_t e = run_product(x, (int)x_dtype, m, qweight, scales, symmetric ? nullptr : zeros, n,
-                                     k, group_size, symmetric ? 1 : 0, y, stream, &name);
+                                     k, group_size, symmetric ? 1 : 0, y, (int)y_dtype, stream, &name);
     return finish(e, name);
+}
+
+q4_status q4_w4a16_gemm(const void* x, q4_dtype x_dtype, int64_t m, const uint32_t* qweight,
+                        const uint16_t* scales, const uint32_t* zeros, int64_t n, int64_t k,
+                        int32_t group_size, int32_t symmetric, float* y, hipStream_t stream) {
+    return q4_w4a16_gemm_out(x, x_dtype, m, qweight, scales, zeros, n, k, group_size, symmetric, y,
+                             Q4_F32, stream);
 }
 
 namespace {

@@ -129,14 +129,39 @@ struct GemvProblem {
     const uint32_t* qweight;
     const uint16_t* scales;
     const uint32_t* zeros;
-    float* y;
+    void* y;  // fp32, fp16 or bf16 elements (GemvBatch::ydt)
     int n;
     int tile0;
 };
 // The problems of one decode launch (a single one, or several sharing m, k, g and dtype):
-// workgroups [p[i].tile0, p[i+1].tile0) serve problem i.
+// workgroups [p[i].tile0, p[i+1].tile0) serve problem i.  ydt: the element type of every
+// y (0 fp32, 1 fp16, 2 bf16; the q4_dtype codes).
 struct GemvBatch {
     GemvProblem p[kMaxGroup];
     int count;
+    int ydt;
 };
+
+// ---------------------------------------------------------------- output epilogue
+// y elements: fp32 as accumulated, or rounded to nearest even to fp16 / bf16 (the output
+// epilogue of a layer that hands 16-bit activations on).
+__device__ __forceinline__ uint32_t y_bytes(int ydt) { return ydt == 0 ? 4u : 2u; }
+__device__ __forceinline__ uint16_t to_y16(float v, int ydt) {
+    if (ydt == 1) return __builtin_bit_cast(uint16_t, (_Float16)v);
+    return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+// One y element at byte offset off of resource ry (an offset past the resource stores nothing).
+__device__ __forceinline__ void store_y(rsrc ry, uint32_t off, float v, int ydt) {
+    if (ydt == 0)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ry, (int)off, 0, 0);
+    else
+        __builtin_amdgcn_raw_buffer_store_b16(to_y16(v, ydt), ry, (int)off, 0, 0);
+}
+// One y element at index i of a plain pointer.
+__device__ __forceinline__ void store_y(void* y, int64_t i, float v, int ydt) {
+    if (ydt == 0)
+        reinterpret_cast<float*>(y)[i] = v;
+    else
+        reinterpret_cast<uint16_t*>(y)[i] = to_y16(v, ydt);
+}
 }  // namespace q4

@@ -54,9 +54,11 @@ hipError_t q4k_quant_mse(const void* w, int w_dtype, int64_t n, int64_t k, int g
 hipError_t q4k_dequant(const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros,
                        int64_t n, int64_t k, int g, int sym, void* out, int out_dtype,
                        hipStream_t stream, const char** kname);
+// y: fp32, fp16 or bf16 elements (ydt = 0, 1, 2: the q4_dtype codes), rounded from the fp32
+// accumulators in the kernel's epilogue.
 hipError_t q4k_gemv(const void* x, int x_dtype, int m, const uint32_t* qweight,
                     const uint16_t* scales, const uint32_t* zeros, int64_t n, int64_t k, int g,
-                    int sym, float* y, hipStream_t stream, const char** kname);
+                    int sym, void* y, int ydt, hipStream_t stream, const char** kname);
 // Decode tile kernels for one group size (32, 64 or 128): UPW units per wave, `waves` waves
 // per 16-row tile, one workgroup per tile of the batch; wide != 0 selects the kernel for
 // m up to 16 that streams the activations instead of staging them.
@@ -73,10 +75,10 @@ hipError_t q4k_gemv_tile_g128(int sym, int x_dtype, int m, int k, int upw, int w
 // activations fit the streaming kernel; returns hipErrorNotSupported (enqueuing nothing)
 // otherwise, so the caller runs them one by one.
 hipError_t q4k_gemv_grouped(const q4::GemvProblem* problems, int count, int x_dtype, int m,
-                            int64_t k, int g, int sym, hipStream_t stream, const char** kname);
+                            int64_t k, int g, int sym, int ydt, hipStream_t stream, const char** kname);
 hipError_t q4k_gemm(const void* x, int x_dtype, int64_t m, const uint32_t* qweight,
                     const uint16_t* scales, const uint32_t* zeros, int64_t n, int64_t k, int g,
-                    int sym, float* y, hipStream_t stream, const char** kname);
+                    int sym, void* y, int ydt, hipStream_t stream, const char** kname);
 // GPTQ error-feedback quantization (static RTN group quantizers, codes chosen against the
 // calibration Hessian); workspace: k*k + n*k + 64*n floats.
 int64_t q4k_gptq_workspace_floats(int64_t n, int64_t k);
