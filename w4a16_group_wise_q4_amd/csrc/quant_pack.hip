@@ -123,13 +123,15 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(const q4::QuantBatch bt
     }
 }
 
-// KV-cache rows (head_dim d dividing 512, at most 8 groups): one wave task is 512 consecutive weights, 512/d
-// input rows (contiguous in memory), and lane l quantizes weights 8l .. 8l+7 of it: row
-// 8l / d of the task, g/8 lanes per group.  A wave loads its task as one contiguous 1 KB
-// (bf16/fp16) and writes one code word per lane.  Each wave keeps P tasks' loads in
-// flight when there are tasks to spare.  The arithmetic is quant_group's, so the codes,
-// scales and zero points are those of the row kernel; the stores go to each row's
-// (head, token) slot of the cache with plain global stores (a wave's rows differ).
+// KV-cache rows (head_dim d dividing 512, at most 8 groups): one wave task is 512/d
+// consecutive tokens of one head (input rows t*heads + h, 512 weights), and lane l
+// quantizes weights 8l .. 8l+7 of it: token 8l / d of the task, g/8 lanes per group, a
+// row's d/8 lanes loading its d contiguous elements.  Tasks are numbered head-major and
+// consecutive waves take consecutive tasks, so a workgroup's codes, scales and zero words
+// land in consecutive cache slots of one head: contiguous runs, where tasks of consecutive
+// input rows would spread each wave's small stores over every head's region.  Each wave
+// keeps P tasks' loads in flight when there are tasks to spare.  The arithmetic is
+// quant_group's, so the codes, scales and zero points are those of the row kernel.
 template <int G, bool SYM, int DT>
 __global__ __launch_bounds__(256) void kv_quant_kernel(const void* __restrict__ kv, int rows, int d, int heads,
                                                        int t_cap, int t0, uint32_t* __restrict__ qc,
@@ -140,26 +142,29 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(const void* __restrict__ 
     const int lane = threadIdx.x & 63;
     const int waves = (int)gridDim.x * (int)(blockDim.x >> 6);
     const int gw = (int)blockIdx.x * (int)(blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int rpt = 512 / d;                  // rows per task
-    const int ro = (8 * lane) / d;            // this lane's row within the task
+    const int rpt = 512 / d;                  // tokens per task
+    const int ro = (8 * lane) / d;            // this lane's token within the task
     const int el = 8 * lane - ro * d;         // its first element within the row
     const int gr = el / G;                    // its group within the row
     const int lpr = d / 8;                    // lanes per row
-    const int tasks = (rows + rpt - 1) / rpt;
+    const int t_new = rows / heads;
+    const int tbn = (t_new + rpt - 1) / rpt;  // tasks per head
+    const int tasks = heads * tbn;
     const q4::rsrc rw = q4::make_rsrc(kv, (uint32_t)rows * (uint32_t)d * EB);
     for (int b = gw; b < tasks; b += P * waves) {
         float v[P][E];
 #pragma unroll
         for (int p = 0; p < P; ++p) {
             const int tk = b + p * waves;
-            const bool live = tk < tasks && tk * rpt + ro < rows;
-            load_slice<E, DT>(rw, live ? ((uint32_t)tk * 512u + 8u * (uint32_t)lane) * EB : kOff, v[p]);
+            const int h = tk / tbn, t = (tk - h * tbn) * rpt + ro;
+            const bool live = tk < tasks && t < t_new;
+            load_slice<E, DT>(rw, live ? ((uint32_t)(t * heads + h) * (uint32_t)d + (uint32_t)el) * EB : kOff, v[p]);
         }
 #pragma unroll
         for (int p = 0; p < P; ++p) {
             const int tk = b + p * waves;
             if (tk >= tasks) break;  // wave-uniform
-            const int row = tk * rpt + ro;  // input row: token * heads + head
+            const int h = tk / tbn, t = (tk - h * tbn) * rpt + ro;
             uint16_t s16;
             int zi;
             uint32_t packed[1];
@@ -169,8 +174,8 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(const void* __restrict__ 
 #pragma unroll
             for (int m = LPG; m < 64; m <<= 1)
                 if (m < lpr) zn |= __shfl_xor(zn, m, 64);
-            if (row < rows) {
-                const int64_t orow = (int64_t)(row % heads) * t_cap + t0 + row / heads;
+            if (t < t_new) {
+                const int64_t orow = (int64_t)h * t_cap + t0 + t;
                 qc[orow * (d / 8) + el / 8] = packed[0];
                 if (el % G == 0) sc[orow * (d / G) + gr] = s16;
                 if (!SYM && el == 0) zc[orow * ((d / G + 7) / 8)] = zn;
@@ -239,7 +244,7 @@ namespace {
 template <int G, bool SYM>
 hipError_t launch_kv(const void* kv, int dt, int rows, int d, int heads, int t_cap, int t0, uint32_t* qc,
                      uint16_t* sc, uint32_t* zc, hipStream_t st) {
-    const int64_t tasks = ((int64_t)rows * d + 511) / 512;
+    const int64_t tasks = (int64_t)heads * ((rows / heads + 512 / d - 1) / (512 / d));
     const int64_t cap = (int64_t)(g_num_cus > 0 ? g_num_cus : 256) * 32;
     const int64_t waves = tasks < cap ? tasks : cap;  // one task per wave while they last
     const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
