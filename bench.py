@@ -271,7 +271,7 @@ def main():
     ap.add_argument("--steps", type=int, default=340)
     ap.add_argument("--warmup", type=int, default=34)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--legs", default="gemm,quant,sweep,mlp,mse,kv,midm,gptq",
+    ap.add_argument("--legs", default="gemm,quant,sweep,mlp,mse,dequant,kv,midm,gptq",
                     help="comma list of legs besides the headline decode GEMV")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy 5 times (the "
@@ -420,6 +420,26 @@ def main():
                                        "lane-instructions/s over the kernel's vector instructions per "
                                        "weight (190.1 asym, 165.0 sym at g128 bf16)",
                            "results": res}
+
+    # ------------------------------------------------------------ full dequantization
+    if "dequant" in legs:
+        res = {}
+        for i, mat in enumerate(cfg["mats"]):
+            p = base[i]
+            for odt, ob in ((torch.bfloat16, 2), (torch.float32, 4)):
+                o = torch.empty((p.n, p.k), dtype=odt, device=dev)
+                q4.q4_dequant(p, out=o)
+                kname = q4.q4_last_kernel()
+                torch.cuda.synchronize()
+                t = graph_ms(capture([lambda p=p, o=o: q4.q4_dequant(p, out=o)] * 10), 10) / 10 * 1e-3
+                db = quant_bytes(p.n, p.k, 128, False, in_bytes=0) + p.n * p.k * ob
+                res[f"{p.n}x{p.k} -> {str(odt).split('.')[-1]}"] = {
+                    "kernel": kname, "us": round(t * 1e6, 2), "bytes": db,
+                    "gbs": round(db / t / 1e9, 1), "frac_hbm": round(db / t / 1e9 / HBM_PEAK_GBS, 4)}
+                del o
+        out["dequant"] = {"workload": "7B-like decode matrices, g128 asym packed, to bf16 and fp32",
+                          "bytes": "codes n*k/2 + scales 2*n*k/g + zero words read, n*k*out "
+                                   "written", "results": res}
 
     # ------------------------------------------------------------ INT4 KV cache (decode attention)
     if "kv" in legs:
