@@ -46,6 +46,7 @@ __all__ = [
     "kv_tokens",
     "query",
     "KV_7B",
+    "sparse_groups",
 ]
 
 
@@ -185,3 +186,25 @@ def query(heads: int, head_dim: int, seed: int, dtype=torch.bfloat16) -> torch.T
 # along the head dimension, asymmetric (the pages' KV scheme), a 4096-token context.
 KV_7B = dict(heads=32, head_dim=128, group_size=32, symmetric=False, t=4096, t_cap=4096,
              k_seed=200, v_seed=201, q_seed=202)
+
+
+def sparse_groups(n: int, k: int, g: int, m: int, dtype=torch.bfloat16):
+    """A decode input built so that almost every code of a group equals its zero point
+    while those columns carry large activations: W [n, k] fp32 is zero except one weight
+    per group of g columns, at column (7j + 3) mod g of group j (the same columns in every
+    row), of magnitude (1 + r mod 7)/8 and sign (-1)^r in row r; x [m, k] is
+    64 * (1 + i/16) on the zero columns of row i, negated where k mod 3 == 0 in the odd
+    rows, and 2^-7 * (1 + i/8) on the weighted ones.  A dot product of such a row is small
+    while sum |x| over each group is about 64 g.  No randomness."""
+    cols = torch.tensor([j * g + (7 * j + 3) % g for j in range(k // g)], dtype=torch.int64)
+    w = torch.zeros(n, k, dtype=torch.float32)
+    r = torch.arange(n, dtype=torch.float32)
+    mag = (1.0 + torch.remainder(r, 7)) / 8.0
+    sign = 1.0 - 2.0 * torch.remainder(r, 2)
+    w[:, cols] = (mag * sign)[:, None]
+    i = torch.arange(m, dtype=torch.float32)[:, None]
+    kk = torch.arange(k)
+    neg = (kk % 3 == 0)[None, :] & (torch.arange(m) % 2 == 1)[:, None]
+    x = 64.0 * (1.0 + i / 16.0) * torch.where(neg, -1.0, 1.0)
+    x[:, cols] = (2.0 ** -7) * (1.0 + i / 8.0)
+    return w, x.to(dtype)

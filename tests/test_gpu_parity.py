@@ -473,6 +473,78 @@ def test_gemv_edge_cases(m, n, k, g, xdtype, sym):
     assert_linear_close(y, host_input(x), packed, n, k, g, sym, what=kname)
 
 
+def sparse_group_cases():
+    """(m, k, g, kernel) for the sparse-group input: the tile kernel (m = 1, 4), the wide
+    kernel (m = 16), the streaming kernel (k not a multiple of 128, or an odd group count)
+    and its column-chunked form (m = 16, activations beyond the LDS budget)."""
+    out = []
+    for g in (32, 64, 128):
+        out += [(1, 2048, g, "tile"), (4, 2048, g, "tile"), (16, 2048, g, "wide"),
+                (1, 2048 + g, g, "mfma"), (4, 2048 + g, g, "mfma"), (16, 4096 + g, g, "mfma")]
+    return out
+
+
+@pytest.mark.parametrize("m,k,g,path", sparse_group_cases())
+@pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("sym", [False, True])
+def test_gemv_sparse_groups(m, k, g, path, xdtype, sym):
+    """Groups whose codes all equal the zero point but one, with large activations on
+    those columns: sum |x| per group is about 64 g while each row's result is small, so a
+    kernel that formed x * (u - z) as a difference of two large biased sums would miss the
+    bound by far.  Every GEMV kernel must stay within it (the operand is the exact u - z)."""
+    n = 40
+    w, x = synthetic.sparse_groups(n, k, g, m, xdtype)
+    note(f"gemv sparse groups m={m} k={k} g={g} {path} {xdtype} sym={sym}")
+    p, _ = pack_guarded(w.to(DEV), g, sym)
+    y, kname = run_linear(x, p)
+    t = "f16" if xdtype == torch.float16 else "bf16"
+    assert kname == f"q4_gemv_{path}_{t}"
+    packed = assert_pack_exact(p, host_input(w), g, sym)
+    worst = assert_linear_close(y, host_input(x), packed, n, k, g, sym, what=kname)
+    assert worst < 1e-4, f"{kname}: worst error / (|x||w|) = {worst:.3g}"
+
+
+def ranged_activations(kind, m, k, seed):
+    """bf16 activations whose exponent range picks the operand route of the decode kernels'
+    bf16 path: 'narrow' N(0,1); 'huge' and 'tiny' the same times 2^100 and 2^-100 (narrow,
+    far from 1); 'wide' with every 37th entry times 2^24 and every 41st times 2^-24 (more
+    than 29 binades in every slice); 'subnormal' with every 53rd entry a bf16 subnormal;
+    'split' wide in the first half of k and narrow in the second."""
+    x = synthetic.activations(m, k, seed, dtype=torch.float32)
+    kk = torch.arange(k)
+    if kind == "huge":
+        x = x * 2.0 ** 100
+    elif kind == "tiny":
+        x = x * 2.0 ** -100
+    elif kind in ("wide", "split"):
+        sel = kk < k // 2 if kind == "split" else torch.ones(k, dtype=torch.bool)
+        x[:, (kk % 37 == 0) & sel] *= 2.0 ** 24
+        x[:, (kk % 41 == 0) & sel] *= 2.0 ** -24
+    elif kind == "subnormal":
+        x[:, kk % 53 == 0] *= 2.0 ** -130
+    return x.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("kind", ["narrow", "huge", "tiny", "wide", "subnormal", "split"])
+@pytest.mark.parametrize("m,n,k,g", [(1, 70, 4096, 128), (3, 40, 2048, 32), (2, 33, 5120, 64),
+                                     (8, 40, 2048, 128), (1, 40, 2048 + 64, 64)])
+def test_gemv_activation_ranges(kind, m, n, k, g):
+    """bf16 activations of every exponent range the decode kernels distinguish: the tile
+    kernel converts a slice to exact fp16 when its nonzero exponents span at most 29
+    binades and keeps the exact bf16 operand otherwise; the other kernels keep the bf16
+    operand.  Each result must meet the bound whichever route a wave took."""
+    w = torch.from_numpy(pins.random_weights(n + k + g, max(n, 12), k)[:n])
+    x = ranged_activations(kind, m, k, seed=m * 29 + k)
+    note(f"gemv activation range {kind} m={m} n={n} k={k} g={g}")
+    for sym in (False, True):
+        p, _ = pack_guarded(w.to(DEV), g, sym)
+        y, kname = run_linear(x, p)
+        assert kname in gemv_kernels()
+        packed = assert_pack_exact(p, host_input(w), g, sym)
+        assert np.isfinite(y).all()
+        assert_linear_close(y, host_input(x), packed, n, k, g, sym, what=f"{kname} {kind}")
+
+
 @pytest.mark.parametrize("m,g", [(1, 64), (5, 64), (16, 64), (17, 64), (64, 64), (1, 128),
                                  (3, 128)])
 @pytest.mark.parametrize("sym", [False, True])

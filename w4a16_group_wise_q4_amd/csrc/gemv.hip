@@ -29,15 +29,14 @@
 // of GW = g/8 words, so the 32 k-slots of each MFMA lie in one group and the group's
 // scale applies to the MFMA result.
 //
-// Dequantization.  bf16 activations: a nibble OR-ed into the mantissa of 128.0 gives
-// the exact bf16 value 128 + u (one v_and_or_b32 per two weights).  The offset is removed
-// per group with a second MFMA whose weight operand is the constant 128 + z (also exact in
-// bf16):
-//   sum x(u - z) = D - C,   D = sum x(128 + u),  C = sum x(128 + z).
-// Where every code of a group equals its zero point (an all-zero group), D and C are the
-// same computation on the same operands, so the group contributes exactly zero.
-// fp16 activations: 1024 + u in fp16 minus (1024 + z) with one packed fp16 subtraction
-// gives the exact u - z.  Either way products are exact and sums are fp32.
+// Dequantization.  The weight operand is the exact small integer u - z.  bf16
+// activations: the nibbles plus 128 - z per byte, XOR 0x80, give u - z as signed bytes,
+// converted exactly to fp32 and narrowed to bf16 by keeping the upper half (natural column
+// order, so the activations are staged as loaded).  fp16 activations: 1024 + u in fp16
+// minus (1024 + z) with one packed fp16 subtraction gives the exact u - z (pairs of
+// columns i, i+4; the staged activations are permuted to match).  Either way products are
+// exact and only the fp32 sums round, so the error of a group's dot product is relative to
+// sum |x| |u - z|.
 #include "q4_device.h"
 #include "gemv_tile.h"
 #include "q4_launch.h"
@@ -70,7 +69,7 @@ template <int G, bool SYM, bool XF16>
 __device__ __forceinline__ void unit_mac(q4::f32x4& acc, const Unit& d, const q4::u32x4* xs,
                                          int wrel, const uint16_t* s_row,
                                          const uint32_t* z_row, int gbase, bool ok0, int c,
-                                         uint32_t kMask, uint32_t kBias, int KWrem) {
+                                         int KWrem, uint32_t kMask, uint32_t kMagic) {
     constexpr int GW = G / 8, LW = G / 32, NH = 4 / LW;
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
@@ -89,20 +88,15 @@ __device__ __forceinline__ void unit_mac(q4::f32x4& acc, const Unit& d, const q4
             const q4::f16x2 bias = {b, b};
 #pragma unroll
             for (int a = 0; a < LW; ++a)
-                dv = q4::mfma_f16(xa[a], q4::decode_f16_exact(d.w[hh * LW + a], bias), dv);
+                dv = q4::mfma_f16(xa[a], q4::decode_f16_exact(d.w[hh * LW + a], bias, kMask, kMagic), dv);
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[i] = ok ? acc[i] + s * dv[i] : acc[i];
         } else {
-            const uint32_t zb = (uint32_t)z * 0x00010001u + kBias;  // bf16 (128+z) x2
-            const q4::u32x4 zop = {zb, zb, zb, zb};
-            q4::f32x4 dc = {0.f, 0.f, 0.f, 0.f};
+            const uint32_t zb = q4::bf16_zero_bias(z);
 #pragma unroll
-            for (int a = 0; a < LW; ++a) {
-                dv = q4::mfma_bf16(xa[a], q4::decode_bf16_biased(d.w[hh * LW + a], kMask, kBias), dv);
-                dc = q4::mfma_bf16(xa[a], zop, dc);
-            }
+            for (int a = 0; a < LW; ++a) dv = q4::mfma_bf16(xa[a], q4::decode_bf16_exact(d.w[hh * LW + a], zb), dv);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = ok ? acc[i] + s * (dv[i] - dc[i]) : acc[i];
+            for (int i = 0; i < 4; ++i) acc[i] = ok ? acc[i] + s * dv[i] : acc[i];
         }
     }
 }
@@ -176,9 +170,8 @@ __global__ __launch_bounds__(MAXT, MINW) void gemv_stream_kernel(const GemvBatch
     uint32_t* meta0 = reinterpret_cast<uint32_t*>(lds + xs_end);
     q4::f32x4* red0 = reinterpret_cast<q4::f32x4*>(lds + xs_end + 2 * mbuf);
     const q4::u32x4* xs = lds + (col < M ? col : M) * RS;  // padding lanes: zero row
-
     const uint32_t kMask = q4::vreg_const(0x000F000Fu);
-    const uint32_t kBias = q4::vreg_const(0x43004300u);
+    const uint32_t kMagic = q4::vreg_const(0x64006400u);
 
     const int units = (K + 127) / 128;
     const int per = (units + S - 1) / S;
@@ -254,7 +247,7 @@ __global__ __launch_bounds__(MAXT, MINW) void gemv_stream_kernel(const GemvBatch
             const bool ok = u < u1;
             const int ue = ok ? u : ulast;
             unit_mac<G, SYM, XF16>(acc, bf[j], xs, ue * 16, s_row, z_row, ue * (4 / LW), ok,
-                                   c, kMask, kBias, KW - ue * 16);
+                                   c, KW - ue * 16, kMask, kMagic);
         }
     };
 
@@ -283,14 +276,14 @@ __global__ __launch_bounds__(MAXT, MINW) void gemv_stream_kernel(const GemvBatch
 #pragma unroll
         for (int j = 0; j < kStage; ++j) {
             const int v = j * nthreads + tid;
-            *(v < xs_end ? lds + v : spare) = q4::pair_perm(xv[j]);
+            *(v < xs_end ? lds + v : spare) = XF16 ? q4::pair_perm(xv[j]) : xv[j];
         }
         for (int v0 = kStage * nthreads; v0 < xs_end; v0 += nthreads) {  // larger m*k only
             const int v = v0 + tid;
             const int m = v / RS, jj = v - m * RS;
             const bool real = v < xs_end && m < M && jj < KW;
             const q4::u32x4 t = q4::buf_load_x4(rx, real ? (m * K + 8 * jj) * 2 : kOOB, 0);
-            *(v < xs_end ? lds + v : spare) = q4::pair_perm(t);
+            *(v < xs_end ? lds + v : spare) = XF16 ? q4::pair_perm(t) : t;
         }
         meta_store(meta0, mv);
     }
@@ -358,7 +351,6 @@ __global__ __launch_bounds__(512) void gemv_chunk_kernel(const uint16_t* __restr
                                                          const uint16_t* __restrict__ scales,
                                                          const uint32_t* __restrict__ zeros, int N,
                                                          int K, int KC, void* __restrict__ y, int ydt) {
-    constexpr int GW = G / 8;   // packed words per group
     constexpr int LW = G / 32;  // words per lane per group (one MFMA per word)
     constexpr int NH = 4 / LW;  // groups per 128-column unit
     extern __shared__ q4::u32x4 lds[];
@@ -385,7 +377,7 @@ __global__ __launch_bounds__(512) void gemv_chunk_kernel(const uint16_t* __restr
 
     const q4::rsrc rx = q4::make_rsrc(x, (uint32_t)M * K * 2u);
     const uint32_t kMask = q4::vreg_const(0x000F000Fu);
-    const uint32_t kBias = q4::vreg_const(0x43004300u);
+    const uint32_t kMagic = q4::vreg_const(0x64006400u);
 
     const int tile = blockIdx.x;
     const int n0 = tile * 16;
@@ -409,8 +401,8 @@ __global__ __launch_bounds__(512) void gemv_chunk_kernel(const uint16_t* __restr
             const bool ok = ub + i < u1;
             const int ue = ok ? ub + i : ulast;
             unit_mac<G, SYM, XF16>(acc, bf[i], xs, ue * 16 - cb / 8, meta_s + col * cg,
-                                   meta_z + col * czw, ue * NH - cb / G, ok, c, kMask, kBias,
-                                   KW - ue * 16);
+                                   meta_z + col * czw, ue * NH - cb / G, ok, c, KW - ue * 16,
+                                   kMask, kMagic);
         }
     };
 
@@ -459,14 +451,14 @@ __global__ __launch_bounds__(512) void gemv_chunk_kernel(const uint16_t* __restr
 #pragma unroll
         for (int j = 0; j < kStage; ++j) {
             const int v = j * nthreads + tid;
-            if (v < nvec) lds[v] = q4::pair_perm(xv[j]);
+            if (v < nvec) lds[v] = XF16 ? q4::pair_perm(xv[j]) : xv[j];
         }
         for (int v0 = kStage * nthreads; v0 < nvec; v0 += nthreads) {
             const int v = v0 + tid;
             const int m = v / RS, jj = v - m * RS;
             const bool real = v < nvec && m < M && jj < vpr;
             const q4::u32x4 t = q4::buf_load_x4(rx, real ? (m * K + cb + 8 * jj) * 2 : kOOB, 0);
-            if (v < nvec) lds[v] = q4::pair_perm(t);
+            if (v < nvec) lds[v] = XF16 ? q4::pair_perm(t) : t;
         }
 #pragma unroll
         for (int j = 0; j < kMS; ++j) {

@@ -30,13 +30,15 @@
 //   g = 64:  register a, lane row c -> unit word 8(a/2) + a%2 + 4(c%2) + 2(c/2)
 //   g = 32:  register a, lane row c -> unit word 4a + c
 //
-// Dequantization as in the streaming kernel: bf16 activations multiply 128 + u (exact,
-// the nibble OR-ed into the mantissa of 128.0) and a second MFMA with the constant 128 + z
-// is subtracted per group, so an all-zero-point group gives exactly zero; fp16 activations
-// multiply the exact u - z from one packed fp16 subtraction of 1024 + z.
+// Dequantization as in the streaming kernel: the weight operand is the exact small integer
+// u - z (q4_device.h), in natural column order for bf16 activations and in (i, i+4) pairs
+// for fp16 ones, whose activation vectors are permuted to match.  Products are exact and
+// the fp32 sums carry the only rounding.
 //
 // LDS (16-byte vectors): S x [m][UPW*16] activation slices | S x 64 x MQ partial sums.
 #pragma once
+
+#include <type_traits>
 
 #include "q4_device.h"
 
@@ -148,6 +150,29 @@ __global__ __launch_bounds__(MQ == 1 ? 1024 : 512) void gemv_tile_kernel(const q
     }
     __builtin_amdgcn_sched_barrier(0);
 
+    // ---- operand route.  fp16 activations use the exact fp16 decode.  bf16 activations
+    // use it too when the nonzero exponents of the wave's slice span at most 29 binades
+    // (q4_device.h): the slice is staged as exact fp16 values x * 2^xs and the wave's sums
+    // are scaled back by 2^-xs.  Otherwise (a wider range, subnormal or non-finite values)
+    // the wave takes the exact bf16 decode.  Both routes multiply exact operands.
+    bool f16r = XF16;
+    int xs = 0;
+    if constexpr (!XF16) {
+        uint32_t hi = 0u, lo = 0xFFFFFFFFu;
+#pragma unroll
+        for (int m = 0; m < MQ; ++m)
+#pragma unroll
+            for (int j = 0; j < XV; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) q4::bf16_exp_range(xv[m][j][e], hi, lo);
+        const uint32_t hmax = (hi & 0xFFFFu) > (hi >> 16) ? (hi & 0xFFFFu) : (hi >> 16);
+        const uint32_t lmin = (lo & 0xFFFFu) < (lo >> 16) ? (lo & 0xFFFFu) : (lo >> 16);
+        const int emax = __builtin_amdgcn_readfirstlane((int)q4::wave_reduce<true>(hmax));
+        const int emin = __builtin_amdgcn_readfirstlane((int)q4::wave_reduce<false>(lmin));
+        f16r = emax == 0 || (emax <= 254 && emin >= 1 && emax - emin <= 29);
+        xs = f16r && emax != 0 ? 142 - emax : 0;  // the bf16 route leaves x unscaled
+    }
+
     // ---- this wave's activation slice into its LDS region, in the decoder's slot order.
     // Rows m..MQ-1 (zeros) go to this wave's partial-sum slots, which it overwrites later:
     // no store (and so no load) sits behind a branch.
@@ -158,7 +183,10 @@ __global__ __launch_bounds__(MQ == 1 ? 1024 : 512) void gemv_tile_kernel(const q
 #pragma unroll
         for (int j = 0; j < XV; ++j) {
             q4::u32x4* dst = xw + m * SLICE + (UPW >= 4 ? j * 64 + lane : (lane & 31));
-            *(m == 0 || m < M ? dst : spare) = q4::pair_perm(xv[m][j]);
+            q4::u32x4 v = xv[m][j];
+            if constexpr (XF16) v = q4::pair_perm(v);
+            else if (f16r) v = q4::bf16_to_f16_pairs(v, xs);
+            *(m == 0 || m < M ? dst : spare) = v;
         }
 
     // zero points of the slice's groups from nibble 0 on (a slice may start mid-word)
@@ -176,11 +204,13 @@ __global__ __launch_bounds__(MQ == 1 ? 1024 : 512) void gemv_tile_kernel(const q
     const int mrow = r < M ? r : M - 1;
     const int lb = G == 128 ? 4 * c : (G == 64 ? 4 * (c & 1) + 2 * (c >> 1) : c);
     const q4::u32x4* xr = xw + mrow * SLICE + lb;
-    const uint32_t kMask = q4::vreg_const(0x000F000Fu);
-    const uint32_t kBias = q4::vreg_const(0x43004300u);
     float acc[MQ];
 #pragma unroll
     for (int q = 0; q < MQ; ++q) acc[q] = 0.f;
+    const uint32_t kMask = q4::vreg_const(0x000F000Fu);
+    const uint32_t kMagic = q4::vreg_const(0x64006400u);
+    auto slice = [&](auto route) {
+    constexpr bool F16 = decltype(route)::value;
 #pragma unroll
     for (int u = 0; u < UPW; ++u) {
         const bool valid = u < nu;
@@ -207,30 +237,36 @@ __global__ __launch_bounds__(MQ == 1 ? 1024 : 512) void gemv_tile_kernel(const q
             int z = 8;
             if constexpr (!SYM) z = (int)((zs[gi >> 3] >> (4 * (gi & 7))) & 0xFu);
             q4::f32x4 dv = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (XF16) {
+            if constexpr (F16) {
                 const _Float16 b = (_Float16)(1024 + z);
                 const q4::f16x2 bias = {b, b};
 #pragma unroll
                 for (int t = 0; t < RPG; ++t) {
                     const int a = h * RPG + t;
-                    dv = q4::mfma_f16(xa[a], q4::decode_f16_exact(wq[a], bias), dv);
+                    dv = q4::mfma_f16(xa[a], q4::decode_f16_exact(wq[a], bias, kMask, kMagic), dv);
                 }
-#pragma unroll
-                for (int q = 0; q < MQ; ++q) acc[q] = valid ? acc[q] + s * dv[q] : acc[q];
             } else {
-                const uint32_t zb = (uint32_t)z * 0x00010001u + kBias;  // bf16 (128+z) x2
-                const q4::u32x4 zop = {zb, zb, zb, zb};
-                q4::f32x4 dc = {0.f, 0.f, 0.f, 0.f};
+                const uint32_t zb = q4::bf16_zero_bias(z);
 #pragma unroll
                 for (int t = 0; t < RPG; ++t) {
                     const int a = h * RPG + t;
-                    dv = q4::mfma_bf16(xa[a], q4::decode_bf16_biased(wq[a], kMask, kBias), dv);
-                    dc = q4::mfma_bf16(xa[a], zop, dc);
+                    dv = q4::mfma_bf16(xa[a], q4::decode_bf16_exact(wq[a], zb), dv);
                 }
-#pragma unroll
-                for (int q = 0; q < MQ; ++q) acc[q] = valid ? acc[q] + s * (dv[q] - dc[q]) : acc[q];
             }
+#pragma unroll
+            for (int q = 0; q < MQ; ++q) acc[q] = valid ? acc[q] + s * dv[q] : acc[q];
         }
+    }
+    };
+    if constexpr (XF16) {
+        slice(std::true_type{});
+    } else {
+        if (f16r)
+            slice(std::true_type{});
+        else
+            slice(std::false_type{});
+#pragma unroll
+        for (int q = 0; q < MQ; ++q) acc[q] = __builtin_amdgcn_ldexpf(acc[q], -xs);
     }
 
     // ---- cross-wave sum (lanes 0..15 hold rows m = 0..MQ-1 of the tile's 16 columns)
@@ -387,7 +423,7 @@ __global__ __launch_bounds__(512) void gemv_wide_kernel(const q4::GemvBatch bt, 
     }
 
     const uint32_t kMask = q4::vreg_const(0x000F000Fu);
-    const uint32_t kBias = q4::vreg_const(0x43004300u);
+    const uint32_t kMagic = q4::vreg_const(0x64006400u);
     float acc[T][4];
 #pragma unroll
     for (int t = 0; t < T; ++t)
@@ -408,7 +444,10 @@ __global__ __launch_bounds__(512) void gemv_wide_kernel(const q4::GemvBatch bt, 
             const uint8_t* sb = ring + (slot * D + j) * UNIT_LDS;
             q4::u32x4 xa[4];
 #pragma unroll
-            for (int a = 0; a < 4; ++a) xa[a] = q4::pair_perm(*reinterpret_cast<const q4::u32x4*>(sb + xaddr[a]));
+            for (int a = 0; a < 4; ++a) {
+                const q4::u32x4 v = *reinterpret_cast<const q4::u32x4*>(sb + xaddr[a]);
+                xa[a] = XF16 ? q4::pair_perm(v) : v;
+            }
 #pragma unroll
             for (int t = 0; t < T; ++t) {
                 uint32_t wq[4] = {wb[slot][j][t][0], wb[slot][j][t][1], wb[slot][j][t][2], wb[slot][j][t][3]};
@@ -434,23 +473,19 @@ __global__ __launch_bounds__(512) void gemv_wide_kernel(const q4::GemvBatch bt, 
 #pragma unroll
                         for (int e = 0; e < RPG; ++e) {
                             const int a = h * RPG + e;
-                            dv = q4::mfma_f16(xa[a], q4::decode_f16_exact(wq[a], bias), dv);
+                            dv = q4::mfma_f16(xa[a], q4::decode_f16_exact(wq[a], bias, kMask, kMagic), dv);
                         }
 #pragma unroll
                         for (int q = 0; q < 4; ++q) acc[t][q] = valid ? acc[t][q] + s * dv[q] : acc[t][q];
                     } else {
-                        const uint32_t zb = (uint32_t)z * 0x00010001u + kBias;
-                        const q4::u32x4 zop = {zb, zb, zb, zb};
-                        q4::f32x4 dc = {0.f, 0.f, 0.f, 0.f};
+                        const uint32_t zb = q4::bf16_zero_bias(z);
 #pragma unroll
                         for (int e = 0; e < RPG; ++e) {
                             const int a = h * RPG + e;
-                            dv = q4::mfma_bf16(xa[a], q4::decode_bf16_biased(wq[a], kMask, kBias), dv);
-                            dc = q4::mfma_bf16(xa[a], zop, dc);
+                            dv = q4::mfma_bf16(xa[a], q4::decode_bf16_exact(wq[a], zb), dv);
                         }
 #pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            acc[t][q] = valid ? acc[t][q] + s * (dv[q] - dc[q]) : acc[t][q];
+                        for (int q = 0; q < 4; ++q) acc[t][q] = valid ? acc[t][q] + s * dv[q] : acc[t][q];
                     }
                 }
             }

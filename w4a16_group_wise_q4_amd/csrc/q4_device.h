@@ -1,7 +1,7 @@
 // q4_device.h — device-side helpers shared by the gfx950 kernels of libq4.
 //
-// Operand types for the CDNA4 16x16x32 MFMA, the exponent-bias nibble decoders, raw
-// buffer loads and the decode GEMV's kernel argument types.  Everything here is specific
+// Operand types for the CDNA4 16x16x32 MFMA, the exact nibble decoders, raw buffer loads
+// and the decode GEMV's kernel argument types.  Everything here is specific
 // to gfx950 (wave64, v_mfma_f32_16x16x32_{bf16,f16}).  The host-side launchers are
 // declared in q4_launch.h.
 #pragma once
@@ -34,10 +34,15 @@ __device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
 }
 
 // ---------------------------------------------------------------- nibble decoders
-// A packed word holds the codes of 8 consecutive columns, column i in bits 4i..4i+3.
-// Decoded pairs come out as (column i, column i+4) in one 32-bit register, i = 0..3, so
-// operand element 2i is column i and element 2i+1 is column i+4.  The activation operand
-// is permuted the same way (pair_perm below).
+// A packed word holds the codes of 8 consecutive columns, column i in bits 4i..4i+3.  Both
+// decoders return the exact small integers u - z (|u - z| <= 15 is exact in bf16 and fp16),
+// so every MFMA product is exact and only the fp32 sums round: the error of a dot product
+// is relative to sum |x| |u - z|, whatever the zero point.
+//
+// fp16: decoded pairs come out as (column i, column i+4) in one 32-bit register, i = 0..3,
+// so operand element 2i is column i and element 2i+1 is column i+4; the activation operand
+// is permuted the same way (pair_perm below).  bf16: natural column order (operand element
+// j is column j), so the activations are used as loaded.
 
 // A constant held in a VGPR the optimizer cannot see through.  gfx9 VOP3 encodings take no
 // literal operand, so (a & K1) | K2 with literal K1, K2 becomes two VOP2 ops; with both
@@ -48,28 +53,94 @@ __device__ __forceinline__ uint32_t vreg_const(uint32_t k) {
     return r;
 }
 
-// bf16 exponent bias: 0x4300 is 128.0 with a zero 7-bit mantissa, so OR-ing a nibble into
-// the low mantissa bits gives exactly 128 + u.  mask = 0x000F000F, bias = 0x43004300 (in
-// registers, see vreg_const): 3 shifts + 4 v_and_or_b32 per word.
-__device__ __forceinline__ u32x4 decode_bf16_biased(uint32_t w, uint32_t mask, uint32_t bias) {
+// Per-group constant of decode_bf16_exact: 128 - z in every byte.
+__device__ __forceinline__ uint32_t bf16_zero_bias(int z) { return 0x80808080u - (uint32_t)z * 0x01010101u; }
+
+// bf16: the nibbles of the even columns (bytes of w & 0x0F0F0F0F) and of the odd columns
+// (bytes of (w >> 4) & 0x0F0F0F0F) plus 128 - z give 128 + u - z in [113, 143] per byte,
+// with no carry between bytes; XOR 0x80 turns each byte into the two's complement of
+// u - z.  Each signed byte converts exactly to fp32 (v_cvt_f32_i32 with a sign-extended
+// byte select), whose upper half is the exact bf16 value; one v_perm_b32 packs two of
+// them.  zb = bf16_zero_bias(z).  7 integer ops, 8 conversions and 4 permutes per word.
+__device__ __forceinline__ u32x4 decode_bf16_exact(uint32_t w, uint32_t zb) {
+    const uint32_t ev = ((w & 0x0F0F0F0Fu) + zb) ^ 0x80808080u;         // columns 0, 2, 4, 6
+    const uint32_t od = (((w >> 4) & 0x0F0F0F0Fu) + zb) ^ 0x80808080u;  // columns 1, 3, 5, 7
     u32x4 r;
-    r[0] = (w & mask) | bias;
-    r[1] = ((w >> 4) & mask) | bias;
-    r[2] = ((w >> 8) & mask) | bias;
-    r[3] = ((w >> 12) & mask) | bias;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const float e = (float)(int8_t)((ev >> (8 * b)) & 0xFF);
+        const float o = (float)(int8_t)((od >> (8 * b)) & 0xFF);
+        // upper halves: bytes 2, 3 of e (column 2b) then bytes 2, 3 of o (column 2b + 1)
+        r[b] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, o), __builtin_bit_cast(uint32_t, e),
+                                     0x07060302u);
+    }
     return r;
 }
 
 // fp16 exponent bias: 0x6400 is 1024.0 with a zero 10-bit mantissa -> 1024 + u; then a
-// packed fp16 subtraction of (1024 + z) leaves the exact small integer u - z.
-__device__ __forceinline__ u32x4 decode_f16_exact(uint32_t w, f16x2 bias) {
+// packed fp16 subtraction of (1024 + z) leaves the exact small integer u - z.  mask =
+// 0x000F000F and magic = 0x64006400 are passed in registers (vreg_const), so each pair is
+// one v_and_or_b32 (after a shift) and one v_pk_add_f16: 11 instructions per word.
+__device__ __forceinline__ u32x4 decode_f16_exact(uint32_t w, f16x2 bias, uint32_t mask, uint32_t magic) {
     u32x4 r;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        uint32_t t = ((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
+        uint32_t t = ((w >> (4 * i)) & mask) | magic;
         f16x2 v = __builtin_bit_cast(f16x2, t) - bias;
         r[i] = __builtin_bit_cast(uint32_t, v);
     }
+    return r;
+}
+
+// ---------------------------------------------------------------- bf16 activations as fp16
+// A bf16 value with exponent field e in [1, 254] (1.m * 2^(e-127), 8 significant bits)
+// times 2^xs is an exact normal fp16 value when e + xs - 127 lies in [-14, 15].  So a set
+// of bf16 values whose nonzero exponent fields span emin..emax with emax - emin <= 29
+// converts exactly to fp16 after scaling by 2^(142 - emax); zeros stay zero.  The decode
+// kernels use this to run bf16 activations through the cheaper exact fp16 weight decode,
+// and scale their sums back by 2^-xs (exact barring fp32 overflow).
+
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+// Per 16-bit half of a register of two bf16 values: the exponent field (for the maximum)
+// and a conservative exponent for the minimum: e - 1 or e for nonzero magnitudes (e - 1
+// when the 7 mantissa bits are 0) and 0x1FF for +-0, which therefore never lowers it.
+__device__ __forceinline__ void bf16_exp_range(uint32_t b, uint32_t& hi, uint32_t& lo) {
+    const u16x2 mag = __builtin_bit_cast(u16x2, b & 0x7FFF7FFFu);
+    const u16x2 e = mag >> (u16x2){7, 7};
+    const u16x2 e1 = (mag - (u16x2){1, 1}) >> (u16x2){7, 7};
+    hi = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, hi), e));
+    lo = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, lo), e1));
+}
+
+// Maximum / minimum of a value over the 64 lanes of a wave (every lane gets the result):
+// DPP within rows of 16, then the 16- and 32-lane swaps.
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t v) {
+    auto op = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+    v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+    v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+    const auto s16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = op(s16[0], s16[1]);
+    const auto s32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return op(s32[0], s32[1]);
+}
+
+// Eight bf16 values (natural order, four registers) times 2^xs as fp16 in the (i, i+4)
+// pair order of decode_f16_exact.  Exact under the range condition above.
+__device__ __forceinline__ u32x4 bf16_to_f16_pairs(u32x4 v, int xs) {
+    auto cv = [xs](uint32_t a, uint32_t b) {  // a, b: fp32 bit patterns of two bf16 values
+        const float fa = __builtin_amdgcn_ldexpf(__builtin_bit_cast(float, a), xs);
+        const float fb = __builtin_amdgcn_ldexpf(__builtin_bit_cast(float, b), xs);
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(fa, fb));
+    };
+    u32x4 r;
+    r[0] = cv(v[0] << 16, v[2] << 16);                  // (x0, x4)
+    r[1] = cv(v[0] & 0xFFFF0000u, v[2] & 0xFFFF0000u);  // (x1, x5)
+    r[2] = cv(v[1] << 16, v[3] << 16);                  // (x2, x6)
+    r[3] = cv(v[1] & 0xFFFF0000u, v[3] & 0xFFFF0000u);  // (x3, x7)
     return r;
 }
 
