@@ -84,8 +84,7 @@ __device__ __forceinline__ void unit_mac(q4::f32x4& acc, const Unit& d, const q4
         if constexpr (!SYM) z = (int)((z_row[gl >> 3] >> (4 * (gl & 7))) & 0xFu);
         q4::f32x4 dv = {0.f, 0.f, 0.f, 0.f};
         if constexpr (XF16) {
-            const _Float16 b = (_Float16)(1024 + z);
-            const q4::f16x2 bias = {b, b};
+            const q4::f16x2 bias = q4::f16_bias_pair((uint32_t)z);
 #pragma unroll
             for (int a = 0; a < LW; ++a)
                 dv = q4::mfma_f16(xa[a], q4::decode_f16_exact(d.w[hh * LW + a], bias, kMask, kMagic), dv);

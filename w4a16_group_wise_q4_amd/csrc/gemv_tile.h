@@ -151,31 +151,40 @@ __global__ __launch_bounds__(MQ == 1 ? 1024 : 512) void gemv_tile_kernel(const q
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- operand route.  fp16 activations use the exact fp16 decode.  bf16 activations
-    // use it too when the nonzero exponents of the wave's slice span at most 29 binades
-    // (q4_device.h): the slice is staged as exact fp16 values x * 2^xs and the wave's sums
-    // are scaled back by 2^-xs.  Otherwise (a wider range, subnormal or non-finite values)
-    // the wave takes the exact bf16 decode.  Both routes multiply exact operands.
+    // use the split fp16 decode when the nonzero exponents of the wave's slice span at most
+    // 25 binades (q4_device.h): the slice is staged as exact fp16 values (x * 2^xs, the odd
+    // columns of each word divided by 16 more) and the wave's sums are scaled back by
+    // 2^-xs.  Otherwise (a wider range, subnormal or non-finite values) the wave takes the
+    // exact bf16 decode.  Both routes multiply exact operands.
     bool f16r = XF16;
     int xs = 0;
     if constexpr (!XF16) {
-        uint32_t hi = 0u, lo = 0xFFFFFFFFu;
+        // rows past m read zeros, which leave both extremes alone
+        q4::u16x2 hi = {0, 0}, lo = {0xFFFF, 0xFFFF};
 #pragma unroll
         for (int m = 0; m < MQ; ++m)
 #pragma unroll
             for (int j = 0; j < XV; ++j)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) q4::bf16_exp_range(xv[m][j][e], hi, lo);
-        const uint32_t hmax = (hi & 0xFFFFu) > (hi >> 16) ? (hi & 0xFFFFu) : (hi >> 16);
-        const uint32_t lmin = (lo & 0xFFFFu) < (lo >> 16) ? (lo & 0xFFFFu) : (lo >> 16);
-        const int emax = __builtin_amdgcn_readfirstlane((int)q4::wave_reduce<true>(hmax));
-        const int emin = __builtin_amdgcn_readfirstlane((int)q4::wave_reduce<false>(lmin));
-        f16r = emax == 0 || (emax <= 254 && emin >= 1 && emax - emin <= 29);
+                for (int e = 0; e < 4; ++e) q4::bf16_mag_range(xv[m][j][e], hi, lo);
+        // largest magnitude in the low half, 0xFFFF - (smallest nonzero magnitude - 1) in
+        // the high half: one maximum over the wave gives both
+        const uint32_t hm = hi[0] > hi[1] ? hi[0] : hi[1];
+        const uint32_t lm = lo[0] < lo[1] ? lo[0] : lo[1];
+        const uint32_t red = q4::wave_max_u16x2(hm | ((0xFFFFu - lm) << 16));
+        const int rr = __builtin_amdgcn_readfirstlane((int)red);
+        const int emax = (rr & 0xFFFF) >> 7;                              // 0: every value is zero
+        const int emin = (int)((0xFFFFu - ((uint32_t)rr >> 16)) + 1u) >> 7;  // smallest nonzero
+        // bitwise, not short-circuit: no branch may split the block the loads sit in
+        f16r = (emax == 0) | ((emax <= 254) & (emin >= 1) & (emax - emin <= 25));
         xs = f16r && emax != 0 ? 142 - emax : 0;  // the bf16 route leaves x unscaled
     }
 
     // ---- this wave's activation slice into its LDS region, in the decoder's slot order.
     // Rows m..MQ-1 (zeros) go to this wave's partial-sum slots, which it overwrites later:
-    // no store (and so no load) sits behind a branch.
+    // no store (and so no load) sits behind a branch.  The fp16 form is computed either
+    // way and selected: a branch here would let the compiler sink the weight loads issued
+    // above below it, behind the wait for the activations and the range reduction.
     q4::u32x4* xw = lds + w * (M * SLICE);
     q4::u32x4* spare = lds + S * M * SLICE + w * 64 + lane;
 #pragma unroll
@@ -184,8 +193,13 @@ __global__ __launch_bounds__(MQ == 1 ? 1024 : 512) void gemv_tile_kernel(const q
         for (int j = 0; j < XV; ++j) {
             q4::u32x4* dst = xw + m * SLICE + (UPW >= 4 ? j * 64 + lane : (lane & 31));
             q4::u32x4 v = xv[m][j];
-            if constexpr (XF16) v = q4::pair_perm(v);
-            else if (f16r) v = q4::bf16_to_f16_pairs(v, xs);
+            if constexpr (XF16) {
+                v = q4::pair_perm(v);
+            } else {
+                const q4::u32x4 h = q4::bf16_to_f16_split(v, xs);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = f16r ? h[e] : v[e];
+            }
             *(m == 0 || m < M ? dst : spare) = v;
         }
 
@@ -208,6 +222,7 @@ __global__ __launch_bounds__(MQ == 1 ? 1024 : 512) void gemv_tile_kernel(const q
 #pragma unroll
     for (int q = 0; q < MQ; ++q) acc[q] = 0.f;
     const uint32_t kMask = q4::vreg_const(0x000F000Fu);
+    const uint32_t kMaskHi = q4::vreg_const(0x00F000F0u);
     const uint32_t kMagic = q4::vreg_const(0x64006400u);
     auto slice = [&](auto route) {
     constexpr bool F16 = decltype(route)::value;
@@ -237,13 +252,20 @@ __global__ __launch_bounds__(MQ == 1 ? 1024 : 512) void gemv_tile_kernel(const q
             int z = 8;
             if constexpr (!SYM) z = (int)((zs[gi >> 3] >> (4 * (gi & 7))) & 0xFu);
             q4::f32x4 dv = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (F16) {
-                const _Float16 b = (_Float16)(1024 + z);
-                const q4::f16x2 bias = {b, b};
+            if constexpr (XF16) {
+                const q4::f16x2 bias = q4::f16_bias_pair((uint32_t)z);
 #pragma unroll
                 for (int t = 0; t < RPG; ++t) {
                     const int a = h * RPG + t;
                     dv = q4::mfma_f16(xa[a], q4::decode_f16_exact(wq[a], bias, kMask, kMagic), dv);
+                }
+            } else if constexpr (F16) {
+                const q4::f16x2 bias_lo = q4::f16_bias_pair((uint32_t)z);
+                const q4::f16x2 bias_hi = q4::f16_bias_pair((uint32_t)z << 4);
+#pragma unroll
+                for (int t = 0; t < RPG; ++t) {
+                    const int a = h * RPG + t;
+                    dv = q4::mfma_f16(xa[a], q4::decode_f16_split(wq[a], bias_lo, bias_hi, kMask, kMaskHi, kMagic), dv);
                 }
             } else {
                 const uint32_t zb = q4::bf16_zero_bias(z);
@@ -468,8 +490,7 @@ __global__ __launch_bounds__(512) void gemv_wide_kernel(const q4::GemvBatch bt, 
                     if constexpr (!SYM) z = (int)((zs[t][gi >> 3] >> (4 * (gi & 7))) & 0xFu);
                     q4::f32x4 dv = {0.f, 0.f, 0.f, 0.f};
                     if constexpr (XF16) {
-                        const _Float16 bb = (_Float16)(1024 + z);
-                        const q4::f16x2 bias = {bb, bb};
+                        const q4::f16x2 bias = q4::f16_bias_pair((uint32_t)z);
 #pragma unroll
                         for (int e = 0; e < RPG; ++e) {
                             const int a = h * RPG + e;

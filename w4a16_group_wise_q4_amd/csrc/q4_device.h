@@ -94,30 +94,31 @@ __device__ __forceinline__ u32x4 decode_f16_exact(uint32_t w, f16x2 bias, uint32
 
 // ---------------------------------------------------------------- bf16 activations as fp16
 // A bf16 value with exponent field e in [1, 254] (1.m * 2^(e-127), 8 significant bits)
-// times 2^xs is an exact normal fp16 value when e + xs - 127 lies in [-14, 15].  So a set
-// of bf16 values whose nonzero exponent fields span emin..emax with emax - emin <= 29
-// converts exactly to fp16 after scaling by 2^(142 - emax); zeros stay zero.  The decode
-// kernels use this to run bf16 activations through the cheaper exact fp16 weight decode,
-// and scale their sums back by 2^-xs (exact barring fp32 overflow).
+// times 2^t is an exact normal fp16 value when e + t - 127 lies in [-14, 15].  So a set of
+// bf16 values whose nonzero exponent fields span emin..emax converts exactly to fp16 after
+// scaling by 2^xs, xs = 142 - emax, and a quarter of those values (2^(xs-4)) still does when
+// emax - emin <= 25; zeros stay zero.  The decode tile kernel uses this to run bf16
+// activations through the cheaper exact fp16 decode below (decode_f16_split), and scales
+// its sums back by 2^-xs (exact barring fp32 overflow).
 
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
-// Per 16-bit half of a register of two bf16 values: the exponent field (for the maximum)
-// and a conservative exponent for the minimum: e - 1 or e for nonzero magnitudes (e - 1
-// when the 7 mantissa bits are 0) and 0x1FF for +-0, which therefore never lowers it.
-__device__ __forceinline__ void bf16_exp_range(uint32_t b, uint32_t& hi, uint32_t& lo) {
+// Running per-half maximum of the magnitudes |b| and minimum of |b| - 1 (mod 2^16, so a
+// zero magnitude gives 0xFFFF and never lowers it) of a register of two bf16 values.
+// Magnitudes of floats order like their bit patterns.
+__device__ __forceinline__ void bf16_mag_range(uint32_t b, u16x2& hi, u16x2& lo) {
     const u16x2 mag = __builtin_bit_cast(u16x2, b & 0x7FFF7FFFu);
-    const u16x2 e = mag >> (u16x2){7, 7};
-    const u16x2 e1 = (mag - (u16x2){1, 1}) >> (u16x2){7, 7};
-    hi = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, hi), e));
-    lo = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, lo), e1));
+    hi = __builtin_elementwise_max(hi, mag);
+    lo = __builtin_elementwise_min(lo, mag - (u16x2){1, 1});
 }
 
-// Maximum / minimum of a value over the 64 lanes of a wave (every lane gets the result):
+// Maximum of each 16-bit half over the 64 lanes of a wave (every lane gets the result):
 // DPP within rows of 16, then the 16- and 32-lane swaps.
-template <bool MAX>
-__device__ __forceinline__ uint32_t wave_reduce(uint32_t v) {
-    auto op = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+__device__ __forceinline__ uint32_t wave_max_u16x2(uint32_t v) {
+    auto op = [](uint32_t a, uint32_t b) {
+        return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                      __builtin_bit_cast(u16x2, b)));
+    };
     v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
     v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
     v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
@@ -128,19 +129,44 @@ __device__ __forceinline__ uint32_t wave_reduce(uint32_t v) {
     return op(s32[0], s32[1]);
 }
 
-// Eight bf16 values (natural order, four registers) times 2^xs as fp16 in the (i, i+4)
-// pair order of decode_f16_exact.  Exact under the range condition above.
-__device__ __forceinline__ u32x4 bf16_to_f16_pairs(u32x4 v, int xs) {
-    auto cv = [xs](uint32_t a, uint32_t b) {  // a, b: fp32 bit patterns of two bf16 values
-        const float fa = __builtin_amdgcn_ldexpf(__builtin_bit_cast(float, a), xs);
-        const float fb = __builtin_amdgcn_ldexpf(__builtin_bit_cast(float, b), xs);
+// Eight bf16 values (natural order, four registers) as the fp16 operand of
+// decode_f16_split: pairs (x_i, x_{i+4}) times 2^xs for i = 0, 2 and times 2^(xs-4) for
+// i = 1, 3.  Exact under the range condition above.
+__device__ __forceinline__ u32x4 bf16_to_f16_split(u32x4 v, int xs) {
+    auto cv = [](uint32_t a, uint32_t b, int t) {  // a, b: fp32 bit patterns of two bf16 values
+        const float fa = __builtin_amdgcn_ldexpf(__builtin_bit_cast(float, a), t);
+        const float fb = __builtin_amdgcn_ldexpf(__builtin_bit_cast(float, b), t);
         return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(fa, fb));
     };
     u32x4 r;
-    r[0] = cv(v[0] << 16, v[2] << 16);                  // (x0, x4)
-    r[1] = cv(v[0] & 0xFFFF0000u, v[2] & 0xFFFF0000u);  // (x1, x5)
-    r[2] = cv(v[1] << 16, v[3] << 16);                  // (x2, x6)
-    r[3] = cv(v[1] & 0xFFFF0000u, v[3] & 0xFFFF0000u);  // (x3, x7)
+    r[0] = cv(v[0] << 16, v[2] << 16, xs);                      // (x0, x4)
+    r[1] = cv(v[0] & 0xFFFF0000u, v[2] & 0xFFFF0000u, xs - 4);  // (x1, x5) / 16
+    r[2] = cv(v[1] << 16, v[3] << 16, xs);                      // (x2, x6)
+    r[3] = cv(v[1] & 0xFFFF0000u, v[3] & 0xFFFF0000u, xs - 4);  // (x3, x7) / 16
+    return r;
+}
+
+// fp16 pair (1024 + v, 1024 + v) for an integer 0 <= v < 1024 (exact), built with integer
+// operations: 1024.0 is 0x6400 and the mantissa's ulp there is 1.
+__device__ __forceinline__ f16x2 f16_bias_pair(uint32_t v) {
+    const uint32_t b = 0x6400u + v;
+    return __builtin_bit_cast(f16x2, b | (b << 16));
+}
+
+// The exact fp16 decode in 9 instructions per word: the nibbles of columns 0/4 and 2/6 sit
+// in the low mantissa bits (1024 + u), those of columns 1/5 and 3/7 four bits higher
+// (1024 + 16u, exact too), so one shift serves all four pairs.  Subtracting 1024 + z and
+// 1024 + 16z (bias_lo, bias_hi) leaves u - z and 16(u - z); the activations of the odd
+// columns are staged divided by 16 to match (bf16_to_f16_split).  m_lo = 0x000F000F,
+// m_hi = 0x00F000F0 and magic = 0x64006400 in registers (vreg_const).
+__device__ __forceinline__ u32x4 decode_f16_split(uint32_t w, f16x2 bias_lo, f16x2 bias_hi,
+                                                  uint32_t m_lo, uint32_t m_hi, uint32_t magic) {
+    const uint32_t w8 = w >> 8;
+    u32x4 r;
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, (w & m_lo) | magic) - bias_lo);
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, (w & m_hi) | magic) - bias_hi);
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, (w8 & m_lo) | magic) - bias_lo);
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, (w8 & m_hi) | magic) - bias_hi);
     return r;
 }
 
