@@ -18,9 +18,10 @@
  * as u = q + 8 (an implicit zero point of 8) ([QA1] §Signed ↔ Unsigned gives the ranges).
  *
  * Conventions shared by every entry point:
- *   - Tensor pointers are device memory owned by the caller.  The library allocates
- *     nothing, frees nothing and does not synchronize: work is enqueued on `stream`
- *     (NULL = the default stream) and the call returns.
+ *   - Tensor pointers are device memory owned by the caller.  No call allocates or frees
+ *     anything, and none synchronizes: work is enqueued on `stream` (NULL = the default
+ *     stream) and the call returns.  The only memory the library holds itself is the
+ *     fixed scratch of q4_kv_attention_noalloc (below).
  *   - Arguments are validated on the host before anything is enqueued; an invalid call
  *     returns a non-zero q4_status and touches no memory.  A launch failure reported by
  *     the runtime returns Q4_ERR_LAUNCH.  Faults during execution surface at the
@@ -48,7 +49,8 @@ typedef enum {
     Q4_ERR_GROUP = 3,   /* group_size not in {32, 64, 128} */
     Q4_ERR_DTYPE = 4,   /* dtype not accepted by this entry point */
     Q4_ERR_ALIGN = 5,   /* a pointer misses its required alignment */
-    Q4_ERR_LAUNCH = 6   /* the HIP runtime rejected the kernel launch */
+    Q4_ERR_LAUNCH = 6,  /* the HIP runtime rejected the kernel launch */
+    Q4_ERR_SCRATCH = 7  /* the sizes need more scratch than q4_kv_attention_noalloc holds */
 } q4_status;
 
 typedef enum { Q4_F32 = 0, Q4_F16 = 1, Q4_BF16 = 2 } q4_dtype;
@@ -235,6 +237,26 @@ q4_status q4_kv_attention(const void* q, q4_dtype q_dtype, int64_t heads, int64_
                           const uint32_t* vz, int32_t group_size, int32_t symmetric, float scale,
                           float* out, void* workspace, int64_t workspace_bytes,
                           hipStream_t stream);
+
+/* q4_kv_attention for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments, results
+ * and rules as q4_kv_attention without workspace and workspace_bytes (the same kernels,
+ * chunking and summation order, so the output is bit-identical).  The per-chunk partials
+ * go to a fixed scratch array of q4_kv_attention_noalloc_max_bytes() bytes (16 MiB) that
+ * the library holds in device memory, one per GPU, from its first call on that GPU until
+ * the process ends; the call itself allocates and frees nothing.  The partials need
+ * heads * chunks * (head_dim + 2) * 4 bytes with chunks <= ceil(n_tok * head_dim / 8192)
+ * (e.g. 1.06 MB for 32 heads of 128 over 4096 tokens); sizes that need more return
+ * Q4_ERR_SCRATCH before anything is enqueued.  Every call on a GPU shares that GPU's
+ * scratch: calls that may overlap on one GPU (other streams, other threads) race and must
+ * be serialized by the caller.  The scratch needs no clearing: each call writes every
+ * partial it reads. */
+q4_status q4_kv_attention_noalloc(const void* q, q4_dtype q_dtype, int64_t heads, int64_t head_dim,
+                                  int64_t n_tok, int64_t t_cap, const uint32_t* kq,
+                                  const uint16_t* ks, const uint32_t* kz, const uint32_t* vq,
+                                  const uint16_t* vs, const uint32_t* vz, int32_t group_size,
+                                  int32_t symmetric, float scale, float* out, hipStream_t stream);
+int64_t q4_kv_attention_noalloc_max_bytes(void);
 
 /* ---- GPTQ ([QA1] GPTQ chapter: §Hessian 정의, §OBQ single-step 수식, §GPTQ block-wise,
  * §알고리즘 개요, §설정 grid; [FL7] §GPTQ: Approximate Second-order Weight Quantization).

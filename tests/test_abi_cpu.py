@@ -38,7 +38,7 @@ def test_layout_version_and_initial_state():
 
 def test_status_strings():
     lib = q4.lib()
-    for code in range(7):
+    for code in range(8):
         s = lib.q4_status_str(code).decode()
         assert s and s != "unknown status"
     assert lib.q4_status_str(99).decode() == "unknown status"
@@ -273,6 +273,36 @@ def _kva(q=A16, qd=BF16, heads=4, d=128, n_tok=100, t_cap=128, kq=A16, ks=A16, k
 def test_kv_attention_validation_rejects_before_launch(call, code):
     assert call() == code
     assert q4.q4_last_kernel() == ""
+
+
+def _kvn(q=A16, qd=BF16, heads=4, d=128, n_tok=100, t_cap=128, kq=A16, ks=A16, kz=A16, vq=A16,
+         vs=A16, vz=A16, g=32, sym=0, scale=0.088, out=A16):
+    return q4.lib().q4_kv_attention_noalloc(q, qd, heads, d, n_tok, t_cap, kq, ks, kz, vq, vs, vz, g,
+                                            sym, scale, out, None)
+
+
+SCRATCH = 7
+
+
+@pytest.mark.parametrize("call,code", [
+    (lambda: _kvn(g=16), GROUP), (lambda: _kvn(d=96), SHAPE), (lambda: _kvn(n_tok=129), SHAPE),
+    (lambda: _kvn(heads=0), SHAPE), (lambda: _kvn(qd=F32), DTYPE), (lambda: _kvn(q=None), NULL),
+    (lambda: _kvn(out=None), NULL), (lambda: _kvn(kz=None), NULL), (lambda: _kvn(q=A16 + 8), ALIGN),
+    (lambda: _kvn(out=A16 + 2), ALIGN), (lambda: _kvn(vz=A16 + 2), ALIGN),
+    # partials of 2048 heads x 32 chunks x 258 floats: beyond the 16 MiB scratch
+    (lambda: _kvn(heads=2048, d=256, g=64, n_tok=8192, t_cap=8192), SCRATCH),
+    (lambda: _kvn(heads=65536, d=64, g=64, n_tok=1, t_cap=1), SCRATCH),
+])
+def test_kv_attention_noalloc_validation_rejects_before_launch(call, code):
+    assert call() == code
+    assert q4.q4_last_kernel() == ""
+
+
+def test_kv_attention_noalloc_scratch_size():
+    lib = q4.lib()
+    assert lib.q4_kv_attention_noalloc_max_bytes() == 16 << 20
+    # the 7B decode step (32 heads of 128 over 4096 tokens) needs 32 x 64 x 130 x 4 bytes
+    assert lib.q4_kv_attention_workspace(32, 128, 4096) <= lib.q4_kv_attention_noalloc_max_bytes()
 
 
 def test_kv_attention_symmetric_accepts_null_zeros():

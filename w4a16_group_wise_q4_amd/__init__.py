@@ -31,6 +31,7 @@ __all__ = ["PackedWeight", "q4_quantize_pack", "q4_quantize_pack_grouped", "q4_q
            "q4_w4a16_gemm",
            "q4_w4a16_gemm_grouped", "q4_last_kernel", "KvCache", "empty_kv_cache",
            "q4_kv_quantize", "q4_kv_attention", "q4_kv_attention_workspace",
+           "q4_kv_attention_noalloc",
            "q4_gptq_quantize", "q4_gptq_workspace",
            "q4_qweight_words", "q4_scale_count", "q4_zero_words", "q4_layout_version",
            "library_path", "Q4Error"]
@@ -41,7 +42,8 @@ _DTYPE_CODE = {torch.float32: Q4_F32, torch.float16: Q4_F16, torch.bfloat16: Q4_
 EXPORTED = ("q4_quantize_pack", "q4_quantize_pack_grouped", "q4_quantize_pack_mse", "q4_dequant",
             "q4_w4a16_gemm", "q4_w4a16_gemm_out",
             "q4_w4a16_gemm_grouped", "q4_w4a16_gemm_grouped_out", "q4_kv_quantize", "q4_kv_attention",
-            "q4_kv_attention_workspace", "q4_gptq_quantize", "q4_gptq_workspace",
+            "q4_kv_attention_workspace", "q4_kv_attention_noalloc",
+            "q4_kv_attention_noalloc_max_bytes", "q4_gptq_quantize", "q4_gptq_workspace",
             "q4_qweight_words",
             "q4_scale_count", "q4_zero_words", "q4_status_str", "q4_last_kernel",
             "q4_layout_version")
@@ -113,6 +115,11 @@ def _load():
     lib.q4_kv_attention.argtypes = [vp, ctypes.c_int, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp,
                                     i32, i32, ctypes.c_float, vp, vp, i64, vp]
     lib.q4_kv_attention.restype = ctypes.c_int
+    lib.q4_kv_attention_noalloc.argtypes = [vp, ctypes.c_int, i64, i64, i64, i64, vp, vp, vp, vp, vp,
+                                            vp, i32, i32, ctypes.c_float, vp, vp]
+    lib.q4_kv_attention_noalloc.restype = ctypes.c_int
+    lib.q4_kv_attention_noalloc_max_bytes.argtypes = []
+    lib.q4_kv_attention_noalloc_max_bytes.restype = i64
     lib.q4_gptq_workspace.argtypes = [i64, i64, i32]
     lib.q4_gptq_workspace.restype = i64
     lib.q4_gptq_quantize.argtypes = [vp, ctypes.c_int, i64, i64, vp, ctypes.c_int, i64, i32, i32,
@@ -408,6 +415,33 @@ def q4_kv_attention(q: torch.Tensor, kcache: KvCache, vcache: KvCache, n_tok: in
         _dev_ptr(vcache.qcache), _dev_ptr(vcache.scache), _dev_ptr(vcache.zcache),
         kcache.group_size, int(kcache.symmetric), float(scale), _dev_ptr(out),
         _dev_ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q)))
+    return out
+
+
+def q4_kv_attention_noalloc(q: torch.Tensor, kcache: KvCache, vcache: KvCache, n_tok: int,
+                            scale: float, out: torch.Tensor) -> torch.Tensor:
+    """q4_kv_attention without a workspace, for callers that cannot allocate (HIP graph
+    capture, serving loops): the partials go to the library's fixed per-GPU scratch, so
+    ``out`` [heads, head_dim] fp32 must be passed in.  Calls on one GPU share that scratch
+    and must not overlap."""
+    _need_cuda("q", q)
+    _need_cuda("out", out)
+    if q.dim() != 2 or q.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("q must be a 2-D fp16 or bf16 tensor [heads, head_dim]")
+    heads, d = q.shape
+    for c in (kcache, vcache):
+        if (c.heads, c.head_dim) != (heads, d):
+            raise ValueError("q does not match the caches' heads / head_dim")
+    if (kcache.group_size, kcache.symmetric, kcache.t_cap) != \
+            (vcache.group_size, vcache.symmetric, vcache.t_cap):
+        raise ValueError("K and V caches must share group_size, symmetry and t_cap")
+    if out.dtype != torch.float32 or tuple(out.shape) != (heads, d) or out.device != q.device:
+        raise ValueError("out must be an fp32 [heads, head_dim] tensor on q's device")
+    _check(_load().q4_kv_attention_noalloc(
+        _dev_ptr(q), _DTYPE_CODE[q.dtype], heads, d, n_tok, kcache.t_cap,
+        _dev_ptr(kcache.qcache), _dev_ptr(kcache.scache), _dev_ptr(kcache.zcache),
+        _dev_ptr(vcache.qcache), _dev_ptr(vcache.scache), _dev_ptr(vcache.zcache),
+        kcache.group_size, int(kcache.symmetric), float(scale), _dev_ptr(out), _stream(q)))
     return out
 
 

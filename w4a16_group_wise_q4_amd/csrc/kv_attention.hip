@@ -31,6 +31,8 @@
 // the workgroup, the chunks, the rest).
 #include "q4_launch.h"
 
+#include <mutex>
+
 namespace {
 
 constexpr int kThreads = 256;
@@ -395,6 +397,39 @@ hipError_t launch_g(const KvArgs& a, int xd, int g, int sym, int nl, int heads, 
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------------------
+// Scratch for callers that cannot allocate (q4_kv_attention_noalloc): the per-chunk
+// partials go to this fixed array instead of a caller workspace.  Every GPU the library
+// runs on holds its own copy until the process ends.  Host code never uses the array's
+// name as an address (on the host it is a stand-in, not device memory): the device
+// address comes from hipGetSymbolAddress, once per device, with that device current.
+// The array has external linkage: the runtime finds a device variable by its symbol in
+// the code object, and an internal-linkage (static) one is emitted as a local symbol it
+// cannot look up.
+__device__ __align__(256) unsigned char q4_kv_noalloc_scratch[kKvScratchBytes];
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t q4k_kv_scratch(void** ptr) {
+    *ptr = nullptr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(q4_kv_noalloc_scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 void q4k_kv_attention_shape(int64_t heads, int64_t d, int64_t n_tok, int* chunks, int* loads) {
     // the most loads per wave (longest chunks) that still give at least 512 workgroups

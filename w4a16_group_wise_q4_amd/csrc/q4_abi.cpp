@@ -337,6 +337,34 @@ q4_status q4_kv_attention(const void* q, q4_dtype q_dtype, int64_t heads, int64_
     return finish(e, name);
 }
 
+q4_status q4_kv_attention_noalloc(const void* q, q4_dtype q_dtype, int64_t heads, int64_t head_dim,
+                                  int64_t n_tok, int64_t t_cap, const uint32_t* kq,
+                                  const uint16_t* ks, const uint32_t* kz, const uint32_t* vq,
+                                  const uint16_t* vs, const uint32_t* vz, int32_t group_size,
+                                  int32_t symmetric, float scale, float* out, hipStream_t stream) {
+    q4_status st = check_kv_sizes(heads, head_dim, group_size, t_cap);
+    if (st != Q4_OK) return st;
+    if (!kv_attention_dims_ok(heads, head_dim, n_tok) || n_tok > t_cap) return Q4_ERR_SHAPE;
+    if (q_dtype != Q4_F16 && q_dtype != Q4_BF16) return Q4_ERR_DTYPE;
+    if (!q || !out) return Q4_ERR_NULL;
+    if ((st = check_packed(kq, ks, kz, symmetric)) != Q4_OK) return st;
+    if ((st = check_packed(vq, vs, vz, symmetric)) != Q4_OK) return st;
+    if (!aligned(q, 16) || !aligned(out, 4)) return Q4_ERR_ALIGN;
+    int chunks = 0, loads = 0;
+    q4k_kv_attention_shape(heads, head_dim, n_tok, &chunks, &loads);
+    if (heads * chunks * (head_dim + 2) * (int64_t)sizeof(float) > kKvScratchBytes) return Q4_ERR_SCRATCH;
+    void* ws = nullptr;
+    if (q4k_kv_scratch(&ws) != hipSuccess || ws == nullptr) return Q4_ERR_LAUNCH;
+    const char* name = "";
+    const hipError_t e = q4k_kv_attention(
+        q, (int)q_dtype, kq, ks, symmetric ? nullptr : kz, vq, vs, symmetric ? nullptr : vz, heads,
+        head_dim, n_tok, t_cap, group_size, symmetric ? 1 : 0, scale, out, static_cast<float*>(ws),
+        chunks, loads, stream, &name);
+    return finish(e, name);
+}
+
+int64_t q4_kv_attention_noalloc_max_bytes(void) { return kKvScratchBytes; }
+
 namespace {
 constexpr int64_t kMaxGptqK = 32768;   // the k x k Hessian: at most 4 GiB of fp32
 }  // namespace
@@ -389,6 +417,7 @@ const char* q4_status_str(q4_status s) {
     case Q4_ERR_DTYPE: return "dtype not accepted by this entry point";
     case Q4_ERR_ALIGN: return "pointer misaligned (w/x/qweight/w_out 16 B, zeros/y 4 B, scales 2 B)";
     case Q4_ERR_LAUNCH: return "kernel launch failed";
+    case Q4_ERR_SCRATCH: return "sizes need more than the fixed scratch of the no-allocation entry point";
     }
     return "unknown status";
 }

@@ -48,6 +48,11 @@ hipError_t q4k_kv_attention(const void* q, int q_dtype, const uint32_t* kq, cons
                             int64_t t_cap, int g, int sym, float scale, float* out,
                             float* workspace, int chunks, int loads, hipStream_t stream,
                             const char** kname);
+// The fixed per-device scratch of the no-allocation attention entry point: its size in
+// bytes, and its device address on the current device (looked up once per device; a
+// failed lookup returns the runtime's error and leaves *ptr NULL).
+constexpr int64_t kKvScratchBytes = int64_t(16) << 20;
+hipError_t q4k_kv_scratch(void** ptr);
 hipError_t q4k_quant_mse(const void* w, int w_dtype, int64_t n, int64_t k, int g, int sym,
                          uint32_t* qweight, uint16_t* scales, uint32_t* zeros,
                          hipStream_t stream, const char** kname);
