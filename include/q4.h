@@ -296,8 +296,22 @@ const char* q4_status_str(q4_status s);
  * ("" before any), so callers can verify which kernel ran ([FL7] §Silent Fallback). */
 const char* q4_last_kernel(void);
 
+/* Every kernel the calling thread's last successful entry-point call enqueued: their
+ * distinct names in launch order, comma-separated (a multi-launch call, such as a chunked
+ * mid-m product, attention's partial and combine kernels or GPTQ, lists each), and the
+ * number of launches.  "" and 0 before any call.  [FL7] §Silent Fallback asks to check the
+ * selected kernel and that nothing fell back. */
+const char* q4_last_kernels(void);
+int64_t q4_last_launch_count(void);
+
 /* Version of the packed layout described above (1). */
 int32_t q4_layout_version(void);
+
+/* Digest of the sources this library was built from (the first 16 hex digits of a SHA-256
+ * over the kernel sources and this header, as the build computes it), so a loader can
+ * refuse a library built from other sources ([FL7] lists the quantizer code version among
+ * what a deployment must be able to reproduce). */
+const char* q4_source_digest(void);
 
 #ifdef __cplusplus
 }

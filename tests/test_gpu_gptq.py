@@ -52,6 +52,11 @@ def run_gpu(w, x, g, sym):
     p = q4.q4_gptq_quantize(w.to(DEV), x.to(DEV), g, sym, workspace=ws)
     torch.cuda.synchronize()
     assert q4.q4_last_kernel().startswith("q4_gptq_")
+    names = q4.q4_last_kernels()
+    assert names[0].startswith("q4_quant_pack_") and "q4_gptq_hessian" in names
+    assert {"q4_gptq_chol_diag", "q4_gptq_fill_zero", "q4_gptq_sweep"} <= set(names)
+    blocks = -(-k // 64)  # the quantizer, the Hessian, a diagonal factor per 64 columns, ...
+    assert q4.q4_last_launch_count() >= 3 + blocks + 1 + blocks
     A = ws[:k * k].view(k, k).cpu().double().numpy()
     qw = p.qweight.cpu().numpy().view(np.uint32)
     sc = p.scales.cpu().view(torch.int16).numpy().view(np.uint16)

@@ -729,6 +729,35 @@ def test_midm_chunked_cases(m, n, k, g, xdtype, sym):
     assert_linear_close(y, host_input(x), packed, n, k, g, sym, cols=cols, what=kname)
 
 
+def test_launch_record_names_every_kernel():
+    """q4_last_kernels / q4_last_launch_count report every launch of the last call: one
+    for a decode product, the grouped chunk launch plus the remainder for a chunked mid-m
+    product, partial and combine for attention."""
+    n, k, g = 1000, 4096, 64
+    w = torch.from_numpy(pins.random_weights(77, n, k))
+    p, _ = pack_guarded(w.to(DEV), g, False)
+    assert q4.q4_last_kernels() == ["q4_quant_pack_f32"] and q4.q4_last_launch_count() == 1
+    x1 = synthetic.activations(1, k, seed=3).to(DEV)
+    q4.q4_w4a16_gemm(x1, p)
+    assert q4.q4_last_kernels() == ["q4_gemv_tile_bf16"] and q4.q4_last_launch_count() == 1
+    x40 = synthetic.activations(40, k, seed=4).to(DEV)
+    note("launch record: chunked m = 40")
+    q4.q4_w4a16_gemm(x40, p)
+    assert q4.q4_last_kernels() == ["q4_gemv_wide_bf16"], q4.q4_last_kernels()
+    assert q4.q4_last_launch_count() == 2          # two 16-row chunks grouped, then 8 rows
+    heads, d = 4, 128
+    kc = q4.empty_kv_cache(heads, 64, d, 32, False, DEV)
+    vc = q4.empty_kv_cache(heads, 64, d, 32, False, DEV)
+    kv = synthetic.kv_tokens(64, heads, d, 5, "k").to(DEV)
+    q4.q4_kv_quantize(kv, kc, 0)
+    q4.q4_kv_quantize(kv, vc, 0)
+    q4.q4_kv_attention(synthetic.query(heads, d, 6).to(DEV), kc, vc, 64, 0.1)
+    assert q4.q4_last_kernel() == "q4_kv_attention_bf16"
+    assert q4.q4_last_kernels() == ["q4_kv_partial_bf16", "q4_kv_combine"]
+    assert q4.q4_last_launch_count() == 2
+    torch.cuda.synchronize()
+
+
 def test_gemm_prefill_70b_sampled():
     """The 70B-like prefill at full size, in the configuration the benchmark times;
     checked on a seeded sample of 40 activation rows x 320 weight rows (with edges)."""

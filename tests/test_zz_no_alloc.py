@@ -92,6 +92,8 @@ def test_noalloc_binding_and_limit():
     kb = q4.KvCache(kc.qcache, kc.scache, kc.zcache, big[0], big[2], big[1], 64, False)
     code = noalloc_raw(qb, kb, kb, big[2], 0.0625, out)
     assert code == Q4_ERR_SCRATCH, code
-    with pytest.raises(q4.Q4Error):
+    # through the binding the same call stops earlier: the cache tensors are far shorter
+    # than 2048 heads x 8192 tokens
+    with pytest.raises(ValueError):
         q4.q4_kv_attention_noalloc(qb, kb, kb, big[2], 0.0625,
                                    torch.empty((2048, 256), dtype=torch.float32, device=DEV))

@@ -29,7 +29,8 @@ from . import _build
 __all__ = ["PackedWeight", "q4_quantize_pack", "q4_quantize_pack_grouped", "q4_quantize_pack_mse",
            "q4_dequant",
            "q4_w4a16_gemm",
-           "q4_w4a16_gemm_grouped", "q4_last_kernel", "KvCache", "empty_kv_cache",
+           "q4_w4a16_gemm_grouped", "q4_last_kernel", "q4_last_kernels", "q4_last_launch_count",
+           "q4_source_digest", "StaleLibraryError", "KvCache", "empty_kv_cache",
            "q4_kv_quantize", "q4_kv_attention", "q4_kv_attention_workspace",
            "q4_kv_attention_noalloc",
            "q4_gptq_quantize", "q4_gptq_workspace",
@@ -46,7 +47,7 @@ EXPORTED = ("q4_quantize_pack", "q4_quantize_pack_grouped", "q4_quantize_pack_ms
             "q4_kv_attention_noalloc_max_bytes", "q4_gptq_quantize", "q4_gptq_workspace",
             "q4_qweight_words",
             "q4_scale_count", "q4_zero_words", "q4_status_str", "q4_last_kernel",
-            "q4_layout_version")
+            "q4_last_kernels", "q4_last_launch_count", "q4_layout_version", "q4_source_digest")
 
 
 class GemmProblem(ctypes.Structure):
@@ -79,6 +80,10 @@ def library_path() -> str:
     return _build.LIBRARY
 
 
+class StaleLibraryError(RuntimeError):
+    """libq4.so was built from sources other than the ones next to it."""
+
+
 def _load():
     global _lib
     if _lib is not None:
@@ -86,6 +91,13 @@ def _load():
     if not os.path.exists(_build.LIBRARY):
         _build.build()  # raises if hipcc fails: there is no fallback
     lib = ctypes.CDLL(_build.LIBRARY)
+    lib.q4_source_digest.argtypes = []
+    lib.q4_source_digest.restype = ctypes.c_char_p
+    built, here = lib.q4_source_digest().decode(), _build.source_digest()
+    if built != here:
+        raise StaleLibraryError(
+            f"{_build.LIBRARY} was built from sources with digest {built}, but the sources "
+            f"here digest to {here}: rebuild it (__graft_entry__.build())")
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     lib.q4_quantize_pack.argtypes = [vp, ctypes.c_int, i64, i64, i32, i32, vp, vp, vp, vp]
     lib.q4_quantize_pack.restype = ctypes.c_int
@@ -135,6 +147,10 @@ def _load():
     lib.q4_status_str.restype = ctypes.c_char_p
     lib.q4_last_kernel.argtypes = []
     lib.q4_last_kernel.restype = ctypes.c_char_p
+    lib.q4_last_kernels.argtypes = []
+    lib.q4_last_kernels.restype = ctypes.c_char_p
+    lib.q4_last_launch_count.argtypes = []
+    lib.q4_last_launch_count.restype = i64
     lib.q4_layout_version.argtypes = []
     lib.q4_layout_version.restype = i32
     _lib = lib
@@ -159,11 +175,77 @@ def _dev_ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _need_cuda(name: str, t: torch.Tensor):
+def _need_cuda(name: str, t: torch.Tensor, device=None):
+    """t is a contiguous tensor on the current GPU (and on ``device`` when given)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor (the library has no CPU path)")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the call's other tensors on {device}")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}, not the current device "
+                         f"cuda:{torch.cuda.current_device()} the kernels launch on")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _need(name: str, t: torch.Tensor, shape, dtypes, device):
+    """A device tensor of exactly this shape and one of these dtypes: a shorter buffer would
+    let a kernel write (or read) past its end."""
+    _need_cuda(name, t, device)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {sorted(map(str, dtypes))}")
+
+
+def _layout_ok(n: int, k: int, g: int) -> bool:
+    """Sizes for which the packed shapes are defined (others are refused by the C ABI)."""
+    return g in (32, 64, 128) and n >= 1 and k >= 1 and k % g == 0
+
+
+def _check_packed(p: "PackedWeight", device, n=None, k=None, group_size=None, symmetric=None):
+    """The packed weight's tensors against its own n, k, group size and mode (and against
+    the call's, when given): qweight int32 [n, k/8], scales fp16 [n, k/g], zeros int32
+    [n, ceil(k/g/8)] unless symmetric."""
+    if not isinstance(p, PackedWeight):
+        raise TypeError("expected a PackedWeight")
+    for nm, want, have in (("n", n, p.n), ("k", k, p.k), ("group_size", group_size, p.group_size),
+                           ("symmetric", symmetric, p.symmetric)):
+        if want is not None and want != have:
+            raise ValueError(f"packed weight has {nm}={have}, the call needs {want}")
+    if not _layout_ok(p.n, p.k, p.group_size):
+        return  # the C ABI refuses these sizes before touching any memory
+    G = p.k // p.group_size
+    _need("qweight", p.qweight, (p.n, p.k // 8), (torch.int32,), device)
+    _need("scales", p.scales, (p.n, G), (torch.float16,), device)
+    if p.symmetric:
+        if p.zeros is not None:
+            _need("zeros", p.zeros, (p.n, (G + 7) // 8), (torch.int32,), device)
+    else:
+        if p.zeros is None:
+            raise ValueError("an asymmetric packed weight needs zeros")
+        _need("zeros", p.zeros, (p.n, (G + 7) // 8), (torch.int32,), device)
+
+
+def _check_cache(name: str, c: "KvCache", device):
+    """A KV cache's tensors against its heads, t_cap, head_dim, group size and mode."""
+    if not isinstance(c, KvCache):
+        raise TypeError(f"{name} must be a KvCache")
+    if c.heads < 1 or c.t_cap < 1 or not _layout_ok(c.heads * c.t_cap, c.head_dim, c.group_size):
+        return  # refused by the C ABI
+    rows, G = c.heads * c.t_cap, c.head_dim // c.group_size
+    _need(f"{name}.qcache", c.qcache, (rows, c.head_dim // 8), (torch.int32,), device)
+    _need(f"{name}.scache", c.scache, (rows, G), (torch.float16,), device)
+    if not c.symmetric:
+        if c.zcache is None:
+            raise ValueError(f"{name}: an asymmetric cache needs zcache")
+        _need(f"{name}.zcache", c.zcache, (rows, (G + 7) // 8), (torch.int32,), device)
+
+
+def _need_workspace(name: str, t: torch.Tensor, device):
+    _need_cuda(name, t, device)
 
 
 @dataclass
@@ -199,6 +281,22 @@ def q4_last_kernel() -> str:
     return _load().q4_last_kernel().decode()
 
 
+def q4_last_kernels() -> list:
+    """Every kernel the last successful call on this thread enqueued (distinct names, in
+    launch order)."""
+    s = _load().q4_last_kernels().decode()
+    return s.split(",") if s else []
+
+
+def q4_last_launch_count() -> int:
+    """How many kernel launches the last successful call on this thread enqueued."""
+    return int(_load().q4_last_launch_count())
+
+
+def q4_source_digest() -> str:
+    return _load().q4_source_digest().decode()
+
+
 def empty_packed(n: int, k: int, group_size: int, symmetric: bool, device) -> PackedWeight:
     G = k // group_size
     return PackedWeight(
@@ -216,6 +314,7 @@ def q4_quantize_pack(w: torch.Tensor, group_size: int = 128, symmetric: bool = F
         raise ValueError("w must be a 2-D fp32, fp16 or bf16 tensor")
     n, k = w.shape
     p = out if out is not None else empty_packed(n, k, group_size, symmetric, w.device)
+    _check_packed(p, w.device, n, k, group_size, bool(symmetric))
     _check(_load().q4_quantize_pack(_dev_ptr(w), _DTYPE_CODE[w.dtype], n, k, group_size,
                                     int(bool(symmetric)), _dev_ptr(p.qweight),
                                     _dev_ptr(p.scales), _dev_ptr(p.zeros), _stream(w)))
@@ -231,6 +330,7 @@ def q4_quantize_pack_mse(w: torch.Tensor, group_size: int = 128, symmetric: bool
         raise ValueError("w must be a 2-D fp32, fp16 or bf16 tensor")
     n, k = w.shape
     p = out if out is not None else empty_packed(n, k, group_size, symmetric, w.device)
+    _check_packed(p, w.device, n, k, group_size, bool(symmetric))
     _check(_load().q4_quantize_pack_mse(_dev_ptr(w), _DTYPE_CODE[w.dtype], n, k, group_size,
                                         int(bool(symmetric)), _dev_ptr(p.qweight),
                                         _dev_ptr(p.scales), _dev_ptr(p.zeros), _stream(w)))
@@ -245,13 +345,15 @@ def q4_quantize_pack_grouped(ws, group_size: int = 128, symmetric: bool = False,
     if not 1 <= count <= MAX_GROUP:
         raise ValueError(f"1 to {MAX_GROUP} matrices per call")
     for w in ws:
-        _need_cuda("w", w)
+        _need_cuda("w", w, ws[0].device)
         if w.dim() != 2 or w.dtype not in _DTYPE_CODE or w.dtype != ws[0].dtype:
             raise ValueError("matrices must be 2-D fp32, fp16 or bf16 tensors of one dtype")
     ps = list(outs) if outs is not None else [
         empty_packed(w.shape[0], w.shape[1], group_size, symmetric, w.device) for w in ws]
     if len(ps) != count:
         raise ValueError("one output per matrix")
+    for w, pk in zip(ws, ps):
+        _check_packed(pk, ws[0].device, w.shape[0], w.shape[1], group_size, bool(symmetric))
     arr = (QuantProblem * count)()
     for i, (w, p) in enumerate(zip(ws, ps)):
         arr[i] = QuantProblem(w.data_ptr(), w.shape[0], w.shape[1], p.qweight.data_ptr(),
@@ -265,8 +367,10 @@ def q4_dequant(p: PackedWeight, out_dtype: torch.dtype = torch.float32,
                out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Full dequantization S * (u - z) -> [n, k] in out_dtype (fp32 exact)."""
     _need_cuda("qweight", p.qweight)
+    _check_packed(p, p.qweight.device)
     o = out if out is not None else torch.empty((p.n, p.k), dtype=out_dtype,
                                                 device=p.qweight.device)
+    _need("out", o, (p.n, p.k), tuple(_DTYPE_CODE), p.qweight.device)
     _check(_load().q4_dequant(_dev_ptr(p.qweight), _dev_ptr(p.scales), _dev_ptr(p.zeros),
                               p.n, p.k, p.group_size, int(p.symmetric), _dev_ptr(o),
                               _DTYPE_CODE[o.dtype], _stream(o)))
@@ -286,7 +390,9 @@ def q4_w4a16_gemm(x: torch.Tensor, p: PackedWeight,
     if out_dtype not in _DTYPE_CODE:
         raise ValueError("the output is fp32, fp16 or bf16")
     m = x.shape[0]
+    _check_packed(p, x.device)
     y = out if out is not None else torch.empty((m, p.n), dtype=out_dtype, device=x.device)
+    _need("out", y, (m, p.n), tuple(_DTYPE_CODE), x.device)
     if out_dtype == torch.float32:
         _check(_load().q4_w4a16_gemm(_dev_ptr(x), _DTYPE_CODE[x.dtype], m, _dev_ptr(p.qweight),
                                      _dev_ptr(p.scales), _dev_ptr(p.zeros), p.n, p.k,
@@ -313,7 +419,8 @@ def q4_w4a16_gemm_grouped(xs, packs, outs=None, out_dtype=torch.float32):
         raise ValueError("one activation tensor per problem (or one shared)")
     p0, x0 = packs[0], xs[0]
     for x, p in zip(xs, packs):
-        _need_cuda("x", x)
+        _need_cuda("x", x, xs[0].device)
+        _check_packed(p, xs[0].device)
         if (x.shape != x0.shape or x.dtype != x0.dtype or x.dim() != 2 or p.k != p0.k
                 or p.group_size != p0.group_size or p.symmetric != p0.symmetric or x.shape[1] != p.k):
             raise ValueError("problems must share m, k, group size, symmetry and dtype")
@@ -329,6 +436,10 @@ def q4_w4a16_gemm_grouped(xs, packs, outs=None, out_dtype=torch.float32):
         raise ValueError("the output is fp32, fp16 or bf16")
     ys = outs if outs is not None else [
         torch.empty((m, p.n), dtype=out_dtype, device=x0.device) for p in packs]
+    if len(ys) != count:
+        raise ValueError("one output per problem")
+    for y, p in zip(ys, packs):
+        _need("out", y, (m, p.n), (out_dtype,), x0.device)
     arr = (GemmProblem * count)()
     for i, (x, p, y) in enumerate(zip(xs, packs, ys)):
         arr[i] = GemmProblem(x.data_ptr(), p.qweight.data_ptr(), p.scales.data_ptr(),
@@ -377,6 +488,7 @@ def q4_kv_quantize(kv: torch.Tensor, cache: KvCache, t0: int) -> KvCache:
     t_new, heads, d = kv.shape
     if heads != cache.heads or d != cache.head_dim:
         raise ValueError("kv does not match the cache's heads / head_dim")
+    _check_cache("cache", cache, kv.device)
     _check(_load().q4_kv_quantize(_dev_ptr(kv), _DTYPE_CODE[kv.dtype], t_new, heads, d,
                                   cache.group_size, int(cache.symmetric), cache.t_cap, t0,
                                   _dev_ptr(cache.qcache), _dev_ptr(cache.scache),
@@ -404,11 +516,15 @@ def q4_kv_attention(q: torch.Tensor, kcache: KvCache, vcache: KvCache, n_tok: in
     if (kcache.group_size, kcache.symmetric, kcache.t_cap) != \
             (vcache.group_size, vcache.symmetric, vcache.t_cap):
         raise ValueError("K and V caches must share group_size, symmetry and t_cap")
+    _check_cache("kcache", kcache, q.device)
+    _check_cache("vcache", vcache, q.device)
     if out is None:
         out = torch.empty((heads, d), dtype=torch.float32, device=q.device)
+    _need("out", out, (heads, d), (torch.float32,), q.device)
     need = q4_kv_attention_workspace(heads, d, n_tok)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _need_workspace("workspace", workspace, q.device)
     _check(_load().q4_kv_attention(
         _dev_ptr(q), _DTYPE_CODE[q.dtype], heads, d, n_tok, kcache.t_cap,
         _dev_ptr(kcache.qcache), _dev_ptr(kcache.scache), _dev_ptr(kcache.zcache),
@@ -425,9 +541,11 @@ def q4_kv_attention_noalloc(q: torch.Tensor, kcache: KvCache, vcache: KvCache, n
     ``out`` [heads, head_dim] fp32 must be passed in.  Calls on one GPU share that scratch
     and must not overlap."""
     _need_cuda("q", q)
-    _need_cuda("out", out)
     if q.dim() != 2 or q.dtype not in (torch.float16, torch.bfloat16):
         raise ValueError("q must be a 2-D fp16 or bf16 tensor [heads, head_dim]")
+    _need("out", out, tuple(q.shape), (torch.float32,), q.device)
+    _check_cache("kcache", kcache, q.device)
+    _check_cache("vcache", vcache, q.device)
     heads, d = q.shape
     for c in (kcache, vcache):
         if (c.heads, c.head_dim) != (heads, d):
@@ -435,8 +553,6 @@ def q4_kv_attention_noalloc(q: torch.Tensor, kcache: KvCache, vcache: KvCache, n
     if (kcache.group_size, kcache.symmetric, kcache.t_cap) != \
             (vcache.group_size, vcache.symmetric, vcache.t_cap):
         raise ValueError("K and V caches must share group_size, symmetry and t_cap")
-    if out.dtype != torch.float32 or tuple(out.shape) != (heads, d) or out.device != q.device:
-        raise ValueError("out must be an fp32 [heads, head_dim] tensor on q's device")
     _check(_load().q4_kv_attention_noalloc(
         _dev_ptr(q), _DTYPE_CODE[q.dtype], heads, d, n_tok, kcache.t_cap,
         _dev_ptr(kcache.qcache), _dev_ptr(kcache.scache), _dev_ptr(kcache.zcache),
@@ -458,16 +574,18 @@ def q4_gptq_quantize(w: torch.Tensor, x: torch.Tensor, group_size: int = 128,
     """GPTQ-quantize W [n, k] (fp32 / fp16 / bf16) against calibration activations
     x [tokens, k] (fp16 / bf16); same packed format, RTN's group scales and zero points."""
     _need_cuda("w", w)
-    _need_cuda("x", x)
+    _need_cuda("x", x, w.device)
     if w.dim() != 2 or w.dtype not in _DTYPE_CODE:
         raise ValueError("w must be a 2-D fp32, fp16 or bf16 tensor")
     if x.dim() != 2 or x.dtype not in (torch.float16, torch.bfloat16) or x.shape[1] != w.shape[1]:
         raise ValueError("x must be a 2-D fp16 or bf16 tensor [tokens, k]")
     n, k = w.shape
     p = out if out is not None else empty_packed(n, k, group_size, symmetric, w.device)
+    _check_packed(p, w.device, n, k, group_size, bool(symmetric))
     need = q4_gptq_workspace(n, k, group_size)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=w.device)
+    _need_workspace("workspace", workspace, w.device)
     _check(_load().q4_gptq_quantize(_dev_ptr(w), _DTYPE_CODE[w.dtype], n, k, _dev_ptr(x),
                                     _DTYPE_CODE[x.dtype], x.shape[0], group_size,
                                     int(bool(symmetric)), float(damp), _dev_ptr(p.qweight),

@@ -2,6 +2,7 @@
 from __future__ import annotations
 
 import glob
+import hashlib
 import os
 import subprocess
 
@@ -28,6 +29,29 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + [os.path.join(CSRC, "q4_abi.cpp")]
 
 
+def digested_files():
+    """Every file the library is built from: the kernel sources, their headers, the C ABI
+    and include/q4.h."""
+    files = []
+    for pat in ("*.hip", "*.h", "*.cpp"):
+        files += glob.glob(os.path.join(CSRC, pat))
+    files += glob.glob(os.path.join(INCLUDE, "*.h"))
+    return sorted(files, key=lambda f: os.path.relpath(f, ROOT))
+
+
+def source_digest() -> str:
+    """First 16 hex digits of a SHA-256 over (relative path, contents) of every source file;
+    compiled into the library and returned by q4_source_digest()."""
+    h = hashlib.sha256()
+    for f in digested_files():
+        h.update(os.path.relpath(f, ROOT).replace(os.sep, "/").encode())
+        h.update(b"\0")
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+        h.update(b"\0")
+    return h.hexdigest()[:16]
+
+
 def _run(cmd):
     res = subprocess.run(cmd, capture_output=True, text=True)
     return res.returncode, res.stdout + res.stderr
@@ -44,7 +68,8 @@ def build(verbose: bool = False) -> str:
     os.makedirs(objdir, exist_ok=True)
     srcs = sources()
     objs = [os.path.join(objdir, os.path.basename(src) + ".%d.o" % os.getpid()) for src in srcs]
-    cmds = [[HIPCC, *FLAGS, "-c", "-I", INCLUDE, "-I", CSRC, src, "-o", obj] for src, obj in zip(srcs, objs)]
+    digest = f'-DQ4_SOURCE_DIGEST="{source_digest()}"'
+    cmds = [[HIPCC, *FLAGS, digest, "-c", "-I", INCLUDE, "-I", CSRC, src, "-o", obj] for src, obj in zip(srcs, objs)]
     workers = max(1, min(len(cmds), os.cpu_count() or 1, 16))
     with ThreadPoolExecutor(max_workers=workers) as pool:
         results = list(pool.map(_run, cmds))

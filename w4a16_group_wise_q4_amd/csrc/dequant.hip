@@ -65,7 +65,7 @@ hipError_t launch(const uint32_t* qw, const uint16_t* sc, const uint32_t* zr, in
         hipLaunchKernelGGL((dequant_kernel<G, SYM, 1>), grid, block, 0, st, qw, sc, zr, k, words, out);
     else
         hipLaunchKernelGGL((dequant_kernel<G, SYM, 2>), grid, block, 0, st, qw, sc, zr, k, words, out);
-    return hipGetLastError();
+    return q4k_launched(*kname);
 }
 
 }  // namespace

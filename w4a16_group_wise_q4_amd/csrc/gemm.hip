@@ -392,7 +392,7 @@ hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16
         *kname = "q4_gemm_mfma_bf16";
         hipLaunchKernelGGL((gemm_kernel<G, SYM, false>), grid, block, lds, st, xp, m, qw, sc, zr, n, k, y, ydt);
     }
-    return hipGetLastError();
+    return q4k_launched(*kname);
 }
 
 }  // namespace

@@ -41,6 +41,9 @@
 #include "gemv_tile.h"
 #include "q4_launch.h"
 
+#include <map>
+#include <tuple>
+
 namespace {
 
 constexpr int kMaxWaves = 8;           // waves per workgroup (all on one 16-row tile)
@@ -499,20 +502,12 @@ __global__ __launch_bounds__(512) void gemv_chunk_kernel(const uint16_t* __restr
     }
 }
 
-int g_num_cus = 0;
-
 // One problem (batch == nullptr) or a batch of problems whose tiles add up to n rows.
 template <int G, bool SYM>
 hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16_t* sc,
                   const uint32_t* zr, int n, int k, void* y, int ydt, hipStream_t st, const char** kname,
                   const GemvBatch* batch = nullptr, int batch_tiles = 0) {
-    if (g_num_cus == 0) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&g_num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            g_num_cus <= 0)
-            g_num_cus = 256;
-    }
+    const int num_cus = q4k_device_cus();
     // Workgroup shape.  With tiles to spare (at least two per CU): 4-wave workgroups,
     // several resident per CU, two batches in flight per wave.  With at most one tile per
     // CU the whole matrix is requested at once and the time after the data arrives
@@ -529,9 +524,9 @@ hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16
             sc4 = ((uintptr_t)sc & 3) == 0;
         }
         int upw = 0, tw = 0, wide = 0;
-        const bool fits = sc4 && (q4t::tile_shape(G, m, k, tiles, g_num_cus, &upw, &tw) ||
+        const bool fits = sc4 && (q4t::tile_shape(G, m, k, tiles, num_cus, &upw, &tw) ||
                                   (wide = q4t::wide_shape(G, m, k, &upw, &tw)));
-        if (wide && q4t::wide_pair(tiles, g_num_cus)) wide = 2;
+        if (wide && q4t::wide_pair(tiles, num_cus)) wide = 2;
         if (fits) {
             GemvBatch one{};
             if (batch == nullptr) {
@@ -547,11 +542,11 @@ hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16
     }
     int shape;  // 0: up to 8 waves   1: up to 4 waves   2: up to 16 waves
     int waves;
-    if (tiles >= 2 * g_num_cus) {
+    if (tiles >= 2 * num_cus) {
         shape = 1;
         waves = (units_k + 3) / 4;
         waves = waves < 1 ? 1 : (waves > 4 ? 4 : waves);
-    } else if (tiles <= g_num_cus && units_k >= 16 && G >= 64) {
+    } else if (tiles <= num_cus && units_k >= 16 && G >= 64) {
         shape = 2;
         waves = (units_k + 1) / 2;
         waves = waves > 16 ? 16 : waves;
@@ -583,38 +578,39 @@ hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16
     const int threads = 64 * waves;
     const size_t lds_stream = stream_lds(waves);
     if (stream) {
-        // Workgroups resident per CU for a kernel at this shape (cached per kernel and
-        // thread).  When every tile gets its own workgroup the one-tile form runs (no
-        // metadata prefetch for a next tile); otherwise persistent workgroups take turns.
+        // Workgroups resident per CU for a kernel at this shape, cached per thread on
+        // (device, kernel, threads, LDS bytes).  When every tile gets its own workgroup the
+        // one-tile form runs (no metadata prefetch for a next tile); otherwise persistent
+        // workgroups take turns.
         auto per_cu = [&](auto kern) {
-            thread_local int cached_threads = -1, cached = 1;
-            thread_local size_t cached_lds = 0;
-            if (cached_threads != threads || cached_lds != lds_stream) {
-                int v = 0;
-                if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kern, threads, lds_stream) != hipSuccess || v < 1)
-                    v = 1;
-                cached_threads = threads;
-                cached_lds = lds_stream;
-                cached = v;
-            }
-            return cached;
+            thread_local std::map<std::tuple<int, const void*, int, size_t>, int> cache;
+            int dev = 0;
+            (void)hipGetDevice(&dev);
+            const auto key = std::make_tuple(dev, reinterpret_cast<const void*>(kern), threads, lds_stream);
+            const auto it = cache.find(key);
+            if (it != cache.end()) return it->second;
+            int v = 0;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kern, threads, lds_stream) != hipSuccess || v < 1)
+                v = 1;
+            cache.emplace(key, v);
+            return v;
         };
         auto run = [&](auto k_multi, auto k_one, const char* name) {
             *kname = name;
             if (batch != nullptr) {  // several problems: one workgroup per tile
                 hipLaunchKernelGGL(k_one, dim3(tiles), dim3(threads), lds_stream, st, *batch, m, k);
-                return hipGetLastError();
+                return q4k_launched(name);
             }
             GemvBatch one{};
             one.p[0] = q4::GemvProblem{x, qw, sc, zr, y, n, 0};
             one.count = 1;
             one.ydt = ydt;
-            const int cap = g_num_cus * per_cu(k_multi);
+            const int cap = num_cus * per_cu(k_multi);
             if (tiles <= cap)
                 hipLaunchKernelGGL(k_one, dim3(tiles), dim3(threads), lds_stream, st, one, m, k);
             else
                 hipLaunchKernelGGL(k_multi, dim3(cap), dim3(threads), lds_stream, st, one, m, k);
-            return hipGetLastError();
+            return q4k_launched(name);
         };
         // A tile's batches are whole ring turns (D units per batch, R batches in flight);
         // pick the batch size that leaves the fewest idle unit slots in a wave's slice.
@@ -670,7 +666,7 @@ hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16
         hipLaunchKernelGGL((gemv_chunk_kernel<G, SYM, false>), dim3(tiles), dim3(threads), lds, st, xp, m,
                            qw, sc, zr, n, k, kc, y, ydt);
     }
-    return hipGetLastError();
+    return q4k_launched(*kname);
 }
 
 }  // namespace

@@ -619,7 +619,7 @@ hipError_t launch_upw(int mq, dim3 grid, dim3 block, size_t lds, hipStream_t st,
         hipLaunchKernelGGL((gemv_tile_kernel<G, SYM, XF16, U, 1, GR>), grid, block, lds, st, bt, m, k);
     else
         hipLaunchKernelGGL((gemv_tile_kernel<G, SYM, XF16, U, 4, GR>), grid, block, lds, st, bt, m, k);
-    return hipGetLastError();
+    return q4k_launched(XF16 ? "q4_gemv_tile_f16" : "q4_gemv_tile_bf16");
 }
 
 template <int G, bool SYM, bool XF16, bool GR>
@@ -648,7 +648,7 @@ hipError_t launch_wide_rows(int upw, dim3 grid, dim3 block, size_t lds, hipStrea
 #define Q4_WIDE(U)                                                                                          \
     if (upw == U) {                                                                                         \
         hipLaunchKernelGGL((gemv_wide_kernel<G, SYM, XF16, U, MR, D, T, GR>), grid, block, lds, st, bt, m, k); \
-        return hipGetLastError();                                                                           \
+        return q4k_launched(XF16 ? "q4_gemv_wide_f16" : "q4_gemv_wide_bf16");                               \
     }
     Q4_WIDE(4) Q4_WIDE(8) Q4_WIDE(12) Q4_WIDE(16)
 #undef Q4_WIDE

@@ -480,6 +480,7 @@ void update(const float* A, const float* D, float* C, int n, int k, int j0, int 
     const int ctiles = (col1 - col0 + NB - 1) / NB;
     hipLaunchKernelGGL(gptq_update_kernel, dim3(((n + NB - 1) / NB) * ctiles), dim3(256), 0, st, A, D, C, n, k, j0,
                        inner, col0, col1);
+    q4k_record("q4_gptq_update");
 }
 
 // Lazy updates at two levels.  Blocks of 64 columns are swept in order inside super-blocks
@@ -497,6 +498,7 @@ hipError_t sweep_all(const void* w, int n, int k, int g, const float* A, float* 
             float* Db = D + (int64_t)(j0 - s0) * n;  // this block's rows of the super-block's errors
             hipLaunchKernelGGL((sweep_kernel<DT, SYM>), dim3((n + 63) / 64), dim3(256), 0, st, w, n, k, g, A, C, sc,
                                zr, qw, Db, j0, bw);
+            q4k_record("q4_gptq_sweep");
             update(A, Db, C, n, k, j0, bw, j0 + bw, s1, st);   // the rest of the super-block
         }
         update(A, D, C, n, k, s0, s1 - s0, s1, k, st);        // every column beyond it
@@ -527,19 +529,24 @@ hipError_t q4k_gptq(const void* w, int w_dtype, int64_t n, int64_t k, const void
         hipLaunchKernelGGL(hessian_kernel<true>, dim3(tiles * tiles), dim3(256), 0, st, xs, (int)tokens, ki, damp, A);
     else
         hipLaunchKernelGGL(hessian_kernel<false>, dim3(tiles * tiles), dim3(256), 0, st, xs, (int)tokens, ki, damp, A);
+    q4k_record("q4_gptq_hessian");
     // 3. Cholesky in place
     for (int j0 = 0; j0 < ki; j0 += NB) {
         const int bw = ki - j0 < NB ? ki - j0 : NB;
         hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(64 * DW), 0, st, A, ki, j0, bw);
+        q4k_record("q4_gptq_chol_diag");
         const int below = ki - j0 - bw;
         if (below > 0) {
             hipLaunchKernelGGL(chol_trsm_kernel, dim3((below + NB - 1) / NB), dim3(256), 0, st, A, ki, j0, bw);
             const int tt = (below + NB - 1) / NB;
             hipLaunchKernelGGL(chol_update_kernel, dim3(tt * tt), dim3(256), 0, st, A, ki, j0, bw);
+            q4k_record("q4_gptq_chol_panel");
+            q4k_record("q4_gptq_chol_update");
         }
     }
     // 4. sweep
     hipLaunchKernelGGL(fill_zero_kernel, dim3(1024), dim3(256), 0, st, C, n * k);
+    q4k_record("q4_gptq_fill_zero");
     switch (w_dtype * 2 + (sym ? 1 : 0)) {
     case 0: e = sweep_all<0, false>(w, ni, ki, g, A, C, scales, zeros, qweight, D, st); break;
     case 1: e = sweep_all<0, true>(w, ni, ki, g, A, C, scales, zeros, qweight, D, st); break;

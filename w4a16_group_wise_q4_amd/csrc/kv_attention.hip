@@ -373,7 +373,7 @@ hipError_t launch_nl(const KvArgs& a, int nl, int heads, hipStream_t st) {
     case 4: hipLaunchKernelGGL((kv_partial_kernel<D, G, SYM, XF16, 4>), grid, block, 0, st, a); break;
     default: hipLaunchKernelGGL((kv_partial_kernel<D, G, SYM, XF16, 8>), grid, block, 0, st, a); break;
     }
-    return hipGetLastError();
+    return q4k_launched(XF16 ? "q4_kv_partial_f16" : "q4_kv_partial_bf16");
 }
 
 template <int D, int G, bool SYM>
@@ -467,5 +467,5 @@ hipError_t q4k_kv_attention(const void* q, int xd, const uint32_t* kq, const uin
     else
         hipLaunchKernelGGL(kv_combine_kernel<256>, cg, cb, 0, st, workspace, chunks, out);
     *kname = xd == 1 ? "q4_kv_attention_f16" : "q4_kv_attention_bf16";
-    return hipGetLastError();
+    return q4k_launched("q4_kv_combine");
 }

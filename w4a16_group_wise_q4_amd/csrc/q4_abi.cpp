@@ -11,11 +11,35 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <cstring>
+#include <string>
+
 #include "q4_launch.h"
+
+#ifndef Q4_SOURCE_DIGEST
+#error "Q4_SOURCE_DIGEST (the digest of the sources, computed by the build) must be defined"
+#endif
 
 namespace {
 
 thread_local const char* g_last_kernel = "";
+
+// The kernels enqueued by the calling thread's current entry-point call (distinct names in
+// launch order, and the number of launches), and those of its last successful call.
+struct LaunchLog {
+    const char* names[32];
+    int distinct;
+    int64_t count;
+};
+thread_local LaunchLog g_cur_log = {{}, 0, 0};
+thread_local LaunchLog g_last_log = {{}, 0, 0};
+thread_local std::string g_last_names;
+
+void begin_call() {
+    g_cur_log.distinct = 0;
+    g_cur_log.count = 0;
+}
 
 constexpr int64_t kMaxElems = int64_t(1) << 40;
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
@@ -66,16 +90,30 @@ q4_status check_quant(const void* w, q4_dtype w_dtype, int64_t n, int64_t k, int
 q4_status finish(hipError_t e, const char* name) {
     if (e != hipSuccess) return Q4_ERR_LAUNCH;
     g_last_kernel = name;
+    g_last_log = g_cur_log;
+    g_last_names.clear();
+    for (int i = 0; i < g_last_log.distinct; ++i) {
+        if (i) g_last_names += ",";
+        g_last_names += g_last_log.names[i];
+    }
     return Q4_OK;
 }
 
 }  // namespace
+
+void q4k_record(const char* name) {
+    ++g_cur_log.count;
+    for (int i = 0; i < g_cur_log.distinct; ++i)
+        if (std::strcmp(g_cur_log.names[i], name) == 0) return;
+    if (g_cur_log.distinct < 32) g_cur_log.names[g_cur_log.distinct++] = name;
+}
 
 extern "C" {
 
 q4_status q4_quantize_pack(const void* w, q4_dtype w_dtype, int64_t n, int64_t k,
                            int32_t group_size, int32_t symmetric, uint32_t* qweight,
                            uint16_t* scales, uint32_t* zeros, hipStream_t stream) {
+    begin_call();
     q4_status st = check_quant(w, w_dtype, n, k, group_size, symmetric, qweight, scales, zeros);
     if (st != Q4_OK) return st;
     const char* name = "";
@@ -87,6 +125,7 @@ q4_status q4_quantize_pack(const void* w, q4_dtype w_dtype, int64_t n, int64_t k
 q4_status q4_quantize_pack_mse(const void* w, q4_dtype w_dtype, int64_t n, int64_t k,
                                int32_t group_size, int32_t symmetric, uint32_t* qweight,
                                uint16_t* scales, uint32_t* zeros, hipStream_t stream) {
+    begin_call();
     q4_status st = check_quant(w, w_dtype, n, k, group_size, symmetric, qweight, scales, zeros);
     if (st != Q4_OK) return st;
     const char* name = "";
@@ -98,6 +137,7 @@ q4_status q4_quantize_pack_mse(const void* w, q4_dtype w_dtype, int64_t n, int64
 q4_status q4_quantize_pack_grouped(const q4_quant_problem* problems, int32_t count,
                                    q4_dtype w_dtype, int32_t group_size, int32_t symmetric,
                                    hipStream_t stream) {
+    begin_call();
     if (!problems) return Q4_ERR_NULL;
     if (count < 1 || count > q4::kMaxGroup) return Q4_ERR_SHAPE;
     q4::QuantProblem qp[q4::kMaxGroup];
@@ -118,6 +158,7 @@ q4_status q4_quantize_pack_grouped(const q4_quant_problem* problems, int32_t cou
 q4_status q4_dequant(const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros,
                      int64_t n, int64_t k, int32_t group_size, int32_t symmetric, void* w_out,
                      q4_dtype out_dtype, hipStream_t stream) {
+    begin_call();
     q4_status st = check_layout(n, k, group_size);
     if (st != Q4_OK) return st;
     if (out_dtype != Q4_F32 && out_dtype != Q4_F16 && out_dtype != Q4_BF16) return Q4_ERR_DTYPE;
@@ -130,20 +171,25 @@ q4_status q4_dequant(const uint32_t* qweight, const uint16_t* scales, const uint
     return finish(e, name);
 }
 
-namespace {
-// Compute units of the current device (cached per device; 256 if the query fails).
-int device_cus() {
-    static int cus[64] = {0};
+}  // extern "C"
+
+// Compute units per device.  Threads that race on the first lookup store the same value.
+int q4k_device_cus() {
+    static std::atomic<int> cus[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cus[dev] == 0) {
-        int c = 0;
+    int c = cus[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
         if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
             c = 256;
-        cus[dev] = c;
+        cus[dev].store(c, std::memory_order_relaxed);
     }
-    return cus[dev];
+    return c;
 }
+
+extern "C" {
+
+namespace {
 
 // One W4A16 product, validated.  m <= 16: the decode GEMV.  16 < m <= 256: the GEMV on
 // 16-row chunks of x sharing the weight (full chunks in grouped launches of up to 8, the
@@ -165,7 +211,7 @@ hipError_t run_product(const void* x, int xd, int64_t m, const uint32_t* qw, con
                        const uint32_t* zr, int64_t n, int64_t k, int g, int sym, void* y, int ydt,
                        hipStream_t st, const char** name) {
     if (m <= 16) return q4k_gemv(x, xd, (int)m, qw, sc, zr, n, k, g, sym, y, ydt, st, name);
-    if (!chunked_gemv(m, n, device_cus())) return q4k_gemm(x, xd, m, qw, sc, zr, n, k, g, sym, y, ydt, st, name);
+    if (!chunked_gemv(m, n, q4k_device_cus())) return q4k_gemm(x, xd, m, qw, sc, zr, n, k, g, sym, y, ydt, st, name);
     const int64_t full = m / 16, rem = m % 16;
     const uint16_t* xs = static_cast<const uint16_t*>(x);
     char* yb = static_cast<char*>(y);
@@ -212,6 +258,7 @@ q4_status check_matmul(const void* x, q4_dtype x_dtype, int64_t m, const uint32_
 q4_status q4_w4a16_gemm_grouped_out(const q4_gemm_problem* problems, int32_t count,
                                     q4_dtype x_dtype, int64_t m, int64_t k, int32_t group_size,
                                     int32_t symmetric, q4_dtype y_dtype, hipStream_t stream) {
+    begin_call();
     if (!problems) return Q4_ERR_NULL;
     if (count < 1 || count > q4::kMaxGroup) return Q4_ERR_SHAPE;
     int64_t rows = 0;
@@ -254,6 +301,7 @@ q4_status q4_w4a16_gemm_out(const void* x, q4_dtype x_dtype, int64_t m, const ui
                             const uint16_t* scales, const uint32_t* zeros, int64_t n, int64_t k,
                             int32_t group_size, int32_t symmetric, void* y, q4_dtype y_dtype,
                             hipStream_t stream) {
+    begin_call();
     const q4_status st = check_matmul(x, x_dtype, m, qweight, scales, zeros, n, k, group_size,
                                       symmetric, y, y_dtype);
     if (st != Q4_OK) return st;
@@ -294,6 +342,7 @@ q4_status q4_kv_quantize(const void* kv, q4_dtype kv_dtype, int64_t t_new, int64
                          int64_t head_dim, int32_t group_size, int32_t symmetric, int64_t t_cap,
                          int64_t t0, uint32_t* qcache, uint16_t* scache, uint32_t* zcache,
                          hipStream_t stream) {
+    begin_call();
     q4_status st = check_kv_sizes(heads, head_dim, group_size, t_cap);
     if (st != Q4_OK) return st;
     if (t_new < 1 || t0 < 0 || t0 > t_cap - t_new) return Q4_ERR_SHAPE;
@@ -318,6 +367,7 @@ q4_status q4_kv_attention(const void* q, q4_dtype q_dtype, int64_t heads, int64_
                           const uint32_t* vz, int32_t group_size, int32_t symmetric, float scale,
                           float* out, void* workspace, int64_t workspace_bytes,
                           hipStream_t stream) {
+    begin_call();
     q4_status st = check_kv_sizes(heads, head_dim, group_size, t_cap);
     if (st != Q4_OK) return st;
     if (!kv_attention_dims_ok(heads, head_dim, n_tok) || n_tok > t_cap) return Q4_ERR_SHAPE;
@@ -342,6 +392,7 @@ q4_status q4_kv_attention_noalloc(const void* q, q4_dtype q_dtype, int64_t heads
                                   const uint16_t* ks, const uint32_t* kz, const uint32_t* vq,
                                   const uint16_t* vs, const uint32_t* vz, int32_t group_size,
                                   int32_t symmetric, float scale, float* out, hipStream_t stream) {
+    begin_call();
     q4_status st = check_kv_sizes(heads, head_dim, group_size, t_cap);
     if (st != Q4_OK) return st;
     if (!kv_attention_dims_ok(heads, head_dim, n_tok) || n_tok > t_cap) return Q4_ERR_SHAPE;
@@ -378,6 +429,7 @@ q4_status q4_gptq_quantize(const void* w, q4_dtype w_dtype, int64_t n, int64_t k
                            q4_dtype x_dtype, int64_t tokens, int32_t group_size, int32_t symmetric,
                            float damp, uint32_t* qweight, uint16_t* scales, uint32_t* zeros,
                            void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+    begin_call();
     q4_status st = check_quant(w, w_dtype, n, k, group_size, symmetric, qweight, scales, zeros);
     if (st != Q4_OK) return st;
     if (k > kMaxGptqK || tokens < 1 || tokens > kMaxDim || tokens > kMaxElems / k) return Q4_ERR_SHAPE;
@@ -423,6 +475,12 @@ const char* q4_status_str(q4_status s) {
 }
 
 const char* q4_last_kernel(void) { return g_last_kernel; }
+
+const char* q4_last_kernels(void) { return g_last_names.c_str(); }
+
+int64_t q4_last_launch_count(void) { return g_last_log.count; }
+
+const char* q4_source_digest(void) { return Q4_SOURCE_DIGEST; }
 
 int32_t q4_layout_version(void) { return 1; }
 

@@ -217,6 +217,19 @@ __device__ __forceinline__ uint32_t buf_load_u16(rsrc r, int voff, int soff) {
 
 }  // namespace q4
 
+// ---------------------------------------------------------------- launch record
+// Every kernel launch the library enqueues is recorded (name, count) for the calling
+// thread's current entry-point call; q4_last_kernels() and q4_last_launch_count() report
+// the record of the last successful call.
+void q4k_record(const char* name);
+// After a single launch: the launch status, with the launch recorded under name if it
+// succeeded.
+inline hipError_t q4k_launched(const char* name) {
+    const hipError_t e = hipGetLastError();
+    if (e == hipSuccess) q4k_record(name);
+    return e;
+}
+
 // ---------------------------------------------------------------- decode GEMV arguments
 namespace q4 {
 constexpr int kMaxGroup = 8;

@@ -48,6 +48,10 @@ hipError_t q4k_kv_attention(const void* q, int q_dtype, const uint32_t* kq, cons
                             int64_t t_cap, int g, int sym, float scale, float* out,
                             float* workspace, int chunks, int loads, hipStream_t stream,
                             const char** kname);
+// Compute units of the current device, looked up once per device (256 if the query
+// fails); safe to call from several threads.
+int q4k_device_cus();
+
 // The fixed per-device scratch of the no-allocation attention entry point: its size in
 // bytes, and its device address on the current device (looked up once per device; a
 // failed lookup returns the runtime's error and leaves *ptr NULL).

@@ -187,19 +187,11 @@ __global__ __launch_bounds__(256) void quant_mse_kernel(const void* __restrict__
     }
 }
 
-int g_num_cus = 0;
-
 template <int G, bool SYM>
 hipError_t launch(const void* w, int dt, int64_t n, int64_t k, uint32_t* qw, uint16_t* sc,
                   uint32_t* zr, hipStream_t st, const char** kname) {
-    if (g_num_cus == 0) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&g_num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            g_num_cus <= 0)
-            g_num_cus = 256;
-    }
-    const int64_t cap = (int64_t)g_num_cus * 32;  // 8 waves per SIMD
+    const int num_cus = q4k_device_cus();
+    const int64_t cap = (int64_t)num_cus * 32;  // 8 waves per SIMD
     const int64_t tasks = n * ((k / G + 7) / 8);
     const int64_t waves = tasks < cap ? tasks : cap;
     const int64_t blocks = (waves + 3) / 4;
@@ -213,7 +205,7 @@ hipError_t launch(const void* w, int dt, int64_t n, int64_t k, uint32_t* qw, uin
         hipLaunchKernelGGL((quant_mse_kernel<G, SYM, 1>), grid, block, 0, st, w, ni, ki, qw, sc, zr);
     else
         hipLaunchKernelGGL((quant_mse_kernel<G, SYM, 2>), grid, block, 0, st, w, ni, ki, qw, sc, zr);
-    return hipGetLastError();
+    return q4k_launched(*kname);
 }
 
 }  // namespace

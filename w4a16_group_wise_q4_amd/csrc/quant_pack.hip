@@ -184,20 +184,12 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(const void* __restrict__ 
     }
 }
 
-int g_num_cus = 0;
-
 template <int G, bool SYM>
 hipError_t launch_dt(const q4::QuantBatch& bt, int dt, hipStream_t st, const char** kname) {
-    if (g_num_cus == 0) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&g_num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            g_num_cus <= 0)
-            g_num_cus = 256;
-    }
+    const int num_cus = q4k_device_cus();
     // enough waves to keep every SIMD busy (8 per SIMD), no more than the largest problem
     // has tasks
-    const int64_t cap = (int64_t)g_num_cus * 32;
+    const int64_t cap = (int64_t)num_cus * 32;
     int64_t tasks = 0;
     for (int i = 0; i < bt.count; ++i) {
         const int64_t t = (int64_t)bt.p[i].n * ((bt.p[i].k / G + 7) / 8);
@@ -214,7 +206,7 @@ hipError_t launch_dt(const q4::QuantBatch& bt, int dt, hipStream_t st, const cha
         hipLaunchKernelGGL((quant_pack_kernel<G, SYM, 1>), grid, block, 0, st, bt);
     else
         hipLaunchKernelGGL((quant_pack_kernel<G, SYM, 2>), grid, block, 0, st, bt);
-    return hipGetLastError();
+    return q4k_launched(*kname);
 }
 
 hipError_t launch_batch(const q4::QuantBatch& bt, int w_dtype, int g, int sym, hipStream_t st,
@@ -245,7 +237,7 @@ template <int G, bool SYM>
 hipError_t launch_kv(const void* kv, int dt, int rows, int d, int heads, int t_cap, int t0, uint32_t* qc,
                      uint16_t* sc, uint32_t* zc, hipStream_t st) {
     const int64_t tasks = (int64_t)heads * ((rows / heads + 512 / d - 1) / (512 / d));
-    const int64_t cap = (int64_t)(g_num_cus > 0 ? g_num_cus : 256) * 32;
+    const int64_t cap = (int64_t)q4k_device_cus() * 32;
     const int64_t waves = tasks < cap ? tasks : cap;  // one task per wave while they last
     const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
     if (dt == 0)
@@ -254,7 +246,8 @@ hipError_t launch_kv(const void* kv, int dt, int rows, int d, int heads, int t_c
         hipLaunchKernelGGL((kv_quant_kernel<G, SYM, 1>), grid, block, 0, st, kv, rows, d, heads, t_cap, t0, qc, sc, zc);
     else
         hipLaunchKernelGGL((kv_quant_kernel<G, SYM, 2>), grid, block, 0, st, kv, rows, d, heads, t_cap, t0, qc, sc, zc);
-    return hipGetLastError();
+    static const char* names[3] = {"q4_kv_quant_f32", "q4_kv_quant_f16", "q4_kv_quant_bf16"};
+    return q4k_launched(names[dt]);
 }
 }  // namespace
 
