@@ -11,6 +11,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libq4.so")
+# the streaming-read probe the benchmark measures its ceiling with (not part of the C ABI)
+PROBE_SOURCE = os.path.join(PKG, "probe", "read_probe.hip")
+PROBE_LIBRARY = os.path.join(PKG, "libq4probe.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -70,12 +73,14 @@ def build(verbose: bool = False) -> str:
     objs = [os.path.join(objdir, os.path.basename(src) + ".%d.o" % os.getpid()) for src in srcs]
     digest = f'-DQ4_SOURCE_DIGEST="{source_digest()}"'
     cmds = [[HIPCC, *FLAGS, digest, "-c", "-I", INCLUDE, "-I", CSRC, src, "-o", obj] for src, obj in zip(srcs, objs)]
+    probe_tmp = PROBE_LIBRARY + ".tmp%d" % os.getpid()
+    cmds.append([HIPCC, *FLAGS, *LINK_FLAGS[1:], PROBE_SOURCE, "-o", probe_tmp])
     workers = max(1, min(len(cmds), os.cpu_count() or 1, 16))
     with ThreadPoolExecutor(max_workers=workers) as pool:
         results = list(pool.map(_run, cmds))
     logs = []
     try:
-        for src, (rc, out) in zip(srcs, results):
+        for src, (rc, out) in zip(srcs + [PROBE_SOURCE], results):
             if rc != 0:
                 raise RuntimeError("hipcc failed on %s:\n%s" % (os.path.basename(src), out))
             logs.append(out)
@@ -94,4 +99,5 @@ def build(verbose: bool = False) -> str:
             if noise not in line:
                 print(line)
     os.replace(tmp, LIBRARY)
+    os.replace(probe_tmp, PROBE_LIBRARY)
     return LIBRARY
