@@ -79,11 +79,13 @@ q4_status q4_quantize_pack(const void* w, q4_dtype w_dtype, int64_t n, int64_t k
  * the range scaled by alpha (asymmetric [alpha*min(x_min,0), alpha*max(x_max,0)], the zero
  * point from -alpha*min(x_min,0) / S; symmetric alpha*max|x|), weights outside the
  * clipped range saturating at the end codes.  A candidate's error is the sum of
- * (x - S(q - z))^2 in IEEE fp64, each group's 8 chunks of g/8 consecutive weights summed
- * in order and then added pairwise ((c0+c1)+(c2+c3))+((c4+c5)+(c6+c7)); the first smallest
- * error wins, so alpha = 1 (the q4_quantize_pack result) is kept unless clipping strictly
- * lowers the error.  Output is the same packed format, bit-identical to the CPU
- * definition.  Arguments, limits and errors as for q4_quantize_pack.  The search costs
+ * (x - S(q - z))^2 in IEEE fp64: each lane adds its g/8 consecutive weights in order and
+ * the 8 lanes' sums are combined in a tree, ((c0+c1)+(c2+c3))+((c4+c5)+(c6+c7)); the
+ * first smallest error wins, so alpha = 1 (the q4_quantize_pack result) is kept unless
+ * clipping strictly lowers the error.  Output is the same packed format: each group is
+ * exactly the quantization at its chosen ratio, and that ratio's error is the smallest
+ * up to the fp64 rounding of the sums (another summation order may break a near-tie the
+ * other way).  Arguments, limits and errors as for q4_quantize_pack.  The search costs
  * about a dozen fp32/fp64 operations per weight and candidate: it is bound by ALU
  * throughput, not memory. */
 q4_status q4_quantize_pack_mse(const void* w, q4_dtype w_dtype, int64_t n, int64_t k,

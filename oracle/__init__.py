@@ -76,6 +76,10 @@ class Oracle:
         lib.orc_quantize_pack.restype = c_int
         lib.orc_quantize_pack_mse.argtypes = [vp, c_int, c_i64, c_i64, c_i64, c_int, vp, vp, vp, vp]
         lib.orc_quantize_pack_mse.restype = c_int
+        lib.orc_quantize_pack_clip.argtypes = [vp, c_int, c_i64, c_i64, c_i64, c_int, vp, vp, vp, vp]
+        lib.orc_quantize_pack_clip.restype = c_int
+        lib.orc_mse_errors.argtypes = [vp, c_int, c_i64, c_i64, c_i64, c_int, vp]
+        lib.orc_mse_errors.restype = c_int
         lib.orc_dequant_f64.argtypes = [vp, vp, vp, c_i64, c_i64, c_i64, c_int, vp]
         lib.orc_dequant_f64.restype = c_int
         lib.orc_linear_f64.argtypes = [vp, c_int, c_i64, vp, c_i64, vp, vp, vp,
@@ -145,6 +149,34 @@ class Oracle:
         if with_choice:
             return qweight, scales, zeros, choice
         return qweight, scales, zeros
+
+    def quantize_pack_clip(self, w, group_size: int, symmetric: bool, ratio):
+        """Quantize + pack of W [n, k] with group (row, j) clipped at alpha = (20 - i) / 20,
+        i = ratio[row, j] (an int, or an [n, G] array): (qweight, scales, zeros)."""
+        arr, code = _as_input(w)
+        n, k = arr.shape
+        G = k // group_size
+        idx = np.ascontiguousarray(np.broadcast_to(np.asarray(ratio, dtype=np.uint8), (n, G)))
+        qweight = np.zeros((n, k // 8), dtype=np.uint32)
+        scales = np.zeros((n, G), dtype=np.uint16)
+        zeros = np.zeros((n, (G + 7) // 8), dtype=np.uint32)
+        rc = self.lib.orc_quantize_pack_clip(_ptr(arr), code, n, k, group_size,
+                                             int(bool(symmetric)), _ptr(idx), _ptr(qweight),
+                                             _ptr(scales), _ptr(zeros))
+        if rc != 0:
+            raise ValueError("oracle quantize_pack_clip rejected the arguments")
+        return qweight, scales, zeros
+
+    def mse_errors(self, w, group_size: int, symmetric: bool) -> np.ndarray:
+        """Every clip candidate's squared error, float64 [n, G, 11] (ratio index last)."""
+        arr, code = _as_input(w)
+        n, k = arr.shape
+        out = np.zeros((n, k // group_size, 11), dtype=np.float64)
+        rc = self.lib.orc_mse_errors(_ptr(arr), code, n, k, group_size, int(bool(symmetric)),
+                                     _ptr(out))
+        if rc != 0:
+            raise ValueError("oracle mse_errors rejected the arguments")
+        return out
 
     def dequant(self, qweight, scales, zeros, n: int, k: int, group_size: int,
                 symmetric: bool) -> np.ndarray:
@@ -241,6 +273,14 @@ def quantize_pack(*a, **kw):
 
 def quantize_pack_mse(*a, **kw):
     return default().quantize_pack_mse(*a, **kw)
+
+
+def quantize_pack_clip(*a, **kw):
+    return default().quantize_pack_clip(*a, **kw)
+
+
+def mse_errors(*a, **kw):
+    return default().mse_errors(*a, **kw)
 
 
 def dequant(*a, **kw):

@@ -119,7 +119,7 @@ int orc_quantize_pack(const void* w, int w_dtype, int64_t n, int64_t k, int64_t 
     memset(qweight, 0, (size_t)(n * (k / 8)) * sizeof(uint32_t));
     if (!symmetric) memset(zeros, 0, (size_t)(n * zw) * sizeof(uint32_t));
 
-    float* v = (float*)malloc((size_t)(g > 0 ? g : 1) * sizeof(float));
+    float* v = (float*)malloc((size_t)g * sizeof(float));
     if (!v) return -1;
     for (int64_t row = 0; row < n; ++row) {
         for (int64_t j = 0; j < G; ++j) {
@@ -187,10 +187,9 @@ int orc_quantize_pack(const void* w, int w_dtype, int64_t n, int64_t k, int64_t 
  *      asymmetric [alpha*min(x_min,0), alpha*max(x_max,0)], symmetric alpha*max|x|, each
  *      product one fp32 rounding; the zero point divides -alpha*min(x_min,0) by S in fp32;
  *      weights outside the clipped range saturate at the end codes;
- *   M3 the error of a candidate is sum over the group of (x - S*(q - z))^2 in IEEE binary64:
- *      the group is cut into 8 chunks of g/8 consecutive weights, each chunk summed in
- *      order from 0, then the chunk sums are added pairwise,
- *      ((c0 + c1) + (c2 + c3)) + ((c4 + c5) + (c6 + c7));
+ *   M3 the error of a candidate is sum over the group of (x - S*(q - z))^2 in IEEE binary64,
+ *      each difference and square one binary64 rounding, the terms added one by one in
+ *      column order: the plain definition, no blocking;
  *   M4 the candidate with the smallest error wins; an equal error keeps the earlier
  *      (larger) ratio, so alpha = 1 (plain RTN) wins unless clipping strictly helps. */
 #define ORC_MSE_CANDIDATES 11
@@ -221,34 +220,30 @@ static double mse_candidate(const float* v, int64_t g, int symmetric, float alph
     const float q_max = symmetric ? 7.0f : 15.0f;
     int z = 0;
     if (!symmetric) z = (int)clampf(rintf(-lo / S), q_min, q_max);
-    const int64_t chunk = g / 8;
-    double part[8];
-    for (int c = 0; c < 8; ++c) {
-        double acc = 0.0;
-        for (int64_t t = c * chunk; t < (c + 1) * chunk; ++t) {
-            const int q = (int)clampf(rintf(v[t] / S) + (float)z, q_min, q_max);
-            if (q_out) q_out[t] = q;
-            const double xhat = (double)S * (double)(q - z);
-            const double d = (double)v[t] - xhat;
-            acc = acc + d * d;
-        }
-        part[c] = acc;
+    double err = 0.0;
+    for (int64_t t = 0; t < g; ++t) {
+        const int q = (int)clampf(rintf(v[t] / S) + (float)z, q_min, q_max);
+        if (q_out) q_out[t] = q;
+        const double xhat = (double)S * (double)(q - z);
+        const double d = (double)v[t] - xhat;
+        err = err + d * d;
     }
-    const double err = ((part[0] + part[1]) + (part[2] + part[3])) +
-                       ((part[4] + part[5]) + (part[6] + part[7]));
     *s16_out = s16;
     *z_out = z;
     return err;
 }
 
-int orc_quantize_pack_mse(const void* w, int w_dtype, int64_t n, int64_t k, int64_t g,
-                          int symmetric, uint32_t* qweight, uint16_t* scales, uint32_t* zeros,
-                          uint8_t* choice) {
+/* The clip search over a whole matrix.  ratio == NULL: each group scans the ratios (M1, M4);
+ * otherwise group (row, j) is quantized at ratio index ratio[row*G + j] without a search.
+ * errors (may be NULL) receives every candidate's error, [n][G][ORC_MSE_CANDIDATES]. */
+static int mse_matrix(const void* w, int w_dtype, int64_t n, int64_t k, int64_t g, int symmetric,
+                      const uint8_t* ratio, uint32_t* qweight, uint16_t* scales, uint32_t* zeros,
+                      uint8_t* choice, double* errors) {
     if (n < 0 || k < 0 || g < 8 || g % 8 != 0 || k % g != 0 || k % 8 != 0) return -1;
     const int64_t G = k / g;
     const int64_t zw = (G + 7) / 8;
-    memset(qweight, 0, (size_t)(n * (k / 8)) * sizeof(uint32_t));
-    if (!symmetric) memset(zeros, 0, (size_t)(n * zw) * sizeof(uint32_t));
+    if (qweight) memset(qweight, 0, (size_t)(n * (k / 8)) * sizeof(uint32_t));
+    if (zeros && !symmetric) memset(zeros, 0, (size_t)(n * zw) * sizeof(uint32_t));
     float* v = (float*)malloc((size_t)g * sizeof(float));
     int* q = (int*)malloc((size_t)g * sizeof(int));
     if (!v || !q) {
@@ -256,28 +251,40 @@ int orc_quantize_pack_mse(const void* w, int w_dtype, int64_t n, int64_t k, int6
         free(q);
         return -1;
     }
-    for (int64_t row = 0; row < n; ++row) {
+    int rc = 0;
+    for (int64_t row = 0; row < n && rc == 0; ++row) {
         for (int64_t j = 0; j < G; ++j) {
             for (int64_t t = 0; t < g; ++t) v[t] = load_elem(w, w_dtype, row * k + j * g + t);
-            /* M1, M4: scan the ratios, keep the first smallest error */
             int best = 0;
-            double best_err = 0.0;
-            for (int i = 0; i < ORC_MSE_CANDIDATES; ++i) {
-                const float alpha = (float)(20 - i) / 20.0f;
-                uint16_t s16;
-                int z;
-                const double e = mse_candidate(v, g, symmetric, alpha, &s16, &z, NULL);
-                if (i == 0 || e < best_err) {
-                    best = i;
-                    best_err = e;
+            if (ratio) {
+                best = ratio[row * G + j];
+                if (best >= ORC_MSE_CANDIDATES) {
+                    rc = -1;
+                    break;
                 }
             }
+            if (!ratio || errors) {
+                /* M1, M4: scan the ratios, keep the first smallest error */
+                double best_err = 0.0;
+                for (int i = 0; i < ORC_MSE_CANDIDATES; ++i) {
+                    const float alpha = (float)(20 - i) / 20.0f;
+                    uint16_t s16;
+                    int z;
+                    const double e = mse_candidate(v, g, symmetric, alpha, &s16, &z, NULL);
+                    if (errors) errors[(row * G + j) * ORC_MSE_CANDIDATES + i] = e;
+                    if (!ratio && (i == 0 || e < best_err)) {
+                        best = i;
+                        best_err = e;
+                    }
+                }
+            }
+            if (choice) choice[row * G + j] = (uint8_t)best;
+            if (!qweight) continue;
             uint16_t s16;
             int z;
             mse_candidate(v, g, symmetric, (float)(20 - best) / 20.0f, &s16, &z, q);
             scales[row * G + j] = s16;
             if (!symmetric) zeros[row * zw + j / 8] |= (uint32_t)z << (4 * (j % 8));
-            if (choice) choice[row * G + j] = (uint8_t)best;
             for (int64_t t = 0; t < g; ++t) {
                 const uint32_t u = (uint32_t)(symmetric ? q[t] + 8 : q[t]);
                 const int64_t col = j * g + t;
@@ -287,7 +294,26 @@ int orc_quantize_pack_mse(const void* w, int w_dtype, int64_t n, int64_t k, int6
     }
     free(v);
     free(q);
-    return 0;
+    return rc;
+}
+
+int orc_quantize_pack_mse(const void* w, int w_dtype, int64_t n, int64_t k, int64_t g,
+                          int symmetric, uint32_t* qweight, uint16_t* scales, uint32_t* zeros,
+                          uint8_t* choice) {
+    return mse_matrix(w, w_dtype, n, k, g, symmetric, NULL, qweight, scales, zeros, choice, NULL);
+}
+
+int orc_quantize_pack_clip(const void* w, int w_dtype, int64_t n, int64_t k, int64_t g,
+                           int symmetric, const uint8_t* ratio, uint32_t* qweight,
+                           uint16_t* scales, uint32_t* zeros) {
+    if (!ratio) return -1;
+    return mse_matrix(w, w_dtype, n, k, g, symmetric, ratio, qweight, scales, zeros, NULL, NULL);
+}
+
+int orc_mse_errors(const void* w, int w_dtype, int64_t n, int64_t k, int64_t g, int symmetric,
+                   double* errors) {
+    if (!errors) return -1;
+    return mse_matrix(w, w_dtype, n, k, g, symmetric, NULL, NULL, NULL, NULL, NULL, errors);
 }
 
 /* ---------------------------------------------------------------- dequant */

@@ -421,6 +421,68 @@ def check_mse_brute_force(o):
     assert int(ch[0, 0]) > 0 and c[int(ch[0, 0])][0] < c[0][0] * (1 - 1e-6)
 
 
+def check_mse_errors_exact(o):
+    """Every candidate's error, as the oracle sums it, is the exact sum of squares of that
+    candidate's reconstruction (rational arithmetic on the independent numpy candidates)
+    to within the rounding of g fp64 squares and g - 1 fp64 additions: relative error at
+    most (g + 2) * 2^-53."""
+    from fractions import Fraction
+    u = 2.0 ** -53
+    rows = [0, 2, 3, 7, 8, 10]  # normal, outliers, one-sided, fp16-subnormal, saturated, underflow
+    for seed, k, g, sym in [(46, 256, 128, False), (47, 128, 32, True), (48, 256, 64, False)]:
+        w = np.ascontiguousarray(random_weights(seed, 12, k)[rows])
+        w[0, :g] *= np.float32(1e-3)                  # small errors next to large ones
+        w[0, g - 1] = np.float32(30)                  # an outlier: clipping matters
+        n = len(rows)
+        errs = o.mse_errors(w, g, sym)
+        assert errs.shape == (n, k // g, MSE_CANDIDATES)
+        for row in range(n):
+            for j in range(k // g):
+                v = w[row, j * g:(j + 1) * g]
+                for i, (_, s16, z, q) in enumerate(mse_candidates_numpy(v, sym)):
+                    S = Fraction(float(np.array([s16], np.uint16).view(np.float16)[0]))
+                    exact = sum((Fraction(float(x)) - S * int(c - z)) ** 2 for x, c in zip(v, q))
+                    got = Fraction(float(errs[row, j, i]))
+                    assert abs(got - exact) <= (g + 2) * Fraction(u) * exact, (seed, row, j, i)
+
+
+def check_mse_pack_at_ratio(o):
+    """Quantizing at a given clip ratio reproduces that candidate of the independent numpy
+    search bit for bit; ratio index 0 (alpha = 1) is the RTN quantizer; the search's
+    result is the pack at its chosen ratio, and that ratio is the first smallest error."""
+    for seed, n, k, g, sym in [(49, 12, 256, 64, False), (50, 12, 256, 128, True)]:
+        w = random_weights(seed, n, k)
+        w[2, 5] = np.float32(-25)
+        G = k // g
+        errs = o.mse_errors(w, g, sym)
+        qm, sm, zm, ch = o.quantize_pack_mse(w, g, sym, with_choice=True)
+        for row in range(n):
+            for j in range(G):
+                e = errs[row, j]
+                assert int(ch[row, j]) == int(np.flatnonzero(e == e.min())[0]), (seed, row, j)
+        qc, sc, zc = o.quantize_pack_clip(w, g, sym, ch)
+        assert np.array_equal(qc, qm) and np.array_equal(sc, sm) and np.array_equal(zc, zm)
+        qr, sr, zr = o.quantize_pack(w, g, sym)
+        q0, s0, z0 = o.quantize_pack_clip(w, g, sym, 0)
+        assert np.array_equal(q0, qr) and np.array_equal(s0, sr) and np.array_equal(z0, zr)
+        for i in (3, MSE_CANDIDATES - 1):
+            qi, si, zi = o.quantize_pack_clip(w, g, sym, i)
+            codes, zz = unpack_codes(qi, k), (None if sym else unpack_zeros(zi, G))
+            for row in range(n):
+                for j in range(G):
+                    _, s16, z, q = mse_candidates_numpy(w[row, j * g:(j + 1) * g], sym)[i]
+                    assert int(si[row, j]) == s16, (seed, i, row, j)
+                    assert np.array_equal(codes[row, j * g:(j + 1) * g], q + 8 if sym else q)
+                    if not sym:
+                        assert int(zz[row, j]) == z, (seed, i, row, j)
+    try:
+        o.quantize_pack_clip(np.zeros((1, 32), np.float32), 32, False, MSE_CANDIDATES)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("a ratio index past the grid was accepted")
+
+
 def check_mse_rtn_limit(o):
     """alpha = 1 is plain RTN: wherever the search keeps it, the bits equal the RTN
     quantizer's (itself pinned by the hand-worked groups)."""
@@ -544,7 +606,8 @@ def check_kv_attention(o):
 ALL_CHECKS = [check_golden_groups, check_fp16_conversion, check_invariants,
               check_brute_force_nearest, check_levels_and_bytes, check_dequant_closed_forms,
               check_linear, check_argument_rejection, check_mse_brute_force,
-              check_mse_rtn_limit, check_kv_cache_placement, check_kv_attention]
+              check_mse_rtn_limit, check_mse_errors_exact, check_mse_pack_at_ratio,
+              check_kv_cache_placement, check_kv_attention]
 
 
 # --------------------------------------------------------------------------- GPTQ
