@@ -50,10 +50,20 @@ typedef enum {
     Q4_ERR_DTYPE = 4,   /* dtype not accepted by this entry point */
     Q4_ERR_ALIGN = 5,   /* a pointer misses its required alignment */
     Q4_ERR_LAUNCH = 6,  /* the HIP runtime rejected the kernel launch */
-    Q4_ERR_SCRATCH = 7  /* the sizes need more scratch than q4_kv_attention_noalloc holds */
+    Q4_ERR_SCRATCH = 7, /* the sizes need more scratch than q4_kv_attention_noalloc holds */
+    /* never returned: they make every int32 a value of the type, so a code or dtype
+     * outside the list above (which the library rejects) is still a valid argument */
+    Q4_STATUS_INT_MIN_ = -2147483647 - 1,
+    Q4_STATUS_INT_MAX_ = 2147483647
 } q4_status;
 
-typedef enum { Q4_F32 = 0, Q4_F16 = 1, Q4_BF16 = 2 } q4_dtype;
+typedef enum {
+    Q4_F32 = 0,
+    Q4_F16 = 1,
+    Q4_BF16 = 2,
+    Q4_DTYPE_INT_MIN_ = -2147483647 - 1, /* never accepted; see q4_status */
+    Q4_DTYPE_INT_MAX_ = 2147483647
+} q4_dtype;
 
 /* RTN quantize-and-pack of W [n][k] (F32, F16 or BF16) into the packed format.
  *   q = clamp(round(w/s) + z, q_min, q_max)      [FL7] §Affine Quantization

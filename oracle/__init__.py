@@ -27,10 +27,13 @@ GCC_FLAGS = ["-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", 
              "-Wall", "-Wextra"]
 
 
-def compile_source(src: str, out: str, include_dir: str = _HERE) -> str:
-    """Compile one oracle C source into a shared library with the oracle's flags."""
+def compile_source(src: str, out: str, include_dir: str = _HERE, compiler: str = "gcc",
+                   extra: Tuple[str, ...] = ()) -> str:
+    """Compile one oracle C source into a shared library with the oracle's flags (extra
+    flags after them, e.g. sanitizers for a debug copy)."""
     tmp = out + ".tmp%d" % os.getpid()
-    subprocess.run(["gcc", *GCC_FLAGS, "-I", include_dir, "-o", tmp, src, "-lm"], check=True)
+    subprocess.run([compiler, *GCC_FLAGS, *extra, "-I", include_dir, "-o", tmp, src, "-lm"],
+                   check=True)
     os.replace(tmp, out)
     return out
 

@@ -77,7 +77,9 @@ _lib = None
 
 
 def library_path() -> str:
-    return _build.LIBRARY
+    """The library the binding loads: $Q4_LIBRARY if set (another build of the same
+    sources, e.g. the host-sanitized one), else the in-tree libq4.so."""
+    return os.environ.get("Q4_LIBRARY") or _build.LIBRARY
 
 
 class StaleLibraryError(RuntimeError):
@@ -88,15 +90,16 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_build.LIBRARY):
+    path = library_path()
+    if path == _build.LIBRARY and not os.path.exists(path):
         _build.build()  # raises if hipcc fails: there is no fallback
-    lib = ctypes.CDLL(_build.LIBRARY)
+    lib = ctypes.CDLL(path)
     lib.q4_source_digest.argtypes = []
     lib.q4_source_digest.restype = ctypes.c_char_p
     built, here = lib.q4_source_digest().decode(), _build.source_digest()
     if built != here:
         raise StaleLibraryError(
-            f"{_build.LIBRARY} was built from sources with digest {built}, but the sources "
+            f"{path} was built from sources with digest {built}, but the sources "
             f"here digest to {here}: rebuild it (__graft_entry__.build())")
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     lib.q4_quantize_pack.argtypes = [vp, ctypes.c_int, i64, i64, i32, i32, vp, vp, vp, vp]

@@ -27,6 +27,15 @@ FLAGS = [
 
 LINK_FLAGS = [f"--offload-arch={ARCH}", "-fPIC", "-shared"]
 
+# A debug build for the CPU: AddressSanitizer and UndefinedBehaviorSanitizer on the host
+# code only (argument validation, launch shapes, the launch record); the device code is
+# compiled as usual and nothing of it is instrumented.
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address",
+                 "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer"]
+CLANG = os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "llvm", "bin", "clang")
+
 
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + [os.path.join(CSRC, "q4_abi.cpp")]
@@ -60,35 +69,37 @@ def _run(cmd):
     return res.returncode, res.stdout + res.stderr
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every kernel and the C ABI into one shared library (always rebuilds).
-
-    Each source compiles to its own object in parallel (the group-size instantiations of
-    the decode tile kernel live in separate files for this), then one link."""
+def _compile_link(flags, link_flags, out, verbose=False, probe=True):
+    """Compile every source to its own object in parallel (the group-size instantiations
+    of the decode tile kernel live in separate files for this), then one link into out;
+    with probe, the read probe library is built in the same pool."""
     from concurrent.futures import ThreadPoolExecutor
 
     objdir = os.path.join(PKG, "_build_obj")
     os.makedirs(objdir, exist_ok=True)
     srcs = sources()
-    objs = [os.path.join(objdir, os.path.basename(src) + ".%d.o" % os.getpid()) for src in srcs]
+    tag = "%d.%s" % (os.getpid(), os.path.basename(out))
+    objs = [os.path.join(objdir, os.path.basename(src) + ".%s.o" % tag) for src in srcs]
     digest = f'-DQ4_SOURCE_DIGEST="{source_digest()}"'
-    cmds = [[HIPCC, *FLAGS, digest, "-c", "-I", INCLUDE, "-I", CSRC, src, "-o", obj] for src, obj in zip(srcs, objs)]
+    cmds = [[HIPCC, *flags, digest, "-c", "-I", INCLUDE, "-I", CSRC, src, "-o", obj]
+            for src, obj in zip(srcs, objs)]
     probe_tmp = PROBE_LIBRARY + ".tmp%d" % os.getpid()
-    cmds.append([HIPCC, *FLAGS, *LINK_FLAGS[1:], PROBE_SOURCE, "-o", probe_tmp])
+    if probe:
+        cmds.append([HIPCC, *FLAGS, *LINK_FLAGS[1:], PROBE_SOURCE, "-o", probe_tmp])
     workers = max(1, min(len(cmds), os.cpu_count() or 1, 16))
     with ThreadPoolExecutor(max_workers=workers) as pool:
         results = list(pool.map(_run, cmds))
     logs = []
+    tmp = out + ".tmp%d" % os.getpid()
     try:
-        for src, (rc, out) in zip(srcs + [PROBE_SOURCE], results):
+        for src, (rc, text) in zip(srcs + [PROBE_SOURCE], results):
             if rc != 0:
-                raise RuntimeError("hipcc failed on %s:\n%s" % (os.path.basename(src), out))
-            logs.append(out)
-        tmp = LIBRARY + ".tmp%d" % os.getpid()
-        rc, out = _run([HIPCC, *LINK_FLAGS, *objs, "-o", tmp])
+                raise RuntimeError("hipcc failed on %s:\n%s" % (os.path.basename(src), text))
+            logs.append(text)
+        rc, text = _run([HIPCC, *link_flags, *objs, "-o", tmp])
         if rc != 0:
-            raise RuntimeError("hipcc failed linking libq4:\n" + out)
-        logs.append(out)
+            raise RuntimeError("hipcc failed linking libq4:\n" + text)
+        logs.append(text)
     finally:
         for obj in objs:
             if os.path.exists(obj):
@@ -98,6 +109,34 @@ def build(verbose: bool = False) -> str:
         for line in "\n".join(logs).splitlines():
             if noise not in line:
                 print(line)
-    os.replace(tmp, LIBRARY)
-    os.replace(probe_tmp, PROBE_LIBRARY)
-    return LIBRARY
+    os.replace(tmp, out)
+    if probe:
+        os.replace(probe_tmp, PROBE_LIBRARY)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every kernel and the C ABI into one shared library (always rebuilds), and
+    the read probe beside it."""
+    return _compile_link(FLAGS, LINK_FLAGS, LIBRARY, verbose=verbose)
+
+
+def build_host_sanitized(out: str) -> str:
+    """libq4 with its host code under AddressSanitizer and UndefinedBehaviorSanitizer, for
+    exercising the C ABI on a CPU.  The process that loads it must have clang's ASan
+    runtime loaded first (LD_PRELOAD=asan_runtime()); load it through the binding by
+    setting Q4_LIBRARY to out.  Carries the same source digest as build()."""
+    flags = [f for f in FLAGS if f != "-O3"] + ["-O1", "-g", *HOST_SANITIZE]
+    link = [*LINK_FLAGS, "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-shared-libsan"]
+    return _compile_link(flags, link, out, probe=False)
+
+
+def asan_runtime() -> str:
+    """Path of clang's shared ASan runtime (which also carries the UBSan handlers)."""
+    res = subprocess.run([CLANG, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                         capture_output=True, text=True, check=True)
+    path = res.stdout.strip()
+    if not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("clang's ASan runtime was not found: " + path)
+    return path

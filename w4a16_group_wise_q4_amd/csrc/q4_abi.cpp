@@ -470,6 +470,7 @@ const char* q4_status_str(q4_status s) {
     case Q4_ERR_ALIGN: return "pointer misaligned (w/x/qweight/w_out 16 B, zeros/y 4 B, scales 2 B)";
     case Q4_ERR_LAUNCH: return "kernel launch failed";
     case Q4_ERR_SCRATCH: return "sizes need more than the fixed scratch of the no-allocation entry point";
+    default: break;
     }
     return "unknown status";
 }
