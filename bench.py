@@ -264,28 +264,31 @@ def gptq_leg(q4, synthetic, torch, dev, tokens=2048):
     f = torch.randn((tokens, 8), generator=gen)
     b = torch.randn((k, 8), generator=gen) / 8 ** 0.5
     x = (torch.randn((tokens, k), generator=gen) + 1.5 * f @ b.T).to(torch.bfloat16).to(dev)
-    ws = torch.empty(q4.q4_gptq_workspace(n, k, g), dtype=torch.uint8, device=dev)
-    p = q4.q4_gptq_quantize(w, x, g, True, workspace=ws)
-    torch.cuda.synchronize()
-    kname = q4.q4_last_kernel()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 3
-    e0.record()
-    for _ in range(reps):
-        q4.q4_gptq_quantize(w, x, g, True, out=p, workspace=ws)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+    ws = torch.empty(q4.q4_gptq_act_order_workspace(n, k, g), dtype=torch.uint8, device=dev)
     # fp32 work: Hessian lower triangle, Cholesky, error-feedback updates
     flops = k * k * tokens + k ** 3 / 3 + n * k * k
     r = q4.q4_quantize_pack(w, g, True)
     xf = x.float()
     wf = w.float()
     err = lambda pk: float(((xf @ (wf - q4.q4_dequant(pk)).t()) ** 2).sum())
-    return {"workload": f"GPTQ of W [{n}x{k}] bf16, {tokens} calibration tokens, g{g} sym",
-            "kernel": kname, "ms": round(ms, 3), "tflops_fp32": round(flops / (ms * 1e-3) / 1e12, 2),
-            "frac_fp32_mfma": round(flops / (ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
-            "layer_error_vs_rtn": round(err(p) / err(r), 4)}
+    res = {"workload": f"GPTQ of W [{n}x{k}] bf16, {tokens} calibration tokens, g{g} sym"}
+    for key, act in (("natural_order", False), ("act_order", True)):
+        p = q4.q4_gptq_quantize(w, x, g, True, workspace=ws, act_order=act)
+        torch.cuda.synchronize()
+        kname = q4.q4_last_kernel()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 3
+        e0.record()
+        for _ in range(reps):
+            q4.q4_gptq_quantize(w, x, g, True, out=p, workspace=ws, act_order=act)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[key] = {"kernel": kname, "ms": round(ms, 3),
+                    "tflops_fp32": round(flops / (ms * 1e-3) / 1e12, 2),
+                    "frac_fp32_mfma": round(flops / (ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
+                    "layer_error_vs_rtn": round(err(p) / err(r), 4)}
+    return res
 
 
 def cpu_model():

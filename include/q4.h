@@ -279,7 +279,8 @@ int64_t q4_kv_attention_noalloc_max_bytes(void);
  *     before the sweep, "static groups"; the format's groups are g consecutive columns);
  *   - H's diagonal is scaled by 1 + damp (the pages use damp = 0.01); a zero diagonal entry
  *     (a feature never active) becomes 1 first; 0 < damp <= 1;
- *   - columns are taken in order; column j is quantized at w_j + sum_{i<j} d_i U_ij / U_jj,
+ *   - columns are taken in natural order (q4_gptq_quantize_act_order below takes them by
+ *     activation energy); column j is quantized at w_j + sum_{i<j} d_i U_ij / U_jj,
  *     d_i = w_i - w_hat_i, H = U U^T with U upper triangular: the pages' update
  *     err_j = (w'_j - w_hat_j) / L_jj, w'_l -= err_j L_jl with H^-1 = L^T L, without the
  *     inverse.
@@ -293,6 +294,23 @@ q4_status q4_gptq_quantize(const void* w, q4_dtype w_dtype, int64_t n, int64_t k
                            q4_dtype x_dtype, int64_t tokens, int32_t group_size, int32_t symmetric,
                            float damp, uint32_t* qweight, uint16_t* scales, uint32_t* zeros,
                            void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/* GPTQ with act-order ([QA1] GPTQ chapter, §설정 grid: the columns whose activations have
+ * the largest |X|^2 are quantized first, so less error accumulates on them): as
+ * q4_gptq_quantize, but the sweep takes the columns by descending energy
+ * e_i = sum_t x_ti^2 (fp32, summed over slices of 32 tokens and then across slices; equal
+ * energies by the lower column index; a feature never active comes last).  Every column
+ * keeps its own group's scale and zero point (the static RTN quantizers), so the output
+ * format and its group layout are unchanged; only the order in which codes are chosen and
+ * errors carried differs.  workspace: at least q4_gptq_act_order_workspace(n, k, group_size)
+ * bytes (the q4_gptq_workspace floats, 3*k more, and n*k bytes of codes).  Other arguments,
+ * rules and errors as q4_gptq_quantize.  About 5k/64 + 6 kernels on `stream`. */
+int64_t q4_gptq_act_order_workspace(int64_t n, int64_t k, int32_t group_size);
+q4_status q4_gptq_quantize_act_order(const void* w, q4_dtype w_dtype, int64_t n, int64_t k,
+                                     const void* x, q4_dtype x_dtype, int64_t tokens,
+                                     int32_t group_size, int32_t symmetric, float damp,
+                                     uint32_t* qweight, uint16_t* scales, uint32_t* zeros,
+                                     void* workspace, int64_t workspace_bytes, hipStream_t stream);
 
 /* Element counts of the three packed arrays (payload + metadata, [FL7] §Memory 계산은
  * Payload와 Metadata로 나눈다): n*k/8 words, n*(k/g) scales, n*ceil((k/g)/8) words.

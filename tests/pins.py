@@ -722,6 +722,91 @@ def check_gptq_lowers_layer_error(gq, o):
         assert eg < 0.9 * er, (sym, eg, er)
 
 
+def check_gptq_act_order_hand_worked(gq, o):
+    """Act-order by hand: column energies sum_t x_ti^2 = [4, 2, 0, 4, 2, 9] sort to the
+    order [5, 0, 3, 1, 4, 2] (largest first, equal energies by the lower index, the
+    never-active column last); energies all equal give the natural order."""
+    x = np.array([[2, 1, 0, 2, 1, 3], [0, 1, 0, 0, 1, 0]], dtype=np.float32)
+    assert gq.act_order(x).tolist() == [5, 0, 3, 1, 4, 2]
+    signs = np.where(np.random.default_rng(70).random((16, 40)) < 0.5, -1.0, 1.0)
+    assert gq.act_order(signs.astype(np.float32)).tolist() == list(range(40))
+
+
+def _upper_factor_sweep(w64, h, s, z, g, order):
+    """The sweep in the upper-factor form (no inverse) over the columns in ``order``:
+    with Hp = h[order][:, order] = U U^T (U upper), the column at position p is quantized
+    at w_p + sum_{i<p} d_i U_ip / U_pp with its own group's quantizer; codes are returned in
+    column order."""
+    n, k = w64.shape
+    hp = h[np.ix_(order, order)]
+    U = np.linalg.cholesky(hp[::-1, ::-1])[::-1, ::-1]
+    wp = w64[:, order]
+    codes = np.zeros((n, k), dtype=np.int64)
+    d = np.zeros((n, k))
+    for p in range(k):
+        gi = order[p] // g
+        v = wp[:, p] + (d[:, :p] @ U[:p, p]) / U[p, p]
+        u = np.clip(np.rint(v / s[:, gi]) + z[:, gi], 0, 15)
+        codes[:, order[p]] = u
+        d[:, p] = wp[:, p] - s[:, gi] * (u - z[:, gi])
+    return codes
+
+
+def check_gptq_act_order_upper_factor(gq, o):
+    """Act-order against the independent upper-factor formulation run in the act-order
+    sequence: the codes must be equal; the sequence crosses groups, and the result differs
+    from the natural-order sweep."""
+    n, k, g = 12, 128, 32
+    x = _gptq_x(71, 400, k)
+    x *= np.linspace(0.3, 3.0, k, dtype=np.float32)[::-1][np.random.default_rng(72).permutation(k)]
+    h = gq.hessian(x)
+    order = gq.act_order(x)
+    assert (np.asarray(order) // g != np.arange(k) // g).any()
+    w = random_weights(73, n, k)
+    qa, sa, za = gq.gptq_quantize(w, h, g, False, oracle=o, order=order)
+    qn, _, _ = gq.gptq_quantize(w, h, g, False, oracle=o)
+    codes = _upper_factor_sweep(w.astype(np.float64), h, f16_values(sa), unpack_zeros(za, k // g),
+                                g, np.asarray(order))
+    assert np.array_equal(unpack_codes(qa, k), codes)
+    assert not np.array_equal(qa, qn)
+
+
+def check_gptq_act_order_permutation_invariance(gq, o):
+    """Permuting the input features within their groups (W's columns, X's columns, H's
+    rows and columns) permutes act-order's codes the same way, bit for bit: the sweep
+    order follows the energies, not the positions.  (The natural order has no such
+    property.)"""
+    n, k, g = 12, 256, 64
+    x = _gptq_x(74, 500, k)
+    w = random_weights(75, n, k)
+    rng = np.random.default_rng(76)
+    pi = np.concatenate([j * g + rng.permutation(g) for j in range(k // g)])
+    h = gq.hessian(x)
+    e = np.sum(x.astype(np.float64) ** 2, axis=0)
+    assert len(np.unique(e)) == k
+    for sym in (False, True):
+        q1, s1, z1 = gq.gptq_quantize(w, h, g, sym, oracle=o, order=gq.act_order(x))
+        q2, s2, z2 = gq.gptq_quantize(np.ascontiguousarray(w[:, pi]), h[np.ix_(pi, pi)], g, sym,
+                                      oracle=o, order=gq.act_order(x[:, pi]))
+        assert np.array_equal(unpack_codes(q1, k)[:, pi], unpack_codes(q2, k)), sym
+        assert np.array_equal(s1, s2)
+
+
+def check_gptq_act_order_lowers_layer_error(gq, o):
+    """With act-order the layer-output error is still below RTN's."""
+    k, g = 256, 64
+    x = _gptq_x(77, 1000, k) * np.geomspace(0.1, 10, 256, dtype=np.float32)
+    h = gq.hessian(x)
+    w = random_weights(78, 24, k)[12:]
+    qa, sa, za = gq.gptq_quantize(w, h, g, True, oracle=o, order=gq.act_order(x))
+    qr, sr, zr = o.quantize_pack(w, g, True)
+    ea = gq.layer_error(w, o.dequant(qa, sa, za, 12, k, g, True), x)
+    er = gq.layer_error(w, o.dequant(qr, sr, zr, 12, k, g, True), x)
+    assert ea < 0.9 * er, (ea, er)
+
+
 GPTQ_CHECKS = [check_gptq_hessian, check_gptq_identity_is_rtn, check_gptq_pair_closed_form,
                check_gptq_block_and_scale_invariance, check_gptq_upper_factor_form,
-               check_gptq_lowers_layer_error]
+               check_gptq_lowers_layer_error, check_gptq_act_order_hand_worked,
+               check_gptq_act_order_upper_factor, check_gptq_act_order_permutation_invariance,
+               check_gptq_act_order_lowers_layer_error]

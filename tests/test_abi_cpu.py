@@ -325,8 +325,9 @@ def test_kv_attention_workspace_size():
 
 
 def _gq(w=A16, wd=BF16, n=16, k=256, x=A16, xd=BF16, tokens=64, g=128, sym=0, damp=0.01, qw=A16, sc=A16,
-        zr=A16, ws=A16, ws_bytes=1 << 40):
-    return q4.lib().q4_gptq_quantize(w, wd, n, k, x, xd, tokens, g, sym, damp, qw, sc, zr, ws, ws_bytes, None)
+        zr=A16, ws=A16, ws_bytes=1 << 40, act_order=False):
+    entry = q4.lib().q4_gptq_quantize_act_order if act_order else q4.lib().q4_gptq_quantize
+    return entry(w, wd, n, k, x, xd, tokens, g, sym, damp, qw, sc, zr, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("call,code", [
@@ -342,8 +343,24 @@ def test_gptq_validation_rejects_before_launch(call, code):
     assert q4.q4_last_kernel() == ""
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(g=16), GROUP), (dict(k=200), SHAPE), (dict(tokens=0), SHAPE), (dict(damp=0.0), SHAPE),
+    (dict(xd=F32), DTYPE), (dict(x=None), NULL), (dict(ws=A16 + 4), ALIGN),
+    (dict(n=16, k=256, ws_bytes=4 * (256 * 256 + 16 * 256 + 256 * 16)), SHAPE),
+])
+def test_gptq_act_order_validation(kw, code):
+    """The act-order entry point shares the rules, and needs its larger workspace: the
+    natural-order size is refused."""
+    assert _gq(act_order=True, **kw) == code
+    assert q4.q4_last_kernel() == ""
+
+
 def test_gptq_workspace_size():
     lib = q4.lib()
     assert lib.q4_gptq_workspace(11008, 4096, 128) == 4 * (4096 * 4096 + 11008 * 4096 + 256 * 11008)
     assert lib.q4_gptq_workspace(16, 200, 32) == -1
     assert lib.q4_gptq_workspace(16, 32768 + 128, 128) == -1
+    n, k = 11008, 4096
+    assert lib.q4_gptq_act_order_workspace(n, k, 128) == (lib.q4_gptq_workspace(n, k, 128)
+                                                           + 4 * 3 * k + n * k)
+    assert lib.q4_gptq_act_order_workspace(16, 200, 32) == -1

@@ -25,6 +25,14 @@ MUTANTS = [
     ("floor_rounding", "np.rint(W[:, j] / s[:, gj])", "np.floor(W[:, j] / s[:, gj])"),
     ("hessian_not_doubled", "h = 2.0 * (x64.T @ x64)", "h = x64.T @ x64"),
     ("update_from_quantized", "err = (W[:, j] - w_hat) / L[j, j]", "err = (wf[:, j] - w_hat) / L[j, j]"),
+    ("act_order_ascending", 'np.argsort(-energy, kind="stable")', 'np.argsort(energy, kind="stable")'),
+    ("act_order_ties_by_higher_index", 'np.argsort(-energy, kind="stable")',
+     'np.lexsort((-np.arange(energy.size), -energy))'),
+    ("act_order_group_of_position", "gj = order[j] // g", "gj = j // g"),
+    ("act_order_codes_not_placed", "placed[:, order] = codes", "placed[:, :] = codes"),
+    ("act_order_hessian_not_permuted", "h = np.asarray(h, dtype=np.float64)[np.ix_(order, order)]",
+     "h = np.asarray(h, dtype=np.float64)"),
+    ("act_order_energy_abs", "energy = np.sum(x64 * x64, axis=0)", "energy = np.sum(np.abs(x64), axis=0)"),
 ]
 
 

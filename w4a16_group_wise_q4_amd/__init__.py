@@ -12,7 +12,8 @@ Entry points (same names as the C ABI):
     q4_w4a16_gemm_grouped(xs, packs)                    -> [y_i], one launch when m <= 16
     q4_kv_quantize(kv, cache, t0)                       -> appends tokens to a KvCache
     q4_kv_attention(q, kcache, vcache, n_tok, scale)    -> out [heads, d] fp32
-    q4_gptq_quantize(w, x, group_size, symmetric)       -> PackedWeight (GPTQ codes)
+    q4_gptq_quantize(w, x, group_size, symmetric)       -> PackedWeight (GPTQ codes;
+                                                           act_order=True for act-order)
     q4_last_kernel()                                    -> name of the last kernel run
 """
 from __future__ import annotations
@@ -33,7 +34,7 @@ __all__ = ["PackedWeight", "q4_quantize_pack", "q4_quantize_pack_grouped", "q4_q
            "q4_source_digest", "StaleLibraryError", "KvCache", "empty_kv_cache",
            "q4_kv_quantize", "q4_kv_attention", "q4_kv_attention_workspace",
            "q4_kv_attention_noalloc",
-           "q4_gptq_quantize", "q4_gptq_workspace",
+           "q4_gptq_quantize", "q4_gptq_workspace", "q4_gptq_act_order_workspace",
            "q4_qweight_words", "q4_scale_count", "q4_zero_words", "q4_layout_version",
            "library_path", "Q4Error"]
 
@@ -45,7 +46,7 @@ EXPORTED = ("q4_quantize_pack", "q4_quantize_pack_grouped", "q4_quantize_pack_ms
             "q4_w4a16_gemm_grouped", "q4_w4a16_gemm_grouped_out", "q4_kv_quantize", "q4_kv_attention",
             "q4_kv_attention_workspace", "q4_kv_attention_noalloc",
             "q4_kv_attention_noalloc_max_bytes", "q4_gptq_quantize", "q4_gptq_workspace",
-            "q4_qweight_words",
+            "q4_gptq_quantize_act_order", "q4_gptq_act_order_workspace", "q4_qweight_words",
             "q4_scale_count", "q4_zero_words", "q4_status_str", "q4_last_kernel",
             "q4_last_kernels", "q4_last_launch_count", "q4_layout_version", "q4_source_digest")
 
@@ -139,6 +140,10 @@ def _load():
     lib.q4_gptq_workspace.restype = i64
     lib.q4_gptq_quantize.argtypes = [vp, ctypes.c_int, i64, i64, vp, ctypes.c_int, i64, i32, i32,
                                      ctypes.c_float, vp, vp, vp, vp, i64, vp]
+    lib.q4_gptq_act_order_workspace.argtypes = [i64, i64, i32]
+    lib.q4_gptq_act_order_workspace.restype = i64
+    lib.q4_gptq_quantize_act_order.argtypes = lib.q4_gptq_quantize.argtypes
+    lib.q4_gptq_quantize_act_order.restype = ctypes.c_int
     lib.q4_gptq_quantize.restype = ctypes.c_int
     lib.q4_qweight_words.argtypes = [i64, i64]
     lib.q4_qweight_words.restype = i64
@@ -570,12 +575,19 @@ def q4_gptq_workspace(n: int, k: int, group_size: int) -> int:
     return int(_load().q4_gptq_workspace(n, k, group_size))
 
 
+def q4_gptq_act_order_workspace(n: int, k: int, group_size: int) -> int:
+    return int(_load().q4_gptq_act_order_workspace(n, k, group_size))
+
+
 def q4_gptq_quantize(w: torch.Tensor, x: torch.Tensor, group_size: int = 128,
                      symmetric: bool = False, damp: float = 0.01,
                      out: Optional[PackedWeight] = None,
-                     workspace: Optional[torch.Tensor] = None) -> PackedWeight:
+                     workspace: Optional[torch.Tensor] = None,
+                     act_order: bool = False) -> PackedWeight:
     """GPTQ-quantize W [n, k] (fp32 / fp16 / bf16) against calibration activations
-    x [tokens, k] (fp16 / bf16); same packed format, RTN's group scales and zero points."""
+    x [tokens, k] (fp16 / bf16); same packed format, RTN's group scales and zero points.
+    With ``act_order`` the columns are swept by descending activation energy
+    (q4_gptq_quantize_act_order)."""
     _need_cuda("w", w)
     _need_cuda("x", x, w.device)
     if w.dim() != 2 or w.dtype not in _DTYPE_CODE:
@@ -585,13 +597,13 @@ def q4_gptq_quantize(w: torch.Tensor, x: torch.Tensor, group_size: int = 128,
     n, k = w.shape
     p = out if out is not None else empty_packed(n, k, group_size, symmetric, w.device)
     _check_packed(p, w.device, n, k, group_size, bool(symmetric))
-    need = q4_gptq_workspace(n, k, group_size)
+    need = (q4_gptq_act_order_workspace if act_order else q4_gptq_workspace)(n, k, group_size)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=w.device)
     _need_workspace("workspace", workspace, w.device)
-    _check(_load().q4_gptq_quantize(_dev_ptr(w), _DTYPE_CODE[w.dtype], n, k, _dev_ptr(x),
-                                    _DTYPE_CODE[x.dtype], x.shape[0], group_size,
-                                    int(bool(symmetric)), float(damp), _dev_ptr(p.qweight),
-                                    _dev_ptr(p.scales), _dev_ptr(p.zeros), _dev_ptr(workspace),
-                                    workspace.numel() * workspace.element_size(), _stream(w)))
+    entry = _load().q4_gptq_quantize_act_order if act_order else _load().q4_gptq_quantize
+    _check(entry(_dev_ptr(w), _DTYPE_CODE[w.dtype], n, k, _dev_ptr(x), _DTYPE_CODE[x.dtype],
+                 x.shape[0], group_size, int(bool(symmetric)), float(damp), _dev_ptr(p.qweight),
+                 _dev_ptr(p.scales), _dev_ptr(p.zeros), _dev_ptr(workspace),
+                 workspace.numel() * workspace.element_size(), _stream(w)))
     return p

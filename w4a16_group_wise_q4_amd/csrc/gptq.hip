@@ -86,16 +86,32 @@ __device__ __forceinline__ float half_to_float(uint16_t h) {
 // token slice of a tile pair is staged once per 128 x 128 outputs).
 constexpr int HB = 128;
 
-template <bool XF16>
+// With PERM, position p of the sweep is feature perm[p] (act-order): the tile is the
+// Hessian of the permuted features, A[a][b] = H[perm[k-1-a]][perm[k-1-b]], gathered from
+// the activations one 16-bit value at a time.
+template <bool XF16, bool PERM>
 __global__ __launch_bounds__(256) void hessian_kernel(const uint16_t* __restrict__ x, int tokens, int k,
-                                                      float damp, float* __restrict__ A) {
+                                                      float damp, const int* __restrict__ perm,
+                                                      float* __restrict__ A) {
     const int tiles = (k + HB - 1) / HB;
     const int I = blockIdx.x / tiles, J = blockIdx.x % tiles;
     if (J > I) return;  // upper tiles: not needed (uniform)
     // token slice [t0, t0 + 64): Xs[s][a] = x[t0 + s][k-1-(128 I + a)], Ys likewise for J
     __shared__ __attribute__((aligned(16))) float Xs[NB][HB], Ys[NB][HB];
+    __shared__ int pX[PERM ? HB : 1], pY[PERM ? HB : 1];  // features of this tile's positions
     const int t = threadIdx.x;
     const int l = t & 63, w = t >> 6, h = l >> 5, li = l & 31;
+    if constexpr (PERM) {
+        // position k-1-(HB I + a) holds feature pX[a] (0 past the last position)
+        if (t < HB) {
+            const int pa = k - 1 - (HB * I + t);
+            pX[t] = pa >= 0 ? perm[pa] : 0;
+        } else {
+            const int pb = k - 1 - (HB * J + (t - HB));
+            pY[t - HB] = pb >= 0 ? perm[pb] : 0;
+        }
+        __syncthreads();
+    }
     const int rb = 64 * (w >> 1), cb = 64 * (w & 1);
     f32x16 acc[2][2] = {};
     // This thread's 16 feature pairs of a slice (one 32-bit word each: features a and a+1
@@ -111,8 +127,15 @@ __global__ __launch_bounds__(256) void hessian_kernel(const uint16_t* __restrict
             const int e = t + 256 * r, s = e / (HB / 2), a = 2 * (e % (HB / 2));
             const int tok = t0 + s;
             const int fa = k - 1 - (HB * I + a), fb = k - 1 - (HB * J + a);
-            xr[r] = tok < tokens && fa >= 0 ? x32[((int64_t)tok * k + fa - 1) / 2] : 0u;
-            yr[r] = tok < tokens && fb >= 0 ? x32[((int64_t)tok * k + fb - 1) / 2] : 0u;
+            if constexpr (PERM) {
+                // positions fa and fa - 1 (fa is odd) are pX[a] and pX[a + 1]
+                const uint16_t* xt = x + (int64_t)tok * k;
+                xr[r] = tok < tokens && fa >= 0 ? ((uint32_t)xt[pX[a]] << 16) | (uint32_t)xt[pX[a + 1]] : 0u;
+                yr[r] = tok < tokens && fb >= 0 ? ((uint32_t)xt[pY[a]] << 16) | (uint32_t)xt[pY[a + 1]] : 0u;
+            } else {
+                xr[r] = tok < tokens && fa >= 0 ? x32[((int64_t)tok * k + fa - 1) / 2] : 0u;
+                yr[r] = tok < tokens && fb >= 0 ? x32[((int64_t)tok * k + fb - 1) / 2] : 0u;
+            }
         }
     };
     fetch(0);
@@ -298,6 +321,77 @@ __global__ void fill_zero_kernel(float* __restrict__ p, int64_t count) {
         p[i] = 0.f;
 }
 
+// ------------------------------------------------------------ act-order
+// The sweep order of act-order ("Quantization Algorithms 단권화", GPTQ chapter, §설정 grid:
+// the columns whose activations carry the most energy first): features by descending
+// e_i = sum_t x_ti^2, equal energies by the lower index.
+//
+// Energies in two passes with a fixed summation order: slice s of `slice` tokens sums
+// sequentially into part[s][i] (one lane per feature, a wave per 64 features and slice),
+// then key[i] = sum_s part[s][i] in order of s.
+template <bool XF16>
+__global__ __launch_bounds__(64) void energy_kernel(const uint16_t* __restrict__ x, int tokens, int k, int slice,
+                                                    float* __restrict__ part) {
+    const int i = (int)blockIdx.x * 64 + (int)threadIdx.x;
+    const int s = (int)blockIdx.y;
+    if (i >= k) return;
+    const int t0 = s * slice, t1 = tokens - t0 < slice ? tokens : t0 + slice;
+    float acc = 0.f;
+    for (int t = t0; t < t1; ++t) {
+        const float v = half_to_float<XF16>(x[(int64_t)t * k + i]);
+        acc = acc + v * v;
+    }
+    part[(int64_t)s * k + i] = acc;
+}
+
+__global__ void energy_sum_kernel(const float* __restrict__ part, int slices, int k, float* __restrict__ key,
+                                  int* __restrict__ rank) {
+    const int i = (int)blockIdx.x * blockDim.x + (int)threadIdx.x;
+    if (i >= k) return;
+    float acc = 0.f;
+    for (int s = 0; s < slices; ++s) acc = acc + part[(int64_t)s * k + i];
+    key[i] = acc;
+    rank[i] = 0;
+}
+
+// rank[i] += #{j in this block's chunk of 1024 : e_j > e_i, or e_j == e_i and j < i}.
+// The energies are compared as their bit patterns: for non-negative floats that is their
+// order, and it stays a strict total order (with the index) whatever the values, so the
+// ranks are a permutation.  Integer counts: the order of the atomic additions is immaterial.
+__global__ __launch_bounds__(256) void rank_kernel(const float* __restrict__ key, int k, int* __restrict__ rank) {
+    __shared__ uint32_t kb[1024];
+    const int i = (int)blockIdx.x * 256 + (int)threadIdx.x;
+    const int c0 = (int)blockIdx.y * 1024;
+    const int cn = k - c0 < 1024 ? k - c0 : 1024;
+    for (int e = threadIdx.x; e < cn; e += 256) kb[e] = __builtin_bit_cast(uint32_t, key[c0 + e]);
+    __syncthreads();
+    if (i >= k) return;
+    const uint32_t mine = __builtin_bit_cast(uint32_t, key[i]);
+    int cnt = 0;
+    for (int e = 0; e < cn; ++e) {
+        const uint32_t o = kb[e];
+        cnt += (o > mine) | ((o == mine) & (c0 + e < i));
+    }
+    if (cnt) atomicAdd(rank + i, cnt);
+}
+
+__global__ void scatter_order_kernel(const int* __restrict__ rank, int k, int* __restrict__ perm) {
+    const int i = (int)blockIdx.x * blockDim.x + (int)threadIdx.x;
+    if (i < k) perm[rank[i]] = i;
+}
+
+// qweight[r][c / 8] from the byte codes codes[r][c] (column order), eight per word.
+__global__ void pack_codes_kernel(const uint8_t* __restrict__ codes, int64_t words, uint32_t* __restrict__ qweight) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const uint64_t c = reinterpret_cast<const uint64_t*>(codes)[i];
+        uint32_t wv = 0u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wv |= (uint32_t)((c >> (8 * e)) & 0xFu) << (4 * e);
+        qweight[i] = wv;
+    }
+}
+
 template <int DT>
 __device__ __forceinline__ float load_w(const void* w, int64_t idx) {
     if constexpr (DT == 0) return reinterpret_cast<const float*>(w)[idx];
@@ -329,13 +423,18 @@ __device__ __forceinline__ float quad_sum(float v) {
     return v + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));  // lane ^ 2
 }
 
-template <int DT, bool SYM>
+//
+// With PERM (act-order) position j0 + j is column perm[j0 + j]: its weight and its group's
+// scale and zero point are gathered per column (lane q holds those of its 16 columns, like
+// C), and its code goes to byte codes[row][perm[j0 + j]]; pack_codes_kernel packs them.
+template <int DT, bool SYM, bool PERM>
 __global__ __launch_bounds__(256) void sweep_kernel(const void* __restrict__ w, int n, int k, int g,
                                                     const float* __restrict__ A, const float* __restrict__ C,
                                                     const uint16_t* __restrict__ scales,
                                                     const uint32_t* __restrict__ zeros,
                                                     uint32_t* __restrict__ qweight, float* __restrict__ Dout,
-                                                    int j0, int bw) {
+                                                    int j0, int bw, const int* __restrict__ perm,
+                                                    uint8_t* __restrict__ codes) {
     __shared__ float UT[NB][NB + 1];  // UT[j][i] = U_ij (i <= j), zero elsewhere
     __shared__ float rU[NB];          // 1 / U_jj
     const int t = threadIdx.x;
@@ -361,7 +460,20 @@ __global__ __launch_bounds__(256) void sweep_kernel(const void* __restrict__ w, 
 #pragma unroll
         for (int e = 0; e < 4; ++e) cv[4 * v + e] = x[e];
     }
-    if constexpr (DT == 0) {
+    // act-order: the fp16 scale (low half) and zero point (bits 16..19) of each column
+    uint32_t szv[PERM ? 16 : 1];
+    if constexpr (PERM) {
+        const int n_groups_ = k / g, zwords_ = (n_groups_ + 7) / 8;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const bool in = c0 + e < bw;
+            const int col = in ? perm[j0 + c0 + e] : 0;
+            const int gi = col / g;
+            wv[e] = in ? load_w<DT>(w, (int64_t)row * k + col) : 0.f;
+            const uint32_t zc = SYM ? 8u : (zeros[(int64_t)row * zwords_ + gi / 8] >> (4 * (gi % 8))) & 0xFu;
+            szv[e] = (uint32_t)scales[(int64_t)row * n_groups_ + gi] | (zc << 16);
+        }
+    } else if constexpr (DT == 0) {
         const float* wrow = reinterpret_cast<const float*>(w) + (int64_t)row * k + j0 + c0;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
@@ -386,6 +498,9 @@ __global__ __launch_bounds__(256) void sweep_kernel(const void* __restrict__ w, 
     uint32_t words[NB / 8];
 #pragma unroll
     for (int m = 0; m < NB / 8; ++m) words[m] = 0u;
+    uint32_t cu[PERM ? 16 : 1];  // codes of this lane's 16 columns (act-order)
+#pragma unroll
+    for (int e = 0; e < (PERM ? 16 : 1); ++e) cu[e] = 0u;
     // The column loop is a serial chain: the divisions by U_jj and by the scale are
     // multiplications by reciprocals taken once per block and once per group, and the
     // lane's share of each dot product runs in two interleaved sums.
@@ -393,11 +508,18 @@ __global__ __launch_bounds__(256) void sweep_kernel(const void* __restrict__ w, 
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
         if (j < bw) {
-            const int col = j0 + j, gi = col / g;
-            if (j == 0 || col % g == 0) {  // a new group (uniform)
-                S = (float)__builtin_bit_cast(_Float16, scales[(int64_t)row * n_groups + gi]);
+            if constexpr (PERM) {
+                const uint32_t sz = __builtin_bit_cast(uint32_t, quad_bcast(__builtin_bit_cast(float, szv[j % 16]), j / 16));
+                S = (float)__builtin_bit_cast(_Float16, (uint16_t)(sz & 0xFFFFu));
                 rS = 1.0f / S;
-                if constexpr (!SYM) z = (float)((zeros[(int64_t)row * zwords + gi / 8] >> (4 * (gi % 8))) & 0xFu);
+                z = (float)(sz >> 16);
+            } else {
+                const int col = j0 + j, gi = col / g;
+                if (j == 0 || col % g == 0) {  // a new group (uniform)
+                    S = (float)__builtin_bit_cast(_Float16, scales[(int64_t)row * n_groups + gi]);
+                    rS = 1.0f / S;
+                    if constexpr (!SYM) z = (float)((zeros[(int64_t)row * zwords + gi / 8] >> (4 * (gi % 8))) & 0xFu);
+                }
             }
             const float cj = quad_bcast(cv[j % 16], j / 16);
             const float wj = quad_bcast(wv[j % 16], j / 16);
@@ -413,13 +535,22 @@ __global__ __launch_bounds__(256) void sweep_kernel(const void* __restrict__ w, 
             const float u = fminf(fmaxf(rintf(wp * rS) + z, 0.f), 15.f);
             const float dj = wj - S * (u - z);
             dl[j / 4] = q == (j & 3) ? dj : dl[j / 4];
-            words[j / 8] |= (uint32_t)u << (4 * (j % 8));
+            if constexpr (PERM) cu[j % 16] = q == j / 16 ? (uint32_t)u : cu[j % 16];
+            else words[j / 8] |= (uint32_t)u << (4 * (j % 8));
         }
     }
-    // lane q stores code words 2q, 2q+1 (columns 16q .. 16q+15) and its own errors
+    if constexpr (PERM) {
+        // lane q stores the codes of its 16 columns at their own positions
 #pragma unroll
-    for (int m = 0; m < NB / 8; ++m)
-        if (m / 2 == q && 8 * m < bw) qweight[(int64_t)row * (k / 8) + j0 / 8 + m] = words[m];
+        for (int e = 0; e < 16; ++e)
+            if (c0 + e < bw) codes[(int64_t)row * k + perm[j0 + c0 + e]] = (uint8_t)cu[e];
+    } else {
+        // lane q stores code words 2q, 2q+1 (columns 16q .. 16q+15)
+#pragma unroll
+        for (int m = 0; m < NB / 8; ++m)
+            if (m / 2 == q && 8 * m < bw) qweight[(int64_t)row * (k / 8) + j0 / 8 + m] = words[m];
+    }
+    // and its own errors
 #pragma unroll
     for (int m = 0; m < NB / 4; ++m)
         if (4 * m + q < bw) Dout[(int64_t)(4 * m + q) * n + row] = dl[m];
@@ -488,16 +619,17 @@ void update(const float* A, const float* D, float* C, int n, int k, int j0, int 
 // errors; after a super-block, every column beyond it takes the errors of all its blocks
 // in one update with an inner size of SB.  The accumulator traffic falls by about SB / 64
 // against updating every later column after every block; the sums are the same.
-template <int DT, bool SYM>
+template <int DT, bool SYM, bool PERM>
 hipError_t sweep_all(const void* w, int n, int k, int g, const float* A, float* C, const uint16_t* sc,
-                     const uint32_t* zr, uint32_t* qw, float* D, hipStream_t st) {
+                     const uint32_t* zr, uint32_t* qw, float* D, const int* perm, uint8_t* codes,
+                     hipStream_t st) {
     for (int s0 = 0; s0 < k; s0 += SB) {
         const int s1 = k - s0 < SB ? k : s0 + SB;
         for (int j0 = s0; j0 < s1; j0 += NB) {
             const int bw = s1 - j0 < NB ? s1 - j0 : NB;
             float* Db = D + (int64_t)(j0 - s0) * n;  // this block's rows of the super-block's errors
-            hipLaunchKernelGGL((sweep_kernel<DT, SYM>), dim3((n + 63) / 64), dim3(256), 0, st, w, n, k, g, A, C, sc,
-                               zr, qw, Db, j0, bw);
+            hipLaunchKernelGGL((sweep_kernel<DT, SYM, PERM>), dim3((n + 63) / 64), dim3(256), 0, st, w, n, k, g, A,
+                               C, sc, zr, qw, Db, j0, bw, perm, codes);
             q4k_record("q4_gptq_sweep");
             update(A, Db, C, n, k, j0, bw, j0 + bw, s1, st);   // the rest of the super-block
         }
@@ -506,29 +638,81 @@ hipError_t sweep_all(const void* w, int n, int k, int g, const float* A, float* 
     return hipGetLastError();
 }
 
+template <bool PERM>
+hipError_t sweep_dispatch(int w_dtype, int sym, const void* w, int n, int k, int g, const float* A, float* C,
+                          const uint16_t* sc, const uint32_t* zr, uint32_t* qw, float* D, const int* perm,
+                          uint8_t* codes, hipStream_t st) {
+    switch (w_dtype * 2 + (sym ? 1 : 0)) {
+    case 0: return sweep_all<0, false, PERM>(w, n, k, g, A, C, sc, zr, qw, D, perm, codes, st);
+    case 1: return sweep_all<0, true, PERM>(w, n, k, g, A, C, sc, zr, qw, D, perm, codes, st);
+    case 2: return sweep_all<1, false, PERM>(w, n, k, g, A, C, sc, zr, qw, D, perm, codes, st);
+    case 3: return sweep_all<1, true, PERM>(w, n, k, g, A, C, sc, zr, qw, D, perm, codes, st);
+    case 4: return sweep_all<2, false, PERM>(w, n, k, g, A, C, sc, zr, qw, D, perm, codes, st);
+    default: return sweep_all<2, true, PERM>(w, n, k, g, A, C, sc, zr, qw, D, perm, codes, st);
+    }
+}
+
+// Tokens per energy slice: 32, or more so that the slices' partial sums (one row of k per
+// slice) fit the k x k Hessian area they are staged in.
+int energy_slice(int64_t tokens, int64_t k) {
+    const int64_t per = (tokens + 31) / 32;
+    return (int)(32 * ((per + k - 1) / k));
+}
+
 }  // namespace
 
 int64_t q4k_gptq_workspace_floats(int64_t n, int64_t k) {
     return k * k + n * k + n * SB;  // A, C, D
 }
 
+int64_t q4k_gptq_act_order_workspace_floats(int64_t n, int64_t k) {
+    // then the energies, the ranks, the order, and n x k byte codes
+    return q4k_gptq_workspace_floats(n, k) + 3 * k + n * k / 4;
+}
+
 hipError_t q4k_gptq(const void* w, int w_dtype, int64_t n, int64_t k, const void* x, int x_dtype,
                     int64_t tokens, int g, int sym, float damp, uint32_t* qweight, uint16_t* scales,
-                    uint32_t* zeros, float* workspace, hipStream_t st, const char** kname) {
+                    uint32_t* zeros, float* workspace, int act_order, hipStream_t st, const char** kname) {
     // 1. static group quantizers (and RTN codes, overwritten below)
     hipError_t e = q4k_quant_pack(w, w_dtype, n, k, g, sym, qweight, scales, zeros, st, kname);
     if (e != hipSuccess) return e;
     float* A = workspace;
     float* C = A + k * k;
     float* D = C + n * k;
+    float* key = D + n * SB;
+    int* rank = reinterpret_cast<int*>(key + k);
+    int* perm = act_order ? rank + k : nullptr;
+    uint8_t* codes = act_order ? reinterpret_cast<uint8_t*>(rank + 2 * k) : nullptr;
     const int ki = (int)k, ni = (int)n;
-    // 2. reversed Hessian, lower triangle
-    const int tiles = (ki + HB - 1) / HB;
     const uint16_t* xs = reinterpret_cast<const uint16_t*>(x);
-    if (x_dtype == 1)
-        hipLaunchKernelGGL(hessian_kernel<true>, dim3(tiles * tiles), dim3(256), 0, st, xs, (int)tokens, ki, damp, A);
+    // 1b. act-order: the sweep order from the activation energies (partials staged in A)
+    if (act_order) {
+        const int slice = energy_slice(tokens, k);
+        const int slices = (int)((tokens + slice - 1) / slice);
+        const dim3 eg((unsigned)((ki + 63) / 64), (unsigned)slices);
+        if (x_dtype == 1)
+            hipLaunchKernelGGL(energy_kernel<true>, eg, dim3(64), 0, st, xs, (int)tokens, ki, slice, A);
+        else
+            hipLaunchKernelGGL(energy_kernel<false>, eg, dim3(64), 0, st, xs, (int)tokens, ki, slice, A);
+        hipLaunchKernelGGL(energy_sum_kernel, dim3((ki + 255) / 256), dim3(256), 0, st, A, slices, ki, key, rank);
+        hipLaunchKernelGGL(rank_kernel, dim3((ki + 255) / 256, (ki + 1023) / 1024), dim3(256), 0, st, key, ki, rank);
+        hipLaunchKernelGGL(scatter_order_kernel, dim3((ki + 255) / 256), dim3(256), 0, st, rank, ki, perm);
+        q4k_record("q4_gptq_energy");
+        q4k_record("q4_gptq_energy_sum");
+        q4k_record("q4_gptq_rank");
+        q4k_record("q4_gptq_order");
+    }
+    // 2. reversed Hessian, lower triangle (of the permuted features with act-order)
+    const int tiles = (ki + HB - 1) / HB;
+    const dim3 hg(tiles * tiles);
+    if (x_dtype == 1 && act_order)
+        hipLaunchKernelGGL((hessian_kernel<true, true>), hg, dim3(256), 0, st, xs, (int)tokens, ki, damp, perm, A);
+    else if (x_dtype == 1)
+        hipLaunchKernelGGL((hessian_kernel<true, false>), hg, dim3(256), 0, st, xs, (int)tokens, ki, damp, perm, A);
+    else if (act_order)
+        hipLaunchKernelGGL((hessian_kernel<false, true>), hg, dim3(256), 0, st, xs, (int)tokens, ki, damp, perm, A);
     else
-        hipLaunchKernelGGL(hessian_kernel<false>, dim3(tiles * tiles), dim3(256), 0, st, xs, (int)tokens, ki, damp, A);
+        hipLaunchKernelGGL((hessian_kernel<false, false>), hg, dim3(256), 0, st, xs, (int)tokens, ki, damp, perm, A);
     q4k_record("q4_gptq_hessian");
     // 3. Cholesky in place
     for (int j0 = 0; j0 < ki; j0 += NB) {
@@ -547,15 +731,19 @@ hipError_t q4k_gptq(const void* w, int w_dtype, int64_t n, int64_t k, const void
     // 4. sweep
     hipLaunchKernelGGL(fill_zero_kernel, dim3(1024), dim3(256), 0, st, C, n * k);
     q4k_record("q4_gptq_fill_zero");
-    switch (w_dtype * 2 + (sym ? 1 : 0)) {
-    case 0: e = sweep_all<0, false>(w, ni, ki, g, A, C, scales, zeros, qweight, D, st); break;
-    case 1: e = sweep_all<0, true>(w, ni, ki, g, A, C, scales, zeros, qweight, D, st); break;
-    case 2: e = sweep_all<1, false>(w, ni, ki, g, A, C, scales, zeros, qweight, D, st); break;
-    case 3: e = sweep_all<1, true>(w, ni, ki, g, A, C, scales, zeros, qweight, D, st); break;
-    case 4: e = sweep_all<2, false>(w, ni, ki, g, A, C, scales, zeros, qweight, D, st); break;
-    default: e = sweep_all<2, true>(w, ni, ki, g, A, C, scales, zeros, qweight, D, st); break;
+    if (act_order) {
+        e = sweep_dispatch<true>(w_dtype, sym, w, ni, ki, g, A, C, scales, zeros, qweight, D, perm, codes, st);
+        if (e != hipSuccess) return e;
+        const int64_t words = n * k / 8;
+        hipLaunchKernelGGL(pack_codes_kernel, dim3((unsigned)((words + 255) / 256 < 4096 ? (words + 255) / 256 : 4096)),
+                           dim3(256), 0, st, codes, words, qweight);
+        q4k_record("q4_gptq_pack_codes");
+        e = hipGetLastError();
+    } else {
+        e = sweep_dispatch<false>(w_dtype, sym, w, ni, ki, g, A, C, scales, zeros, qweight, D, nullptr, nullptr, st);
     }
-    static const char* names[3] = {"q4_gptq_f32", "q4_gptq_f16", "q4_gptq_bf16"};
-    *kname = names[w_dtype];
+    static const char* names[2][3] = {{"q4_gptq_f32", "q4_gptq_f16", "q4_gptq_bf16"},
+                                      {"q4_gptq_act_order_f32", "q4_gptq_act_order_f16", "q4_gptq_act_order_bf16"}};
+    *kname = names[act_order ? 1 : 0][w_dtype];
     return e;
 }

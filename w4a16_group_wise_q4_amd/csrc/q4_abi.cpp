@@ -425,10 +425,16 @@ int64_t q4_gptq_workspace(int64_t n, int64_t k, int32_t group_size) {
     return q4k_gptq_workspace_floats(n, k) * (int64_t)sizeof(float);
 }
 
-q4_status q4_gptq_quantize(const void* w, q4_dtype w_dtype, int64_t n, int64_t k, const void* x,
-                           q4_dtype x_dtype, int64_t tokens, int32_t group_size, int32_t symmetric,
-                           float damp, uint32_t* qweight, uint16_t* scales, uint32_t* zeros,
-                           void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+int64_t q4_gptq_act_order_workspace(int64_t n, int64_t k, int32_t group_size) {
+    if (check_layout(n, k, group_size) != Q4_OK || k > kMaxGptqK) return -1;
+    return q4k_gptq_act_order_workspace_floats(n, k) * (int64_t)sizeof(float);
+}
+
+namespace {
+q4_status gptq_call(const void* w, q4_dtype w_dtype, int64_t n, int64_t k, const void* x,
+                    q4_dtype x_dtype, int64_t tokens, int32_t group_size, int32_t symmetric,
+                    float damp, uint32_t* qweight, uint16_t* scales, uint32_t* zeros,
+                    void* workspace, int64_t workspace_bytes, int act_order, hipStream_t stream) {
     begin_call();
     q4_status st = check_quant(w, w_dtype, n, k, group_size, symmetric, qweight, scales, zeros);
     if (st != Q4_OK) return st;
@@ -437,12 +443,32 @@ q4_status q4_gptq_quantize(const void* w, q4_dtype w_dtype, int64_t n, int64_t k
     if (x_dtype != Q4_F16 && x_dtype != Q4_BF16) return Q4_ERR_DTYPE;
     if (!x || !workspace) return Q4_ERR_NULL;
     if (!aligned(x, 16) || !aligned(workspace, 16)) return Q4_ERR_ALIGN;
-    if (workspace_bytes < q4_gptq_workspace(n, k, group_size)) return Q4_ERR_SHAPE;
+    const int64_t need = act_order ? q4_gptq_act_order_workspace(n, k, group_size)
+                                   : q4_gptq_workspace(n, k, group_size);
+    if (workspace_bytes < need) return Q4_ERR_SHAPE;
     const char* name = "";
     const hipError_t e = q4k_gptq(w, (int)w_dtype, n, k, x, (int)x_dtype, tokens, group_size,
                                   symmetric ? 1 : 0, damp, qweight, scales, symmetric ? nullptr : zeros,
-                                  static_cast<float*>(workspace), stream, &name);
+                                  static_cast<float*>(workspace), act_order, stream, &name);
     return finish(e, name);
+}
+}  // namespace
+
+q4_status q4_gptq_quantize(const void* w, q4_dtype w_dtype, int64_t n, int64_t k, const void* x,
+                           q4_dtype x_dtype, int64_t tokens, int32_t group_size, int32_t symmetric,
+                           float damp, uint32_t* qweight, uint16_t* scales, uint32_t* zeros,
+                           void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+    return gptq_call(w, w_dtype, n, k, x, x_dtype, tokens, group_size, symmetric, damp, qweight,
+                     scales, zeros, workspace, workspace_bytes, 0, stream);
+}
+
+q4_status q4_gptq_quantize_act_order(const void* w, q4_dtype w_dtype, int64_t n, int64_t k,
+                                     const void* x, q4_dtype x_dtype, int64_t tokens,
+                                     int32_t group_size, int32_t symmetric, float damp,
+                                     uint32_t* qweight, uint16_t* scales, uint32_t* zeros,
+                                     void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+    return gptq_call(w, w_dtype, n, k, x, x_dtype, tokens, group_size, symmetric, damp, qweight,
+                     scales, zeros, workspace, workspace_bytes, 1, stream);
 }
 
 int64_t q4_qweight_words(int64_t n, int64_t k) {

@@ -89,8 +89,11 @@ hipError_t q4k_gemm(const void* x, int x_dtype, int64_t m, const uint32_t* qweig
                     const uint16_t* scales, const uint32_t* zeros, int64_t n, int64_t k, int g,
                     int sym, void* y, int ydt, hipStream_t stream, const char** kname);
 // GPTQ error-feedback quantization (static RTN group quantizers, codes chosen against the
-// calibration Hessian); workspace: k*k + n*k + 64*n floats.
+// calibration Hessian); workspace: k*k + n*k + 256*n floats, and with act_order (columns
+// swept by descending activation energy) 3*k + n*k/4 more.
 int64_t q4k_gptq_workspace_floats(int64_t n, int64_t k);
+int64_t q4k_gptq_act_order_workspace_floats(int64_t n, int64_t k);
 hipError_t q4k_gptq(const void* w, int w_dtype, int64_t n, int64_t k, const void* x, int x_dtype,
                     int64_t tokens, int g, int sym, float damp, uint32_t* qweight, uint16_t* scales,
-                    uint32_t* zeros, float* workspace, hipStream_t stream, const char** kname);
+                    uint32_t* zeros, float* workspace, int act_order, hipStream_t stream,
+                    const char** kname);
