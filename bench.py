@@ -435,6 +435,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--legs", default="gemm,quant,sweep,mlp,mse,dequant,kv,midm,gptq",
                     help="comma list of legs besides the headline decode GEMV")
+    ap.add_argument("--mlp-n", default="", help="mlp leg: only these weight row counts (comma list)")
+    ap.add_argument("--mlp-g", default="", help="mlp leg: only these group sizes (comma list)")
+    ap.add_argument("--mlp-sym", default="", choices=["", "sym", "asym"], help="mlp leg: only this mode")
+    ap.add_argument("--mlp-m", default="", help="mlp leg: only these batch sizes (comma list)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy 5 times (the "
                          "reference kernel for scaling HBM byte counters) and exit")
@@ -687,12 +691,17 @@ def main():
     # ------------------------------------------------------------ MLP batch sweep (GEMV, m <= 16)
     if "mlp" in legs:
         c3 = synthetic.MLP_SWEEP
+        pick = lambda arg, vals: [v for v in vals if not arg or str(v) in arg.split(",")]
         res = {}
         for mat in c3["mats"]:
+            if args.mlp_n and str(mat.n) not in args.mlp_n.split(","):
+                continue
             w = mat.make().to(dev)
             x16 = synthetic.activations(16, mat.k, c3["x_seed"]).to(dev)
-            for g in c3["group_sizes"]:
+            for g in pick(args.mlp_g, c3["group_sizes"]):
                 for sym in c3["symmetric"]:
+                    if args.mlp_sym and args.mlp_sym != ("sym" if sym else "asym"):
+                        continue
                     p0 = q4.q4_quantize_pack(w, g, sym)
                     nb = gemv_bytes(1, mat.n, mat.k, g, sym)
                     cps = max(2, -(-4 * MALL_BYTES // nb))
@@ -700,7 +709,7 @@ def main():
                                            None if sym else p0.zeros.clone(), mat.n, mat.k, g, sym)
                            for _ in range(cps)]
                     row = {}
-                    for m in c3["ms"]:
+                    for m in pick(args.mlp_m, c3["ms"]):
                         xm = x16[:m].contiguous()
                         ym = torch.empty((m, mat.n), dtype=torch.float32, device=dev)
                         q4.q4_w4a16_gemm(xm, pks[0], out=ym)
