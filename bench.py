@@ -675,14 +675,25 @@ def main():
             for m in (17, 32, 64, 128, 256):
                 xm = x256[:m].contiguous()
                 ym = torch.empty((m, n_), dtype=torch.float32, device=dev)
-                q4.q4_w4a16_gemm(xm, pks[0], out=ym)
-                torch.cuda.synchronize()
-                kname = q4.q4_last_kernel()
-                t = graph_ms(capture([lambda pp=pp: q4.q4_w4a16_gemm(xm, pp, out=ym) for pp in pks]), 3) / cps * 1e-3
+                need = q4.q4_w4a16_gemm_workspace(m, n_, k_, 128)
+                ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
                 byt = gemv_bytes(m, n_, k_, 128, False)
-                row[f"m{m}"] = {"us": round(t * 1e6, 2), "gbs": round(byt / t / 1e9, 1),
-                                "frac_hbm": round(byt / t / 1e9 / HBM_PEAK_GBS, 4),
-                                "tflops": round(2.0 * m * n_ * k_ / t / 1e12, 1), "kernel": kname}
+                entry = {}
+                # the default (K split into the workspace where that fills the device), then
+                # the product unsplit
+                for key, split in (("split", True), ("unsplit", False)):
+                    if key == "split" and need == 0:
+                        continue
+                    q4.q4_w4a16_gemm(xm, pks[0], out=ym, workspace=ws, split=split)
+                    torch.cuda.synchronize()
+                    kname = "+".join(q4.q4_last_kernels())
+                    t = graph_ms(capture([lambda pp=pp: q4.q4_w4a16_gemm(xm, pp, out=ym, workspace=ws, split=split)
+                                          for pp in pks]), 3) / cps * 1e-3
+                    entry[key] = {"us": round(t * 1e6, 2), "gbs": round(byt / t / 1e9, 1),
+                                  "frac_hbm": round(byt / t / 1e9 / HBM_PEAK_GBS, 4),
+                                  "tflops": round(2.0 * m * n_ * k_ / t / 1e12, 1), "kernel": kname}
+                row[f"m{m}"] = entry
+                del ws
             res[nm] = row
             del pks, p0, x256
         out["midm"] = {"workload": "W4A16 products at m = 17..256 (decode batches of the pages' "

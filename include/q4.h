@@ -162,6 +162,26 @@ q4_status q4_w4a16_gemm_out(const void* x, q4_dtype x_dtype, int64_t m,
                             void* y, q4_dtype y_dtype, hipStream_t stream);
 
 /* One problem of a grouped call: y = x . x_hat^T for one packed weight. */
+/* q4_w4a16_gemm_out with a workspace for products that would leave compute units idle
+ * (mid-size batches on narrow weights, [FL7] §Batch와 Context에 따라 속도가 달라진다: between
+ * the bandwidth-bound decode and the compute-bound prefill).  When the product runs as the
+ * GEMM and its 128 x 128 tiles number fewer than the device's compute units, its K range
+ * is split into up to 16 parts of at least 512 columns: each part's fp32 partial sums go to
+ * the workspace, then one pass adds the parts in a fixed order (one fp32 rounding per
+ * addition, the same every call) and writes y in y_dtype.  The accuracy bound is that of
+ * q4_w4a16_gemm.  workspace: device memory of at least q4_w4a16_gemm_workspace(m, n, k,
+ * group_size) bytes, 16-byte aligned, contents ignored; NULL runs the product unsplit
+ * (exactly as q4_w4a16_gemm_out); a non-NULL workspace that is too small is Q4_ERR_SHAPE.
+ * Other arguments, rules and errors as q4_w4a16_gemm_out. */
+q4_status q4_w4a16_gemm_ws(const void* x, q4_dtype x_dtype, int64_t m,
+                           const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros,
+                           int64_t n, int64_t k, int32_t group_size, int32_t symmetric,
+                           void* y, q4_dtype y_dtype, void* workspace, int64_t workspace_bytes,
+                           hipStream_t stream);
+/* Bytes of workspace q4_w4a16_gemm_ws uses for this product (m*n*4 per part), 0 when it
+ * would not split it, -1 for sizes the entry points reject. */
+int64_t q4_w4a16_gemm_workspace(int64_t m, int64_t n, int64_t k, int32_t group_size);
+
 typedef struct {
     const void* x;            /* [m][k] activations, in the dtype of the call */
     const uint32_t* qweight;  /* [n][k/8] packed codes */

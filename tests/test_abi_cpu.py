@@ -364,3 +364,28 @@ def test_gptq_workspace_size():
     assert lib.q4_gptq_act_order_workspace(n, k, 128) == (lib.q4_gptq_workspace(n, k, 128)
                                                            + 4 * 3 * k + n * k)
     assert lib.q4_gptq_act_order_workspace(16, 200, 32) == -1
+
+
+def _gws(x=A16, xd=BF16, m=128, qw=A16, sc=A16, zr=A16, n=4096, k=11008, g=128, sym=0, y=A16, yd=F32,
+         ws=A16, ws_bytes=1 << 40):
+    return q4.lib().q4_w4a16_gemm_ws(x, xd, m, qw, sc, zr, n, k, g, sym, y, yd, ws, ws_bytes, None)
+
+
+def test_gemm_workspace_size_and_rules():
+    """Split-K sizes (this host has no GPU: 256 CUs assumed): parts x m x n fp32 partials for
+    a narrow mid-size product, 0 where the product does not split, -1 for rejected sizes;
+    the workspace entry point refuses a short or misaligned workspace before launching."""
+    lib = q4.lib()
+    # 128 x 4096: 32 tiles of 128 x 128 -> 8 parts (172 stages, at least 8 per part)
+    assert lib.q4_w4a16_gemm_workspace(128, 4096, 11008, 128) == 8 * 128 * 4096 * 4
+    assert lib.q4_w4a16_gemm_workspace(16, 4096, 11008, 128) == 0     # the GEMV
+    assert lib.q4_w4a16_gemm_workspace(64, 4096, 11008, 128) == 0     # chunked GEMV
+    assert lib.q4_w4a16_gemm_workspace(2048, 28672, 8192, 128) == 0   # tiles fill the CUs
+    assert lib.q4_w4a16_gemm_workspace(128, 4096, 96, 32) == 0        # too few stages
+    assert lib.q4_w4a16_gemm_workspace(128, 4096, 100, 32) == -1
+    need = lib.q4_w4a16_gemm_workspace(128, 4096, 11008, 128)
+    assert _gws(ws_bytes=need - 1) == SHAPE
+    assert _gws(ws=A16 + 4) == ALIGN
+    assert _gws(g=48) == GROUP and _gws(x=None) == NULL
+    assert q4.q4_last_kernel() == ""
+

@@ -20,10 +20,12 @@ from gpu_util import (DEV, SENTINEL_F32, SENTINEL_I32, assert_linear_close, asse
 pytestmark = pytest.mark.gpu
 
 
-def run_linear(x_cpu, p, guard=True):
+def run_linear(x_cpu, p, guard=True, split=False):
+    """One product through q4_w4a16_gemm into a guarded fp32 output; unsplit unless asked
+    (the split-K path has tests of its own)."""
     m = x_cpu.shape[0]
     yb, yv = guarded((m, p.n), torch.float32, SENTINEL_F32)
-    q4.q4_w4a16_gemm(x_cpu.to(DEV), p, out=yv)
+    q4.q4_w4a16_gemm(x_cpu.to(DEV), p, out=yv, split=split)
     kname = q4.q4_last_kernel()
     torch.cuda.synchronize()
     assert guard_intact(yb), "store outside y"
@@ -729,6 +731,69 @@ def test_midm_chunked_cases(m, n, k, g, xdtype, sym):
     assert_linear_close(y, host_input(x), packed, n, k, g, sym, cols=cols, what=kname)
 
 
+# mid-size batches on narrow weights: the GEMM with its K range split into a workspace
+# (m > 64, or m > 32 from 2^27 weights on, where 128 x 128 tiles leave CUs idle), including
+# ragged m, k % 64 == 32 (a short last stage in the last split) and every group size
+SPLITK_CASES = [(128, 4096, 11008, 128), (256, 4096, 11008, 64), (100, 300, 4096, 32),
+                (200, 11008, 4096, 128), (80, 28672, 2048, 128), (65, 1000, 8192, 64),
+                (72, 500, 4096 + 32, 32)]
+
+
+@pytest.mark.parametrize("m,n,k,g", SPLITK_CASES)
+@pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("sym", [False, True])
+def test_gemm_splitk_cases(m, n, k, g, xdtype, sym):
+    need = q4.q4_w4a16_gemm_workspace(m, n, k, g)
+    assert need > 0 and need % (4 * m * n) == 0, need
+    w = torch.from_numpy(pins.random_weights(m + 3 * n + k, max(n, 12), k)[:n])
+    x = synthetic.activations(m, k, seed=m + 11 * k).to(xdtype)
+    note(f"gemm split-K m={m} n={n} k={k} g={g} {xdtype} sym={sym} parts={need // (4 * m * n)}")
+    p, _ = pack_guarded(w.to(DEV), g, sym)
+    wsb, wsv = guarded((need // 4,), torch.float32, SENTINEL_F32)
+    yb, yv = guarded((m, n), torch.float32, SENTINEL_F32)
+    q4.q4_w4a16_gemm(x.to(DEV), p, out=yv, workspace=wsv)
+    torch.cuda.synchronize()
+    gname = "q4_gemm_mfma_f16" if xdtype == torch.float16 else "q4_gemm_mfma_bf16"
+    assert q4.q4_last_kernels() == [gname, "q4_gemm_splitk_reduce"], q4.q4_last_kernels()
+    assert guard_intact(yb), "store outside y"
+    assert guard_intact(wsb), "store outside the workspace"
+    y = yv.cpu().numpy()
+    packed = assert_pack_exact(p, host_input(w), g, sym)
+    cols = None if m * n * k <= 1 << 28 else synthetic.sample_rows(n, 200, 9).numpy()
+    assert_linear_close(y, host_input(x), packed, n, k, g, sym, cols=cols, what=f"{gname} split-K")
+    # the parts add in a fixed order: a second call gives the same bits
+    q4.q4_w4a16_gemm(x.to(DEV), p, out=yv, workspace=wsv)
+    assert np.array_equal(yv.cpu().numpy(), y)
+    # 16-bit output: the rounding of the same fp32 sums
+    yh = q4.q4_w4a16_gemm(x.to(DEV), p, out_dtype=torch.bfloat16, workspace=wsv)
+    assert torch.equal(yh.cpu(), torch.from_numpy(y).to(torch.bfloat16))
+
+
+def test_gemm_splitk_workspace_rules():
+    """The binding allocates the workspace when not given; a short one is refused by the
+    C ABI; split=False and no workspace run the product unsplit."""
+    m, n, k, g = 128, 4096, 11008, 128
+    w = torch.from_numpy(pins.random_weights(5, n, k))
+    p = q4.q4_quantize_pack(w.to(DEV), g, False)
+    x = synthetic.activations(m, k, seed=6).to(DEV)
+    y1 = q4.q4_w4a16_gemm(x, p)
+    assert q4.q4_last_kernels()[-1] == "q4_gemm_splitk_reduce"
+    y0 = q4.q4_w4a16_gemm(x, p, split=False)
+    assert "q4_gemm_splitk_reduce" not in q4.q4_last_kernels()
+    need = q4.q4_w4a16_gemm_workspace(m, n, k, g)
+    short = torch.empty(need - 16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(q4.Q4Error):
+        q4.q4_w4a16_gemm(x, p, workspace=short)
+    torch.cuda.synchronize()
+    rows = np.arange(0, m, 17)
+    cols = synthetic.sample_rows(n, 64, 4).numpy()
+    packed = (p.qweight.cpu().numpy().view(np.uint32), p.scales.cpu().view(torch.int16).numpy().view(np.uint16),
+              p.zeros.cpu().numpy().view(np.uint32))
+    for y in (y0, y1):
+        assert_linear_close(y.cpu().numpy(), host_input(x.cpu()), packed, n, k, g, False, rows=rows,
+                            cols=cols, what="split-K rules")
+
+
 def test_launch_record_names_every_kernel():
     """q4_last_kernels / q4_last_launch_count report every launch of the last call: one
     for a decode product, the grouped chunk launch plus the remainder for a chunked mid-m
@@ -829,7 +894,7 @@ def test_output_epilogue(m, n, k, g, path, ydt, xdtype):
     p, _ = pack_guarded(w.to(DEV), g, sym)
     y32, k32 = run_linear(x, p)
     yb, yv = guarded((m, n), ydt, SENTINEL_F32)
-    q4.q4_w4a16_gemm(x.to(DEV), p, out=yv)
+    q4.q4_w4a16_gemm(x.to(DEV), p, out=yv, split=False)
     k16 = q4.q4_last_kernel()
     torch.cuda.synchronize()
     assert guard_intact(yb), "store outside y"

@@ -42,7 +42,7 @@ Q4_F32, Q4_F16, Q4_BF16 = 0, 1, 2
 _DTYPE_CODE = {torch.float32: Q4_F32, torch.float16: Q4_F16, torch.bfloat16: Q4_BF16}
 
 EXPORTED = ("q4_quantize_pack", "q4_quantize_pack_grouped", "q4_quantize_pack_mse", "q4_dequant",
-            "q4_w4a16_gemm", "q4_w4a16_gemm_out",
+            "q4_w4a16_gemm", "q4_w4a16_gemm_out", "q4_w4a16_gemm_ws", "q4_w4a16_gemm_workspace",
             "q4_w4a16_gemm_grouped", "q4_w4a16_gemm_grouped_out", "q4_kv_quantize", "q4_kv_attention",
             "q4_kv_attention_workspace", "q4_kv_attention_noalloc",
             "q4_kv_attention_noalloc_max_bytes", "q4_gptq_quantize", "q4_gptq_workspace",
@@ -117,6 +117,11 @@ def _load():
     lib.q4_w4a16_gemm_out.argtypes = [vp, ctypes.c_int, i64, vp, vp, vp, i64, i64, i32, i32, vp,
                                       ctypes.c_int, vp]
     lib.q4_w4a16_gemm_out.restype = ctypes.c_int
+    lib.q4_w4a16_gemm_ws.argtypes = [vp, ctypes.c_int, i64, vp, vp, vp, i64, i64, i32, i32, vp,
+                                     ctypes.c_int, vp, i64, vp]
+    lib.q4_w4a16_gemm_ws.restype = ctypes.c_int
+    lib.q4_w4a16_gemm_workspace.argtypes = [i64, i64, i64, i32]
+    lib.q4_w4a16_gemm_workspace.restype = i64
     lib.q4_w4a16_gemm_grouped.argtypes = [ctypes.POINTER(GemmProblem), i32, ctypes.c_int, i64, i64,
                                           i32, i32, vp]
     lib.q4_w4a16_gemm_grouped.restype = ctypes.c_int
@@ -385,11 +390,20 @@ def q4_dequant(p: PackedWeight, out_dtype: torch.dtype = torch.float32,
     return o
 
 
+def q4_w4a16_gemm_workspace(m: int, n: int, k: int, group_size: int) -> int:
+    """Bytes of workspace q4_w4a16_gemm_ws uses to split this product's K range (0: none)."""
+    return int(_load().q4_w4a16_gemm_workspace(m, n, k, group_size))
+
+
 def q4_w4a16_gemm(x: torch.Tensor, p: PackedWeight,
                   out: Optional[torch.Tensor] = None,
-                  out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
-    """y = x · (S (u - z))^T, x [m, k] fp16/bf16, y [m, n] fp32 (q4_w4a16_gemm), or fp16 /
-    bf16 rounded from the fp32 sums in the kernel's epilogue (q4_w4a16_gemm_out)."""
+                  out_dtype: torch.dtype = torch.float32,
+                  workspace: Optional[torch.Tensor] = None, split: bool = True) -> torch.Tensor:
+    """y = x · (S (u - z))^T, x [m, k] fp16/bf16, y [m, n] fp32, or fp16 / bf16 rounded from
+    the fp32 sums in the kernel's epilogue (q4_w4a16_gemm_ws).  A product that would leave
+    compute units idle splits its K range into a workspace: ``workspace`` (a contiguous
+    device tensor of at least q4_w4a16_gemm_workspace bytes), allocated here when needed
+    and not given; ``split=False`` runs every product unsplit (q4_w4a16_gemm_out)."""
     _need_cuda("x", x)
     if x.dim() != 2 or x.dtype not in (torch.float16, torch.bfloat16) or x.shape[1] != p.k:
         raise ValueError("x must be [m, k] fp16 or bf16 with k matching the packed weight")
@@ -401,15 +415,21 @@ def q4_w4a16_gemm(x: torch.Tensor, p: PackedWeight,
     _check_packed(p, x.device)
     y = out if out is not None else torch.empty((m, p.n), dtype=out_dtype, device=x.device)
     _need("out", y, (m, p.n), tuple(_DTYPE_CODE), x.device)
-    if out_dtype == torch.float32:
-        _check(_load().q4_w4a16_gemm(_dev_ptr(x), _DTYPE_CODE[x.dtype], m, _dev_ptr(p.qweight),
-                                     _dev_ptr(p.scales), _dev_ptr(p.zeros), p.n, p.k,
-                                     p.group_size, int(p.symmetric), _dev_ptr(y), _stream(x)))
-    else:
-        _check(_load().q4_w4a16_gemm_out(_dev_ptr(x), _DTYPE_CODE[x.dtype], m, _dev_ptr(p.qweight),
-                                         _dev_ptr(p.scales), _dev_ptr(p.zeros), p.n, p.k,
-                                         p.group_size, int(p.symmetric), _dev_ptr(y),
-                                         _DTYPE_CODE[out_dtype], _stream(x)))
+    if not split:
+        workspace = None
+    elif workspace is None:
+        need = q4_w4a16_gemm_workspace(m, p.n, p.k, p.group_size)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0
+    if workspace is not None:
+        _need_workspace("workspace", workspace, x.device)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_load().q4_w4a16_gemm_ws(_dev_ptr(x), _DTYPE_CODE[x.dtype], m, _dev_ptr(p.qweight),
+                                    _dev_ptr(p.scales), _dev_ptr(p.zeros), p.n, p.k,
+                                    p.group_size, int(p.symmetric), _dev_ptr(y),
+                                    _DTYPE_CODE[out_dtype], _dev_ptr(workspace) if workspace is not None
+                                    else None, ws_bytes, _stream(x)))
     return y
 
 

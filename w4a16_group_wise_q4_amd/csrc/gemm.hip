@@ -41,7 +41,7 @@
 
 namespace {
 
-constexpr int BM = 128, BN = 256, BK = 64;
+constexpr int BM = 128, BK = 64;  // activation rows and k per stage of a workgroup tile
 constexpr int NTHREADS = 256;
 constexpr int RING = 3;                   // LDS stages of activations
 constexpr int A_STAGE = BM * BK * 2;      // bytes of one activation stage (16 KB)
@@ -91,40 +91,50 @@ __device__ __forceinline__ constexpr int word_of(int kk, int h) {
 
 // Per-lane weight-side registers of one stage: the lane's 4 words for each of its two
 // 32-row blocks, the scales of the stage's groups (1, or 2 when g = 32) and the zero word.
-template <int G>
+template <int G, int NJ>
 struct BStage {
     static constexpr int NGS = G == 32 ? 2 : 1;
-    uint32_t w[2][4];
-    uint32_t s[2][NGS];
-    uint32_t z[2];
+    uint32_t w[NJ][4];
+    uint32_t s[NJ][NGS];
+    uint32_t z[NJ];
 };
 
-template <int G, bool SYM, bool XF16>
+// NJ: 32-row weight blocks per wave (the workgroup tile is 128 x 128 NJ).  With per > 0 the
+// K range is split: the blocks of split s (blockIdx.x / tiles) take stages
+// [s per, (s + 1) per) and write their fp32 partial sums to part[s][M][N] instead of y.
+template <int G, bool SYM, bool XF16, int NJ>
 __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const uint16_t* __restrict__ x, int M,
                                                           const uint32_t* __restrict__ qweight,
                                                           const uint16_t* __restrict__ scales,
                                                           const uint32_t* __restrict__ zeros,
-                                                          int N, int K, void* __restrict__ y, int ydt) {
+                                                          int N, int K, void* __restrict__ y, int ydt,
+                                                          int per, float* __restrict__ part) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // RING x A_STAGE
-    constexpr int NGS = BStage<G>::NGS;
+    constexpr int BN = 128 * NJ;
+    constexpr int NGS = BStage<G, NJ>::NGS;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int mtiles = (M + BM - 1) / BM;
-    const int mt = (int)blockIdx.x % mtiles, nt = (int)blockIdx.x / mtiles;  // XCD-friendly order
+    const int tiles = mtiles * ((N + BN - 1) / BN);
+    const int split = (int)blockIdx.x / tiles, tile = (int)blockIdx.x - split * tiles;
+    const int mt = tile % mtiles, nt = tile / mtiles;  // XCD-friendly order
     const int m0 = mt * BM, n0 = nt * BN;
     const int KW = K / 8;
     const int n_groups = K / G;
     const int zwords = (n_groups + 7) >> 3;
     const int stages = (K + BK - 1) / BK;
+    // this block's stages [sb, se)
+    const int sb = per > 0 ? split * per : 0;
+    const int se = per > 0 && sb + per < stages ? sb + per : stages;
 
     // activations of this row block
     const int arows = __builtin_amdgcn_readfirstlane(M - m0 < BM ? M - m0 : BM);
     const q4::rsrc rx = q4::make_rsrc(x + (int64_t)m0 * K, (uint32_t)arows * (uint32_t)K * 2u);
-    // this wave's 64 weight rows
-    const int wn0 = n0 + 64 * wave;
+    // this wave's 32 NJ weight rows
+    const int wn0 = n0 + 32 * NJ * wave;
     int wrows = N - wn0;
-    wrows = wrows < 0 ? 0 : (wrows > 64 ? 64 : wrows);
+    wrows = wrows < 0 ? 0 : (wrows > 32 * NJ ? 32 * NJ : wrows);
     // uniform values computed with vector instructions: pin them to scalars, or every load
     // through the resources below becomes a waterfall loop
     wrows = __builtin_amdgcn_readfirstlane(wrows);
@@ -148,9 +158,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const uint16_t* __res
         aoff[q] = ((uint32_t)(32 * wave + 8 * q + (lane >> 3)) * (uint32_t)K + 8u * ca) * 2u;
     const int tail_chunks = (K % BK) / 8;  // valid chunks of a short last stage (0: none short)
     const uint32_t tail_mask = tail_chunks != 0 && ca >= tail_chunks ? kOOB : 0u;
-    uint32_t qoff[2], soff[2], zoff[2];
+    uint32_t qoff[NJ], soff[NJ], zoff[NJ];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NJ; ++j) {
         const uint32_t row = (uint32_t)(32 * j + col);
         const uint32_t rowmask = (int)row < wrows ? 0u : kOOB;
         qoff[j] = (row * (uint32_t)KW * 4u + (G >= 64 ? 16u : 8u) * h) | rowmask;
@@ -161,7 +171,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const uint16_t* __res
     // ---- loads of one stage (fixed count and order: 4 activation DMAs, then per block j
     //      the words, the scales and the zero word)
     auto load_a = [&](int s) {  // rows [32 wave, +32) of stage s into ring slot s % RING
-        const uint32_t tm = s >= stages ? kOOB : (s == stages - 1 ? tail_mask : 0u);
+        const uint32_t tm = s >= se ? kOOB : (s == stages - 1 ? tail_mask : 0u);
         const int so = __builtin_amdgcn_readfirstlane(2 * s * BK);
         uint8_t* slot = smem + (s % RING) * A_STAGE;
 #pragma unroll
@@ -169,19 +179,19 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const uint16_t* __res
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr)(slot + (32 * wave + 8 * q) * (BK * 2)), 16,
                                                      (int)(aoff[q] | tm), so, 0, 0);
     };
-    auto load_b = [&](BStage<G>& b, int s) {
+    auto load_b = [&](BStage<G, NJ>& b, int s) {
         const int wso = __builtin_amdgcn_readfirstlane(4 * s * (BK / 8));  // the stage's first word
         const int g0 = G == 128 ? (s >> 1) : (G == 64 ? s : 2 * s);        // its first group
         const int sso = __builtin_amdgcn_readfirstlane(2 * g0);
         const int zso = __builtin_amdgcn_readfirstlane(4 * (g0 >> 3));
-        const uint32_t pm = s >= stages ? kOOB : 0u;  // past the last stage: read nothing
+        const uint32_t pm = s >= se ? kOOB : 0u;  // past the block's last stage: read nothing
         // a short last stage (k % 64 == 32) holds words 0..3 and one group: the words and the
         // scale past the row read nothing
         const bool short_stage = s == stages - 1 && (K % BK) != 0;
         const uint32_t hm = short_stage && (G == 32 || h == 1) ? kOOB : 0u;  // words 4..7
         const uint32_t sm = short_stage ? kOOB : 0u;                         // second group
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NJ; ++j) {
             if constexpr (G >= 64) {
                 const q4::u32x4 t = q4::buf_load_x4(rq, (int)(qoff[j] | pm | hm), wso);
                 b.w[j][0] = t[0]; b.w[j][1] = t[1]; b.w[j][2] = t[2]; b.w[j][3] = t[3];
@@ -200,14 +210,16 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const uint16_t* __res
         }
     };
 
-    f32x16 acc[4][2];
+    f32x16 acc[4][NJ];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    float s_cur[2] = {1.f, 1.f};
+    float s_cur[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) s_cur[j] = 1.f;
     int g_cur = -1;
 
     // LDS operand addresses: row 32i + col of the slot, chunk word_of(kk, h) at its swizzled
@@ -218,17 +230,17 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const uint16_t* __res
         apos[kk] = (uint32_t)col * (BK * 2) + ((uint32_t)(word_of<G>(kk, h) ^ (col & 7)) << 4);
 
     // ---- compute of one stage
-    auto compute = [&](const BStage<G>& b, int s) {
+    auto compute = [&](const BStage<G, NJ>& b, int s) {
         const uint8_t* slot = smem + (s % RING) * A_STAGE;
-        float sn[NGS][2], ratio[NGS][2];
-        uint32_t zrep[NGS][2];
+        float sn[NGS][NJ], ratio[NGS][NJ];
+        uint32_t zrep[NGS][NJ];
         bool fresh[NGS], zmask[NGS];
 #pragma unroll
         for (int q = 0; q < NGS; ++q) {  // the stage's groups (one, or two when g = 32)
             const int gk = G == 128 ? (s >> 1) : (G == 64 ? s : 2 * s + q);
             bool zs = false;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < NJ; ++j) {
                 sn[q][j] = q4::f16_bits_to_float((uint16_t)b.s[j][q]);
                 zs = zs || sn[q][j] == 0.0f;
                 const int z = SYM ? 8 : (int)((b.z[j] >> (4 * (gk & 7))) & 0xFu);
@@ -238,10 +250,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const uint16_t* __res
             // entering a new group (wave-uniform): the accumulator moves to its units
             fresh[q] = gk != g_cur;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) ratio[q][j] = 1.0f;
+            for (int j = 0; j < NJ; ++j) ratio[q][j] = 1.0f;
             if (fresh[q]) {
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
+                for (int j = 0; j < NJ; ++j) {
                     ratio[q][j] = sn[q][j] != 0.0f && g_cur >= 0 ? s_cur[j] / sn[q][j] : 1.0f;
                     if (sn[q][j] != 0.0f) s_cur[j] = sn[q][j];
                 }
@@ -254,7 +266,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const uint16_t* __res
         // extra registers would spill: one read per MFMA, as it is needed.
         constexpr int AP = G == 128 ? 2 : 1;
         q4::u32x4 aop[AP][4];
-        q4::u32x4 bnext[2];
+        q4::u32x4 bnext[NJ];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             if constexpr (AP == 2) {
@@ -268,16 +280,16 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const uint16_t* __res
             }
             const int q = G == 32 ? (kk >> 1) : 0;  // group slot of this MFMA
             const bool rescale = fresh[q] && (G == 32 ? (kk & 1) == 0 : kk == 0);
-            q4::u32x4 bop[2];
+            q4::u32x4 bop[NJ];
             if constexpr (G == 64) {
                 // decoded one k-slot ahead: slot kk + 1's words while slot kk's MFMAs run
                 // (see the schedule below)
                 if (kk == 0) {
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) bnext[j] = dequant_word<XF16>(b.w[j][0], zrep[q][j]);
+                    for (int j = 0; j < NJ; ++j) bnext[j] = dequant_word<XF16>(b.w[j][0], zrep[q][j]);
                 }
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
+                for (int j = 0; j < NJ; ++j) {
                     bop[j] = bnext[j];
                     // zero-scale groups (rare) get a zero operand; a select, so no branch
                     // splits the slot's code
@@ -286,14 +298,14 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const uint16_t* __res
                 }
                 if (kk < 3) {
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) bnext[j] = dequant_word<XF16>(b.w[j][kk + 1 < 4 ? kk + 1 : 3], zrep[0][j]);
+                    for (int j = 0; j < NJ; ++j) bnext[j] = dequant_word<XF16>(b.w[j][kk + 1 < 4 ? kk + 1 : 3], zrep[0][j]);
                 }
             } else {
 #pragma unroll
-                for (int j = 0; j < 2; ++j) bop[j] = dequant_word<XF16>(b.w[j][kk], zrep[q][j]);
+                for (int j = 0; j < NJ; ++j) bop[j] = dequant_word<XF16>(b.w[j][kk], zrep[q][j]);
                 if (zmask[q]) {  // rare: zero the operand of zero-scale groups
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) bop[j] &= sn[q][j] != 0.0f ? 0xFFFFFFFFu : 0u;
+                    for (int j = 0; j < NJ; ++j) bop[j] &= sn[q][j] != 0.0f ? 0xFFFFFFFFu : 0u;
                 }
             }
             const uint8_t* ab = slot + apos[kk];
@@ -302,7 +314,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const uint16_t* __res
                 const q4::u32x4 a = AP == 2 ? aop[(kk & 1) % AP][i]
                                             : *reinterpret_cast<const q4::u32x4*>(ab + i * 32 * (BK * 2));
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
+                for (int j = 0; j < NJ; ++j) {
                     // each 32x32 tile moves to the new group's units right before its own MFMA,
                     // so the multiplies issue while the MFMAs of the other tiles run
                     if (rescale) {
@@ -333,16 +345,16 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const uint16_t* __res
     };
 
     // ---- pipeline: stages s and s+1 are in flight when stage s starts
-    constexpr int LOADS = 4 + 2 * ((G >= 64 ? 1 : 2) + NGS + (SYM ? 0 : 1));  // vector loads per stage
+    constexpr int LOADS = 4 + NJ * ((G >= 64 ? 1 : 2) + NGS + (SYM ? 0 : 1));  // vector loads per stage
     constexpr int WAIT = (LOADS & 15) | ((LOADS >> 4) << 14) | (0x7 << 4) | (0xF << 8);  // vmcnt(LOADS)
-    BStage<G> bs[3];
-    load_a(0);
-    load_b(bs[0], 0);
+    BStage<G, NJ> bs[3];
+    load_a(sb);
+    load_b(bs[0], sb);
     __builtin_amdgcn_sched_barrier(0);
-    load_a(1);
-    load_b(bs[1], 1);
+    load_a(sb + 1);
+    load_b(bs[1], sb + 1);
     __builtin_amdgcn_sched_barrier(0);
-    auto step = [&](int s, BStage<G>& cur, BStage<G>& nxt2) {
+    auto step = [&](int s, BStage<G, NJ>& cur, BStage<G, NJ>& nxt2) {
         // This wave's loads of stage s have landed (those of stage s+1 stay in flight); the
         // barrier then makes every wave's activation DMA visible and frees slot s-1.  A plain
         // s_barrier: __syncthreads() would also wait for the DMA of stage s+1.
@@ -353,19 +365,20 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const uint16_t* __res
         __builtin_amdgcn_sched_barrier(0);
         compute(cur, s);
     };
-    int s = 0;
-    for (; s + 3 <= stages; s += 3) {
+    int s = sb;
+    for (; s + 3 <= se; s += 3) {
         step(s, bs[0], bs[2]);
         step(s + 1, bs[1], bs[0]);
         step(s + 2, bs[2], bs[1]);
     }
-    if (s < stages) step(s, bs[0], bs[2]);
-    if (s + 1 < stages) step(s + 1, bs[1], bs[0]);
+    if (s < se) step(s, bs[0], bs[2]);
+    if (s + 1 < se) step(s + 1, bs[1], bs[0]);
 
-    // epilogue: back to true units, store.  Lane (col, h), register r of a 32x32 tile holds
-    // row (r & 3) + 4h + 8(r >> 2), column col.
+    // epilogue: back to true units, store (y, or this split's fp32 partial sums).  Lane
+    // (col, h), register r of a 32x32 tile holds row (r & 3) + 4h + 8(r >> 2), column col.
+    float* pp = part != nullptr ? part + (int64_t)split * M * N : nullptr;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NJ; ++j) {
         const int nn = wn0 + 32 * j + col;
         if (nn >= N) continue;
 #pragma unroll
@@ -373,40 +386,108 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const uint16_t* __res
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int mm = m0 + 32 * i + (r & 3) + 4 * h + 8 * (r >> 2);
-                if (mm < M) q4::store_y(y, (int64_t)mm * N + nn, acc[i][j][r] * s_cur[j], ydt);
+                if (mm >= M) continue;
+                const float v = acc[i][j][r] * s_cur[j];
+                if (pp != nullptr)
+                    pp[(int64_t)mm * N + nn] = v;
+                else
+                    q4::store_y(y, (int64_t)mm * N + nn, v, ydt);
             }
     }
 }
 
-template <int G, bool SYM>
-hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16_t* sc,
-                  const uint32_t* zr, int n, int k, void* y, int ydt, hipStream_t st, const char** kname) {
-    const int mtiles = (m + BM - 1) / BM, ntiles = (n + BN - 1) / BN;
-    const dim3 grid((unsigned)(mtiles * ntiles)), block(NTHREADS);
+// y[i] = the sum over the splits of part[s][i], in order of s (one rounding per addition,
+// the same order every call), stored as ydt.
+__global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits, int64_t count,
+                                     void* __restrict__ y, int ydt) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        float acc = part[i];
+        for (int sp = 1; sp < splits; ++sp) acc = acc + part[(int64_t)sp * count + i];
+        q4::store_y(y, i, acc, ydt);
+    }
+}
+
+// The tile and split for a product: the 128 x 256 tile while it gives at least one
+// workgroup per CU; otherwise the 128 x 128 tile, and, when a workspace is given and that
+// still leaves CUs idle, the K range split so that the workgroups cover every CU (each split
+// at least 8 stages, at most 16 splits).
+struct GemmPlan {
+    int nj;     // 32-row weight blocks per wave: 2 (128 x 256 tile) or 1 (128 x 128)
+    int per;    // stages per split (0: no split)
+    int splits;
+};
+GemmPlan plan(int64_t m, int64_t n, int64_t k, int num_cus, bool may_split) {
+    const int cus = num_cus > 0 ? num_cus : 256;
+    const int64_t mtiles = (m + BM - 1) / BM;
+    const int64_t stages = (k + BK - 1) / BK;
+    if (mtiles * ((n + 255) / 256) >= cus) return {2, 0, 1};
+    const int64_t tiles = mtiles * ((n + 127) / 128);
+    if (!may_split || tiles >= cus) return {1, 0, 1};
+    int64_t splits = (cus + tiles - 1) / tiles;
+    if (splits > 16) splits = 16;
+    if (splits > stages / 8) splits = stages / 8;
+    if (splits < 2) return {1, 0, 1};
+    const int64_t per = (stages + splits - 1) / splits;
+    return {1, (int)per, (int)((stages + per - 1) / per)};
+}
+
+template <int G, bool SYM, int NJ>
+void launch_nj(const void* x, int xd, int m, const uint32_t* qw, const uint16_t* sc, const uint32_t* zr,
+               int n, int k, void* y, int ydt, int per, int splits, float* part, hipStream_t st) {
+    const int mtiles = (m + BM - 1) / BM, ntiles = (n + 128 * NJ - 1) / (128 * NJ);
+    const dim3 grid((unsigned)(mtiles * ntiles * splits)), block(NTHREADS);
     const size_t lds = (size_t)RING * A_STAGE;
     const uint16_t* xp = reinterpret_cast<const uint16_t*>(x);
-    if (xd == 1) {
-        *kname = "q4_gemm_mfma_f16";
-        hipLaunchKernelGGL((gemm_kernel<G, SYM, true>), grid, block, lds, st, xp, m, qw, sc, zr, n, k, y, ydt);
-    } else {
-        *kname = "q4_gemm_mfma_bf16";
-        hipLaunchKernelGGL((gemm_kernel<G, SYM, false>), grid, block, lds, st, xp, m, qw, sc, zr, n, k, y, ydt);
-    }
-    return q4k_launched(*kname);
+    if (xd == 1)
+        hipLaunchKernelGGL((gemm_kernel<G, SYM, true, NJ>), grid, block, lds, st, xp, m, qw, sc, zr, n, k, y, ydt,
+                           per, part);
+    else
+        hipLaunchKernelGGL((gemm_kernel<G, SYM, false, NJ>), grid, block, lds, st, xp, m, qw, sc, zr, n, k, y, ydt,
+                           per, part);
+}
+
+template <int G, bool SYM>
+hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16_t* sc,
+                  const uint32_t* zr, int n, int k, void* y, int ydt, float* ws, int64_t ws_floats,
+                  hipStream_t st, const char** kname) {
+    GemmPlan pl = plan(m, n, k, q4k_device_cus(), ws != nullptr);
+    if (pl.splits > 1 && (int64_t)pl.splits * m * n > ws_floats) pl = {1, 0, 1};
+    float* part = pl.splits > 1 ? ws : nullptr;
+    *kname = xd == 1 ? "q4_gemm_mfma_f16" : "q4_gemm_mfma_bf16";
+    if (pl.nj == 2)
+        launch_nj<G, SYM, 2>(x, xd, m, qw, sc, zr, n, k, y, ydt, 0, 1, nullptr, st);
+    else
+        launch_nj<G, SYM, 1>(x, xd, m, qw, sc, zr, n, k, y, ydt, pl.per, pl.splits, part, st);
+    hipError_t e = q4k_launched(*kname);
+    if (e != hipSuccess || part == nullptr) return e;
+    const int64_t count = (int64_t)m * n;
+    const int64_t blocks = (count + 255) / 256 < 4096 ? (count + 255) / 256 : 4096;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, st, part, pl.splits, count, y,
+                       ydt);
+    return q4k_launched("q4_gemm_splitk_reduce");
 }
 
 }  // namespace
 
+int64_t q4k_gemm_workspace_floats(int64_t m, int64_t n, int64_t k) {
+    const GemmPlan pl = plan(m, n, k, q4k_device_cus(), true);
+    return pl.splits > 1 ? (int64_t)pl.splits * m * n : 0;
+}
+
 hipError_t q4k_gemm(const void* x, int x_dtype, int64_t m, const uint32_t* qweight,
                     const uint16_t* scales, const uint32_t* zeros, int64_t n, int64_t k, int g,
-                    int sym, void* y, int ydt, hipStream_t stream, const char** kname) {
+                    int sym, void* y, int ydt, float* workspace, int64_t workspace_floats,
+                    hipStream_t stream, const char** kname) {
     const int mi = (int)m, ni = (int)n, ki = (int)k;
+    float* ws = workspace;
+    const int64_t wf = workspace_floats;
     switch (g * 2 + (sym ? 1 : 0)) {
-    case 64: return launch<32, false>(x, x_dtype, mi, qweight, scales, zeros, ni, ki, y, ydt, stream, kname);
-    case 65: return launch<32, true>(x, x_dtype, mi, qweight, scales, zeros, ni, ki, y, ydt, stream, kname);
-    case 128: return launch<64, false>(x, x_dtype, mi, qweight, scales, zeros, ni, ki, y, ydt, stream, kname);
-    case 129: return launch<64, true>(x, x_dtype, mi, qweight, scales, zeros, ni, ki, y, ydt, stream, kname);
-    case 256: return launch<128, false>(x, x_dtype, mi, qweight, scales, zeros, ni, ki, y, ydt, stream, kname);
-    default: return launch<128, true>(x, x_dtype, mi, qweight, scales, zeros, ni, ki, y, ydt, stream, kname);
+    case 64: return launch<32, false>(x, x_dtype, mi, qweight, scales, zeros, ni, ki, y, ydt, ws, wf, stream, kname);
+    case 65: return launch<32, true>(x, x_dtype, mi, qweight, scales, zeros, ni, ki, y, ydt, ws, wf, stream, kname);
+    case 128: return launch<64, false>(x, x_dtype, mi, qweight, scales, zeros, ni, ki, y, ydt, ws, wf, stream, kname);
+    case 129: return launch<64, true>(x, x_dtype, mi, qweight, scales, zeros, ni, ki, y, ydt, ws, wf, stream, kname);
+    case 256: return launch<128, false>(x, x_dtype, mi, qweight, scales, zeros, ni, ki, y, ydt, ws, wf, stream, kname);
+    default: return launch<128, true>(x, x_dtype, mi, qweight, scales, zeros, ni, ki, y, ydt, ws, wf, stream, kname);
     }
 }

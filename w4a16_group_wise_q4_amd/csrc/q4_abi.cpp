@@ -207,11 +207,23 @@ bool chunked_gemv(int64_t m, int64_t n, int cus) {
     return gemm_wgs <= 2 * (int64_t)cus && chunks * n < 144 * 1024;
 }
 
+// Whether a product with a workspace runs as the split-K GEMM (rather than as below): where
+// the GEMM's tiles leave CUs idle, from m > 64 on (below that the chunked GEMV is as fast or
+// faster on the 7B projections), and from m > 32 on for matrices of 2^27 weights and more
+// (the 70B projection at m = 64: 94 against 114 us).
+bool splitk_gemm(int64_t m, int64_t n, int64_t k) {
+    if (m <= 32 || (m <= 64 && n * k < (int64_t(1) << 27))) return false;
+    return q4k_gemm_workspace_floats(m, n, k) > 0;
+}
+
 hipError_t run_product(const void* x, int xd, int64_t m, const uint32_t* qw, const uint16_t* sc,
                        const uint32_t* zr, int64_t n, int64_t k, int g, int sym, void* y, int ydt,
-                       hipStream_t st, const char** name) {
+                       float* ws, int64_t ws_floats, hipStream_t st, const char** name) {
     if (m <= 16) return q4k_gemv(x, xd, (int)m, qw, sc, zr, n, k, g, sym, y, ydt, st, name);
-    if (!chunked_gemv(m, n, q4k_device_cus())) return q4k_gemm(x, xd, m, qw, sc, zr, n, k, g, sym, y, ydt, st, name);
+    if (ws != nullptr && splitk_gemm(m, n, k))
+        return q4k_gemm(x, xd, m, qw, sc, zr, n, k, g, sym, y, ydt, ws, ws_floats, st, name);
+    if (!chunked_gemv(m, n, q4k_device_cus()))
+        return q4k_gemm(x, xd, m, qw, sc, zr, n, k, g, sym, y, ydt, nullptr, 0, st, name);
     const int64_t full = m / 16, rem = m % 16;
     const uint16_t* xs = static_cast<const uint16_t*>(x);
     char* yb = static_cast<char*>(y);
@@ -284,7 +296,7 @@ q4_status q4_w4a16_gemm_grouped_out(const q4_gemm_problem* problems, int32_t cou
         const q4_gemm_problem& p = problems[i];
         const hipError_t e = run_product(p.x, (int)x_dtype, m, p.qweight, p.scales,
                                          symmetric ? nullptr : p.zeros, p.n, k, group_size,
-                                         symmetric ? 1 : 0, p.y, (int)y_dtype, stream, &name);
+                                         symmetric ? 1 : 0, p.y, (int)y_dtype, nullptr, 0, stream, &name);
         if (e != hipSuccess) return Q4_ERR_LAUNCH;
     }
     return finish(hipSuccess, name);
@@ -301,13 +313,34 @@ q4_status q4_w4a16_gemm_out(const void* x, q4_dtype x_dtype, int64_t m, const ui
                             const uint16_t* scales, const uint32_t* zeros, int64_t n, int64_t k,
                             int32_t group_size, int32_t symmetric, void* y, q4_dtype y_dtype,
                             hipStream_t stream) {
+    return q4_w4a16_gemm_ws(x, x_dtype, m, qweight, scales, zeros, n, k, group_size, symmetric, y,
+                            y_dtype, nullptr, 0, stream);
+}
+
+int64_t q4_w4a16_gemm_workspace(int64_t m, int64_t n, int64_t k, int32_t group_size) {
+    if (check_layout(n, k, group_size) != Q4_OK || k > kMaxMatmulK || n > kMaxMatmulN) return -1;
+    if (m < 1 || m > kMaxDim || m > kMaxElems / k || m > kMaxMatmulOut / n) return -1;
+    return splitk_gemm(m, n, k) ? q4k_gemm_workspace_floats(m, n, k) * (int64_t)sizeof(float) : 0;
+}
+
+q4_status q4_w4a16_gemm_ws(const void* x, q4_dtype x_dtype, int64_t m, const uint32_t* qweight,
+                           const uint16_t* scales, const uint32_t* zeros, int64_t n, int64_t k,
+                           int32_t group_size, int32_t symmetric, void* y, q4_dtype y_dtype,
+                           void* workspace, int64_t workspace_bytes, hipStream_t stream) {
     begin_call();
     const q4_status st = check_matmul(x, x_dtype, m, qweight, scales, zeros, n, k, group_size,
                                       symmetric, y, y_dtype);
     if (st != Q4_OK) return st;
+    int64_t ws_floats = 0;
+    if (workspace != nullptr) {
+        if (!aligned(workspace, 16)) return Q4_ERR_ALIGN;
+        if (workspace_bytes < q4_w4a16_gemm_workspace(m, n, k, group_size)) return Q4_ERR_SHAPE;
+        ws_floats = workspace_bytes / (int64_t)sizeof(float);
+    }
     const char* name = "";
     const hipError_t e = run_product(x, (int)x_dtype, m, qweight, scales, symmetric ? nullptr : zeros, n,
-                                     k, group_size, symmetric ? 1 : 0, y, (int)y_dtype, stream, &name);
+                                     k, group_size, symmetric ? 1 : 0, y, (int)y_dtype,
+                                     static_cast<float*>(workspace), ws_floats, stream, &name);
     return finish(e, name);
 }
 

@@ -85,9 +85,14 @@ hipError_t q4k_gemv_tile_g128(int sym, int x_dtype, int m, int k, int upw, int w
 // otherwise, so the caller runs them one by one.
 hipError_t q4k_gemv_grouped(const q4::GemvProblem* problems, int count, int x_dtype, int m,
                             int64_t k, int g, int sym, int ydt, hipStream_t stream, const char** kname);
+// Prefill GEMM; with a workspace (floats) a product that leaves CUs idle splits its K range
+// (partials in the workspace, then an ordered reduction into y).  q4k_gemm_workspace_floats
+// gives the size it would use, 0 when it would not split.
+int64_t q4k_gemm_workspace_floats(int64_t m, int64_t n, int64_t k);
 hipError_t q4k_gemm(const void* x, int x_dtype, int64_t m, const uint32_t* qweight,
                     const uint16_t* scales, const uint32_t* zeros, int64_t n, int64_t k, int g,
-                    int sym, void* y, int ydt, hipStream_t stream, const char** kname);
+                    int sym, void* y, int ydt, float* workspace, int64_t workspace_floats,
+                    hipStream_t stream, const char** kname);
 // GPTQ error-feedback quantization (static RTN group quantizers, codes chosen against the
 // calibration Hessian); workspace: k*k + n*k + 256*n floats, and with act_order (columns
 // swept by descending activation energy) 3*k + n*k/4 more.
