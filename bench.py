@@ -112,11 +112,13 @@ def capture(fns):
     return g
 
 
-def graph_ms(graph, reps):
-    """Mean duration in ms of one replay: HIP events on the launch stream."""
+def graph_ms(graph, reps, warm=3):
+    """Mean duration in ms of one replay: HIP events on the launch stream, after `warm`
+    untimed replays (the first replays after the device was idle run slow)."""
     import torch
     stream = torch.cuda.current_stream()
-    graph.replay()
+    for _ in range(warm):
+        graph.replay()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -430,8 +432,10 @@ def cpu_baseline(seconds=6.0, max_threads=16):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=340)
-    ap.add_argument("--warmup", type=int, default=34)
+    ap.add_argument("--steps", type=int, default=1020)
+    # the device needs about 40 replays of the decode graph (1360 launches, about 12 ms)
+    # after idle before its launches reach their steady duration
+    ap.add_argument("--warmup", type=int, default=1360)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--legs", default="gemm,quant,sweep,mlp,mse,dequant,kv,midm,gptq",
                     help="comma list of legs besides the headline decode GEMV")
@@ -491,8 +495,12 @@ def main():
     full = capture([f for c in range(copies) for f in step_fns(c)])
     tail_n = args.steps % copies
     tail = capture([f for c in range(tail_n) for f in step_fns(c)]) if tail_n else None
-    for _ in range(max(1, args.warmup // copies)):
+    # W untimed warmup steps: whole replays of the copies, then single steps for the rest
+    for _ in range(args.warmup // copies):
         full.replay()
+    for c in range(args.warmup % copies):
+        for f in step_fns(c):
+            f()
     torch.cuda.synchronize()
     # the timed region: exactly K steps, synchronized on both sides, nothing else inside;
     # HIP events on the stream the graphs replay on bracket the same K launches (one
