@@ -9,12 +9,15 @@
 // "Quantization Algorithms 단권화" §Signed ↔ Unsigned; round-to-nearest as the
 // calibration-free RTN baseline of the same page (§Calibration-free).
 //
-// Work mapping (HBM-bound: 2 or 4 bytes read and 0.5 byte written per weight):
-//   one wave = one row x 8 consecutive groups = exactly one 32-bit zero-point word;
-//   lane l handles E = g/8 consecutive weights of group l/8; the 8 lanes of a group
-//   reduce min/max (or max|w|) with three xor shuffles; each lane then packs its E
-//   codes (E/8 words, or half a word when g = 32) and the wave writes a contiguous
-//   run of 4*g bytes of qweight.  The 8 zero points are OR-combined across the wave.
+// Work mapping (2 or 4 bytes read and 0.5 byte written per weight; the exact arithmetic
+// makes the kernel about as much VALU-bound as HBM-bound):
+//   one wave task = one row x 16 consecutive groups = two 32-bit zero-point words;
+//   lane l handles E = g/4 consecutive weights of group l/4; the 4 lanes of a group
+//   reduce min/max (or max|w|) with two xor shuffles; each lane then packs its E codes
+//   (E/8 words) and the wave writes a contiguous run of 8*g bytes of qweight.  Each half
+//   wave OR-combines the 8 zero points of its word.  Four lanes per group (rather than
+//   eight) halve the per-weight cost of the group's scale, zero point and reciprocal,
+//   which every lane of the group computes.
 //
 // Arithmetic is IEEE fp32 in the order written (no contraction, correctly rounded
 // divisions for the scale and zero point, round-half-to-even), so codes, scales and zero
@@ -30,21 +33,23 @@ namespace {
 
 using namespace q4q;
 
-// Persistent waves over the (row, zero word) tasks of every problem of the launch, one
-// problem after another.  For a problem with Z = min(zero words per row, waves) and
-// R = min(waves / Z, n), wave gw starts at (row r0, zero word z0) = (gw / Z, gw % Z) and
-// steps by R rows and Z zero words, so every task is done exactly once and consecutive
-// matrices of a grouped launch form one stream.
+// Persistent waves over the (row, zero-word pair) tasks of every problem of the launch, one
+// problem after another.  For a problem with Z = min(zero-word pairs per row, waves) and
+// R = min(waves / Z, n), wave gw starts at (row r0, pair z0) = (gw / Z, gw % Z) and steps
+// by R rows and Z pairs, so every task is done exactly once and consecutive matrices of a
+// grouped launch form one stream.
 template <int G, bool SYM, int DT>
 __global__ __launch_bounds__(256) void quant_pack_kernel(const q4::QuantBatch bt) {
-    constexpr int E = G / 8;                // weights per lane
+    constexpr int ZT = 2;                   // zero-point words per task
+    constexpr int E = G * ZT / 8;           // weights per lane
+    constexpr int LPG = G / E;              // lanes per group
     constexpr uint32_t EB = DT == 0 ? 4 : 2;  // bytes per weight
     constexpr uint32_t kOff = 0xFFFFFFF0u;   // an offset past every resource
     const int lane = threadIdx.x & 63;
     const int waves = (int)gridDim.x * (int)(blockDim.x >> 6);
     const int gw = (int)blockIdx.x * (int)(blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int grp = lane >> 3;
-    const int t = lane & 7;
+    const int grp = lane / LPG;             // group within the task
+    const int t = lane % LPG;
     for (int pi = 0; pi < bt.count; ++pi) {
         const void* __restrict__ w = bt.p[pi].w;
         uint32_t* __restrict__ qweight = bt.p[pi].qweight;
@@ -54,7 +59,8 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(const q4::QuantBatch bt
         const int heads = bt.p[pi].heads, t_cap = bt.p[pi].t_cap, t0 = bt.p[pi].t0;
         const int n_groups = k / G;
         const int zwords = (n_groups + 7) >> 3;
-        const int Z = zwords < waves ? zwords : waves;
+        const int zpairs = (zwords + ZT - 1) / ZT;
+        const int Z = zpairs < waves ? zpairs : waves;
         const int R = waves / Z < n ? waves / Z : n;
         const int r0 = gw / Z, z0 = gw - r0 * Z;
         if (r0 >= R) continue;  // wave-uniform: the waves past R * Z sit this problem out
@@ -64,7 +70,7 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(const q4::QuantBatch bt
             const bool live = rr < n;
             const q4::rsrc rw = q4::make_rsrc(reinterpret_cast<const char*>(w) + (int64_t)(live ? rr : 0) * k * EB,
                                               (uint32_t)k * EB);
-            const int gi = zz * 8 + grp;
+            const int gi = zz * 8 * ZT + grp;
             const uint32_t el = (uint32_t)gi * G + (uint32_t)t * E;
             load_slice<E, DT>(rw, live && gi < n_groups ? el * EB : kOff, dst);
         };
@@ -78,7 +84,7 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(const q4::QuantBatch bt
 #pragma unroll
             for (int e = 0; e < E; ++e) v[e] = vn[e];
             int nrow = row, nzw = zw + Z;
-            if (nzw >= zwords) {
+            if (nzw >= zpairs) {
                 nzw = z0;
                 nrow = row + R;
             }
@@ -89,7 +95,7 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(const q4::QuantBatch bt
                 const q4::rsrc rq = q4::make_rsrc(qweight + orow * (k / 8), (uint32_t)k / 2u);
                 const q4::rsrc rs = q4::make_rsrc(scales + orow * n_groups, (uint32_t)n_groups * 2u);
                 const q4::rsrc rz = q4::make_rsrc(zeros + orow * zwords, (uint32_t)zwords * 4u);
-                const int gidx = zw * 8 + grp;
+                const int gidx = zw * 8 * ZT + grp;
                 const bool valid = gidx < n_groups;
                 const uint32_t elem = (uint32_t)gidx * G + (uint32_t)t * E;  // within the row
 
@@ -100,21 +106,25 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(const q4::QuantBatch bt
 
                 // codes: E/2 bytes per lane, contiguous across the wave
                 const uint32_t qoff = valid ? elem / 2u : kOff;
-                if constexpr (E == 16) {
+                if constexpr (E == 32) {
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        __builtin_bit_cast(q4::u32x4, q4::u32x4{packed[0], packed[1], packed[2], packed[3]}), rq,
+                        (int)qoff, 0, 0);
+                } else if constexpr (E == 16) {
                     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(q4::u32x2, q4::u32x2{packed[0], packed[1]}),
                                                           rq, (int)qoff, 0, 0);
-                } else if constexpr (E == 8) {
+                } else {  // E == 8
                     __builtin_amdgcn_raw_buffer_store_b32(packed[0], rq, (int)qoff, 0, 0);
-                } else {  // E == 4: half a word
-                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)packed[0], rq, (int)qoff, 0, 0);
                 }
                 __builtin_amdgcn_raw_buffer_store_b16(s16, rs, (int)(valid && t == 0 ? (uint32_t)gidx * 2u : kOff), 0, 0);
                 if constexpr (!SYM) {
-                    uint32_t zn = valid ? ((uint32_t)zi << (4 * grp)) : 0u;
-                    zn |= __shfl_xor(zn, 8, 64);
-                    zn |= __shfl_xor(zn, 16, 64);
-                    zn |= __shfl_xor(zn, 32, 64);
-                    __builtin_amdgcn_raw_buffer_store_b32(zn, rz, (int)(lane == 0 ? (uint32_t)zw * 4u : kOff), 0, 0);
+                    // the 8 groups of each zero word sit in one half wave (lanes 32 h ..)
+                    uint32_t zn = valid ? ((uint32_t)zi << (4 * (grp & 7))) : 0u;
+#pragma unroll
+                    for (int m = LPG; m < 32; m <<= 1) zn |= __shfl_xor(zn, m, 64);
+                    const int word = zw * ZT + (lane >> 5);
+                    const bool head = (lane & 31) == 0 && word < zwords;
+                    __builtin_amdgcn_raw_buffer_store_b32(zn, rz, (int)(head ? (uint32_t)word * 4u : kOff), 0, 0);
                 }
             }
             row = nrow;
@@ -192,7 +202,7 @@ hipError_t launch_dt(const q4::QuantBatch& bt, int dt, hipStream_t st, const cha
     const int64_t cap = (int64_t)num_cus * 32;
     int64_t tasks = 0;
     for (int i = 0; i < bt.count; ++i) {
-        const int64_t t = (int64_t)bt.p[i].n * ((bt.p[i].k / G + 7) / 8);
+        const int64_t t = (int64_t)bt.p[i].n * (((bt.p[i].k / G + 7) / 8 + 1) / 2);  // zero-word pairs
         tasks = t > tasks ? t : tasks;
     }
     const int64_t waves = tasks < cap ? tasks : cap;
