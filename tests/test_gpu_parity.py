@@ -580,7 +580,8 @@ def test_linear_special_inputs(m, g, sym):
             assert np.all(np.abs(y[i].astype(np.float64) - xhat[:, kk]) <= bound), (i, kk)
 
 
-@pytest.mark.parametrize("m,g", [(1, 64), (16, 64), (17, 64), (300, 64), (1, 128), (4, 128)])
+@pytest.mark.parametrize("m,g", [(1, 64), (16, 64), (17, 64), (300, 64), (1, 128), (4, 128), (300, 128),
+                                 (300, 32)])
 @pytest.mark.parametrize("sym", [False, True])
 def test_linear_zero_scale_groups(m, g, sym):
     """Packed weights from elsewhere may hold S = 0 for a group (a group of zeros stored
@@ -683,9 +684,10 @@ def matmul_kernels(m, n, xdtype=torch.bfloat16):
 
 # the prefill GEMM itself, also at small m where the grid is wide (n large); k = 96 and 160
 # end on a half stage (k % 64 == 32, g = 32)
+# (the last three: m >= 512 with a tile per CU, the 256 x 128 tile: ragged m and n, k % 64 == 32)
 GEMM_CASES = [(17, 73800, 256, 128), (130, 16400, 384, 64), (300, 129, 96, 32), (256, 9300, 1024, 128),
               (129, 16448, 4096 + 64, 64), (64, 36900, 512, 32), (257, 300, 512, 128), (128, 18500, 1024, 64),
-              (40, 73800, 160, 32)]
+              (40, 73800, 160, 32), (520, 16400, 512, 64), (600, 11000, 1024 + 32, 32), (1000, 8300, 1024, 128)]
 
 
 @pytest.mark.parametrize("m,n,k,g", GEMM_CASES)
@@ -853,7 +855,7 @@ def test_gemm_prefill_70b_sampled():
 # 128), the chunked mid-M GEMV and the prefill GEMM (a ragged m, and k ending on a half stage)
 EPILOGUE_CASES = [(1, 300, 1024, 128, "tile"), (3, 130, 2048, 64, "tile"), (8, 100, 1024, 32, "wide"),
                   (16, 16392, 512, 128, "wide"), (2, 300, 4096 + 64, 64, "mfma"), (40, 1000, 1024, 64, "midm"),
-                  (300, 129, 96, 32, "gemm"), (257, 300, 512, 128, "gemm")]
+                  (300, 129, 96, 32, "gemm"), (257, 300, 512, 128, "gemm"), (520, 16400, 512, 128, "gemm")]
 HALF_ULP = {torch.bfloat16: 2.0 ** -8, torch.float16: 2.0 ** -11}
 
 

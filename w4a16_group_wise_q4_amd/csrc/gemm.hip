@@ -37,14 +37,20 @@
 // Placement.  Consecutive workgroups land on consecutive XCDs (8 per MI355X), so block b
 // takes activation block b % mtiles: with 16 row blocks (m = 2048) each XCD's L2 holds
 // two 2 MB activation blocks while the packed weights stream through.
+#include <type_traits>
+
 #include "q4_launch.h"
 
 namespace {
 
-constexpr int BM = 128, BK = 64;  // activation rows and k per stage of a workgroup tile
+constexpr int BK = 64;  // k per stage of a workgroup tile
 constexpr int NTHREADS = 256;
-constexpr int RING = 3;                   // LDS stages of activations
-constexpr int A_STAGE = BM * BK * 2;      // bytes of one activation stage (16 KB)
+// MI: 32-row activation blocks per wave (the workgroup tile has 32 MI activation rows).
+// The activation ring holds 3 stages of 128 rows (loads two stages ahead) or 2 stages of
+// 256 rows (one stage ahead; its stages take twice as long), 48 or 64 KB: two workgroups
+// per CU either way.
+constexpr int ring_of(int mi) { return mi == 8 ? 2 : 3; }
+constexpr int a_stage_of(int mi) { return 32 * mi * BK * 2; }  // bytes of one activation stage
 constexpr uint32_t kOOB = 0x80000000u;    // an offset past every resource: reads 0
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -62,11 +68,13 @@ __device__ __forceinline__ f32x16 mfma32_f16(q4::u32x4 a, q4::u32x4 b, f32x16 c)
 // 8 codes of one packed word minus z, as exact 16-bit floats in natural k order
 // (elements 0..7 = k 8j..8j+7).  Bytes 128 + u - z (no borrow between bytes), then XOR 0x80
 // gives u - z as signed bytes, converted exactly to fp32 and narrowed by keeping the upper
-// half (bf16) or converting (fp16; small integers are exact either way).
+// half (bf16) or converting (fp16; small integers are exact either way).  nm is the nibble
+// mask 0x0F0F0F0F, or 0 together with zrep = 0 for a group whose scale is zero: every
+// element is then 0, so such a group adds nothing without a branch of its own.
 template <bool XF16>
-__device__ __forceinline__ q4::u32x4 dequant_word(uint32_t w, uint32_t zrep) {
-    const uint32_t lo = (((w & 0x0F0F0F0Fu) | 0x80808080u) - zrep) ^ 0x80808080u;         // k 0,2,4,6
-    const uint32_t hi = ((((w >> 4) & 0x0F0F0F0Fu) | 0x80808080u) - zrep) ^ 0x80808080u;  // k 1,3,5,7
+__device__ __forceinline__ q4::u32x4 dequant_word(uint32_t w, uint32_t zrep, uint32_t nm) {
+    const uint32_t lo = (((w & nm) | 0x80808080u) - zrep) ^ 0x80808080u;         // k 0,2,4,6
+    const uint32_t hi = ((((w >> 4) & nm) | 0x80808080u) - zrep) ^ 0x80808080u;  // k 1,3,5,7
     q4::u32x4 r;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
@@ -99,10 +107,11 @@ struct BStage {
     uint32_t z[NJ];
 };
 
-// NJ: 32-row weight blocks per wave (the workgroup tile is 128 x 128 NJ).  With per > 0 the
-// K range is split: the blocks of split s (blockIdx.x / tiles) take stages
-// [s per, (s + 1) per) and write their fp32 partial sums to part[s][M][N] instead of y.
-template <int G, bool SYM, bool XF16, int NJ>
+// NJ: 32-row weight blocks per wave, MI: 32-row activation blocks per wave (the workgroup
+// tile is 32 MI x 128 NJ).  With per > 0 the K range is split: the blocks of split s
+// (blockIdx.x / tiles) take stages [s per, (s + 1) per) and write their fp32 partial sums
+// to part[s][M][N] instead of y.
+template <int G, bool SYM, bool XF16, int NJ, int MI>
 __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const uint16_t* __restrict__ x, int M,
                                                           const uint32_t* __restrict__ qweight,
                                                           const uint16_t* __restrict__ scales,
@@ -110,7 +119,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const uint16_t* __res
                                                           int N, int K, void* __restrict__ y, int ydt,
                                                           int per, float* __restrict__ part) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // RING x A_STAGE
-    constexpr int BN = 128 * NJ;
+    constexpr int BM = 32 * MI, BN = 128 * NJ;
+    constexpr int RING = ring_of(MI), AHEAD = RING - 1;  // stages in the ring, loaded ahead
+    constexpr int A_STAGE = a_stage_of(MI);
+    constexpr int WROWS = 8 * MI;  // activation rows each wave moves into a stage
     constexpr int NGS = BStage<G, NJ>::NGS;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -147,15 +159,15 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const uint16_t* __res
 
     // Per-lane parts of the load offsets; the per-stage part is a uniform scalar offset.
     // Rows past the end of a block read nothing (their per-lane offset carries kOOB), and
-    // so do the loads for the two stages after the last one (issued by the pipeline, never
+    // so do the loads for the stages after the last one (issued by the pipeline, never
     // used): every mask goes into the per-lane offset.  The k tail (k % 64 == 32): the
     // activation chunks past k are read as zeros, so whatever the weight words past the
     // end of a row hold meets a zero.
     const int ca = (lane & 7) ^ ((lane >> 3) & 7);  // activation chunk this lane moves (DMA rows are 8-aligned)
-    uint32_t aoff[4];
+    uint32_t aoff[MI];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-        aoff[q] = ((uint32_t)(32 * wave + 8 * q + (lane >> 3)) * (uint32_t)K + 8u * ca) * 2u;
+    for (int q = 0; q < MI; ++q)
+        aoff[q] = ((uint32_t)(WROWS * wave + 8 * q + (lane >> 3)) * (uint32_t)K + 8u * ca) * 2u;
     const int tail_chunks = (K % BK) / 8;  // valid chunks of a short last stage (0: none short)
     const uint32_t tail_mask = tail_chunks != 0 && ca >= tail_chunks ? kOOB : 0u;
     uint32_t qoff[NJ], soff[NJ], zoff[NJ];
@@ -168,15 +180,15 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const uint16_t* __res
         zoff[j] = (row * (uint32_t)zwords * 4u) | rowmask;
     }
 
-    // ---- loads of one stage (fixed count and order: 4 activation DMAs, then per block j
+    // ---- loads of one stage (fixed count and order: MI activation DMAs, then per block j
     //      the words, the scales and the zero word)
-    auto load_a = [&](int s) {  // rows [32 wave, +32) of stage s into ring slot s % RING
+    auto load_a = [&](int s) {  // rows [WROWS wave, +WROWS) of stage s into ring slot s % RING
         const uint32_t tm = s >= se ? kOOB : (s == stages - 1 ? tail_mask : 0u);
         const int so = __builtin_amdgcn_readfirstlane(2 * s * BK);
         uint8_t* slot = smem + (s % RING) * A_STAGE;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr)(slot + (32 * wave + 8 * q) * (BK * 2)), 16,
+        for (int q = 0; q < MI; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr)(slot + (WROWS * wave + 8 * q) * (BK * 2)), 16,
                                                      (int)(aoff[q] | tm), so, 0, 0);
     };
     auto load_b = [&](BStage<G, NJ>& b, int s) {
@@ -210,9 +222,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const uint16_t* __res
         }
     };
 
-    f32x16 acc[4][NJ];
+    f32x16 acc[MI][NJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -229,43 +241,41 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const uint16_t* __res
     for (int kk = 0; kk < 4; ++kk)
         apos[kk] = (uint32_t)col * (BK * 2) + ((uint32_t)(word_of<G>(kk, h) ^ (col & 7)) << 4);
 
-    // ---- compute of one stage
-    auto compute = [&](const BStage<G, NJ>& b, int s) {
+    // ---- compute of one stage.  FRESH (a compile-time tag): the stage opens a group (every
+    // stage when g <= 64; at g = 128 the caller picks the variant per stage), so its MFMAs
+    // move the accumulators to the new group's units first.  Both variants are straight-line
+    // code, which leaves the scheduler free to interleave decodes, rescales and MFMAs.
+    auto compute = [&](const BStage<G, NJ>& b, int s, auto fresh_tag) {
+        constexpr bool FRESH = decltype(fresh_tag)::value;
         const uint8_t* slot = smem + (s % RING) * A_STAGE;
-        float sn[NGS][NJ], ratio[NGS][NJ];
-        uint32_t zrep[NGS][NJ];
-        bool fresh[NGS], zmask[NGS];
+        float ratio[NGS][NJ];
+        uint32_t zrep[NGS][NJ], nm[NGS][NJ];
 #pragma unroll
         for (int q = 0; q < NGS; ++q) {  // the stage's groups (one, or two when g = 32)
             const int gk = G == 128 ? (s >> 1) : (G == 64 ? s : 2 * s + q);
-            bool zs = false;
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                sn[q][j] = q4::f16_bits_to_float((uint16_t)b.s[j][q]);
-                zs = zs || sn[q][j] == 0.0f;
+                const float sn = q4::f16_bits_to_float((uint16_t)b.s[j][q]);
+                const bool live = sn != 0.0f;  // a zero scale: the group's operand is zero
                 const int z = SYM ? 8 : (int)((b.z[j] >> (4 * (gk & 7))) & 0xFu);
-                zrep[q][j] = (uint32_t)z * 0x01010101u;
-            }
-            zmask[q] = __builtin_amdgcn_ballot_w64(zs) != 0;  // a zero scale anywhere in the wave
-            // entering a new group (wave-uniform): the accumulator moves to its units
-            fresh[q] = gk != g_cur;
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) ratio[q][j] = 1.0f;
-            if (fresh[q]) {
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) {
-                    ratio[q][j] = sn[q][j] != 0.0f && g_cur >= 0 ? s_cur[j] / sn[q][j] : 1.0f;
-                    if (sn[q][j] != 0.0f) s_cur[j] = sn[q][j];
+                zrep[q][j] = live ? (uint32_t)z * 0x01010101u : 0u;
+                nm[q][j] = live ? 0x0F0F0F0Fu : 0u;
+                ratio[q][j] = 1.0f;
+                if constexpr (FRESH) {
+                    // the units stay those of the previous group across a zero scale
+                    ratio[q][j] = live && g_cur >= 0 ? s_cur[j] / sn : 1.0f;
+                    if (live) s_cur[j] = sn;
                 }
-                g_cur = gk;
             }
+            if constexpr (FRESH) g_cur = gk;
         }
-        // g = 128: the activation operands of two MFMA k-slots are read from LDS ahead of
-        // their MFMAs (32 registers), so each MFMA waits for a read issued long before.  At
-        // g = 32 and 64 (a group boundary every stage or two per stage, with its rescale) the
-        // extra registers would spill: one read per MFMA, as it is needed.
-        constexpr int AP = G == 128 ? 2 : 1;
-        q4::u32x4 aop[AP][4];
+        // g = 128 with 128-row tiles: the activation operands of two MFMA k-slots are read
+        // from LDS ahead of their MFMAs (32 registers), so each MFMA waits for a read issued
+        // long before.  At g = 32 and 64 (a group boundary every stage or two per stage, with
+        // its rescale) and with 256-row tiles the extra registers would spill: one read per
+        // MFMA, as it is needed.
+        constexpr int AP = G == 128 && MI == 4 ? 2 : 1;
+        q4::u32x4 aop[AP][MI];
         q4::u32x4 bnext[NJ];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
@@ -274,43 +284,33 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const uint16_t* __res
 #pragma unroll
                     for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
+                        for (int i = 0; i < MI; ++i)
                             aop[k2][i] = *reinterpret_cast<const q4::u32x4*>(slot + apos[kk + k2] + i * 32 * (BK * 2));
                 }
             }
             const int q = G == 32 ? (kk >> 1) : 0;  // group slot of this MFMA
-            const bool rescale = fresh[q] && (G == 32 ? (kk & 1) == 0 : kk == 0);
+            const bool rescale = FRESH && (G == 32 ? (kk & 1) == 0 : kk == 0);
             q4::u32x4 bop[NJ];
             if constexpr (G == 64) {
                 // decoded one k-slot ahead: slot kk + 1's words while slot kk's MFMAs run
-                // (see the schedule below)
                 if (kk == 0) {
 #pragma unroll
-                    for (int j = 0; j < NJ; ++j) bnext[j] = dequant_word<XF16>(b.w[j][0], zrep[q][j]);
+                    for (int j = 0; j < NJ; ++j) bnext[j] = dequant_word<XF16>(b.w[j][0], zrep[q][j], nm[q][j]);
                 }
 #pragma unroll
-                for (int j = 0; j < NJ; ++j) {
-                    bop[j] = bnext[j];
-                    // zero-scale groups (rare) get a zero operand; a select, so no branch
-                    // splits the slot's code
-                    const uint32_t keep = zmask[q] && sn[q][j] == 0.0f ? 0u : 0xFFFFFFFFu;
-                    bop[j] &= keep;
-                }
+                for (int j = 0; j < NJ; ++j) bop[j] = bnext[j];
                 if (kk < 3) {
 #pragma unroll
-                    for (int j = 0; j < NJ; ++j) bnext[j] = dequant_word<XF16>(b.w[j][kk + 1 < 4 ? kk + 1 : 3], zrep[0][j]);
+                    for (int j = 0; j < NJ; ++j)
+                        bnext[j] = dequant_word<XF16>(b.w[j][kk + 1 < 4 ? kk + 1 : 3], zrep[0][j], nm[0][j]);
                 }
             } else {
 #pragma unroll
-                for (int j = 0; j < NJ; ++j) bop[j] = dequant_word<XF16>(b.w[j][kk], zrep[q][j]);
-                if (zmask[q]) {  // rare: zero the operand of zero-scale groups
-#pragma unroll
-                    for (int j = 0; j < NJ; ++j) bop[j] &= sn[q][j] != 0.0f ? 0xFFFFFFFFu : 0u;
-                }
+                for (int j = 0; j < NJ; ++j) bop[j] = dequant_word<XF16>(b.w[j][kk], zrep[q][j], nm[q][j]);
             }
             const uint8_t* ab = slot + apos[kk];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < MI; ++i) {
                 const q4::u32x4 a = AP == 2 ? aop[(kk & 1) % AP][i]
                                             : *reinterpret_cast<const q4::u32x4*>(ab + i * 32 * (BK * 2));
 #pragma unroll
@@ -327,52 +327,69 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const uint16_t* __res
                         acc[i][j] = mfma32_bf16(a, bop[j], acc[i][j]);
                 }
             }
-            // g = 64, a slot without a group change: each MFMA followed by five VALU
-            // instructions (the next slot's decode), so the decode issues while the matrix
-            // cores work.  On the 70B prefill this takes g = 64 from 571 to 823 TFLOP/s
-            // (its register pressure falls with it); at g = 128 and g = 32 the early decode
-            // and the forced order were 1-3% slower than the compiler's own, so they keep it.
-            if constexpr (G == 64) {
-                if (!rescale) {
-#pragma unroll
-                    for (int r = 0; r < 8; ++r) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // five VALU
-                    }
-                }
-            }
         }
     };
 
-    // ---- pipeline: stages s and s+1 are in flight when stage s starts
-    constexpr int LOADS = 4 + NJ * ((G >= 64 ? 1 : 2) + NGS + (SYM ? 0 : 1));  // vector loads per stage
-    constexpr int WAIT = (LOADS & 15) | ((LOADS >> 4) << 14) | (0x7 << 4) | (0xF << 8);  // vmcnt(LOADS)
-    BStage<G, NJ> bs[3];
-    load_a(sb);
-    load_b(bs[0], sb);
-    __builtin_amdgcn_sched_barrier(0);
-    load_a(sb + 1);
-    load_b(bs[1], sb + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    auto step = [&](int s, BStage<G, NJ>& cur, BStage<G, NJ>& nxt2) {
-        // This wave's loads of stage s have landed (those of stage s+1 stay in flight); the
-        // barrier then makes every wave's activation DMA visible and frees slot s-1.  A plain
-        // s_barrier: __syncthreads() would also wait for the DMA of stage s+1.
+    // ---- pipeline: stages s .. s + AHEAD - 1 are in flight when stage s starts
+    constexpr int LOADS = MI + NJ * ((G >= 64 ? 1 : 2) + NGS + (SYM ? 0 : 1));  // vector loads per stage
+    constexpr int WN = LOADS * (AHEAD - 1);  // loads left in flight once stage s has landed
+    static_assert(WN < 64, "vmcnt holds 6 bits");
+    constexpr int WAIT = (WN & 15) | ((WN >> 4) << 14) | (0x7 << 4) | (0xF << 8);  // vmcnt(WN)
+    BStage<G, NJ> bs[AHEAD + 1];
+#pragma unroll
+    for (int a = 0; a < AHEAD; ++a) {
+        load_a(sb + a);
+        load_b(bs[a], sb + a);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    auto step = [&](int s, BStage<G, NJ>& cur, BStage<G, NJ>& nxt, auto fresh_tag) {
+        // This wave's loads of stage s have landed (those of the stages after it stay in
+        // flight); the barrier then makes every wave's activation DMA visible and frees the
+        // slot of stage s - 1.  A plain s_barrier: __syncthreads() would also wait for the
+        // loads still in flight.
         __builtin_amdgcn_s_waitcnt(WAIT);
         asm volatile("s_barrier" ::: "memory");
-        load_a(s + 2);                     // (past the last stage: offsets off the end)
-        load_b(nxt2, s + 2);
+        load_a(s + AHEAD);                 // (past the last stage: offsets off the end)
+        load_b(nxt, s + AHEAD);
         __builtin_amdgcn_sched_barrier(0);
-        compute(cur, s);
+        compute(cur, s, fresh_tag);
     };
+    // The loop is unrolled over the register ring (AHEAD + 1 stages) and, at g = 128, over
+    // the group's two stages, so that whether a stage opens a group is known at compile time
+    // (a branch between two compute variants makes the compiler copy the accumulators at
+    // the join).  A split starts on an even stage (plan() keeps per even).
+    constexpr std::true_type kFresh{};
+    constexpr std::integral_constant<bool, G != 128> kOdd{};  // a stage at an odd index
     int s = sb;
-    for (; s + 3 <= se; s += 3) {
-        step(s, bs[0], bs[2]);
-        step(s + 1, bs[1], bs[0]);
-        step(s + 2, bs[2], bs[1]);
+    if constexpr (AHEAD == 1) {  // register ring of 2: the unroll by 2 covers both
+        for (; s + 2 <= se; s += 2) {
+            step(s, bs[0], bs[1], kFresh);
+            step(s + 1, bs[1], bs[0], kOdd);
+        }
+        if (s < se) step(s, bs[0], bs[1], kFresh);
+    } else if constexpr (G == 128) {
+        for (; s + 6 <= se; s += 6) {
+            step(s, bs[0], bs[2], kFresh);
+            step(s + 1, bs[1], bs[0], kOdd);
+            step(s + 2, bs[2], bs[1], kFresh);
+            step(s + 3, bs[0], bs[2], kOdd);
+            step(s + 4, bs[1], bs[0], kFresh);
+            step(s + 5, bs[2], bs[1], kOdd);
+        }
+        if (s < se) step(s, bs[0], bs[2], kFresh);
+        if (s + 1 < se) step(s + 1, bs[1], bs[0], kOdd);
+        if (s + 2 < se) step(s + 2, bs[2], bs[1], kFresh);
+        if (s + 3 < se) step(s + 3, bs[0], bs[2], kOdd);
+        if (s + 4 < se) step(s + 4, bs[1], bs[0], kFresh);
+    } else {
+        for (; s + 3 <= se; s += 3) {
+            step(s, bs[0], bs[2], kFresh);
+            step(s + 1, bs[1], bs[0], kFresh);
+            step(s + 2, bs[2], bs[1], kFresh);
+        }
+        if (s < se) step(s, bs[0], bs[2], kFresh);
+        if (s + 1 < se) step(s + 1, bs[1], bs[0], kFresh);
     }
-    if (s < se) step(s, bs[0], bs[2]);
-    if (s + 1 < se) step(s + 1, bs[1], bs[0]);
 
     // epilogue: back to true units, store (y, or this split's fp32 partial sums).  Lane
     // (col, h), register r of a 32x32 tile holds row (r & 3) + 4h + 8(r >> 2), column col.
@@ -382,7 +399,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const uint16_t* __res
         const int nn = wn0 + 32 * j + col;
         if (nn >= N) continue;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int mm = m0 + 32 * i + (r & 3) + 4 * h + 8 * (r >> 2);
@@ -408,43 +425,47 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits,
     }
 }
 
-// The tile and split for a product: the 128 x 256 tile while it gives at least one
-// workgroup per CU; otherwise the 128 x 128 tile, and, when a workspace is given and that
-// still leaves CUs idle, the K range split so that the workgroups cover every CU (each split
-// at least 8 stages, at most 16 splits).
+// The tile and split for a product.  From m = 512 on, the 256 x 128 tile (each decoded
+// weight word feeds 8 MFMAs instead of 4) while it gives at least one workgroup per CU;
+// otherwise the 128 x 256 tile while that does; otherwise the 128 x 128 tile, and, when a
+// workspace is given and that still leaves CUs idle, the K range split so that the
+// workgroups cover every CU (each split at least 8 stages, at most 16 splits).
 struct GemmPlan {
-    int nj;     // 32-row weight blocks per wave: 2 (128 x 256 tile) or 1 (128 x 128)
+    int nj;     // 32-row weight blocks per wave: 2 (128 x 256 tile) or 1
+    int mi;     // 32-row activation blocks per wave: 8 (256 x 128 tile) or 4
     int per;    // stages per split (0: no split)
     int splits;
 };
 GemmPlan plan(int64_t m, int64_t n, int64_t k, int num_cus, bool may_split) {
     const int cus = num_cus > 0 ? num_cus : 256;
-    const int64_t mtiles = (m + BM - 1) / BM;
+    const int64_t mtiles = (m + 127) / 128;
     const int64_t stages = (k + BK - 1) / BK;
-    if (mtiles * ((n + 255) / 256) >= cus) return {2, 0, 1};
+    if (m >= 512 && ((m + 255) / 256) * ((n + 127) / 128) >= cus) return {1, 8, 0, 1};
+    if (mtiles * ((n + 255) / 256) >= cus) return {2, 4, 0, 1};
     const int64_t tiles = mtiles * ((n + 127) / 128);
-    if (!may_split || tiles >= cus) return {1, 0, 1};
+    if (!may_split || tiles >= cus) return {1, 4, 0, 1};
     int64_t splits = (cus + tiles - 1) / tiles;
     if (splits > 16) splits = 16;
     if (splits > stages / 8) splits = stages / 8;
-    if (splits < 2) return {1, 0, 1};
-    const int64_t per = (stages + splits - 1) / splits;
-    return {1, (int)per, (int)((stages + per - 1) / per)};
+    if (splits < 2) return {1, 4, 0, 1};
+    // per even: every split starts on the first stage of a g = 128 group
+    const int64_t per = ((stages + splits - 1) / splits + 1) & ~(int64_t)1;
+    return {1, 4, (int)per, (int)((stages + per - 1) / per)};
 }
 
-template <int G, bool SYM, int NJ>
-void launch_nj(const void* x, int xd, int m, const uint32_t* qw, const uint16_t* sc, const uint32_t* zr,
-               int n, int k, void* y, int ydt, int per, int splits, float* part, hipStream_t st) {
-    const int mtiles = (m + BM - 1) / BM, ntiles = (n + 128 * NJ - 1) / (128 * NJ);
+template <int G, bool SYM, int NJ, int MI>
+void launch_tile(const void* x, int xd, int m, const uint32_t* qw, const uint16_t* sc, const uint32_t* zr,
+                 int n, int k, void* y, int ydt, int per, int splits, float* part, hipStream_t st) {
+    const int mtiles = (m + 32 * MI - 1) / (32 * MI), ntiles = (n + 128 * NJ - 1) / (128 * NJ);
     const dim3 grid((unsigned)(mtiles * ntiles * splits)), block(NTHREADS);
-    const size_t lds = (size_t)RING * A_STAGE;
+    const size_t lds = (size_t)ring_of(MI) * a_stage_of(MI);
     const uint16_t* xp = reinterpret_cast<const uint16_t*>(x);
     if (xd == 1)
-        hipLaunchKernelGGL((gemm_kernel<G, SYM, true, NJ>), grid, block, lds, st, xp, m, qw, sc, zr, n, k, y, ydt,
-                           per, part);
+        hipLaunchKernelGGL((gemm_kernel<G, SYM, true, NJ, MI>), grid, block, lds, st, xp, m, qw, sc, zr, n, k, y,
+                           ydt, per, part);
     else
-        hipLaunchKernelGGL((gemm_kernel<G, SYM, false, NJ>), grid, block, lds, st, xp, m, qw, sc, zr, n, k, y, ydt,
-                           per, part);
+        hipLaunchKernelGGL((gemm_kernel<G, SYM, false, NJ, MI>), grid, block, lds, st, xp, m, qw, sc, zr, n, k, y,
+                           ydt, per, part);
 }
 
 template <int G, bool SYM>
@@ -452,13 +473,15 @@ hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16
                   const uint32_t* zr, int n, int k, void* y, int ydt, float* ws, int64_t ws_floats,
                   hipStream_t st, const char** kname) {
     GemmPlan pl = plan(m, n, k, q4k_device_cus(), ws != nullptr);
-    if (pl.splits > 1 && (int64_t)pl.splits * m * n > ws_floats) pl = {1, 0, 1};
+    if (pl.splits > 1 && (int64_t)pl.splits * m * n > ws_floats) pl = {1, 4, 0, 1};
     float* part = pl.splits > 1 ? ws : nullptr;
     *kname = xd == 1 ? "q4_gemm_mfma_f16" : "q4_gemm_mfma_bf16";
-    if (pl.nj == 2)
-        launch_nj<G, SYM, 2>(x, xd, m, qw, sc, zr, n, k, y, ydt, 0, 1, nullptr, st);
+    if (pl.mi == 8)
+        launch_tile<G, SYM, 1, 8>(x, xd, m, qw, sc, zr, n, k, y, ydt, 0, 1, nullptr, st);
+    else if (pl.nj == 2)
+        launch_tile<G, SYM, 2, 4>(x, xd, m, qw, sc, zr, n, k, y, ydt, 0, 1, nullptr, st);
     else
-        launch_nj<G, SYM, 1>(x, xd, m, qw, sc, zr, n, k, y, ydt, pl.per, pl.splits, part, st);
+        launch_tile<G, SYM, 1, 4>(x, xd, m, qw, sc, zr, n, k, y, ydt, pl.per, pl.splits, part, st);
     hipError_t e = q4k_launched(*kname);
     if (e != hipSuccess || part == nullptr) return e;
     const int64_t count = (int64_t)m * n;
