@@ -161,7 +161,6 @@ q4_status q4_w4a16_gemm_out(const void* x, q4_dtype x_dtype, int64_t m,
                             int64_t n, int64_t k, int32_t group_size, int32_t symmetric,
                             void* y, q4_dtype y_dtype, hipStream_t stream);
 
-/* One problem of a grouped call: y = x . x_hat^T for one packed weight. */
 /* q4_w4a16_gemm_out with a workspace for products that would leave compute units idle
  * (mid-size batches on narrow weights, [FL7] §Batch와 Context에 따라 속도가 달라진다: between
  * the bandwidth-bound decode and the compute-bound prefill).  When the product runs as the
@@ -182,6 +181,7 @@ q4_status q4_w4a16_gemm_ws(const void* x, q4_dtype x_dtype, int64_t m,
  * would not split it, -1 for sizes the entry points reject. */
 int64_t q4_w4a16_gemm_workspace(int64_t m, int64_t n, int64_t k, int32_t group_size);
 
+/* One problem of a grouped call: y = x . x_hat^T for one packed weight. */
 typedef struct {
     const void* x;            /* [m][k] activations, in the dtype of the call */
     const uint32_t* qweight;  /* [n][k/8] packed codes */

@@ -7,20 +7,22 @@
 // contraction with the dequantization fused into the operand path (path A of
 // §Kernel이 없으면 압축 이점이 사라진다).
 //
-// Tiles.  A workgroup of 4 waves computes a 128 x 256 block of y (128 activation rows x
-// 256 weight rows); wave w owns all 128 rows x weight rows [64w, 64w+64) as 4 x 2 tiles
-// of v_mfma_f32_32x32x16 (bf16 or fp16 inputs, fp32 accumulation).  The K loop walks 64
-// columns per stage.
+// Tiles.  A workgroup of 4 waves computes a 32 MI x 128 NJ block of y (activation rows x
+// weight rows); every wave owns all 32 MI activation rows and 32 NJ weight rows as MI x NJ
+// tiles of v_mfma_f32_32x32x16 (bf16 or fp16 inputs, fp32 accumulation): 128 x 256
+// (MI = 4, NJ = 2), 128 x 128 (4, 1) or 256 x 128 (8, 1, where each decoded weight word
+// feeds 8 MFMAs).  The K loop walks 64 columns per stage.
 //
-// Operands.  Activations are shared by the 4 waves: they go from HBM/L2 straight into a
-// three-stage LDS ring with buffer-to-LDS loads (no registers), two stages ahead of the
-// MFMAs, in an XOR-swizzled layout (16-byte chunk c of row r at position c ^ (r & 7)) that
-// makes both the 1 KB loads and the operand reads bank-conflict free.  Weights are not
-// shared: each lane of the 32x32x16 MFMA's weight operand needs 8 consecutive k of one
-// weight row, which is exactly one packed word, so every lane loads its own words (and
-// the scale and zero point of its row) into registers two stages ahead and dequantizes
-// them right before the MFMA.  Every stage issues the same loads in the same order, so
-// each wait is a fixed count and the two stages in flight stay in flight.
+// Operands.  Activations are shared by the 4 waves: they go from HBM/L2 straight into an
+// LDS ring with buffer-to-LDS loads (no registers), in an XOR-swizzled layout (16-byte
+// chunk c of row r at position c ^ (r & 7)) that makes both the 1 KB loads and the operand
+// reads bank-conflict free: three stages of 128 rows loaded two ahead, or two stages of
+// 256 rows loaded one ahead.  Weights are not shared: each lane of the 32x32x16 MFMA's
+// weight operand needs 8 consecutive k of one weight row, which is exactly one packed word,
+// so every lane loads its own words (and the scale and zero point of its row) into
+// registers with its stage's activations and dequantizes them right before the MFMA.
+// Every stage issues the same loads in the same order, so each wait is a fixed count and
+// the stages in flight stay in flight.
 //
 // k slots.  An MFMA consumes 16 k: lanes 0-31 supply 8 and lanes 32-63 another 8.  With
 // g >= 64 lane half h takes words 4h..4h+3 of the stage (one 16-byte load) and MFMA kk
