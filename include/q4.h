@@ -335,6 +335,19 @@ q4_status q4_gptq_quantize_act_order(const void* w, q4_dtype w_dtype, int64_t n,
 /* Element counts of the three packed arrays (payload + metadata, [FL7] §Memory 계산은
  * Payload와 Metadata로 나눈다): n*k/8 words, n*(k/g) scales, n*ceil((k/g)/8) words.
  * Return -1 for arguments the entry points would reject. */
+/* Corrupted scale detection ([FL7] §Quantized Artifact Security, Runtime: a loaded
+ * quantized artifact is checked, not trusted).  Every scale this format stores is an fp16
+ * value >= 0 (a group's range over 15 or its largest magnitude over 7, rounded; 0 or -0 for
+ * a group of zeros), so a scale that is infinite, NaN or negative (sign set, nonzero
+ * magnitude) marks a corrupted artifact.  scales: [n][k/group_size] fp16 bits, 2-byte
+ * aligned.  result: device memory of 3 int64, 8-byte aligned, overwritten (no clearing
+ * needed): [0] the number of non-finite scales, [1] the number of negative scales, [2] the
+ * flat index n*(k/g)+g of the first bad scale, or -1 when there is none.  Asynchronous on
+ * stream, like the other calls; the values are exact integers whatever the launch order.
+ * Errors: Q4_ERR_GROUP, Q4_ERR_SHAPE (as q4_dequant), Q4_ERR_NULL, Q4_ERR_ALIGN. */
+q4_status q4_check_scales(const uint16_t* scales, int64_t n, int64_t k, int32_t group_size,
+                          int64_t* result, hipStream_t stream);
+
 int64_t q4_qweight_words(int64_t n, int64_t k);
 int64_t q4_scale_count(int64_t n, int64_t k, int32_t group_size);
 int64_t q4_zero_words(int64_t n, int64_t k, int32_t group_size);

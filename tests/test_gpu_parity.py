@@ -10,6 +10,7 @@ import pytest
 import torch
 
 import oracle
+from oracle import scales as oscales
 import pins
 from clip_check import check_clip_choice
 import synthetic
@@ -769,6 +770,37 @@ def test_gemm_splitk_cases(m, n, k, g, xdtype, sym):
     # 16-bit output: the rounding of the same fp32 sums
     yh = q4.q4_w4a16_gemm(x.to(DEV), p, out_dtype=torch.bfloat16, workspace=wsv)
     assert torch.equal(yh.cpu(), torch.from_numpy(y).to(torch.bfloat16))
+
+
+# corrupted scale detection: ragged n, k % 64 == 32, sym and asym, the 7B MLP shape
+@pytest.mark.parametrize("n,k,g,sym", [(300, 1024, 128, False), (77, 4096 + 32, 32, True),
+                                       (11008, 4096, 128, False), (5, 64, 64, True)])
+def test_check_scales(n, k, g, sym):
+    """A packed weight from the quantizer reports no corrupted scale; scales overwritten
+    with infinities, NaNs and negative values (and -0, which stays legal) give the oracle's
+    counts and first index, through the binding and through the C ABI into a guarded
+    result."""
+    w = torch.from_numpy(pins.random_weights(n + k, max(n, 12), k)[:n])
+    note(f"check scales n={n} k={k} g={g} sym={sym}")
+    p, _ = pack_guarded(w.to(DEV), g, sym)
+    assert q4.q4_check_scales(p) == (0, 0, -1)
+    assert q4.q4_last_kernels() == ["q4_check_scales_clear", "q4_check_scales", "q4_check_scales_finish"]
+    so = p.scales.cpu().numpy().view(np.uint16).copy()
+    G = k // g
+    rng = np.random.default_rng(n + g)
+    idx = rng.choice(n * G, size=min(40, n * G), replace=False)
+    pats = np.array([0x7C00, 0xFC00, 0x7E00, 0xBC00, 0x8001, 0x8000, 0xFE01], dtype=np.uint16)
+    flat = so.reshape(-1)
+    flat[idx] = pats[np.arange(idx.size) % pats.size]
+    p.scales.copy_(torch.from_numpy(so.view(np.float16)).to(DEV))
+    exp = oscales.check_scales(so)
+    assert exp[0] > 0 and exp[1] > 0
+    rb, rv = guarded((3,), torch.int64, -7)
+    assert q4.lib().q4_check_scales(p.scales.data_ptr(), n, k, g, rv.data_ptr(), None) == 0
+    torch.cuda.synchronize()
+    assert guard_intact(rb, sentinel=-7), "store outside the result"
+    assert tuple(rv.cpu().tolist()) == exp
+    assert q4.q4_check_scales(p) == exp
 
 
 def test_gemm_splitk_workspace_rules():

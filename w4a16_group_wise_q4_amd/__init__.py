@@ -21,14 +21,14 @@ from __future__ import annotations
 import ctypes
 import os
 from dataclasses import dataclass
-from typing import Optional
+from typing import Optional, Tuple
 
 import torch
 
 from . import _build
 
 __all__ = ["PackedWeight", "q4_quantize_pack", "q4_quantize_pack_grouped", "q4_quantize_pack_mse",
-           "q4_dequant",
+           "q4_dequant", "q4_check_scales",
            "q4_w4a16_gemm",
            "q4_w4a16_gemm_grouped", "q4_last_kernel", "q4_last_kernels", "q4_last_launch_count",
            "q4_source_digest", "StaleLibraryError", "KvCache", "empty_kv_cache",
@@ -47,7 +47,7 @@ EXPORTED = ("q4_quantize_pack", "q4_quantize_pack_grouped", "q4_quantize_pack_ms
             "q4_kv_attention_workspace", "q4_kv_attention_noalloc",
             "q4_kv_attention_noalloc_max_bytes", "q4_gptq_quantize", "q4_gptq_workspace",
             "q4_gptq_quantize_act_order", "q4_gptq_act_order_workspace", "q4_qweight_words",
-            "q4_scale_count", "q4_zero_words", "q4_status_str", "q4_last_kernel",
+            "q4_scale_count", "q4_zero_words", "q4_check_scales", "q4_status_str", "q4_last_kernel",
             "q4_last_kernels", "q4_last_launch_count", "q4_layout_version", "q4_source_digest")
 
 
@@ -112,6 +112,8 @@ def _load():
     lib.q4_quantize_pack_grouped.restype = ctypes.c_int
     lib.q4_dequant.argtypes = [vp, vp, vp, i64, i64, i32, i32, vp, ctypes.c_int, vp]
     lib.q4_dequant.restype = ctypes.c_int
+    lib.q4_check_scales.argtypes = [vp, i64, i64, i32, vp, vp]
+    lib.q4_check_scales.restype = ctypes.c_int
     lib.q4_w4a16_gemm.argtypes = [vp, ctypes.c_int, i64, vp, vp, vp, i64, i64, i32, i32, vp, vp]
     lib.q4_w4a16_gemm.restype = ctypes.c_int
     lib.q4_w4a16_gemm_out.argtypes = [vp, ctypes.c_int, i64, vp, vp, vp, i64, i64, i32, i32, vp,
@@ -388,6 +390,18 @@ def q4_dequant(p: PackedWeight, out_dtype: torch.dtype = torch.float32,
                               p.n, p.k, p.group_size, int(p.symmetric), _dev_ptr(o),
                               _DTYPE_CODE[o.dtype], _stream(o)))
     return o
+
+
+def q4_check_scales(p: PackedWeight) -> Tuple[int, int, int]:
+    """Corrupted scale detection: (number of non-finite scales, number of negative scales,
+    flat index of the first such scale or -1) over p's fp16 scales (q4_check_scales)."""
+    _need_cuda("scales", p.scales)
+    _check_packed(p, p.scales.device)
+    res = torch.empty(3, dtype=torch.int64, device=p.scales.device)
+    _check(_load().q4_check_scales(_dev_ptr(p.scales), p.n, p.k, p.group_size, _dev_ptr(res),
+                                   _stream(res)))
+    nonfinite, negative, first = (int(v) for v in res.cpu().tolist())
+    return nonfinite, negative, first
 
 
 def q4_w4a16_gemm_workspace(m: int, n: int, k: int, group_size: int) -> int:

@@ -171,6 +171,18 @@ q4_status q4_dequant(const uint32_t* qweight, const uint16_t* scales, const uint
     return finish(e, name);
 }
 
+q4_status q4_check_scales(const uint16_t* scales, int64_t n, int64_t k, int32_t group_size,
+                          int64_t* result, hipStream_t stream) {
+    begin_call();
+    const q4_status st = check_layout(n, k, group_size);
+    if (st != Q4_OK) return st;
+    if (!scales || !result) return Q4_ERR_NULL;
+    if (!aligned(scales, 2) || !aligned(result, 8)) return Q4_ERR_ALIGN;
+    const char* name = "";
+    const hipError_t e = q4k_check_scales(scales, n * (k / group_size), result, stream, &name);
+    return finish(e, name);
+}
+
 }  // extern "C"
 
 // Compute units per device.  Threads that race on the first lookup store the same value.

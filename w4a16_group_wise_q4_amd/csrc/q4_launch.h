@@ -51,6 +51,10 @@ hipError_t q4k_kv_attention(const void* q, int q_dtype, const uint32_t* kq, cons
 // Compute units of the current device, looked up once per device (256 if the query
 // fails); safe to call from several threads.
 int q4k_device_cus();
+// Corrupted scale detection over count fp16 scales: result (3 int64, device) = non-finite
+// count, negative count, first bad index or -1.
+hipError_t q4k_check_scales(const uint16_t* scales, int64_t count, int64_t* result, hipStream_t stream,
+                            const char** kname);
 
 // The fixed per-device scratch of the no-allocation attention entry point: its size in
 // bytes, and its device address on the current device (looked up once per device; a
