@@ -333,9 +333,10 @@ def test_gemv_mlp_sweep(idx, g, sym):
 
 def gemv_kernels(xdtype=torch.bfloat16):
     """Names of the decode kernels for an activation dtype: the tile kernel (m <= 4), the
-    wide tile kernel (4 < m <= 16) and the streaming kernel (shapes neither takes)."""
+    wide tile kernel (4 < m <= 16), the resident kernel (8 < m <= 16 with many tiles) and
+    the streaming kernel (shapes none of them takes)."""
     t = "f16" if xdtype == torch.float16 else "bf16"
-    return {f"q4_gemv_tile_{t}", f"q4_gemv_wide_{t}", f"q4_gemv_mfma_{t}"}
+    return {f"q4_gemv_tile_{t}", f"q4_gemv_wide_{t}", f"q4_gemv_resident_{t}", f"q4_gemv_mfma_{t}"}
 
 
 # (m, n, k): every slice width of the tile kernel (2, 4, 8, 12 and 16 units per wave, two
@@ -440,6 +441,94 @@ def test_gemm_grouped_wide_pair(m, xdtype):
                             what="grouped pair")
 
 
+def resident_fits(g, m, k, tiles, num_cus=256):
+    """Whether the launcher picks the resident kernel: 8 < m <= 16, slices of 4 or 8 units
+    over at most eight waves, an even group count, all activations (16 rows per 128-column
+    unit) and two regions of partial sums within 160 KiB of LDS, and at least two tiles per
+    workgroup the CUs hold at that LDS size."""
+    if not 8 < m <= 16 or k % 128 or (k // g) % 2:
+        return False
+    units = k // 128
+    shapes = [(-(-units // u), u) for u in (4, 8) if -(-units // u) <= 8]
+    if not shapes:
+        return False
+    waves = max(sw for sw, _ in shapes)
+    lds = units * 16 * 256 + 2 * waves * 64 * 16
+    if lds > 160 * 1024:
+        return False
+    return tiles >= 2 * num_cus * (160 * 1024 // lds)
+
+
+# (m, n, k, g): resident products -- ragged last tiles (8, 15, 6 rows), workgroups of three
+# tiles (odd: the tile after the last pair), of two and three tiles in one launch, and of two
+# (even: the pair loop's last prefetch reads nothing); slices of 4 units (8 and 4 waves) and
+# of 8 units over 5 waves with a short last slice (k = 4608)
+RESIDENT_CASES = [(16, 8200, 4096, 128), (12, 9999, 4096, 64), (9, 16390, 2048, 32),
+                  (16, 8192, 4608, 128), (13, 8300, 4608, 32)]
+
+
+@pytest.mark.parametrize("m,n,k,g", RESIDENT_CASES)
+@pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("sym", [False, True])
+def test_gemv_resident_cases(m, n, k, g, xdtype, sym):
+    w = torch.from_numpy(pins.random_weights(n + 13 * k + m + g, n, k))
+    x = synthetic.activations(m, k, seed=m * 29 + k).to(xdtype)
+    note(f"gemv resident m={m} n={n} k={k} g={g} {xdtype} sym={sym}")
+    p, _ = pack_guarded(w.to(DEV), g, sym)
+    assert resident_fits(g, m, k, -(-n // 16))
+    y, kname = run_linear(x, p)  # stores outside y are checked there
+    t = "f16" if xdtype == torch.float16 else "bf16"
+    assert kname == f"q4_gemv_resident_{t}"
+    packed = assert_pack_exact(p, host_input(w), g, sym)
+    # every 5th column, the first tiles' and the last (ragged) tile's columns
+    cols = np.unique(np.concatenate([np.arange(0, n, 5), np.arange(0, 48), np.arange(n - 24, n)]))
+    assert_linear_close(y, host_input(x), packed, n, k, g, sym, cols=cols, what=kname)
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float16, torch.bfloat16])
+def test_gemv_resident_output_dtype(out_dtype):
+    """The resident kernel's 16-bit epilogue: y rounded once from the fp32 sums, equal to the
+    fp32 result rounded to nearest even."""
+    m, n, k, g = 16, 8200, 4096, 128
+    w = torch.from_numpy(pins.random_weights(91, n, k))
+    x = synthetic.activations(m, k, seed=92).to(DEV)
+    note(f"gemv resident output {out_dtype}")
+    p, _ = pack_guarded(w.to(DEV), g, False)
+    y32 = q4.q4_w4a16_gemm(x, p)
+    assert q4.q4_last_kernel() == "q4_gemv_resident_bf16"
+    yb, yv = guarded((m, n), out_dtype, 0.0)
+    q4.q4_w4a16_gemm(x, p, out=yv)
+    torch.cuda.synchronize()
+    assert q4.q4_last_kernel() == "q4_gemv_resident_bf16"
+    assert torch.equal(yv.cpu(), y32.cpu().to(out_dtype))
+
+
+@pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("g,sym", [(128, False), (32, True)])
+def test_gemm_grouped_resident(xdtype, g, sym):
+    """Three problems sharing x (519 tiles: the launch's workgroups cross problems, ragged
+    last tiles) through the resident kernel; the same problems with one x each take the wide
+    kernel.  Every output of every problem, both ways."""
+    m, k = 16, 4096
+    ns = [4096, 4000 - 3, 200]
+    ws = [torch.from_numpy(pins.random_weights(71 + i, n, k)) for i, n in enumerate(ns)]
+    x = synthetic.activations(m, k, seed=73).to(xdtype)
+    note(f"grouped resident g={g} sym={sym} {xdtype}")
+    packs = [pack_guarded(w.to(DEV), g, sym)[0] for w in ws]
+    packed = [assert_pack_exact(p, host_input(w), g, sym) for w, p in zip(ws, packs)]
+    t = "f16" if xdtype == torch.float16 else "bf16"
+    assert resident_fits(g, m, k, sum(-(-n // 16) for n in ns))
+    for xs, want in ((x.to(DEV), "resident"), ([x.clone().to(DEV) for _ in ns], "wide")):
+        guards = [guarded((m, n), torch.float32, SENTINEL_F32) for n in ns]
+        q4.q4_w4a16_gemm_grouped(xs, packs, outs=[v for _, v in guards])
+        torch.cuda.synchronize()
+        assert q4.q4_last_kernel() == f"q4_gemv_{want}_{t}"
+        for p, pk, (gb, gv) in zip(packs, packed, guards):
+            assert guard_intact(gb), "store outside y"
+            assert_linear_close(gv.cpu().numpy(), host_input(x), pk, p.n, k, g, sym,
+                                what=f"grouped {want}")
+
+
 @pytest.mark.parametrize("m,n,k", TILE_CASES)
 @pytest.mark.parametrize("g", [32, 64, 128])
 @pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
@@ -530,12 +619,14 @@ def ranged_activations(kind, m, k, seed):
 
 @pytest.mark.parametrize("kind", ["narrow", "huge", "tiny", "wide", "subnormal", "split"])
 @pytest.mark.parametrize("m,n,k,g", [(1, 70, 4096, 128), (3, 40, 2048, 32), (2, 33, 5120, 64),
-                                     (8, 40, 2048, 128), (1, 40, 2048 + 64, 64)])
+                                     (8, 40, 2048, 128), (1, 40, 2048 + 64, 64),
+                                     (16, 8200, 4096, 128)])
 def test_gemv_activation_ranges(kind, m, n, k, g):
     """bf16 activations of every exponent range the decode kernels distinguish: the tile
     kernel converts a slice to exact fp16 when its nonzero exponents span at most 29
-    binades and keeps the exact bf16 operand otherwise; the other kernels keep the bf16
-    operand.  Each result must meet the bound whichever route a wave took."""
+    binades and keeps the exact bf16 operand otherwise; the other kernels (wide, resident,
+    streaming) keep the bf16 operand.  Each result must meet the bound whichever route a
+    wave took."""
     w = torch.from_numpy(pins.random_weights(n + k + g, max(n, 12), k)[:n])
     x = ranged_activations(kind, m, k, seed=m * 29 + k)
     note(f"gemv activation range {kind} m={m} n={n} k={k} g={g}")

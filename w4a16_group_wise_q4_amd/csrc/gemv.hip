@@ -523,10 +523,20 @@ hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16
         } else {
             sc4 = ((uintptr_t)sc & 3) == 0;
         }
+        // the resident kernel stages one x for every problem of the launch (8 < m <= 16)
+        bool one_x = true;
+        if (batch != nullptr)
+            for (int i = 1; i < batch->count; ++i) one_x = one_x && batch->p[i].x == batch->p[0].x;
         int upw = 0, tw = 0, wide = 0;
-        const bool fits = sc4 && (q4t::tile_shape(G, m, k, tiles, num_cus, &upw, &tw) ||
-                                  (wide = q4t::wide_shape(G, m, k, &upw, &tw)));
-        if (wide && q4t::wide_pair(tiles, num_cus)) wide = 2;
+        bool fits = false;
+        if (sc4 && one_x && q4t::resident_shape(G, m, k, tiles, num_cus, &upw, &tw)) {
+            fits = true;
+            wide = 3;
+        } else {
+            fits = sc4 && (q4t::tile_shape(G, m, k, tiles, num_cus, &upw, &tw) ||
+                           (wide = q4t::wide_shape(G, m, k, &upw, &tw)));
+            if (wide && q4t::wide_pair(tiles, num_cus)) wide = 2;
+        }
         if (fits) {
             GemvBatch one{};
             if (batch == nullptr) {

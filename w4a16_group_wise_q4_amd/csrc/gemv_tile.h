@@ -38,9 +38,14 @@
 // LDS (16-byte vectors): S x [m][UPW*16] activation slices | S x 64 x MQ partial sums.
 #pragma once
 
+#include <map>
+#include <mutex>
+#include <tuple>
 #include <type_traits>
 
 #include "q4_device.h"
+
+int q4k_device_cus();
 
 namespace q4t {
 
@@ -70,6 +75,9 @@ __device__ __forceinline__ void load_dwords(q4::rsrc rs, int off, uint32_t (&v)[
     }
     if constexpr (NV % 2 == 1) v[NV - 1] = q4::buf_load_x1(rs, off + 4 * (NV - 1), 0);
 }
+
+// Vector loads that load_dwords<nv> issues.
+constexpr int dword_loads(int nv) { return nv / 4 + (nv % 4 >= 2 ? 1 : 0) + nv % 2; }
 
 __device__ __forceinline__ void swap32(uint32_t& a, uint32_t& b) {
     const auto t = __builtin_amdgcn_permlane32_swap(a, b, false, false);
@@ -550,6 +558,252 @@ __global__ __launch_bounds__(512) void gemv_wide_kernel(const q4::GemvBatch bt, 
     }
 }
 
+// Resident kernel (8 < m <= 16, all m x K activations within the LDS budget, at least two
+// tiles per workgroup): persistent workgroups.  Each workgroup stages the whole of x into
+// LDS once, with direct-to-LDS loads of 4 whole rows x 256 bytes swizzled exactly as in the
+// wide kernel's ring (unit u, row R: chunk c at position c ^ R), and then serves tiles
+// b, b + P, b + 2P, ... of the batch (P workgroups).  Per tile, wave w takes units
+// [w*UPW, w*UPW + nu) of the tile's 16 rows as in the tile kernel.  Before computing a tile
+// it issues every load of its slice of the next one (into a second register set; offsets
+// past the buffers when there is no next tile, so the wait counts never depend on a
+// branch), which keeps one tile's weights in flight per wave.  The cross-wave sums of
+// consecutive tiles alternate between two LDS regions, so one barrier per tile orders
+// them.  Each staged activation byte feeds every tile the workgroup serves, where the wide
+// kernel stages all of x again for each 16-row tile: at m = 16 the wide kernel moves four
+// activation bytes through each CU's memory pipeline per weight byte.  With one tile per
+// workgroup, or m <= 8, the wide kernel measured faster (the staging is not shared, or is
+// small, and one workgroup per CU hides less latency than the wide kernel's two).
+template <int G, bool SYM, bool XF16, int UPW, bool GROUPED>
+__global__ __launch_bounds__(512) void gemv_resident_kernel(const q4::GemvBatch bt, int M, int K, int tiles) {
+    constexpr int NG = 128 / G, RPG = 4 / NG, GPS = UPW * NG, SV = GPS / 2;
+    constexpr int ZOFF = GPS % 8 == 0 ? 0 : 8 - gcd8(GPS);
+    constexpr int ZV = (ZOFF + GPS + 7) / 8;
+    constexpr int MR = 16;              // activation rows staged per unit (rows past m read nothing)
+    constexpr int UNIT_LDS = MR * 256;  // bytes of one unit's activation rows
+    // vector loads per tile and wave, in issue order: scales, zero points, packed words
+    constexpr int nvec = dword_loads(SV) + (SYM ? 0 : dword_loads(ZV)) + UPW;
+    static_assert(nvec < 64, "vmcnt range");
+    constexpr int WAIT_TILE = (nvec & 15) | ((nvec >> 4) << 14) | (0x7 << 4) | (0xF << 8);  // vmcnt(nvec)
+    constexpr int WAIT_ALL = (0x7 << 4) | (0xF << 8);                                         // vmcnt(0)
+    extern __shared__ q4::u32x4 lds[];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int S = blockDim.x >> 6;
+    const int P = gridDim.x;
+    const int r = lane & 15, c = lane >> 4;
+    const int KW = K >> 3, units = K >> 7, ng = K / G, zw = (ng + 7) >> 3;
+    const int U0 = w * UPW, G0 = U0 * NG;
+    const int nu = units - U0 < UPW ? units - U0 : UPW;
+    uint8_t* xs = reinterpret_cast<uint8_t*>(lds);
+    float* red = reinterpret_cast<float*>(xs + units * UNIT_LDS);  // 2 regions of S x 64 x 4
+
+    // ---- every activation row of the batch's shared x into LDS: units * MR/4 loads of 1 KB,
+    // dealt round-robin to the waves.  Rows past m read nothing (and are never read back).
+    {
+        const q4::rsrc rx = q4::make_rsrc(bt.p[0].x, (uint32_t)M * (uint32_t)K * 2u);
+        const int nl = units * (MR / 4);
+        for (int j = w; j < nl; j += S) {
+            const int u = j / (MR / 4), a = j % (MR / 4);
+            const int R = 4 * a + (lane >> 4);
+            const uint32_t off = R < M ? (uint32_t)(R * K + u * 128 + 8 * ((lane & 15) ^ R)) * 2u : (uint32_t)kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rx, (__attribute__((address_space(3))) void*)(xs + u * UNIT_LDS + a * 1024), 16, (int)off, 0, 0, 0);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    struct Set {
+        uint32_t sv[SV];
+        uint32_t zv[ZV];
+        q4::u32x4 wv[UPW];
+    };
+    // problem and first row of tile t (t < tiles)
+    auto locate = [&](int t, int& pi, int& n0) {
+        pi = 0;
+        if constexpr (GROUPED) {
+#pragma unroll
+            for (int i = 1; i < q4::kMaxGroup; ++i)
+                if (i < bt.count && t >= bt.p[i].tile0) pi = i;
+        }
+        n0 = (t - bt.p[pi].tile0) * 16;
+    };
+    // every load of this wave's slice of tile t; nothing is read when t >= tiles
+    auto issue = [&](int t, Set& s) {
+        const bool live = t < tiles;
+        int pi, n0;
+        locate(live ? t : 0, pi, n0);
+        const int N = bt.p[pi].n;
+        const int rows = N - n0 < 16 ? N - n0 : 16;
+        const bool lr = live && r < rows;
+        const q4::rsrc rs = q4::make_rsrc(bt.p[pi].scales + (int64_t)n0 * ng, (uint32_t)rows * ng * 2u);
+        load_dwords<SV>(rs, lr ? (r * ng + G0) * 2 : kOOB, s.sv);
+        if constexpr (!SYM) {
+            const q4::rsrc rz = q4::make_rsrc(bt.p[pi].zeros + (int64_t)n0 * zw, (uint32_t)rows * zw * 4u);
+            load_dwords<ZV>(rz, lr ? (r * zw + (G0 >> 3)) * 4 : kOOB, s.zv);
+        } else {
+#pragma unroll
+            for (int j = 0; j < ZV; ++j) s.zv[j] = 0;
+        }
+        const q4::rsrc rq = q4::make_rsrc(bt.p[pi].qweight + (int64_t)n0 * KW, (uint32_t)rows * KW * 4u);
+        const int qo = lr ? r * KW * 4 + c * 16 : kOOB;
+#pragma unroll
+        for (int u = 0; u < UPW; ++u) s.wv[u] = q4::buf_load_x4(rq, u < nu ? qo : kOOB, (U0 + u) * 64);
+    };
+
+    // read addresses: row min(l%16, m-1), chunk lb + imm(a) at its swizzled position
+    const int mrow = r < M ? r : M - 1;
+    const int lb = G == 128 ? 4 * c : (G == 64 ? 4 * (c & 1) + 2 * (c >> 1) : c);
+    uint32_t xaddr[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const int imm = G == 128 ? a : (G == 64 ? 8 * (a >> 1) + (a & 1) : 4 * a);
+        xaddr[a] = (uint32_t)(mrow * 256 + (((lb + imm) ^ mrow) << 4));
+    }
+    const uint32_t kMask = q4::vreg_const(0x000F000Fu);
+    const uint32_t kMagic = q4::vreg_const(0x64006400u);
+
+    // dequantize, multiply and sum tile t from set s; cross-wave sum in region par
+    auto compute = [&](int t, Set& s, int par) {
+        uint32_t zs[ZV];
+#pragma unroll
+        for (int j = 0; j < ZV; ++j) zs[j] = s.zv[j];
+        if constexpr (!SYM && ZOFF != 0) {
+            const uint32_t sh = 4u * (uint32_t)(G0 & 7);
+#pragma unroll
+            for (int j = 0; j + 1 < ZV; ++j) zs[j] = __builtin_amdgcn_alignbit(s.zv[j + 1], s.zv[j], sh);
+            zs[ZV - 1] = s.zv[ZV - 1] >> sh;
+        }
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < UPW; ++u) {
+            const bool valid = u < nu;
+            // slots past the slice read a staged unit (their products are discarded)
+            const uint8_t* sb = xs + (valid ? U0 + u : 0) * UNIT_LDS;
+            q4::u32x4 xa[4];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const q4::u32x4 v = *reinterpret_cast<const q4::u32x4*>(sb + xaddr[a]);
+                xa[a] = XF16 ? q4::pair_perm(v) : v;
+            }
+            uint32_t wq[4] = {s.wv[u][0], s.wv[u][1], s.wv[u][2], s.wv[u][3]};
+            if constexpr (G <= 64) {
+                swap32(wq[0], wq[2]);
+                swap32(wq[1], wq[3]);
+            }
+            if constexpr (G == 32) {
+                swap16(wq[0], wq[1]);
+                swap16(wq[2], wq[3]);
+            }
+#pragma unroll
+            for (int h = 0; h < NG; ++h) {
+                const int gi = u * NG + h;
+                const uint32_t sw = s.sv[gi >> 1];
+                const float sc = q4::f16_bits_to_float((uint16_t)((gi & 1) ? (sw >> 16) : sw));
+                int z = 8;
+                if constexpr (!SYM) z = (int)((zs[gi >> 3] >> (4 * (gi & 7))) & 0xFu);
+                q4::f32x4 dv = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (XF16) {
+                    const q4::f16x2 bias = q4::f16_bias_pair((uint32_t)z);
+#pragma unroll
+                    for (int e = 0; e < RPG; ++e) {
+                        const int a = h * RPG + e;
+                        dv = q4::mfma_f16(xa[a], q4::decode_f16_exact(wq[a], bias, kMask, kMagic), dv);
+                    }
+                } else {
+                    const uint32_t zb = q4::bf16_zero_bias(z);
+#pragma unroll
+                    for (int e = 0; e < RPG; ++e) {
+                        const int a = h * RPG + e;
+                        dv = q4::mfma_bf16(xa[a], q4::decode_bf16_exact(wq[a], zb), dv);
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[q] = valid ? acc[q] + sc * dv[q] : acc[q];
+            }
+        }
+        // lane l holds rows m = 4(l/16)..+3 of the tile's column l%16
+        float* rd = red + par * (S * 256);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) rd[(w * 64 + lane) * 4 + q] = acc[q];
+        __syncthreads();
+        if (w == 0) {
+            int pi, n0;
+            locate(t, pi, n0);
+            const int N = bt.p[pi].n;
+            const int rows = N - n0 < 16 ? N - n0 : 16;
+            float sum[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int v = 0; v < S; ++v)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) sum[q] += rd[(v * 64 + lane) * 4 + q];
+            const q4::rsrc ry = q4::make_rsrc(bt.p[pi].y, (uint32_t)M * (uint32_t)N * q4::y_bytes(bt.ydt));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int m = 4 * c + q;
+                const bool st = m < M && r < rows;
+                const uint32_t off = st ? ((uint32_t)m * (uint32_t)N + (uint32_t)(n0 + r)) * q4::y_bytes(bt.ydt) : kStoreOOB;
+                q4::store_y(ry, off, sum[q], bt.ydt);
+            }
+        }
+    };
+
+    // Tiles t0, t0 + P, ... of this workgroup, in pairs: while one tile is computed the
+    // next one's loads are in flight.  The loop body has no exit, so the loads pending at its
+    // back edge are always exactly one register set's (a loop that could leave between the
+    // two halves makes the compiler wait for every load at its top, and then only one tile
+    // at a time is in flight).  Keeping more tiles in flight (two groups of two sets) was
+    // measured slower: the weights of later tiles queue in the memory pipeline ahead of the
+    // current one's.
+    const int nt = (tiles - (int)blockIdx.x + P - 1) / P;
+    Set A, B;
+    int t = blockIdx.x;
+    issue(t, A);
+    __builtin_amdgcn_sched_barrier(0);
+    // the activations (issued first) have landed once at most this tile's loads are
+    // outstanding; the barrier makes every wave's share visible
+    __builtin_amdgcn_s_waitcnt(WAIT_TILE);
+    __syncthreads();
+    for (int i = 0; i + 1 < nt; i += 2) {
+        issue(t + P, B);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(t, A, 0);
+        t += P;
+        issue(t + P, A);  // past the last tile when nt is even: reads nothing
+        __builtin_amdgcn_sched_barrier(0);
+        compute(t, B, 1);
+        t += P;
+    }
+    if (nt & 1) compute(t, A, 0);
+    // loads past the buffers retire before the wave ends
+    __builtin_amdgcn_s_waitcnt(WAIT_ALL);
+}
+
+// LDS of the resident kernel: the staged activations (units x 16 rows x 256 bytes) and two
+// regions of cross-wave sums.
+inline size_t resident_lds(int k, int waves) { return (size_t)(k / 128) * 16 * 256 + (size_t)2 * waves * 64 * 16; }
+constexpr size_t kResidentLdsMax = 160 * 1024;  // LDS per workgroup on gfx950
+// The resident kernel's shape: 8 < m <= 16; slices of 4 or 8 units over at most 8 waves
+// (the shape nearest eight waves); K a multiple of 128 with an even number of groups per
+// row; the activations within the LDS budget; and at least two tiles for every workgroup
+// the CUs hold at that LDS size.
+inline bool resident_shape(int g, int m, int k, int tiles, int num_cus, int* upw, int* waves) {
+    if (m <= 8 || m > 16 || k % 128 != 0 || (k / g) % 2 != 0) return false;
+    const int units = k / 128;
+    *upw = 0;
+    for (int u : {4, 8}) {
+        const int sw = (units + u - 1) / u;
+        if (sw > 8) continue;
+        if (*upw == 0 || (8 - sw) * 4096 + (sw * u - units) < (8 - *waves) * 4096 + (*waves * *upw - units)) {
+            *upw = u;
+            *waves = sw;
+        }
+    }
+    if (*upw == 0) return false;
+    const size_t lds = resident_lds(k, *waves);
+    if (lds > kResidentLdsMax) return false;
+    const int slots = (num_cus > 0 ? num_cus : 256) * (int)(kResidentLdsMax / lds);
+    return tiles >= 2 * slots;
+}
+
 // LDS of the wide kernel per workgroup: each wave's ring of two batches of D units.
 constexpr int wide_rows(int m) { return m <= 4 ? 4 : (m <= 8 ? 8 : 16); }
 constexpr int wide_batch(int m) { return m <= 8 ? 2 : 1; }
@@ -668,11 +922,66 @@ hipError_t launch_wide(int upw, int pair, dim3 grid, dim3 block, size_t lds, hip
     }
 }
 
-// Launch for a shape from tile_shape (wide == 0) or wide_shape (wide == 1: one workgroup of
-// 64 * waves threads per tile; wide == 2: per two tiles).
+// Workgroups of kernel kern resident per CU at (threads, LDS bytes), looked up once per
+// (device, kernel, threads, LDS bytes).
+template <typename Kern>
+int resident_per_cu(Kern kern, int threads, size_t lds) {
+    static std::mutex mu;
+    static std::map<std::tuple<int, const void*, int, size_t>, int> cache;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    const auto key = std::make_tuple(dev, reinterpret_cast<const void*>(kern), threads, lds);
+    std::lock_guard<std::mutex> lock(mu);
+    const auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    int v = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kern, threads, lds) != hipSuccess || v < 1) v = 1;
+    cache.emplace(key, v);
+    return v;
+}
+
+// The resident kernel for a shape from resident_shape: P persistent workgroups, as few as
+// give every workgroup the same number of tiles (give or take one) within one round.
+template <int G, bool SYM, bool XF16, bool GR>
+hipError_t launch_resident(int upw, int m, int k, int waves, const q4::GemvBatch& bt, int tiles, hipStream_t st) {
+    const size_t lds = resident_lds(k, waves);
+    const int threads = 64 * waves;
+    const char* name = XF16 ? "q4_gemv_resident_f16" : "q4_gemv_resident_bf16";
+    auto run = [&](auto kern) {
+        const int cus = q4k_device_cus();
+        const int slots = (cus > 0 ? cus : 256) * resident_per_cu(kern, threads, lds);
+        const int per = (tiles + slots - 1) / slots;
+        const int grid = (tiles + per - 1) / per;
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3((unsigned)threads), lds, st, bt, m, k, tiles);
+        return q4k_launched(name);
+    };
+    if (upw == 4) return run(gemv_resident_kernel<G, SYM, XF16, 4, GR>);
+    if (upw == 8) return run(gemv_resident_kernel<G, SYM, XF16, 8, GR>);
+    return hipErrorInvalidValue;
+}
+
+// Launch for a shape from tile_shape (wide == 0), wide_shape (wide == 1: one workgroup of
+// 64 * waves threads per tile; wide == 2: per two tiles) or resident_shape (wide == 3:
+// persistent workgroups over the batch's tiles, its problems sharing one x).
 template <int G>
 hipError_t launch_tile(int sym, int xd, int m, int k, int upw, int waves, int wide,
                        const q4::GemvBatch& bt, int tiles, hipStream_t st, const char** kname) {
+    if (wide == 3) {
+        const bool gr = bt.count > 1;
+        *kname = xd == 1 ? "q4_gemv_resident_f16" : "q4_gemv_resident_bf16";
+        if (sym) {
+            if (xd == 1)
+                return gr ? launch_resident<G, true, true, true>(upw, m, k, waves, bt, tiles, st)
+                          : launch_resident<G, true, true, false>(upw, m, k, waves, bt, tiles, st);
+            return gr ? launch_resident<G, true, false, true>(upw, m, k, waves, bt, tiles, st)
+                      : launch_resident<G, true, false, false>(upw, m, k, waves, bt, tiles, st);
+        }
+        if (xd == 1)
+            return gr ? launch_resident<G, false, true, true>(upw, m, k, waves, bt, tiles, st)
+                      : launch_resident<G, false, true, false>(upw, m, k, waves, bt, tiles, st);
+        return gr ? launch_resident<G, false, false, true>(upw, m, k, waves, bt, tiles, st)
+                  : launch_resident<G, false, false, false>(upw, m, k, waves, bt, tiles, st);
+    }
     if (wide) {  // wide kernel: each wave's activation ring (its partial sums reuse it)
         // Two 16-row tiles per workgroup (sharing every activation unit) while that still
         // leaves two tiles per CU; the problems' first workgroups are recounted for it.
