@@ -174,6 +174,48 @@ def read_ceiling(torch, dev, sizes):
     return res
 
 
+def join_cost(torch, dev, launches=10):
+    """What joining partial sums across the workgroups of one launch costs (the probe
+    kernels of libq4probe.so, join_probe.hip): launches of row blocks x splits workgroups
+    of 512 threads, 688 in all as in a 11008-row decode GEMV, each writing 512 partial sums;
+    the last arriver of each row block adds them.  Per launch, graph-replayed: the partial
+    stores alone, the join through device-scope release/acquire fences, and the join
+    through device-scope relaxed atomics; every launch's sums are checked."""
+    import ctypes
+    from w4a16_group_wise_q4_amd import _build
+    lib = ctypes.CDLL(_build.PROBE_LIBRARY)
+    vp = ctypes.c_void_p
+    lib.q4probe_join.argtypes = [vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+    lib.q4probe_join.restype = ctypes.c_int
+    lib.q4probe_join_part_floats.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.q4probe_join_part_floats.restype = ctypes.c_int64
+    res = {}
+    for rb, s in ((172, 4), (86, 8), (688, 1)):
+        part = torch.zeros(lib.q4probe_join_part_floats(rb, s), dtype=torch.float32, device=dev)
+        cnt = torch.zeros(rb, dtype=torch.int32, device=dev)
+        y = torch.zeros((launches + 1, rb, 512), dtype=torch.float32, device=dev)
+        row = {}
+        for mode, key in ((0, "partials_only_us"), (1, "fence_join_us"), (2, "atomic_join_us")):
+            def one(it, mode=mode):
+                st = vp(torch.cuda.current_stream().cuda_stream)
+                if lib.q4probe_join(vp(part.data_ptr()), vp(cnt.data_ptr()), vp(y.data_ptr()), rb, s, mode, it, st):
+                    raise RuntimeError("join probe launch failed")
+            y.zero_()
+            g = capture([lambda it=it: one(it) for it in range(1, launches + 1)])
+            y.zero_()
+            row[key] = round(graph_ms(g, 5) / launches * 1e3, 3)
+            if mode:
+                want = torch.arange(1, launches + 1, device=dev, dtype=torch.float32) * (s * (s + 1) / 2)
+                ok = bool(torch.equal(y[1:], want[:, None, None].expand(launches, rb, 512)))
+                ok = ok and int(cnt.abs().sum().item()) == 0
+                row[key.replace("_us", "_sums_ok")] = ok
+        res[f"{rb}x{s}"] = row
+        del part, cnt, y
+    return {"what": "one launch of row blocks x splits workgroups (688 in all), 512 partial sums "
+                    "each, joined by the last arriver of each row block; per launch, graph-replayed",
+            "results": res}
+
+
 def kv_cache_bytes(heads, t, d, g, sym=False):
     """Bytes of one INT4 cache (K or V) holding t tokens: codes, scales, zero words."""
     zeros = 0 if sym else 4 * ((d // g + 7) // 8)
@@ -437,7 +479,7 @@ def main():
     # after idle before its launches reach their steady duration
     ap.add_argument("--warmup", type=int, default=1360)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--legs", default="gemm,quant,sweep,mlp,mse,dequant,kv,midm,gptq",
+    ap.add_argument("--legs", default="gemm,quant,sweep,mlp,mse,dequant,kv,midm,gptq,join",
                     help="comma list of legs besides the headline decode GEMV")
     ap.add_argument("--mlp-n", default="", help="mlp leg: only these weight row counts (comma list)")
     ap.add_argument("--mlp-g", default="", help="mlp leg: only these group sizes (comma list)")
@@ -656,6 +698,10 @@ def main():
         out["dequant"] = {"workload": "7B-like decode matrices, g128 asym packed, to bf16 and fp32",
                           "bytes": "codes n*k/2 + scales 2*n*k/g + zero words read, n*k*out "
                                    "written", "results": res}
+
+    # ------------------------------------------------------------ split-K join cost (probe)
+    if "join" in legs:
+        out["split_k_join"] = join_cost(torch, dev)
 
     # ------------------------------------------------------------ INT4 KV cache (decode attention)
     if "kv" in legs:

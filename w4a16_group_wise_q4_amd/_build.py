@@ -11,8 +11,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libq4.so")
-# the streaming-read probe the benchmark measures its ceiling with (not part of the C ABI)
-PROBE_SOURCE = os.path.join(PKG, "probe", "read_probe.hip")
+# the probes the benchmark measures ceilings and costs with (not part of the C ABI): the
+# streaming read and the cross-workgroup join of partial sums
+PROBE_SOURCES = [os.path.join(PKG, "probe", "read_probe.hip"), os.path.join(PKG, "probe", "join_probe.hip")]
 PROBE_LIBRARY = os.path.join(PKG, "libq4probe.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -85,16 +86,18 @@ def _compile_link(flags, link_flags, out, verbose=False, probe=True):
             for src, obj in zip(srcs, objs)]
     probe_tmp = PROBE_LIBRARY + ".tmp%d" % os.getpid()
     if probe:
-        cmds.append([HIPCC, *FLAGS, *LINK_FLAGS[1:], PROBE_SOURCE, "-o", probe_tmp])
+        cmds.append([HIPCC, *FLAGS, *LINK_FLAGS[1:], *PROBE_SOURCES, "-o", probe_tmp])
     workers = max(1, min(len(cmds), os.cpu_count() or 1, 16))
     with ThreadPoolExecutor(max_workers=workers) as pool:
         results = list(pool.map(_run, cmds))
     logs = []
     tmp = out + ".tmp%d" % os.getpid()
     try:
-        for src, (rc, text) in zip(srcs + [PROBE_SOURCE], results):
+        labels = [os.path.basename(src) for src in srcs]
+        labels.append("the probes (%s)" % ", ".join(os.path.basename(f) for f in PROBE_SOURCES))
+        for label, (rc, text) in zip(labels, results):
             if rc != 0:
-                raise RuntimeError("hipcc failed on %s:\n%s" % (os.path.basename(src), text))
+                raise RuntimeError("hipcc failed on %s:\n%s" % (label, text))
             logs.append(text)
         rc, text = _run([HIPCC, *link_flags, *objs, "-o", tmp])
         if rc != 0:
