@@ -362,6 +362,15 @@ def tile_fits(g, m, k, n, num_cus=256):
     return False
 
 
+def tile_route(g, m, k, n, num_cus=256):
+    """Whether the launcher runs the tile kernel: it fits (tile_fits), and either m = 1 or
+    the launch has more than four tiles per CU (from m = 2 on, launches with fewer go to the
+    wide kernel when it fits)."""
+    if not tile_fits(g, m, k, n, num_cus):
+        return False
+    return m == 1 or -(-n // 16) > 4 * num_cus or not wide_fits(g, m, k)
+
+
 def wide_fits(g, m, k):
     """Whether the wide tile kernel can take a product (m <= 16; the launcher uses it for
     m > 4 and for the m <= 4 shapes the tile kernel cannot take): slices of 4..16 units over
@@ -540,10 +549,33 @@ def test_gemv_tile_cases(m, n, k, g, xdtype, sym):
     p, _ = pack_guarded(w.to(DEV), g, sym)
     y, kname = run_linear(x, p)
     t = "f16" if xdtype == torch.float16 else "bf16"
-    want = "tile" if tile_fits(g, m, k, n) else ("wide" if wide_fits(g, m, k) else "mfma")
+    want = "tile" if tile_route(g, m, k, n) else ("wide" if wide_fits(g, m, k) else "mfma")
     assert kname == f"q4_gemv_{want}_{t}"
     packed = assert_pack_exact(p, host_input(w), g, sym)
     assert_linear_close(y, host_input(x), packed, n, k, g, sym, what=kname)
+
+
+# (m, n, k): m = 2..4 with more than four tiles per CU, where the tile kernel runs (fewer
+# tiles go to the wide kernel); ragged last tiles, slices of 2 to 8 units
+TILE_MANY_CASES = [(2, 16400, 512), (3, 16401, 2048), (4, 16500, 4096)]
+
+
+@pytest.mark.parametrize("m,n,k", TILE_MANY_CASES)
+@pytest.mark.parametrize("g", [32, 64, 128])
+@pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("sym", [False, True])
+def test_gemv_tile_many_tiles(m, n, k, g, xdtype, sym):
+    w = torch.from_numpy(pins.random_weights(n + 7 * k + m + g, n, k))
+    x = synthetic.activations(m, k, seed=m * 37 + k).to(xdtype)
+    note(f"gemv tile many tiles m={m} n={n} k={k} g={g} {xdtype} sym={sym}")
+    p, _ = pack_guarded(w.to(DEV), g, sym)
+    assert tile_route(g, m, k, n)
+    y, kname = run_linear(x, p)
+    t = "f16" if xdtype == torch.float16 else "bf16"
+    assert kname == f"q4_gemv_tile_{t}"
+    packed = assert_pack_exact(p, host_input(w), g, sym)
+    cols = np.unique(np.concatenate([np.arange(0, n, 5), np.arange(n - 24, n)]))
+    assert_linear_close(y, host_input(x), packed, n, k, g, sym, cols=cols, what=kname)
 
 
 GEMV_EDGE = [(1, 16, 32, 32), (16, 1, 32, 32), (5, 37, 96, 32), (16, 33, 192, 64),
@@ -566,25 +598,26 @@ def test_gemv_edge_cases(m, n, k, g, xdtype, sym):
 
 
 def sparse_group_cases():
-    """(m, k, g, kernel) for the sparse-group input: the tile kernel (m = 1, 4), the wide
-    kernel (m = 16), the streaming kernel (k not a multiple of 128, or an odd group count)
-    and its column-chunked form (m = 16, activations beyond the LDS budget)."""
+    """(m, k, g, kernel, n) for the sparse-group input: the tile kernel (m = 1, and m = 4
+    over more than four tiles per CU), the wide kernel (m = 4 and 16), the resident kernel
+    (m = 16 over many tiles), the streaming kernel (k not a multiple of 128, or an odd group
+    count) and its column-chunked form (m = 16, activations beyond the LDS budget)."""
     out = []
     for g in (32, 64, 128):
-        out += [(1, 2048, g, "tile"), (4, 2048, g, "tile"), (16, 2048, g, "wide"),
-                (1, 2048 + g, g, "mfma"), (4, 2048 + g, g, "mfma"), (16, 4096 + g, g, "mfma")]
+        out += [(1, 2048, g, "tile", 40), (4, 2048, g, "tile", 16400), (4, 2048, g, "wide", 40),
+                (16, 2048, g, "wide", 40), (16, 2048, g, "resident", 16400),
+                (1, 2048 + g, g, "mfma", 40), (4, 2048 + g, g, "mfma", 40), (16, 4096 + g, g, "mfma", 40)]
     return out
 
 
-@pytest.mark.parametrize("m,k,g,path", sparse_group_cases())
+@pytest.mark.parametrize("m,k,g,path,n", sparse_group_cases())
 @pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float16])
 @pytest.mark.parametrize("sym", [False, True])
-def test_gemv_sparse_groups(m, k, g, path, xdtype, sym):
+def test_gemv_sparse_groups(m, k, g, path, n, xdtype, sym):
     """Groups whose codes all equal the zero point but one, with large activations on
     those columns: sum |x| per group is about 64 g while each row's result is small, so a
     kernel that formed x * (u - z) as a difference of two large biased sums would miss the
     bound by far.  Every GEMV kernel must stay within it (the operand is the exact u - z)."""
-    n = 40
     w, x = synthetic.sparse_groups(n, k, g, m, xdtype)
     note(f"gemv sparse groups m={m} k={k} g={g} {path} {xdtype} sym={sym}")
     p, _ = pack_guarded(w.to(DEV), g, sym)
@@ -620,13 +653,13 @@ def ranged_activations(kind, m, k, seed):
 @pytest.mark.parametrize("kind", ["narrow", "huge", "tiny", "wide", "subnormal", "split"])
 @pytest.mark.parametrize("m,n,k,g", [(1, 70, 4096, 128), (3, 40, 2048, 32), (2, 33, 5120, 64),
                                      (8, 40, 2048, 128), (1, 40, 2048 + 64, 64),
-                                     (16, 8200, 4096, 128)])
+                                     (16, 8200, 4096, 128), (3, 16400, 2048, 32)])
 def test_gemv_activation_ranges(kind, m, n, k, g):
     """bf16 activations of every exponent range the decode kernels distinguish: the tile
-    kernel converts a slice to exact fp16 when its nonzero exponents span at most 29
-    binades and keeps the exact bf16 operand otherwise; the other kernels (wide, resident,
-    streaming) keep the bf16 operand.  Each result must meet the bound whichever route a
-    wave took."""
+    kernel (m = 1, and m = 3 over more than four tiles per CU) converts a slice to exact
+    fp16 when its nonzero exponents span at most 29 binades and keeps the exact bf16
+    operand otherwise; the other kernels (wide, resident, streaming) keep the bf16 operand.
+    Each result must meet the bound whichever route a wave took."""
     w = torch.from_numpy(pins.random_weights(n + k + g, max(n, 12), k)[:n])
     x = ranged_activations(kind, m, k, seed=m * 29 + k)
     note(f"gemv activation range {kind} m={m} n={n} k={k} g={g}")
@@ -976,7 +1009,8 @@ def test_gemm_prefill_70b_sampled():
 # (m, n, k, g, path): every product path with a 16-bit output: the tile kernel, the wide
 # kernel (one tile and two tiles per workgroup), the streaming kernel (k not a multiple of
 # 128), the chunked mid-M GEMV and the prefill GEMM (a ragged m, and k ending on a half stage)
-EPILOGUE_CASES = [(1, 300, 1024, 128, "tile"), (3, 130, 2048, 64, "tile"), (8, 100, 1024, 32, "wide"),
+EPILOGUE_CASES = [(1, 300, 1024, 128, "tile"), (3, 16500, 1024, 64, "tile"), (3, 130, 2048, 64, "wide"),
+                  (8, 100, 1024, 32, "wide"),
                   (16, 16392, 512, 128, "wide"), (2, 300, 4096 + 64, 64, "mfma"), (40, 1000, 1024, 64, "midm"),
                   (300, 129, 96, 32, "gemm"), (257, 300, 512, 128, "gemm"), (520, 16400, 512, 128, "gemm")]
 HALF_ULP = {torch.bfloat16: 2.0 ** -8, torch.float16: 2.0 ** -11}

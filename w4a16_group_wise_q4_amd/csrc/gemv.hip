@@ -532,6 +532,14 @@ hipError_t launch(const void* x, int xd, int m, const uint32_t* qw, const uint16
         if (sc4 && one_x && q4t::resident_shape(G, m, k, tiles, num_cus, &upw, &tw)) {
             fits = true;
             wide = 3;
+        } else if (sc4 && m >= 2 && tiles <= 4 * num_cus && q4t::wide_shape(G, m, k, &upw, &tw)) {
+            // 2 <= m <= 4 with at most four tiles per CU: the wide kernel, whose waves
+            // stream their activations unit by unit, measured faster than the tile kernel,
+            // whose waves wait for their whole activation slice before any arithmetic
+            // (8.15 against 9.68 us on 4096x11008 at m = 2; 10.6 against 12.2 on 8192x8192
+            // at m = 4).  With more tiles, and at m = 1, the tile kernel is faster.
+            fits = true;
+            wide = q4t::wide_pair(tiles, num_cus) ? 2 : 1;
         } else {
             fits = sc4 && (q4t::tile_shape(G, m, k, tiles, num_cus, &upw, &tw) ||
                            (wide = q4t::wide_shape(G, m, k, &upw, &tw)));
