@@ -789,8 +789,36 @@ def main():
                     res[f"{mat.n}x{mat.k} g{g} {'sym' if sym else 'asym'}"] = row
                     del pks, p0
             del w
+        # the gate and up projections of one layer (two 11008x4096 matrices sharing x) as
+        # one grouped launch, g128 asym: the form a decoder layer runs them in
+        grouped = {}
+        mat = c3["mats"][0]
+        if not args.mlp_n or str(mat.n) in args.mlp_n.split(","):
+            w = mat.make().to(dev)
+            x16 = synthetic.activations(16, mat.k, c3["x_seed"]).to(dev)
+            p0 = q4.q4_quantize_pack(w, 128, False)
+            del w
+            nb = 2 * gemv_bytes(1, mat.n, mat.k, 128, False)
+            cps = max(2, -(-4 * MALL_BYTES // nb))
+            pks = [[q4.PackedWeight(p0.qweight.clone(), p0.scales.clone(), p0.zeros.clone(), mat.n, mat.k,
+                                    128, False) for _ in range(2)] for _ in range(cps)]
+            for m in pick(args.mlp_m, c3["ms"]):
+                xm = x16[:m].contiguous()
+                ys = [torch.empty((m, mat.n), dtype=torch.float32, device=dev) for _ in range(2)]
+                q4.q4_w4a16_gemm_grouped(xm, pks[0], outs=ys)
+                torch.cuda.synchronize()
+                kname = q4.q4_last_kernel()
+                t = graph_ms(capture([lambda pp=pp: q4.q4_w4a16_gemm_grouped(xm, pp, outs=ys)
+                                      for pp in pks]), 5) / cps * 1e-3
+                byt = 2 * gemv_bytes(m, mat.n, mat.k, 128, False) - 2 * m * mat.k  # x read once
+                grouped[f"m{m}"] = {"us": round(t * 1e6, 3), "gbs": round(byt / t / 1e9, 1),
+                                    "frac_hbm": round(byt / t / 1e9 / HBM_PEAK_GBS, 4), "kernel": kname}
+            del pks, p0
         out["mlp_sweep"] = {"workload": "7B-like MLP GEMV, W [11008x4096] and [4096x11008], "
-                                        "m in 1..16, one launch per product", "results": res}
+                                        "m in 1..16, one launch per product", "results": res,
+                            "gate_up_grouped": {"workload": "two 11008x4096 g128 asym matrices "
+                                                            "sharing x, one grouped launch",
+                                                "results": grouped}}
 
     # ------------------------------------------------------------ checkpoint quantize + GEMV sweep
     if "quant" in legs or "sweep" in legs:
